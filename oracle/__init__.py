@@ -1,0 +1,9 @@
+"""CPU oracle (test infrastructure only; see cacheblend_oracle's header)."""
+from .cacheblend_oracle import (rope_theta, rope_rotate, rmsnorm, silu, attention,
+                                qkv_rows, finish_rows, prefill, schedule,
+                                kv_deviation, topk_select, rerotate_chunks, blend,
+                                kv_size_bytes, check_offsets)
+
+__all__ = ["rope_theta", "rope_rotate", "rmsnorm", "silu", "attention", "qkv_rows",
+           "finish_rows", "prefill", "schedule", "kv_deviation", "topk_select",
+           "rerotate_chunks", "blend", "kv_size_bytes", "check_offsets"]

@@ -1,0 +1,328 @@
+"""CPU oracle for CacheBlend-style fusion of independently precomputed chunk KV caches.
+
+TEST INFRASTRUCTURE ONLY.  This is the plain, slow, obviously-correct
+reference that the HIP library is checked against.  Only tests/,
+__graft_entry__.smoke() and bench.py's cpu_baseline leg may import it.  It
+imports nothing from the product package, and the product never imports it.
+
+Arithmetic is NumPy in float64 by default (`dtype=np.float32` exists only to
+time a CPU baseline); no blocking, fusion or reordering beyond what the
+definitions below state.
+
+Pages followed (cited by page title and section):
+  [CB1] "論文解説: CacheBlend — RAGシステム向けKV Cache融合による高速LLMサービング"
+        (0h-n0.github.io): sections "KVキャッシュの定義と偏差メトリクス"
+        (KV deviation, eq. 1), "選択的再計算" (Steps 1-4, K/V merge eqs.),
+        "HKVD（High KV Deviation）トークン選定" (gradual filtering and the
+        top-k selection code), "RoPE（Rotary Position Embedding）との整合性"
+        (rotation matrix R(m), theta_i), "設定パラメータ" (check layer,
+        ratio, min tokens).
+  [CB2] "CacheBlend: Fast Large Language Model Serving for RAG with Cached
+        Knowledge Fusion" explainer (abeam.tech): sections "チャンク単位でKVを
+        保存する" (positions corrected to the real input positions) and
+        "高いずれを持つトークンだけを再計算する" (Q/K/V from selected tokens
+        only; selected tokens attend over the whole input).
+  [PC]  "論文解説: Prompt Cache — モジュラーAttention再利用による低レイテンシ推論"
+        (0h-n0.github.io): section "RoPEにおける位置調整" (k(p) = R(p-p')k(p')).
+
+Readings taken where the pages are silent or disagree (each is listed with
+its reason in the design notes):
+  * Q, K and V are computed for the selected chunk rows plus the suffix only.
+  * Chunks are precomputed at chunk-local positions 0..n_c-1; at fusion the
+    cached K of chunk c is rotated by its offset o_c; V is not rotated.
+  * Deviation = sum of squared differences over the concatenated K and V of
+    all KV heads (mode 'KV'); 'K' and 'V' restrict it to one of the two.
+    It compares the recomputed row against the re-rotated cached row.
+  * Layer indices are 0-based; layer 0 recomputes every chunk row, the check
+    layer is layer 1.
+  * Rows recomputed but not kept keep their cached K/V in the fused cache.
+  * Top-k ties: order by (deviation descending, position ascending), NaN
+    above +inf, -0.0 equal to +0.0; the kept set is returned in ascending
+    position order.
+  * Pre-norm Llama block: RMSNorm, RoPE on interleaved pairs (2i, 2i+1) with
+    theta_i = base^(-2i/d_head), causal softmax attention with GQA head map
+    h -> floor(h * H_kv / H_q), SwiGLU MLP, no biases.
+
+Pin status: every function here is pinned by tests/test_oracle_pins.py except
+the constants of the gradual schedule (`schedule`, kind 'gradual'), which are
+a proposal the pages do not fix: parity unpinned (both sides consume the same
+integer schedule).
+"""
+import math
+
+import numpy as np
+
+
+# --------------------------------------------------------------------------
+# RoPE  [CB1 "RoPE（Rotary Position Embedding）との整合性": R(m) acts on each
+# pair (2i, 2i+1) with angle m*theta_i, theta_i = 10000^(-2i/d);
+# PC "RoPEにおける位置調整": moving a key from p' to p is R(p - p').]
+# --------------------------------------------------------------------------
+def rope_theta(head_dim: int, base: float) -> np.ndarray:
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return base ** (-2.0 * i / head_dim)
+
+
+def rope_rotate(x: np.ndarray, pos, base: float) -> np.ndarray:
+    """Apply R(pos * theta_i) to every pair (x[..., 2i], x[..., 2i+1]).
+
+    x: [n, H, d_head]; pos: [n] (or a scalar) rotation amount per row.  Used both
+    to encode a row at absolute position pos and to move a cached key by a
+    position delta (the rotation composes additively).
+    """
+    x = np.asarray(x)
+    n, _, dh = x.shape
+    pos = np.broadcast_to(np.asarray(pos, dtype=np.float64), (n,))
+    ang = pos[:, None] * rope_theta(dh, base)[None, :]          # [n, dh/2]
+    c = np.cos(ang)[:, None, :].astype(x.dtype)
+    s = np.sin(ang)[:, None, :].astype(x.dtype)
+    x0 = x[..., 0::2]
+    x1 = x[..., 1::2]
+    y = np.empty_like(x)
+    y[..., 0::2] = x0 * c - x1 * s
+    y[..., 1::2] = x0 * s + x1 * c
+    return y
+
+
+# --------------------------------------------------------------------------
+# Transformer block pieces (pre-norm Llama block)
+# --------------------------------------------------------------------------
+def rmsnorm(x: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    ms = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(ms + eps) * g
+
+
+def silu(x: np.ndarray) -> np.ndarray:
+    return x / (1.0 + np.exp(-x))
+
+
+def attention(q, qpos, k, v, kpos):
+    """Causal softmax attention by real position [CB1 "選択的再計算" Step 4;
+    CB2: the selected tokens attend over the whole fused input].
+
+    q: [nq, Hq, dh] at positions qpos; k, v: [nk, Hkv, dh] at positions kpos.
+    Key j is visible to query i iff kpos[j] <= qpos[i].  Query head h reads KV
+    head floor(h * Hkv / Hq).
+    """
+    nq, hq, dh = q.shape
+    hkv = k.shape[1]
+    qpos = np.asarray(qpos)
+    kpos = np.asarray(kpos)
+    out = np.zeros_like(q)
+    hidden = kpos[None, :] > qpos[:, None]                     # [nq, nk]
+    scale = 1.0 / math.sqrt(dh)
+    for h in range(hq):
+        g = (h * hkv) // hq
+        s = (q[:, h, :] @ k[:, g, :].T) * scale
+        s = np.where(hidden, -np.inf, s)
+        m = np.max(s, axis=1, keepdims=True)
+        p = np.exp(s - m)
+        p = p / np.sum(p, axis=1, keepdims=True)
+        out[:, h, :] = p @ v[:, g, :]
+    return out
+
+
+def qkv_rows(w, shape, x, pos):
+    """Step 2 of selective recompute for the rows x at positions pos."""
+    n = x.shape[0]
+    hn = rmsnorm(x, w["attn_norm"].astype(x.dtype), shape.rms_eps)
+    q = (hn @ w["wq"].T).reshape(n, shape.n_q_heads, shape.head_dim)
+    k = (hn @ w["wk"].T).reshape(n, shape.n_kv_heads, shape.head_dim)
+    v = (hn @ w["wv"].T).reshape(n, shape.n_kv_heads, shape.head_dim)
+    return rope_rotate(q, pos, shape.rope_base), rope_rotate(k, pos, shape.rope_base), v
+
+
+def finish_rows(w, shape, x, att):
+    """O projection + residual, then RMSNorm + SwiGLU MLP + residual."""
+    n = x.shape[0]
+    h = x + att.reshape(n, shape.q_dim) @ w["wo"].T
+    hn = rmsnorm(h, w["mlp_norm"].astype(x.dtype), shape.rms_eps)
+    return h + (silu(hn @ w["w_gate"].T) * (hn @ w["w_up"].T)) @ w["w_down"].T
+
+
+def _cast_weights(weights, dtype):
+    return [None if w is None else {k: np.asarray(a, dtype=dtype) for k, a in w.items()}
+            for w in weights]
+
+
+def prefill(weights, shape, x, pos0: int = 0, n_layers=None, dtype=np.float64):
+    """Ordinary full prefill of n tokens at positions pos0..pos0+n-1.
+
+    Returns (K [L][n][Hkv][dh], V [L][n][Hkv][dh], per-layer outputs [L][n][d]).
+    Also used to precompute a chunk's KV alone at chunk-local positions
+    (pos0 = 0) [CB2 "チャンク単位でKVを保存する"].
+    """
+    L = shape.n_layers if n_layers is None else n_layers
+    W = _cast_weights(weights[:L], dtype)
+    x = np.asarray(x, dtype=dtype)
+    n = x.shape[0]
+    pos = np.arange(pos0, pos0 + n)
+    ks = np.zeros((L, n, shape.n_kv_heads, shape.head_dim), dtype=dtype)
+    vs = np.zeros_like(ks)
+    outs = []
+    for l in range(L):
+        q, k, v = qkv_rows(W[l], shape, x, pos)
+        ks[l], vs[l] = k, v
+        x = finish_rows(W[l], shape, x, attention(q, pos, k, v, pos))
+        outs.append(x)
+    return ks, vs, outs
+
+
+# --------------------------------------------------------------------------
+# Recompute schedule  [CB1 "HKVD（High KV Deviation）トークン選定" gradual
+# filtering; "設定パラメータ" check layer [1], ratio [0.15]]
+# --------------------------------------------------------------------------
+def schedule(n_chunk_tokens: int, r_bp: int, kind: str, n_layers: int):
+    """Integer schedule s[0..L]: s[0] = chunk rows recomputed at layer 0,
+    s[l+1] = chunk rows kept after layer l.
+
+    r_bp is the ratio in basis points.  k = max(floor(n*r), 1) as in the
+    selection code of CB1.  'fixed': ratio r from the check layer (1) on.
+    'gradual' (constants are a proposal, parity unpinned): the check layer
+    keeps r1 = min(1, 1.2 r) and the excess over r halves at every later layer.
+    """
+    L, n = n_layers, n_chunk_tokens
+    if r_bp < 0 or r_bp > 10000:
+        raise ValueError("ratio out of range")
+    if r_bp == 0 or n == 0:
+        return [0] * (L + 1)
+    s = [n, n]
+    if kind == "fixed":
+        kk = max(1, (n * r_bp) // 10000)
+        s += [kk] * (L - 1)
+    elif kind == "gradual":
+        r1 = min(10000, (12 * r_bp) // 10)
+        for l in range(1, L):
+            e = min(l - 1, 30)
+            kk = max(1, (n * (r_bp * 2 ** e + r1 - r_bp)) // (10000 * 2 ** e))
+            s.append(min(kk, s[-1]))
+    else:
+        raise ValueError(kind)
+    return s[:L + 1]
+
+
+# --------------------------------------------------------------------------
+# KV deviation and HKVD selection  [CB1 eq. 1 (token KV deviation, L2 norm)
+# and the selection code (sum of squared differences, k = max(int(n r), 1),
+# top-k, indices re-sorted by position)]
+# --------------------------------------------------------------------------
+def kv_deviation(k_new, v_new, k_cached, v_cached, mode: str = "KV"):
+    """Per-row squared L2 distance between recomputed and cached KV rows."""
+    n = k_new.shape[0]
+    dk = np.sum(((k_new - k_cached) ** 2).reshape(n, -1), axis=1)
+    dv = np.sum(((v_new - v_cached) ** 2).reshape(n, -1), axis=1)
+    if mode == "KV":
+        return dk + dv
+    if mode == "K":
+        return dk
+    if mode == "V":
+        return dv
+    raise ValueError(mode)
+
+
+def topk_select(dev, k: int) -> np.ndarray:
+    """Indices of the k largest deviations, returned in ascending order.
+
+    Total order: NaN first, then larger value first, then smaller index first
+    (so equal values, including -0.0 vs +0.0, keep position order).
+    """
+    dev = [float(x) for x in np.asarray(dev).ravel()]
+    order = sorted(range(len(dev)),
+                   key=lambda j: (0 if math.isnan(dev[j]) else 1,
+                                  0.0 if math.isnan(dev[j]) else -dev[j], j))
+    return np.array(sorted(order[:k]), dtype=np.int64)
+
+
+# --------------------------------------------------------------------------
+# Fusion (blend)  [CB1 "選択的再計算" Steps 1-4 and K/V merge eqs.;
+# "HKVD トークン選定" gradual filtering; CB2 sections on position correction
+# and selective recompute]
+# --------------------------------------------------------------------------
+def rerotate_chunks(shape, chunks, offsets, n_tokens, dtype=np.float64):
+    """Fused cache before recompute: chunk c's cached K rotated by its offset,
+    V copied, both placed at positions o_c..o_c+n_c-1."""
+    L = chunks[0][0].shape[0] if chunks else shape.n_layers
+    fk = np.zeros((L, n_tokens, shape.n_kv_heads, shape.head_dim), dtype=dtype)
+    fv = np.zeros_like(fk)
+    for (kc, vc), o in zip(chunks, offsets):
+        nc = kc.shape[1]
+        for l in range(L):
+            fk[l, o:o + nc] = rope_rotate(np.asarray(kc[l], dtype=dtype), o, shape.rope_base)
+            fv[l, o:o + nc] = np.asarray(vc[l], dtype=dtype)
+    return fk, fv
+
+
+def check_offsets(chunks, offsets):
+    o = 0
+    for (kc, _), oc in zip(chunks, offsets):
+        if oc != o:
+            raise ValueError("chunk offsets must start at 0 and be contiguous")
+        o += kc.shape[1]
+    return o
+
+
+def blend(weights, shape, x0, chunks, offsets, n_suffix, sched, dev_mode="KV",
+          min_tokens=0, dtype=np.float64, n_layers=None):
+    """Fuse independently precomputed chunk KVs with selective recompute.
+
+    weights: per-layer dicts; x0: [N][d] embeddings of all prompt tokens in
+    fused order; chunks: list of (K [L][n_c][Hkv][dh], V) precomputed at
+    chunk-local positions; offsets: contiguous chunk starts; the last n_suffix
+    tokens are the query suffix; sched: integer schedule s[0..L].
+
+    Returns a dict with fused_k/fused_v [L][N][Hkv][dh], sel (list of kept
+    chunk positions per layer, ascending), dev [L][N_c] (NaN where not
+    measured), layer_pos/layer_out (rows and outputs of every layer), hidden
+    (final rows).
+    """
+    L = shape.n_layers if n_layers is None else n_layers
+    W = _cast_weights(weights[:L], dtype)
+    nc_tot = check_offsets(chunks, offsets)
+    N = nc_tot + n_suffix
+    x0 = np.asarray(x0, dtype=dtype)
+    assert x0.shape[0] == N
+    sched = list(sched)
+    if len(sched) != L + 1:
+        raise ValueError("schedule needs L+1 entries")
+    if N < min_tokens:                      # short prompt: plain full prefill
+        sched = [nc_tot] * (L + 1)
+    if sched[0] not in (0, nc_tot) or any(b > a for a, b in zip(sched, sched[1:])):
+        raise ValueError("schedule must start at 0 or N_c and be non-increasing")
+
+    fk, fv = rerotate_chunks(shape, chunks, offsets, N, dtype)
+    dev = np.full((L, nc_tot), np.nan)
+    suffix = np.arange(nc_tot, N)
+    C = np.arange(nc_tot) if sched[0] == nc_tot else np.arange(0)
+    x = x0[np.concatenate([C, suffix])]
+    sel, layer_pos, layer_out = [], [], []
+    for l in range(L):
+        R = np.concatenate([C, suffix])            # Step 1: rows recomputed here
+        q, k, v = qkv_rows(W[l], shape, x, R)      # Step 2
+        nC = len(C)
+        if nC:
+            d = kv_deviation(k[:nC], v[:nC], fk[l][C], fv[l][C], dev_mode)
+            dev[l, C] = d
+            keep = (np.arange(nC) if sched[l + 1] == nC
+                    else topk_select(d, sched[l + 1]))
+        else:
+            keep = np.arange(0)
+        rows = np.concatenate([keep, nC + np.arange(n_suffix)]).astype(np.int64)
+        P = R[rows]
+        fk[l][P] = k[rows]                         # Step 3: K/V merge
+        fv[l][P] = v[rows]
+        att = attention(q[rows], P, fk[l], fv[l], np.arange(N))   # Step 4
+        x = finish_rows(W[l], shape, x[rows], att)
+        C = C[keep]
+        sel.append(C.copy())
+        layer_pos.append(P)
+        layer_out.append(x)
+    return {"fused_k": fk, "fused_v": fv, "sel": sel, "dev": dev,
+            "layer_pos": layer_pos, "layer_out": layer_out, "hidden": x,
+            "schedule": sched}
+
+
+def kv_size_bytes(n_layers, n_kv_heads, head_dim, n_tokens, bytes_per_elem):
+    """Bytes of a K and V cache: 2 * L * H_kv * d_head * S * b  [CacheGen
+    explainer, KV cache structure section; CachedAttention explainer,
+    cost analysis section]."""
+    return 2 * n_layers * n_kv_heads * head_dim * n_tokens * bytes_per_elem

@@ -1,0 +1,341 @@
+"""Pins for the CPU oracle: values the pages print, closed forms, invariants,
+library routines and brute force.  Each test names what it pins and the page
+passage (page title + section) it comes from."""
+import itertools
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from workloads import TINY, WORKLOADS, ModelShape
+from tests.helpers import make_case, run_blend, run_full, rel_err
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+TINY_W = WORKLOADS["tiny"]
+
+
+def _read_cases(name):
+    cases, cur = [], None
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        key, *vals = line.split()
+        if key == "case":
+            cur = {}
+            cases.append(cur)
+        else:
+            cur[key] = [float(v) for v in vals]
+    return cases
+
+
+# ---------------------------------------------------------------- RoPE
+def test_rope_worked_example_golden():
+    """CacheBlend explainer (0h-n0), RoPE section: R(m) and theta_i, hand-worked
+    examples (catches sign, pairing-convention and frequency mistakes)."""
+    for c in _read_cases("rope_worked_example.txt"):
+        dh = int(c["head_dim"][0])
+        x = np.array(c["x"]).reshape(1, 1, dh)
+        y = oracle.rope_rotate(x, c["pos"][0], c["base"][0]).ravel()
+        np.testing.assert_allclose(y, c["y"], rtol=0, atol=2e-16)
+
+
+def test_rope_rerotate_closed_form():
+    """Prompt Cache explainer, RoPE position adjustment: a key encoded at p'
+    and rotated by p - p' equals the key encoded at p directly."""
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((50, 4, 64))
+    j = rng.integers(0, 3000, size=50)
+    for delta in (0, 1, 640, 3840, 8191):
+        a = oracle.rope_rotate(oracle.rope_rotate(x, j, 1e4), delta, 1e4)
+        b = oracle.rope_rotate(x, j + delta, 1e4)
+        assert rel_err(a, b) < 1e-12
+        xf = x.astype(np.float32)
+        a32 = oracle.rope_rotate(oracle.rope_rotate(xf, j, 1e4), delta, 1e4)
+        assert rel_err(a32, b) < 1e-5
+
+
+def test_rope_relative_position_identity():
+    """CacheBlend explainer (0h-n0), RoPE section: the score between a query at
+    m+l and a key at m depends on l only; for q = k it is
+    sum_i (q_2i^2 + q_2i+1^2) cos(l theta_i)."""
+    rng = np.random.default_rng(2)
+    dh = 128
+    q = rng.standard_normal((1, 1, dh))
+    k = rng.standard_normal((1, 1, dh))
+    th = 1e4 ** (-2.0 * np.arange(dh // 2) / dh)
+    for l in (0, 1, 7, 300):
+        scores = []
+        for m in (0, 5, 1000, 4000):
+            qa = oracle.rope_rotate(q, m + l, 1e4).ravel()
+            ka = oracle.rope_rotate(k, m, 1e4).ravel()
+            scores.append(qa @ ka)
+        assert max(scores) - min(scores) < 1e-10 * max(1.0, abs(scores[0]))
+        qq = oracle.rope_rotate(q, 17 + l, 1e4).ravel() @ oracle.rope_rotate(q, 17, 1e4).ravel()
+        qv = q.ravel()
+        closed = np.sum((qv[0::2] ** 2 + qv[1::2] ** 2) * np.cos(l * th))
+        assert abs(qq - closed) < 1e-10 * abs(closed)
+
+
+# ---------------------------------------------------------------- block pieces
+def test_rmsnorm_and_silu_vs_library():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((7, 33))
+    g = rng.standard_normal(33)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (33,), torch.from_numpy(g),
+                                       eps=1e-5).numpy()
+    assert rel_err(oracle.rmsnorm(x, g, 1e-5), ref) < 1e-14
+    # closed form: a constant row c maps to c / sqrt(c^2 + eps)
+    c = np.full((1, 8), 3.0)
+    np.testing.assert_allclose(oracle.rmsnorm(c, np.ones(8), 1e-5), 3.0 / math.sqrt(9 + 1e-5),
+                               rtol=1e-15)
+    ref = torch.nn.functional.silu(torch.from_numpy(x)).numpy()
+    assert rel_err(oracle.silu(x), ref) < 1e-14
+
+
+@pytest.mark.parametrize("hq,hkv", [(4, 4), (4, 2), (6, 1)])
+def test_attention_vs_sdpa(hq, hkv):
+    """Causal attention by real position (scattered, sorted query positions)
+    equals torch's scaled_dot_product_attention with a boolean mask; GQA head
+    map equals SDPA's grouped-query semantics."""
+    rng = np.random.default_rng(4)
+    nk, dh = 90, 16
+    qpos = np.sort(rng.choice(nk, size=23, replace=False))
+    q = rng.standard_normal((23, hq, dh))
+    k = rng.standard_normal((nk, hkv, dh))
+    v = rng.standard_normal((nk, hkv, dh))
+    got = oracle.attention(q, qpos, k, v, np.arange(nk))
+    mask = torch.from_numpy(np.arange(nk)[None, :] <= qpos[:, None])
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q).transpose(0, 1), torch.from_numpy(k).transpose(0, 1),
+        torch.from_numpy(v).transpose(0, 1), attn_mask=mask,
+        enable_gqa=(hq != hkv)).transpose(0, 1).numpy()
+    assert rel_err(got, ref) < 1e-13
+
+
+def test_projection_orientation_brute_force():
+    """Weights are row-major [out][in]: y_i = sum_j W[i][j] x_j (loop form)."""
+    shape = ModelShape(1, 8, 2, 1, 4, 12, vocab=16)
+    rng = np.random.default_rng(5)
+    w = {"attn_norm": np.ones(8), "wq": rng.standard_normal((8, 8)),
+         "wk": rng.standard_normal((4, 8)), "wv": rng.standard_normal((4, 8))}
+    x = rng.standard_normal((1, 8))
+    q, k, v = oracle.qkv_rows(w, shape, x, np.array([0]))
+    hn = x[0] / math.sqrt(np.mean(x[0] ** 2) + shape.rms_eps)
+    for i in range(4):
+        assert abs(v.ravel()[i] - sum(w["wv"][i][j] * hn[j] for j in range(8))) < 1e-12
+    for i in range(8):   # position 0: no rotation
+        assert abs(q.ravel()[i] - sum(w["wq"][i][j] * hn[j] for j in range(8))) < 1e-12
+
+
+# ---------------------------------------------------------------- prefill invariants
+def test_prefill_causal_prefix():
+    """A token's K/V and output depend only on the tokens before it: the
+    prefill of a prefix equals the leading rows of the longer prefill."""
+    case = make_case(TINY, (40,), 0, seed=0)
+    k, v, outs = run_full(case)
+    k2, v2, outs2 = oracle.prefill(case.weights, case.shape, case.x0[:17])
+    assert rel_err(k2, k[:, :17]) < 1e-12 and rel_err(v2, v[:, :17]) < 1e-12
+    assert rel_err(outs2[-1], outs[-1][:17]) < 1e-12
+
+
+def test_prefill_position_shift():
+    """Shifting every position by p rotates K by p at every layer and leaves V
+    and the outputs unchanged (scores depend on relative distance only)."""
+    case = make_case(TINY, (48,), 0, seed=1)
+    k0, v0, o0 = run_full(case)
+    kp, vp, op = oracle.prefill(case.weights, case.shape, case.x0, pos0=1000)
+    for l in range(TINY.n_layers):
+        assert rel_err(kp[l], oracle.rope_rotate(k0[l], 1000, TINY.rope_base)) < 1e-10
+        assert rel_err(vp[l], v0[l]) < 1e-10
+    assert rel_err(op[-1], o0[-1]) < 1e-10
+
+
+# ---------------------------------------------------------------- deviation / top-k
+def test_deviation_definition():
+    """CacheBlend explainer (0h-n0) eq. 1 squared (L2 over the token's KV) and
+    the selection code's sum of squared K differences."""
+    rng = np.random.default_rng(6)
+    kn, kc, vn, vc = (rng.standard_normal((9, 3, 8)) for _ in range(4))
+    d = oracle.kv_deviation(kn, vn, kc, vc, "KV")
+    for j in range(9):
+        ref = np.linalg.norm(np.concatenate([(kn[j] - kc[j]).ravel(), (vn[j] - vc[j]).ravel()]))
+        assert abs(d[j] - ref ** 2) < 1e-12 * ref ** 2
+    dk = torch.sum((torch.from_numpy(kn - kc).reshape(9, -1)) ** 2, dim=-1).numpy()
+    assert rel_err(oracle.kv_deviation(kn, vn, kc, vc, "K"), dk) < 1e-15
+
+
+def _brute_topk(dev, k):
+    """The unique k-subset whose every member precedes every non-member under
+    (NaN first, larger value first, smaller index first)."""
+    n = len(dev)
+
+    def before(a, b):
+        da, db = dev[a], dev[b]
+        na, nb = math.isnan(da), math.isnan(db)
+        if na != nb:
+            return na
+        if not na and da != db:
+            return da > db
+        return a < b
+
+    found = [s for s in itertools.combinations(range(n), k)
+             if all(before(a, b) for a in s for b in range(n) if b not in s)]
+    assert len(found) == 1
+    return list(found[0])
+
+
+def test_topk_brute_force_with_ties_and_nan():
+    rng = np.random.default_rng(7)
+    for trial in range(60):
+        n = int(rng.integers(1, 11))
+        vals = rng.choice([0.0, -0.0, 1.0, 2.5, np.inf, np.nan, -1.0, 3.0], size=n)
+        for k in range(1, n + 1):
+            assert list(oracle.topk_select(vals, k)) == _brute_topk(list(vals), k)
+
+
+def test_topk_vs_torch_distinct():
+    """On distinct values the kept set equals torch.topk's, then sorted by
+    position as in the CacheBlend explainer's selection code."""
+    rng = np.random.default_rng(8)
+    for n, k in [(1, 1), (10, 1), (10, 10), (384, 57), (3840, 691), (8192, 1228)]:
+        d = rng.permutation(n).astype(np.float64) + rng.random(n) * 0.5
+        ref = torch.topk(torch.from_numpy(d), k).indices.sort().values.numpy()
+        np.testing.assert_array_equal(oracle.topk_select(d, k), ref)
+
+
+# ---------------------------------------------------------------- schedule
+def test_schedule_shape_and_endpoints():
+    """k = max(floor(n r), 1) (selection code); r = 100% recomputes all, r = 0
+    recomputes none (full KV reuse); non-increasing."""
+    assert oracle.schedule(384, 1500, "fixed", 2) == [384, 384, 57]
+    assert oracle.schedule(3840, 1500, "fixed", 4) == [3840, 3840, 576, 576, 576]
+    assert oracle.schedule(10, 1, "fixed", 3) == [10, 10, 1, 1]
+    assert oracle.schedule(384, 0, "gradual", 2) == [0, 0, 0]
+    for L in (1, 2, 32, 60):
+        for r in (1, 500, 1000, 1500, 1800, 5000, 10000):
+            for kind in ("fixed", "gradual"):
+                s = oracle.schedule(3840, r, kind, L)
+                assert len(s) == L + 1 and s[0] == 3840 and s[1] == 3840
+                assert all(b <= a for a, b in zip(s, s[1:]))
+                if r == 10000:
+                    assert s == [3840] * (L + 1)
+    # gradual proposal (parity unpinned): regression values
+    assert oracle.schedule(384, 1500, "gradual", 2) == [384, 384, 69]
+    s = oracle.schedule(3840, 1500, "gradual", 32)
+    assert s[:10] == [3840, 3840, 691, 633, 604, 590, 583, 579, 577, 576]
+    assert s[-1] == 576
+
+
+def test_kv_size_formula_vs_printed_examples():
+    for line in open(os.path.join(GOLDEN, "kv_size_examples.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        name, L, H, dh, S, b, approx, tol = line.split()
+        got = oracle.kv_size_bytes(int(L), int(H), int(dh), int(S), int(b))
+        assert abs(got - float(approx)) <= float(tol) * float(approx), name
+    assert oracle.kv_size_bytes(80, 64, 128, 4000, 2) / 32e9 == pytest.approx(0.33, abs=0.01)
+
+
+# ---------------------------------------------------------------- blend invariants
+@pytest.fixture(scope="module")
+def tiny_case():
+    return make_case(TINY, TINY_W.chunk_lens, TINY_W.n_suffix, seed=0)
+
+
+@pytest.fixture(scope="module")
+def tiny_full(tiny_case):
+    return run_full(tiny_case)
+
+
+def test_full_recompute_equals_prefill(tiny_case, tiny_full):
+    """P-a: r = 100% (every chunk row kept at every layer) is an ordinary full
+    prefill of the fused prompt."""
+    L, nc = TINY.n_layers, tiny_case.n_chunk_tokens
+    res = run_blend(tiny_case, [nc] * (L + 1))
+    k, v, outs = tiny_full
+    assert rel_err(res["fused_k"], k) < 1e-10
+    assert rel_err(res["fused_v"], v) < 1e-10
+    assert rel_err(res["hidden"], outs[-1]) < 1e-10
+    # min_tokens above N forces the same full prefill
+    res2 = oracle.blend(tiny_case.weights, TINY, tiny_case.x0, tiny_case.chunks,
+                        tiny_case.offsets, tiny_case.n_suffix, [0] * (L + 1),
+                        min_tokens=10 ** 6)
+    assert rel_err(res2["fused_k"], k) < 1e-10
+
+
+def test_single_chunk_r0_is_cache():
+    """P-b: one chunk at offset 0 with no recompute leaves the cache as is."""
+    case = make_case(TINY, (96,), 0, seed=2)
+    res = run_blend(case, [0] * (TINY.n_layers + 1))
+    np.testing.assert_array_equal(res["fused_k"], case.chunks[0][0])
+    np.testing.assert_array_equal(res["fused_v"], case.chunks[0][1])
+
+
+def test_layer0_deviation_vanishes(tiny_case):
+    """P-f: layer-0 K/V depend on the token and its position only, so the
+    recomputed rows equal the re-rotated cache up to rounding."""
+    res = run_blend(tiny_case, oracle.schedule(tiny_case.n_chunk_tokens, 1500, "gradual", 2))
+    scale = np.max(np.sum(tiny_case.chunks[0][0][0].reshape(128, -1) ** 2, axis=1))
+    assert np.nanmax(res["dev"][0]) < 1e-24 * scale
+
+
+def test_first_chunk_matches_full_prefill(tiny_case, tiny_full):
+    """P-g: the chunk at offset 0 has no preceding context, so its rows equal
+    full prefill at every layer whatever is selected."""
+    res = run_blend(tiny_case, oracle.schedule(tiny_case.n_chunk_tokens, 1500, "gradual", 2))
+    k, v, _ = tiny_full
+    n0 = tiny_case.chunks[0][0].shape[1]
+    assert rel_err(res["fused_k"][:, :n0], k[:, :n0]) < 1e-10
+    assert rel_err(res["fused_v"][:, :n0], v[:, :n0]) < 1e-10
+    assert np.max(res["dev"][1][:n0]) < 1e-20 * np.max(res["dev"][1][n0:])
+
+
+def test_check_layer_identity(tiny_case, tiny_full):
+    """P-h: at the check layer the recomputed K/V are exact, so dev_1 is the
+    true deviation of the cache from full prefill (eq. 1 squared) and the
+    fused-vs-full error equals the deviation of the rows not kept."""
+    nc = tiny_case.n_chunk_tokens
+    k, v, _ = tiny_full
+    fk0, fv0 = oracle.rerotate_chunks(TINY, tiny_case.chunks, tiny_case.offsets,
+                                      tiny_case.n_tokens)
+    true_dev = oracle.kv_deviation(k[1][:nc], v[1][:nc], fk0[1][:nc], fv0[1][:nc])
+    for r in (500, 1500, 5000):
+        res = run_blend(tiny_case, oracle.schedule(nc, r, "fixed", 2))
+        assert rel_err(res["dev"][1], true_dev) < 1e-10
+        kept = set(res["sel"][1].tolist())
+        err = np.sum((res["fused_k"][1][:nc] - k[1][:nc]) ** 2, axis=(1, 2)) + \
+            np.sum((res["fused_v"][1][:nc] - v[1][:nc]) ** 2, axis=(1, 2))
+        dropped = [j for j in range(nc) if j not in kept]
+        assert abs(err.sum() - true_dev[dropped].sum()) < 1e-9 * true_dev.sum()
+        # the kept rows are exactly the largest deviations
+        assert min(true_dev[list(kept)]) >= max(true_dev[dropped])
+
+
+def test_deviation_falls_as_r_grows():
+    """North-star check: total KV deviation of the fused cache from full
+    prefill does not grow as r grows, and is zero at r = 100% (tiny config,
+    seeds 0-4, gradual schedule)."""
+    rs = [0, 500, 1000, 1500, 1800, 5000, 10000]
+    for seed in range(5):
+        case = make_case(TINY, TINY_W.chunk_lens, TINY_W.n_suffix, seed=seed)
+        k, v, _ = run_full(case)
+        tot = []
+        for r in rs:
+            res = run_blend(case, oracle.schedule(case.n_chunk_tokens, r, "gradual", 2))
+            tot.append(float(np.sum((res["fused_k"] - k) ** 2) + np.sum((res["fused_v"] - v) ** 2)))
+        assert all(b <= a * (1 + 1e-12) for a, b in zip(tot, tot[1:])), (seed, tot)
+        assert tot[-1] < 1e-20 * tot[0]
+
+
+def test_gqa_blend_full_recompute():
+    """P-a again with grouped-query attention (Yi-style 56/8 ratio scaled down)."""
+    shape = ModelShape(2, 128, 7, 1, 16, 256, vocab=512)
+    case = make_case(shape, (40, 24), 8, seed=3)
+    nc = case.n_chunk_tokens
+    res = run_blend(case, [nc] * 3)
+    k, v, outs = run_full(case)
+    assert rel_err(res["fused_k"], k) < 1e-10 and rel_err(res["hidden"], outs[-1]) < 1e-10
