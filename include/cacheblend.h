@@ -1,0 +1,296 @@
+/*
+ * cacheblend.h — C ABI of libcacheblend.so: fusion of independently
+ * precomputed per-chunk KV caches with selective recompute, on one AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operation (pages cited by title and section):
+ *  - "論文解説: CacheBlend — RAGシステム向けKV Cache融合による高速LLMサービング"
+ *    (0h-n0.github.io), section "選択的再計算": each layer recomputes Q/K/V
+ *    for a selected token set only, merges the recomputed K/V of that set
+ *    with the precomputed K/V of the other tokens, and runs ordinary attention;
+ *    section "HKVD（High KV Deviation）トークン選定": the set is chosen by
+ *    per-token KV deviation and narrowed layer by layer (gradual filtering);
+ *    section "RoPE（Rotary Position Embedding）との整合性": rotation R(m);
+ *    section "vLLM統合": the serving interface is fetch-per-layer,
+ *    prefill-per-layer and synchronize, mirrored by cb_fetch_kv,
+ *    cb_prefill_layer and cb_synchronize; section "設定パラメータ": check
+ *    layer, recompute ratio and minimum token count.
+ *  - "CacheBlend" explainer (abeam.tech), section "チャンク単位でKVを保存す
+ *    る": chunk caches are computed alone and their positions are corrected
+ *    to the real input positions at reuse.
+ *  - "論文解説: Prompt Cache" (0h-n0.github.io), section "RoPEにおける位置調整":
+ *    a key encoded at p' moves to p by the rotation R(p - p').
+ *
+ * Conventions used by every call:
+ *  - Pointers are plain addresses.  "device" = HIP device memory on the
+ *    current device; "host" = ordinary host memory; "pinned" = page-locked
+ *    host memory from hipHostMalloc.  The caller allocates and owns every
+ *    buffer passed in; the library never frees caller memory.
+ *  - Element type of weights, chunk KVs, x0 and the fused KV is the model
+ *    dtype (CB_F32 = IEEE float32, CB_BF16 = bfloat16); deviations and
+ *    hidden outputs are float32; indices are int32.
+ *  - Layouts are row-major.  A KV row is [H_kv][d_head]; a cache is
+ *    [L][tokens][H_kv][d_head]; weight matrices are [out][in].
+ *  - RoPE pairs are interleaved (2i, 2i+1) with theta_i = base^(-2i/d_head);
+ *    cos/sin of pos*theta_i are evaluated in float64 and rounded once to
+ *    float32.
+ *  - `stream` is a hipStream_t (NULL = the null stream).  Work is queued
+ *    asynchronously; results are ready once the stream has been synchronized.
+ *  - Errors: every call returns cb_status.  Arguments are validated before
+ *    anything is queued, so a failed call has no side effects.  The message
+ *    of the last failure on the calling thread is cb_last_error().  No C++
+ *    exception or abort crosses the ABI.  Faults of queued work surface at
+ *    the next synchronizing call.
+ */
+#ifndef CACHEBLEND_H
+#define CACHEBLEND_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CB_ABI_VERSION 1
+
+typedef enum cb_status {
+    CB_OK = 0,
+    CB_E_INVALID = -1,     /* null pointer, bad enum, negative size       */
+    CB_E_SHAPE = -2,       /* sizes that do not fit together / unsupported */
+    CB_E_NOT_PINNED = -3,  /* host chunk KV is not page-locked             */
+    CB_E_SCHEDULE = -4,    /* schedule not monotone / out of range         */
+    CB_E_OOM = -5,         /* workspace allocation failed                  */
+    CB_E_HIP = -6,         /* a HIP runtime call failed                    */
+    CB_E_BAD_STATE = -7,   /* layer-stepped calls out of order             */
+    CB_E_UNSUPPORTED = -8  /* valid request the library does not implement */
+} cb_status;
+
+typedef enum cb_dtype { CB_F32 = 0, CB_BF16 = 1 } cb_dtype;
+
+/* Recompute schedule kinds (CacheBlend explainer (0h-n0), sections on HKVD
+ * selection and configuration parameters).  With n = chunk tokens and r in
+ * basis points, both give s[0] = s[1] = n (layer 0 recomputes every chunk
+ * row; layer 1 is the check layer) and r = 0 gives s = 0 (full KV reuse):
+ *  FIXED:   s[l] = max(1, floor(n r / 10000)) for l >= 2.
+ *  GRADUAL: r1 = min(10000, floor(1.2 r)); for l >= 1,
+ *           s[l+1] = max(1, floor(n (r 2^e + r1 - r) / (10000 2^e))),
+ *           e = min(l-1, 30), clamped to be non-increasing. */
+typedef enum cb_schedule_kind { CB_SCHED_GRADUAL = 0, CB_SCHED_FIXED = 1 } cb_schedule_kind;
+
+/* Deviation measure: sum of squared differences between the recomputed row
+ * and the re-rotated cached row, over K and V (default), K only or V only
+ * (CacheBlend explainer (0h-n0), eq. 1 and the selection code). */
+typedef enum cb_dev_mode { CB_DEV_KV = 0, CB_DEV_K = 1, CB_DEV_V = 2 } cb_dev_mode;
+
+typedef struct cb_model_cfg {
+    int32_t n_layers;
+    int32_t d_model;
+    int32_t n_q_heads;
+    int32_t n_kv_heads;   /* must divide n_q_heads (GQA)                 */
+    int32_t head_dim;     /* even; 64 or 128                             */
+    int32_t ffn_dim;
+    double  rope_base;    /* e.g. 10000                                  */
+    float   rms_eps;      /* e.g. 1e-5                                   */
+    int32_t dtype;        /* cb_dtype                                    */
+} cb_model_cfg;
+
+/* One pre-norm Llama block.  All device pointers in the model dtype:
+ * attn_norm[d], wq[Hq*dh][d], wk[Hkv*dh][d], wv[Hkv*dh][d], wo[d][Hq*dh],
+ * mlp_norm[d], w_gate[F][d], w_up[F][d], w_down[d][F].  No biases. */
+typedef struct cb_layer_weights {
+    const void* attn_norm;
+    const void* wq;
+    const void* wk;
+    const void* wv;
+    const void* wo;
+    const void* mlp_norm;
+    const void* w_gate;
+    const void* w_up;
+    const void* w_down;
+} cb_layer_weights;
+
+/* A precomputed chunk cache at chunk-local positions 0..n_tokens-1.
+ * k, v: [L][n_tokens][H_kv][d_head]; layer l starts at element
+ * l * layer_stride (layer_stride >= n_tokens*H_kv*d_head), which lets chunks
+ * live inside a larger pool.  on_host = 0: device memory; 1: pinned host
+ * memory, copied to the device layer by layer on the library's side stream. */
+typedef struct cb_chunk_kv {
+    const void* k;
+    const void* v;
+    int32_t n_tokens;
+    int32_t on_host;
+    int64_t layer_stride;
+} cb_chunk_kv;
+
+typedef struct cb_request {
+    int32_t n_chunks;
+    const cb_chunk_kv* chunks;      /* host [n_chunks]                      */
+    const int32_t* chunk_offsets;   /* host [n_chunks]: 0, then contiguous  */
+    int32_t n_suffix;               /* query tokens after the last chunk    */
+    const void* x0;                 /* device [N][d]: layer-0 input rows of
+                                       all N prompt tokens in fused order   */
+    const int32_t* schedule;        /* host [L+1] or NULL: s[0..L] (see
+                                       cb_schedule_kind); NULL = derive it
+                                       from recompute_bp and schedule_kind  */
+    int32_t recompute_bp;           /* r in basis points, 0..10000          */
+    int32_t schedule_kind;          /* cb_schedule_kind                     */
+    int32_t dev_mode;               /* cb_dev_mode                          */
+    int32_t min_tokens;             /* N < min_tokens: plain full prefill   */
+} cb_request;
+
+/* Outputs of a fusion.  N = chunk tokens N_c + suffix. */
+typedef struct cb_outputs {
+    void* fused_k;      /* device [L][N][H_kv][d_head], model dtype (required) */
+    void* fused_v;      /* device [L][N][H_kv][d_head], model dtype (required) */
+    int32_t* sel_idx;   /* device [L][N_c] or NULL: row l holds the positions
+                           kept after layer l, ascending, first s[l+1] valid  */
+    int32_t* sel_count; /* host [L] or NULL: s[l+1], written before return   */
+    float* hidden_out;  /* device [N_s + s[L]][d] or NULL: output rows of the
+                           last layer (kept chunk rows then suffix, by position) */
+    float* deviation;   /* device [L][N_c] or NULL: per-token deviation where
+                           measured, NaN elsewhere                            */
+} cb_outputs;
+
+typedef struct cb_model cb_model;
+typedef struct cb_plan cb_plan;
+
+/* ------------------------------------------------------------- basics */
+int cb_abi_version(void);
+/* Message of the last failed call on this thread ("" if none).  Valid until
+ * the next failing call on the same thread. */
+const char* cb_last_error(void);
+
+/* Host helper: the integer schedule s[0..n_layers] into s_out (host). */
+cb_status cb_schedule(int32_t n_chunk_tokens, int32_t recompute_bp, int32_t kind,
+                      int32_t n_layers, int32_t* s_out);
+
+/* ------------------------------------------------------------- model */
+/* Validates cfg and copies the weight pointer table (not the weights: the
+ * caller keeps them alive until cb_model_destroy).  Builds the RoPE table on
+ * the current device.  *out receives the handle. */
+cb_status cb_model_create(const cb_model_cfg* cfg, const cb_layer_weights* layers,
+                          cb_model** out);
+void cb_model_destroy(cb_model* model);
+
+/* ------------------------------------------------------------- fusion */
+/* One-shot fusion of a request: per layer, rotate the chunk caches to their
+ * real positions, recompute the scheduled rows, measure deviation, keep the
+ * top rows, merge them into the fused cache, attend over the whole fused
+ * cache, finish the block.  Equivalent to cb_plan_create, then cb_fetch_kv
+ * and cb_prefill_layer for every layer, then cb_plan_destroy. */
+cb_status cb_blend(cb_model* model, const cb_request* req, const cb_outputs* out,
+                   void* stream);
+
+/* Layer-stepped form.  cb_plan_create validates everything and reserves the
+ * workspace (stream-ordered on `stream`).  cb_fetch_kv(plan, l) queues the
+ * load (pinned host -> device for host chunks) and rotation of layer l's
+ * chunk caches into fused_k/v[l] on the plan's side stream and records an
+ * event; layers may be fetched in any order, each at most once.
+ * cb_prefill_layer(plan, l) must be called for l = 0, 1, ... in order; it
+ * fetches layer l first if that was not done, makes `stream` wait for the
+ * fetch, and queues the layer.  cb_synchronize blocks until all queued work
+ * of the plan is done.  cb_plan_destroy releases the plan (it does not wait;
+ * the workspace is freed in stream order). */
+cb_status cb_plan_create(cb_model* model, const cb_request* req, const cb_outputs* out,
+                         void* stream, cb_plan** plan);
+cb_status cb_fetch_kv(cb_plan* plan, int32_t layer);
+cb_status cb_prefill_layer(cb_plan* plan, int32_t layer);
+cb_status cb_synchronize(cb_plan* plan);
+void cb_plan_destroy(cb_plan* plan);
+
+/* Full prefill of n_tokens rows x0 (device [n][d], model dtype) at
+ * positions pos0..pos0+n-1.  k_out/v_out: device [L][n][H_kv][d_head] model
+ * dtype; hidden_out: device [n][d] float32 or NULL.  With pos0 = 0 this
+ * precomputes a chunk cache at chunk-local positions. */
+cb_status cb_prefill(cb_model* model, const void* x0, int32_t n_tokens, int32_t pos0,
+                     void* k_out, void* v_out, float* hidden_out, void* stream);
+
+/* ------------------------------------------------------------- timing
+ * Per-kernel-class timing of the fusion path with HIP events recorded on the
+ * stream each kernel runs on (the caller's stream, or the side stream for
+ * rotation).  Off by default; while on, every launch of a plan on this model
+ * is bracketed by an event pair.  Algorithmic work per launch is accumulated
+ * from the launch shapes: flops for the projections, bytes moved for the
+ * bandwidth-bound kernels (attention flops depend on the kept positions and
+ * are left to the caller). */
+typedef enum cb_kernel_class {
+    CB_K_ROTATE = 0,    /* chunk K rotation + V copy into the fused cache   */
+    CB_K_RMSNORM,
+    CB_K_GEMM_QKV,
+    CB_K_DEVIATION,
+    CB_K_SELECT,
+    CB_K_SCATTER,
+    CB_K_ATTENTION,
+    CB_K_GEMM_O,
+    CB_K_GEMM_GATEUP,
+    CB_K_GEMM_DOWN,
+    CB_K_COUNT
+} cb_kernel_class;
+
+typedef struct cb_kernel_stat {
+    int64_t launches;
+    double total_ms;    /* summed event-measured durations   */
+    double flops;       /* summed algorithmic flops          */
+    double bytes;       /* summed algorithmic bytes moved    */
+} cb_kernel_stat;
+
+/* enable != 0 turns timing on and clears the statistics; 0 turns it off. */
+cb_status cb_profile_enable(cb_model* model, int32_t enable);
+/* Waits for the timed work and writes stats[CB_K_COUNT] (host). */
+cb_status cb_profile_read(cb_model* model, cb_kernel_stat* stats);
+
+/* ------------------------------------------------------------- kernels
+ * Single steps of the path, exposed for parity tests.  All pointers are
+ * device pointers unless stated. */
+
+/* RoPE re-alignment (Prompt Cache explainer, RoPE position adjustment):
+ * k_out[t] = R(delta) k_in[t] for n_tokens rows of [n_heads][head_dim];
+ * v_out[t] = v_in[t] when v_in is not NULL.  In-place (k_out == k_in) is
+ * allowed; otherwise buffers must not overlap. */
+cb_status cb_rope_rerotate(int32_t dtype, const void* k_in, void* k_out,
+                           const void* v_in, void* v_out, int32_t n_tokens,
+                           int32_t n_heads, int32_t head_dim, int32_t delta,
+                           double rope_base, void* stream);
+
+/* KV deviation (CacheBlend explainer (0h-n0), eq. 1 squared):
+ * dev[i] = sum over the row of (k_new - k_cached)^2 (+ (v_new - v_cached)^2)
+ * for n_rows rows of row_elems elements; fp32 accumulation. */
+cb_status cb_deviation(int32_t dtype, const void* k_new, const void* v_new,
+                       const void* k_cached, const void* v_cached, int32_t n_rows,
+                       int32_t row_elems, int32_t dev_mode, float* dev_out, void* stream);
+
+/* HKVD selection: the k indices of the largest dev values under the total
+ * order (NaN first, larger first, -0.0 == +0.0, then smaller index first),
+ * written ascending to idx_out[0..k).  0 <= k <= n. */
+cb_status cb_topk_select(const float* dev, int32_t n, int32_t k, int32_t* idx_out,
+                         void* stream);
+
+/* dst row i = src row idx[i] (gather) / dst row idx[i] = src row i (scatter);
+ * rows of row_bytes bytes (a multiple of 4); idx device int32[n_rows]. */
+cb_status cb_gather_rows(const void* src, void* dst, const int32_t* idx, int32_t n_rows,
+                         int64_t row_bytes, void* stream);
+cb_status cb_scatter_rows(const void* src, void* dst, const int32_t* idx, int32_t n_rows,
+                          int64_t row_bytes, void* stream);
+
+/* y = x / sqrt(mean(x^2) + eps) * g over rows of d; x float32 or model
+ * dtype (x_dtype), g and y in y_dtype. */
+cb_status cb_rmsnorm(int32_t x_dtype, const void* x, int32_t y_dtype, const void* g,
+                     void* y, int32_t rows, int32_t d, float eps, void* stream);
+
+/* c[m][n] = sum_k a[m][k] b[n][k] (float32 out) on the matrix cores.
+ * k must be a multiple of 64 (bf16) or 32 (f32). */
+cb_status cb_gemm(int32_t dtype, const void* a, const void* b, float* c, int32_t m,
+                  int32_t n, int32_t k, void* stream);
+
+/* Causal attention by real position: n_q query rows q [n_q][Hq][dh] at
+ * positions q_pos (device int32, ascending) over keys k, v [n_kv][Hkv][dh] at
+ * positions 0..n_kv-1; key j visible to query i iff j <= q_pos[i]; query
+ * head h reads KV head h / (Hq/Hkv); out [n_q][Hq][dh] in dtype. */
+cb_status cb_attention(int32_t dtype, const void* q, const int32_t* q_pos, int32_t n_q,
+                       const void* k, const void* v, int32_t n_kv, int32_t n_q_heads,
+                       int32_t n_kv_heads, int32_t head_dim, void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CACHEBLEND_H */

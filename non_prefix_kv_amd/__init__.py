@@ -1,0 +1,309 @@
+"""Python binding of libcacheblend.so (C ABI in include/cacheblend.h).
+
+Argument marshalling only: every step of the fusion path runs in the HIP
+kernels of the library.  PyTorch tensors are accepted for device memory and
+`torch.cuda` streams; they are passed to the library as raw pointers.  There
+is no fallback: importing this package fails when the library is not built.
+"""
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcacheblend.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m non_prefix_kv_amd.build` (hipcc, gfx950)")
+_lib = ctypes.CDLL(LIB_PATH)
+
+# ------------------------------------------------------------------ constants
+CB_ABI_VERSION = 1
+CB_OK, CB_E_INVALID, CB_E_SHAPE, CB_E_NOT_PINNED, CB_E_SCHEDULE = 0, -1, -2, -3, -4
+CB_E_OOM, CB_E_HIP, CB_E_BAD_STATE, CB_E_UNSUPPORTED = -5, -6, -7, -8
+CB_F32, CB_BF16 = 0, 1
+CB_SCHED_GRADUAL, CB_SCHED_FIXED = 0, 1
+CB_DEV_KV, CB_DEV_K, CB_DEV_V = 0, 1, 2
+
+_c_i32, _c_i64, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+
+
+class cb_model_cfg(ctypes.Structure):
+    _fields_ = [("n_layers", _c_i32), ("d_model", _c_i32), ("n_q_heads", _c_i32),
+                ("n_kv_heads", _c_i32), ("head_dim", _c_i32), ("ffn_dim", _c_i32),
+                ("rope_base", ctypes.c_double), ("rms_eps", ctypes.c_float),
+                ("dtype", _c_i32)]
+
+
+class cb_layer_weights(ctypes.Structure):
+    _fields_ = [(n, _c_p) for n in ("attn_norm", "wq", "wk", "wv", "wo", "mlp_norm",
+                                     "w_gate", "w_up", "w_down")]
+
+
+class cb_chunk_kv(ctypes.Structure):
+    _fields_ = [("k", _c_p), ("v", _c_p), ("n_tokens", _c_i32), ("on_host", _c_i32),
+                ("layer_stride", _c_i64)]
+
+
+class cb_request(ctypes.Structure):
+    _fields_ = [("n_chunks", _c_i32), ("chunks", ctypes.POINTER(cb_chunk_kv)),
+                ("chunk_offsets", ctypes.POINTER(_c_i32)), ("n_suffix", _c_i32),
+                ("x0", _c_p), ("schedule", ctypes.POINTER(_c_i32)),
+                ("recompute_bp", _c_i32), ("schedule_kind", _c_i32), ("dev_mode", _c_i32),
+                ("min_tokens", _c_i32)]
+
+
+class cb_outputs(ctypes.Structure):
+    _fields_ = [("fused_k", _c_p), ("fused_v", _c_p), ("sel_idx", _c_p),
+                ("sel_count", ctypes.POINTER(_c_i32)), ("hidden_out", _c_p),
+                ("deviation", _c_p)]
+
+
+def _sig(name, res, *args):
+    f = getattr(_lib, name)
+    f.restype = res
+    f.argtypes = list(args)
+    return f
+
+
+_P = ctypes.POINTER
+_fn = {
+    "cb_abi_version": (ctypes.c_int,),
+    "cb_last_error": (ctypes.c_char_p,),
+    "cb_schedule": (ctypes.c_int, _c_i32, _c_i32, _c_i32, _c_i32, _P(_c_i32)),
+    "cb_model_create": (ctypes.c_int, _P(cb_model_cfg), _P(cb_layer_weights), _P(_c_p)),
+    "cb_model_destroy": (None, _c_p),
+    "cb_blend": (ctypes.c_int, _c_p, _P(cb_request), _P(cb_outputs), _c_p),
+    "cb_plan_create": (ctypes.c_int, _c_p, _P(cb_request), _P(cb_outputs), _c_p, _P(_c_p)),
+    "cb_fetch_kv": (ctypes.c_int, _c_p, _c_i32),
+    "cb_prefill_layer": (ctypes.c_int, _c_p, _c_i32),
+    "cb_synchronize": (ctypes.c_int, _c_p),
+    "cb_plan_destroy": (None, _c_p),
+    "cb_prefill": (ctypes.c_int, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p),
+    "cb_rope_rerotate": (ctypes.c_int, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
+                         _c_i32, ctypes.c_double, _c_p),
+    "cb_deviation": (ctypes.c_int, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p,
+                     _c_p),
+    "cb_topk_select": (ctypes.c_int, _c_p, _c_i32, _c_i32, _c_p, _c_p),
+    "cb_gather_rows": (ctypes.c_int, _c_p, _c_p, _c_p, _c_i32, _c_i64, _c_p),
+    "cb_scatter_rows": (ctypes.c_int, _c_p, _c_p, _c_p, _c_i32, _c_i64, _c_p),
+    "cb_rmsnorm": (ctypes.c_int, _c_i32, _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_i32,
+                   ctypes.c_float, _c_p),
+    "cb_gemm": (ctypes.c_int, _c_i32, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p),
+    "cb_attention": (ctypes.c_int, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_i32,
+                     _c_i32, _c_i32, _c_p, _c_p),
+}
+RAW = {name: _sig(name, spec[0], *spec[1:]) for name, spec in _fn.items()}
+EXPORTED = tuple(_fn)
+
+
+class CBError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"cacheblend status {status}: {msg}")
+        self.status = status
+
+
+def _check(st):
+    if st != CB_OK:
+        raise CBError(st, RAW["cb_last_error"]().decode())
+    return st
+
+
+def _ptr(t):
+    """Raw address of a tensor / int / None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return CB_F32
+    if t.dtype == torch.bfloat16:
+        return CB_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+# ------------------------------------------------------------------ basics
+def cb_abi_version():
+    return RAW["cb_abi_version"]()
+
+
+def cb_last_error():
+    return RAW["cb_last_error"]().decode()
+
+
+def cb_schedule(n_chunk_tokens, recompute_bp, kind, n_layers):
+    out = (_c_i32 * (n_layers + 1))()
+    _check(RAW["cb_schedule"](n_chunk_tokens, recompute_bp, kind, n_layers, out))
+    return list(out)
+
+
+# ------------------------------------------------------------------ model
+class Model:
+    """cb_model over torch weight tensors (kept referenced for its lifetime).
+
+    layers: list of dicts with attn_norm, wq, wk, wv, wo, mlp_norm, w_gate,
+    w_up, w_down as contiguous device tensors of one dtype.
+    """
+
+    def __init__(self, n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim,
+                 layers, rope_base=10000.0, rms_eps=1e-5, dtype=None):
+        if dtype is None:
+            dtype = _dtype_code(layers[0]["wq"])
+        self.cfg = cb_model_cfg(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim,
+                                rope_base, rms_eps, dtype)
+        self._keep = layers
+        arr = (cb_layer_weights * n_layers)()
+        for i, w in enumerate(layers):
+            for f, _ in cb_layer_weights._fields_:
+                t = w[f]
+                if not t.is_contiguous():
+                    raise ValueError(f"layer {i} {f} is not contiguous")
+                setattr(arr[i], f, t.data_ptr())
+        h = _c_p()
+        _check(RAW["cb_model_create"](ctypes.byref(self.cfg), arr, ctypes.byref(h)))
+        self.handle = h
+
+    def close(self):
+        if getattr(self, "handle", None):
+            RAW["cb_model_destroy"](self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _request(chunks, offsets, n_suffix, x0, schedule, recompute_bp, schedule_kind, dev_mode,
+             min_tokens):
+    """chunks: list of dicts {k, v, n_tokens, on_host, layer_stride} with tensors or ints."""
+    arr = (cb_chunk_kv * max(1, len(chunks)))()
+    for i, c in enumerate(chunks):
+        arr[i].k = _ptr(c["k"])
+        arr[i].v = _ptr(c["v"])
+        arr[i].n_tokens = c["n_tokens"]
+        arr[i].on_host = int(c.get("on_host", 0))
+        arr[i].layer_stride = c["layer_stride"]
+    offs = (_c_i32 * max(1, len(offsets)))(*offsets)
+    sched = None
+    if schedule is not None:
+        sched = (_c_i32 * len(schedule))(*schedule)
+    req = cb_request(len(chunks), arr, offs, n_suffix, _ptr(x0),
+                     sched if sched is not None else ctypes.POINTER(_c_i32)(),
+                     recompute_bp, schedule_kind, dev_mode, min_tokens)
+    return req, (arr, offs, sched)
+
+
+def _outputs(fused_k, fused_v, sel_idx, sel_count, hidden_out, deviation):
+    return cb_outputs(_ptr(fused_k), _ptr(fused_v), _ptr(sel_idx),
+                      sel_count if sel_count is not None else ctypes.POINTER(_c_i32)(),
+                      _ptr(hidden_out), _ptr(deviation))
+
+
+def cb_blend(model, chunks, offsets, n_suffix, x0, fused_k, fused_v, sel_idx=None,
+             hidden_out=None, deviation=None, schedule=None, recompute_bp=1500,
+             schedule_kind=CB_SCHED_GRADUAL, dev_mode=CB_DEV_KV, min_tokens=0, stream=None):
+    """Queues one fusion; returns the host list sel_count[l] = s[l+1]."""
+    req, keep = _request(chunks, offsets, n_suffix, x0, schedule, recompute_bp, schedule_kind,
+                         dev_mode, min_tokens)
+    L = model.cfg.n_layers
+    cnt = (_c_i32 * L)()
+    out = _outputs(fused_k, fused_v, sel_idx, cnt, hidden_out, deviation)
+    _check(RAW["cb_blend"](model.handle, ctypes.byref(req), ctypes.byref(out), _stream(stream)))
+    del keep
+    return list(cnt)
+
+
+class Plan:
+    """Layer-stepped fusion: cb_plan_create / cb_fetch_kv / cb_prefill_layer /
+    cb_synchronize / cb_plan_destroy."""
+
+    def __init__(self, model, chunks, offsets, n_suffix, x0, fused_k, fused_v, sel_idx=None,
+                 hidden_out=None, deviation=None, schedule=None, recompute_bp=1500,
+                 schedule_kind=CB_SCHED_GRADUAL, dev_mode=CB_DEV_KV, min_tokens=0,
+                 stream=None):
+        req, self._keep = _request(chunks, offsets, n_suffix, x0, schedule, recompute_bp,
+                                   schedule_kind, dev_mode, min_tokens)
+        self._cnt = (_c_i32 * model.cfg.n_layers)()
+        out = _outputs(fused_k, fused_v, sel_idx, self._cnt, hidden_out, deviation)
+        h = _c_p()
+        _check(RAW["cb_plan_create"](model.handle, ctypes.byref(req), ctypes.byref(out),
+                                     _stream(stream), ctypes.byref(h)))
+        self.handle = h
+        self.sel_count = list(self._cnt)
+
+    def fetch_kv(self, layer):
+        _check(RAW["cb_fetch_kv"](self.handle, layer))
+
+    def prefill_layer(self, layer):
+        _check(RAW["cb_prefill_layer"](self.handle, layer))
+
+    def synchronize(self):
+        _check(RAW["cb_synchronize"](self.handle))
+
+    def destroy(self):
+        if self.handle:
+            RAW["cb_plan_destroy"](self.handle)
+            self.handle = None
+
+
+def cb_prefill(model, x0, n_tokens, pos0, k_out, v_out, hidden_out=None, stream=None):
+    _check(RAW["cb_prefill"](model.handle, _ptr(x0), n_tokens, pos0, _ptr(k_out), _ptr(v_out),
+                             _ptr(hidden_out), _stream(stream)))
+
+
+# ------------------------------------------------------------------ kernel level
+def cb_rope_rerotate(k_in, k_out, v_in, v_out, n_tokens, n_heads, head_dim, delta,
+                     rope_base=10000.0, stream=None):
+    _check(RAW["cb_rope_rerotate"](_dtype_code(k_in), _ptr(k_in), _ptr(k_out), _ptr(v_in),
+                                   _ptr(v_out), n_tokens, n_heads, head_dim, delta, rope_base,
+                                   _stream(stream)))
+
+
+def cb_deviation(k_new, v_new, k_cached, v_cached, n_rows, row_elems, dev_mode, dev_out,
+                 stream=None):
+    _check(RAW["cb_deviation"](_dtype_code(k_new), _ptr(k_new), _ptr(v_new), _ptr(k_cached),
+                               _ptr(v_cached), n_rows, row_elems, dev_mode, _ptr(dev_out),
+                               _stream(stream)))
+
+
+def cb_topk_select(dev, n, k, idx_out, stream=None):
+    _check(RAW["cb_topk_select"](_ptr(dev), n, k, _ptr(idx_out), _stream(stream)))
+
+
+def cb_gather_rows(src, dst, idx, n_rows, row_bytes, stream=None):
+    _check(RAW["cb_gather_rows"](_ptr(src), _ptr(dst), _ptr(idx), n_rows, row_bytes,
+                                 _stream(stream)))
+
+
+def cb_scatter_rows(src, dst, idx, n_rows, row_bytes, stream=None):
+    _check(RAW["cb_scatter_rows"](_ptr(src), _ptr(dst), _ptr(idx), n_rows, row_bytes,
+                                  _stream(stream)))
+
+
+def cb_rmsnorm(x, g, y, rows, d, eps=1e-5, stream=None):
+    _check(RAW["cb_rmsnorm"](_dtype_code(x), _ptr(x), _dtype_code(y), _ptr(g), _ptr(y), rows, d,
+                             eps, _stream(stream)))
+
+
+def cb_gemm(a, b, c, m, n, k, stream=None):
+    _check(RAW["cb_gemm"](_dtype_code(a), _ptr(a), _ptr(b), _ptr(c), m, n, k, _stream(stream)))
+
+
+def cb_attention(q, q_pos, n_q, k, v, n_kv, n_q_heads, n_kv_heads, head_dim, out, stream=None):
+    _check(RAW["cb_attention"](_dtype_code(q), _ptr(q), _ptr(q_pos), n_q, _ptr(k), _ptr(v), n_kv,
+                               n_q_heads, n_kv_heads, head_dim, _ptr(out), _stream(stream)))

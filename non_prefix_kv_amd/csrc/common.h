@@ -1,0 +1,71 @@
+// Internal helpers shared by the gfx950 kernels and the runtime.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace cb {
+
+using bf16 = __bf16;
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+enum DType : int { F32 = 0, BF16 = 1 };
+
+__host__ __device__ inline int elem_size(int dtype) { return dtype == BF16 ? 2 : 4; }
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+// gfx950 converts with round-to-nearest-even in hardware.
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float x) { return static_cast<bf16>(x); }
+
+// A fragment: 8 consecutive reduction-dim elements held by one lane.
+template <typename T> struct Frag;
+template <> struct Frag<bf16> { bf16x8 v; };
+template <> struct Frag<float> { floatx8 v; };
+
+// 16x16 output tile += A(16 x 32) * B(32 x 16).  Lane l supplies row (l % 16)
+// of A and column (l % 16) of B with the 8 reduction elements of lane group
+// l / 16; the accumulator holds C[4 * (l / 16) + i][l % 16], i = 0..3.
+// bf16: one v_mfma_f32_16x16x32_bf16.  f32: eight v_mfma_f32_16x16x4_f32,
+// the j-th taking element j of every lane (a fixed permutation of the
+// reduction index, identical on both operands).
+__device__ __forceinline__ void mfma16(floatx4& acc, const Frag<bf16>& a, const Frag<bf16>& b) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, b.v, acc, 0, 0, 0);
+}
+__device__ __forceinline__ void mfma16(floatx4& acc, const Frag<float>& a, const Frag<float>& b) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[j], b.v[j], acc, 0, 0, 0);
+}
+
+template <typename T>
+__device__ __forceinline__ Frag<T> load_frag(const T* p);   // 8 contiguous elements
+template <> __device__ __forceinline__ Frag<bf16> load_frag<bf16>(const bf16* p) {
+    Frag<bf16> f;
+    f.v = *reinterpret_cast<const bf16x8*>(p);
+    return f;
+}
+template <> __device__ __forceinline__ Frag<float> load_frag<float>(const float* p) {
+    Frag<float> f;
+    floatx4 a = *reinterpret_cast<const floatx4*>(p);
+    floatx4 b = *reinterpret_cast<const floatx4*>(p + 4);
+    f.v = floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return f;
+}
+
+__device__ __forceinline__ float warp_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+}  // namespace cb

@@ -1,0 +1,239 @@
+// Bandwidth-bound kernels: RoPE re-alignment of cached keys, row gather /
+// scatter, K/V merge into the fused cache, RMSNorm.
+//
+// RoPE re-alignment follows the Prompt Cache explainer (0h-n0.github.io),
+// section "RoPEにおける位置調整": a key encoded at chunk-local position p'
+// is moved to its real position p = p' + delta by the pair rotation
+// R(delta * theta_i); the CacheBlend explainer's RoPE section fixes R and
+// theta_i.  Values are not rotated.
+#include "kernels.h"
+
+namespace cb {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+template <typename T> struct Vec8;
+template <> struct Vec8<bf16> {
+    static __device__ __forceinline__ void load(const bf16* p, float* x) {
+        bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = static_cast<float>(v[i]);
+    }
+    static __device__ __forceinline__ void store(bf16* p, const float* x) {
+        bf16x8 v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = static_cast<bf16>(x[i]);
+        *reinterpret_cast<bf16x8*>(p) = v;
+    }
+    static __device__ __forceinline__ void copy(const bf16* s, bf16* d) {
+        *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(s);
+    }
+};
+template <> struct Vec8<float> {
+    static __device__ __forceinline__ void load(const float* p, float* x) {
+        floatx4 a = *reinterpret_cast<const floatx4*>(p);
+        floatx4 b = *reinterpret_cast<const floatx4*>(p + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+    }
+    static __device__ __forceinline__ void store(float* p, const float* x) {
+        *reinterpret_cast<floatx4*>(p) = floatx4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<floatx4*>(p + 4) = floatx4{x[4], x[5], x[6], x[7]};
+    }
+    static __device__ __forceinline__ void copy(const float* s, float* d) {
+        *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(s);
+        *reinterpret_cast<u32x4*>(d + 4) = *reinterpret_cast<const u32x4*>(s + 4);
+    }
+};
+
+// One thread moves 8 consecutive elements of one K row (4 rotation pairs)
+// and the matching 8 elements of the V row.  Consecutive threads cover
+// consecutive 16/32-byte pieces of a row, so every wave reads and writes
+// whole contiguous segments.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void rerotate_kernel(
+    const RotJobs jobs, int layer, T* __restrict__ kd, T* __restrict__ vd,
+    int row_elems, int head_dim, const float2* __restrict__ tab, int half) {
+    const RotJob& j = jobs.j[blockIdx.y];
+    const int vecs = row_elems >> 3;
+    const int64_t u = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (u >= (int64_t)j.n_tokens * vecs) return;
+    const int t = (int)(u / vecs);
+    const int c = (int)(u - (int64_t)t * vecs) * 8;
+    const int64_t d_off = (int64_t)(j.dst_row + t) * row_elems + c;
+    const int64_t s_off = (int64_t)layer * j.src_layer_stride + (int64_t)t * row_elems + c;
+    const T* ks = j.k_src ? static_cast<const T*>(j.k_src) + s_off : kd + d_off;
+
+    float x[8];
+    Vec8<T>::load(ks, x);
+    const int ad = j.delta < 0 ? -j.delta : j.delta;
+    const float sg = j.delta < 0 ? -1.f : 1.f;
+    const float2* tr = tab + (int64_t)ad * half + ((c % head_dim) >> 1);
+    float y[8];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const float2 cs = tr[p];
+        const float sn = sg * cs.y;
+        y[2 * p] = x[2 * p] * cs.x - x[2 * p + 1] * sn;
+        y[2 * p + 1] = x[2 * p] * sn + x[2 * p + 1] * cs.x;
+    }
+    Vec8<T>::store(kd + d_off, y);
+    if (j.v_src) Vec8<T>::copy(static_cast<const T*>(j.v_src) + s_off, vd + d_off);
+}
+
+__global__ __launch_bounds__(kThreads) void move_rows_kernel(
+    const char* __restrict__ src, char* __restrict__ dst, const int* __restrict__ idx,
+    int64_t row_bytes, int scatter) {
+    const int r = blockIdx.x;
+    const int64_t srow = scatter ? r : idx[r];
+    const int64_t drow = scatter ? idx[r] : r;
+    const char* s = src + srow * row_bytes;
+    char* d = dst + drow * row_bytes;
+    if ((row_bytes & 15) == 0) {
+        for (int64_t o = (int64_t)threadIdx.x * 16; o < row_bytes; o += kThreads * 16)
+            *reinterpret_cast<u32x4*>(d + o) = *reinterpret_cast<const u32x4*>(s + o);
+    } else {
+        for (int64_t o = (int64_t)threadIdx.x * 4; o < row_bytes; o += kThreads * 4)
+            *reinterpret_cast<uint32_t*>(d + o) = *reinterpret_cast<const uint32_t*>(s + o);
+    }
+}
+
+template <typename T>
+__global__ __launch_bounds__(kThreads) void scatter_kv_kernel(
+    const T* __restrict__ kn, const T* __restrict__ vn, const int* __restrict__ sidx,
+    const int* __restrict__ pos, int row_base, T* __restrict__ fk, T* __restrict__ fv,
+    int kv_dim) {
+    const int r = blockIdx.x;
+    const int s = sidx ? sidx[r] : r;
+    const int64_t d = (int64_t)((pos ? pos[s] : s) - row_base) * kv_dim;
+    const int64_t so = (int64_t)s * kv_dim;
+    for (int c = threadIdx.x * 8; c < kv_dim; c += kThreads * 8) {
+        Vec8<T>::copy(kn + so + c, fk + d + c);
+        Vec8<T>::copy(vn + so + c, fv + d + c);
+    }
+}
+
+__device__ __forceinline__ float block_sum(float v, float* red) {
+    v = warp_sum(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[w] = v;
+    __syncthreads();
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < kThreads / 64; ++i) t += red[i];
+    return t;
+}
+
+template <typename TX, typename TY>
+__global__ __launch_bounds__(kThreads) void rmsnorm_kernel(
+    const TX* __restrict__ x, const int* __restrict__ idx, const TY* __restrict__ g,
+    TY* __restrict__ y, float* __restrict__ xc, int d, float eps) {
+    __shared__ float red[kThreads / 64];
+    const int r = blockIdx.x;
+    const TX* xr = x + (int64_t)(idx ? idx[r] : r) * d;
+    float ss = 0.f;
+    for (int c = threadIdx.x; c < d; c += kThreads) {
+        const float v = to_f32(xr[c]);
+        ss += v * v;
+    }
+    ss = block_sum(ss, red);
+    const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+    TY* yr = y + (int64_t)r * d;
+    float* xcr = xc ? xc + (int64_t)r * d : nullptr;
+    for (int c = threadIdx.x; c < d; c += kThreads) {
+        const float v = to_f32(xr[c]);
+        yr[c] = from_f32<TY>(v * inv * to_f32(g[c]));
+        if (xcr) xcr[c] = v;
+    }
+}
+
+__global__ void iota_kernel(int* p, int n, int base) {
+    const int i = blockIdx.x * kThreads + threadIdx.x;
+    if (i < n) p[i] = base + i;
+}
+
+}  // namespace
+
+hipError_t launch_rerotate(int dtype, const RotJobs& jobs, int layer, void* k_dst, void* v_dst,
+                           int n_heads, int head_dim, const RopeTab& rope, hipStream_t s) {
+    if (jobs.n <= 0 || jobs.max_tokens <= 0) return hipSuccess;
+    if (jobs.n > kMaxRotJobs) return hipErrorInvalidValue;
+    const int row = n_heads * head_dim;
+    if (head_dim % 8 != 0 || rope.half != head_dim / 2) return hipErrorInvalidValue;
+    for (int i = 0; i < jobs.n; ++i) {
+        const int ad = jobs.j[i].delta < 0 ? -jobs.j[i].delta : jobs.j[i].delta;
+        if (ad >= rope.n_pos || jobs.j[i].n_tokens > jobs.max_tokens) return hipErrorInvalidValue;
+    }
+    const int64_t units = (int64_t)jobs.max_tokens * (row / 8);
+    dim3 grid((unsigned)((units + kThreads - 1) / kThreads), (unsigned)jobs.n);
+    if (dtype == BF16)
+        hipLaunchKernelGGL(rerotate_kernel<bf16>, grid, dim3(kThreads), 0, s, jobs, layer,
+                           (bf16*)k_dst, (bf16*)v_dst, row, head_dim, rope.tab, rope.half);
+    else
+        hipLaunchKernelGGL(rerotate_kernel<float>, grid, dim3(kThreads), 0, s, jobs, layer,
+                           (float*)k_dst, (float*)v_dst, row, head_dim, rope.tab, rope.half);
+    return hipGetLastError();
+}
+
+hipError_t launch_iota(int* p, int n, int base, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(iota_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0, s, p, n,
+                       base);
+    return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const void* src, void* dst, const int* idx, int n_rows,
+                              int64_t row_bytes, hipStream_t s) {
+    if (n_rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(move_rows_kernel, dim3(n_rows), dim3(kThreads), 0, s, (const char*)src,
+                       (char*)dst, idx, row_bytes, 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter_rows(const void* src, void* dst, const int* idx, int n_rows,
+                               int64_t row_bytes, hipStream_t s) {
+    if (n_rows <= 0) return hipSuccess;
+    hipLaunchKernelGGL(move_rows_kernel, dim3(n_rows), dim3(kThreads), 0, s, (const char*)src,
+                       (char*)dst, idx, row_bytes, 1);
+    return hipGetLastError();
+}
+
+hipError_t launch_scatter_kv(int dtype, const void* k_new, const void* v_new,
+                             const int* src_idx, const int* pos, int row_base, void* fk,
+                             void* fv, int n_rows, int kv_dim, hipStream_t s) {
+    if (n_rows <= 0) return hipSuccess;
+    if (kv_dim % 8 != 0) return hipErrorInvalidValue;
+    if (dtype == BF16)
+        hipLaunchKernelGGL(scatter_kv_kernel<bf16>, dim3(n_rows), dim3(kThreads), 0, s,
+                           (const bf16*)k_new, (const bf16*)v_new, src_idx, pos, row_base,
+                           (bf16*)fk, (bf16*)fv, kv_dim);
+    else
+        hipLaunchKernelGGL(scatter_kv_kernel<float>, dim3(n_rows), dim3(kThreads), 0, s,
+                           (const float*)k_new, (const float*)v_new, src_idx, pos, row_base,
+                           (float*)fk, (float*)fv, kv_dim);
+    return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(int x_dtype, const void* x, const int* idx, int y_dtype,
+                          const void* g, void* y, float* x_copy, int rows, int d, float eps,
+                          hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    dim3 grid(rows), block(kThreads);
+    if (x_dtype == F32 && y_dtype == F32)
+        hipLaunchKernelGGL((rmsnorm_kernel<float, float>), grid, block, 0, s, (const float*)x,
+                           idx, (const float*)g, (float*)y, x_copy, d, eps);
+    else if (x_dtype == F32 && y_dtype == BF16)
+        hipLaunchKernelGGL((rmsnorm_kernel<float, bf16>), grid, block, 0, s, (const float*)x,
+                           idx, (const bf16*)g, (bf16*)y, x_copy, d, eps);
+    else if (x_dtype == BF16 && y_dtype == BF16)
+        hipLaunchKernelGGL((rmsnorm_kernel<bf16, bf16>), grid, block, 0, s, (const bf16*)x,
+                           idx, (const bf16*)g, (bf16*)y, x_copy, d, eps);
+    else
+        hipLaunchKernelGGL((rmsnorm_kernel<bf16, float>), grid, block, 0, s, (const bf16*)x,
+                           idx, (const float*)g, (float*)y, x_copy, d, eps);
+    return hipGetLastError();
+}
+
+}  // namespace cb

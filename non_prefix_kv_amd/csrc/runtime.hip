@@ -1,0 +1,738 @@
+// libcacheblend runtime: argument validation, RoPE tables, workspace,
+// streams/events and the per-layer schedule of the fusion path, exported
+// through the C ABI declared in include/cacheblend.h.
+//
+// Per layer l (CacheBlend explainer (0h-n0), section "選択的再計算", Steps
+// 1-4, with the token set narrowed as in section "HKVDトークン選定"):
+//   side stream : [pinned host -> HBM copy of chunk K/V of layer l]
+//                 rotate chunk K by its offset into fused_k[l], V into fused_v[l]
+//   main stream : wait for the fetch of layer l, then
+//     1 RMSNorm of the rows R (kept chunk rows of the previous layer + suffix)
+//     2 QKV projection, RoPE at real positions                   (matrix cores)
+//     3 deviation of the recomputed chunk rows vs the rotated cache
+//     4 keep the top s[l+1] rows (exact radix select), + suffix rows
+//     5 merge their K/V into fused[l]
+//     6 attention of the kept rows over fused[l][0..N)           (matrix cores)
+//     7 O projection + residual, 8 RMSNorm, 9 gate/up + SiLU*up, 10 down + residual
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/cacheblend.h"
+#include "kernels.h"
+
+using namespace cb;
+
+// ---------------------------------------------------------------- errors
+namespace {
+
+thread_local std::string g_err;
+
+cb_status fail(cb_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return st;
+}
+
+#define CB_HIP(call)                                                                   \
+    do {                                                                               \
+        hipError_t e_ = (call);                                                        \
+        if (e_ != hipSuccess)                                                          \
+            return fail(CB_E_HIP, "%s failed: %s", #call, hipGetErrorString(e_));       \
+    } while (0)
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// ---------------------------------------------------------------- RoPE tables
+// (cos, sin)(pos * theta_i), theta_i = base^(-2i/d_head): angles in float64,
+// rounded once to float32.  Tables only grow; superseded tables stay
+// allocated so work already queued keeps valid pointers.
+struct RopeCache {
+    std::mutex mu;
+    std::map<std::tuple<int, double, int>, RopeTab> cur;
+    std::vector<void*> keep;
+};
+RopeCache& rope_cache() {
+    static RopeCache c;
+    return c;
+}
+
+cb_status get_rope(double base, int head_dim, int n_pos, RopeTab* out) {
+    int dev = 0;
+    CB_HIP(hipGetDevice(&dev));
+    RopeCache& c = rope_cache();
+    std::lock_guard<std::mutex> lk(c.mu);
+    auto key = std::make_tuple(dev, base, head_dim);
+    auto it = c.cur.find(key);
+    if (it != c.cur.end() && it->second.n_pos >= n_pos) {
+        *out = it->second;
+        return CB_OK;
+    }
+    int want = std::max(n_pos, 16384);
+    if (it != c.cur.end()) want = std::max(want, 2 * it->second.n_pos);
+    const int half = head_dim / 2;
+    std::vector<float2> host((size_t)want * half);
+    for (int p = 0; p < want; ++p)
+        for (int i = 0; i < half; ++i) {
+            const double theta = std::pow(base, -2.0 * i / head_dim);
+            const double ang = (double)p * theta;
+            host[(size_t)p * half + i] = make_float2((float)std::cos(ang), (float)std::sin(ang));
+        }
+    void* d = nullptr;
+    if (hipMalloc(&d, host.size() * sizeof(float2)) != hipSuccess)
+        return fail(CB_E_OOM, "RoPE table allocation (%zu bytes) failed",
+                    host.size() * sizeof(float2));
+    CB_HIP(hipMemcpy(d, host.data(), host.size() * sizeof(float2), hipMemcpyHostToDevice));
+    c.keep.push_back(d);
+    RopeTab t;
+    t.tab = static_cast<const float2*>(d);
+    t.n_pos = want;
+    t.half = half;
+    c.cur[key] = t;
+    *out = t;
+    return CB_OK;
+}
+
+// ---------------------------------------------------------------- schedule
+cb_status make_schedule(int n, int r_bp, int kind, int L, int* s) {
+    if (L <= 0 || n < 0) return fail(CB_E_INVALID, "schedule: n_layers %d, chunk tokens %d", L, n);
+    if (r_bp < 0 || r_bp > 10000) return fail(CB_E_SCHEDULE, "recompute_bp %d not in 0..10000", r_bp);
+    if (kind != CB_SCHED_GRADUAL && kind != CB_SCHED_FIXED)
+        return fail(CB_E_INVALID, "unknown schedule kind %d", kind);
+    if (r_bp == 0 || n == 0) {
+        for (int l = 0; l <= L; ++l) s[l] = 0;
+        return CB_OK;
+    }
+    s[0] = n;
+    s[1] = n;
+    const int64_t nn = n;
+    if (kind == CB_SCHED_FIXED) {
+        const int k = (int)std::max<int64_t>(1, nn * r_bp / 10000);
+        for (int l = 2; l <= L; ++l) s[l] = k;
+    } else {
+        const int64_t r1 = std::min<int64_t>(10000, (12 * (int64_t)r_bp) / 10);
+        for (int l = 1; l < L; ++l) {
+            const int e = std::min(l - 1, 30);
+            const int64_t p2 = (int64_t)1 << e;
+            // n * (r 2^e + r1 - r) / (10000 2^e) in exact integer arithmetic
+            const __int128 num = (__int128)nn * ((int64_t)r_bp * p2 + r1 - r_bp);
+            const __int128 den = (__int128)10000 * p2;
+            int64_t k = (int64_t)(num / den);
+            if (k < 1) k = 1;
+            s[l + 1] = (int)std::min<int64_t>(k, s[l]);
+        }
+    }
+    return CB_OK;
+}
+
+bool aligned_to(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+enum class MemKind { Device, Pinned, Other };
+MemKind mem_kind(const void* p) {
+    hipPointerAttribute_t at;
+    memset(&at, 0, sizeof at);
+    if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+        (void)hipGetLastError();
+        return MemKind::Other;
+    }
+    if (at.type == hipMemoryTypeDevice || at.type == hipMemoryTypeManaged) return MemKind::Device;
+    if (at.type == hipMemoryTypeHost) return MemKind::Pinned;
+    return MemKind::Other;
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+// ---------------------------------------------------------------- model
+struct cb_model {
+    cb_model_cfg cfg;
+    std::vector<cb_layer_weights> w;
+    RopeTab rope;
+    int device = 0;
+    hipStream_t side = nullptr;   // fetch (H2D + rotation) stream, default priority
+    std::mutex mu;
+    std::vector<hipEvent_t> event_pool;
+    int es() const { return elem_size(cfg.dtype); }
+    int qd() const { return cfg.n_q_heads * cfg.head_dim; }
+    int kvd() const { return cfg.n_kv_heads * cfg.head_dim; }
+};
+
+// ---------------------------------------------------------------- plan
+struct cb_plan {
+    cb_model* m = nullptr;
+    hipStream_t stream = nullptr;
+    int L = 0, N = 0, Nc = 0, Ns = 0, row_base = 0;
+    bool prefill_mode = false;
+    std::vector<int> s;
+    std::vector<cb_chunk_kv> chunks;
+    std::vector<int> offsets;
+    const void* x0 = nullptr;
+    int dev_mode = CB_DEV_KV;
+    cb_outputs out{};
+    // workspace
+    void* ws = nullptr;
+    float *X = nullptr, *Hres = nullptr, *dev = nullptr;
+    void *Hn = nullptr, *Q = nullptr, *Kn = nullptr, *Vn = nullptr, *attn = nullptr,
+         *act = nullptr;
+    int *pos_a = nullptr, *pos_b = nullptr, *sel_local = nullptr;
+    std::vector<RotJobs> jobs;   // rotation jobs, 16 chunks per launch
+
+    // streams / events
+    hipEvent_t ready = nullptr;                 // workspace + prior main work
+    std::vector<hipEvent_t> fetched, layer_start;
+    std::vector<char> fetch_done;
+    int next_layer = 0;
+};
+
+namespace {
+
+cb_status validate_cfg(const cb_model_cfg* c) {
+    if (!c) return fail(CB_E_INVALID, "cfg is NULL");
+    if (c->dtype != CB_F32 && c->dtype != CB_BF16) return fail(CB_E_INVALID, "dtype %d", c->dtype);
+    if (c->n_layers <= 0 || c->d_model <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 ||
+        c->ffn_dim <= 0)
+        return fail(CB_E_INVALID, "model sizes must be positive");
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return fail(CB_E_UNSUPPORTED, "head_dim %d (64 or 128 supported)", c->head_dim);
+    if (c->n_q_heads % c->n_kv_heads) return fail(CB_E_SHAPE, "n_kv_heads must divide n_q_heads");
+    const int kmul = c->dtype == CB_BF16 ? 64 : 32;
+    if (c->d_model % kmul || c->ffn_dim % kmul || (c->n_q_heads * c->head_dim) % kmul)
+        return fail(CB_E_SHAPE, "d_model, ffn_dim and Hq*head_dim must be multiples of %d", kmul);
+    if (!(c->rope_base > 1.0) || !(c->rms_eps >= 0.f))
+        return fail(CB_E_INVALID, "rope_base must be > 1 and rms_eps >= 0");
+    return CB_OK;
+}
+
+// Carves the workspace for up to `max_rows` recomputed rows.
+size_t carve(cb_plan* p, char* base, int max_rows) {
+    const cb_model_cfg& c = p->m->cfg;
+    const size_t es = p->m->es(), R = (size_t)std::max(1, max_rows);
+    size_t off = 0;
+    auto take = [&](size_t bytes) -> char* {
+        char* r = base ? base + off : nullptr;
+        off = align_up(off + bytes, 256);
+        return r;
+    };
+    p->X = (float*)take(R * c.d_model * 4);
+    p->Hres = (float*)take(R * c.d_model * 4);
+    p->Hn = take(R * c.d_model * es);
+    p->Q = take(R * p->m->qd() * es);
+    p->Kn = take(R * p->m->kvd() * es);
+    p->Vn = take(R * p->m->kvd() * es);
+    p->attn = take(R * p->m->qd() * es);
+    p->act = take(R * c.ffn_dim * es);
+    p->dev = (float*)take(std::max<size_t>(1, p->Nc) * 4);
+    p->pos_a = (int*)take(R * 4);
+    p->pos_b = (int*)take(R * 4);
+    p->sel_local = (int*)take(R * 4);
+    return off;
+}
+
+cb_status plan_alloc(cb_plan* p) {
+    const int max_rows = p->s[0] + p->Ns;
+    const size_t bytes = carve(p, nullptr, max_rows);
+    if (hipMallocAsync(&p->ws, bytes, p->stream) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(CB_E_OOM, "workspace of %zu bytes", bytes);
+    }
+    carve(p, (char*)p->ws, max_rows);
+    return CB_OK;
+}
+
+// Events come from a per-model pool: re-recording an event that a stream
+// already waited on is safe (the wait captured the earlier recording).
+cb_status plan_events(cb_plan* p) {
+    std::lock_guard<std::mutex> lk(p->m->mu);
+    auto get = [&](hipEvent_t* e) -> hipError_t {
+        if (!p->m->event_pool.empty()) {
+            *e = p->m->event_pool.back();
+            p->m->event_pool.pop_back();
+            return hipSuccess;
+        }
+        return hipEventCreateWithFlags(e, hipEventDisableTiming);
+    };
+    CB_HIP(get(&p->ready));
+    p->fetched.assign(p->L, nullptr);
+    p->layer_start.assign(p->L, nullptr);
+    p->fetch_done.assign(p->L, 0);
+    for (int l = 0; l < p->L; ++l) {
+        CB_HIP(get(&p->fetched[l]));
+        CB_HIP(get(&p->layer_start[l]));
+    }
+    return CB_OK;
+}
+
+// Initial row positions: R_0 = (all chunk rows if s[0] = N_c) + suffix.
+cb_status plan_start(cb_plan* p) {
+    const int base = p->s[0] == p->Nc ? 0 : p->Nc;
+    CB_HIP(launch_iota(p->pos_a, p->N - base, p->row_base + base, p->stream));
+    CB_HIP(hipEventRecord(p->ready, p->stream));
+    CB_HIP(hipStreamWaitEvent(p->m->side, p->ready, 0));
+    return CB_OK;
+}
+
+void plan_free(cb_plan* p) {
+    if (!p) return;
+    if (p->ws) {
+        // the side stream may still be rotating: main waits for its last event
+        for (int l = 0; l < p->L; ++l)
+            if (p->fetch_done[l]) (void)hipStreamWaitEvent(p->stream, p->fetched[l], 0);
+        (void)hipFreeAsync(p->ws, p->stream);
+    }
+    {
+        std::lock_guard<std::mutex> lk(p->m->mu);
+        if (p->ready) p->m->event_pool.push_back(p->ready);
+        for (auto e : p->fetched) if (e) p->m->event_pool.push_back(e);
+        for (auto e : p->layer_start) if (e) p->m->event_pool.push_back(e);
+    }
+    delete p;
+}
+
+int64_t layer_elems(const cb_plan* p) { return (int64_t)p->N * p->m->kvd(); }
+
+cb_status do_fetch(cb_plan* p, int l) {
+    if (p->fetch_done[l]) return CB_OK;
+    cb_model* m = p->m;
+    const hipStream_t side = m->side;
+    // keep the side stream at most two layers ahead of the main stream
+    if (l >= 2 && p->layer_start[l - 2] && l - 2 < p->next_layer)
+        CB_HIP(hipStreamWaitEvent(side, p->layer_start[l - 2], 0));
+    const size_t es = m->es();
+    char* fk = (char*)p->out.fused_k + (size_t)l * layer_elems(p) * es;
+    char* fv = (char*)p->out.fused_v + (size_t)l * layer_elems(p) * es;
+    for (size_t c = 0; c < p->chunks.size(); ++c) {
+        const cb_chunk_kv& ck = p->chunks[c];
+        if (!ck.on_host) continue;
+        const size_t bytes = (size_t)ck.n_tokens * m->kvd() * es;
+        const size_t src = (size_t)l * ck.layer_stride * es;
+        const size_t dst = (size_t)p->offsets[c] * m->kvd() * es;
+        CB_HIP(hipMemcpyAsync(fk + dst, (const char*)ck.k + src, bytes, hipMemcpyHostToDevice, side));
+        CB_HIP(hipMemcpyAsync(fv + dst, (const char*)ck.v + src, bytes, hipMemcpyHostToDevice, side));
+    }
+    for (const RotJobs& js : p->jobs)
+        CB_HIP(launch_rerotate(m->cfg.dtype, js, l, fk, fv, m->cfg.n_kv_heads, m->cfg.head_dim,
+                               m->rope, side));
+    CB_HIP(hipEventRecord(p->fetched[l], side));
+    p->fetch_done[l] = 1;
+    return CB_OK;
+}
+
+cb_status do_layer(cb_plan* p, int l) {
+    cb_model* m = p->m;
+    const cb_model_cfg& c = m->cfg;
+    const cb_layer_weights& w = m->w[l];
+    const hipStream_t st = p->stream;
+    const int dt = c.dtype, es = m->es();
+    const int nC = p->s[l], k = p->s[l + 1], mR = nC + p->Ns, mQ = k + p->Ns;
+    CB_HIP(hipEventRecord(p->layer_start[l], st));
+    CB_HIP(hipStreamWaitEvent(st, p->fetched[l], 0));
+    if (mR == 0) return CB_OK;
+    void* fk = (char*)p->out.fused_k + (size_t)l * layer_elems(p) * es;
+    void* fv = (char*)p->out.fused_v + (size_t)l * layer_elems(p) * es;
+    int* pos_r = p->pos_a;
+    int* pos_q = p->pos_b;
+
+    // 1. RMSNorm of the input rows (layer 0 gathers them from x0 by position)
+    if (l == 0) {
+        const bool all_rows = (nC == p->Nc) && p->row_base == 0;
+        CB_HIP(launch_rmsnorm(dt, p->x0, (all_rows || p->prefill_mode) ? nullptr : pos_r, dt,
+                              w.attn_norm, p->Hn, p->X, mR, c.d_model, c.rms_eps, st));
+    } else {
+        CB_HIP(launch_rmsnorm(F32, p->X, nullptr, dt, w.attn_norm, p->Hn, nullptr, mR, c.d_model,
+                              c.rms_eps, st));
+    }
+    // 2. QKV projection with RoPE at the real positions
+    GemmArgs g{};
+    g.a = p->Hn; g.b0 = w.wq; g.b1 = w.wk; g.b2 = w.wv;
+    g.n0 = m->qd(); g.n1 = m->kvd();
+    g.M = mR; g.N = m->qd() + 2 * m->kvd(); g.K = c.d_model;
+    g.out0 = p->Q; g.out1 = p->Kn; g.out2 = p->Vn;
+    g.pos = pos_r; g.rope = m->rope; g.head_dim = c.head_dim;
+    CB_HIP(launch_gemm(dt, EPI_QKV, g, st));
+    // 3. deviation of the recomputed chunk rows against the rotated cache
+    float* dev_out = p->out.deviation ? p->out.deviation + (size_t)l * p->Nc : nullptr;
+    if (nC > 0 && (k < nC || dev_out))
+        CB_HIP(launch_deviation(dt, p->Kn, p->Vn, fk, fv, pos_r, 0, nC, m->kvd(), p->dev_mode,
+                                p->dev, dev_out, st));
+    // 4. keep the top s[l+1] chunk rows, then the suffix rows
+    int* sel_pos = p->out.sel_idx ? p->out.sel_idx + (size_t)l * p->Nc : nullptr;
+    CB_HIP(launch_select(p->dev, nC, k, p->Ns, pos_r, p->sel_local, pos_q, sel_pos, st));
+    // 5. merge the kept rows' K/V into the fused cache
+    CB_HIP(launch_scatter_kv(dt, p->Kn, p->Vn, p->sel_local, pos_r, p->row_base, fk, fv, mQ,
+                             m->kvd(), st));
+    // 6. attention over the whole fused cache of this layer
+    AttnArgs a{};
+    a.q = p->Q; a.qidx = p->sel_local; a.q_pos = pos_q; a.n_q = mQ;
+    a.k = fk; a.v = fv; a.n_kv = p->N; a.kv_pos0 = p->row_base;
+    a.n_q_heads = c.n_q_heads; a.n_kv_heads = c.n_kv_heads; a.head_dim = c.head_dim;
+    a.out = p->attn;
+    CB_HIP(launch_attention(dt, a, st));
+    // 7. O projection + residual
+    GemmArgs go{};
+    go.a = p->attn; go.b0 = w.wo; go.M = mQ; go.N = c.d_model; go.K = m->qd();
+    go.out0 = p->Hres; go.resid = p->X; go.ridx = p->sel_local;
+    CB_HIP(launch_gemm(dt, EPI_RESID, go, st));
+    // 8. RMSNorm, 9. gate/up with SiLU(gate)*up
+    CB_HIP(launch_rmsnorm(F32, p->Hres, nullptr, dt, w.mlp_norm, p->Hn, nullptr, mQ, c.d_model,
+                          c.rms_eps, st));
+    GemmArgs gu{};
+    gu.a = p->Hn; gu.b0 = w.w_gate; gu.b1 = w.w_up; gu.M = mQ; gu.N = c.ffn_dim; gu.K = c.d_model;
+    gu.out0 = p->act;
+    CB_HIP(launch_gemm(dt, EPI_SWIGLU, gu, st));
+    // 10. down projection + residual -> next layer input (or the caller's output)
+    GemmArgs gd{};
+    gd.a = p->act; gd.b0 = w.w_down; gd.M = mQ; gd.N = c.d_model; gd.K = c.ffn_dim;
+    const bool last = l == p->L - 1;
+    gd.out0 = (last && p->out.hidden_out) ? p->out.hidden_out : p->X;
+    gd.resid = p->Hres; gd.ridx = nullptr;
+    CB_HIP(launch_gemm(dt, EPI_RESID, gd, st));
+    std::swap(p->pos_a, p->pos_b);
+    return CB_OK;
+}
+
+cb_status validate_request(cb_model* m, const cb_request* r, const cb_outputs* o, cb_plan* p) {
+    if (!r || !o) return fail(CB_E_INVALID, "request/outputs is NULL");
+    if (!o->fused_k || !o->fused_v) return fail(CB_E_INVALID, "fused_k/fused_v are required");
+    if (!r->x0) return fail(CB_E_INVALID, "x0 is NULL");
+    if (r->n_chunks < 0 || r->n_suffix < 0) return fail(CB_E_INVALID, "negative counts");
+    if (r->n_chunks > 0 && (!r->chunks || !r->chunk_offsets))
+        return fail(CB_E_INVALID, "chunks/chunk_offsets are NULL");
+    if (r->dev_mode < 0 || r->dev_mode > 2) return fail(CB_E_INVALID, "dev_mode %d", r->dev_mode);
+    const int L = m->cfg.n_layers;
+    const int64_t row_elems = m->kvd();
+    int64_t o_next = 0;
+    p->chunks.assign(r->chunks, r->chunks + r->n_chunks);
+    p->offsets.assign(r->chunk_offsets, r->chunk_offsets + r->n_chunks);
+    for (int c = 0; c < r->n_chunks; ++c) {
+        const cb_chunk_kv& ck = r->chunks[c];
+        if (!ck.k || !ck.v) return fail(CB_E_INVALID, "chunk %d has a NULL k/v", c);
+        if (ck.n_tokens <= 0) return fail(CB_E_INVALID, "chunk %d has %d tokens", c, ck.n_tokens);
+        if (r->chunk_offsets[c] != o_next)
+            return fail(CB_E_INVALID, "chunk %d offset %d: offsets must start at 0 and be contiguous",
+                        c, r->chunk_offsets[c]);
+        if (ck.layer_stride < (int64_t)ck.n_tokens * row_elems)
+            return fail(CB_E_SHAPE, "chunk %d layer_stride %lld < n_tokens*H_kv*d_head", c,
+                        (long long)ck.layer_stride);
+        const MemKind mk = mem_kind(ck.k), mv = mem_kind(ck.v);
+        if (ck.on_host) {
+            if (mk != MemKind::Pinned || mv != MemKind::Pinned)
+                return fail(CB_E_NOT_PINNED, "chunk %d: host K/V must be pinned (hipHostMalloc)", c);
+        } else if (mk != MemKind::Device || mv != MemKind::Device) {
+            return fail(CB_E_INVALID, "chunk %d: on_host = 0 but K/V are not device memory", c);
+        }
+        if (!aligned_to(ck.k, 16) || !aligned_to(ck.v, 16) || (ck.layer_stride * m->es()) % 16)
+            return fail(CB_E_SHAPE, "chunk %d: K/V and layer stride must be 16-byte aligned", c);
+        o_next += ck.n_tokens;
+    }
+    if (o_next + r->n_suffix > (1 << 30)) return fail(CB_E_SHAPE, "prompt too long");
+    p->Nc = (int)o_next;
+    p->Ns = r->n_suffix;
+    p->N = p->Nc + p->Ns;
+    if (p->N == 0) return fail(CB_E_INVALID, "empty prompt");
+    p->L = L;
+    p->s.assign(L + 1, 0);
+    if (r->schedule) {
+        p->s.assign(r->schedule, r->schedule + L + 1);
+    } else {
+        cb_status st = make_schedule(p->Nc, r->recompute_bp, r->schedule_kind, L, p->s.data());
+        if (st != CB_OK) return st;
+    }
+    if (r->min_tokens > 0 && p->N < r->min_tokens) p->s.assign(L + 1, p->Nc);
+    if (p->s[0] != 0 && p->s[0] != p->Nc)
+        return fail(CB_E_SCHEDULE, "s[0] = %d must be 0 or the chunk token count %d", p->s[0], p->Nc);
+    for (int l = 0; l < L; ++l)
+        if (p->s[l + 1] > p->s[l] || p->s[l + 1] < 0)
+            return fail(CB_E_SCHEDULE, "schedule must be non-increasing (s[%d]=%d, s[%d]=%d)", l,
+                        p->s[l], l + 1, p->s[l + 1]);
+    p->x0 = r->x0;
+    p->dev_mode = r->dev_mode;
+    p->out = *o;
+    for (size_t c = 0; c < p->chunks.size(); ++c) {
+        const cb_chunk_kv& ck = p->chunks[c];
+        if (c % kMaxRotJobs == 0) p->jobs.push_back(RotJobs{});
+        RotJobs& js = p->jobs.back();
+        RotJob& j = js.j[js.n++];
+        j.k_src = ck.on_host ? nullptr : ck.k;
+        j.v_src = ck.on_host ? nullptr : ck.v;
+        j.src_layer_stride = ck.layer_stride;
+        j.dst_row = p->offsets[c];
+        j.n_tokens = ck.n_tokens;
+        j.delta = p->offsets[c];       // chunk-local position 0 -> real position o_c
+        js.max_tokens = std::max(js.max_tokens, ck.n_tokens);
+    }
+    return CB_OK;
+}
+
+cb_status ensure_rope(cb_model* m, int n_pos) {
+    if (m->rope.n_pos >= n_pos) return CB_OK;
+    return get_rope(m->cfg.rope_base, m->cfg.head_dim, n_pos, &m->rope);
+}
+
+}  // namespace
+
+// ================================================================ C ABI
+extern "C" {
+
+int cb_abi_version(void) { return CB_ABI_VERSION; }
+
+const char* cb_last_error(void) { return g_err.c_str(); }
+
+cb_status cb_schedule(int32_t n_chunk_tokens, int32_t recompute_bp, int32_t kind,
+                      int32_t n_layers, int32_t* s_out) {
+    if (!s_out) return fail(CB_E_INVALID, "s_out is NULL");
+    return make_schedule(n_chunk_tokens, recompute_bp, kind, n_layers, s_out);
+}
+
+cb_status cb_model_create(const cb_model_cfg* cfg, const cb_layer_weights* layers,
+                          cb_model** out) {
+    if (!out) return fail(CB_E_INVALID, "out is NULL");
+    *out = nullptr;
+    cb_status st = validate_cfg(cfg);
+    if (st != CB_OK) return st;
+    if (!layers) return fail(CB_E_INVALID, "layers is NULL");
+    for (int l = 0; l < cfg->n_layers; ++l) {
+        const cb_layer_weights& w = layers[l];
+        const void* ps[] = {w.attn_norm, w.wq, w.wk, w.wv, w.wo, w.mlp_norm, w.w_gate, w.w_up, w.w_down};
+        for (const void* q : ps) {
+            if (!q) return fail(CB_E_INVALID, "layer %d has a NULL weight", l);
+            if (!aligned_to(q, 16)) return fail(CB_E_SHAPE, "layer %d weight not 16-byte aligned", l);
+        }
+    }
+    cb_model* m = new cb_model();
+    m->cfg = *cfg;
+    m->w.assign(layers, layers + cfg->n_layers);
+    if (hipGetDevice(&m->device) != hipSuccess) {
+        delete m;
+        return fail(CB_E_HIP, "hipGetDevice failed");
+    }
+    st = get_rope(cfg->rope_base, cfg->head_dim, 16384, &m->rope);
+    if (st != CB_OK) {
+        delete m;
+        return st;
+    }
+    if (hipStreamCreateWithFlags(&m->side, hipStreamNonBlocking) != hipSuccess) {
+        delete m;
+        return fail(CB_E_HIP, "side stream creation failed");
+    }
+    *out = m;
+    return CB_OK;
+}
+
+void cb_model_destroy(cb_model* m) {
+    if (!m) return;
+    if (m->side) {
+        (void)hipStreamSynchronize(m->side);
+        (void)hipStreamDestroy(m->side);
+    }
+    for (auto e : m->event_pool) (void)hipEventDestroy(e);
+    delete m;
+}
+
+cb_status cb_plan_create(cb_model* m, const cb_request* r, const cb_outputs* o, void* stream,
+                         cb_plan** out) {
+    if (!m || !out) return fail(CB_E_INVALID, "model/out is NULL");
+    *out = nullptr;
+    cb_plan* p = new cb_plan();
+    p->m = m;
+    p->stream = as_stream(stream);
+    cb_status st = validate_request(m, r, o, p);
+    if (st == CB_OK) st = ensure_rope(m, p->N);
+    if (st != CB_OK) {
+        delete p;
+        return st;
+    }
+    if (o->sel_count)
+        for (int l = 0; l < p->L; ++l) o->sel_count[l] = p->s[l + 1];
+    st = plan_alloc(p);
+    if (st == CB_OK) st = plan_events(p);
+    if (st == CB_OK) st = plan_start(p);
+    if (st != CB_OK) {
+        plan_free(p);
+        return st;
+    }
+    *out = p;
+    return CB_OK;
+}
+
+cb_status cb_fetch_kv(cb_plan* p, int32_t layer) {
+    if (!p) return fail(CB_E_INVALID, "plan is NULL");
+    if (layer < 0 || layer >= p->L) return fail(CB_E_INVALID, "layer %d out of range", layer);
+    return do_fetch(p, layer);
+}
+
+cb_status cb_prefill_layer(cb_plan* p, int32_t layer) {
+    if (!p) return fail(CB_E_INVALID, "plan is NULL");
+    if (layer != p->next_layer)
+        return fail(CB_E_BAD_STATE, "layer %d requested, layer %d is next", layer, p->next_layer);
+    cb_status st = do_fetch(p, layer);
+    if (st != CB_OK) return st;
+    st = do_layer(p, layer);
+    if (st != CB_OK) return st;
+    p->next_layer++;
+    return CB_OK;
+}
+
+cb_status cb_synchronize(cb_plan* p) {
+    if (!p) return fail(CB_E_INVALID, "plan is NULL");
+    CB_HIP(hipStreamSynchronize(p->m->side));
+    CB_HIP(hipStreamSynchronize(p->stream));
+    return CB_OK;
+}
+
+void cb_plan_destroy(cb_plan* p) { plan_free(p); }
+
+cb_status cb_blend(cb_model* m, const cb_request* r, const cb_outputs* o, void* stream) {
+    cb_plan* p = nullptr;
+    cb_status st = cb_plan_create(m, r, o, stream, &p);
+    if (st != CB_OK) return st;
+    for (int l = 0; l < p->L && st == CB_OK; ++l) {
+        if (l + 1 < p->L) st = do_fetch(p, l + 1);
+        if (st == CB_OK) st = cb_prefill_layer(p, l);
+    }
+    plan_free(p);
+    return st;
+}
+
+cb_status cb_prefill(cb_model* m, const void* x0, int32_t n_tokens, int32_t pos0, void* k_out,
+                     void* v_out, float* hidden_out, void* stream) {
+    if (!m || !x0 || !k_out || !v_out) return fail(CB_E_INVALID, "NULL argument");
+    if (n_tokens <= 0 || pos0 < 0) return fail(CB_E_INVALID, "n_tokens %d, pos0 %d", n_tokens, pos0);
+    cb_plan* p = new cb_plan();
+    p->m = m;
+    p->stream = as_stream(stream);
+    p->prefill_mode = true;
+    p->L = m->cfg.n_layers;
+    p->Nc = 0;
+    p->Ns = n_tokens;
+    p->N = n_tokens;
+    p->row_base = pos0;
+    p->s.assign(p->L + 1, 0);
+    p->x0 = x0;
+    p->out.fused_k = k_out;
+    p->out.fused_v = v_out;
+    p->out.hidden_out = hidden_out;
+    cb_status st = ensure_rope(m, pos0 + n_tokens);
+    if (st == CB_OK) st = plan_alloc(p);
+    if (st == CB_OK) st = plan_events(p);
+    if (st == CB_OK) st = plan_start(p);
+    for (int l = 0; l < p->L && st == CB_OK; ++l) st = cb_prefill_layer(p, l);
+    plan_free(p);
+    return st;
+}
+
+// ------------------------------------------------------------- kernel-level
+cb_status cb_rope_rerotate(int32_t dtype, const void* k_in, void* k_out, const void* v_in,
+                           void* v_out, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
+                           int32_t delta, double rope_base, void* stream) {
+    if (dtype != CB_F32 && dtype != CB_BF16) return fail(CB_E_INVALID, "dtype %d", dtype);
+    if (n_tokens > 0 && (!k_in || !k_out || (v_in && !v_out)))
+        return fail(CB_E_INVALID, "NULL buffer");
+    if (n_tokens < 0 || n_heads <= 0 || head_dim <= 0 || head_dim % 8)
+        return fail(CB_E_SHAPE, "bad sizes (head_dim must be a multiple of 8)");
+    if (!(rope_base > 1.0)) return fail(CB_E_INVALID, "rope_base must be > 1");
+    if (delta == INT32_MIN) return fail(CB_E_INVALID, "delta out of range");
+    RopeTab rt;
+    const int ad = delta < 0 ? -delta : delta;
+    cb_status st = get_rope(rope_base, head_dim, ad + 1, &rt);
+    if (st != CB_OK) return st;
+    RotJobs js{};
+    RotJob& j = js.j[0];
+    j.k_src = k_in == k_out ? nullptr : k_in;
+    j.v_src = v_in;
+    j.n_tokens = n_tokens;
+    j.delta = delta;
+    js.n = 1;
+    js.max_tokens = n_tokens;
+    CB_HIP(launch_rerotate(dtype, js, 0, k_out, v_out, n_heads, head_dim, rt, as_stream(stream)));
+    return CB_OK;
+}
+
+cb_status cb_deviation(int32_t dtype, const void* k_new, const void* v_new, const void* k_cached,
+                       const void* v_cached, int32_t n_rows, int32_t row_elems, int32_t dev_mode,
+                       float* dev_out, void* stream) {
+    if (dtype != CB_F32 && dtype != CB_BF16) return fail(CB_E_INVALID, "dtype %d", dtype);
+    if (dev_mode < 0 || dev_mode > 2) return fail(CB_E_INVALID, "dev_mode %d", dev_mode);
+    if (!dev_out || !k_new || !k_cached || !v_new || !v_cached)
+        return fail(CB_E_INVALID, "NULL buffer");
+    if (n_rows < 0 || row_elems <= 0 || row_elems % 8)
+        return fail(CB_E_SHAPE, "row_elems must be a positive multiple of 8");
+    CB_HIP(launch_deviation(dtype, k_new, v_new, k_cached, v_cached, nullptr, 0, n_rows, row_elems,
+                            dev_mode, dev_out, nullptr, as_stream(stream)));
+    return CB_OK;
+}
+
+cb_status cb_topk_select(const float* dev, int32_t n, int32_t k, int32_t* idx_out, void* stream) {
+    if (n < 0 || k < 0 || k > n) return fail(CB_E_INVALID, "need 0 <= k <= n (k=%d, n=%d)", k, n);
+    if (n > 0 && (!dev || (k > 0 && !idx_out))) return fail(CB_E_INVALID, "NULL buffer");
+    CB_HIP(launch_topk(dev, n, k, idx_out, as_stream(stream)));
+    return CB_OK;
+}
+
+cb_status cb_gather_rows(const void* src, void* dst, const int32_t* idx, int32_t n_rows,
+                         int64_t row_bytes, void* stream) {
+    if (n_rows < 0 || row_bytes <= 0 || row_bytes % 4) return fail(CB_E_SHAPE, "bad row size");
+    if (n_rows > 0 && (!src || !dst || !idx)) return fail(CB_E_INVALID, "NULL buffer");
+    CB_HIP(launch_gather_rows(src, dst, idx, n_rows, row_bytes, as_stream(stream)));
+    return CB_OK;
+}
+
+cb_status cb_scatter_rows(const void* src, void* dst, const int32_t* idx, int32_t n_rows,
+                          int64_t row_bytes, void* stream) {
+    if (n_rows < 0 || row_bytes <= 0 || row_bytes % 4) return fail(CB_E_SHAPE, "bad row size");
+    if (n_rows > 0 && (!src || !dst || !idx)) return fail(CB_E_INVALID, "NULL buffer");
+    CB_HIP(launch_scatter_rows(src, dst, idx, n_rows, row_bytes, as_stream(stream)));
+    return CB_OK;
+}
+
+cb_status cb_rmsnorm(int32_t x_dtype, const void* x, int32_t y_dtype, const void* g, void* y,
+                     int32_t rows, int32_t d, float eps, void* stream) {
+    if ((x_dtype != CB_F32 && x_dtype != CB_BF16) || (y_dtype != CB_F32 && y_dtype != CB_BF16))
+        return fail(CB_E_INVALID, "dtype");
+    if (rows < 0 || d <= 0) return fail(CB_E_SHAPE, "bad sizes");
+    if (rows > 0 && (!x || !g || !y)) return fail(CB_E_INVALID, "NULL buffer");
+    CB_HIP(launch_rmsnorm(x_dtype, x, nullptr, y_dtype, g, y, nullptr, rows, d, eps,
+                          as_stream(stream)));
+    return CB_OK;
+}
+
+cb_status cb_gemm(int32_t dtype, const void* a, const void* b, float* c, int32_t m, int32_t n,
+                  int32_t k, void* stream) {
+    if (dtype != CB_F32 && dtype != CB_BF16) return fail(CB_E_INVALID, "dtype %d", dtype);
+    if (m < 0 || n < 0 || k <= 0) return fail(CB_E_SHAPE, "bad sizes");
+    const int kmul = dtype == CB_BF16 ? 64 : 32;
+    if (k % kmul) return fail(CB_E_SHAPE, "k = %d must be a multiple of %d", k, kmul);
+    if (m > 0 && n > 0 && (!a || !b || !c)) return fail(CB_E_INVALID, "NULL buffer");
+    if (!aligned_to(a, 16) || !aligned_to(b, 16)) return fail(CB_E_SHAPE, "a/b not 16-byte aligned");
+    GemmArgs g{};
+    g.a = a; g.b0 = b; g.M = m; g.N = n; g.K = k; g.out0 = c;
+    CB_HIP(launch_gemm(dtype, EPI_STORE_F32, g, as_stream(stream)));
+    return CB_OK;
+}
+
+cb_status cb_attention(int32_t dtype, const void* q, const int32_t* q_pos, int32_t n_q,
+                       const void* k, const void* v, int32_t n_kv, int32_t n_q_heads,
+                       int32_t n_kv_heads, int32_t head_dim, void* out, void* stream) {
+    if (dtype != CB_F32 && dtype != CB_BF16) return fail(CB_E_INVALID, "dtype %d", dtype);
+    if (n_q < 0 || n_kv <= 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads)
+        return fail(CB_E_SHAPE, "bad sizes");
+    if (head_dim != 64 && head_dim != 128) return fail(CB_E_UNSUPPORTED, "head_dim %d", head_dim);
+    if (n_q > 0 && (!q || !q_pos || !k || !v || !out)) return fail(CB_E_INVALID, "NULL buffer");
+    AttnArgs a{};
+    a.q = q; a.q_pos = q_pos; a.n_q = n_q; a.k = k; a.v = v; a.n_kv = n_kv;
+    a.n_q_heads = n_q_heads; a.n_kv_heads = n_kv_heads; a.head_dim = head_dim; a.out = out;
+    CB_HIP(launch_attention(dtype, a, as_stream(stream)));
+    return CB_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,224 @@
+// KV deviation and HKVD (high KV deviation) selection.
+//
+// Deviation: CacheBlend explainer (0h-n0.github.io), section
+// "KVキャッシュの定義と偏差メトリクス", eq. 1 (per-token L2 distance of the KV
+// row), squared as in the section "HKVDトークン選定" selection code; it is
+// measured between the recomputed row and the re-rotated cached row.
+// Selection: the same section's code keeps the k rows of largest deviation
+// and returns them in position order.  Ties are broken by position so the
+// kept set is unique: order = (NaN first, larger value first, -0.0 == +0.0,
+// smaller index first).
+//
+// The selection is exact integer work: every deviation maps to a 32-bit rank
+// key (smaller = kept first); a 4-pass radix select over 8-bit digits finds
+// the k-th smallest key T and how many rows equal to T are still needed; the
+// kept rows are those below T plus the first `need` rows equal to T in
+// index order; a block-wide scan writes them in ascending index order.
+#include "kernels.h"
+
+namespace cb {
+
+namespace {
+
+constexpr int kDevThreads = 256;
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+
+template <typename T>
+__device__ __forceinline__ float sq_diff8(const T* a, const T* b) {
+    Frag<T> x = load_frag<T>(a);
+    Frag<T> y = load_frag<T>(b);
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float d = to_f32(x.v[i]) - to_f32(y.v[i]);
+        s += d * d;
+    }
+    return s;
+}
+
+// One wave per row: lanes stride over the row in 8-element pieces.
+template <typename T>
+__global__ __launch_bounds__(kDevThreads) void deviation_kernel(
+    const T* __restrict__ kn, const T* __restrict__ vn, const T* __restrict__ kc,
+    const T* __restrict__ vc, const int* __restrict__ pos, int row_base, int n_rows, int kv_dim,
+    int mode, float* __restrict__ dev, float* __restrict__ dev_pos_out) {
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * (kDevThreads / 64) + (threadIdx.x >> 6);
+    if (r >= n_rows) return;
+    const int64_t no = (int64_t)r * kv_dim;
+    const int64_t co = (int64_t)(pos ? pos[r] - row_base : r) * kv_dim;
+    float acc = 0.f;
+    if (mode != 2)
+        for (int c = lane * 8; c < kv_dim; c += 512) acc += sq_diff8(kn + no + c, kc + co + c);
+    if (mode != 1)
+        for (int c = lane * 8; c < kv_dim; c += 512) acc += sq_diff8(vn + no + c, vc + co + c);
+    acc = warp_sum(acc);
+    if (lane == 0) {
+        dev[r] = acc;
+        if (dev_pos_out) dev_pos_out[pos[r]] = acc;
+    }
+}
+
+__device__ __forceinline__ uint32_t rank_key(float f) {
+    if (f != f) return 0u;                      // NaN ranks above everything
+    uint32_t b = __float_as_uint(f);
+    if (f == 0.f) b = 0u;                       // -0.0 ranks with +0.0
+    const uint32_t asc = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ~asc;                                // larger value -> smaller key
+}
+
+// Exclusive scan of one int per thread over the block; returns the total too.
+__device__ int block_exclusive_scan(int v, int* wsum, int& total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int t = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += t;
+    }
+    if (lane == 63) wsum[w] = inc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int i = 0; i < kSelWaves; ++i) {
+            const int t = wsum[i];
+            wsum[i] = run;
+            run += t;
+        }
+        wsum[kSelWaves] = run;
+    }
+    __syncthreads();
+    const int ex = wsum[w] + inc - v;
+    total = wsum[kSelWaves];
+    __syncthreads();
+    return ex;
+}
+
+// Marks the kept rows of dev[0..n) (k of them) and returns, per thread, the
+// exclusive prefix of kept rows over its contiguous segment [beg, end).
+struct SelState {
+    uint32_t T;
+    int need;
+};
+
+__device__ SelState radix_threshold(const float* __restrict__ dev, int n, int k,
+                                    uint32_t* hist, int* bcast) {
+    uint32_t prefix = 0, mask = 0;
+    int kk = k;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = threadIdx.x; i < 256; i += kSelThreads) hist[i] = 0;
+        __syncthreads();
+        for (int i = threadIdx.x; i < n; i += kSelThreads) {
+            const uint32_t key = rank_key(dev[i]);
+            if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int cum = 0, d = 255;
+            for (int i = 0; i < 256; ++i) {
+                const int h = (int)hist[i];
+                if (cum + h >= kk) { d = i; break; }
+                cum += h;
+            }
+            bcast[0] = d;
+            bcast[1] = kk - cum;
+        }
+        __syncthreads();
+        prefix |= (uint32_t)bcast[0] << shift;
+        mask |= 0xFFu << shift;
+        kk = bcast[1];
+        __syncthreads();
+    }
+    return SelState{prefix, kk};
+}
+
+// Writes the kept indices (ascending) through `emit(slot, index)`.
+template <typename Emit>
+__device__ void select_rows(const float* __restrict__ dev, int n, int k, Emit emit) {
+    __shared__ uint32_t hist[256];
+    __shared__ int bcast[2];
+    __shared__ int wsum[kSelWaves + 1];
+    if (k <= 0) return;
+    if (k >= n) {
+        for (int i = threadIdx.x; i < n; i += kSelThreads) emit(i, i);
+        return;
+    }
+    const SelState st = radix_threshold(dev, n, k, hist, bcast);
+    const int per = (n + kSelThreads - 1) / kSelThreads;
+    const int beg = min(n, (int)threadIdx.x * per), end = min(n, beg + per);
+    int eq = 0;
+    for (int i = beg; i < end; ++i) eq += rank_key(dev[i]) == st.T;
+    int tot;
+    int e = block_exclusive_scan(eq, wsum, tot);
+    int cnt = 0;
+    for (int i = beg; i < end; ++i) {
+        const uint32_t key = rank_key(dev[i]);
+        cnt += key < st.T || (key == st.T && e++ < st.need);
+    }
+    e -= eq;   // back to this segment's first equal-key rank
+    int slot = block_exclusive_scan(cnt, wsum, tot);
+    for (int i = beg; i < end; ++i) {
+        const uint32_t key = rank_key(dev[i]);
+        if (key < st.T || (key == st.T && e++ < st.need)) emit(slot++, i);
+    }
+}
+
+__global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restrict__ dev, int n,
+                                                          int k, int* __restrict__ out) {
+    select_rows(dev, n, k, [&](int slot, int i) { out[slot] = i; });
+}
+
+__global__ __launch_bounds__(kSelThreads) void blend_select_kernel(
+    const float* __restrict__ dev, int n_c, int k, int n_s, const int* __restrict__ pos_r,
+    int* __restrict__ sel_local, int* __restrict__ pos_q, int* __restrict__ sel_pos) {
+    select_rows(dev, n_c, k, [&](int slot, int i) {
+        const int p = pos_r[i];
+        sel_local[slot] = i;
+        pos_q[slot] = p;
+        if (sel_pos) sel_pos[slot] = p;
+    });
+    for (int s = threadIdx.x; s < n_s; s += kSelThreads) {
+        sel_local[k + s] = n_c + s;
+        pos_q[k + s] = pos_r[n_c + s];
+    }
+}
+
+}  // namespace
+
+hipError_t launch_deviation(int dtype, const void* k_new, const void* v_new,
+                            const void* k_cached, const void* v_cached, const int* pos,
+                            int row_base, int n_rows, int kv_dim, int mode, float* dev,
+                            float* dev_pos_out, hipStream_t s) {
+    if (n_rows <= 0) return hipSuccess;
+    if (kv_dim % 8 != 0) return hipErrorInvalidValue;
+    const int per = kDevThreads / 64;
+    dim3 grid((n_rows + per - 1) / per), block(kDevThreads);
+    if (dtype == BF16)
+        hipLaunchKernelGGL(deviation_kernel<bf16>, grid, block, 0, s, (const bf16*)k_new,
+                           (const bf16*)v_new, (const bf16*)k_cached, (const bf16*)v_cached, pos,
+                           row_base, n_rows, kv_dim, mode, dev, dev_pos_out);
+    else
+        hipLaunchKernelGGL(deviation_kernel<float>, grid, block, 0, s, (const float*)k_new,
+                           (const float*)v_new, (const float*)k_cached,
+                           (const float*)v_cached, pos, row_base, n_rows, kv_dim, mode, dev,
+                           dev_pos_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* dev, int n, int k, int* idx_out, hipStream_t s) {
+    if (n <= 0 || k <= 0) return hipSuccess;
+    hipLaunchKernelGGL(topk_kernel, dim3(1), dim3(kSelThreads), 0, s, dev, n, k, idx_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_select(const float* dev, int n_c, int k, int n_s, const int* pos_r,
+                         int* sel_local, int* pos_q, int* sel_pos, hipStream_t s) {
+    if (k > n_c || k < 0 || n_s < 0) return hipErrorInvalidValue;
+    if (k + n_s == 0) return hipSuccess;
+    hipLaunchKernelGGL(blend_select_kernel, dim3(1), dim3(kSelThreads), 0, s, dev, n_c, k, n_s,
+                       pos_r, sel_local, pos_q, sel_pos);
+    return hipGetLastError();
+}
+
+}  // namespace cb

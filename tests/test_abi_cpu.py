@@ -1,0 +1,108 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/cacheblend.h declares, and its host-only logic (schedule, argument
+validation) behaves as documented.  No kernel is launched here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "cacheblend.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(cb_[a-z_0-9]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def npk():
+    import non_prefix_kv_amd
+    return non_prefix_kv_amd
+
+
+def test_exports_every_declared_symbol(npk):
+    lib = ctypes.CDLL(npk.LIB_PATH)
+    names = _declared()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(npk.EXPORTED)
+
+
+def test_abi_version(npk):
+    assert npk.cb_abi_version() == npk.CB_ABI_VERSION == 1
+
+
+@pytest.mark.parametrize("n", [0, 1, 10, 384, 3840, 7680, 8192])
+@pytest.mark.parametrize("r", [0, 1, 500, 1000, 1500, 1800, 5000, 9999, 10000])
+@pytest.mark.parametrize("kind", ["gradual", "fixed"])
+def test_schedule_matches_oracle(npk, n, r, kind):
+    code = npk.CB_SCHED_GRADUAL if kind == "gradual" else npk.CB_SCHED_FIXED
+    for L in (1, 2, 32, 40, 60):
+        assert npk.cb_schedule(n, r, code, L) == oracle.schedule(n, r, kind, L)
+
+
+def test_schedule_rejects_bad_args(npk):
+    with pytest.raises(npk.CBError) as e:
+        npk.cb_schedule(100, 10001, npk.CB_SCHED_FIXED, 4)
+    assert e.value.status == npk.CB_E_SCHEDULE
+    with pytest.raises(npk.CBError) as e:
+        npk.cb_schedule(100, 100, 7, 4)
+    assert e.value.status == npk.CB_E_INVALID
+    assert "kind" in npk.cb_last_error()
+
+
+def test_model_create_validation(npk):
+    raw = npk.RAW["cb_model_create"]
+    h = ctypes.c_void_p()
+    assert raw(None, None, ctypes.byref(h)) == npk.CB_E_INVALID
+    cfg = npk.cb_model_cfg(2, 256, 4, 4, 96, 1024, 1e4, 1e-5, npk.CB_BF16)
+    assert raw(ctypes.byref(cfg), None, ctypes.byref(h)) == npk.CB_E_UNSUPPORTED
+    cfg = npk.cb_model_cfg(2, 256, 4, 3, 64, 1024, 1e4, 1e-5, npk.CB_BF16)
+    assert raw(ctypes.byref(cfg), None, ctypes.byref(h)) == npk.CB_E_SHAPE
+    cfg = npk.cb_model_cfg(2, 250, 4, 4, 64, 1024, 1e4, 1e-5, npk.CB_BF16)
+    assert raw(ctypes.byref(cfg), None, ctypes.byref(h)) == npk.CB_E_SHAPE
+    cfg = npk.cb_model_cfg(2, 256, 4, 4, 64, 1024, 1e4, 1e-5, 5)
+    assert raw(ctypes.byref(cfg), None, ctypes.byref(h)) == npk.CB_E_INVALID
+    cfg = npk.cb_model_cfg(2, 256, 4, 4, 64, 1024, 1e4, 1e-5, npk.CB_F32)
+    assert raw(ctypes.byref(cfg), None, ctypes.byref(h)) == npk.CB_E_INVALID   # NULL layers
+    w = (npk.cb_layer_weights * 2)()
+    assert raw(ctypes.byref(cfg), w, ctypes.byref(h)) == npk.CB_E_INVALID     # NULL weights
+    assert not h.value
+
+
+def test_kernel_entry_validation(npk):
+    R = npk.RAW
+    assert R["cb_topk_select"](None, 5, 6, None, None) == npk.CB_E_INVALID
+    assert R["cb_topk_select"](None, -1, 0, None, None) == npk.CB_E_INVALID
+    assert R["cb_gemm"](npk.CB_BF16, None, None, None, 8, 8, 48, None) == npk.CB_E_SHAPE
+    assert R["cb_gemm"](3, None, None, None, 8, 8, 64, None) == npk.CB_E_INVALID
+    assert R["cb_attention"](npk.CB_BF16, None, None, 4, None, None, 8, 4, 4, 96, None,
+                             None) == npk.CB_E_UNSUPPORTED
+    assert R["cb_attention"](npk.CB_BF16, None, None, 4, None, None, 8, 4, 3, 64, None,
+                             None) == npk.CB_E_SHAPE
+    assert R["cb_rope_rerotate"](npk.CB_BF16, None, None, None, None, 4, 2, 64, 3, 1e4,
+                                 None) == npk.CB_E_INVALID
+    assert R["cb_rope_rerotate"](npk.CB_BF16, 16, 16, None, None, 4, 2, 60, 3, 1e4,
+                                 None) == npk.CB_E_SHAPE
+    assert R["cb_deviation"](npk.CB_F32, 16, 16, 16, 16, 4, 64, 3, 16, None) == npk.CB_E_INVALID
+    assert R["cb_gather_rows"](16, 16, 16, 4, 6, None) == npk.CB_E_SHAPE
+    assert R["cb_rmsnorm"](npk.CB_F32, None, npk.CB_F32, None, None, 3, 8, 1e-5,
+                           None) == npk.CB_E_INVALID
+    # NULL handles are rejected, never dereferenced
+    assert R["cb_fetch_kv"](None, 0) == npk.CB_E_INVALID
+    assert R["cb_prefill_layer"](None, 0) == npk.CB_E_INVALID
+    assert R["cb_synchronize"](None) == npk.CB_E_INVALID
+    R["cb_plan_destroy"](None)
+    R["cb_model_destroy"](None)
+
+
+def test_binding_has_no_fallback():
+    """The package refuses to import without the built library."""
+    src = open(os.path.join(ROOT, "non_prefix_kv_amd", "__init__.py")).read()
+    assert "raise ImportError" in src
+    assert "oracle" not in src
