@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libcacheblend.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m non_prefix_kv_amd.build` (hipcc, gfx950)")
+                      "`python non_prefix_kv_amd/build.py` (hipcc, gfx950)")
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ------------------------------------------------------------------ constants
@@ -58,6 +58,15 @@ class cb_outputs(ctypes.Structure):
                 ("deviation", _c_p)]
 
 
+class cb_kernel_stat(ctypes.Structure):
+    _fields_ = [("launches", _c_i64), ("total_ms", ctypes.c_double), ("flops", ctypes.c_double),
+                ("bytes", ctypes.c_double)]
+
+
+KERNEL_CLASSES = ("rotate", "rmsnorm", "gemm_qkv", "deviation", "select", "scatter",
+                  "attention", "gemm_o", "gemm_gateup", "gemm_down")
+
+
 def _sig(name, res, *args):
     f = getattr(_lib, name)
     f.restype = res
@@ -79,6 +88,8 @@ _fn = {
     "cb_synchronize": (ctypes.c_int, _c_p),
     "cb_plan_destroy": (None, _c_p),
     "cb_prefill": (ctypes.c_int, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p),
+    "cb_profile_enable": (ctypes.c_int, _c_p, _c_i32),
+    "cb_profile_read": (ctypes.c_int, _c_p, _P(cb_kernel_stat)),
     "cb_rope_rerotate": (ctypes.c_int, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
                          _c_i32, ctypes.c_double, _c_p),
     "cb_deviation": (ctypes.c_int, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p,
@@ -264,6 +275,18 @@ class Plan:
 def cb_prefill(model, x0, n_tokens, pos0, k_out, v_out, hidden_out=None, stream=None):
     _check(RAW["cb_prefill"](model.handle, _ptr(x0), n_tokens, pos0, _ptr(k_out), _ptr(v_out),
                              _ptr(hidden_out), _stream(stream)))
+
+
+def cb_profile_enable(model, enable=True):
+    _check(RAW["cb_profile_enable"](model.handle, 1 if enable else 0))
+
+
+def cb_profile_read(model):
+    """{class name: {launches, total_ms, flops, bytes}} of the timed launches."""
+    arr = (cb_kernel_stat * len(KERNEL_CLASSES))()
+    _check(RAW["cb_profile_read"](model.handle, arr))
+    return {n: {"launches": a.launches, "total_ms": a.total_ms, "flops": a.flops,
+                "bytes": a.bytes} for n, a in zip(KERNEL_CLASSES, arr)}
 
 
 # ------------------------------------------------------------------ kernel level

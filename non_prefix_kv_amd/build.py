@@ -1,6 +1,7 @@
 """Builds libcacheblend.so in-tree with hipcc for gfx950.
 
-Usage: python -m non_prefix_kv_amd.build   (or __graft_entry__.build()).
+Usage: python non_prefix_kv_amd/build.py   (or __graft_entry__.build()); run it by
+path: importing the package itself loads the built library.
 Every source is compiled each time (parallel hipcc processes), then linked.
 """
 import concurrent.futures as cf

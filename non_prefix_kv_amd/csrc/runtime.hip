@@ -163,6 +163,16 @@ struct cb_model {
     hipStream_t side = nullptr;   // fetch (H2D + rotation) stream, default priority
     std::mutex mu;
     std::vector<hipEvent_t> event_pool;
+    // per-kernel-class timing (cb_profile_*)
+    struct ProfRec {
+        int cls;
+        hipEvent_t a, b;
+        double flops, bytes;
+    };
+    bool prof = false;
+    std::vector<ProfRec> prof_pending;
+    std::vector<hipEvent_t> timing_pool;
+    cb_kernel_stat stats[CB_K_COUNT] = {};
     int es() const { return elem_size(cfg.dtype); }
     int qd() const { return cfg.n_q_heads * cfg.head_dim; }
     int kvd() const { return cfg.n_kv_heads * cfg.head_dim; }
@@ -196,6 +206,41 @@ struct cb_plan {
 };
 
 namespace {
+
+// Brackets one launch with timing events when profiling is on.
+class Span {
+public:
+    Span(cb_model* m, int cls, hipStream_t s, double flops, double bytes)
+        : m_(m), cls_(cls), s_(s), flops_(flops), bytes_(bytes) {
+        if (m_->prof && (a_ = take()) != nullptr) (void)hipEventRecord(a_, s_);
+    }
+    ~Span() {
+        if (!a_) return;
+        hipEvent_t b = take();
+        if (!b) return;
+        (void)hipEventRecord(b, s_);
+        std::lock_guard<std::mutex> lk(m_->mu);
+        m_->prof_pending.push_back({cls_, a_, b, flops_, bytes_});
+    }
+
+private:
+    hipEvent_t take() {
+        std::lock_guard<std::mutex> lk(m_->mu);
+        if (!m_->timing_pool.empty()) {
+            hipEvent_t e = m_->timing_pool.back();
+            m_->timing_pool.pop_back();
+            return e;
+        }
+        hipEvent_t e = nullptr;
+        if (hipEventCreate(&e) != hipSuccess) return nullptr;
+        return e;
+    }
+    cb_model* m_;
+    int cls_;
+    hipStream_t s_;
+    double flops_, bytes_;
+    hipEvent_t a_ = nullptr;
+};
 
 cb_status validate_cfg(const cb_model_cfg* c) {
     if (!c) return fail(CB_E_INVALID, "cfg is NULL");
@@ -320,9 +365,14 @@ cb_status do_fetch(cb_plan* p, int l) {
         CB_HIP(hipMemcpyAsync(fk + dst, (const char*)ck.k + src, bytes, hipMemcpyHostToDevice, side));
         CB_HIP(hipMemcpyAsync(fv + dst, (const char*)ck.v + src, bytes, hipMemcpyHostToDevice, side));
     }
-    for (const RotJobs& js : p->jobs)
+    for (const RotJobs& js : p->jobs) {
+        double bytes = 0;
+        for (int i = 0; i < js.n; ++i)
+            bytes += (double)js.j[i].n_tokens * m->kvd() * es * (js.j[i].v_src ? 4 : 2);
+        Span sp(m, CB_K_ROTATE, side, 0, bytes);
         CB_HIP(launch_rerotate(m->cfg.dtype, js, l, fk, fv, m->cfg.n_kv_heads, m->cfg.head_dim,
                                m->rope, side));
+    }
     CB_HIP(hipEventRecord(p->fetched[l], side));
     p->fetch_done[l] = 1;
     return CB_OK;
@@ -335,6 +385,7 @@ cb_status do_layer(cb_plan* p, int l) {
     const hipStream_t st = p->stream;
     const int dt = c.dtype, es = m->es();
     const int nC = p->s[l], k = p->s[l + 1], mR = nC + p->Ns, mQ = k + p->Ns;
+    const double d = c.d_model, F = c.ffn_dim, qd = m->qd(), kvd = m->kvd();
     CB_HIP(hipEventRecord(p->layer_start[l], st));
     CB_HIP(hipStreamWaitEvent(st, p->fetched[l], 0));
     if (mR == 0) return CB_OK;
@@ -344,59 +395,92 @@ cb_status do_layer(cb_plan* p, int l) {
     int* pos_q = p->pos_b;
 
     // 1. RMSNorm of the input rows (layer 0 gathers them from x0 by position)
-    if (l == 0) {
-        const bool all_rows = (nC == p->Nc) && p->row_base == 0;
-        CB_HIP(launch_rmsnorm(dt, p->x0, (all_rows || p->prefill_mode) ? nullptr : pos_r, dt,
-                              w.attn_norm, p->Hn, p->X, mR, c.d_model, c.rms_eps, st));
-    } else {
-        CB_HIP(launch_rmsnorm(F32, p->X, nullptr, dt, w.attn_norm, p->Hn, nullptr, mR, c.d_model,
-                              c.rms_eps, st));
+    {
+        const double in_es = l == 0 ? es : 4;
+        Span sp(m, CB_K_RMSNORM, st, 0, mR * d * (in_es + es + (l == 0 ? 4 : 0)));
+        if (l == 0) {
+            const bool all_rows = (nC == p->Nc) && p->row_base == 0;
+            CB_HIP(launch_rmsnorm(dt, p->x0, (all_rows || p->prefill_mode) ? nullptr : pos_r, dt,
+                                  w.attn_norm, p->Hn, p->X, mR, c.d_model, c.rms_eps, st));
+        } else {
+            CB_HIP(launch_rmsnorm(F32, p->X, nullptr, dt, w.attn_norm, p->Hn, nullptr, mR,
+                                  c.d_model, c.rms_eps, st));
+        }
     }
     // 2. QKV projection with RoPE at the real positions
-    GemmArgs g{};
-    g.a = p->Hn; g.b0 = w.wq; g.b1 = w.wk; g.b2 = w.wv;
-    g.n0 = m->qd(); g.n1 = m->kvd();
-    g.M = mR; g.N = m->qd() + 2 * m->kvd(); g.K = c.d_model;
-    g.out0 = p->Q; g.out1 = p->Kn; g.out2 = p->Vn;
-    g.pos = pos_r; g.rope = m->rope; g.head_dim = c.head_dim;
-    CB_HIP(launch_gemm(dt, EPI_QKV, g, st));
+    {
+        GemmArgs g{};
+        g.a = p->Hn; g.b0 = w.wq; g.b1 = w.wk; g.b2 = w.wv;
+        g.n0 = m->qd(); g.n1 = m->kvd();
+        g.M = mR; g.N = m->qd() + 2 * m->kvd(); g.K = c.d_model;
+        g.out0 = p->Q; g.out1 = p->Kn; g.out2 = p->Vn;
+        g.pos = pos_r; g.rope = m->rope; g.head_dim = c.head_dim;
+        const double n = g.N;
+        Span sp(m, CB_K_GEMM_QKV, st, 2.0 * mR * n * d, (mR * d + n * d + mR * n) * es);
+        CB_HIP(launch_gemm(dt, EPI_QKV, g, st));
+    }
     // 3. deviation of the recomputed chunk rows against the rotated cache
     float* dev_out = p->out.deviation ? p->out.deviation + (size_t)l * p->Nc : nullptr;
-    if (nC > 0 && (k < nC || dev_out))
+    if (nC > 0 && (k < nC || dev_out)) {
+        const double parts = p->dev_mode == CB_DEV_KV ? 4 : 2;
+        Span sp(m, CB_K_DEVIATION, st, 0, nC * (parts * kvd * es + 12.0));
         CB_HIP(launch_deviation(dt, p->Kn, p->Vn, fk, fv, pos_r, 0, nC, m->kvd(), p->dev_mode,
                                 p->dev, dev_out, st));
+    }
     // 4. keep the top s[l+1] chunk rows, then the suffix rows
     int* sel_pos = p->out.sel_idx ? p->out.sel_idx + (size_t)l * p->Nc : nullptr;
-    CB_HIP(launch_select(p->dev, nC, k, p->Ns, pos_r, p->sel_local, pos_q, sel_pos, st));
+    {
+        Span sp(m, CB_K_SELECT, st, 0, 4.0 * nC + 12.0 * mQ);
+        CB_HIP(launch_select(p->dev, nC, k, p->Ns, pos_r, p->sel_local, pos_q, sel_pos, st));
+    }
     // 5. merge the kept rows' K/V into the fused cache
-    CB_HIP(launch_scatter_kv(dt, p->Kn, p->Vn, p->sel_local, pos_r, p->row_base, fk, fv, mQ,
-                             m->kvd(), st));
+    {
+        Span sp(m, CB_K_SCATTER, st, 0, 4.0 * mQ * kvd * es);
+        CB_HIP(launch_scatter_kv(dt, p->Kn, p->Vn, p->sel_local, pos_r, p->row_base, fk, fv, mQ,
+                                 m->kvd(), st));
+    }
     // 6. attention over the whole fused cache of this layer
-    AttnArgs a{};
-    a.q = p->Q; a.qidx = p->sel_local; a.q_pos = pos_q; a.n_q = mQ;
-    a.k = fk; a.v = fv; a.n_kv = p->N; a.kv_pos0 = p->row_base;
-    a.n_q_heads = c.n_q_heads; a.n_kv_heads = c.n_kv_heads; a.head_dim = c.head_dim;
-    a.out = p->attn;
-    CB_HIP(launch_attention(dt, a, st));
+    {
+        AttnArgs a{};
+        a.q = p->Q; a.qidx = p->sel_local; a.q_pos = pos_q; a.n_q = mQ;
+        a.k = fk; a.v = fv; a.n_kv = p->N; a.kv_pos0 = p->row_base;
+        a.n_q_heads = c.n_q_heads; a.n_kv_heads = c.n_kv_heads; a.head_dim = c.head_dim;
+        a.out = p->attn;
+        Span sp(m, CB_K_ATTENTION, st, 0, 0);
+        CB_HIP(launch_attention(dt, a, st));
+    }
     // 7. O projection + residual
-    GemmArgs go{};
-    go.a = p->attn; go.b0 = w.wo; go.M = mQ; go.N = c.d_model; go.K = m->qd();
-    go.out0 = p->Hres; go.resid = p->X; go.ridx = p->sel_local;
-    CB_HIP(launch_gemm(dt, EPI_RESID, go, st));
+    {
+        GemmArgs go{};
+        go.a = p->attn; go.b0 = w.wo; go.M = mQ; go.N = c.d_model; go.K = m->qd();
+        go.out0 = p->Hres; go.resid = p->X; go.ridx = p->sel_local;
+        Span sp(m, CB_K_GEMM_O, st, 2.0 * mQ * d * qd, (mQ * qd + d * qd) * es + mQ * d * 8);
+        CB_HIP(launch_gemm(dt, EPI_RESID, go, st));
+    }
     // 8. RMSNorm, 9. gate/up with SiLU(gate)*up
-    CB_HIP(launch_rmsnorm(F32, p->Hres, nullptr, dt, w.mlp_norm, p->Hn, nullptr, mQ, c.d_model,
-                          c.rms_eps, st));
-    GemmArgs gu{};
-    gu.a = p->Hn; gu.b0 = w.w_gate; gu.b1 = w.w_up; gu.M = mQ; gu.N = c.ffn_dim; gu.K = c.d_model;
-    gu.out0 = p->act;
-    CB_HIP(launch_gemm(dt, EPI_SWIGLU, gu, st));
+    {
+        Span sp(m, CB_K_RMSNORM, st, 0, mQ * d * (4 + es));
+        CB_HIP(launch_rmsnorm(F32, p->Hres, nullptr, dt, w.mlp_norm, p->Hn, nullptr, mQ,
+                              c.d_model, c.rms_eps, st));
+    }
+    {
+        GemmArgs gu{};
+        gu.a = p->Hn; gu.b0 = w.w_gate; gu.b1 = w.w_up; gu.M = mQ; gu.N = c.ffn_dim;
+        gu.K = c.d_model;
+        gu.out0 = p->act;
+        Span sp(m, CB_K_GEMM_GATEUP, st, 4.0 * mQ * F * d, (mQ * d + 2 * F * d + mQ * F) * es);
+        CB_HIP(launch_gemm(dt, EPI_SWIGLU, gu, st));
+    }
     // 10. down projection + residual -> next layer input (or the caller's output)
-    GemmArgs gd{};
-    gd.a = p->act; gd.b0 = w.w_down; gd.M = mQ; gd.N = c.d_model; gd.K = c.ffn_dim;
-    const bool last = l == p->L - 1;
-    gd.out0 = (last && p->out.hidden_out) ? p->out.hidden_out : p->X;
-    gd.resid = p->Hres; gd.ridx = nullptr;
-    CB_HIP(launch_gemm(dt, EPI_RESID, gd, st));
+    {
+        GemmArgs gd{};
+        gd.a = p->act; gd.b0 = w.w_down; gd.M = mQ; gd.N = c.d_model; gd.K = c.ffn_dim;
+        const bool last = l == p->L - 1;
+        gd.out0 = (last && p->out.hidden_out) ? p->out.hidden_out : p->X;
+        gd.resid = p->Hres; gd.ridx = nullptr;
+        Span sp(m, CB_K_GEMM_DOWN, st, 2.0 * mQ * d * F, (mQ * F + d * F) * es + mQ * d * 8);
+        CB_HIP(launch_gemm(dt, EPI_RESID, gd, st));
+    }
     std::swap(p->pos_a, p->pos_b);
     return CB_OK;
 }
@@ -536,6 +620,11 @@ void cb_model_destroy(cb_model* m) {
         (void)hipStreamDestroy(m->side);
     }
     for (auto e : m->event_pool) (void)hipEventDestroy(e);
+    for (auto e : m->timing_pool) (void)hipEventDestroy(e);
+    for (auto& r : m->prof_pending) {
+        (void)hipEventDestroy(r.a);
+        (void)hipEventDestroy(r.b);
+    }
     delete m;
 }
 
@@ -628,6 +717,50 @@ cb_status cb_prefill(cb_model* m, const void* x0, int32_t n_tokens, int32_t pos0
     if (st == CB_OK) st = plan_start(p);
     for (int l = 0; l < p->L && st == CB_OK; ++l) st = cb_prefill_layer(p, l);
     plan_free(p);
+    return st;
+}
+
+cb_status cb_profile_enable(cb_model* m, int32_t enable) {
+    if (!m) return fail(CB_E_INVALID, "model is NULL");
+    if (enable) {
+        cb_kernel_stat tmp[CB_K_COUNT];
+        cb_status st = cb_profile_read(m, tmp);   // drain anything pending
+        if (st != CB_OK) return st;
+        std::lock_guard<std::mutex> lk(m->mu);
+        for (auto& x : m->stats) x = cb_kernel_stat{};
+    }
+    m->prof = enable != 0;
+    return CB_OK;
+}
+
+cb_status cb_profile_read(cb_model* m, cb_kernel_stat* stats) {
+    if (!m || !stats) return fail(CB_E_INVALID, "NULL argument");
+    std::vector<cb_model::ProfRec> recs;
+    {
+        std::lock_guard<std::mutex> lk(m->mu);
+        recs.swap(m->prof_pending);
+    }
+    cb_status st = CB_OK;
+    for (auto& r : recs) {
+        float ms = 0.f;
+        if (st == CB_OK) {
+            hipError_t e = hipEventSynchronize(r.b);
+            if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.a, r.b);
+            if (e != hipSuccess) st = fail(CB_E_HIP, "profile event: %s", hipGetErrorString(e));
+        }
+        std::lock_guard<std::mutex> lk(m->mu);
+        if (st == CB_OK) {
+            cb_kernel_stat& k = m->stats[r.cls];
+            k.launches += 1;
+            k.total_ms += ms;
+            k.flops += r.flops;
+            k.bytes += r.bytes;
+        }
+        m->timing_pool.push_back(r.a);
+        m->timing_pool.push_back(r.b);
+    }
+    std::lock_guard<std::mutex> lk(m->mu);
+    for (int i = 0; i < CB_K_COUNT; ++i) stats[i] = m->stats[i];
     return st;
 }
 

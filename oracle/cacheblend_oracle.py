@@ -49,6 +49,7 @@ a proposal the pages do not fix: parity unpinned (both sides consume the same
 integer schedule).
 """
 import math
+import time
 
 import numpy as np
 
@@ -262,7 +263,7 @@ def check_offsets(chunks, offsets):
 
 
 def blend(weights, shape, x0, chunks, offsets, n_suffix, sched, dev_mode="KV",
-          min_tokens=0, dtype=np.float64, n_layers=None):
+          min_tokens=0, dtype=np.float64, n_layers=None, timings=None):
     """Fuse independently precomputed chunk KVs with selective recompute.
 
     weights: per-layer dicts; x0: [N][d] embeddings of all prompt tokens in
@@ -273,7 +274,8 @@ def blend(weights, shape, x0, chunks, offsets, n_suffix, sched, dev_mode="KV",
     Returns a dict with fused_k/fused_v [L][N][Hkv][dh], sel (list of kept
     chunk positions per layer, ascending), dev [L][N_c] (NaN where not
     measured), layer_pos/layer_out (rows and outputs of every layer), hidden
-    (final rows).
+    (final rows).  When `timings` is a list, the wall time of every layer is
+    appended to it (seconds); the arithmetic is unaffected.
     """
     L = shape.n_layers if n_layers is None else n_layers
     W = _cast_weights(weights[:L], dtype)
@@ -296,6 +298,7 @@ def blend(weights, shape, x0, chunks, offsets, n_suffix, sched, dev_mode="KV",
     x = x0[np.concatenate([C, suffix])]
     sel, layer_pos, layer_out = [], [], []
     for l in range(L):
+        t_start = time.perf_counter()
         R = np.concatenate([C, suffix])            # Step 1: rows recomputed here
         q, k, v = qkv_rows(W[l], shape, x, R)      # Step 2
         nC = len(C)
@@ -316,6 +319,8 @@ def blend(weights, shape, x0, chunks, offsets, n_suffix, sched, dev_mode="KV",
         sel.append(C.copy())
         layer_pos.append(P)
         layer_out.append(x)
+        if timings is not None:
+            timings.append(time.perf_counter() - t_start)
     return {"fused_k": fk, "fused_v": fv, "sel": sel, "dev": dev,
             "layer_pos": layer_pos, "layer_out": layer_out, "hidden": x,
             "schedule": sched}
