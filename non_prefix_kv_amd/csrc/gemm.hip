@@ -41,16 +41,15 @@ __device__ __forceinline__ int xcd_remap(int hw, int total) {
     return xcd * base + min(xcd, rem) + j;
 }
 
+// Row v (0..BN-1) of the block's B tile.  Rows past N are clamped to the
+// last row: they only feed output columns that are never stored.
 template <typename T, int EPI>
 __device__ __forceinline__ const T* b_row_ptr(const GemmArgs& g, int v, int n_tile) {
-    // v: row of the block's B tile (0..BN-1)
     if (EPI == EPI_SWIGLU) {
-        const int oc = n_tile * (BN / 2) + (v >> 5) * 16 + (v & 15);
-        if (oc >= g.N) return nullptr;
+        const int oc = min(n_tile * (BN / 2) + (v >> 5) * 16 + (v & 15), g.N - 1);
         return static_cast<const T*>((v & 16) ? g.b1 : g.b0) + (int64_t)oc * g.K;
     } else {
-        const int n = n_tile * BN + v;
-        if (n >= g.N) return nullptr;
+        const int n = min(n_tile * BN + v, g.N - 1);
         if (EPI == EPI_QKV) {
             if (n < g.n0) return static_cast<const T*>(g.b0) + (int64_t)n * g.K;
             if (n < g.n0 + g.n1) return static_cast<const T*>(g.b1) + (int64_t)(n - g.n0) * g.K;
@@ -86,19 +85,21 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
         const int r = ld_row + 32 * p;
         const int m = min(m_tile * BM + r, g.M - 1);
         a_src[p] = static_cast<const T*>(g.a) + (int64_t)m * g.K + ld_col;
-        const T* b = b_row_ptr<T, EPI>(g, r, n_tile);
-        b_src[p] = b ? b + ld_col : nullptr;
+        b_src[p] = b_row_ptr<T, EPI>(g, r, n_tile) + ld_col;
     }
-    u32x4 ra[4], rb[4];
-    auto load_stage = [&](int kt) {
+    // Two register stage sets: while stage kt is multiplied out of LDS,
+    // stage kt+1 waits in registers for its LDS store and stage kt+2 is in
+    // flight from memory (prefetch distance 2 hides global latency).
+    u32x4 sa0[4], sb0[4], sa1[4], sb1[4];
+    auto load_stage = [&](int kt, u32x4 (&ra)[4], u32x4 (&rb)[4]) {
         const int ko = kt * BK;
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             ra[p] = *reinterpret_cast<const u32x4*>(a_src[p] + ko);
-            rb[p] = b_src[p] ? *reinterpret_cast<const u32x4*>(b_src[p] + ko) : u32x4{0, 0, 0, 0};
+            rb[p] = *reinterpret_cast<const u32x4*>(b_src[p] + ko);
         }
     };
-    auto store_stage = [&](int buf) {
+    auto store_stage = [&](int buf, const u32x4 (&ra)[4], const u32x4 (&rb)[4]) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
             const int r = ld_row + 32 * p;
@@ -114,29 +115,59 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
 
     const int KT = g.K / BK;
-    load_stage(0);
-    store_stage(0);
-    __syncthreads();
     const int fr = lane & 15, fk = (lane >> 4) * 8;
-    for (int kt = 0; kt < KT; ++kt) {
-        const int cur = kt & 1;
-        if (kt + 1 < KT) load_stage(kt + 1);
+    auto compute = [&](int buf) {
 #pragma unroll
         for (int ks = 0; ks < BK; ks += 32) {
             Frag<T> af[4], bfr[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                af[i] = load_frag<T>(&sA[cur][(wm * 64 + i * 16 + fr) * LDK + ks + fk]);
+                af[i] = load_frag<T>(&sA[buf][(wm * 64 + i * 16 + fr) * LDK + ks + fk]);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                bfr[j] = load_frag<T>(&sB[cur][(wn * 64 + j * 16 + fr) * LDK + ks + fk]);
+                bfr[j] = load_frag<T>(&sB[buf][(wn * 64 + j * 16 + fr) * LDK + ks + fk]);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) mfma16(acc[i][j], af[i], bfr[j]);
         }
-        if (kt + 1 < KT) store_stage(cur ^ 1);
+    };
+    // Steady state, unrolled by two so buffers and register sets are static:
+    // on entry stage kt is in LDS buffer 0 and stage kt+1 in set 1.
+    load_stage(0, sa0, sb0);
+    if (KT > 1) load_stage(1, sa1, sb1);
+    store_stage(0, sa0, sb0);
+    __syncthreads();
+    int kt = 0;
+    for (; kt + 3 < KT; kt += 2) {
+        load_stage(kt + 2, sa0, sb0);
+        __builtin_amdgcn_sched_barrier(0);   // issue the loads before the math
+        compute(0);
+        store_stage(1, sa1, sb1);
         __syncthreads();
+        load_stage(kt + 3, sa1, sb1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1);
+        store_stage(0, sa0, sb0);
+        __syncthreads();
+    }
+    // One to three stages remain.
+    if (kt + 2 < KT) {
+        load_stage(kt + 2, sa0, sb0);
+        compute(0);
+        store_stage(1, sa1, sb1);
+        __syncthreads();
+        compute(1);
+        store_stage(0, sa0, sb0);
+        __syncthreads();
+        compute(0);
+    } else if (kt + 1 < KT) {
+        compute(0);
+        store_stage(1, sa1, sb1);
+        __syncthreads();
+        compute(1);
+    } else {
+        compute(0);
     }
 
     // Epilogue.  acc[i][j][e] = C[row][col] with
