@@ -15,6 +15,8 @@
 // through LDS.  Blocks whose keys all lie after a wave's last query position
 // are skipped by that wave; blocks after the workgroup's last position are
 // never loaded.  Tiles are issued longest-first.
+#include <climits>
+
 #include "kernels.h"
 
 namespace cb {
@@ -45,8 +47,24 @@ __device__ __forceinline__ Frag<float> load_quad_pair(const float* p) {
     return f;
 }
 
+// Four keys of one V column packed for a single LDS store (sVt is [d][key]);
+// rows[q] holds 16 bytes of key q.  Element extraction by shifts keeps the
+// staging registers out of memory.
+__device__ __forceinline__ uint32_t bf16_bits(const u32x4& r, int i) {
+    return (r[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+}
+__device__ __forceinline__ void store_vt4(bf16* dst, const u32x4 (&rows)[4], int i) {
+    const u32x2 w{bf16_bits(rows[0], i) | (bf16_bits(rows[1], i) << 16),
+                  bf16_bits(rows[2], i) | (bf16_bits(rows[3], i) << 16)};
+    *reinterpret_cast<u32x2*>(dst) = w;
+}
+__device__ __forceinline__ void store_vt4(float* dst, const u32x4 (&rows)[4], int i) {
+    const u32x4 w{rows[0][i], rows[1][i], rows[2][i], rows[3][i]};
+    *reinterpret_cast<u32x4*>(dst) = w;
+}
+
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
     constexpr int KB = AttnCfg<T>::KB;
     constexpr int LDK = D + 16 / (int)sizeof(T);        // sK row stride (elements)
     constexpr int LDV = KB + 4;                          // sVt row stride (elements)
@@ -54,9 +72,13 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
     constexpr int NKS = KB / 32;                         // 32-key MFMA steps per block
     constexpr int NDS = D / 32;                          // 32-dim steps for S
     constexpr int NDT = D / 16;                          // 16-dim output tiles
-    constexpr int VEC = 16 / (int)sizeof(T);
-    __shared__ __attribute__((aligned(16))) T sK[KB * LDK];
-    __shared__ __attribute__((aligned(16))) T sVt[D * LDV];
+    constexpr int VEC = 16 / (int)sizeof(T);             // elements per 16-byte load
+    constexpr int KU = KB * D / VEC / kThreads;          // K loads per thread per block
+    constexpr int VUNITS = (KB / 4) * (D / VEC);         // V units of 4 keys x VEC dims
+    static_assert(KU >= 1 && KB * D / VEC == KU * kThreads, "K tile split");
+    static_assert(VUNITS <= kThreads, "V tile split");
+    __shared__ __attribute__((aligned(16))) T sK[2][KB * LDK];
+    __shared__ __attribute__((aligned(16))) T sVt[2][D * LDV];
     __shared__ int sred[2][kThreads / 64];
 
     const int n_tiles = (a.n_q + QT - 1) / QT;
@@ -102,23 +124,45 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
 
     const T* kbase = static_cast<const T*>(a.k) + hk * D;
     const T* vbase = static_cast<const T*>(a.v) + hk * D;
-    for (int kb = 0; kb < n_kb; ++kb) {
+    // Register staging of the next key block: K as KU 16-byte pieces of
+    // single rows, V as 4 rows x 16 bytes so the transposed LDS image can be
+    // written 4 keys at a time.  Rows past n_kv are clamped to the last key:
+    // their scores are masked and the finite values they hold meet p = 0.
+    u32x4 rk[KU], rv[4];
+    const bool v_unit = tid < VUNITS;
+    const int vr0 = (tid / (D / VEC)) * 4, vc = (tid % (D / VEC)) * VEC;
+    auto load_block = [&](int kb) {
         const int k0 = kb * KB;
-        // K block -> sK (row-major), V block -> sVt (transposed); rows past
-        // n_kv are zero so masked probabilities never meet garbage values.
-        for (int u = tid; u < KB * (D / VEC); u += kThreads) {
-            const int r = u / (D / VEC), c = (u % (D / VEC)) * VEC;
-            const bool ok = k0 + r < a.n_kv;
-            u32x4 kv = ok ? *reinterpret_cast<const u32x4*>(kbase + (int64_t)(k0 + r) * kv_ld + c)
-                          : u32x4{0, 0, 0, 0};
-            *reinterpret_cast<u32x4*>(&sK[r * LDK + c]) = kv;
-            u32x4 vv = ok ? *reinterpret_cast<const u32x4*>(vbase + (int64_t)(k0 + r) * kv_ld + c)
-                          : u32x4{0, 0, 0, 0};
-            const T* ve = reinterpret_cast<const T*>(&vv);
 #pragma unroll
-            for (int i = 0; i < VEC; ++i) sVt[(c + i) * LDV + r] = ve[i];
+        for (int j = 0; j < KU; ++j) {
+            const int u = tid + j * kThreads;
+            const int r = u / (D / VEC), c = (u % (D / VEC)) * VEC;
+            const int kr = min(k0 + r, a.n_kv - 1);
+            rk[j] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)kr * kv_ld + c);
         }
-        __syncthreads();
+        if (v_unit) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int vr = min(k0 + vr0 + q, a.n_kv - 1);
+                rv[q] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)vr * kv_ld + vc);
+            }
+        }
+    };
+    auto store_block = [&](int buf) {
+#pragma unroll
+        for (int j = 0; j < KU; ++j) {
+            const int u = tid + j * kThreads;
+            const int r = u / (D / VEC), c = (u % (D / VEC)) * VEC;
+            *reinterpret_cast<u32x4*>(&sK[buf][r * LDK + c]) = rk[j];
+        }
+        if (v_unit) {
+#pragma unroll
+            for (int i = 0; i < VEC; ++i) store_vt4(&sVt[buf][(vc + i) * LDV + vr0], rv, i);
+        }
+    };
+
+    auto compute = [&](int cur, int kb) {
+        const int k0 = kb * KB;
         if (a.kv_pos0 + k0 <= wmax) {     // wave-uniform: some key visible to this wave
             floatx4 st[NKT];
 #pragma unroll
@@ -126,7 +170,7 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
                 st[t] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int s = 0; s < NDS; ++s) {
-                    Frag<T> kf = load_frag<T>(&sK[(t * 16 + fr) * LDK + s * 32 + g * 8]);
+                    Frag<T> kf = load_frag<T>(&sK[cur][(t * 16 + fr) * LDK + s * 32 + g * 8]);
                     mfma16(st[t], kf, qf[s]);
                 }
             }
@@ -167,12 +211,41 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
             for (int dt = 0; dt < NDT; ++dt) {
 #pragma unroll
                 for (int s2 = 0; s2 < NKS; ++s2) {
-                    const T* vr = &sVt[(dt * 16 + fr) * LDV + s2 * 32 + g * 4];
+                    const T* vr = &sVt[cur][(dt * 16 + fr) * LDV + s2 * 32 + g * 4];
                     mfma16(o[dt], load_quad_pair(vr), pf[s2]);
                 }
             }
         }
+    };
+    // Steady state unrolled by two (static LDS buffers): on entry block kb is
+    // in buffer 0; block kb+1 is fetched into registers during the math.
+    if (n_kb > 0) {
+        load_block(0);
+        store_block(0);
+    }
+    __syncthreads();
+    int kb = 0;
+    for (; kb + 2 < n_kb; kb += 2) {
+        load_block(kb + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(0, kb);
+        store_block(1);
         __syncthreads();
+        load_block(kb + 2);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1, kb + 1);
+        store_block(0);
+        __syncthreads();
+    }
+    if (kb + 1 < n_kb) {
+        load_block(kb + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(0, kb);
+        store_block(1);
+        __syncthreads();
+        compute(1, kb + 1);
+    } else if (kb < n_kb) {
+        compute(0, kb);
     }
     float l_tot = l_run + __shfl_xor(l_run, 16, 64);
     l_tot += __shfl_xor(l_tot, 32, 64);
@@ -185,6 +258,319 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e) op[dt * 16 + g * 4 + e] = from_f32<T>(o[dt][e] * inv);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 path: 32 queries per wave on 32x32x16 MFMAs.  Each K or V fragment
+// read from LDS now feeds a 32x32 output tile, halving LDS bytes per flop
+// relative to 16-query waves.  Two waves per workgroup (64 queries of one
+// head), 32-key blocks double-buffered in LDS with the next block prefetched
+// into registers.  Layout of v_mfma_f32_32x32x16_bf16: lane l supplies row
+// (l % 32) of A and column (l % 32) of B with reduction elements
+// 8 * (l / 32) + 0..7; accumulator element i of lane l is
+// C[8 * (i / 4) + 4 * (l / 32) + i % 4][l % 32].
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ void mfma32(floatx16& acc, const bf16x8& a, const bf16x8& b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+
+constexpr int kT32 = 256;   // threads per workgroup (4 waves)
+constexpr int QT32 = 128;   // queries per workgroup
+constexpr int KB32 = 32;    // keys per block
+
+// Hardware workgroup ids are dealt round-robin over the 8 XCDs; renumber so
+// each XCD gets a contiguous logical range (blocks that read the same key
+// segment of the same head then share one L2).
+__device__ __forceinline__ int xcd_order(int hw, int total) {
+    const int xcd = hw & 7, j = hw >> 3;
+    const int base = total >> 3, rem = total & 7;
+    return xcd * base + min(xcd, rem) + j;
+}
+
+template <int D>
+__global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a) {
+    constexpr int LDK = D + 8;                 // sK row stride (elements)
+    constexpr int LDV = KB32 + 4;              // sVt row stride (elements)
+    constexpr int NDS = D / 16;                // 16-dim reduction steps for S
+    constexpr int NDT = D / 32;                // 32-dim output tiles
+    constexpr int KU = KB32 * D / 8 / kT32;    // 16-byte K pieces per thread
+    constexpr int VUNITS = (KB32 / 4) * (D / 8);
+    static_assert(KU >= 1 && KB32 * D / 8 == KU * kT32, "K tile split");
+    static_assert(VUNITS <= kT32, "V tile split");
+    __shared__ __attribute__((aligned(16))) bf16 sK[2][KB32 * LDK];
+    __shared__ __attribute__((aligned(16))) bf16 sVt[2][D * LDV];
+    __shared__ int sred[kT32 / 64];
+
+    // logical id -> (tile, segment, head), tile fastest, longest tiles first
+    const int n_tiles = (a.n_q + QT32 - 1) / QT32;
+    const int n_segs = a.seg_keys > 0 ? a.max_seg : 1;
+    const int logical = xcd_order(blockIdx.x, n_tiles * n_segs * a.n_q_heads);
+    const int qt = n_tiles - 1 - logical % n_tiles;
+    const int seg = (logical / n_tiles) % n_segs;
+    const int h = logical / (n_tiles * n_segs);
+    const int hk = h / (a.n_q_heads / a.n_kv_heads);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int fr = lane & 31, g = lane >> 5;
+    const int q_ld = a.n_q_heads * D, kv_ld = a.n_kv_heads * D;
+
+    const int qi_raw = qt * QT32 + wave * 32 + fr;
+    const bool q_ok = qi_raw < a.n_q;
+    const int qi = q_ok ? qi_raw : a.n_q - 1;
+    const int qpos = a.q_pos[qi];
+    int wmax = qpos, wmin = qpos;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+        wmax = max(wmax, __shfl_xor(wmax, o, 64));
+        wmin = min(wmin, __shfl_xor(wmin, o, 64));
+    }
+    if (lane == 0) sred[wave] = wmax;
+    __syncthreads();
+    int bmax = sred[0];
+#pragma unroll
+    for (int w = 1; w < kT32 / 64; ++w) bmax = max(bmax, sred[w]);
+    const int nk = min(a.n_kv, bmax - a.kv_pos0 + 1);
+    // Key segment of this workgroup (whole range when not split).
+    const int n_seg = a.seg_keys > 0 ? max(1, (nk + a.seg_keys - 1) / a.seg_keys) : 1;
+    if (seg >= n_seg) return;                          // uniform over the workgroup
+    const int kb_beg = a.seg_keys > 0 ? seg * (a.seg_keys / KB32) : 0;
+    const int k_end = a.seg_keys > 0 ? min(nk, (seg + 1) * a.seg_keys) : nk;
+    const int n_kb = k_end > kb_beg * KB32 ? (k_end - kb_beg * KB32 + KB32 - 1) / KB32 : 0;
+
+    const int qrow = a.qidx ? a.qidx[qi] : qi;
+    const bf16* qp = static_cast<const bf16*>(a.q) + (int64_t)qrow * q_ld + h * D;
+    bf16x8 qf[NDS];
+#pragma unroll
+    for (int s = 0; s < NDS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + s * 16 + g * 8);
+
+    floatx16 o[NDT];
+#pragma unroll
+    for (int t = 0; t < NDT; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
+    const float sl2 = 1.4426950408889634f / sqrtf((float)D);
+
+    const bf16* kbase = static_cast<const bf16*>(a.k) + hk * D;
+    const bf16* vbase = static_cast<const bf16*>(a.v) + hk * D;
+    // Two register stage sets (prefetch distance 2).  V unit = 4 keys x 8
+    // dims; consecutive lanes step over keys first so the transposed 8-byte
+    // LDS stores of 16 lanes fill 32 distinct banks.  Rows past n_kv are
+    // clamped to the last key: their scores are masked.
+    const bool v_unit = tid < VUNITS;
+    const int vr0 = (tid % (KB32 / 4)) * 4, vc = (tid / (KB32 / 4)) * 8;
+    u32x4 rk0[KU], rv0[4], rk1[KU], rv1[4];
+    auto load_block = [&](int kb, u32x4 (&rk)[KU], u32x4 (&rv)[4]) {
+        const int k0 = (kb_beg + kb) * KB32;
+#pragma unroll
+        for (int j = 0; j < KU; ++j) {
+            const int u = tid + j * kT32;
+            const int r = u / (D / 8), c = (u % (D / 8)) * 8;
+            const int kr = min(k0 + r, a.n_kv - 1);
+            rk[j] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)kr * kv_ld + c);
+        }
+        if (v_unit) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int vr = min(k0 + vr0 + q, a.n_kv - 1);
+                rv[q] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)vr * kv_ld + vc);
+            }
+        }
+    };
+    auto store_block = [&](int buf, const u32x4 (&rk)[KU], const u32x4 (&rv)[4]) {
+#pragma unroll
+        for (int j = 0; j < KU; ++j) {
+            const int u = tid + j * kT32;
+            const int r = u / (D / 8), c = (u % (D / 8)) * 8;
+            *reinterpret_cast<u32x4*>(&sK[buf][r * LDK + c]) = rk[j];
+        }
+        if (v_unit) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) store_vt4(&sVt[buf][(vc + i) * LDV + vr0], rv, i);
+        }
+    };
+    auto compute = [&](int cur, int kb) {
+        const int k0 = (kb_beg + kb) * KB32;
+        if (a.kv_pos0 + k0 > wmax) return;          // wave-uniform: nothing visible
+        floatx16 st;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) st[i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NDS; ++s) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[cur][fr * LDK + s * 16 + g * 8]);
+            mfma32(st, kf, qf[s]);
+        }
+        const bool need_mask = (k0 + KB32 > a.n_kv) || (a.kv_pos0 + k0 + KB32 - 1 > wmin);
+        float mloc = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float sc = st[i] * sl2;
+            if (need_mask) {
+                const int kj = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
+                if (kj >= a.n_kv || a.kv_pos0 + kj > qpos) sc = -INFINITY;
+            }
+            st[i] = sc;
+            mloc = fmaxf(mloc, sc);
+        }
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        const float m_new = fmaxf(m_run, mloc);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = exp2f(m_run - m_use);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int t = 0; t < NDT; ++t) o[t] *= alpha;
+        bf16x8 pf[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p = exp2f(st[i] - m_use);
+            l_run += p;
+            pf[i >> 3][i & 7] = static_cast<bf16>(p);
+        }
+        // P^T slot j of half hh holds key 16 hh + 8 (j / 4) + 4 g + j % 4.
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const bf16* vr = &sVt[cur][(dt * 32 + fr) * LDV + hh * 16 + g * 4];
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
+                const u32x4 w{lo[0], lo[1], hi[0], hi[1]};
+                mfma32(o[dt], __builtin_bit_cast(bf16x8, w), pf[hh]);
+            }
+    };
+    // Steady state unrolled by two: on entry block kb is in LDS buffer 0 and
+    // block kb+1 in register set 1; block kb+2 is fetched during the math.
+    if (n_kb > 0) load_block(0, rk0, rv0);
+    if (n_kb > 1) load_block(1, rk1, rv1);
+    if (n_kb > 0) store_block(0, rk0, rv0);
+    __syncthreads();
+    int kb = 0;
+    for (; kb + 3 < n_kb; kb += 2) {
+        load_block(kb + 2, rk0, rv0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(0, kb);
+        store_block(1, rk1, rv1);
+        __syncthreads();
+        load_block(kb + 3, rk1, rv1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1, kb + 1);
+        store_block(0, rk0, rv0);
+        __syncthreads();
+    }
+    if (kb + 2 < n_kb) {
+        load_block(kb + 2, rk0, rv0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(0, kb);
+        store_block(1, rk1, rv1);
+        __syncthreads();
+        compute(1, kb + 1);
+        store_block(0, rk0, rv0);
+        __syncthreads();
+        compute(0, kb + 2);
+    } else if (kb + 1 < n_kb) {
+        compute(0, kb);
+        store_block(1, rk1, rv1);
+        __syncthreads();
+        compute(1, kb + 1);
+    } else if (kb < n_kb) {
+        compute(0, kb);
+    }
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (n_seg > 1) {
+        // Partial of this segment: unnormalized O, running max (log2 units) and sum.
+        const int64_t slot = ((int64_t)qt * a.n_q_heads + h) * a.max_seg + seg;
+        const int ql = wave * 32 + fr;
+        float* po = a.part_o + (slot * QT32 + ql) * D;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+            for (int i4 = 0; i4 < 4; ++i4)
+                *reinterpret_cast<floatx4*>(po + dt * 32 + 8 * i4 + 4 * g) =
+                    floatx4{o[dt][i4 * 4], o[dt][i4 * 4 + 1], o[dt][i4 * 4 + 2], o[dt][i4 * 4 + 3]};
+        if (g == 0) {
+            float* pm = a.part_ml + (slot * QT32 + ql) * 2;
+            pm[0] = m_run;
+            pm[1] = l_tot;
+        }
+        return;
+    }
+    if (!q_ok) return;
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    bf16* op = static_cast<bf16*>(a.out) + (int64_t)qi * q_ld + h * D;
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+            bf16x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = static_cast<bf16>(o[dt][i4 * 4 + e] * inv);
+            *reinterpret_cast<bf16x4*>(op + dt * 32 + 8 * i4 + 4 * g) = v;
+        }
+}
+
+// Merges the segment partials of split tiles: with per-segment max m_s and
+// sum l_s, O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
+// Tiles that were not split were finished by their only workgroup.
+template <int D>
+__global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
+    const int n_tiles = (a.n_q + QT32 - 1) / QT32;
+    const int qt = n_tiles - 1 - (int)blockIdx.x;
+    const int h = blockIdx.y;
+    // Same key extent as the attention workgroups of this tile.
+    __shared__ int smax;
+    if (threadIdx.x == 0) smax = INT_MIN;
+    __syncthreads();
+    const int q0 = qt * QT32;
+    const int nq_t = min(QT32, a.n_q - q0);
+    for (int i = threadIdx.x; i < nq_t; i += 256) atomicMax(&smax, a.q_pos[q0 + i]);
+    __syncthreads();
+    const int nk = min(a.n_kv, smax - a.kv_pos0 + 1);
+    const int n_seg = max(1, (nk + a.seg_keys - 1) / a.seg_keys);
+    if (n_seg <= 1) return;
+    const int64_t slot0 = ((int64_t)qt * a.n_q_heads + h) * a.max_seg;
+    constexpr int C4 = D / 4;                       // float4 chunks per query row
+    for (int u = threadIdx.x; u < nq_t * C4; u += 256) {
+        const int ql = u / C4, c = (u % C4) * 4;
+        float M = -INFINITY;
+        for (int sg = 0; sg < n_seg; ++sg)
+            M = fmaxf(M, a.part_ml[((slot0 + sg) * QT32 + ql) * 2]);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        float L = 0.f;
+        floatx4 acc{0.f, 0.f, 0.f, 0.f};
+        for (int sg = 0; sg < n_seg; ++sg) {
+            const float* pm = a.part_ml + ((slot0 + sg) * QT32 + ql) * 2;
+            const float w = exp2f(pm[0] - Mu);
+            L += w * pm[1];
+            acc += w * *reinterpret_cast<const floatx4*>(a.part_o + ((slot0 + sg) * QT32 + ql) * D + c);
+        }
+        const float inv = L > 0.f ? 1.0f / L : 0.f;
+        bf16x4 v{static_cast<bf16>(acc[0] * inv), static_cast<bf16>(acc[1] * inv),
+                 static_cast<bf16>(acc[2] * inv), static_cast<bf16>(acc[3] * inv)};
+        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.out) +
+                                   (int64_t)(q0 + ql) * a.n_q_heads * D + h * D + c) = v;
+    }
+}
+
+template <int D>
+hipError_t launch32(const AttnArgs& a, hipStream_t s) {
+    const int tiles = (a.n_q + QT32 - 1) / QT32;
+    const bool split = a.seg_keys > 0 && a.max_seg > 1;
+    if (split && (a.seg_keys % KB32 || !a.part_o || !a.part_ml ||
+                  (int64_t)a.max_seg * a.seg_keys < a.n_kv))
+        return hipErrorInvalidValue;
+    AttnArgs b = a;
+    if (!split) {
+        b.seg_keys = 0;
+        b.max_seg = 1;
+    }
+    const int64_t blocks = (int64_t)tiles * a.n_q_heads * b.max_seg;
+    if (blocks > INT_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attention32_kernel<D>), dim3((unsigned)blocks), dim3(kT32), 0, s, b);
+    if (split)
+        hipLaunchKernelGGL((attention_combine_kernel<D>), dim3(tiles, a.n_q_heads), dim3(256), 0, s,
+                           b);
+    return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
     dim3 grid((a.n_q + QT - 1) / QT, a.n_q_heads);
@@ -194,13 +580,28 @@ hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
 
 }  // namespace
 
+size_t attention_split_plan(int dtype, int n_q, int n_kv, int n_q_heads, int head_dim,
+                            int* seg_keys, int* max_seg) {
+    *seg_keys = 0;
+    *max_seg = 1;
+    if (dtype != BF16 || n_q <= 0) return 0;
+    const int64_t tiles = (n_q + QT32 - 1) / QT32;
+    // Split only when the plain grid leaves the GPU short of workgroups.
+    if (tiles * n_q_heads >= 2048 || n_kv <= 1024) return 0;
+    const int sk = 512;
+    const int ms = (n_kv + sk - 1) / sk;
+    *seg_keys = sk;
+    *max_seg = ms;
+    return (size_t)tiles * n_q_heads * ms * QT32 * (head_dim + 2) * sizeof(float);
+}
+
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
     if (a.n_q <= 0) return hipSuccess;
     if (a.n_kv_heads <= 0 || a.n_q_heads % a.n_kv_heads != 0) return hipErrorInvalidValue;
     if (a.head_dim == 128)
-        return dtype == BF16 ? launch_t<bf16, 128>(a, s) : launch_t<float, 128>(a, s);
+        return dtype == BF16 ? launch32<128>(a, s) : launch_t<float, 128>(a, s);
     if (a.head_dim == 64)
-        return dtype == BF16 ? launch_t<bf16, 64>(a, s) : launch_t<float, 64>(a, s);
+        return dtype == BF16 ? launch32<64>(a, s) : launch_t<float, 64>(a, s);
     return hipErrorInvalidValue;
 }
 

@@ -121,7 +121,20 @@ struct AttnArgs {
     int kv_pos0;
     int n_q_heads, n_kv_heads, head_dim;
     void* out;          // [n_q][Hq*dh]
+    // Split over keys (bf16 path): query tiles whose visible keys exceed
+    // seg_keys are cut into segments processed by separate workgroups; their
+    // unnormalized partial outputs and (max, sum) go to part_o / part_ml and a
+    // combine pass merges them.  seg_keys = 0 disables splitting.
+    int seg_keys;
+    int max_seg;
+    float* part_o;      // [tiles][Hq][max_seg][64][dh]
+    float* part_ml;     // [tiles][Hq][max_seg][64][2]
 };
 hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
+
+// Split plan for n_q queries over n_kv keys: fills seg_keys / max_seg and
+// returns the workspace bytes the partials need (0 when not split).
+size_t attention_split_plan(int dtype, int n_q, int n_kv, int n_q_heads, int head_dim,
+                            int* seg_keys, int* max_seg);
 
 }  // namespace cb

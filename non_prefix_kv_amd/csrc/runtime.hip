@@ -196,6 +196,8 @@ struct cb_plan {
     void *Hn = nullptr, *Q = nullptr, *Kn = nullptr, *Vn = nullptr, *attn = nullptr,
          *act = nullptr;
     int *pos_a = nullptr, *pos_b = nullptr, *sel_local = nullptr;
+    float* attn_part = nullptr;  // split-attention partials
+    size_t attn_part_bytes = 0;
     std::vector<RotJobs> jobs;   // rotation jobs, 16 chunks per launch
 
     // streams / events
@@ -281,6 +283,15 @@ size_t carve(cb_plan* p, char* base, int max_rows) {
     p->pos_a = (int*)take(R * 4);
     p->pos_b = (int*)take(R * 4);
     p->sel_local = (int*)take(R * 4);
+    // largest split-attention workspace over the query-row counts that occur
+    size_t part = 0;
+    for (int l = 0; l < p->L; ++l) {
+        int sk, ms;
+        part = std::max(part, attention_split_plan(c.dtype, p->s[l + 1] + p->Ns, p->N,
+                                                   c.n_q_heads, c.head_dim, &sk, &ms));
+    }
+    p->attn_part_bytes = part;
+    p->attn_part = part ? (float*)take(part) : nullptr;
     return off;
 }
 
@@ -446,6 +457,13 @@ cb_status do_layer(cb_plan* p, int l) {
         a.k = fk; a.v = fv; a.n_kv = p->N; a.kv_pos0 = p->row_base;
         a.n_q_heads = c.n_q_heads; a.n_kv_heads = c.n_kv_heads; a.head_dim = c.head_dim;
         a.out = p->attn;
+        const size_t need = attention_split_plan(dt, mQ, p->N, c.n_q_heads, c.head_dim,
+                                                 &a.seg_keys, &a.max_seg);
+        if (need > p->attn_part_bytes) return fail(CB_E_OOM, "attention split workspace");
+        if (need) {
+            a.part_o = p->attn_part;
+            a.part_ml = p->attn_part + need / sizeof(float) / (c.head_dim + 2) * c.head_dim;
+        }
         Span sp(m, CB_K_ATTENTION, st, 0, 0);
         CB_HIP(launch_attention(dt, a, st));
     }
@@ -864,7 +882,21 @@ cb_status cb_attention(int32_t dtype, const void* q, const int32_t* q_pos, int32
     AttnArgs a{};
     a.q = q; a.q_pos = q_pos; a.n_q = n_q; a.k = k; a.v = v; a.n_kv = n_kv;
     a.n_q_heads = n_q_heads; a.n_kv_heads = n_kv_heads; a.head_dim = head_dim; a.out = out;
-    CB_HIP(launch_attention(dtype, a, as_stream(stream)));
+    const hipStream_t st = as_stream(stream);
+    const size_t need = attention_split_plan(dtype, n_q, n_kv, n_q_heads, head_dim, &a.seg_keys,
+                                             &a.max_seg);
+    void* ws = nullptr;
+    if (need) {
+        if (hipMallocAsync(&ws, need, st) != hipSuccess) {
+            (void)hipGetLastError();
+            return fail(CB_E_OOM, "attention workspace of %zu bytes", need);
+        }
+        a.part_o = (float*)ws;
+        a.part_ml = (float*)ws + need / sizeof(float) / (head_dim + 2) * head_dim;
+    }
+    const hipError_t e = launch_attention(dtype, a, st);
+    if (ws) (void)hipFreeAsync(ws, st);
+    if (e != hipSuccess) return fail(CB_E_HIP, "attention launch: %s", hipGetErrorString(e));
     return CB_OK;
 }
 

@@ -209,3 +209,16 @@ def test_error_paths(lib, tiny):
     p.prefill_layer(1)
     p.synchronize()
     p.destroy()
+
+
+def test_long_context_bf16_blend_vs_oracle(lib):
+    """A context long enough for the attention to split its keys over several
+    workgroups (segments merged by the combine pass), ragged chunk lengths."""
+    case = make_case(TINY, (500, 403, 611), 61, seed=5, dtype="bf16")
+    model = make_model(lib, case, "bf16")
+    sched = oracle.schedule(case.n_chunk_tokens, 1500, "gradual", TINY.n_layers)
+    gpu = run_gpu_blend(lib, model, case, "bf16", sched)
+    compare(case, gpu, run_blend(case, sched), sched, "bf16")
+    full = [case.n_chunk_tokens] * 3
+    gpu = run_gpu_blend(lib, model, case, "bf16", full)
+    compare(case, gpu, run_blend(case, full), full, "bf16")

@@ -167,7 +167,9 @@ def test_gemm_vs_definition(lib, dt, m, n, k):
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("nq,nkv,hq,hkv,dh", [(1, 1, 1, 1, 64), (23, 90, 4, 4, 64),
                                               (70, 416, 4, 2, 64), (200, 1000, 8, 1, 128),
-                                              (832, 4096, 4, 4, 128), (129, 129, 2, 2, 128)])
+                                              (832, 4096, 4, 4, 128), (129, 129, 2, 2, 128),
+                                              (1, 3000, 2, 1, 128), (300, 2500, 4, 2, 64),
+                                              (64, 1025, 3, 3, 128)])
 def test_attention_vs_oracle(lib, dt, nq, nkv, hq, hkv, dh):
     rng = np.random.default_rng(nq + nkv)
     qpos = np.sort(rng.choice(nkv, size=nq, replace=False))
