@@ -398,30 +398,33 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a) {
             const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[cur][fr * LDK + s * 16 + g * 8]);
             mfma32(st, kf, qf[s]);
         }
+        // Scores stay unscaled; the running max is kept in scaled (log2)
+        // units and the scale is folded into one FMA before v_exp_f32.
         const bool need_mask = (k0 + KB32 > a.n_kv) || (a.kv_pos0 + k0 + KB32 - 1 > wmin);
-        float mloc = -INFINITY;
+        if (need_mask) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float sc = st[i] * sl2;
-            if (need_mask) {
+            for (int i = 0; i < 16; ++i) {
                 const int kj = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
-                if (kj >= a.n_kv || a.kv_pos0 + kj > qpos) sc = -INFINITY;
+                if (kj >= a.n_kv || a.kv_pos0 + kj > qpos) st[i] = -INFINITY;
             }
-            st[i] = sc;
-            mloc = fmaxf(mloc, sc);
         }
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+        float mloc = st[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, st[i]);
+        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * sl2;
         const float m_new = fmaxf(m_run, mloc);
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = exp2f(m_run - m_use);
-        m_run = m_new;
-        l_run *= alpha;
+        if (__ballot(m_new != m_run)) {           // rescale only when some max moved
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+            l_run *= alpha;
 #pragma unroll
-        for (int t = 0; t < NDT; ++t) o[t] *= alpha;
+            for (int t = 0; t < NDT; ++t) o[t] *= alpha;
+        }
+        m_run = m_new;
         bf16x8 pf[2];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const float p = exp2f(st[i] - m_use);
+            const float p = __builtin_amdgcn_exp2f(fmaf(st[i], sl2, -m_use));
             l_run += p;
             pf[i >> 3][i & 7] = static_cast<bf16>(p);
         }
@@ -509,45 +512,54 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a) {
 
 // Merges the segment partials of split tiles: with per-segment max m_s and
 // sum l_s, O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
-// Tiles that were not split were finished by their only workgroup.
+// Tiles that were not split were finished by their only workgroup.  One
+// thread per (query, 4 output dims); workgroups cover 8 queries of one tile
+// and head, so the merge is spread over the whole GPU.
+constexpr int kCombQ = 8;
 template <int D>
 __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
+    constexpr int C4 = D / 4;                       // float4 chunks per query row
     const int n_tiles = (a.n_q + QT32 - 1) / QT32;
-    const int qt = n_tiles - 1 - (int)blockIdx.x;
+    const int per_tile = QT32 / kCombQ;
+    const int qt = blockIdx.x / per_tile, qg = blockIdx.x % per_tile;
     const int h = blockIdx.y;
-    // Same key extent as the attention workgroups of this tile.
-    __shared__ int smax;
-    if (threadIdx.x == 0) smax = INT_MIN;
-    __syncthreads();
     const int q0 = qt * QT32;
     const int nq_t = min(QT32, a.n_q - q0);
-    for (int i = threadIdx.x; i < nq_t; i += 256) atomicMax(&smax, a.q_pos[q0 + i]);
+    if (qg * kCombQ >= nq_t) return;
+    // key extent of the tile, as seen by its attention workgroups
+    __shared__ int wmx[4];
+    int mx = INT_MIN;
+    for (int i = threadIdx.x; i < nq_t; i += 256) mx = max(mx, a.q_pos[q0 + i]);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) mx = max(mx, __shfl_xor(mx, o, 64));
+    if ((threadIdx.x & 63) == 0) wmx[threadIdx.x >> 6] = mx;
     __syncthreads();
-    const int nk = min(a.n_kv, smax - a.kv_pos0 + 1);
+    mx = max(max(wmx[0], wmx[1]), max(wmx[2], wmx[3]));
+    const int nk = min(a.n_kv, mx - a.kv_pos0 + 1);
     const int n_seg = max(1, (nk + a.seg_keys - 1) / a.seg_keys);
     if (n_seg <= 1) return;
+    (void)n_tiles;
+    const int ql = qg * kCombQ + (int)threadIdx.x / C4;
+    const int c = ((int)threadIdx.x % C4) * 4;
+    if ((int)threadIdx.x >= kCombQ * C4 || ql >= nq_t) return;
     const int64_t slot0 = ((int64_t)qt * a.n_q_heads + h) * a.max_seg;
-    constexpr int C4 = D / 4;                       // float4 chunks per query row
-    for (int u = threadIdx.x; u < nq_t * C4; u += 256) {
-        const int ql = u / C4, c = (u % C4) * 4;
-        float M = -INFINITY;
-        for (int sg = 0; sg < n_seg; ++sg)
-            M = fmaxf(M, a.part_ml[((slot0 + sg) * QT32 + ql) * 2]);
-        const float Mu = M == -INFINITY ? 0.f : M;
-        float L = 0.f;
-        floatx4 acc{0.f, 0.f, 0.f, 0.f};
-        for (int sg = 0; sg < n_seg; ++sg) {
-            const float* pm = a.part_ml + ((slot0 + sg) * QT32 + ql) * 2;
-            const float w = exp2f(pm[0] - Mu);
-            L += w * pm[1];
-            acc += w * *reinterpret_cast<const floatx4*>(a.part_o + ((slot0 + sg) * QT32 + ql) * D + c);
-        }
-        const float inv = L > 0.f ? 1.0f / L : 0.f;
-        bf16x4 v{static_cast<bf16>(acc[0] * inv), static_cast<bf16>(acc[1] * inv),
-                 static_cast<bf16>(acc[2] * inv), static_cast<bf16>(acc[3] * inv)};
-        *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.out) +
-                                   (int64_t)(q0 + ql) * a.n_q_heads * D + h * D + c) = v;
+    float M = -INFINITY;
+    for (int sg = 0; sg < n_seg; ++sg)
+        M = fmaxf(M, a.part_ml[((slot0 + sg) * QT32 + ql) * 2]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float L = 0.f;
+    floatx4 acc{0.f, 0.f, 0.f, 0.f};
+    for (int sg = 0; sg < n_seg; ++sg) {
+        const float* pm = a.part_ml + ((slot0 + sg) * QT32 + ql) * 2;
+        const float w = __builtin_amdgcn_exp2f(pm[0] - Mu);
+        L += w * pm[1];
+        acc += w * *reinterpret_cast<const floatx4*>(a.part_o + ((slot0 + sg) * QT32 + ql) * D + c);
     }
+    const float inv = L > 0.f ? 1.0f / L : 0.f;
+    bf16x4 v{static_cast<bf16>(acc[0] * inv), static_cast<bf16>(acc[1] * inv),
+             static_cast<bf16>(acc[2] * inv), static_cast<bf16>(acc[3] * inv)};
+    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.out) +
+                               (int64_t)(q0 + ql) * a.n_q_heads * D + h * D + c) = v;
 }
 
 template <int D>
@@ -566,8 +578,8 @@ hipError_t launch32(const AttnArgs& a, hipStream_t s) {
     if (blocks > INT_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attention32_kernel<D>), dim3((unsigned)blocks), dim3(kT32), 0, s, b);
     if (split)
-        hipLaunchKernelGGL((attention_combine_kernel<D>), dim3(tiles, a.n_q_heads), dim3(256), 0, s,
-                           b);
+        hipLaunchKernelGGL((attention_combine_kernel<D>), dim3(tiles * (QT32 / kCombQ), a.n_q_heads),
+                           dim3(256), 0, s, b);
     return hipGetLastError();
 }
 

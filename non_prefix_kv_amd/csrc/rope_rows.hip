@@ -149,6 +149,45 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_kernel(
     }
 }
 
+// Row held in registers (8 consecutive elements per thread and step, up to
+// 4 steps = 8192 elements): one read of x, one write of y.
+template <typename TX, typename TY>
+__global__ __launch_bounds__(kThreads) void rmsnorm_vec_kernel(
+    const TX* __restrict__ x, const int* __restrict__ idx, const TY* __restrict__ g,
+    TY* __restrict__ y, float* __restrict__ xc, int d, float eps) {
+    constexpr int MAXV = 4;
+    __shared__ float red[kThreads / 64];
+    const int r = blockIdx.x;
+    const TX* xr = x + (int64_t)(idx ? idx[r] : r) * d;
+    float v[MAXV][8];
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+        const int c = (k * kThreads + threadIdx.x) * 8;
+        if (c < d) {
+            Vec8<TX>::load(xr + c, v[k]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) ss += v[k][i] * v[k][i];
+        }
+    }
+    ss = block_sum(ss, red);
+    const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+    TY* yr = y + (int64_t)r * d;
+    float* xcr = xc ? xc + (int64_t)r * d : nullptr;
+#pragma unroll
+    for (int k = 0; k < MAXV; ++k) {
+        const int c = (k * kThreads + threadIdx.x) * 8;
+        if (c < d) {
+            float gv[8], o[8];
+            Vec8<TY>::load(g + c, gv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[i] = v[k][i] * inv * gv[i];
+            Vec8<TY>::store(yr + c, o);
+            if (xcr) Vec8<float>::store(xcr + c, v[k]);
+        }
+    }
+}
+
 __global__ void iota_kernel(int* p, int n, int base) {
     const int i = blockIdx.x * kThreads + threadIdx.x;
     if (i < n) p[i] = base + i;
@@ -221,6 +260,24 @@ hipError_t launch_rmsnorm(int x_dtype, const void* x, const int* idx, int y_dtyp
                           hipStream_t s) {
     if (rows <= 0) return hipSuccess;
     dim3 grid(rows), block(kThreads);
+    const bool vec = d % 8 == 0 && d <= 4 * kThreads * 8 && ((uintptr_t)x % 16) == 0 &&
+                     ((uintptr_t)g % 16) == 0 && ((uintptr_t)y % 16) == 0 &&
+                     ((uintptr_t)x_copy % 16) == 0;
+    if (vec) {
+        if (x_dtype == F32 && y_dtype == F32)
+            hipLaunchKernelGGL((rmsnorm_vec_kernel<float, float>), grid, block, 0, s,
+                               (const float*)x, idx, (const float*)g, (float*)y, x_copy, d, eps);
+        else if (x_dtype == F32 && y_dtype == BF16)
+            hipLaunchKernelGGL((rmsnorm_vec_kernel<float, bf16>), grid, block, 0, s,
+                               (const float*)x, idx, (const bf16*)g, (bf16*)y, x_copy, d, eps);
+        else if (x_dtype == BF16 && y_dtype == BF16)
+            hipLaunchKernelGGL((rmsnorm_vec_kernel<bf16, bf16>), grid, block, 0, s,
+                               (const bf16*)x, idx, (const bf16*)g, (bf16*)y, x_copy, d, eps);
+        else
+            hipLaunchKernelGGL((rmsnorm_vec_kernel<bf16, float>), grid, block, 0, s,
+                               (const bf16*)x, idx, (const float*)g, (float*)y, x_copy, d, eps);
+        return hipGetLastError();
+    }
     if (x_dtype == F32 && y_dtype == F32)
         hipLaunchKernelGGL((rmsnorm_kernel<float, float>), grid, block, 0, s, (const float*)x,
                            idx, (const float*)g, (float*)y, x_copy, d, eps);
