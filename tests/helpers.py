@@ -30,10 +30,12 @@ class Case:
         return self.n_chunk_tokens + self.n_suffix
 
 
-def make_case(shape, chunk_lens, n_suffix, seed=0, dtype="f64", n_layers=None):
+def make_case(shape, chunk_lens, n_suffix, seed=0, dtype="f64", n_layers=None,
+              precompute_dtype=np.float64):
     """Weights/x0 drawn from the seeded generators and rounded to `dtype`;
     chunk KVs precomputed by the oracle alone at chunk-local positions and
-    rounded to `dtype` as a stored cache would be."""
+    rounded to `dtype` as a stored cache would be (`precompute_dtype` only
+    sets the arithmetic of that precompute, e.g. float32 at full width)."""
     L = shape.n_layers if n_layers is None else n_layers
     if L != shape.n_layers:
         shape = dataclasses.replace(shape, n_layers=L)
@@ -43,7 +45,7 @@ def make_case(shape, chunk_lens, n_suffix, seed=0, dtype="f64", n_layers=None):
     x0 = emb[make_tokens(shape, n, seed=seed)]
     chunks, offsets, o = [], [], 0
     for nc in chunk_lens:
-        k, v, _ = oracle.prefill(w, shape, x0[o:o + nc], pos0=0)
+        k, v, _ = oracle.prefill(w, shape, x0[o:o + nc], pos0=0, dtype=precompute_dtype)
         chunks.append((round_to(k, dtype), round_to(v, dtype)))
         offsets.append(o)
         o += nc
