@@ -205,6 +205,65 @@ void cb_plan_destroy(cb_plan* plan);
 cb_status cb_prefill(cb_model* model, const void* x0, int32_t n_tokens, int32_t pos0,
                      void* k_out, void* v_out, float* hidden_out, void* stream);
 
+/* ------------------------------------------------------------- batches
+ * Several requests fused in one call (the serving case of the CacheBlend
+ * explainer (0h-n0), section "vLLM統合": many RAG requests whose contexts
+ * draw on a shared store of chunk caches).  Every request is fused exactly as
+ * cb_blend would fuse it alone; the rows of all requests are stacked in each
+ * projection, and attention, deviation and selection stay per request.
+ *
+ * Chunks come from a pool; a request lists pool indices in prompt order and
+ * its chunk offsets are the running sums of their lengths (0, n_0,
+ * n_0 + n_1, ...).  A pool chunk may be used by several requests or several
+ * times in one request: a host-resident chunk is copied to the device once
+ * per layer and rotated from there into every place it is used.
+ *
+ * Stacking: request b has N_b = N_c,b + N_s,b prompt tokens and owns rows
+ * G_b .. G_b + N_b - 1 of every stacked [sum N] array, G_b = N_0 + ... +
+ * N_{b-1}, in its own fused order.  Its chunk-token columns of [L][sum N_c]
+ * outputs start at C_b = N_c,0 + ... + N_c,b-1.  Positions, sel_idx
+ * entries and deviation columns are the request's own (0 = its first
+ * token). */
+typedef struct cb_batch_item {
+    int32_t n_chunks;
+    const int32_t* chunk_ids;     /* host [n_chunks]: indices into the pool   */
+    int32_t n_suffix;             /* query tokens after the last chunk        */
+    const int32_t* schedule;      /* host [L+1] or NULL: derive it from the
+                                     batch's recompute_bp / schedule_kind     */
+} cb_batch_item;
+
+typedef struct cb_batch_request {
+    int32_t n_pool;
+    const cb_chunk_kv* pool;      /* host [n_pool]; only used entries are read */
+    int32_t n_requests;
+    const cb_batch_item* items;   /* host [n_requests]                        */
+    const void* x0;               /* device [sum N][d], model dtype, stacked  */
+    int32_t recompute_bp;
+    int32_t schedule_kind;
+    int32_t dev_mode;
+    int32_t min_tokens;           /* per request: N_b < min_tokens -> full prefill */
+} cb_batch_request;
+
+typedef struct cb_batch_outputs {
+    void* fused_k;      /* device [L][sum N][H_kv][d_head] (required)          */
+    void* fused_v;      /* device [L][sum N][H_kv][d_head] (required)          */
+    int32_t* sel_idx;   /* device [L][sum N_c] or NULL: request b's kept
+                           positions after layer l at columns C_b.., ascending,
+                           first s_b[l+1] valid                                */
+    int32_t* sel_count; /* host [n_requests][L] or NULL: s_b[l+1]              */
+    float* hidden_out;  /* device [sum (s_b[L] + N_s,b)][d] or NULL: last-layer
+                           output rows, request by request (kept chunk rows,
+                           then suffix, by position)                           */
+    float* deviation;   /* device [L][sum N_c] or NULL: deviation by position
+                           at columns C_b.., NaN where not measured            */
+} cb_batch_outputs;
+
+/* One-shot fusion of a batch; stream-ordered like cb_blend.  Per layer the
+ * used host chunks are copied once on the side stream and rotated into
+ * every request that uses them while the previous layer computes. */
+cb_status cb_blend_batch(cb_model* model, const cb_batch_request* req,
+                         const cb_batch_outputs* out, void* stream);
+
 /* ------------------------------------------------------------- timing
  * Per-kernel-class timing of the fusion path with HIP events recorded on the
  * stream each kernel runs on (the caller's stream, or the side stream for

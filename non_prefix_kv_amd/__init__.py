@@ -58,6 +58,24 @@ class cb_outputs(ctypes.Structure):
                 ("deviation", _c_p)]
 
 
+class cb_batch_item(ctypes.Structure):
+    _fields_ = [("n_chunks", _c_i32), ("chunk_ids", ctypes.POINTER(_c_i32)),
+                ("n_suffix", _c_i32), ("schedule", ctypes.POINTER(_c_i32))]
+
+
+class cb_batch_request(ctypes.Structure):
+    _fields_ = [("n_pool", _c_i32), ("pool", ctypes.POINTER(cb_chunk_kv)),
+                ("n_requests", _c_i32), ("items", ctypes.POINTER(cb_batch_item)),
+                ("x0", _c_p), ("recompute_bp", _c_i32), ("schedule_kind", _c_i32),
+                ("dev_mode", _c_i32), ("min_tokens", _c_i32)]
+
+
+class cb_batch_outputs(ctypes.Structure):
+    _fields_ = [("fused_k", _c_p), ("fused_v", _c_p), ("sel_idx", _c_p),
+                ("sel_count", ctypes.POINTER(_c_i32)), ("hidden_out", _c_p),
+                ("deviation", _c_p)]
+
+
 class cb_kernel_stat(ctypes.Structure):
     _fields_ = [("launches", _c_i64), ("total_ms", ctypes.c_double), ("flops", ctypes.c_double),
                 ("bytes", ctypes.c_double)]
@@ -87,6 +105,7 @@ _fn = {
     "cb_prefill_layer": (ctypes.c_int, _c_p, _c_i32),
     "cb_synchronize": (ctypes.c_int, _c_p),
     "cb_plan_destroy": (None, _c_p),
+    "cb_blend_batch": (ctypes.c_int, _c_p, _P(cb_batch_request), _P(cb_batch_outputs), _c_p),
     "cb_prefill": (ctypes.c_int, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p),
     "cb_profile_enable": (ctypes.c_int, _c_p, _c_i32),
     "cb_profile_read": (ctypes.c_int, _c_p, _P(cb_kernel_stat)),
@@ -199,8 +218,7 @@ class Model:
             pass
 
 
-def _request(chunks, offsets, n_suffix, x0, schedule, recompute_bp, schedule_kind, dev_mode,
-             min_tokens):
+def _chunk_array(chunks):
     """chunks: list of dicts {k, v, n_tokens, on_host, layer_stride} with tensors or ints."""
     arr = (cb_chunk_kv * max(1, len(chunks)))()
     for i, c in enumerate(chunks):
@@ -209,6 +227,12 @@ def _request(chunks, offsets, n_suffix, x0, schedule, recompute_bp, schedule_kin
         arr[i].n_tokens = c["n_tokens"]
         arr[i].on_host = int(c.get("on_host", 0))
         arr[i].layer_stride = c["layer_stride"]
+    return arr
+
+
+def _request(chunks, offsets, n_suffix, x0, schedule, recompute_bp, schedule_kind, dev_mode,
+             min_tokens):
+    arr = _chunk_array(chunks)
     offs = (_c_i32 * max(1, len(offsets)))(*offsets)
     sched = None
     if schedule is not None:
@@ -237,6 +261,38 @@ def cb_blend(model, chunks, offsets, n_suffix, x0, fused_k, fused_v, sel_idx=Non
     _check(RAW["cb_blend"](model.handle, ctypes.byref(req), ctypes.byref(out), _stream(stream)))
     del keep
     return list(cnt)
+
+
+def cb_blend_batch(model, pool, requests, x0, fused_k, fused_v, sel_idx=None, hidden_out=None,
+                   deviation=None, recompute_bp=1500, schedule_kind=CB_SCHED_GRADUAL,
+                   dev_mode=CB_DEV_KV, min_tokens=0, stream=None):
+    """Queues the fusion of a batch.  pool: chunk dicts as for cb_blend;
+    requests: list of dicts {chunk_ids: [...], n_suffix, schedule (optional)}.
+    Returns sel_count as a list per request of s_b[l+1]."""
+    parr = _chunk_array(pool)
+    items = (cb_batch_item * len(requests))()
+    keep = []
+    for i, r in enumerate(requests):
+        ids = (_c_i32 * max(1, len(r["chunk_ids"])))(*r["chunk_ids"])
+        keep.append(ids)
+        items[i].n_chunks = len(r["chunk_ids"])
+        items[i].chunk_ids = ids
+        items[i].n_suffix = r["n_suffix"]
+        sch = r.get("schedule")
+        if sch is not None:
+            sa = (_c_i32 * len(sch))(*sch)
+            keep.append(sa)
+            items[i].schedule = sa
+    req = cb_batch_request(len(pool), parr, len(requests), items, _ptr(x0), recompute_bp,
+                           schedule_kind, dev_mode, min_tokens)
+    L = model.cfg.n_layers
+    cnt = (_c_i32 * (L * len(requests)))()
+    out = cb_batch_outputs(_ptr(fused_k), _ptr(fused_v), _ptr(sel_idx), cnt, _ptr(hidden_out),
+                           _ptr(deviation))
+    _check(RAW["cb_blend_batch"](model.handle, ctypes.byref(req), ctypes.byref(out),
+                                 _stream(stream)))
+    del keep
+    return [list(cnt[b * L:(b + 1) * L]) for b in range(len(requests))]
 
 
 class Plan:

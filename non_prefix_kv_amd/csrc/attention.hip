@@ -15,7 +15,10 @@
 // through LDS.  Blocks whose keys all lie after a wave's last query position
 // are skipped by that wave; blocks after the workgroup's last position are
 // never loaded.  Tiles are issued longest-first.
+#include <algorithm>
 #include <climits>
+#include <utility>
+#include <vector>
 
 #include "kernels.h"
 
@@ -64,7 +67,7 @@ __device__ __forceinline__ void store_vt4(float* dst, const u32x4 (&rows)[4], in
 }
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a, const AttnTiles tl) {
     constexpr int KB = AttnCfg<T>::KB;
     constexpr int LDK = D + 16 / (int)sizeof(T);        // sK row stride (elements)
     constexpr int LDV = KB + 4;                          // sVt row stride (elements)
@@ -81,8 +84,8 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) T sVt[2][D * LDV];
     __shared__ int sred[2][kThreads / 64];
 
-    const int n_tiles = (a.n_q + QT - 1) / QT;
-    const int qt = n_tiles - 1 - (int)blockIdx.x;      // longest tiles first
+    const AttnRange& tile = tl.t[blockIdx.x];          // tiles come longest first
+    const int n_kv = tile.n_kv;
     const int h = blockIdx.y;
     const int hk = h / (a.n_q_heads / a.n_kv_heads);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -90,9 +93,9 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
     const int q_ld = a.n_q_heads * D, kv_ld = a.n_kv_heads * D;
 
     // This lane's query (column of S^T).
-    const int qi_raw = qt * QT + wave * 16 + fr;
-    const bool q_ok = qi_raw < a.n_q;
-    const int qi = q_ok ? qi_raw : a.n_q - 1;
+    const int ql = wave * 16 + fr;
+    const bool q_ok = ql < tile.nq;
+    const int qi = tile.q0 + (q_ok ? ql : tile.nq - 1);
     const int qpos = a.q_pos[qi];
     // Workgroup / wave position range.
     int wmax = qpos, wmin = qpos;
@@ -106,7 +109,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
     int bmax = sred[0][0];
 #pragma unroll
     for (int w = 1; w < kThreads / 64; ++w) bmax = max(bmax, sred[0][w]);
-    const int nk = min(a.n_kv, bmax - a.kv_pos0 + 1);
+    const int nk = min(n_kv, bmax - a.kv_pos0 + 1);
     const int n_kb = nk > 0 ? (nk + KB - 1) / KB : 0;
 
     // Q fragments (B operand of S^T = K Q^T), kept in registers.
@@ -122,8 +125,8 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
     float m_run = -INFINITY, l_run = 0.f;
     const float sl2 = 1.4426950408889634f / sqrtf((float)D);   // log2(e) / sqrt(D)
 
-    const T* kbase = static_cast<const T*>(a.k) + hk * D;
-    const T* vbase = static_cast<const T*>(a.v) + hk * D;
+    const T* kbase = static_cast<const T*>(a.k) + (int64_t)tile.g0 * kv_ld + hk * D;
+    const T* vbase = static_cast<const T*>(a.v) + (int64_t)tile.g0 * kv_ld + hk * D;
     // Register staging of the next key block: K as KU 16-byte pieces of
     // single rows, V as 4 rows x 16 bytes so the transposed LDS image can be
     // written 4 keys at a time.  Rows past n_kv are clamped to the last key:
@@ -137,13 +140,13 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
         for (int j = 0; j < KU; ++j) {
             const int u = tid + j * kThreads;
             const int r = u / (D / VEC), c = (u % (D / VEC)) * VEC;
-            const int kr = min(k0 + r, a.n_kv - 1);
+            const int kr = min(k0 + r, n_kv - 1);
             rk[j] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)kr * kv_ld + c);
         }
         if (v_unit) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int vr = min(k0 + vr0 + q, a.n_kv - 1);
+                const int vr = min(k0 + vr0 + q, n_kv - 1);
                 rv[q] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)vr * kv_ld + vc);
             }
         }
@@ -174,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
                     mfma16(st[t], kf, qf[s]);
                 }
             }
-            const bool need_mask = (k0 + KB > a.n_kv) || (a.kv_pos0 + k0 + KB - 1 > wmin);
+            const bool need_mask = (k0 + KB > n_kv) || (a.kv_pos0 + k0 + KB - 1 > wmin);
             float mloc = -INFINITY;
 #pragma unroll
             for (int t = 0; t < NKT; ++t)
@@ -183,7 +186,7 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a) {
                     float sc = st[t][e] * sl2;
                     if (need_mask) {
                         const int kj = k0 + t * 16 + g * 4 + e;
-                        if (kj >= a.n_kv || a.kv_pos0 + kj > qpos) sc = -INFINITY;
+                        if (kj >= n_kv || a.kv_pos0 + kj > qpos) sc = -INFINITY;
                     }
                     st[t][e] = sc;
                     mloc = fmaxf(mloc, sc);
@@ -287,7 +290,7 @@ __device__ __forceinline__ int xcd_order(int hw, int total) {
 }
 
 template <int D>
-__global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a, const AttnTiles tl) {
     constexpr int LDK = D + 8;                 // sK row stride (elements)
     constexpr int LDV = KB32 + 4;              // sVt row stride (elements)
     constexpr int NDS = D / 16;                // 16-dim reduction steps for S
@@ -300,21 +303,23 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a) {
     __shared__ __attribute__((aligned(16))) bf16 sVt[2][D * LDV];
     __shared__ int sred[kT32 / 64];
 
-    // logical id -> (tile, segment, head), tile fastest, longest tiles first
-    const int n_tiles = (a.n_q + QT32 - 1) / QT32;
+    // logical id -> (tile, segment, head), tile fastest; tiles come longest first
+    const int n_tiles = tl.n;
     const int n_segs = a.seg_keys > 0 ? a.max_seg : 1;
     const int logical = xcd_order(blockIdx.x, n_tiles * n_segs * a.n_q_heads);
-    const int qt = n_tiles - 1 - logical % n_tiles;
+    const int qt = logical % n_tiles;
     const int seg = (logical / n_tiles) % n_segs;
     const int h = logical / (n_tiles * n_segs);
+    const AttnRange& tile = tl.t[qt];
+    const int n_kv = tile.n_kv;
     const int hk = h / (a.n_q_heads / a.n_kv_heads);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int fr = lane & 31, g = lane >> 5;
     const int q_ld = a.n_q_heads * D, kv_ld = a.n_kv_heads * D;
 
-    const int qi_raw = qt * QT32 + wave * 32 + fr;
-    const bool q_ok = qi_raw < a.n_q;
-    const int qi = q_ok ? qi_raw : a.n_q - 1;
+    const int ql = wave * 32 + fr;
+    const bool q_ok = ql < tile.nq;
+    const int qi = tile.q0 + (q_ok ? ql : tile.nq - 1);
     const int qpos = a.q_pos[qi];
     int wmax = qpos, wmin = qpos;
 #pragma unroll
@@ -327,7 +332,7 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a) {
     int bmax = sred[0];
 #pragma unroll
     for (int w = 1; w < kT32 / 64; ++w) bmax = max(bmax, sred[w]);
-    const int nk = min(a.n_kv, bmax - a.kv_pos0 + 1);
+    const int nk = min(n_kv, bmax - a.kv_pos0 + 1);
     // Key segment of this workgroup (whole range when not split).
     const int n_seg = a.seg_keys > 0 ? max(1, (nk + a.seg_keys - 1) / a.seg_keys) : 1;
     if (seg >= n_seg) return;                          // uniform over the workgroup
@@ -349,8 +354,8 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a) {
     float m_run = -INFINITY, l_run = 0.f;
     const float sl2 = 1.4426950408889634f / sqrtf((float)D);
 
-    const bf16* kbase = static_cast<const bf16*>(a.k) + hk * D;
-    const bf16* vbase = static_cast<const bf16*>(a.v) + hk * D;
+    const bf16* kbase = static_cast<const bf16*>(a.k) + (int64_t)tile.g0 * kv_ld + hk * D;
+    const bf16* vbase = static_cast<const bf16*>(a.v) + (int64_t)tile.g0 * kv_ld + hk * D;
     // Two register stage sets (prefetch distance 2).  V unit = 4 keys x 8
     // dims; consecutive lanes step over keys first so the transposed 8-byte
     // LDS stores of 16 lanes fill 32 distinct banks.  Rows past n_kv are
@@ -364,13 +369,13 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a) {
         for (int j = 0; j < KU; ++j) {
             const int u = tid + j * kT32;
             const int r = u / (D / 8), c = (u % (D / 8)) * 8;
-            const int kr = min(k0 + r, a.n_kv - 1);
+            const int kr = min(k0 + r, n_kv - 1);
             rk[j] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)kr * kv_ld + c);
         }
         if (v_unit) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int vr = min(k0 + vr0 + q, a.n_kv - 1);
+                const int vr = min(k0 + vr0 + q, n_kv - 1);
                 rv[q] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)vr * kv_ld + vc);
             }
         }
@@ -400,12 +405,12 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a) {
         }
         // Scores stay unscaled; the running max is kept in scaled (log2)
         // units and the scale is folded into one FMA before v_exp_f32.
-        const bool need_mask = (k0 + KB32 > a.n_kv) || (a.kv_pos0 + k0 + KB32 - 1 > wmin);
+        const bool need_mask = (k0 + KB32 > n_kv) || (a.kv_pos0 + k0 + KB32 - 1 > wmin);
         if (need_mask) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 const int kj = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
-                if (kj >= a.n_kv || a.kv_pos0 + kj > qpos) st[i] = -INFINITY;
+                if (kj >= n_kv || a.kv_pos0 + kj > qpos) st[i] = -INFINITY;
             }
         }
         float mloc = st[0];
@@ -481,7 +486,6 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a) {
     if (n_seg > 1) {
         // Partial of this segment: unnormalized O, running max (log2 units) and sum.
         const int64_t slot = ((int64_t)qt * a.n_q_heads + h) * a.max_seg + seg;
-        const int ql = wave * 32 + fr;
         float* po = a.part_o + (slot * QT32 + ql) * D;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
@@ -517,28 +521,26 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a) {
 // and head, so the merge is spread over the whole GPU.
 constexpr int kCombQ = 8;
 template <int D>
-__global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a, const AttnTiles tl) {
     constexpr int C4 = D / 4;                       // float4 chunks per query row
-    const int n_tiles = (a.n_q + QT32 - 1) / QT32;
     const int per_tile = QT32 / kCombQ;
     const int qt = blockIdx.x / per_tile, qg = blockIdx.x % per_tile;
     const int h = blockIdx.y;
-    const int q0 = qt * QT32;
-    const int nq_t = min(QT32, a.n_q - q0);
+    const AttnRange& tile = tl.t[qt];
+    const int nq_t = tile.nq;
     if (qg * kCombQ >= nq_t) return;
     // key extent of the tile, as seen by its attention workgroups
     __shared__ int wmx[4];
     int mx = INT_MIN;
-    for (int i = threadIdx.x; i < nq_t; i += 256) mx = max(mx, a.q_pos[q0 + i]);
+    for (int i = threadIdx.x; i < nq_t; i += 256) mx = max(mx, a.q_pos[tile.q0 + i]);
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) mx = max(mx, __shfl_xor(mx, o, 64));
     if ((threadIdx.x & 63) == 0) wmx[threadIdx.x >> 6] = mx;
     __syncthreads();
     mx = max(max(wmx[0], wmx[1]), max(wmx[2], wmx[3]));
-    const int nk = min(a.n_kv, mx - a.kv_pos0 + 1);
+    const int nk = min(tile.n_kv, mx - a.kv_pos0 + 1);
     const int n_seg = max(1, (nk + a.seg_keys - 1) / a.seg_keys);
     if (n_seg <= 1) return;
-    (void)n_tiles;
     const int ql = qg * kCombQ + (int)threadIdx.x / C4;
     const int c = ((int)threadIdx.x % C4) * 4;
     if ((int)threadIdx.x >= kCombQ * C4 || ql >= nq_t) return;
@@ -559,62 +561,111 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a) {
     bf16x4 v{static_cast<bf16>(acc[0] * inv), static_cast<bf16>(acc[1] * inv),
              static_cast<bf16>(acc[2] * inv), static_cast<bf16>(acc[3] * inv)};
     *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.out) +
-                               (int64_t)(q0 + ql) * a.n_q_heads * D + h * D + c) = v;
+                               (int64_t)(tile.q0 + ql) * a.n_q_heads * D + h * D + c) = v;
+}
+
+// Query tiles of height `qth` cut from the ranges, ordered by an estimate of
+// their visible keys (rows of a range ascend in position, so later tiles of
+// a range see more keys), longest first; stable for equal estimates.
+std::vector<AttnRange> make_tiles(const AttnRange* r, int n_r, int qth) {
+    std::vector<std::pair<double, AttnRange>> w;
+    for (int i = 0; i < n_r; ++i) {
+        const AttnRange& x = r[i];
+        for (int q = 0; q < x.nq; q += qth) {
+            const AttnRange t{x.q0 + q, std::min(qth, x.nq - q), x.g0, x.n_kv};
+            w.push_back({(double)x.n_kv * (q + t.nq) / x.nq, t});
+        }
+    }
+    std::stable_sort(w.begin(), w.end(),
+                     [](const auto& a, const auto& b) { return a.first > b.first; });
+    std::vector<AttnRange> out(w.size());
+    for (size_t i = 0; i < w.size(); ++i) out[i] = w[i].second;
+    return out;
+}
+
+// Split plan of one launch of n tiles: segments of 512 keys when the plain
+// grid leaves the GPU short of workgroups.
+struct SplitPlan {
+    int seg_keys = 0, max_seg = 1;
+    size_t bytes = 0;
+};
+SplitPlan split_plan(const AttnRange* t, int n, int n_q_heads, int head_dim) {
+    SplitPlan p;
+    int max_kv = 0;
+    for (int i = 0; i < n; ++i) max_kv = std::max(max_kv, t[i].n_kv);
+    if ((int64_t)n * n_q_heads >= 2048 || max_kv <= 1024) return p;
+    p.seg_keys = 512;
+    p.max_seg = (max_kv + p.seg_keys - 1) / p.seg_keys;
+    p.bytes = (size_t)n * n_q_heads * p.max_seg * QT32 * (head_dim + 2) * sizeof(float);
+    return p;
 }
 
 template <int D>
-hipError_t launch32(const AttnArgs& a, hipStream_t s) {
-    const int tiles = (a.n_q + QT32 - 1) / QT32;
-    const bool split = a.seg_keys > 0 && a.max_seg > 1;
-    if (split && (a.seg_keys % KB32 || !a.part_o || !a.part_ml ||
-                  (int64_t)a.max_seg * a.seg_keys < a.n_kv))
-        return hipErrorInvalidValue;
-    AttnArgs b = a;
-    if (!split) {
-        b.seg_keys = 0;
-        b.max_seg = 1;
+hipError_t launch32(const AttnArgs& a0, const AttnTiles& tl, void* ws, size_t ws_bytes,
+                    hipStream_t s) {
+    const SplitPlan sp = split_plan(tl.t, tl.n, a0.n_q_heads, D);
+    AttnArgs a = a0;
+    a.seg_keys = sp.seg_keys;
+    a.max_seg = sp.max_seg;
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
+    if (sp.bytes) {
+        if (!ws || ws_bytes < sp.bytes) return hipErrorInvalidValue;
+        a.part_o = static_cast<float*>(ws);
+        a.part_ml = a.part_o + (size_t)tl.n * a.n_q_heads * sp.max_seg * QT32 * D;
     }
-    const int64_t blocks = (int64_t)tiles * a.n_q_heads * b.max_seg;
+    const int64_t blocks = (int64_t)tl.n * a.n_q_heads * a.max_seg;
     if (blocks > INT_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attention32_kernel<D>), dim3((unsigned)blocks), dim3(kT32), 0, s, b);
-    if (split)
-        hipLaunchKernelGGL((attention_combine_kernel<D>), dim3(tiles * (QT32 / kCombQ), a.n_q_heads),
-                           dim3(256), 0, s, b);
+    hipLaunchKernelGGL((attention32_kernel<D>), dim3((unsigned)blocks), dim3(kT32), 0, s, a, tl);
+    if (sp.bytes)
+        hipLaunchKernelGGL((attention_combine_kernel<D>), dim3(tl.n * (QT32 / kCombQ), a.n_q_heads),
+                           dim3(256), 0, s, a, tl);
     return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t launch_t(const AttnArgs& a, hipStream_t s) {
-    dim3 grid((a.n_q + QT - 1) / QT, a.n_q_heads);
-    hipLaunchKernelGGL((attention_kernel<T, D>), grid, dim3(kThreads), 0, s, a);
+hipError_t launch_t(const AttnArgs& a, const AttnTiles& tl, hipStream_t s) {
+    hipLaunchKernelGGL((attention_kernel<T, D>), dim3(tl.n, a.n_q_heads), dim3(kThreads), 0, s, a,
+                       tl);
     return hipGetLastError();
 }
 
+int tile_height(int dtype) { return dtype == BF16 ? QT32 : QT; }
+
 }  // namespace
 
-size_t attention_split_plan(int dtype, int n_q, int n_kv, int n_q_heads, int head_dim,
-                            int* seg_keys, int* max_seg) {
-    *seg_keys = 0;
-    *max_seg = 1;
-    if (dtype != BF16 || n_q <= 0) return 0;
-    const int64_t tiles = (n_q + QT32 - 1) / QT32;
-    // Split only when the plain grid leaves the GPU short of workgroups.
-    if (tiles * n_q_heads >= 2048 || n_kv <= 1024) return 0;
-    const int sk = 512;
-    const int ms = (n_kv + sk - 1) / sk;
-    *seg_keys = sk;
-    *max_seg = ms;
-    return (size_t)tiles * n_q_heads * ms * QT32 * (head_dim + 2) * sizeof(float);
+size_t attention_workspace(int dtype, const AttnRange* r, int n_r, int n_q_heads, int head_dim) {
+    if (dtype != BF16 || n_r <= 0) return 0;
+    const std::vector<AttnRange> tiles = make_tiles(r, n_r, tile_height(dtype));
+    size_t need = 0;
+    for (size_t i = 0; i < tiles.size(); i += kMaxAttnTiles) {
+        const int n = (int)std::min<size_t>(kMaxAttnTiles, tiles.size() - i);
+        need = std::max(need, split_plan(&tiles[i], n, n_q_heads, head_dim).bytes);
+    }
+    return need;
 }
 
-hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s) {
-    if (a.n_q <= 0) return hipSuccess;
+hipError_t launch_attention(int dtype, const AttnArgs& a, const AttnRange* r, int n_r, void* ws,
+                            size_t ws_bytes, hipStream_t s) {
+    if (n_r <= 0) return hipSuccess;
     if (a.n_kv_heads <= 0 || a.n_q_heads % a.n_kv_heads != 0) return hipErrorInvalidValue;
-    if (a.head_dim == 128)
-        return dtype == BF16 ? launch32<128>(a, s) : launch_t<float, 128>(a, s);
-    if (a.head_dim == 64)
-        return dtype == BF16 ? launch32<64>(a, s) : launch_t<float, 64>(a, s);
-    return hipErrorInvalidValue;
+    if (a.head_dim != 64 && a.head_dim != 128) return hipErrorInvalidValue;
+    for (int i = 0; i < n_r; ++i)
+        if (r[i].nq < 0 || (r[i].nq > 0 && r[i].n_kv <= 0)) return hipErrorInvalidValue;
+    const std::vector<AttnRange> tiles = make_tiles(r, n_r, tile_height(dtype));
+    for (size_t i = 0; i < tiles.size(); i += kMaxAttnTiles) {
+        AttnTiles tl;
+        tl.n = (int)std::min<size_t>(kMaxAttnTiles, tiles.size() - i);
+        for (int j = 0; j < tl.n; ++j) tl.t[j] = tiles[i + j];
+        hipError_t e;
+        if (dtype == BF16)
+            e = a.head_dim == 128 ? launch32<128>(a, tl, ws, ws_bytes, s)
+                                  : launch32<64>(a, tl, ws, ws_bytes, s);
+        else
+            e = a.head_dim == 128 ? launch_t<float, 128>(a, tl, s) : launch_t<float, 64>(a, tl, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace cb

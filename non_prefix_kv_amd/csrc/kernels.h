@@ -26,8 +26,8 @@ struct RotJob {
     int pad_;
 };
 
-// Jobs travel by value in the kernel arguments (one launch per 16 chunks).
-constexpr int kMaxRotJobs = 16;
+// Jobs travel by value in the kernel arguments (one launch per 64 chunks).
+constexpr int kMaxRotJobs = 64;
 struct RotJobs {
     RotJob j[kMaxRotJobs];
     int n;
@@ -55,31 +55,67 @@ hipError_t launch_rmsnorm(int x_dtype, const void* x, const int* idx, int y_dtyp
                           float eps, hipStream_t s);
 
 // K/V rows of the recomputed set into the fused cache: for r < n_rows,
-// fused row pos[src_idx[r]] (src_idx nullptr: identity; pos nullptr: the
-// source row index) minus row_base receives k_new/v_new row src_idx[r].
+// fused row dst_row[r] receives k_new/v_new row src_idx[r].
 hipError_t launch_scatter_kv(int dtype, const void* k_new, const void* v_new,
-                             const int* src_idx, const int* pos, int row_base,
-                             void* fk, void* fv, int n_rows, int kv_dim, hipStream_t s);
+                             const int* src_idx, const int* dst_row, void* fk, void* fv,
+                             int n_rows, int kv_dim, hipStream_t s);
+
+// ------------------------------------------------------------------ requests
+// Rows of several requests are stacked in every projection.  Per layer,
+// request b owns the recomputed rows R[r_off .. r_off + n_c + n_s) (its n_c
+// chunk rows by position, then its n_s suffix rows) and the query rows
+// Q[q_off .. q_off + k + n_s) (the k chunk rows it keeps, then the suffix).
+// Each stacked row carries a local position (RoPE, causality) and a global
+// row of the fused cache.  Tables travel by value in kernel arguments,
+// kMaxReq requests per launch.
+constexpr int kMaxReq = 64;
+struct ReqRows {
+    int r_off, n_c, n_s, k;
+    int q_off;
+    int c_off;      // compact slot of the first chunk row in the deviation array
+    int out_col;    // column of the request in per-layer [sum N_c] outputs
+    int pad_;
+};
+struct ReqTab {
+    ReqRows r[kMaxReq];
+    int n;
+    int max_c;      // largest n_c in the table
+};
+
+// Initial rows of request b: count rows from r_off with local positions
+// lp0 + i and global rows g0 + i.
+struct RowInit {
+    int r_off, count, lp0, g0;
+};
+struct RowInitTab {
+    RowInit r[kMaxReq];
+    int n;
+};
+hipError_t launch_init_rows(const RowInitTab& t, int* pos, int* rows, hipStream_t s);
+
+// Fills p[0..n) with the float value v.
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 
 // ------------------------------------------------------------------ selection
-// dev[r] = deviation of new row r against cached row crow(r) (crow = pos[r]
-// - row_base, or r when pos is null); when dev_pos_out is not null also
-// dev_pos_out[pos[r]] = dev[r].
+// For every request of the table and i < n_c: dev[c_off + i] = deviation of
+// new row (r_off + i) against cached row crow = grow[r_off + i] (grow null:
+// r_off + i).
 hipError_t launch_deviation(int dtype, const void* k_new, const void* v_new,
-                            const void* k_cached, const void* v_cached, const int* pos,
-                            int row_base, int n_rows, int kv_dim, int mode, float* dev,
-                            float* dev_pos_out, hipStream_t s);
+                            const void* k_cached, const void* v_cached, const int* grow,
+                            const ReqTab& t, int kv_dim, int mode, float* dev, hipStream_t s);
 
 // Kernel-level top-k: idx_out[0..k) = kept indices, ascending.
 hipError_t launch_topk(const float* dev, int n, int k, int* idx_out, hipStream_t s);
 
-// Blend bookkeeping for one layer.  R rows = n_c chunk rows then n_s suffix
-// rows, positions pos_r.  Keeps the k chunk rows with largest dev (all when
-// k == n_c), then writes sel_local[0..k+n_s) = kept R-row indices followed by
-// the suffix rows, pos_q = their positions, sel_pos (optional) = kept chunk
-// positions.
-hipError_t launch_select(const float* dev, int n_c, int k, int n_s, const int* pos_r,
-                         int* sel_local, int* pos_q, int* sel_pos, hipStream_t s);
+// Blend bookkeeping for one layer, one workgroup per request: keeps the k
+// chunk rows with the largest deviation (all of them when k == n_c) and
+// writes Q: sel_local[q_off + t] = stacked R index of kept row t (ascending
+// position) then of the suffix rows; pos_q / row_q their local positions and
+// global rows.  Optional: sel_pos[out_col + t] = kept local positions, and
+// (when dev_out) dev_out[out_col + pos] = the deviation of every chunk row.
+hipError_t launch_select(const float* dev, const ReqTab& t, const int* pos_r, const int* row_r,
+                         int* sel_local, int* pos_q, int* row_q, int* sel_pos, float* dev_out,
+                         hipStream_t s);
 
 // ------------------------------------------------------------------ GEMM
 enum Epi : int {
@@ -108,33 +144,46 @@ struct GemmArgs {
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& g, hipStream_t s);
 
 // ------------------------------------------------------------------ attention
-// out[i] = causal attention of q row qidx[i] (qidx null: i) at position
-// q_pos[i] over keys/values rows 0..n_kv-1 at positions kv_pos0 + j.
+// Causal attention of query rows over one request's keys.  A request range
+// covers output rows q0..q0+nq-1 (row i reads q row qidx[i], qidx null: i,
+// at position q_pos[i]); its keys/values are rows g0..g0+n_kv-1 of k/v at
+// positions kv_pos0 + j.  The launcher cuts ranges into query tiles of the
+// kernel's height, orders them longest first and passes them by value,
+// kMaxAttnTiles per launch.
+struct AttnRange {
+    int q0, nq, g0, n_kv;
+};
+constexpr int kMaxAttnTiles = 128;
+struct AttnTiles {
+    AttnRange t[kMaxAttnTiles];   // nq <= tile height
+    int n;
+};
+
 struct AttnArgs {
     const void* q;      // [*][Hq*dh]
     const int* qidx;    // row map into q (nullptr = identity)
-    const int* q_pos;   // [n_q]
-    int n_q;
-    const void* k;      // [n_kv][Hkv*dh]
+    const int* q_pos;   // per output row
+    const void* k;      // [*][Hkv*dh]
     const void* v;
-    int n_kv;
     int kv_pos0;
     int n_q_heads, n_kv_heads, head_dim;
-    void* out;          // [n_q][Hq*dh]
-    // Split over keys (bf16 path): query tiles whose visible keys exceed
-    // seg_keys are cut into segments processed by separate workgroups; their
-    // unnormalized partial outputs and (max, sum) go to part_o / part_ml and a
-    // combine pass merges them.  seg_keys = 0 disables splitting.
+    void* out;          // [*][Hq*dh]
+    // Split over keys (bf16 path): tiles whose visible keys exceed seg_keys
+    // are cut into segments processed by separate workgroups; their
+    // unnormalized partial outputs and (max, sum) go to part_o / part_ml and
+    // a combine pass merges them.  Set by the launcher.
     int seg_keys;
     int max_seg;
-    float* part_o;      // [tiles][Hq][max_seg][64][dh]
-    float* part_ml;     // [tiles][Hq][max_seg][64][2]
+    float* part_o;      // [tiles][Hq][max_seg][tile height][dh]
+    float* part_ml;     // [tiles][Hq][max_seg][tile height][2]
 };
-hipError_t launch_attention(int dtype, const AttnArgs& a, hipStream_t s);
 
-// Split plan for n_q queries over n_kv keys: fills seg_keys / max_seg and
-// returns the workspace bytes the partials need (0 when not split).
-size_t attention_split_plan(int dtype, int n_q, int n_kv, int n_q_heads, int head_dim,
-                            int* seg_keys, int* max_seg);
+// Workspace bytes the split partials of these ranges need (0: no split).
+size_t attention_workspace(int dtype, const AttnRange* r, int n_r, int n_q_heads, int head_dim);
+
+// Launches the attention of all ranges; `ws` holds at least
+// attention_workspace(...) bytes.
+hipError_t launch_attention(int dtype, const AttnArgs& a, const AttnRange* r, int n_r, void* ws,
+                            size_t ws_bytes, hipStream_t s);
 
 }  // namespace cb

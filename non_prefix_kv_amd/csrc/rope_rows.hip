@@ -6,6 +6,8 @@
 // is moved to its real position p = p' + delta by the pair rotation
 // R(delta * theta_i); the CacheBlend explainer's RoPE section fixes R and
 // theta_i.  Values are not rotated.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace cb {
@@ -103,11 +105,10 @@ __global__ __launch_bounds__(kThreads) void move_rows_kernel(
 template <typename T>
 __global__ __launch_bounds__(kThreads) void scatter_kv_kernel(
     const T* __restrict__ kn, const T* __restrict__ vn, const int* __restrict__ sidx,
-    const int* __restrict__ pos, int row_base, T* __restrict__ fk, T* __restrict__ fv,
-    int kv_dim) {
+    const int* __restrict__ drow, T* __restrict__ fk, T* __restrict__ fv, int kv_dim) {
     const int r = blockIdx.x;
     const int s = sidx ? sidx[r] : r;
-    const int64_t d = (int64_t)((pos ? pos[s] : s) - row_base) * kv_dim;
+    const int64_t d = (int64_t)(drow ? drow[r] : r) * kv_dim;
     const int64_t so = (int64_t)s * kv_dim;
     for (int c = threadIdx.x * 8; c < kv_dim; c += kThreads * 8) {
         Vec8<T>::copy(kn + so + c, fk + d + c);
@@ -193,6 +194,22 @@ __global__ void iota_kernel(int* p, int n, int base) {
     if (i < n) p[i] = base + i;
 }
 
+// blockIdx.y = request of the table.
+__global__ __launch_bounds__(kThreads) void init_rows_kernel(const RowInitTab t, int* pos,
+                                                            int* rows) {
+    const RowInit& q = t.r[blockIdx.y];
+    for (int i = blockIdx.x * kThreads + threadIdx.x; i < q.count; i += gridDim.x * kThreads) {
+        pos[q.r_off + i] = q.lp0 + i;
+        rows[q.r_off + i] = q.g0 + i;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void fill_kernel(float* p, int64_t n, float v) {
+    for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * kThreads)
+        p[i] = v;
+}
+
 }  // namespace
 
 hipError_t launch_rerotate(int dtype, const RotJobs& jobs, int layer, void* k_dst, void* v_dst,
@@ -223,6 +240,27 @@ hipError_t launch_iota(int* p, int n, int base, hipStream_t s) {
     return hipGetLastError();
 }
 
+hipError_t launch_init_rows(const RowInitTab& t, int* pos, int* rows, hipStream_t s) {
+    if (t.n <= 0) return hipSuccess;
+    if (t.n > kMaxReq) return hipErrorInvalidValue;
+    int mx = 0;
+    for (int b = 0; b < t.n; ++b) {
+        if (t.r[b].count < 0) return hipErrorInvalidValue;
+        mx = std::max(mx, t.r[b].count);
+    }
+    if (mx == 0) return hipSuccess;
+    const int gx = std::min((mx + kThreads - 1) / kThreads, 1024);
+    hipLaunchKernelGGL(init_rows_kernel, dim3(gx, t.n), dim3(kThreads), 0, s, t, pos, rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s) {
+    if (n <= 0) return hipSuccess;
+    const int64_t gx = std::min<int64_t>((n + kThreads - 1) / kThreads, 4096);
+    hipLaunchKernelGGL(fill_kernel, dim3((unsigned)gx), dim3(kThreads), 0, s, p, n, v);
+    return hipGetLastError();
+}
+
 hipError_t launch_gather_rows(const void* src, void* dst, const int* idx, int n_rows,
                               int64_t row_bytes, hipStream_t s) {
     if (n_rows <= 0) return hipSuccess;
@@ -240,17 +278,17 @@ hipError_t launch_scatter_rows(const void* src, void* dst, const int* idx, int n
 }
 
 hipError_t launch_scatter_kv(int dtype, const void* k_new, const void* v_new,
-                             const int* src_idx, const int* pos, int row_base, void* fk,
-                             void* fv, int n_rows, int kv_dim, hipStream_t s) {
+                             const int* src_idx, const int* dst_row, void* fk, void* fv,
+                             int n_rows, int kv_dim, hipStream_t s) {
     if (n_rows <= 0) return hipSuccess;
     if (kv_dim % 8 != 0) return hipErrorInvalidValue;
     if (dtype == BF16)
         hipLaunchKernelGGL(scatter_kv_kernel<bf16>, dim3(n_rows), dim3(kThreads), 0, s,
-                           (const bf16*)k_new, (const bf16*)v_new, src_idx, pos, row_base,
-                           (bf16*)fk, (bf16*)fv, kv_dim);
+                           (const bf16*)k_new, (const bf16*)v_new, src_idx, dst_row, (bf16*)fk,
+                           (bf16*)fv, kv_dim);
     else
         hipLaunchKernelGGL(scatter_kv_kernel<float>, dim3(n_rows), dim3(kThreads), 0, s,
-                           (const float*)k_new, (const float*)v_new, src_idx, pos, row_base,
+                           (const float*)k_new, (const float*)v_new, src_idx, dst_row,
                            (float*)fk, (float*)fv, kv_dim);
     return hipGetLastError();
 }

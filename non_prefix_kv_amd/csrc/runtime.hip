@@ -179,26 +179,55 @@ struct cb_model {
 };
 
 // ---------------------------------------------------------------- plan
+// One plan fuses a batch of requests (cb_blend: a batch of one).  Request b
+// owns rows G..G+N-1 of every stacked [sum N] array; per layer its
+// recomputed rows R and query rows Q are contiguous blocks of the stacked
+// workspace rows (see ReqRows).
+struct ReqInfo {
+    int G = 0, N = 0, Nc = 0, Ns = 0;
+    int C = 0;                    // first column in [L][sum N_c] outputs
+    int pos0 = 0;                 // position of the request's first token
+    std::vector<int> s;           // schedule s[0..L]
+    std::vector<int> ids;         // pool entries in prompt order
+    std::vector<int> offsets;     // chunk offsets
+};
+
 struct cb_plan {
     cb_model* m = nullptr;
     hipStream_t stream = nullptr;
-    int L = 0, N = 0, Nc = 0, Ns = 0, row_base = 0;
-    bool prefill_mode = false;
-    std::vector<int> s;
-    std::vector<cb_chunk_kv> chunks;
-    std::vector<int> offsets;
+    int L = 0, Ntot = 0, Nctot = 0;
+    std::vector<ReqInfo> reqs;
+    std::vector<cb_chunk_kv> pool;
     const void* x0 = nullptr;
     int dev_mode = CB_DEV_KV;
-    cb_outputs out{};
+    int kv_pos0 = 0;              // position of key row 0 of a request
+    // outputs
+    void* fused_k = nullptr;
+    void* fused_v = nullptr;
+    int* sel_idx = nullptr;
+    float* hidden_out = nullptr;
+    float* deviation = nullptr;
     // workspace
     void* ws = nullptr;
     float *X = nullptr, *Hres = nullptr, *dev = nullptr;
     void *Hn = nullptr, *Q = nullptr, *Kn = nullptr, *Vn = nullptr, *attn = nullptr,
          *act = nullptr;
-    int *pos_a = nullptr, *pos_b = nullptr, *sel_local = nullptr;
-    float* attn_part = nullptr;  // split-attention partials
-    size_t attn_part_bytes = 0;
-    std::vector<RotJobs> jobs;   // rotation jobs, 16 chunks per launch
+    int *pos_a = nullptr, *pos_b = nullptr, *row_a = nullptr, *row_b = nullptr,
+        *sel_local = nullptr;
+    void* attn_ws = nullptr;      // split-attention partials
+    size_t attn_ws_bytes = 0;
+    // fetch: host chunks copied once per layer into their first place of use,
+    // then rotation jobs that copy from a source (launched first) and jobs
+    // that rotate in place (launched after, they overwrite those sources)
+    struct H2D {
+        const char* k;
+        const char* v;
+        size_t layer_bytes;       // bytes between layers of the source
+        size_t bytes;             // bytes per layer
+        int64_t dst_row;
+    };
+    std::vector<H2D> h2d;
+    std::vector<RotJobs> jobs_copy, jobs_inplace;
 
     // streams / events
     hipEvent_t ready = nullptr;                 // workspace + prior main work
@@ -261,7 +290,59 @@ cb_status validate_cfg(const cb_model_cfg* c) {
     return CB_OK;
 }
 
-// Carves the workspace for up to `max_rows` recomputed rows.
+// Row blocks of every request at layer l.
+struct LayerRows {
+    std::vector<ReqRows> r;
+    int mR = 0, mQ = 0, nC = 0;
+    bool select_needed = false;   // some request keeps fewer chunk rows than it recomputes
+};
+LayerRows layer_rows(const cb_plan* p, int l) {
+    LayerRows lr;
+    lr.r.reserve(p->reqs.size());
+    for (const ReqInfo& q : p->reqs) {
+        ReqRows x{};
+        x.r_off = lr.mR;
+        x.n_c = q.s[l];
+        x.n_s = q.Ns;
+        x.k = q.s[l + 1];
+        x.q_off = lr.mQ;
+        x.c_off = lr.nC;
+        x.out_col = q.C;
+        lr.r.push_back(x);
+        lr.mR += x.n_c + x.n_s;
+        lr.mQ += x.k + x.n_s;
+        lr.nC += x.n_c;
+        lr.select_needed |= x.k < x.n_c;
+    }
+    return lr;
+}
+
+// The request table split into launches of kMaxReq requests.
+std::vector<ReqTab> req_tabs(const std::vector<ReqRows>& rows) {
+    std::vector<ReqTab> t;
+    for (size_t i = 0; i < rows.size(); i += kMaxReq) {
+        ReqTab x{};
+        x.n = (int)std::min<size_t>(kMaxReq, rows.size() - i);
+        for (int j = 0; j < x.n; ++j) {
+            x.r[j] = rows[i + j];
+            x.max_c = std::max(x.max_c, x.r[j].n_c);
+        }
+        t.push_back(x);
+    }
+    return t;
+}
+
+// Attention ranges of layer l: each request's query rows over its own keys.
+std::vector<AttnRange> attn_ranges(const cb_plan* p, const LayerRows& lr) {
+    std::vector<AttnRange> a;
+    for (size_t b = 0; b < p->reqs.size(); ++b) {
+        const int nq = lr.r[b].k + lr.r[b].n_s;
+        if (nq > 0) a.push_back(AttnRange{lr.r[b].q_off, nq, p->reqs[b].G, p->reqs[b].N});
+    }
+    return a;
+}
+
+// Carves the workspace for up to `max_rows` stacked rows.
 size_t carve(cb_plan* p, char* base, int max_rows) {
     const cb_model_cfg& c = p->m->cfg;
     const size_t es = p->m->es(), R = (size_t)std::max(1, max_rows);
@@ -279,24 +360,28 @@ size_t carve(cb_plan* p, char* base, int max_rows) {
     p->Vn = take(R * p->m->kvd() * es);
     p->attn = take(R * p->m->qd() * es);
     p->act = take(R * c.ffn_dim * es);
-    p->dev = (float*)take(std::max<size_t>(1, p->Nc) * 4);
+    p->dev = (float*)take(std::max<size_t>(1, p->Nctot) * 4);
     p->pos_a = (int*)take(R * 4);
     p->pos_b = (int*)take(R * 4);
+    p->row_a = (int*)take(R * 4);
+    p->row_b = (int*)take(R * 4);
     p->sel_local = (int*)take(R * 4);
-    // largest split-attention workspace over the query-row counts that occur
-    size_t part = 0;
-    for (int l = 0; l < p->L; ++l) {
-        int sk, ms;
-        part = std::max(part, attention_split_plan(c.dtype, p->s[l + 1] + p->Ns, p->N,
-                                                   c.n_q_heads, c.head_dim, &sk, &ms));
-    }
-    p->attn_part_bytes = part;
-    p->attn_part = part ? (float*)take(part) : nullptr;
+    p->attn_ws = p->attn_ws_bytes ? take(p->attn_ws_bytes) : nullptr;
     return off;
 }
 
 cb_status plan_alloc(cb_plan* p) {
-    const int max_rows = p->s[0] + p->Ns;
+    const cb_model_cfg& c = p->m->cfg;
+    int max_rows = 0;
+    size_t aw = 0;
+    for (int l = 0; l < p->L; ++l) {
+        const LayerRows lr = layer_rows(p, l);
+        max_rows = std::max(max_rows, lr.mR);
+        const std::vector<AttnRange> ar = attn_ranges(p, lr);
+        aw = std::max(aw, attention_workspace(c.dtype, ar.data(), (int)ar.size(), c.n_q_heads,
+                                              c.head_dim));
+    }
+    p->attn_ws_bytes = aw;
     const size_t bytes = carve(p, nullptr, max_rows);
     if (hipMallocAsync(&p->ws, bytes, p->stream) != hipSuccess) {
         (void)hipGetLastError();
@@ -329,10 +414,24 @@ cb_status plan_events(cb_plan* p) {
     return CB_OK;
 }
 
-// Initial row positions: R_0 = (all chunk rows if s[0] = N_c) + suffix.
+// Initial rows: R_0 of request b = (all its chunk rows if s[0] = N_c) +
+// suffix, positions from pos0, global rows from G.  Unmeasured deviations
+// read NaN.
 cb_status plan_start(cb_plan* p) {
-    const int base = p->s[0] == p->Nc ? 0 : p->Nc;
-    CB_HIP(launch_iota(p->pos_a, p->N - base, p->row_base + base, p->stream));
+    RowInitTab t{};
+    int r_off = 0;
+    for (size_t b = 0; b < p->reqs.size(); ++b) {
+        const ReqInfo& q = p->reqs[b];
+        const int base = q.s[0] == q.Nc ? 0 : q.Nc;
+        t.r[t.n++] = RowInit{r_off, q.N - base, q.pos0 + base, q.G + base};
+        r_off += q.N - base;
+        if (t.n == kMaxReq || b + 1 == p->reqs.size()) {
+            CB_HIP(launch_init_rows(t, p->pos_a, p->row_a, p->stream));
+            t.n = 0;
+        }
+    }
+    if (p->deviation)
+        CB_HIP(launch_fill(p->deviation, (int64_t)p->L * p->Nctot, NAN, p->stream));
     CB_HIP(hipEventRecord(p->ready, p->stream));
     CB_HIP(hipStreamWaitEvent(p->m->side, p->ready, 0));
     return CB_OK;
@@ -355,7 +454,13 @@ void plan_free(cb_plan* p) {
     delete p;
 }
 
-int64_t layer_elems(const cb_plan* p) { return (int64_t)p->N * p->m->kvd(); }
+int64_t layer_elems(const cb_plan* p) { return (int64_t)p->Ntot * p->m->kvd(); }
+
+double job_bytes(const RotJobs& js, double row_bytes) {
+    double b = 0;
+    for (int i = 0; i < js.n; ++i) b += js.j[i].n_tokens * row_bytes * (js.j[i].v_src ? 4 : 2);
+    return b;
+}
 
 cb_status do_fetch(cb_plan* p, int l) {
     if (p->fetch_done[l]) return CB_OK;
@@ -364,26 +469,20 @@ cb_status do_fetch(cb_plan* p, int l) {
     // keep the side stream at most two layers ahead of the main stream
     if (l >= 2 && p->layer_start[l - 2] && l - 2 < p->next_layer)
         CB_HIP(hipStreamWaitEvent(side, p->layer_start[l - 2], 0));
-    const size_t es = m->es();
-    char* fk = (char*)p->out.fused_k + (size_t)l * layer_elems(p) * es;
-    char* fv = (char*)p->out.fused_v + (size_t)l * layer_elems(p) * es;
-    for (size_t c = 0; c < p->chunks.size(); ++c) {
-        const cb_chunk_kv& ck = p->chunks[c];
-        if (!ck.on_host) continue;
-        const size_t bytes = (size_t)ck.n_tokens * m->kvd() * es;
-        const size_t src = (size_t)l * ck.layer_stride * es;
-        const size_t dst = (size_t)p->offsets[c] * m->kvd() * es;
-        CB_HIP(hipMemcpyAsync(fk + dst, (const char*)ck.k + src, bytes, hipMemcpyHostToDevice, side));
-        CB_HIP(hipMemcpyAsync(fv + dst, (const char*)ck.v + src, bytes, hipMemcpyHostToDevice, side));
+    const size_t es = m->es(), row_bytes = (size_t)m->kvd() * es;
+    char* fk = (char*)p->fused_k + (size_t)l * layer_elems(p) * es;
+    char* fv = (char*)p->fused_v + (size_t)l * layer_elems(p) * es;
+    for (const cb_plan::H2D& h : p->h2d) {
+        const size_t src = (size_t)l * h.layer_bytes, dst = (size_t)h.dst_row * row_bytes;
+        CB_HIP(hipMemcpyAsync(fk + dst, h.k + src, h.bytes, hipMemcpyHostToDevice, side));
+        CB_HIP(hipMemcpyAsync(fv + dst, h.v + src, h.bytes, hipMemcpyHostToDevice, side));
     }
-    for (const RotJobs& js : p->jobs) {
-        double bytes = 0;
-        for (int i = 0; i < js.n; ++i)
-            bytes += (double)js.j[i].n_tokens * m->kvd() * es * (js.j[i].v_src ? 4 : 2);
-        Span sp(m, CB_K_ROTATE, side, 0, bytes);
-        CB_HIP(launch_rerotate(m->cfg.dtype, js, l, fk, fv, m->cfg.n_kv_heads, m->cfg.head_dim,
-                               m->rope, side));
-    }
+    for (const std::vector<RotJobs>* set : {&p->jobs_copy, &p->jobs_inplace})
+        for (const RotJobs& js : *set) {
+            Span sp(m, CB_K_ROTATE, side, 0, job_bytes(js, (double)row_bytes));
+            CB_HIP(launch_rerotate(m->cfg.dtype, js, l, fk, fv, m->cfg.n_kv_heads,
+                                   m->cfg.head_dim, m->rope, side));
+        }
     CB_HIP(hipEventRecord(p->fetched[l], side));
     p->fetch_done[l] = 1;
     return CB_OK;
@@ -395,24 +494,26 @@ cb_status do_layer(cb_plan* p, int l) {
     const cb_layer_weights& w = m->w[l];
     const hipStream_t st = p->stream;
     const int dt = c.dtype, es = m->es();
-    const int nC = p->s[l], k = p->s[l + 1], mR = nC + p->Ns, mQ = k + p->Ns;
+    const LayerRows lr = layer_rows(p, l);
+    const int mR = lr.mR, mQ = lr.mQ;
     const double d = c.d_model, F = c.ffn_dim, qd = m->qd(), kvd = m->kvd();
     CB_HIP(hipEventRecord(p->layer_start[l], st));
     CB_HIP(hipStreamWaitEvent(st, p->fetched[l], 0));
     if (mR == 0) return CB_OK;
-    void* fk = (char*)p->out.fused_k + (size_t)l * layer_elems(p) * es;
-    void* fv = (char*)p->out.fused_v + (size_t)l * layer_elems(p) * es;
-    int* pos_r = p->pos_a;
-    int* pos_q = p->pos_b;
+    void* fk = (char*)p->fused_k + (size_t)l * layer_elems(p) * es;
+    void* fv = (char*)p->fused_v + (size_t)l * layer_elems(p) * es;
+    const int *pos_r = p->pos_a, *row_r = p->row_a;
+    int *pos_q = p->pos_b, *row_q = p->row_b;
+    const std::vector<ReqTab> tabs = req_tabs(lr.r);
 
-    // 1. RMSNorm of the input rows (layer 0 gathers them from x0 by position)
+    // 1. RMSNorm of the input rows (layer 0 gathers them from x0 by fused row)
     {
         const double in_es = l == 0 ? es : 4;
         Span sp(m, CB_K_RMSNORM, st, 0, mR * d * (in_es + es + (l == 0 ? 4 : 0)));
         if (l == 0) {
-            const bool all_rows = (nC == p->Nc) && p->row_base == 0;
-            CB_HIP(launch_rmsnorm(dt, p->x0, (all_rows || p->prefill_mode) ? nullptr : pos_r, dt,
-                                  w.attn_norm, p->Hn, p->X, mR, c.d_model, c.rms_eps, st));
+            const bool all_rows = mR == p->Ntot;
+            CB_HIP(launch_rmsnorm(dt, p->x0, all_rows ? nullptr : row_r, dt, w.attn_norm, p->Hn,
+                                  p->X, mR, c.d_model, c.rms_eps, st));
         } else {
             CB_HIP(launch_rmsnorm(F32, p->X, nullptr, dt, w.attn_norm, p->Hn, nullptr, mR,
                                   c.d_model, c.rms_eps, st));
@@ -431,41 +532,40 @@ cb_status do_layer(cb_plan* p, int l) {
         CB_HIP(launch_gemm(dt, EPI_QKV, g, st));
     }
     // 3. deviation of the recomputed chunk rows against the rotated cache
-    float* dev_out = p->out.deviation ? p->out.deviation + (size_t)l * p->Nc : nullptr;
-    if (nC > 0 && (k < nC || dev_out)) {
+    const bool measure = lr.nC > 0 && (lr.select_needed || p->deviation);
+    if (measure) {
         const double parts = p->dev_mode == CB_DEV_KV ? 4 : 2;
-        Span sp(m, CB_K_DEVIATION, st, 0, nC * (parts * kvd * es + 12.0));
-        CB_HIP(launch_deviation(dt, p->Kn, p->Vn, fk, fv, pos_r, 0, nC, m->kvd(), p->dev_mode,
-                                p->dev, dev_out, st));
+        Span sp(m, CB_K_DEVIATION, st, 0, lr.nC * (parts * kvd * es + 8.0));
+        for (const ReqTab& t : tabs)
+            CB_HIP(launch_deviation(dt, p->Kn, p->Vn, fk, fv, row_r, t, m->kvd(), p->dev_mode,
+                                    p->dev, st));
     }
-    // 4. keep the top s[l+1] chunk rows, then the suffix rows
-    int* sel_pos = p->out.sel_idx ? p->out.sel_idx + (size_t)l * p->Nc : nullptr;
+    // 4. per request: keep the top s[l+1] chunk rows, then the suffix rows
     {
-        Span sp(m, CB_K_SELECT, st, 0, 4.0 * nC + 12.0 * mQ);
-        CB_HIP(launch_select(p->dev, nC, k, p->Ns, pos_r, p->sel_local, pos_q, sel_pos, st));
+        int* sel_pos = p->sel_idx ? p->sel_idx + (size_t)l * p->Nctot : nullptr;
+        float* dev_out = (measure && p->deviation) ? p->deviation + (size_t)l * p->Nctot : nullptr;
+        Span sp(m, CB_K_SELECT, st, 0, 4.0 * lr.nC + 16.0 * mQ);
+        for (const ReqTab& t : tabs)
+            CB_HIP(launch_select(p->dev, t, pos_r, row_r, p->sel_local, pos_q, row_q, sel_pos,
+                                 dev_out, st));
     }
     // 5. merge the kept rows' K/V into the fused cache
     {
         Span sp(m, CB_K_SCATTER, st, 0, 4.0 * mQ * kvd * es);
-        CB_HIP(launch_scatter_kv(dt, p->Kn, p->Vn, p->sel_local, pos_r, p->row_base, fk, fv, mQ,
-                                 m->kvd(), st));
+        CB_HIP(launch_scatter_kv(dt, p->Kn, p->Vn, p->sel_local, row_q, fk, fv, mQ, m->kvd(), st));
     }
-    // 6. attention over the whole fused cache of this layer
+    // 6. attention of each request's kept rows over its whole fused cache
     {
         AttnArgs a{};
-        a.q = p->Q; a.qidx = p->sel_local; a.q_pos = pos_q; a.n_q = mQ;
-        a.k = fk; a.v = fv; a.n_kv = p->N; a.kv_pos0 = p->row_base;
+        a.q = p->Q; a.qidx = p->sel_local; a.q_pos = pos_q;
+        a.k = fk; a.v = fv; a.kv_pos0 = p->kv_pos0;
         a.n_q_heads = c.n_q_heads; a.n_kv_heads = c.n_kv_heads; a.head_dim = c.head_dim;
         a.out = p->attn;
-        const size_t need = attention_split_plan(dt, mQ, p->N, c.n_q_heads, c.head_dim,
-                                                 &a.seg_keys, &a.max_seg);
-        if (need > p->attn_part_bytes) return fail(CB_E_OOM, "attention split workspace");
-        if (need) {
-            a.part_o = p->attn_part;
-            a.part_ml = p->attn_part + need / sizeof(float) / (c.head_dim + 2) * c.head_dim;
-        }
+        const std::vector<AttnRange> ar = attn_ranges(p, lr);
         Span sp(m, CB_K_ATTENTION, st, 0, 0);
-        CB_HIP(launch_attention(dt, a, st));
+        const hipError_t e = launch_attention(dt, a, ar.data(), (int)ar.size(), p->attn_ws,
+                                              p->attn_ws_bytes, st);
+        if (e != hipSuccess) return fail(CB_E_HIP, "attention launch: %s", hipGetErrorString(e));
     }
     // 7. O projection + residual
     {
@@ -494,15 +594,113 @@ cb_status do_layer(cb_plan* p, int l) {
         GemmArgs gd{};
         gd.a = p->act; gd.b0 = w.w_down; gd.M = mQ; gd.N = c.d_model; gd.K = c.ffn_dim;
         const bool last = l == p->L - 1;
-        gd.out0 = (last && p->out.hidden_out) ? p->out.hidden_out : p->X;
+        gd.out0 = (last && p->hidden_out) ? p->hidden_out : p->X;
         gd.resid = p->Hres; gd.ridx = nullptr;
         Span sp(m, CB_K_GEMM_DOWN, st, 2.0 * mQ * d * F, (mQ * F + d * F) * es + mQ * d * 8);
         CB_HIP(launch_gemm(dt, EPI_RESID, gd, st));
     }
     std::swap(p->pos_a, p->pos_b);
+    std::swap(p->row_a, p->row_b);
     return CB_OK;
 }
 
+// Checks one chunk cache descriptor.
+cb_status check_chunk(cb_model* m, const cb_chunk_kv& ck, int idx) {
+    if (!ck.k || !ck.v) return fail(CB_E_INVALID, "chunk %d has a NULL k/v", idx);
+    if (ck.n_tokens <= 0) return fail(CB_E_INVALID, "chunk %d has %d tokens", idx, ck.n_tokens);
+    if (ck.layer_stride < (int64_t)ck.n_tokens * m->kvd())
+        return fail(CB_E_SHAPE, "chunk %d layer_stride %lld < n_tokens*H_kv*d_head", idx,
+                    (long long)ck.layer_stride);
+    const MemKind mk = mem_kind(ck.k), mv = mem_kind(ck.v);
+    if (ck.on_host) {
+        if (mk != MemKind::Pinned || mv != MemKind::Pinned)
+            return fail(CB_E_NOT_PINNED, "chunk %d: host K/V must be pinned (hipHostMalloc)", idx);
+    } else if (mk != MemKind::Device || mv != MemKind::Device) {
+        return fail(CB_E_INVALID, "chunk %d: on_host = 0 but K/V are not device memory", idx);
+    }
+    if (!aligned_to(ck.k, 16) || !aligned_to(ck.v, 16) || (ck.layer_stride * m->es()) % 16)
+        return fail(CB_E_SHAPE, "chunk %d: K/V and layer stride must be 16-byte aligned", idx);
+    return CB_OK;
+}
+
+// Schedule of one request: explicit, or derived; min_tokens forces a full
+// prefill; validated to be non-increasing with s[0] in {0, N_c}.
+cb_status request_schedule(cb_plan* p, ReqInfo& q, const int32_t* sched, int r_bp, int kind,
+                           int min_tokens, int b) {
+    const int L = p->L;
+    q.s.assign(L + 1, 0);
+    if (sched) {
+        q.s.assign(sched, sched + L + 1);
+    } else {
+        cb_status st = make_schedule(q.Nc, r_bp, kind, L, q.s.data());
+        if (st != CB_OK) return st;
+    }
+    if (min_tokens > 0 && q.N < min_tokens) q.s.assign(L + 1, q.Nc);
+    if (q.s[0] != 0 && q.s[0] != q.Nc)
+        return fail(CB_E_SCHEDULE, "request %d: s[0] = %d must be 0 or the chunk token count %d",
+                    b, q.s[0], q.Nc);
+    for (int l = 0; l < L; ++l)
+        if (q.s[l + 1] > q.s[l] || q.s[l + 1] < 0)
+            return fail(CB_E_SCHEDULE,
+                        "request %d: schedule must be non-increasing (s[%d]=%d, s[%d]=%d)", b, l,
+                        q.s[l], l + 1, q.s[l + 1]);
+    return CB_OK;
+}
+
+// Stacking offsets and the fetch program (copies and rotation jobs).
+cb_status plan_layout(cb_plan* p) {
+    int64_t G = 0, C = 0;
+    for (ReqInfo& q : p->reqs) {
+        q.G = (int)G;
+        q.C = (int)C;
+        G += q.N;
+        C += q.Nc;
+        if (G > (1 << 30)) return fail(CB_E_SHAPE, "batch too long (%lld tokens)", (long long)G);
+    }
+    p->Ntot = (int)G;
+    p->Nctot = (int)C;
+    if (p->Ntot == 0) return fail(CB_E_INVALID, "empty prompt");
+    const size_t es = p->m->es(), row_elems = p->m->kvd();
+    std::vector<int64_t> first_row(p->pool.size(), -1);
+    std::vector<RotJob> copy, inplace;
+    for (const ReqInfo& q : p->reqs)
+        for (size_t c = 0; c < q.ids.size(); ++c) {
+            const cb_chunk_kv& ck = p->pool[q.ids[c]];
+            RotJob j{};
+            j.src_layer_stride = ck.layer_stride;
+            j.dst_row = q.G + q.offsets[c];
+            j.n_tokens = ck.n_tokens;
+            j.delta = q.offsets[c];       // chunk-local position 0 -> real position o_c
+            if (!ck.on_host) {
+                j.k_src = ck.k;
+                j.v_src = ck.v;
+                copy.push_back(j);
+            } else if (first_row[q.ids[c]] < 0) {
+                first_row[q.ids[c]] = j.dst_row;
+                p->h2d.push_back({(const char*)ck.k, (const char*)ck.v,
+                                  (size_t)ck.layer_stride * es, ck.n_tokens * row_elems * es,
+                                  j.dst_row});
+                inplace.push_back(j);     // k_src = v_src = null: rotate where it landed
+            } else {
+                const size_t off = (size_t)first_row[q.ids[c]] * row_elems * es;
+                j.k_src = (const char*)p->fused_k + off;
+                j.v_src = (const char*)p->fused_v + off;
+                j.src_layer_stride = layer_elems(p);
+                copy.push_back(j);
+            }
+        }
+    for (auto [src, dst] : {std::make_pair(&copy, &p->jobs_copy),
+                            std::make_pair(&inplace, &p->jobs_inplace)})
+        for (size_t i = 0; i < src->size(); ++i) {
+            if (i % kMaxRotJobs == 0) dst->push_back(RotJobs{});
+            RotJobs& js = dst->back();
+            js.j[js.n++] = (*src)[i];
+            js.max_tokens = std::max(js.max_tokens, (*src)[i].n_tokens);
+        }
+    return CB_OK;
+}
+
+// A single request as a batch of one (its chunks form the pool).
 cb_status validate_request(cb_model* m, const cb_request* r, const cb_outputs* o, cb_plan* p) {
     if (!r || !o) return fail(CB_E_INVALID, "request/outputs is NULL");
     if (!o->fused_k || !o->fused_v) return fail(CB_E_INVALID, "fused_k/fused_v are required");
@@ -511,74 +709,123 @@ cb_status validate_request(cb_model* m, const cb_request* r, const cb_outputs* o
     if (r->n_chunks > 0 && (!r->chunks || !r->chunk_offsets))
         return fail(CB_E_INVALID, "chunks/chunk_offsets are NULL");
     if (r->dev_mode < 0 || r->dev_mode > 2) return fail(CB_E_INVALID, "dev_mode %d", r->dev_mode);
-    const int L = m->cfg.n_layers;
-    const int64_t row_elems = m->kvd();
+    p->L = m->cfg.n_layers;
+    ReqInfo q;
     int64_t o_next = 0;
-    p->chunks.assign(r->chunks, r->chunks + r->n_chunks);
-    p->offsets.assign(r->chunk_offsets, r->chunk_offsets + r->n_chunks);
     for (int c = 0; c < r->n_chunks; ++c) {
         const cb_chunk_kv& ck = r->chunks[c];
-        if (!ck.k || !ck.v) return fail(CB_E_INVALID, "chunk %d has a NULL k/v", c);
-        if (ck.n_tokens <= 0) return fail(CB_E_INVALID, "chunk %d has %d tokens", c, ck.n_tokens);
+        cb_status st = check_chunk(m, ck, c);
+        if (st != CB_OK) return st;
         if (r->chunk_offsets[c] != o_next)
             return fail(CB_E_INVALID, "chunk %d offset %d: offsets must start at 0 and be contiguous",
                         c, r->chunk_offsets[c]);
-        if (ck.layer_stride < (int64_t)ck.n_tokens * row_elems)
-            return fail(CB_E_SHAPE, "chunk %d layer_stride %lld < n_tokens*H_kv*d_head", c,
-                        (long long)ck.layer_stride);
-        const MemKind mk = mem_kind(ck.k), mv = mem_kind(ck.v);
-        if (ck.on_host) {
-            if (mk != MemKind::Pinned || mv != MemKind::Pinned)
-                return fail(CB_E_NOT_PINNED, "chunk %d: host K/V must be pinned (hipHostMalloc)", c);
-        } else if (mk != MemKind::Device || mv != MemKind::Device) {
-            return fail(CB_E_INVALID, "chunk %d: on_host = 0 but K/V are not device memory", c);
-        }
-        if (!aligned_to(ck.k, 16) || !aligned_to(ck.v, 16) || (ck.layer_stride * m->es()) % 16)
-            return fail(CB_E_SHAPE, "chunk %d: K/V and layer stride must be 16-byte aligned", c);
+        p->pool.push_back(ck);
+        q.ids.push_back(c);
+        q.offsets.push_back((int)o_next);
         o_next += ck.n_tokens;
+        if (o_next > (1 << 30)) return fail(CB_E_SHAPE, "prompt too long");
     }
     if (o_next + r->n_suffix > (1 << 30)) return fail(CB_E_SHAPE, "prompt too long");
-    p->Nc = (int)o_next;
-    p->Ns = r->n_suffix;
-    p->N = p->Nc + p->Ns;
-    if (p->N == 0) return fail(CB_E_INVALID, "empty prompt");
-    p->L = L;
-    p->s.assign(L + 1, 0);
-    if (r->schedule) {
-        p->s.assign(r->schedule, r->schedule + L + 1);
-    } else {
-        cb_status st = make_schedule(p->Nc, r->recompute_bp, r->schedule_kind, L, p->s.data());
-        if (st != CB_OK) return st;
-    }
-    if (r->min_tokens > 0 && p->N < r->min_tokens) p->s.assign(L + 1, p->Nc);
-    if (p->s[0] != 0 && p->s[0] != p->Nc)
-        return fail(CB_E_SCHEDULE, "s[0] = %d must be 0 or the chunk token count %d", p->s[0], p->Nc);
-    for (int l = 0; l < L; ++l)
-        if (p->s[l + 1] > p->s[l] || p->s[l + 1] < 0)
-            return fail(CB_E_SCHEDULE, "schedule must be non-increasing (s[%d]=%d, s[%d]=%d)", l,
-                        p->s[l], l + 1, p->s[l + 1]);
+    q.Nc = (int)o_next;
+    q.Ns = r->n_suffix;
+    q.N = q.Nc + q.Ns;
+    if (q.N == 0) return fail(CB_E_INVALID, "empty prompt");
+    cb_status st = request_schedule(p, q, r->schedule, r->recompute_bp, r->schedule_kind,
+                                    r->min_tokens, 0);
+    if (st != CB_OK) return st;
+    p->reqs.push_back(std::move(q));
     p->x0 = r->x0;
     p->dev_mode = r->dev_mode;
-    p->out = *o;
-    for (size_t c = 0; c < p->chunks.size(); ++c) {
-        const cb_chunk_kv& ck = p->chunks[c];
-        if (c % kMaxRotJobs == 0) p->jobs.push_back(RotJobs{});
-        RotJobs& js = p->jobs.back();
-        RotJob& j = js.j[js.n++];
-        j.k_src = ck.on_host ? nullptr : ck.k;
-        j.v_src = ck.on_host ? nullptr : ck.v;
-        j.src_layer_stride = ck.layer_stride;
-        j.dst_row = p->offsets[c];
-        j.n_tokens = ck.n_tokens;
-        j.delta = p->offsets[c];       // chunk-local position 0 -> real position o_c
-        js.max_tokens = std::max(js.max_tokens, ck.n_tokens);
+    p->fused_k = o->fused_k;
+    p->fused_v = o->fused_v;
+    p->sel_idx = o->sel_idx;
+    p->hidden_out = o->hidden_out;
+    p->deviation = o->deviation;
+    return plan_layout(p);
+}
+
+cb_status validate_batch(cb_model* m, const cb_batch_request* r, const cb_batch_outputs* o,
+                         cb_plan* p) {
+    if (!r || !o) return fail(CB_E_INVALID, "request/outputs is NULL");
+    if (!o->fused_k || !o->fused_v) return fail(CB_E_INVALID, "fused_k/fused_v are required");
+    if (!r->x0) return fail(CB_E_INVALID, "x0 is NULL");
+    if (r->n_requests <= 0 || !r->items) return fail(CB_E_INVALID, "no requests");
+    if (r->n_pool < 0 || (r->n_pool > 0 && !r->pool)) return fail(CB_E_INVALID, "pool is NULL");
+    if (r->dev_mode < 0 || r->dev_mode > 2) return fail(CB_E_INVALID, "dev_mode %d", r->dev_mode);
+    p->L = m->cfg.n_layers;
+    p->pool.assign(r->pool, r->pool + r->n_pool);
+    std::vector<char> checked(r->n_pool, 0);
+    for (int b = 0; b < r->n_requests; ++b) {
+        const cb_batch_item& it = r->items[b];
+        if (it.n_chunks < 0 || it.n_suffix < 0)
+            return fail(CB_E_INVALID, "request %d: negative counts", b);
+        if (it.n_chunks > 0 && !it.chunk_ids)
+            return fail(CB_E_INVALID, "request %d: chunk_ids is NULL", b);
+        ReqInfo q;
+        int64_t o_next = 0;
+        for (int c = 0; c < it.n_chunks; ++c) {
+            const int id = it.chunk_ids[c];
+            if (id < 0 || id >= r->n_pool)
+                return fail(CB_E_INVALID, "request %d: chunk id %d not in the pool", b, id);
+            if (!checked[id]) {
+                cb_status st = check_chunk(m, p->pool[id], id);
+                if (st != CB_OK) return st;
+                checked[id] = 1;
+            }
+            q.ids.push_back(id);
+            q.offsets.push_back((int)o_next);
+            o_next += p->pool[id].n_tokens;
+            if (o_next > (1 << 30)) return fail(CB_E_SHAPE, "request %d too long", b);
+        }
+        if (o_next + it.n_suffix > (1 << 30)) return fail(CB_E_SHAPE, "request %d too long", b);
+        q.Nc = (int)o_next;
+        q.Ns = it.n_suffix;
+        q.N = q.Nc + q.Ns;
+        if (q.N == 0) return fail(CB_E_INVALID, "request %d is empty", b);
+        cb_status st = request_schedule(p, q, it.schedule, r->recompute_bp, r->schedule_kind,
+                                        r->min_tokens, b);
+        if (st != CB_OK) return st;
+        p->reqs.push_back(std::move(q));
     }
-    return CB_OK;
+    p->x0 = r->x0;
+    p->dev_mode = r->dev_mode;
+    p->fused_k = o->fused_k;
+    p->fused_v = o->fused_v;
+    p->sel_idx = o->sel_idx;
+    p->hidden_out = o->hidden_out;
+    p->deviation = o->deviation;
+    return plan_layout(p);
 }
 
 cb_status ensure_rope(cb_model* m, int n_pos) {
     if (m->rope.n_pos >= n_pos) return CB_OK;
     return get_rope(m->cfg.rope_base, m->cfg.head_dim, n_pos, &m->rope);
+}
+
+int max_position(const cb_plan* p) {
+    int mx = 0;
+    for (const ReqInfo& q : p->reqs) mx = std::max(mx, q.pos0 + q.N);
+    return mx;
+}
+
+// Workspace, events and initial rows of a validated plan.
+cb_status plan_setup(cb_plan* p) {
+    cb_status st = ensure_rope(p->m, max_position(p));
+    if (st == CB_OK) st = plan_alloc(p);
+    if (st == CB_OK) st = plan_events(p);
+    if (st == CB_OK) st = plan_start(p);
+    return st;
+}
+
+cb_status run_all_layers(cb_plan* p) {
+    cb_status st = CB_OK;
+    for (int l = 0; l < p->L && st == CB_OK; ++l) {
+        st = do_fetch(p, l);
+        if (st == CB_OK && l + 1 < p->L) st = do_fetch(p, l + 1);   // overlaps layer l
+        if (st == CB_OK) st = do_layer(p, l);
+        if (st == CB_OK) p->next_layer++;
+    }
+    return st;
 }
 
 }  // namespace
@@ -654,16 +901,13 @@ cb_status cb_plan_create(cb_model* m, const cb_request* r, const cb_outputs* o, 
     p->m = m;
     p->stream = as_stream(stream);
     cb_status st = validate_request(m, r, o, p);
-    if (st == CB_OK) st = ensure_rope(m, p->N);
     if (st != CB_OK) {
         delete p;
         return st;
     }
     if (o->sel_count)
-        for (int l = 0; l < p->L; ++l) o->sel_count[l] = p->s[l + 1];
-    st = plan_alloc(p);
-    if (st == CB_OK) st = plan_events(p);
-    if (st == CB_OK) st = plan_start(p);
+        for (int l = 0; l < p->L; ++l) o->sel_count[l] = p->reqs[0].s[l + 1];
+    st = plan_setup(p);
     if (st != CB_OK) {
         plan_free(p);
         return st;
@@ -703,10 +947,27 @@ cb_status cb_blend(cb_model* m, const cb_request* r, const cb_outputs* o, void* 
     cb_plan* p = nullptr;
     cb_status st = cb_plan_create(m, r, o, stream, &p);
     if (st != CB_OK) return st;
-    for (int l = 0; l < p->L && st == CB_OK; ++l) {
-        if (l + 1 < p->L) st = do_fetch(p, l + 1);
-        if (st == CB_OK) st = cb_prefill_layer(p, l);
+    st = run_all_layers(p);
+    plan_free(p);
+    return st;
+}
+
+cb_status cb_blend_batch(cb_model* m, const cb_batch_request* r, const cb_batch_outputs* o,
+                         void* stream) {
+    if (!m) return fail(CB_E_INVALID, "model is NULL");
+    cb_plan* p = new cb_plan();
+    p->m = m;
+    p->stream = as_stream(stream);
+    cb_status st = validate_batch(m, r, o, p);
+    if (st != CB_OK) {
+        delete p;
+        return st;
     }
+    if (o->sel_count)
+        for (size_t b = 0; b < p->reqs.size(); ++b)
+            for (int l = 0; l < p->L; ++l) o->sel_count[b * p->L + l] = p->reqs[b].s[l + 1];
+    st = plan_setup(p);
+    if (st == CB_OK) st = run_all_layers(p);
     plan_free(p);
     return st;
 }
@@ -714,26 +975,26 @@ cb_status cb_blend(cb_model* m, const cb_request* r, const cb_outputs* o, void* 
 cb_status cb_prefill(cb_model* m, const void* x0, int32_t n_tokens, int32_t pos0, void* k_out,
                      void* v_out, float* hidden_out, void* stream) {
     if (!m || !x0 || !k_out || !v_out) return fail(CB_E_INVALID, "NULL argument");
-    if (n_tokens <= 0 || pos0 < 0) return fail(CB_E_INVALID, "n_tokens %d, pos0 %d", n_tokens, pos0);
+    if (n_tokens <= 0 || pos0 < 0 || (int64_t)pos0 + n_tokens > (1 << 30))
+        return fail(CB_E_INVALID, "n_tokens %d, pos0 %d", n_tokens, pos0);
     cb_plan* p = new cb_plan();
     p->m = m;
     p->stream = as_stream(stream);
-    p->prefill_mode = true;
     p->L = m->cfg.n_layers;
-    p->Nc = 0;
-    p->Ns = n_tokens;
-    p->N = n_tokens;
-    p->row_base = pos0;
-    p->s.assign(p->L + 1, 0);
+    ReqInfo q;
+    q.Ns = n_tokens;
+    q.N = n_tokens;
+    q.pos0 = pos0;
+    q.s.assign(p->L + 1, 0);
+    p->reqs.push_back(std::move(q));
+    p->kv_pos0 = pos0;
     p->x0 = x0;
-    p->out.fused_k = k_out;
-    p->out.fused_v = v_out;
-    p->out.hidden_out = hidden_out;
-    cb_status st = ensure_rope(m, pos0 + n_tokens);
-    if (st == CB_OK) st = plan_alloc(p);
-    if (st == CB_OK) st = plan_events(p);
-    if (st == CB_OK) st = plan_start(p);
-    for (int l = 0; l < p->L && st == CB_OK; ++l) st = cb_prefill_layer(p, l);
+    p->fused_k = k_out;
+    p->fused_v = v_out;
+    p->hidden_out = hidden_out;
+    cb_status st = plan_layout(p);
+    if (st == CB_OK) st = plan_setup(p);
+    if (st == CB_OK) st = run_all_layers(p);
     plan_free(p);
     return st;
 }
@@ -818,8 +1079,12 @@ cb_status cb_deviation(int32_t dtype, const void* k_new, const void* v_new, cons
         return fail(CB_E_INVALID, "NULL buffer");
     if (n_rows < 0 || row_elems <= 0 || row_elems % 8)
         return fail(CB_E_SHAPE, "row_elems must be a positive multiple of 8");
-    CB_HIP(launch_deviation(dtype, k_new, v_new, k_cached, v_cached, nullptr, 0, n_rows, row_elems,
-                            dev_mode, dev_out, nullptr, as_stream(stream)));
+    ReqTab t{};
+    t.n = 1;
+    t.max_c = n_rows;
+    t.r[0].n_c = n_rows;
+    CB_HIP(launch_deviation(dtype, k_new, v_new, k_cached, v_cached, nullptr, t, row_elems,
+                            dev_mode, dev_out, as_stream(stream)));
     return CB_OK;
 }
 
@@ -880,21 +1145,19 @@ cb_status cb_attention(int32_t dtype, const void* q, const int32_t* q_pos, int32
     if (head_dim != 64 && head_dim != 128) return fail(CB_E_UNSUPPORTED, "head_dim %d", head_dim);
     if (n_q > 0 && (!q || !q_pos || !k || !v || !out)) return fail(CB_E_INVALID, "NULL buffer");
     AttnArgs a{};
-    a.q = q; a.q_pos = q_pos; a.n_q = n_q; a.k = k; a.v = v; a.n_kv = n_kv;
+    a.q = q; a.q_pos = q_pos; a.k = k; a.v = v;
     a.n_q_heads = n_q_heads; a.n_kv_heads = n_kv_heads; a.head_dim = head_dim; a.out = out;
     const hipStream_t st = as_stream(stream);
-    const size_t need = attention_split_plan(dtype, n_q, n_kv, n_q_heads, head_dim, &a.seg_keys,
-                                             &a.max_seg);
+    const AttnRange range{0, n_q, 0, n_kv};
+    const size_t need = attention_workspace(dtype, &range, 1, n_q_heads, head_dim);
     void* ws = nullptr;
     if (need) {
         if (hipMallocAsync(&ws, need, st) != hipSuccess) {
             (void)hipGetLastError();
             return fail(CB_E_OOM, "attention workspace of %zu bytes", need);
         }
-        a.part_o = (float*)ws;
-        a.part_ml = (float*)ws + need / sizeof(float) / (head_dim + 2) * head_dim;
     }
-    const hipError_t e = launch_attention(dtype, a, st);
+    const hipError_t e = launch_attention(dtype, a, &range, 1, ws, need, st);
     if (ws) (void)hipFreeAsync(ws, st);
     if (e != hipSuccess) return fail(CB_E_HIP, "attention launch: %s", hipGetErrorString(e));
     return CB_OK;

@@ -38,26 +38,26 @@ __device__ __forceinline__ float sq_diff8(const T* a, const T* b) {
 }
 
 // One wave per row: lanes stride over the row in 8-element pieces.
+// blockIdx.y = request of the table, blockIdx.x * 4 + wave = its chunk row.
 template <typename T>
 __global__ __launch_bounds__(kDevThreads) void deviation_kernel(
     const T* __restrict__ kn, const T* __restrict__ vn, const T* __restrict__ kc,
-    const T* __restrict__ vc, const int* __restrict__ pos, int row_base, int n_rows, int kv_dim,
-    int mode, float* __restrict__ dev, float* __restrict__ dev_pos_out) {
+    const T* __restrict__ vc, const int* __restrict__ grow, const ReqTab t, int kv_dim,
+    int mode, float* __restrict__ dev) {
+    const ReqRows& q = t.r[blockIdx.y];
     const int lane = threadIdx.x & 63;
-    const int r = blockIdx.x * (kDevThreads / 64) + (threadIdx.x >> 6);
-    if (r >= n_rows) return;
+    const int i = blockIdx.x * (kDevThreads / 64) + (threadIdx.x >> 6);
+    if (i >= q.n_c) return;
+    const int r = q.r_off + i;
     const int64_t no = (int64_t)r * kv_dim;
-    const int64_t co = (int64_t)(pos ? pos[r] - row_base : r) * kv_dim;
+    const int64_t co = (int64_t)(grow ? grow[r] : r) * kv_dim;
     float acc = 0.f;
     if (mode != 2)
         for (int c = lane * 8; c < kv_dim; c += 512) acc += sq_diff8(kn + no + c, kc + co + c);
     if (mode != 1)
         for (int c = lane * 8; c < kv_dim; c += 512) acc += sq_diff8(vn + no + c, vc + co + c);
     acc = warp_sum(acc);
-    if (lane == 0) {
-        dev[r] = acc;
-        if (dev_pos_out) dev_pos_out[pos[r]] = acc;
-    }
+    if (lane == 0) dev[q.c_off + i] = acc;
 }
 
 __device__ __forceinline__ uint32_t rank_key(float f) {
@@ -169,40 +169,51 @@ __global__ __launch_bounds__(kSelThreads) void topk_kernel(const float* __restri
     select_rows(dev, n, k, [&](int slot, int i) { out[slot] = i; });
 }
 
+// One workgroup per request of the table.
 __global__ __launch_bounds__(kSelThreads) void blend_select_kernel(
-    const float* __restrict__ dev, int n_c, int k, int n_s, const int* __restrict__ pos_r,
-    int* __restrict__ sel_local, int* __restrict__ pos_q, int* __restrict__ sel_pos) {
-    select_rows(dev, n_c, k, [&](int slot, int i) {
-        const int p = pos_r[i];
-        sel_local[slot] = i;
-        pos_q[slot] = p;
-        if (sel_pos) sel_pos[slot] = p;
+    const float* __restrict__ dev, const ReqTab t, const int* __restrict__ pos_r,
+    const int* __restrict__ row_r, int* __restrict__ sel_local, int* __restrict__ pos_q,
+    int* __restrict__ row_q, int* __restrict__ sel_pos, float* __restrict__ dev_out) {
+    const ReqRows& q = t.r[blockIdx.x];
+    const float* d = dev + q.c_off;
+    select_rows(d, q.n_c, q.k, [&](int slot, int i) {
+        const int r = q.r_off + i;
+        const int p = pos_r[r];
+        sel_local[q.q_off + slot] = r;
+        pos_q[q.q_off + slot] = p;
+        row_q[q.q_off + slot] = row_r[r];
+        if (sel_pos) sel_pos[q.out_col + slot] = p;
     });
-    for (int s = threadIdx.x; s < n_s; s += kSelThreads) {
-        sel_local[k + s] = n_c + s;
-        pos_q[k + s] = pos_r[n_c + s];
+    for (int s = threadIdx.x; s < q.n_s; s += kSelThreads) {
+        const int r = q.r_off + q.n_c + s;
+        sel_local[q.q_off + q.k + s] = r;
+        pos_q[q.q_off + q.k + s] = pos_r[r];
+        row_q[q.q_off + q.k + s] = row_r[r];
     }
+    if (dev_out)
+        for (int i = threadIdx.x; i < q.n_c; i += kSelThreads)
+            dev_out[q.out_col + pos_r[q.r_off + i]] = d[i];
 }
 
 }  // namespace
 
 hipError_t launch_deviation(int dtype, const void* k_new, const void* v_new,
-                            const void* k_cached, const void* v_cached, const int* pos,
-                            int row_base, int n_rows, int kv_dim, int mode, float* dev,
-                            float* dev_pos_out, hipStream_t s) {
-    if (n_rows <= 0) return hipSuccess;
-    if (kv_dim % 8 != 0) return hipErrorInvalidValue;
+                            const void* k_cached, const void* v_cached, const int* grow,
+                            const ReqTab& t, int kv_dim, int mode, float* dev, hipStream_t s) {
+    if (t.n <= 0 || t.max_c <= 0) return hipSuccess;
+    if (t.n > kMaxReq || kv_dim % 8 != 0) return hipErrorInvalidValue;
+    for (int b = 0; b < t.n; ++b)
+        if (t.r[b].n_c > t.max_c || t.r[b].n_c < 0) return hipErrorInvalidValue;
     const int per = kDevThreads / 64;
-    dim3 grid((n_rows + per - 1) / per), block(kDevThreads);
+    dim3 grid((t.max_c + per - 1) / per, t.n), block(kDevThreads);
     if (dtype == BF16)
         hipLaunchKernelGGL(deviation_kernel<bf16>, grid, block, 0, s, (const bf16*)k_new,
-                           (const bf16*)v_new, (const bf16*)k_cached, (const bf16*)v_cached, pos,
-                           row_base, n_rows, kv_dim, mode, dev, dev_pos_out);
+                           (const bf16*)v_new, (const bf16*)k_cached, (const bf16*)v_cached, grow,
+                           t, kv_dim, mode, dev);
     else
         hipLaunchKernelGGL(deviation_kernel<float>, grid, block, 0, s, (const float*)k_new,
                            (const float*)v_new, (const float*)k_cached,
-                           (const float*)v_cached, pos, row_base, n_rows, kv_dim, mode, dev,
-                           dev_pos_out);
+                           (const float*)v_cached, grow, t, kv_dim, mode, dev);
     return hipGetLastError();
 }
 
@@ -212,12 +223,17 @@ hipError_t launch_topk(const float* dev, int n, int k, int* idx_out, hipStream_t
     return hipGetLastError();
 }
 
-hipError_t launch_select(const float* dev, int n_c, int k, int n_s, const int* pos_r,
-                         int* sel_local, int* pos_q, int* sel_pos, hipStream_t s) {
-    if (k > n_c || k < 0 || n_s < 0) return hipErrorInvalidValue;
-    if (k + n_s == 0) return hipSuccess;
-    hipLaunchKernelGGL(blend_select_kernel, dim3(1), dim3(kSelThreads), 0, s, dev, n_c, k, n_s,
-                       pos_r, sel_local, pos_q, sel_pos);
+hipError_t launch_select(const float* dev, const ReqTab& t, const int* pos_r, const int* row_r,
+                         int* sel_local, int* pos_q, int* row_q, int* sel_pos, float* dev_out,
+                         hipStream_t s) {
+    if (t.n <= 0) return hipSuccess;
+    if (t.n > kMaxReq) return hipErrorInvalidValue;
+    for (int b = 0; b < t.n; ++b) {
+        const ReqRows& q = t.r[b];
+        if (q.k > q.n_c || q.k < 0 || q.n_s < 0) return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL(blend_select_kernel, dim3(t.n), dim3(kSelThreads), 0, s, dev, t, pos_r,
+                       row_r, sel_local, pos_q, row_q, sel_pos, dev_out);
     return hipGetLastError();
 }
 

@@ -67,3 +67,63 @@ def run_gpu_blend(npk, model, case, dt, schedule, dev_mode=0, on_host=False, pla
     torch.cuda.synchronize()
     return {"fused_k": fk, "fused_v": fv, "sel": sel, "dev": dev_out, "hidden": hid[:n_last],
             "sel_count": cnt}
+
+
+def pool_inputs(bcase, dt, on_host=False):
+    """Pool chunk caches (device or pinned host); unused entries get the
+    first used entry's buffers (they are never read)."""
+    used = [c for c in bcase.pool if c is not None]
+    filler = used[0] if used else None
+    out = []
+    for c in bcase.pool:
+        k, v = c if c is not None else filler
+        kt, vt = dev(k, dt), dev(v, dt)
+        if on_host:
+            kt = kt.cpu().pin_memory()
+            vt = vt.cpu().pin_memory()
+        n = k.shape[1]
+        out.append({"k": kt, "v": vt, "n_tokens": n, "on_host": int(on_host),
+                    "layer_stride": n * k.shape[2] * k.shape[3]})
+    return out
+
+
+def run_gpu_batch(npk, model, bcase, dt, schedules=None, recompute_bp=1500,
+                  schedule_kind=0, dev_mode=0, on_host=False, dev_fill=float("nan")):
+    """cb_blend_batch over the whole batch; returns the stacked outputs split
+    per request (views) plus the raw stacked tensors."""
+    s = bcase.shape
+    L = s.n_layers
+    tdt = TORCH_DT[dt]
+    pool = pool_inputs(bcase, dt, on_host)
+    reqs = []
+    for i, r in enumerate(bcase.requests):
+        d = {"chunk_ids": r["chunk_ids"], "n_suffix": r["n_suffix"]}
+        if schedules is not None:
+            d["schedule"] = schedules[i]
+        reqs.append(d)
+    Ns = [c.n_tokens for c in bcase.cases]
+    Ncs = [c.n_chunk_tokens for c in bcase.cases]
+    Ntot, Nctot = sum(Ns), sum(Ncs)
+    x0 = dev(bcase.x0, dt)
+    fk = torch.full((L, Ntot, s.n_kv_heads, s.head_dim), float("nan"), dtype=tdt, device="cuda")
+    fv = torch.full_like(fk, float("nan"))
+    sel = torch.full((L, max(1, Nctot)), -1, dtype=torch.int32, device="cuda")
+    dev_out = torch.full((L, max(1, Nctot)), dev_fill, dtype=torch.float32, device="cuda")
+    # hidden rows per request are s_b[L] + N_s,b; computed from the returned counts,
+    # so allocate the upper bound N_b
+    hid = torch.full((Ntot, s.d_model), float("nan"), dtype=torch.float32, device="cuda")
+    cnt = npk.cb_blend_batch(model, pool, reqs, x0, fk, fv, sel_idx=sel, hidden_out=hid,
+                             deviation=dev_out, recompute_bp=recompute_bp,
+                             schedule_kind=schedule_kind, dev_mode=dev_mode)
+    torch.cuda.synchronize()
+    per = []
+    G = C = H = 0
+    for b, c in enumerate(bcase.cases):
+        n_last = c.n_suffix + cnt[b][-1]
+        per.append({"fused_k": fk[:, G:G + Ns[b]], "fused_v": fv[:, G:G + Ns[b]],
+                    "sel": sel[:, C:C + Ncs[b]], "dev": dev_out[:, C:C + Ncs[b]],
+                    "hidden": hid[H:H + n_last], "sel_count": cnt[b]})
+        G += Ns[b]
+        C += Ncs[b]
+        H += n_last
+    return per, {"fused_k": fk, "fused_v": fv, "sel": sel, "dev": dev_out, "hidden": hid[:H]}

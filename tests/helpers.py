@@ -67,3 +67,42 @@ def rel_err(got, ref):
     ref = np.asarray(ref, dtype=np.float64)
     den = np.max(np.abs(ref))
     return float(np.max(np.abs(got - ref)) / (den if den > 0 else 1.0))
+
+
+@dataclasses.dataclass
+class BatchCase:
+    shape: ModelShape
+    weights: list
+    pool: list                # [(K [L][n][Hkv][dh], V)] float64, rounded; None if unused
+    requests: list            # [{"chunk_ids": [...], "n_suffix": int}]
+    cases: list               # per request: Case over its own chunks (oracle input)
+    x0: np.ndarray            # stacked [sum N][d]
+    dtype: str
+
+
+def make_batch_case(shape, pool_lens, requests, seed=0, dtype="f64", n_layers=None,
+                    precompute_dtype=np.float64):
+    """A batch over a chunk pool: each used pool chunk is precomputed once by
+    the oracle at chunk-local positions from its own tokens; request b's
+    prompt is its chunks' tokens in order then its suffix tokens."""
+    from workloads import make_batch_tokens
+    L = shape.n_layers if n_layers is None else n_layers
+    if L != shape.n_layers:
+        shape = dataclasses.replace(shape, n_layers=L)
+    w = make_weights_np(shape, seed=seed, dtype=dtype)
+    emb = make_embedding_np(shape, seed=seed, dtype=dtype)
+    pool_tok, suf_tok = make_batch_tokens(shape, pool_lens, requests, seed=seed)
+    used = sorted({i for r in requests for i in r["chunk_ids"]})
+    pool = [None] * len(pool_lens)
+    for i in used:
+        k, v, _ = oracle.prefill(w, shape, emb[pool_tok[i]], pos0=0, dtype=precompute_dtype)
+        pool[i] = (round_to(k, dtype), round_to(v, dtype))
+    cases, xs = [], []
+    for r, st in zip(requests, suf_tok):
+        toks = np.concatenate([pool_tok[i] for i in r["chunk_ids"]] + [st]).astype(np.int64)
+        x0 = emb[toks]
+        offsets = list(np.cumsum([0] + [len(pool_tok[i]) for i in r["chunk_ids"]])[:-1])
+        cases.append(Case(shape, w, x0, [pool[i] for i in r["chunk_ids"]],
+                          [int(o) for o in offsets], int(r["n_suffix"]), dtype))
+        xs.append(x0)
+    return BatchCase(shape, w, pool, requests, cases, np.concatenate(xs, axis=0), dtype)

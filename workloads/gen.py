@@ -12,7 +12,8 @@ from .shapes import ModelShape, BatchedWorkload
 
 WEIGHT_STD = 0.02
 _TENSOR_IDS = {"embed": 0, "wq": 1, "wk": 2, "wv": 3, "wo": 4,
-               "w_gate": 5, "w_up": 6, "w_down": 7, "tokens": 8}
+               "w_gate": 5, "w_up": 6, "w_down": 7, "tokens": 8,
+               "batch_tokens": 9}
 
 
 def _rng(seed: int, layer: int, tensor: str) -> np.random.Generator:
@@ -88,3 +89,13 @@ def make_batched_requests(w: BatchedWorkload, seed: int = 0):
         suffix = int(g.integers(w.suffix_range[0], w.suffix_range[1] + 1))
         reqs.append({"chunk_ids": [int(i) for i in ids], "n_suffix": suffix})
     return pool_lens.astype(np.int64), reqs
+
+
+def make_batch_tokens(shape: ModelShape, pool_lens, reqs, seed: int = 0):
+    """Token ids of every pool chunk and of every request's suffix (seeded;
+    a chunk has the same tokens wherever it is used)."""
+    g = _rng(seed, -1, "batch_tokens")
+    pool_tokens = [g.integers(0, shape.vocab, size=int(n), dtype=np.int64) for n in pool_lens]
+    suffix_tokens = [g.integers(0, shape.vocab, size=int(r["n_suffix"]), dtype=np.int64)
+                     for r in reqs]
+    return pool_tokens, suffix_tokens

@@ -97,3 +97,8 @@ class BatchedWorkload:
 
 
 BATCHED_LLAMA7B = BatchedWorkload("batched-32req-llama2-7b-shape-zipf1.1", LLAMA7B)
+# Small batch of the tiny model for parity tests: ragged chunks shared
+# between requests, short suffixes.
+BATCHED_TINY = BatchedWorkload("batched-6req-tiny", TINY, n_requests=6, pool_size=10,
+                               chunk_len_range=(17, 150), chunks_per_req=(1, 4),
+                               suffix_range=(1, 40))
