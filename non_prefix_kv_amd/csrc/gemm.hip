@@ -9,14 +9,19 @@
 //   EPI_STORE_F32 plain fp32 store (kernel-level entry point)
 //
 // Tiling for gfx950: a 128x128 output tile per 256-thread workgroup, four
-// wave64s in a 2x2 grid, each wave 64x64 as 4x4 16x16 MFMA tiles.  K advances
+// wave64s in a 2x2 grid, each wave 64x64: 2x2 32x32x16 MFMA tiles for bf16
+// (the 32x32 form issues about 1.4x the flops per cycle of the 16x16x32 form
+// on gfx950: 1.87 vs 1.35 PFLOP/s measured in a register-only loop), 4x4
+// 16x16 tiles of 16x16x4 f32 MFMAs for f32.  K advances
 // 128 bytes per step (64 bf16 / 32 f32) through double-buffered LDS.  LDS rows
-// are unpadded 128-byte rows of eight 16-byte chunks stored at chunk index
-// (chunk XOR row % 8): the fragment reads of 16 rows and the staging stores
-// are then free of bank conflicts (measured: zero conflict cycles, versus a
-// third of LDS cycles with 16-byte row padding).  Workgroups are renumbered
+// are unpadded 128-byte rows of eight 16-byte chunks stored at a swizzled
+// chunk index (see swz): fragment reads and staging stores are then free of
+// bank conflicts (measured: zero conflict cycles, versus a third of LDS
+// cycles with 16-byte row padding).  Workgroups are renumbered
 // so that consecutive tile ids (the row tiles that share one weight column
 // block) land on the same XCD and reuse that XCD's L2.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace cb {
@@ -24,6 +29,7 @@ namespace cb {
 namespace {
 
 constexpr int BM = 128, BN = 128, kThreads = 256;
+constexpr int kGroupM = 8;               // row tiles per rasterization group
 constexpr int kRowBytes = 128;           // K-slice per stage, bytes per row
 
 template <typename T> struct Tile {
@@ -34,10 +40,16 @@ template <typename T> struct Tile {
 
 // Element offset in a swizzled LDS tile of the 16-byte chunk that holds
 // row r, element column c (c a multiple of 16 bytes' worth of elements).
+// The chunk index is XORed with a function of the row chosen so that the
+// fragment reads are free of bank conflicts (measured with
+// SQ_LDS_BANK_CONFLICT): rows 0..15 of one chunk column for the 16x16 f32
+// fragments (key: row % 8), rows 0..31 of two chunk columns for the 32x32
+// bf16 fragments (key: (row / 2) % 8; row % 8 gives a 2-way conflict there).
 template <typename T>
 __device__ __forceinline__ int swz(int r, int c) {
     constexpr int VEC = Tile<T>::VEC;
-    return r * Tile<T>::LDK + (((c / VEC) ^ r) & 7) * VEC;
+    const int key = sizeof(T) == 2 ? (r >> 1) : r;
+    return r * Tile<T>::LDK + (((c / VEC) ^ key) & 7) * VEC;
 }
 
 // A fragment (8 consecutive reduction elements of one row) from a swizzled
@@ -64,13 +76,25 @@ __device__ __forceinline__ int xcd_remap(int hw, int total) {
     return xcd * base + min(xcd, rem) + j;
 }
 
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ void mfma32(floatx16& acc, const bf16x8& a, const bf16x8& b) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+}
+
+template <typename T> constexpr bool is_bf16() { return sizeof(T) == 2; }
+
 // Row v (0..BN-1) of the block's B tile.  Rows past N are clamped to the
-// last row: they only feed output columns that are never stored.
+// last row: they only feed output columns that are never stored.  For the
+// gate/up launch the tile interleaves gate and up rows so that each wave's
+// two MFMA column tiles (32 wide for bf16, pairs of 16 for f32) hold gate
+// and up of the same output columns.
 template <typename T, int EPI>
 __device__ __forceinline__ const T* b_row_ptr(const GemmArgs& g, int v, int n_tile) {
     if (EPI == EPI_SWIGLU) {
-        const int oc = min(n_tile * (BN / 2) + (v >> 5) * 16 + (v & 15), g.N - 1);
-        return static_cast<const T*>((v & 16) ? g.b1 : g.b0) + (int64_t)oc * g.K;
+        constexpr int W = is_bf16<T>() ? 32 : 16;
+        const int oc = min(n_tile * (BN / 2) + (v / (2 * W)) * W + (v % W), g.N - 1);
+        return static_cast<const T*>((v & W) ? g.b1 : g.b0) + (int64_t)oc * g.K;
     } else {
         const int n = min(n_tile * BN + v, g.N - 1);
         if (EPI == EPI_QKV) {
@@ -79,6 +103,81 @@ __device__ __forceinline__ const T* b_row_ptr(const GemmArgs& g, int v, int n_ti
             return static_cast<const T*>(g.b2) + (int64_t)(n - g.n0 - g.n1) * g.K;
         }
         return static_cast<const T*>(g.b0) + (int64_t)n * g.K;
+    }
+}
+
+// Epilogue of one wave's 64x64 block.  Element e of accumulator (i, j) is
+// C[row][col] with
+//   bf16: row = wm*64 + i*32 + 8*(e/4) + 4*(lane/32) + e%4, col = wn*64 + j*32 + lane%32
+//   f32:  row = wm*64 + i*16 + 4*(lane/16) + e,            col = wn*64 + j*16 + lane%16
+// (offsets within the block tile).  One output column per lane.
+template <typename T, int EPI, typename Acc, int NT>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, const Acc (&acc)[NT][NT], int m_tile,
+                                         int n_tile, int wm, int wn, int lane) {
+    constexpr int TW = is_bf16<T>() ? 32 : 16;          // MFMA tile width
+    constexpr int NE = (int)(sizeof(Acc) / 4);
+    const int cl = lane % TW;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int row = m_tile * BM + wm * 64 + i * TW +
+                            (is_bf16<T>() ? 8 * (e / 4) + 4 * (lane / 32) + e % 4
+                                          : 4 * (lane / 16) + e);
+            const bool row_ok = row < g.M;
+            if (EPI == EPI_SWIGLU) {
+#pragma unroll
+                for (int jj = 0; jj < NT / 2; ++jj) {
+                    const int oc = n_tile * (BN / 2) + wn * 32 + jj * TW + cl;
+                    if (row_ok && oc < g.N) {
+                        const float gt = acc[i][2 * jj][e], up = acc[i][2 * jj + 1][e];
+                        static_cast<T*>(g.out0)[(int64_t)row * g.N + oc] =
+                            from_f32<T>(silu_f(gt) * up);
+                    }
+                }
+            } else if (EPI == EPI_QKV) {
+                const int p = row_ok ? g.pos[row] : 0;
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int col = n_tile * BN + wn * 64 + j * TW + cl;
+                    const float x = acc[i][j][e];
+                    const float partner = __shfl_xor(x, 1, 64);
+                    if (!row_ok || col >= g.N) continue;
+                    float y = x;
+                    T* dst;
+                    int64_t off;
+                    int seg_col;
+                    if (col < g.n0) {
+                        dst = static_cast<T*>(g.out0); seg_col = col;
+                        off = (int64_t)row * g.n0 + seg_col;
+                    } else if (col < g.n0 + g.n1) {
+                        dst = static_cast<T*>(g.out1); seg_col = col - g.n0;
+                        off = (int64_t)row * g.n1 + seg_col;
+                    } else {
+                        dst = static_cast<T*>(g.out2); seg_col = col - g.n0 - g.n1;
+                        off = (int64_t)row * (g.N - g.n0 - g.n1) + seg_col;
+                    }
+                    if (col < g.n0 + g.n1) {
+                        const int d = seg_col % g.head_dim;
+                        const float2 cs = g.rope.tab[(int64_t)p * g.rope.half + (d >> 1)];
+                        y = (d & 1) ? partner * cs.y + x * cs.x : x * cs.x - partner * cs.y;
+                    }
+                    dst[off] = from_f32<T>(y);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < NT; ++j) {
+                    const int col = n_tile * BN + wn * 64 + j * TW + cl;
+                    if (!row_ok || col >= g.N) continue;
+                    float y = acc[i][j][e];
+                    if (EPI == EPI_RESID) {
+                        const int rr = g.ridx ? g.ridx[row] : row;
+                        y += g.resid[(int64_t)rr * g.N + col];
+                    }
+                    static_cast<float*>(g.out0)[(int64_t)row * g.N + col] = y;
+                }
+            }
+        }
     }
 }
 
@@ -92,8 +191,16 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
     const int m_tiles = (g.M + BM - 1) / BM;
     const int n_cols_per_tile = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
     const int n_tiles = (g.N + n_cols_per_tile - 1) / n_cols_per_tile;
+    // Logical tiles in groups of kGroupM row tiles: the workgroups resident
+    // on one XCD at a time cover a kGroupM x (64 / kGroupM) patch of output
+    // tiles, so each K slice of A and of B they load is shared in that XCD's
+    // L2 by several of them.
     const int tile = xcd_remap(blockIdx.x, m_tiles * n_tiles);
-    const int m_tile = tile % m_tiles, n_tile = tile / m_tiles;
+    const int group = tile / (kGroupM * n_tiles);
+    const int first_m = group * kGroupM;
+    const int gm = min(m_tiles - first_m, kGroupM);
+    const int in_group = tile - group * kGroupM * n_tiles;
+    const int m_tile = first_m + in_group % gm, n_tile = in_group / gm;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -132,26 +239,54 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
         }
     };
 
-    floatx4 acc[4][4];
+    // Accumulators: bf16 2x2 32x32 tiles, f32 4x4 16x16 tiles (64 floats per lane).
+    constexpr int NT = is_bf16<T>() ? 2 : 4;
+    using Acc = typename std::conditional<is_bf16<T>(), floatx16, floatx4>::type;
+    Acc acc[NT][NT];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NT; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+            for (int e = 0; e < (int)(sizeof(Acc) / 4); ++e) acc[i][j][e] = 0.f;
 
     const int KT = g.K / BK;
-    const int fr = lane & 15, fk = (lane >> 4) * 8;
     auto compute = [&](int buf) {
+        if constexpr (is_bf16<T>()) {
+            // lane l: row l % 32 of the tile, reduction elements 8 (l / 32) + 0..7
+            const int fr = lane & 31, fk = (lane >> 5) * 8;
 #pragma unroll
-        for (int ks = 0; ks < BK; ks += 32) {
-            Frag<T> af[4], bfr[4];
+            for (int ks = 0; ks < BK; ks += 16) {
+                bf16x8 af[2], bfr[2];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) af[i] = lds_frag<T>(sA[buf], wm * 64 + i * 16 + fr, ks + fk);
+                for (int i = 0; i < 2; ++i)
+                    af[i] = *reinterpret_cast<const bf16x8*>(
+                        &sA[buf][swz<T>(wm * 64 + i * 32 + fr, ks + fk)]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bfr[j] = lds_frag<T>(sB[buf], wn * 64 + j * 16 + fr, ks + fk);
+                for (int j = 0; j < 2; ++j)
+                    bfr[j] = *reinterpret_cast<const bf16x8*>(
+                        &sB[buf][swz<T>(wn * 64 + j * 32 + fr, ks + fk)]);
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+                for (int i = 0; i < 2; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j) mfma16(acc[i][j], af[i], bfr[j]);
+                    for (int j = 0; j < 2; ++j) mfma32(acc[i][j], af[i], bfr[j]);
+            }
+        } else {
+            const int fr = lane & 15, fk = (lane >> 4) * 8;
+#pragma unroll
+            for (int ks = 0; ks < BK; ks += 32) {
+                Frag<T> af[4], bfr[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    af[i] = lds_frag<T>(sA[buf], wm * 64 + i * 16 + fr, ks + fk);
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    bfr[j] = lds_frag<T>(sB[buf], wn * 64 + j * 16 + fr, ks + fk);
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) mfma16(acc[i][j], af[i], bfr[j]);
+            }
         }
     };
     // Steady state, unrolled by two so buffers and register sets are static:
@@ -192,69 +327,327 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
         compute(0);
     }
 
-    // Epilogue.  acc[i][j][e] = C[row][col] with
-    // row = m_tile*128 + wm*64 + i*16 + 4*(lane/16) + e, col = ... + j*16 + lane%16.
-    const int row0 = m_tile * BM + wm * 64 + (lane >> 4) * 4;
+    epilogue<T, EPI>(g, acc, m_tile, n_tile, wm, wn, lane);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 path with direct-to-LDS loads.  Each buffer_load ... lds of a wave
+// writes 64 x 16 B to consecutive LDS bytes: the 8 lanes of one tile row
+// fetch that row's 16-byte chunks in swizzled order, so the LDS image is the
+// same conflict-free layout as above without staging registers or LDS store
+// instructions.  S stages of A and B (32 KB each) form a ring: while stage kt
+// is multiplied out, stages kt+1 .. kt+S-1 are in flight.  Rows past M (or
+// past the end of a weight matrix) lie outside the buffer resource's range
+// and read as zero.  Fragments of the next 16-wide K step are read from LDS
+// while the current step's MFMAs run.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor: base address, stride 0, range `bytes`.
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xFFFF), bytes, 0x00020000};
+}
+
+// 16 bytes per lane from buffer offset voff + soff into LDS at m0 + 16 * lane.
+// Issued as inline assembly so that the compiler's memory model does not see
+// a store to LDS (it would otherwise wait for every outstanding copy before
+// any LDS read); completion is tracked by the explicit vmcnt waits below and
+// the "memory" clobber keeps LDS reads from moving across the copy.
+__device__ __forceinline__ void dma16(i32x4 rsrc, int voff, int soff, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
+                 : "memory", "m0");
+}
+
+// Byte range of the wave's 32-row slice: rows left (clamped to 0..32) x row bytes.
+__device__ __forceinline__ int slice_bytes(int64_t rows_left, int row_bytes) {
+    const int r = rows_left < 0 ? 0 : (rows_left > 32 ? 32 : (int)rows_left);
+    return r * row_bytes;
+}
+
+// s_waitcnt with only the vector-memory counter limited to n (n < 64).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Epilogue of the direct-to-LDS kernel, staged through LDS so that global
+// traffic is row-contiguous: every wave writes its 64x64 fp32 block into a
+// row-major 128 x (128 + 8) tile (the 8-float pad puts the two half-waves of
+// a store on disjoint banks), then each thread finishes 4 consecutive
+// columns of 16 rows: one 16-byte residual / RoPE-table load and one vector
+// store per row.  `lds` is free, 16-byte aligned memory of >= 128*136 floats.
+constexpr int kEpiLd = BN + 8;
+template <int EPI>
+__device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const floatx16 (&acc)[2][2],
+                                             int m_tile, int n_tile, int wm, int wn, int lane,
+                                             float* lds) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int row = row0 + i * 16 + e;
-            const bool row_ok = row < g.M;
-            if (EPI == EPI_SWIGLU) {
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-                    const int oc = n_tile * (BN / 2) + wn * 32 + jj * 16 + fr;
-                    if (row_ok && oc < g.N) {
-                        const float gt = acc[i][2 * jj][e], up = acc[i][2 * jj + 1][e];
-                        static_cast<T*>(g.out0)[(int64_t)row * g.N + oc] =
-                            from_f32<T>(silu_f(gt) * up);
-                    }
-                }
-            } else if (EPI == EPI_QKV) {
-                const int p = row_ok ? g.pos[row] : 0;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int col = n_tile * BN + wn * 64 + j * 16 + fr;
-                    const float x = acc[i][j][e];
-                    const float partner = __shfl_xor(x, 1, 64);
-                    if (!row_ok || col >= g.N) continue;
-                    float y = x;
-                    T* dst;
-                    int64_t off;
-                    int seg_col;
-                    if (col < g.n0) {
-                        dst = static_cast<T*>(g.out0); seg_col = col;
-                        off = (int64_t)row * g.n0 + seg_col;
-                    } else if (col < g.n0 + g.n1) {
-                        dst = static_cast<T*>(g.out1); seg_col = col - g.n0;
-                        off = (int64_t)row * g.n1 + seg_col;
-                    } else {
-                        dst = static_cast<T*>(g.out2); seg_col = col - g.n0 - g.n1;
-                        off = (int64_t)row * (g.N - g.n0 - g.n1) + seg_col;
-                    }
-                    if (col < g.n0 + g.n1) {
-                        const int d = seg_col % g.head_dim;
-                        const float2 cs = g.rope.tab[(int64_t)p * g.rope.half + (d >> 1)];
-                        y = (d & 1) ? partner * cs.y + x * cs.x : x * cs.x - partner * cs.y;
-                    }
-                    dst[off] = from_f32<T>(y);
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int col = n_tile * BN + wn * 64 + j * 16 + fr;
-                    if (!row_ok || col >= g.N) continue;
-                    float y = acc[i][j][e];
-                    if (EPI == EPI_RESID) {
-                        const int rr = g.ridx ? g.ridx[row] : row;
-                        y += g.resid[(int64_t)rr * g.N + col];
-                    }
-                    static_cast<float*>(g.out0)[(int64_t)row * g.N + col] = y;
-                }
+            for (int e = 0; e < 16; ++e) {
+                const int r = wm * 64 + i * 32 + 8 * (e / 4) + 4 * (lane / 32) + e % 4;
+                const int c = wn * 64 + j * 32 + lane % 32;
+                lds[r * kEpiLd + c] = acc[i][j][e];
+            }
+    __syncthreads();
+    const int t = threadIdx.x;
+    const int cc = (t % 32) * 4;                  // first of this thread's 4 columns
+    const int row0 = m_tile * BM + t / 32;
+    if (EPI == EPI_SWIGLU) {
+        // output columns oc, oc+1 of the tile's 64: gate at LDS column
+        // (oc/32)*64 + oc%32, up 32 columns further
+        const int oc = (t % 32) * 2;
+        const int gc = (oc / 32) * 64 + oc % 32;
+        const int col = n_tile * (BN / 2) + oc;
+#pragma unroll 4
+        for (int p = 0; p < 16; ++p) {
+            const int rl = t / 32 + 8 * p, row = row0 + 8 * p;
+            if (row >= g.M) break;
+            const float2 gt = *reinterpret_cast<const float2*>(&lds[rl * kEpiLd + gc]);
+            const float2 up = *reinterpret_cast<const float2*>(&lds[rl * kEpiLd + gc + 32]);
+            bf16* dst = static_cast<bf16*>(g.out0) + (int64_t)row * g.N + col;
+            if (col + 1 < g.N) {
+                typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                *reinterpret_cast<bf16x2*>(dst) =
+                    bf16x2{static_cast<bf16>(silu_f(gt.x) * up.x), static_cast<bf16>(silu_f(gt.y) * up.y)};
+            } else if (col < g.N) {
+                dst[0] = static_cast<bf16>(silu_f(gt.x) * up.x);
             }
         }
+        return;
     }
+    const int col = n_tile * BN + cc;
+    if (EPI == EPI_QKV) {
+        // the tile lies in one of q, k, v (checked by the launcher)
+        const int c0 = n_tile * BN;
+        bf16* base;
+        int width, local;
+        bool rope;
+        if (c0 < g.n0) { base = static_cast<bf16*>(g.out0); width = g.n0; local = col; rope = true; }
+        else if (c0 < g.n0 + g.n1) {
+            base = static_cast<bf16*>(g.out1); width = g.n1; local = col - g.n0; rope = true;
+        } else {
+            base = static_cast<bf16*>(g.out2); width = g.N - g.n0 - g.n1; local = col - g.n0 - g.n1;
+            rope = false;
+        }
+        const int hd = local % g.head_dim;         // multiple of 4: pairs (hd, hd+1), (hd+2, hd+3)
+#pragma unroll 4
+        for (int p = 0; p < 16; ++p) {
+            const int rl = t / 32 + 8 * p, row = row0 + 8 * p;
+            if (row >= g.M) break;
+            const floatx4 x = *reinterpret_cast<const floatx4*>(&lds[rl * kEpiLd + cc]);
+            floatx4 y = x;
+            if (rope) {
+                const floatx4 cs = *reinterpret_cast<const floatx4*>(
+                    &g.rope.tab[(int64_t)g.pos[row] * g.rope.half + (hd >> 1)]);
+                y[0] = x[0] * cs[0] - x[1] * cs[1];
+                y[1] = x[0] * cs[1] + x[1] * cs[0];
+                y[2] = x[2] * cs[2] - x[3] * cs[3];
+                y[3] = x[2] * cs[3] + x[3] * cs[2];
+            }
+            *reinterpret_cast<bf16x4*>(base + (int64_t)row * width + local) =
+                bf16x4{static_cast<bf16>(y[0]), static_cast<bf16>(y[1]), static_cast<bf16>(y[2]),
+                       static_cast<bf16>(y[3])};
+        }
+        return;
+    }
+    // STORE_F32 / RESID: fp32 rows; vector path when the row length allows
+    const bool vec = (g.N % 4) == 0;
+#pragma unroll 4
+    for (int p = 0; p < 16; ++p) {
+        const int rl = t / 32 + 8 * p, row = row0 + 8 * p;
+        if (row >= g.M) break;
+        floatx4 y = *reinterpret_cast<const floatx4*>(&lds[rl * kEpiLd + cc]);
+        float* dst = static_cast<float*>(g.out0) + (int64_t)row * g.N + col;
+        const float* res = nullptr;
+        if (EPI == EPI_RESID)
+            res = g.resid + (int64_t)(g.ridx ? g.ridx[row] : row) * g.N + col;
+        if (vec && col + 3 < g.N) {
+            if (EPI == EPI_RESID) y += *reinterpret_cast<const floatx4*>(res);
+            *reinterpret_cast<floatx4*>(dst) = y;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                if (col + k < g.N) dst[k] = y[k] + (EPI == EPI_RESID ? res[k] : 0.f);
+        }
+    }
+}
+
+
+template <int EPI, int S>
+__global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(GemmArgs g) {
+    static_assert(S >= 3 && S <= 4, "stages");
+    constexpr int BK = 64;                    // bf16 per stage row (128 B)
+    constexpr int HALF = BM * BK;             // elements of the A (then B) part of a stage
+    __shared__ __attribute__((aligned(16))) bf16 sm0[S * 2 * HALF];   // stage ring
+    auto stage = [&](auto ic) -> bf16* { return sm0 + decltype(ic)::value * 2 * HALF; };
+
+    const int m_tiles = (g.M + BM - 1) / BM;
+    const int n_cols_per_tile = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+    const int n_tiles = (g.N + n_cols_per_tile - 1) / n_cols_per_tile;
+    const int tile = xcd_remap(blockIdx.x, m_tiles * n_tiles);
+    const int group = tile / (kGroupM * n_tiles);
+    const int first_m = group * kGroupM;
+    const int gm = min(m_tiles - first_m, kGroupM);
+    const int in_group = tile - group * kGroupM * n_tiles;
+    const int m_tile = first_m + in_group % gm, n_tile = in_group / gm;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar descriptors
+    const int wm = wave >> 1, wn = wave & 1;
+    const int Kb = g.K * 2;                   // bytes per row
+
+    // This wave loads rows 32*wave .. +31 of the A tile and of the B tile.
+    const bf16* a_base = static_cast<const bf16*>(g.a) + ((int64_t)m_tile * BM + 32 * wave) * g.K;
+    const int a_bytes = slice_bytes((int64_t)g.M - (int64_t)m_tile * BM - 32 * wave, Kb);
+    const bf16* b_base;
+    int64_t b_rows;
+    if (EPI == EPI_SWIGLU) {
+        const int oc0 = n_tile * (BN / 2) + (wave >> 1) * 32;
+        b_base = static_cast<const bf16*>((wave & 1) ? g.b1 : g.b0) + (int64_t)oc0 * g.K;
+        b_rows = g.N - oc0;
+    } else if (EPI == EPI_QKV) {
+        // the whole 128-column tile lies inside one of q, k, v
+        const int c0 = n_tile * BN;
+        const void* mat;
+        int local, rows;
+        if (c0 < g.n0) { mat = g.b0; local = c0; rows = g.n0; }
+        else if (c0 < g.n0 + g.n1) { mat = g.b1; local = c0 - g.n0; rows = g.n1; }
+        else { mat = g.b2; local = c0 - g.n0 - g.n1; rows = g.N - g.n0 - g.n1; }
+        b_base = static_cast<const bf16*>(mat) + ((int64_t)local + 32 * wave) * g.K;
+        b_rows = rows - local - 32 * wave;
+    } else {
+        b_base = static_cast<const bf16*>(g.b0) + ((int64_t)n_tile * BN + 32 * wave) * g.K;
+        b_rows = g.N - (int64_t)n_tile * BN - 32 * wave;
+    }
+    const int b_bytes = slice_bytes(b_rows, Kb);
+
+    // Lane i fetches row i/8 (of 8) at LDS slot i%8, i.e. global chunk
+    // slot ^ key(row), key(r) = (r/2) % 8; rows 8j.. of the wave's 32 differ
+    // in key by 4 for odd j.
+    const int r8 = lane >> 3, slot = lane & 7;
+    const int v_even = r8 * Kb + ((slot ^ (r8 >> 1)) & 7) * 16;
+    const int v_odd = r8 * Kb + ((slot ^ ((r8 >> 1) + 4)) & 7) * 16;
+
+    const int KT = g.K / BK;
+    auto issue = [&](int kt, bf16* buf) {
+        // stages past the end read nothing: an empty range makes every access miss
+        const bool live = kt < KT;
+        const i32x4 xa = make_rsrc(a_base, live ? a_bytes : 0);
+        const i32x4 xb = make_rsrc(b_base, live ? b_bytes : 0);
+        const int ko = kt * 128;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int vo = (j & 1) ? v_odd : v_even;
+            const int so = ko + 8 * j * Kb;
+            const uint32_t da = (uint32_t)reinterpret_cast<uintptr_t>(buf + (32 * wave + 8 * j) * BK);
+            dma16(xa, vo, so, da);
+            dma16(xb, vo, so, da + HALF * 2);
+        }
+    };
+
+    floatx16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    const int fr = lane & 31, fk = (lane >> 5) * 8;
+    auto read_frags = [&](const bf16* buf, int ks, bf16x8 (&fa)[2], bf16x8 (&fb)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            fa[i] = *reinterpret_cast<const bf16x8*>(&buf[swz<bf16>(wm * 64 + i * 32 + fr, ks + fk)]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            fb[j] = *reinterpret_cast<const bf16x8*>(
+                &buf[HALF + swz<bf16>(wn * 64 + j * 32 + fr, ks + fk)]);
+    };
+    auto mfma_step = [&](const bf16x8 (&fa)[2], const bf16x8 (&fb)[2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) mfma32(acc[i][j], fa[i], fb[j]);
+    };
+    // One K stage out of buffer I (its first fragments already in fa0/fb0).
+    // The barrier that publishes stage kt+1 sits between the second and
+    // third 16-wide steps, so it overlaps queued MFMAs; after it the buffer
+    // of stage kt-1 is refilled with stage kt+S-1 and the first fragments of
+    // stage kt+1 are read while the last MFMAs of stage kt run.
+    bf16x8 fa0[2], fb0[2], fa1[2], fb1[2];
+    // Keeps each region's 4 MFMAs interleaved one to one with the 4 fragment
+    // reads of the next 16-wide step (the reads then return under the MFMAs).
+    auto interleave = [&]() {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        }
+    };
+    auto step = [&](auto ic, int kt) {
+        constexpr int I = decltype(ic)::value;
+        const bf16* buf = stage(ic);
+        read_frags(buf, 16, fa1, fb1);
+        mfma_step(fa0, fb0);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(buf, 32, fa0, fb0);
+        mfma_step(fa1, fb1);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<(S - 3) * 8>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(buf, 48, fa1, fb1);
+        // the copies of stage kt+S-1 go out between the MFMAs of this step
+        {
+            const int kn = kt + S - 1;
+            bf16* dst = stage(std::integral_constant<int, (I + S - 1) % S>{});
+            const bool live = kn < KT;
+            const i32x4 xa = make_rsrc(a_base, live ? a_bytes : 0);
+            const i32x4 xb = make_rsrc(b_base, live ? b_bytes : 0);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                mfma32(acc[t >> 1][t & 1], fa0[t >> 1], fb0[t & 1]);
+                const int vo = (t & 1) ? v_odd : v_even;
+                const int so = kn * 128 + 8 * t * Kb;
+                const uint32_t da =
+                    (uint32_t)reinterpret_cast<uintptr_t>(dst + (32 * wave + 8 * t) * BK);
+                dma16(xa, vo, so, da);
+                dma16(xb, vo, so, da + HALF * 2);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // (after the last stage this reads a buffer of zeros that is never used)
+        read_frags(stage(std::integral_constant<int, (I + 1) % S>{}), 0, fa0, fb0);
+        mfma_step(fa1, fb1);
+        interleave();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    issue(0, stage(std::integral_constant<int, 0>{}));
+    issue(1, stage(std::integral_constant<int, 1>{}));
+    if constexpr (S > 3) issue(2, stage(std::integral_constant<int, 2>{}));
+    wait_vm<(S - 2) * 8>();
+    __builtin_amdgcn_s_barrier();
+    read_frags(sm0, 0, fa0, fb0);
+    for (int kt = 0; kt < KT; kt += S) {     // KT is a multiple of S
+        step(std::integral_constant<int, 0>{}, kt);
+        step(std::integral_constant<int, 1>{}, kt + 1);
+        step(std::integral_constant<int, 2>{}, kt + 2);
+        if constexpr (S > 3) step(std::integral_constant<int, 3>{}, kt + 3);
+    }
+    // the trailing copies (empty ranges) still write LDS: let them land, and
+    // let every wave finish its last fragment reads, before reusing LDS
+    wait_vm<0>();
+    __syncthreads();
+    static_assert(S * 2 * HALF * 2 >= BM * kEpiLd * 4, "epilogue staging fits the stage ring");
+    epilogue_lds<EPI>(g, acc, m_tile, n_tile, wm, wn, lane, reinterpret_cast<float*>(sm0));
 }
 
 template <typename T, int EPI>
@@ -266,8 +659,40 @@ hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
     return hipGetLastError();
 }
 
+constexpr int kDmaStages = 4;            // LDS ring depth of the bf16 kernel
+
+template <int EPI>
+hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
+    const int m_tiles = (g.M + BM - 1) / BM;
+    const int cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
+    const int n_tiles = (g.N + cols - 1) / cols;
+    hipLaunchKernelGGL((gemm_dma_kernel<EPI, kDmaStages>), dim3(m_tiles * n_tiles),
+                       dim3(kThreads), 0, s, g);
+    return hipGetLastError();
+}
+
+// The direct-to-LDS kernel needs whole 16-byte chunks per row, buffer
+// offsets below 2^31 and, for q/k/v, tiles that do not straddle matrices.
+bool dma_ok(int epi, const GemmArgs& g) {
+    if (g.K % (64 * kDmaStages) != 0 || (int64_t)g.K * 2 * 32 + 128 >= (int64_t)1 << 31)
+        return false;
+    if (epi == EPI_QKV && (g.n0 % BN != 0 || g.n1 % BN != 0)) return false;
+    return true;
+}
+
 template <typename T>
 hipError_t launch_dtype(int epi, const GemmArgs& g, hipStream_t s) {
+    if constexpr (is_bf16<T>()) {
+        if (dma_ok(epi, g)) {
+            switch (epi) {
+                case EPI_STORE_F32: return launch_dma<EPI_STORE_F32>(g, s);
+                case EPI_QKV: return launch_dma<EPI_QKV>(g, s);
+                case EPI_RESID: return launch_dma<EPI_RESID>(g, s);
+                case EPI_SWIGLU: return launch_dma<EPI_SWIGLU>(g, s);
+            }
+            return hipErrorInvalidValue;
+        }
+    }
     switch (epi) {
         case EPI_STORE_F32: return launch_t<T, EPI_STORE_F32>(g, s);
         case EPI_QKV: return launch_t<T, EPI_QKV>(g, s);
