@@ -11,6 +11,10 @@ the roofline of the dominant kernel, the speedup over the library's own full
 recompute (r = 100%) and the CPU oracle timed on a bounded sample.
 
 Usage: python bench.py [--steps K] [--warmup W] [--workload llama7b-4k]
+
+Other workloads: llama13b-8k, yi34b-8k (chunk caches in pinned host memory)
+and batch-7b (32 requests over a 200-chunk pool with Zipf reuse, pool in
+pinned host memory; one step = one cb_blend_batch).
 """
 import argparse
 import json
@@ -51,12 +55,9 @@ def log(*a):
 
 
 # ------------------------------------------------------------------ inputs
-def make_inputs(npk, w, seed, torch):
-    """Random-init weights N(0, 0.02^2) on the device (bf16), uniform random
-    tokens, embedding rows as layer-0 input, chunk caches precomputed alone
-    with cb_prefill at chunk-local positions."""
-    from workloads import make_tokens
-    S = w.shape
+def make_model(npk, S, seed, torch):
+    """Random-init weights N(0, 0.02^2) on the device (bf16), unit norm gains,
+    and an embedding table of the same distribution."""
     dev = torch.device("cuda:0")
     bf = torch.bfloat16
     gen = torch.Generator(device=dev)
@@ -79,6 +80,17 @@ def make_inputs(npk, w, seed, torch):
     model = npk.Model(S.n_layers, S.d_model, S.n_q_heads, S.n_kv_heads, S.head_dim, S.ffn_dim,
                       layers, rope_base=S.rope_base, rms_eps=S.rms_eps)
     emb = normal((S.vocab, S.d_model), 0, -1)
+    return model, layers, emb
+
+
+def make_inputs(npk, w, seed, torch):
+    """Uniform random tokens, embedding rows as layer-0 input, chunk caches
+    precomputed alone with cb_prefill at chunk-local positions."""
+    from workloads import make_tokens
+    S = w.shape
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    model, layers, emb = make_model(npk, S, seed, torch)
     tok = torch.from_numpy(make_tokens(S, w.n_tokens, seed)).to(dev)
     x0 = emb[tok].contiguous()
     del emb
@@ -94,6 +106,57 @@ def make_inputs(npk, w, seed, torch):
                        "layer_stride": n * S.kv_dim})
     torch.cuda.synchronize()
     return model, layers, x0, chunks
+
+
+def make_batch_inputs(npk, w, seed, torch, pool_on_host):
+    """Batched serving slice: a chunk pool with Zipf reuse (see
+    workloads.make_batched_requests).  Every pool chunk a request uses is
+    precomputed alone with cb_prefill and stored once, all chunks of a layer
+    side by side in one [L][U][H_kv*d_h] buffer per K and V (pinned host
+    memory, or device memory for the resident-pool comparison)."""
+    from workloads import make_batched_requests, make_batch_tokens
+    S = w.shape
+    L, kvd = S.n_layers, S.kv_dim
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    model, layers, emb = make_model(npk, S, seed, torch)
+    pool_lens, reqs = make_batched_requests(w, seed)
+    pool_tok, suf_tok = make_batch_tokens(S, pool_lens, reqs, seed)
+    used = sorted({i for r in reqs for i in r["chunk_ids"]})
+    row = {}
+    U = 0
+    for i in used:
+        row[i] = U
+        U += int(pool_lens[i])
+    where = dict(device="cpu", pin_memory=True) if pool_on_host else dict(device=dev)
+    pk = torch.empty((L, U, kvd), dtype=bf, **where)
+    pv = torch.empty((L, U, kvd), dtype=bf, **where)
+    for i in used:
+        n, o = int(pool_lens[i]), row[i]
+        x = emb[torch.from_numpy(pool_tok[i]).to(dev)].contiguous()
+        k = torch.empty((L, n, kvd), dtype=bf, device=dev)
+        v = torch.empty_like(k)
+        npk.cb_prefill(model, x, n, 0, k, v)
+        for l in range(L):
+            pk[l, o:o + n].copy_(k[l])
+            pv[l, o:o + n].copy_(v[l])
+    torch.cuda.synchronize()
+    pool = []
+    for i in range(len(pool_lens)):
+        if i in row:
+            off = row[i] * kvd * 2
+            pool.append({"k": pk.data_ptr() + off, "v": pv.data_ptr() + off,
+                         "n_tokens": int(pool_lens[i]), "on_host": int(pool_on_host),
+                         "layer_stride": U * kvd})
+        else:   # never referenced, never read
+            pool.append({"k": 0, "v": 0, "n_tokens": 1, "on_host": 0, "layer_stride": kvd})
+    toks = np.concatenate([np.concatenate([pool_tok[i] for i in r["chunk_ids"]] + [t])
+                           for r, t in zip(reqs, suf_tok)]).astype(np.int64)
+    x0 = emb[torch.from_numpy(toks).to(dev)].contiguous()
+    del emb
+    info = {"pool_lens": pool_lens, "requests": reqs, "unique_chunks": len(used),
+            "unique_tokens": U}
+    return model, layers, x0, pool, (pk, pv), info
 
 
 # ------------------------------------------------------------------ HBM traffic
@@ -168,6 +231,185 @@ def cpu_baseline(w, seed, n_tokens):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def kernel_breakdown(st, pk):
+    kernels = {}
+    for name, s in st.items():
+        if not s["launches"]:
+            continue
+        sec = s["total_ms"] / 1e3
+        e = {"launches_per_step": s["launches"] / pk,
+             "ms_per_step": s["total_ms"] / pk,
+             "us_per_launch": s["total_ms"] / s["launches"] * 1e3}
+        if s["flops"]:
+            e["tflops"] = s["flops"] / sec / 1e12
+            e["frac_mfma_bf16"] = e["tflops"] / PEAK_BF16_TFLOPS
+        if s["bytes"] and not s["flops"]:
+            e["gbs"] = s["bytes"] / sec / 1e9
+            e["frac_hbm"] = e["gbs"] / PEAK_HBM_GBS
+        kernels[name] = e
+    return kernels
+
+
+def roofline(st, kernels, traffic):
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    d = st[dom]
+    if d["flops"]:
+        ach = d["flops"] / (d["total_ms"] / 1e3) / 1e12
+        return {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                "traffic": traffic(dom), "kernel": dom,
+                "per_launch": f"{d['flops'] / d['launches'] / 1e9:.2f} GFLOP avg",
+                "us_per_launch": d["total_ms"] / d["launches"] * 1e3}
+    ach = d["bytes"] / (d["total_ms"] / 1e3) / 1e9
+    return {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": ach / PEAK_HBM_GBS, "traffic": None, "kernel": dom}
+
+
+def cpu_baseline_batch(w, seed, reqs, pool_lens, n_total):
+    """The oracle on two requests of the batch (the first two), first three
+    layers each at full width and context; each request's time is composed
+    as t0 + t1 + (L - 2) * t2 and the pair's tokens/s stands for the batch."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    from workloads import make_weights_np
+    import dataclasses
+    S = w.shape
+    ls = min(3, S.n_layers)
+    S3 = dataclasses.replace(S, n_layers=ls)
+    weights = make_weights_np(S3, seed=seed, dtype="f32")
+    rng = np.random.default_rng(seed)
+    total, toks, parts = 0.0, 0, []
+    for r in reqs[:2]:
+        lens = [int(pool_lens[i]) for i in r["chunk_ids"]]
+        n_c = sum(lens)
+        n = n_c + r["n_suffix"]
+        x0 = (rng.standard_normal((n, S.d_model)) * 0.02).astype(np.float32)
+        chunks = [(rng.standard_normal((ls, m, S.n_kv_heads, S.head_dim)).astype(np.float32),
+                   rng.standard_normal((ls, m, S.n_kv_heads, S.head_dim)).astype(np.float32))
+                  for m in lens]
+        offs = list(np.cumsum([0] + lens)[:-1])
+        sched = oracle.schedule(n_c, w.r_bp, w.schedule_kind, S.n_layers)[:ls + 1]
+        times = []
+        oracle.blend(weights, S3, x0, chunks, [int(o) for o in offs], r["n_suffix"], sched,
+                     dtype=np.float32, timings=times)
+        t = sum(times) + (S.n_layers - ls) * times[-1]
+        total += t
+        toks += n
+        parts.append(f"{n} tokens: layers {[round(x, 3) for x in times]} s -> {t:.2f} s")
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": toks / total, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"oracle.blend float32 on the first two requests of the batch (random "
+                       f"chunk caches), layers 0-2 each at full width, whole prompt composed as "
+                       f"t0 + t1 + {S.n_layers - 2}*t2: " + "; ".join(parts) +
+                       f"; the batch ({n_total} tokens) at the same rate would take "
+                       f"{n_total / (toks / total):.1f} s"),
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main_batched(args, npk, torch, w):
+    """One step = one cb_blend_batch of the whole batch (pool in pinned host
+    memory, copied to HBM layer by layer on the side stream)."""
+    import dataclasses
+    if args.r_bp is not None:
+        w = dataclasses.replace(w, r_bp=args.r_bp)
+    if args.schedule is not None:
+        w = dataclasses.replace(w, schedule_kind=args.schedule)
+    S = w.shape
+    L = S.n_layers
+    log(f"[bench] workload {w.name}: building inputs (pool in pinned host memory)")
+    model, layers, x0, pool, pool_bufs, info = make_batch_inputs(npk, w, args.seed, torch, True)
+    reqs = info["requests"]
+    lens = [sum(int(info["pool_lens"][i]) for i in r["chunk_ids"]) for r in reqs]
+    Ntot = sum(lens) + sum(r["n_suffix"] for r in reqs)
+    Nctot = sum(lens)
+    kind = npk.CB_SCHED_GRADUAL if w.schedule_kind == "gradual" else npk.CB_SCHED_FIXED
+    dev = torch.device("cuda:0")
+    fk = torch.empty((L, Ntot, S.n_kv_heads, S.head_dim), dtype=torch.bfloat16, device=dev)
+    fv = torch.empty_like(fk)
+    sel = torch.empty((L, Nctot), dtype=torch.int32, device=dev)
+    counts = [None]
+
+    def step(p=pool):
+        counts[0] = npk.cb_blend_batch(model, p, reqs, x0, fk, fv, sel_idx=sel,
+                                       recompute_bp=w.r_bp, schedule_kind=kind)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) / args.steps * 1e3
+    h2d_bytes = 2 * L * info["unique_tokens"] * S.kv_dim * 2
+    out = {"metric": "effective prompt tok/s of a batch of requests at r=15%, Llama-7B shape",
+           "value": Ntot / (ms / 1e3), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": ms, "ms_per_layer": ms / L,
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic: random-init N(0,0.02) weights, uniform random tokens, pool "
+                   "chunk caches precomputed alone by cb_prefill",
+           "config": {"workload": w.name, "requests": len(reqs), "prompt_tokens": Ntot,
+                      "chunk_tokens": Nctot, "pool_chunks": len(info["pool_lens"]),
+                      "unique_chunks_used": info["unique_chunks"],
+                      "unique_chunk_tokens": info["unique_tokens"], "recompute_bp": w.r_bp,
+                      "schedule": w.schedule_kind, "pool": "pinned host",
+                      "h2d_bytes_per_step": h2d_bytes},
+           "h2d_gbs_effective": h2d_bytes / (ms / 1e3) / 1e9}
+
+    if not args.no_profile:
+        log("[bench] kernel timing pass")
+        npk.cb_profile_enable(model, True)
+        pk = max(1, min(args.steps, 2))
+        torch.cuda.synchronize()
+        for _ in range(pk):
+            step()
+        torch.cuda.synchronize()
+        st = npk.cb_profile_read(model)
+        npk.cb_profile_enable(model, False)
+        sel_h = sel.cpu().numpy()
+        att_terms, C = 0, 0
+        for r, n_c, cnt in zip(reqs, lens, counts[0]):
+            suffix_sum = sum(p + 1 for p in range(n_c, n_c + r["n_suffix"]))
+            for l in range(L):
+                att_terms += int(np.sum(sel_h[l, C:C + cnt[l]].astype(np.int64) + 1)) + suffix_sum
+            C += n_c
+        st["attention"]["flops"] = 4.0 * S.n_q_heads * S.head_dim * att_terms * pk
+        kernels = kernel_breakdown(st, pk)
+        out["kernels"] = kernels
+        out["roofline"] = roofline(st, kernels, lambda k: None)
+
+    if not args.no_full_compare:
+        log("[bench] same batch with the pool resident in HBM")
+        pk_, pv_ = pool_bufs
+        dk, dv = pk_.to(dev), pv_.to(dev)
+        dpool = []
+        for e in pool:
+            if e["k"]:
+                e = dict(e, k=dk.data_ptr() + (e["k"] - pk_.data_ptr()),
+                         v=dv.data_ptr() + (e["v"] - pv_.data_ptr()), on_host=0)
+            dpool.append(e)
+        step(dpool)
+        torch.cuda.synchronize()
+        tr0 = time.perf_counter()
+        nr = max(1, min(args.steps, 3))
+        for _ in range(nr):
+            step(dpool)
+        torch.cuda.synchronize()
+        msr = (time.perf_counter() - tr0) / nr * 1e3
+        out["hbm_pool_ms_per_step"] = msr
+        out["hbm_pool_tok_s"] = Ntot / (msr / 1e3)
+        del dk, dv
+
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle sample")
+        del fk, fv
+        torch.cuda.empty_cache()
+        out["cpu_baseline"] = cpu_baseline_batch(w, args.seed, reqs, info["pool_lens"], Ntot)
+    print(json.dumps(out), flush=True)
+
+
 # ------------------------------------------------------------------ main
 def main():
     args = parse()
@@ -182,9 +424,12 @@ def main():
         return
     import torch
     import non_prefix_kv_amd as npk
-    from workloads import WORKLOADS
+    from workloads import WORKLOADS, BATCHED_WORKLOADS
     import dataclasses
 
+    if args.workload in BATCHED_WORKLOADS:
+        main_batched(args, npk, torch, BATCHED_WORKLOADS[args.workload])
+        return
     w = WORKLOADS[args.workload]
     if args.r_bp is not None:
         w = dataclasses.replace(w, r_bp=args.r_bp)
@@ -249,36 +494,9 @@ def main():
         att_terms = sum(int(np.sum(sel_h[l, :sched[l + 1]].astype(np.int64) + 1)) + suffix_sum
                         for l in range(L))
         st["attention"]["flops"] = 4.0 * S.n_q_heads * S.head_dim * att_terms * pk
-        kernels = {}
-        for name, s in st.items():
-            if not s["launches"]:
-                continue
-            sec = s["total_ms"] / 1e3
-            e = {"launches_per_step": s["launches"] / pk,
-                 "ms_per_step": s["total_ms"] / pk,
-                 "us_per_launch": s["total_ms"] / s["launches"] * 1e3}
-            if s["flops"]:
-                e["tflops"] = s["flops"] / sec / 1e12
-                e["frac_mfma_bf16"] = e["tflops"] / PEAK_BF16_TFLOPS
-            if s["bytes"] and not s["flops"]:
-                e["gbs"] = s["bytes"] / sec / 1e9
-                e["frac_hbm"] = e["gbs"] / PEAK_HBM_GBS
-            kernels[name] = e
+        kernels = kernel_breakdown(st, pk)
         out["kernels"] = kernels
-        dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
-        d = st[dom]
-        if d["flops"]:
-            ach = d["flops"] / (d["total_ms"] / 1e3) / 1e12
-            out["roofline"] = {"bound": "mfma", "achieved": ach, "peak": PEAK_BF16_TFLOPS,
-                               "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
-                               "traffic": recorded_traffic(dom), "kernel": dom,
-                               "per_launch": f"{d['flops'] / d['launches'] / 1e9:.2f} GFLOP avg",
-                               "us_per_launch": d["total_ms"] / d["launches"] * 1e3}
-        else:
-            ach = d["bytes"] / (d["total_ms"] / 1e3) / 1e9
-            out["roofline"] = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS,
-                               "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None,
-                               "kernel": dom}
+        out["roofline"] = roofline(st, kernels, recorded_traffic)
 
     if not args.no_full_compare:
         log("[bench] full recompute (r = 100%) comparison")

@@ -228,6 +228,11 @@ struct cb_plan {
     };
     std::vector<H2D> h2d;
     std::vector<RotJobs> jobs_copy, jobs_inplace;
+    // Layers the side stream may run ahead of the main stream.  Rotation
+    // kernels share the compute units with the layers, so device-resident
+    // chunks are fetched just ahead; host copies run on the copy engines and
+    // each layer's destination is its own, so they start as early as possible.
+    int lookahead = 2;
 
     // streams / events
     hipEvent_t ready = nullptr;                 // workspace + prior main work
@@ -466,9 +471,10 @@ cb_status do_fetch(cb_plan* p, int l) {
     if (p->fetch_done[l]) return CB_OK;
     cb_model* m = p->m;
     const hipStream_t side = m->side;
-    // keep the side stream at most two layers ahead of the main stream
-    if (l >= 2 && p->layer_start[l - 2] && l - 2 < p->next_layer)
-        CB_HIP(hipStreamWaitEvent(side, p->layer_start[l - 2], 0));
+    // keep the side stream at most `lookahead` layers ahead of the main stream
+    const int behind = l - p->lookahead;
+    if (behind >= 0 && behind < p->next_layer)
+        CB_HIP(hipStreamWaitEvent(side, p->layer_start[behind], 0));
     const size_t es = m->es(), row_bytes = (size_t)m->kvd() * es;
     char* fk = (char*)p->fused_k + (size_t)l * layer_elems(p) * es;
     char* fv = (char*)p->fused_v + (size_t)l * layer_elems(p) * es;
@@ -689,6 +695,7 @@ cb_status plan_layout(cb_plan* p) {
                 copy.push_back(j);
             }
         }
+    p->lookahead = p->h2d.empty() ? 2 : std::max(2, p->L);
     for (auto [src, dst] : {std::make_pair(&copy, &p->jobs_copy),
                             std::make_pair(&inplace, &p->jobs_inplace)})
         for (size_t i = 0; i < src->size(); ++i) {
@@ -819,9 +826,13 @@ cb_status plan_setup(cb_plan* p) {
 
 cb_status run_all_layers(cb_plan* p) {
     cb_status st = CB_OK;
+    int fetched = 0;
     for (int l = 0; l < p->L && st == CB_OK; ++l) {
-        st = do_fetch(p, l);
-        if (st == CB_OK && l + 1 < p->L) st = do_fetch(p, l + 1);   // overlaps layer l
+        // queue the fetch of the next layer before layer l (the side stream
+        // runs it during layer l; how far it may run ahead is set by the
+        // event waits in do_fetch, host-side queueing just keeps pace)
+        for (; fetched < p->L && fetched <= l + 1 && st == CB_OK; ++fetched)
+            st = do_fetch(p, fetched);
         if (st == CB_OK) st = do_layer(p, l);
         if (st == CB_OK) p->next_layer++;
     }

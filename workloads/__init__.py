@@ -5,13 +5,14 @@ fusion method's arithmetic lives here, so the oracle and the HIP path can both
 take their inputs from it without sharing any computation.
 """
 from .shapes import (ModelShape, Workload, TINY, LLAMA7B, LLAMA13B, YI34B,
-                     WORKLOADS, BatchedWorkload, BATCHED_LLAMA7B, BATCHED_TINY)
+                     WORKLOADS, BatchedWorkload, BATCHED_LLAMA7B, BATCHED_TINY,
+                     BATCHED_WORKLOADS)
 from .gen import (make_weights_np, make_tokens, make_embedding_np, round_to,
                   make_batched_requests, make_batch_tokens)
 
 __all__ = [
     "ModelShape", "Workload", "TINY", "LLAMA7B", "LLAMA13B", "YI34B", "WORKLOADS",
-    "BatchedWorkload", "BATCHED_LLAMA7B", "BATCHED_TINY",
+    "BatchedWorkload", "BATCHED_LLAMA7B", "BATCHED_TINY", "BATCHED_WORKLOADS",
     "make_weights_np", "make_tokens", "make_embedding_np", "round_to",
     "make_batched_requests", "make_batch_tokens",
 ]

@@ -102,3 +102,5 @@ BATCHED_LLAMA7B = BatchedWorkload("batched-32req-llama2-7b-shape-zipf1.1", LLAMA
 BATCHED_TINY = BatchedWorkload("batched-6req-tiny", TINY, n_requests=6, pool_size=10,
                                chunk_len_range=(17, 150), chunks_per_req=(1, 4),
                                suffix_range=(1, 40))
+
+BATCHED_WORKLOADS = {"batch-7b": BATCHED_LLAMA7B}
