@@ -292,15 +292,14 @@ __device__ __forceinline__ int xcd_order(int hw, int total) {
 template <int D>
 __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a, const AttnTiles tl) {
     constexpr int LDK = D + 8;                 // sK row stride (elements)
-    constexpr int LDV = KB32 + 4;              // sVt row stride (elements)
+    constexpr int LDV = D + 32;                // sV row stride: rows 1..3 apart fall 64 B
+                                               // apart in bank space (transposed reads)
     constexpr int NDS = D / 16;                // 16-dim reduction steps for S
     constexpr int NDT = D / 32;                // 32-dim output tiles
-    constexpr int KU = KB32 * D / 8 / kT32;    // 16-byte K pieces per thread
-    constexpr int VUNITS = (KB32 / 4) * (D / 8);
+    constexpr int KU = KB32 * D / 8 / kT32;    // 16-byte K (and V) pieces per thread
     static_assert(KU >= 1 && KB32 * D / 8 == KU * kT32, "K tile split");
-    static_assert(VUNITS <= kT32, "V tile split");
     __shared__ __attribute__((aligned(16))) bf16 sK[2][KB32 * LDK];
-    __shared__ __attribute__((aligned(16))) bf16 sVt[2][D * LDV];
+    __shared__ __attribute__((aligned(16))) bf16 sV[2][KB32 * LDV];
     __shared__ int sred[kT32 / 64];
 
     // logical id -> (tile, segment, head), tile fastest; tiles come longest first
@@ -356,42 +355,45 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a, const 
 
     const bf16* kbase = static_cast<const bf16*>(a.k) + (int64_t)tile.g0 * kv_ld + hk * D;
     const bf16* vbase = static_cast<const bf16*>(a.v) + (int64_t)tile.g0 * kv_ld + hk * D;
-    // Two register stage sets (prefetch distance 2).  V unit = 4 keys x 8
-    // dims; consecutive lanes step over keys first so the transposed 8-byte
-    // LDS stores of 16 lanes fill 32 distinct banks.  Rows past n_kv are
-    // clamped to the last key: their scores are masked.
-    const bool v_unit = tid < VUNITS;
-    const int vr0 = (tid % (KB32 / 4)) * 4, vc = (tid / (KB32 / 4)) * 8;
-    u32x4 rk0[KU], rv0[4], rk1[KU], rv1[4];
-    auto load_block = [&](int kb, u32x4 (&rk)[KU], u32x4 (&rv)[4]) {
+    // Two register stage sets (prefetch distance 2).  K and V blocks are
+    // fetched with buffer loads whose range ends at the last key: rows past
+    // it read as zero (their scores are masked).  Both are stored row-major;
+    // V^T fragments come from transposing LDS reads.
+    int voff[KU];
+#pragma unroll
+    for (int j = 0; j < KU; ++j) {
+        const int u = tid + j * kT32;
+        voff[j] = ((u / (D / 8)) * kv_ld + (u % (D / 8)) * 8) * 2;
+    }
+    u32x4 rk0[KU], rv0[KU], rk1[KU], rv1[KU];
+    auto load_block = [&](int kb, u32x4 (&rk)[KU], u32x4 (&rv)[KU]) {
         const int k0 = (kb_beg + kb) * KB32;
+        const int rows = min(KB32, n_kv - k0);
+        const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16*>(kbase + (int64_t)k0 * kv_ld), (short)0, rows * kv_ld * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<bf16*>(vbase + (int64_t)k0 * kv_ld), (short)0, rows * kv_ld * 2, 0x00020000);
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
-            const int u = tid + j * kT32;
-            const int r = u / (D / 8), c = (u % (D / 8)) * 8;
-            const int kr = min(k0 + r, n_kv - 1);
-            rk[j] = *reinterpret_cast<const u32x4*>(kbase + (int64_t)kr * kv_ld + c);
-        }
-        if (v_unit) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int vr = min(k0 + vr0 + q, n_kv - 1);
-                rv[q] = *reinterpret_cast<const u32x4*>(vbase + (int64_t)vr * kv_ld + vc);
-            }
+            rk[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsk, voff[j], 0, 0));
+            rv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsv, voff[j], 0, 0));
         }
     };
-    auto store_block = [&](int buf, const u32x4 (&rk)[KU], const u32x4 (&rv)[4]) {
+    auto store_block = [&](int buf, const u32x4 (&rk)[KU], const u32x4 (&rv)[KU]) {
 #pragma unroll
         for (int j = 0; j < KU; ++j) {
             const int u = tid + j * kT32;
             const int r = u / (D / 8), c = (u % (D / 8)) * 8;
             *reinterpret_cast<u32x4*>(&sK[buf][r * LDK + c]) = rk[j];
-        }
-        if (v_unit) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) store_vt4(&sVt[buf][(vc + i) * LDV + vr0], rv, i);
+            *reinterpret_cast<u32x4*>(&sV[buf][r * LDV + c]) = rv[j];
         }
     };
+    // Transposing read of V: within each 16-lane group the instruction hands
+    // lane j the j-th column of the 4 x 16 block addressed by the group
+    // (lane s points at row s / 4, columns 4 (s % 4) .. +3), so lane l gets 4
+    // consecutive keys of one dimension.  Row offset of this lane:
+    const int tr_g = lane >> 4, tr_s = lane & 15;
+    const int tr_off = (4 * (tr_g >> 1) + (tr_s >> 2)) * LDV + 16 * (tr_g & 1) + 4 * (tr_s & 3);
     auto compute = [&](int cur, int kb) {
         const int k0 = (kb_beg + kb) * KB32;
         if (a.kv_pos0 + k0 > wmax) return;          // wave-uniform: nothing visible
@@ -433,15 +435,19 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a, const 
             l_run += p;
             pf[i >> 3][i & 7] = static_cast<bf16>(p);
         }
-        // P^T slot j of half hh holds key 16 hh + 8 (j / 4) + 4 g + j % 4.
+        // P^T slot j of half hh holds key 16 hh + 8 (j / 4) + 4 g + j % 4; the
+        // V^T fragment (row = dimension, 8 keys) is read in that key order.
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const bf16* vr = &sVt[cur][(dt * 32 + fr) * LDV + hh * 16 + g * 4];
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(vr);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(vr + 8);
-                const u32x4 w{lo[0], lo[1], hi[0], hi[1]};
+                typedef short i16x4 __attribute__((ext_vector_type(4)));
+                typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+                const bf16* vr = &sV[cur][tr_off + hh * 16 * LDV + dt * 32];
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)vr);
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr + 8 * LDV));
+                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
+                const u32x4 w{l2[0], l2[1], h2[0], h2[1]};
                 mfma32(o[dt], __builtin_bit_cast(bf16x8, w), pf[hh]);
             }
     };
