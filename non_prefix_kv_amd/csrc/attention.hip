@@ -279,6 +279,7 @@ __device__ __forceinline__ void mfma32(floatx16& acc, const bf16x8& a, const bf1
 constexpr int kT32 = 256;   // threads per workgroup (4 waves)
 constexpr int QT32 = 128;   // queries per workgroup
 constexpr int KB32 = 32;    // keys per block
+constexpr float kLazyLog2 = 8.0f;   // rescale threshold of the running maximum (log2 units)
 
 // Hardware workgroup ids are dealt round-robin over the 8 XCDs; renumber so
 // each XCD gets a contiguous logical range (blocks that read the same key
@@ -419,9 +420,15 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a, const 
 #pragma unroll
         for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, st[i]);
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * sl2;
-        const float m_new = fmaxf(m_run, mloc);
+        // The reference maximum only moves when a score exceeds it by more
+        // than kLazyLog2 (probabilities then stay below 2^kLazyLog2): after
+        // the first keys O and l are rarely rescaled.  Any reference gives
+        // the same normalized result; the combine pass merges segments by
+        // their own references.
+        const bool grow = mloc > m_run + kLazyLog2;      // false for an all-masked block
+        const float m_new = grow ? mloc : m_run;
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        if (__ballot(m_new != m_run)) {           // rescale only when some max moved
+        if (__ballot(grow)) {
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
             l_run *= alpha;
 #pragma unroll
@@ -444,10 +451,10 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a, const 
                 typedef short i16x4 __attribute__((ext_vector_type(4)));
                 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
                 const bf16* vr = &sV[cur][tr_off + hh * 16 * LDV + dt * 32];
+                typedef short i16x8 __attribute__((ext_vector_type(8)));
                 const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)vr);
                 const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr + 8 * LDV));
-                const u32x2 l2 = __builtin_bit_cast(u32x2, lo), h2 = __builtin_bit_cast(u32x2, hi);
-                const u32x4 w{l2[0], l2[1], h2[0], h2[1]};
+                const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
                 mfma32(o[dt], __builtin_bit_cast(bf16x8, w), pf[hh]);
             }
     };
