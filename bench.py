@@ -47,7 +47,91 @@ def parse():
     ap.add_argument("--no-full-compare", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="summarize a rocprofv3 kernel_trace.csv of a bench run (timed steps "
+                         "only) as a markdown table, then exit")
+    ap.add_argument("--counter-summary", metavar="CSV", nargs="+",
+                    help="average rocprofv3 counter_collection.csv values per kernel over the "
+                         "timed steps, then exit")
     return ap.parse_args()
+
+
+# ------------------------------------------------------------------ profiles
+# The timed loop is preceded by one tiny torch kernel (the marker); every
+# dispatch after the last non-library kernel belongs to the timed steps when
+# bench.py runs with --no-profile --no-full-compare --no-cpu-baseline.
+def _is_lib(name):
+    return "cb::" in name or name.startswith("_ZN2cb")
+
+
+def _timed_rows(rows, key):
+    rows = sorted(rows, key=key)
+    last = max((i for i, r in enumerate(rows) if not _is_lib(r["Kernel_Name"])), default=-1)
+    return rows[last + 1:]
+
+
+def _short(name):
+    """Readable kernel name: demangled names lose the namespace and argument
+    list; mangled ones keep the identifier and the template arguments."""
+    import re
+    if name.startswith("_ZN2cb12_GLOBAL__N_1"):
+        rest = name[len("_ZN2cb12_GLOBAL__N_1"):]
+        m = re.match(r"(\d+)", rest)
+        n = int(m.group(1))
+        ident = rest[len(m.group(1)):len(m.group(1)) + n]
+        targs = rest[len(m.group(1)) + n:]
+        targs = targs[1:targs.index("EE")] if targs.startswith("I") and "EE" in targs else ""
+        out = []
+        while targs:
+            if targs.startswith("DF16b"):
+                out.append("bf16")
+                targs = targs[5:]
+            elif targs.startswith("Li"):
+                e = targs.index("E")
+                out.append(targs[2:e])
+                targs = targs[e + 1:]
+            else:
+                out.append({"f": "f32", "i": "int"}.get(targs[0], targs[0]))
+                targs = targs[1:]
+        return f"{ident}<{', '.join(out)}>" if out else ident
+    n = name.replace("void ", "").replace("cb::(anonymous namespace)::", "")
+    return re.sub(r"\(.*\)$", "", n)
+
+
+def trace_summary(path):
+    import csv
+    rows = _timed_rows(list(csv.DictReader(open(path))), lambda r: int(r["Start_Timestamp"]))
+    agg = {}
+    for r in rows:
+        k = _short(r["Kernel_Name"])
+        d = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        a = agg.setdefault(k, [0, 0])
+        a[0] += 1
+        a[1] += d
+    total = sum(v[1] for v in agg.values())
+    print("| Kernel | Calls | Avg (us) | Total (ms) | Share |")
+    print("|---|---:|---:|---:|---:|")
+    for k, (n, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
+        print(f"| {k} | {n} | {t / n / 1e3:.1f} | {t / 1e6:.3f} | {100 * t / total:.1f}% |")
+    print(f"\n{len(rows)} dispatches, {total / 1e6:.3f} ms of kernel time")
+
+
+def counter_summary(paths):
+    import csv
+    out = {}
+    for path in paths:
+        rows = list(csv.DictReader(open(path)))
+        by_dispatch = {}
+        for r in rows:
+            by_dispatch.setdefault(int(r["Dispatch_Id"]), []).append(r)
+        disp = _timed_rows([v[0] for v in by_dispatch.values()], lambda r: int(r["Dispatch_Id"]))
+        for r0 in disp:
+            k = _short(r0["Kernel_Name"])
+            for r in by_dispatch[int(r0["Dispatch_Id"])]:
+                out.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    res = {k: {c: {"dispatches": len(v), "mean": sum(v) / len(v)} for c, v in d.items()}
+           for k, d in out.items()}
+    print(json.dumps(res, indent=1))
 
 
 def log(*a):
@@ -164,17 +248,18 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_gemm_gateup_llama7b.json"
 KERNEL_SRC = os.path.join(ROOT, "non_prefix_kv_amd", "csrc", "gemm.hip")
 
 
-def recorded_traffic(kernel):
+def recorded_traffic(kernel, workload):
     """HBM bytes per launch of the dominant kernel from the committed
-    rocprofv3 FETCH_SIZE/WRITE_SIZE runs, or None when absent or when the
-    kernel source changed since the counters were taken."""
+    rocprofv3 FETCH_SIZE/WRITE_SIZE runs, or None when absent, taken on
+    another workload, or when the kernel source changed since."""
     import hashlib
     try:
         rec = json.load(open(TRAFFIC_FILE))
         src = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_class") != kernel or rec.get("source_sha256") != src:
+    if (rec.get("kernel_class") != kernel or rec.get("source_sha256") != src
+            or rec.get("workload_key") != workload):
         return None
     return rec.get("bytes_per_launch")
 
@@ -337,6 +422,8 @@ def main_batched(args, npk, torch, w):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    torch.ones(1, device=dev).mul_(3.0)      # marker: last non-library kernel before the timed steps
+    torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -419,6 +506,12 @@ def main():
                                    "shard across GPUs here (see the design notes on "
                                    "data-parallel serving by request)", "n_gpus": args.gpus}))
         sys.exit(2)
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
+    if args.counter_summary:
+        counter_summary(args.counter_summary)
+        return
     if args.copy_calibration:
         copy_calibration()
         return
@@ -455,6 +548,8 @@ def main():
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
+    torch.cuda.synchronize()
+    torch.ones(1, device=dev).mul_(3.0)      # marker: last non-library kernel before the timed steps
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
     t0 = time.perf_counter()
@@ -496,7 +591,7 @@ def main():
         st["attention"]["flops"] = 4.0 * S.n_q_heads * S.head_dim * att_terms * pk
         kernels = kernel_breakdown(st, pk)
         out["kernels"] = kernels
-        out["roofline"] = roofline(st, kernels, recorded_traffic)
+        out["roofline"] = roofline(st, kernels, lambda k: recorded_traffic(k, args.workload))
 
     if not args.no_full_compare:
         log("[bench] full recompute (r = 100%) comparison")
