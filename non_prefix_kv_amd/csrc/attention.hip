@@ -280,6 +280,7 @@ constexpr int kT32 = 256;   // threads per workgroup (4 waves)
 constexpr int QT32 = 128;   // queries per workgroup
 constexpr int KB32 = 32;    // keys per block
 constexpr float kLazyLog2 = 8.0f;   // rescale threshold of the running maximum (log2 units)
+constexpr int kSplitUnits = 2048;   // (query tile, head, key segment) units wanted per launch
 
 // Hardware workgroup ids are dealt round-robin over the 8 XCDs; renumber so
 // each XCD gets a contiguous logical range (blocks that read the same key
@@ -606,9 +607,15 @@ SplitPlan split_plan(const AttnRange* t, int n, int n_q_heads, int head_dim) {
     SplitPlan p;
     int max_kv = 0;
     for (int i = 0; i < n; ++i) max_kv = std::max(max_kv, t[i].n_kv);
-    if ((int64_t)n * n_q_heads >= 2048 || max_kv <= 1024) return p;
-    p.seg_keys = 512;
+    const int64_t units = (int64_t)n * n_q_heads;
+    if (units >= kSplitUnits || max_kv <= 1024) return p;
+    // Enough segments for ~kSplitUnits work units (the partials cost HBM
+    // traffic), each at least 512 keys long.
+    const int want = (int)std::min<int64_t>((kSplitUnits + units - 1) / units,
+                                            (max_kv + 511) / 512);
+    p.seg_keys = ((max_kv + want - 1) / want + KB32 - 1) / KB32 * KB32;
     p.max_seg = (max_kv + p.seg_keys - 1) / p.seg_keys;
+    if (p.max_seg <= 1) return SplitPlan{};
     p.bytes = (size_t)n * n_q_heads * p.max_seg * QT32 * (head_dim + 2) * sizeof(float);
     return p;
 }

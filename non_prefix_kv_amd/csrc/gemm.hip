@@ -342,10 +342,13 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
 // while the current step's MFMAs run.
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-// Raw buffer descriptor: base address, stride 0, range `bytes`.
+// Raw buffer descriptor: base address, stride 0, range `bytes` (uniform
+// values; read from the first lane so the descriptor lives in SGPRs).
 __device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
     const uint64_t a = reinterpret_cast<uint64_t>(base);
-    return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xFFFF), bytes, 0x00020000};
+    return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)a),
+                 __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xFFFF)),
+                 __builtin_amdgcn_readfirstlane(bytes), 0x00020000};
 }
 
 // 16 bytes per lane from buffer offset voff + soff into LDS at m0 + 16 * lane.
@@ -354,10 +357,10 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
 // any LDS read); completion is tracked by the explicit vmcnt waits below and
 // the "memory" clobber keeps LDS reads from moving across the copy.
 __device__ __forceinline__ void dma16(i32x4 rsrc, int voff, int soff, uint32_t m0) {
-    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
-                 : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
-                 : "memory", "m0");
+                 : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
+                 : "memory");
 }
 
 // Byte range of the wave's 32-row slice: rows left (clamped to 0..32) x row bytes.
@@ -945,16 +948,34 @@ hipError_t launch_big(const GemmArgs& g, hipStream_t s) {
     return hipGetLastError();
 }
 
-// Tile choice, from measurements on MI355X (bf16, K = 4096 / 11008):
-// with M >= 4096 rows the 256x256 kernel runs 1.2-1.3x faster per flop
-// (1110-1300 vs 860-1040 TFLOP/s); with ~832 rows it is faster only for
-// the wide q/k/v product (880 vs 790) and much slower where N = 4096 leaves
-// most CUs idle (340-390 vs 730-890).
+int num_cus() {
+    static int n = [] {
+        int dev = 0, c = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+            c = 256;
+        return c;
+    }();
+    return n;
+}
+
+// Tile choice.  Both kernels run one workgroup per CU (256 at a time); a
+// 256x256 tile costs about 3 times a 128x128 one (4x the work at ~1.3x the
+// efficiency; 2.8 for the q/k/v product, whose RoPE epilogue is relatively
+// cheaper on large tiles).  Compare whole rounds of workgroups; ties go to
+// the small tile.  Measured on MI355X (bf16): large products (>= 4096 rows)
+// 1.2-1.3x faster on 256x256; at ~832 rows the q/k/v product gains
+// (880 vs 790 TF/s) while N = 4096 products lose badly (340 vs 760).
 bool big_ok(int epi, const GemmArgs& g) {
     if (g.K % (BBK * kBigStages) != 0 || (int64_t)g.K * 2 * 64 + 64 >= (int64_t)1 << 31) return false;
     if (epi == EPI_QKV && (g.n0 % BBN != 0 || g.n1 % BBN != 0)) return false;
-    if (g.M >= 1536) return true;
-    return epi == EPI_QKV && g.M >= 512 && g.N >= 8192;
+    const int64_t rows_b = epi == EPI_SWIGLU ? 2 * (int64_t)g.N : g.N;   // B rows
+    const int64_t small = ((g.M + BM - 1) / BM) * ((rows_b + BN - 1) / BN);
+    const int64_t big = ((g.M + BBM - 1) / BBM) * ((rows_b + BBN - 1) / BBN);
+    const int64_t cus = num_cus();
+    const double cost_small = (double)((small + cus - 1) / cus);
+    const double cost_big = (epi == EPI_QKV ? 2.8 : 3.0) * ((big + cus - 1) / cus);
+    return cost_big < cost_small;
 }
 
 template <int EPI>

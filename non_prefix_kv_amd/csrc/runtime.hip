@@ -161,6 +161,7 @@ struct cb_model {
     RopeTab rope;
     int device = 0;
     hipStream_t side = nullptr;   // fetch (H2D + rotation) stream, default priority
+    hipMemPool_t pool = nullptr;  // plan workspaces; keeps its memory between plans
     std::mutex mu;
     std::vector<hipEvent_t> event_pool;
     // per-kernel-class timing (cb_profile_*)
@@ -388,7 +389,7 @@ cb_status plan_alloc(cb_plan* p) {
     }
     p->attn_ws_bytes = aw;
     const size_t bytes = carve(p, nullptr, max_rows);
-    if (hipMallocAsync(&p->ws, bytes, p->stream) != hipSuccess) {
+    if (hipMallocFromPoolAsync(&p->ws, bytes, p->m->pool, p->stream) != hipSuccess) {
         (void)hipGetLastError();
         return fail(CB_E_OOM, "workspace of %zu bytes", bytes);
     }
@@ -504,8 +505,10 @@ cb_status do_layer(cb_plan* p, int l) {
     const int mR = lr.mR, mQ = lr.mQ;
     const double d = c.d_model, F = c.ffn_dim, qd = m->qd(), kvd = m->kvd();
     CB_HIP(hipEventRecord(p->layer_start[l], st));
-    CB_HIP(hipStreamWaitEvent(st, p->fetched[l], 0));
-    if (mR == 0) return CB_OK;
+    if (mR == 0) {
+        CB_HIP(hipStreamWaitEvent(st, p->fetched[l], 0));
+        return CB_OK;
+    }
     void* fk = (char*)p->fused_k + (size_t)l * layer_elems(p) * es;
     void* fv = (char*)p->fused_v + (size_t)l * layer_elems(p) * es;
     const int *pos_r = p->pos_a, *row_r = p->row_a;
@@ -537,6 +540,8 @@ cb_status do_layer(cb_plan* p, int l) {
         Span sp(m, CB_K_GEMM_QKV, st, 2.0 * mR * n * d, (mR * d + n * d + mR * n) * es);
         CB_HIP(launch_gemm(dt, EPI_QKV, g, st));
     }
+    // fused[l] is first read below: steps 1-2 overlap the fetch of this layer
+    CB_HIP(hipStreamWaitEvent(st, p->fetched[l], 0));
     // 3. deviation of the recomputed chunk rows against the rotated cache
     const bool measure = lr.nC > 0 && (lr.select_needed || p->deviation);
     if (measure) {
@@ -885,6 +890,20 @@ cb_status cb_model_create(const cb_model_cfg* cfg, const cb_layer_weights* layer
         delete m;
         return fail(CB_E_HIP, "side stream creation failed");
     }
+    // Workspaces come from a pool of the model's own that keeps freed memory
+    // (a plan's workspace is re-mapped on every call otherwise).
+    hipMemPoolProps props{};
+    props.allocType = hipMemAllocationTypePinned;
+    props.location.type = hipMemLocationTypeDevice;
+    props.location.id = m->device;
+    if (hipMemPoolCreate(&m->pool, &props) != hipSuccess) {
+        (void)hipGetLastError();
+        (void)hipStreamDestroy(m->side);
+        delete m;
+        return fail(CB_E_HIP, "memory pool creation failed");
+    }
+    uint64_t keep = UINT64_MAX;
+    (void)hipMemPoolSetAttribute(m->pool, hipMemPoolAttrReleaseThreshold, &keep);
     *out = m;
     return CB_OK;
 }
@@ -894,6 +913,10 @@ void cb_model_destroy(cb_model* m) {
     if (m->side) {
         (void)hipStreamSynchronize(m->side);
         (void)hipStreamDestroy(m->side);
+    }
+    if (m->pool) {
+        (void)hipDeviceSynchronize();   // plans free their workspace in stream order
+        (void)hipMemPoolDestroy(m->pool);
     }
     for (auto e : m->event_pool) (void)hipEventDestroy(e);
     for (auto e : m->timing_pool) (void)hipEventDestroy(e);

@@ -152,7 +152,8 @@ def test_rmsnorm_vs_oracle(lib, dt, rows, d):
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("m,n,k", [(1, 16, 64), (7, 130, 64), (130, 128, 256), (832, 384, 4096),
                                    (257, 1000, 1024), (128, 11008, 512), (3, 4096, 11008),
-                                   (1600, 520, 384), (2048, 256, 128), (1537, 2000, 1152)])
+                                   (1600, 520, 384), (2048, 256, 128), (1537, 2000, 1152),
+                                   (832, 4096, 4096), (1000, 1536, 2048), (640, 2816, 1536)])
 def test_gemm_vs_definition(lib, dt, m, n, k):
     rng = np.random.default_rng(m * 7 + n)
     a = round_to(rng.standard_normal((m, k)), dt)
@@ -170,7 +171,7 @@ def test_gemm_vs_definition(lib, dt, m, n, k):
                                               (70, 416, 4, 2, 64), (200, 1000, 8, 1, 128),
                                               (832, 4096, 4, 4, 128), (129, 129, 2, 2, 128),
                                               (1, 3000, 2, 1, 128), (300, 2500, 4, 2, 64),
-                                              (64, 1025, 3, 3, 128)])
+                                              (64, 1025, 3, 3, 128), (640, 4096, 64, 8, 64)])
 def test_attention_vs_oracle(lib, dt, nq, nkv, hq, hkv, dh):
     rng = np.random.default_rng(nq + nkv)
     qpos = np.sort(rng.choice(nkv, size=nq, replace=False))
