@@ -2,8 +2,10 @@
 from .cacheblend_oracle import (rope_theta, rope_rotate, rmsnorm, silu, attention,
                                 qkv_rows, finish_rows, prefill, schedule,
                                 kv_deviation, topk_select, rerotate_chunks, blend,
-                                kv_size_bytes, check_offsets)
+                                kv_size_bytes, check_offsets, quantize_channels,
+                                dequantize_channels, pack_codes, unpack_codes)
 
 __all__ = ["rope_theta", "rope_rotate", "rmsnorm", "silu", "attention", "qkv_rows",
            "finish_rows", "prefill", "schedule", "kv_deviation", "topk_select",
-           "rerotate_chunks", "blend", "kv_size_bytes", "check_offsets"]
+           "rerotate_chunks", "blend", "kv_size_bytes", "check_offsets",
+           "quantize_channels", "dequantize_channels", "pack_codes", "unpack_codes"]

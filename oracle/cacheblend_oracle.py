@@ -24,6 +24,10 @@ Pages followed (cited by page title and section):
         only; selected tokens attend over the whole input).
   [PC]  "論文解説: Prompt Cache — モジュラーAttention再利用による低レイテンシ推論"
         (0h-n0.github.io): section "RoPEにおける位置調整" (k(p) = R(p-p')k(p')).
+  [CG]  "論文解説: CacheGen — KVキャッシュ圧縮とストリーミングで長文コンテキストの
+        LLM推論を高速化" (0h-n0.github.io): "技術的詳細", step 1 "チャネル別
+        量子化" (per-channel scale and zero point) and "圧縮率と品質のトレード
+        オフ" (bit widths).
 
 Readings taken where the pages are silent or disagree (each is listed with
 its reason in the design notes):
@@ -39,6 +43,9 @@ its reason in the design notes):
   * Top-k ties: order by (deviation descending, position ascending), NaN
     above +inf, -0.0 equal to +0.0; the kept set is returned in ascending
     position order.
+  * Quantized chunk KV: statistics per chunk, layer and channel over the
+    chunk's tokens; K is quantized as stored (chunk-local positions, before
+    rotation); round() is round half to even; codes decided in float32.
   * Pre-norm Llama block: RMSNorm, RoPE on interleaved pairs (2i, 2i+1) with
     theta_i = base^(-2i/d_head), causal softmax attention with GQA head map
     h -> floor(h * H_kv / H_q), SwiGLU MLP, no biases.
@@ -324,6 +331,70 @@ def blend(weights, shape, x0, chunks, offsets, n_suffix, sched, dev_mode="KV",
     return {"fused_k": fk, "fused_v": fv, "sel": sel, "dev": dev,
             "layer_pos": layer_pos, "layer_out": layer_out, "hidden": x,
             "schedule": sched}
+
+
+# --------------------------------------------------------------------------
+# Per-channel quantized chunk KV  [CG "技術的詳細", "ステップ1: チャネル別量子化":
+# per channel c of the H*d_h channels, zero point z_c = min over tokens,
+# scale s_c = (max - min) / (2^b - 1), code = round((x - z_c) / s_c);
+# restored as code * s_c + z_c ("デコード"); b = 8 by default, 4 and 2 also
+# listed in "圧縮率と品質のトレードオフ"]
+# --------------------------------------------------------------------------
+def quantize_channels(x, bits: int):
+    """Codes of x [L][n][H_kv][d_h] per layer and channel.
+
+    The code is an integer decided in float32, as the kernel decides it:
+    z = min_t x, s = (max_t x - z) / (2^b - 1), code = rint((x - z) / s)
+    (round half to even), clamped to [0, 2^b - 1]; a channel with s = 0
+    (all tokens equal) gets code 0.  Inputs must be finite.
+
+    Returns codes [L][n][H_kv*d_h] (uint8, one code per element), scale and
+    zero [L][H_kv*d_h] (float32).
+    """
+    if bits not in (4, 8):
+        raise ValueError("bits must be 4 or 8")
+    x = np.asarray(x, dtype=np.float32)
+    L, n = x.shape[0], x.shape[1]
+    flat = x.reshape(L, n, -1)
+    levels = np.float32(2 ** bits - 1)
+    zero = flat.min(axis=1)
+    scale = (flat.max(axis=1) - zero) / levels
+    codes = np.zeros(flat.shape, dtype=np.uint8)
+    for l in range(L):
+        live = scale[l] > 0
+        q = np.rint((flat[l][:, live] - zero[l][live]) / scale[l][live])
+        codes[l][:, live] = np.clip(q, 0, levels).astype(np.uint8)
+    return codes, scale.astype(np.float32), zero.astype(np.float32)
+
+
+def dequantize_channels(codes, scale, zero, n_kv_heads, head_dim):
+    """x' = code * s_c + z_c in float64, shaped [L][n][H_kv][d_h]."""
+    codes = np.asarray(codes, dtype=np.float64)
+    y = codes * np.asarray(scale, np.float64)[:, None, :] + np.asarray(zero, np.float64)[:, None, :]
+    return y.reshape(codes.shape[0], codes.shape[1], n_kv_heads, head_dim)
+
+
+def pack_codes(codes, bits: int) -> np.ndarray:
+    """Storage bytes of the codes along the channel axis: 8-bit codes as
+    they are; 4-bit codes two per byte, channel 2i in the low nibble and
+    channel 2i+1 in the high nibble (a storage layout of this library; the
+    pages fix none)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    if bits == 8:
+        return codes.copy()
+    if codes.shape[-1] % 2:
+        raise ValueError("4-bit packing needs an even channel count")
+    return (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_codes(packed, bits: int) -> np.ndarray:
+    packed = np.asarray(packed, dtype=np.uint8)
+    if bits == 8:
+        return packed.copy()
+    out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = packed & 15
+    out[..., 1::2] = packed >> 4
+    return out
 
 
 def kv_size_bytes(n_layers, n_kv_heads, head_dim, n_tokens, bytes_per_elem):

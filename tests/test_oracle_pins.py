@@ -339,3 +339,100 @@ def test_gqa_blend_full_recompute():
     res = run_blend(case, [nc] * 3)
     k, v, outs = run_full(case)
     assert rel_err(res["fused_k"], k) < 1e-10 and rel_err(res["hidden"], outs[-1]) < 1e-10
+
+
+# ------------------------------------------------------------ quantized chunk KV
+# CacheGen explainer, "ステップ1: チャネル別量子化" and "圧縮率と品質のトレードオフ".
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantize_exact_grid_roundtrip(bits):
+    """Values on a per-channel grid z + q*s (s a power of two, both extreme
+    codes present) come back as exactly q and exactly x: pins the zero point
+    (the minimum), the denominator 2^b - 1 and the orientation of the map."""
+    rng = np.random.default_rng(11)
+    L, n, H, dh = 2, 9, 2, 8
+    C = H * dh
+    top = 2 ** bits - 1
+    q = rng.integers(0, top + 1, size=(L, n, C))
+    q[:, 0, :] = 0
+    q[:, 1, :] = top
+    e = rng.integers(-12, -2, size=(L, 1, C)).astype(np.float64)
+    s = 2.0 ** e
+    z = rng.integers(-500, 500, size=(L, 1, C)) * s
+    x = (z + q * s).astype(np.float32)
+    assert np.array_equal(x.astype(np.float64), z + q * s)       # exact in float32
+    codes, scale, zero = oracle.quantize_channels(x.reshape(L, n, H, dh), bits)
+    assert np.array_equal(codes, q)
+    assert np.array_equal(scale, s[:, 0, :].astype(np.float32))
+    assert np.array_equal(zero, z[:, 0, :].astype(np.float32))
+    back = oracle.dequantize_channels(codes, scale, zero, H, dh)
+    assert np.array_equal(back.reshape(L, n, C), x.astype(np.float64))
+
+
+@pytest.mark.parametrize("bits", [8, 4])
+def test_quantize_error_bound_and_extremes(bits):
+    """|x' - x| <= s_c / 2 (nearest level), min -> 0 and max -> 2^b - 1."""
+    rng = np.random.default_rng(12)
+    L, n, H, dh = 3, 40, 2, 16
+    x = (rng.standard_normal((L, n, H, dh)) * rng.uniform(0.01, 3, size=(L, 1, H, dh))
+         ).astype(np.float32)
+    codes, scale, zero = oracle.quantize_channels(x, bits)
+    back = oracle.dequantize_channels(codes, scale, zero, H, dh).reshape(L, n, -1)
+    flat = x.reshape(L, n, -1).astype(np.float64)
+    err = np.abs(back - flat)
+    bound = scale.astype(np.float64)[:, None, :] * 0.5 * (1 + 1e-5) + 1e-6 * np.abs(flat)
+    assert np.all(err <= bound)
+    lo, hi = flat.argmin(axis=1), flat.argmax(axis=1)
+    li = np.arange(L)[:, None]
+    ci = np.arange(flat.shape[2])[None, :]
+    assert np.all(codes[li, lo, ci] == 0)
+    assert np.all(codes[li, hi, ci] == 2 ** bits - 1)
+
+
+def test_quantize_nearest_level_brute_force():
+    """Each code is the level z + q*s nearest to x among all 2^b levels
+    (checked away from ties)."""
+    rng = np.random.default_rng(13)
+    for bits in (4, 8):
+        x = rng.standard_normal((1, 7, 1, 6)).astype(np.float32)
+        codes, scale, zero = oracle.quantize_channels(x, bits)
+        flat = x.reshape(7, 6).astype(np.float64)
+        levels = zero[0].astype(np.float64)[None, :] + \
+            np.arange(2 ** bits)[:, None] * scale[0].astype(np.float64)[None, :]
+        for t in range(7):
+            for c in range(6):
+                d = np.abs(levels[:, c] - flat[t, c])
+                order = np.argsort(d)
+                if d[order[1]] - d[order[0]] < 1e-6 * scale[0, c]:
+                    continue
+                assert codes[0, t, c] == order[0]
+
+
+def test_quantize_constant_channel():
+    x = np.ones((1, 5, 1, 4), dtype=np.float32) * np.float32(0.375)
+    x[0, :, 0, 1] = np.arange(5)
+    codes, scale, zero = oracle.quantize_channels(x, 8)
+    assert scale[0, 0] == 0 and np.all(codes[0, :, 0] == 0)
+    back = oracle.dequantize_channels(codes, scale, zero, 1, 4)
+    assert np.all(back[0, :, 0, 0] == 0.375)
+    assert codes[0, 0, 1] == 0 and codes[0, 4, 1] == 255
+
+
+def test_code_packing():
+    codes = np.array([[1, 2, 3, 4, 15, 0]], dtype=np.uint8)
+    assert oracle.pack_codes(codes, 4).tolist() == [[0x21, 0x43, 0x0F]]
+    rng = np.random.default_rng(14)
+    c = rng.integers(0, 16, size=(3, 5, 8)).astype(np.uint8)
+    assert np.array_equal(oracle.unpack_codes(oracle.pack_codes(c, 4), 4), c)
+    assert np.array_equal(oracle.pack_codes(c, 8), c)
+
+
+@pytest.mark.parametrize("bits,ratio", [(8, 2), (4, 4)])
+def test_code_bytes_vs_printed_ratio(bits, ratio):
+    """Code bytes against FP16 storage: about 2x for 8 bits and 4x for 4
+    bits, as the CacheGen explainer's trade-off table prints (the per-channel
+    scale and zero are 8 bytes per channel per layer on top)."""
+    L, n, H, dh = 2, 64, 2, 8
+    codes = np.zeros((L, n, H * dh), dtype=np.uint8)
+    fp16_bytes = oracle.kv_size_bytes(L, H, dh, n, 2) // 2      # K alone
+    assert fp16_bytes / oracle.pack_codes(codes, bits).nbytes == ratio
