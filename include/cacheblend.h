@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 1
+#define CB_ABI_VERSION 2
 
 typedef enum cb_status {
     CB_OK = 0,
@@ -109,17 +109,36 @@ typedef struct cb_layer_weights {
     const void* w_down;
 } cb_layer_weights;
 
+/* Storage format of a chunk cache.  PLAIN: the model dtype.  U8 / U4:
+ * per-channel quantized codes (CacheGen explainer (0h-n0), "技術的詳細",
+ * step 1 "チャネル別量子化"; 8 and 4 bits from its trade-off table): for
+ * each layer and each of the C = H_kv*d_head channels c, over the chunk's
+ * tokens, zero z_c = min x, scale s_c = (max x - z_c) / (2^b - 1), code =
+ * round-half-even((x - z_c) / s_c) clamped to [0, 2^b - 1] (code 0 where
+ * s_c = 0), decided in float32.  The fused cache receives code * s_c + z_c
+ * (K then rotated like PLAIN).  U8 stores one code per byte; U4 two per
+ * byte, channel 2i in the low nibble and 2i+1 in the high nibble.
+ * cb_quantize_kv produces both. */
+typedef enum cb_kv_format { CB_KV_PLAIN = 0, CB_KV_U8 = 1, CB_KV_U4 = 2 } cb_kv_format;
+
 /* A precomputed chunk cache at chunk-local positions 0..n_tokens-1.
- * k, v: [L][n_tokens][H_kv][d_head]; layer l starts at element
- * l * layer_stride (layer_stride >= n_tokens*H_kv*d_head), which lets chunks
- * live inside a larger pool.  on_host = 0: device memory; 1: pinned host
- * memory, copied to the device layer by layer on the library's side stream. */
+ * k, v: [L][n_tokens][H_kv][d_head]; layer l starts at element (PLAIN) or
+ * code (U8/U4) l * layer_stride (layer_stride >= n_tokens*H_kv*d_head),
+ * which lets chunks live inside a larger pool.  on_host = 0: device memory;
+ * 1: pinned host memory, copied to the device layer by layer on the
+ * library's side stream.  Quantized chunks also pass qparams:
+ * [L][4][H_kv*d_head] float32 (k scale, k zero, v scale, v zero of every
+ * channel), in the same kind of memory as k and v.  k, v and qparams must
+ * be 16-byte aligned, and the bytes of a layer stride a multiple of 16. */
 typedef struct cb_chunk_kv {
     const void* k;
     const void* v;
     int32_t n_tokens;
     int32_t on_host;
     int64_t layer_stride;
+    int32_t kv_format;        /* cb_kv_format                              */
+    int32_t reserved;         /* must be 0                                 */
+    const float* qparams;     /* U8/U4: [L][4][H_kv*d_head]; PLAIN: NULL   */
 } cb_chunk_kv;
 
 typedef struct cb_request {
@@ -310,6 +329,29 @@ cb_status cb_rope_rerotate(int32_t dtype, const void* k_in, void* k_out,
                            const void* v_in, void* v_out, int32_t n_tokens,
                            int32_t n_heads, int32_t head_dim, int32_t delta,
                            double rope_base, void* stream);
+
+/* Per-channel quantization of one chunk tensor (K or V) in the format
+ * described at cb_kv_format.  x: [n_layers][n_tokens][row] in dtype, layer
+ * l at element l * x_layer_stride.  bits: 8 or 4.  codes: [n_layers]
+ * [n_tokens][row * bits / 8] bytes, dense (layer l at byte l * n_tokens *
+ * row * bits / 8).  scale, zero: float32, the row values of layer l at
+ * element l * param_stride (param_stride = 4 * row with scale = qparams
+ * and zero = qparams + row for K, + 2 row and + 3 row for V, gives the
+ * qparams layout of cb_chunk_kv).  row must be a multiple of 8; pointers
+ * 16-byte aligned; x must be finite. */
+cb_status cb_quantize_kv(int32_t dtype, const void* x, int32_t n_layers, int32_t n_tokens,
+                         int32_t row, int64_t x_layer_stride, int32_t bits, void* codes,
+                         float* scale, float* zero, int64_t param_stride, void* stream);
+
+/* Dequantization fused with RoPE re-alignment, for one layer:
+ * k_out[t] = R(delta) (k_codes[t] * s_k + z_k), v_out[t] = v_codes[t] * s_v
+ * + z_v (when v_codes is not NULL) for n_tokens rows of [n_heads][head_dim];
+ * qparams: [4][n_heads*head_dim] (k scale, k zero, v scale, v zero);
+ * kv_format CB_KV_U8 or CB_KV_U4; outputs in dtype. */
+cb_status cb_dequant_rerotate(int32_t dtype, int32_t kv_format, const void* k_codes,
+                              const void* v_codes, const float* qparams, void* k_out,
+                              void* v_out, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
+                              int32_t delta, double rope_base, void* stream);
 
 /* KV deviation (CacheBlend explainer (0h-n0), eq. 1 squared):
  * dev[i] = sum over the row of (k_new - k_cached)^2 (+ (v_new - v_cached)^2)

@@ -17,12 +17,13 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ------------------------------------------------------------------ constants
-CB_ABI_VERSION = 1
+CB_ABI_VERSION = 2
 CB_OK, CB_E_INVALID, CB_E_SHAPE, CB_E_NOT_PINNED, CB_E_SCHEDULE = 0, -1, -2, -3, -4
 CB_E_OOM, CB_E_HIP, CB_E_BAD_STATE, CB_E_UNSUPPORTED = -5, -6, -7, -8
 CB_F32, CB_BF16 = 0, 1
 CB_SCHED_GRADUAL, CB_SCHED_FIXED = 0, 1
 CB_DEV_KV, CB_DEV_K, CB_DEV_V = 0, 1, 2
+CB_KV_PLAIN, CB_KV_U8, CB_KV_U4 = 0, 1, 2
 
 _c_i32, _c_i64, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
 
@@ -41,7 +42,8 @@ class cb_layer_weights(ctypes.Structure):
 
 class cb_chunk_kv(ctypes.Structure):
     _fields_ = [("k", _c_p), ("v", _c_p), ("n_tokens", _c_i32), ("on_host", _c_i32),
-                ("layer_stride", _c_i64)]
+                ("layer_stride", _c_i64), ("kv_format", _c_i32), ("reserved", _c_i32),
+                ("qparams", _c_p)]
 
 
 class cb_request(ctypes.Structure):
@@ -111,6 +113,10 @@ _fn = {
     "cb_profile_read": (ctypes.c_int, _c_p, _P(cb_kernel_stat)),
     "cb_rope_rerotate": (ctypes.c_int, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
                          _c_i32, ctypes.c_double, _c_p),
+    "cb_quantize_kv": (ctypes.c_int, _c_i32, _c_p, _c_i32, _c_i32, _c_i32, _c_i64, _c_i32, _c_p,
+                       _c_p, _c_p, _c_i64, _c_p),
+    "cb_dequant_rerotate": (ctypes.c_int, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_i32,
+                            _c_i32, _c_i32, _c_i32, ctypes.c_double, _c_p),
     "cb_deviation": (ctypes.c_int, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p,
                      _c_p),
     "cb_topk_select": (ctypes.c_int, _c_p, _c_i32, _c_i32, _c_p, _c_p),
@@ -219,7 +225,9 @@ class Model:
 
 
 def _chunk_array(chunks):
-    """chunks: list of dicts {k, v, n_tokens, on_host, layer_stride} with tensors or ints."""
+    """chunks: list of dicts {k, v, n_tokens, on_host, layer_stride} with
+    tensors or ints, plus kv_format (CB_KV_U8 / CB_KV_U4) and qparams for
+    quantized chunks."""
     arr = (cb_chunk_kv * max(1, len(chunks)))()
     for i, c in enumerate(chunks):
         arr[i].k = _ptr(c["k"])
@@ -227,6 +235,8 @@ def _chunk_array(chunks):
         arr[i].n_tokens = c["n_tokens"]
         arr[i].on_host = int(c.get("on_host", 0))
         arr[i].layer_stride = c["layer_stride"]
+        arr[i].kv_format = int(c.get("kv_format", CB_KV_PLAIN))
+        arr[i].qparams = _ptr(c.get("qparams"))
     return arr
 
 
@@ -351,6 +361,38 @@ def cb_rope_rerotate(k_in, k_out, v_in, v_out, n_tokens, n_heads, head_dim, delt
     _check(RAW["cb_rope_rerotate"](_dtype_code(k_in), _ptr(k_in), _ptr(k_out), _ptr(v_in),
                                    _ptr(v_out), n_tokens, n_heads, head_dim, delta, rope_base,
                                    _stream(stream)))
+
+
+def cb_quantize_kv(x, n_layers, n_tokens, row, x_layer_stride, bits, codes, scale, zero,
+                   param_stride, stream=None):
+    _check(RAW["cb_quantize_kv"](_dtype_code(x), _ptr(x), n_layers, n_tokens, row,
+                                 x_layer_stride, bits, _ptr(codes), _ptr(scale), _ptr(zero),
+                                 param_stride, _stream(stream)))
+
+
+def cb_dequant_rerotate(kv_format, k_codes, v_codes, qparams, k_out, v_out, n_tokens, n_heads,
+                        head_dim, delta, rope_base=10000.0, stream=None):
+    _check(RAW["cb_dequant_rerotate"](_dtype_code(k_out), kv_format, _ptr(k_codes),
+                                      _ptr(v_codes), _ptr(qparams), _ptr(k_out), _ptr(v_out),
+                                      n_tokens, n_heads, head_dim, delta, rope_base,
+                                      _stream(stream)))
+
+
+def quantize_chunk(k, v, bits, stream=None):
+    """Device codes of a chunk cache k, v [L][n][H_kv][d_head] (model dtype):
+    returns {k, v, qparams, kv_format, n_tokens, layer_stride} ready for
+    cb_blend / cb_blend_batch (device-resident)."""
+    import torch
+    L, n = k.shape[0], k.shape[1]
+    row = k.shape[2] * k.shape[3]
+    kc = torch.empty((L, n, row * bits // 8), dtype=torch.uint8, device=k.device)
+    vc = torch.empty_like(kc)
+    qp = torch.empty((L, 4, row), dtype=torch.float32, device=k.device)
+    for x, codes, j in ((k, kc, 0), (v, vc, 2)):
+        cb_quantize_kv(x, L, n, row, n * row, bits, codes, qp[:, j], qp[:, j + 1], 4 * row,
+                       stream)
+    return {"k": kc, "v": vc, "qparams": qp, "n_tokens": n, "layer_stride": n * row,
+            "kv_format": CB_KV_U8 if bits == 8 else CB_KV_U4}
 
 
 def cb_deviation(k_new, v_new, k_cached, v_cached, n_rows, row_elems, dev_mode, dev_out,

@@ -39,6 +39,42 @@ struct RotJobs {
 hipError_t launch_rerotate(int dtype, const RotJobs& jobs, int layer, void* k_dst, void* v_dst,
                            int n_heads, int head_dim, const RopeTab& rope, hipStream_t s);
 
+// ------------------------------------------------------------------ quantized chunks
+// Per-channel quantized chunk caches (8- or 4-bit codes, a float32 scale and
+// zero point per layer and channel; 4-bit codes two per byte, even channel
+// in the low nibble).
+
+// One quantized chunk to dequantize into the fused cache of one layer.
+struct QRotJob {
+    const uint8_t* k;           // K codes of layer 0
+    const uint8_t* v;           // V codes of layer 0 (nullptr: no V)
+    const float* qp;            // [4][row] of layer 0: k scale, k zero, v scale, v zero
+    int64_t code_layer_stride;  // bytes between layers of k / v
+    int64_t qp_layer_stride;    // floats between layers of qp
+    int dst_row;                // first destination row (chunk offset)
+    int n_tokens;
+    int delta;                  // rotation amount
+    int staged;                 // host bookkeeping: k/v/qp are offsets into a staging area
+};
+
+constexpr int kMaxQRotJobs = 32;
+struct QRotJobs {
+    QRotJob j[kMaxQRotJobs];
+    int n;
+    int max_tokens;
+};
+
+// For every job and token t: K row (dst_row + t) of k_dst = R(delta) *
+// dequant(K codes row t of layer `layer`); V row = dequant(V codes row t).
+hipError_t launch_dequant_rerotate(int dtype, int bits, const QRotJobs& jobs, int layer,
+                                   void* k_dst, void* v_dst, int n_heads, int head_dim,
+                                   const RopeTab& rope, hipStream_t s);
+
+// Codes, scale and zero of x [n_layers][n_tokens][row] per layer and channel.
+hipError_t launch_quantize(int dtype, const void* x, int n_layers, int n_tokens, int row,
+                           int64_t x_layer_stride, int bits, void* codes, float* scale,
+                           float* zero, int64_t param_stride, hipStream_t s);
+
 // p[i] = base + i for i < n.
 hipError_t launch_iota(int* p, int n, int base, hipStream_t s);
 

@@ -16,40 +16,6 @@ namespace {
 
 constexpr int kThreads = 256;
 
-template <typename T> struct Vec8;
-template <> struct Vec8<bf16> {
-    static __device__ __forceinline__ void load(const bf16* p, float* x) {
-        bf16x8 v = *reinterpret_cast<const bf16x8*>(p);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = static_cast<float>(v[i]);
-    }
-    static __device__ __forceinline__ void store(bf16* p, const float* x) {
-        bf16x8 v;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = static_cast<bf16>(x[i]);
-        *reinterpret_cast<bf16x8*>(p) = v;
-    }
-    static __device__ __forceinline__ void copy(const bf16* s, bf16* d) {
-        *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(s);
-    }
-};
-template <> struct Vec8<float> {
-    static __device__ __forceinline__ void load(const float* p, float* x) {
-        floatx4 a = *reinterpret_cast<const floatx4*>(p);
-        floatx4 b = *reinterpret_cast<const floatx4*>(p + 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
-    }
-    static __device__ __forceinline__ void store(float* p, const float* x) {
-        *reinterpret_cast<floatx4*>(p) = floatx4{x[0], x[1], x[2], x[3]};
-        *reinterpret_cast<floatx4*>(p + 4) = floatx4{x[4], x[5], x[6], x[7]};
-    }
-    static __device__ __forceinline__ void copy(const float* s, float* d) {
-        *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(s);
-        *reinterpret_cast<u32x4*>(d + 4) = *reinterpret_cast<const u32x4*>(s + 4);
-    }
-};
-
 // One thread moves 8 consecutive elements of one K row (4 rotation pairs)
 // and the matching 8 elements of the V row.  Consecutive threads cover
 // consecutive 16/32-byte pieces of a row, so every wave reads and writes

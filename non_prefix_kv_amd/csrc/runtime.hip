@@ -229,6 +229,22 @@ struct cb_plan {
     };
     std::vector<H2D> h2d;
     std::vector<RotJobs> jobs_copy, jobs_inplace;
+    // quantized chunks: host ones are copied each layer (codes and that
+    // layer's parameters) into a staging area of the workspace, then every
+    // use is decoded from there; device ones are decoded from where they are
+    struct QH2D {
+        const char* k;
+        const char* v;
+        const char* qp;
+        size_t layer_bytes;       // code bytes between layers of the source
+        size_t bytes;             // code bytes per layer
+        size_t qp_bytes;          // parameter bytes per layer
+        size_t stage_off;         // staging offset: k codes, v codes, parameters
+    };
+    std::vector<QH2D> qh2d;
+    size_t stage_bytes = 0;
+    char* stage = nullptr;
+    std::vector<QRotJobs> qjobs[2];   // [0]: 8-bit, [1]: 4-bit codes
     // Layers the side stream may run ahead of the main stream.  Rotation
     // kernels share the compute units with the layers, so device-resident
     // chunks are fetched just ahead; host copies run on the copy engines and
@@ -373,6 +389,7 @@ size_t carve(cb_plan* p, char* base, int max_rows) {
     p->row_b = (int*)take(R * 4);
     p->sel_local = (int*)take(R * 4);
     p->attn_ws = p->attn_ws_bytes ? take(p->attn_ws_bytes) : nullptr;
+    p->stage = p->stage_bytes ? take(p->stage_bytes) : nullptr;
     return off;
 }
 
@@ -394,6 +411,17 @@ cb_status plan_alloc(cb_plan* p) {
         return fail(CB_E_OOM, "workspace of %zu bytes", bytes);
     }
     carve(p, (char*)p->ws, max_rows);
+    // decode jobs of staged chunks point into the staging area from now on
+    for (auto& set : p->qjobs)
+        for (QRotJobs& js : set)
+            for (int i = 0; i < js.n; ++i) {
+                QRotJob& j = js.j[i];
+                if (!j.staged) continue;
+                j.k = (const uint8_t*)(p->stage + (uintptr_t)j.k);
+                j.v = (const uint8_t*)(p->stage + (uintptr_t)j.v);
+                j.qp = (const float*)(p->stage + (uintptr_t)j.qp);
+                j.staged = 0;
+            }
     return CB_OK;
 }
 
@@ -489,6 +517,27 @@ cb_status do_fetch(cb_plan* p, int l) {
             Span sp(m, CB_K_ROTATE, side, 0, job_bytes(js, (double)row_bytes));
             CB_HIP(launch_rerotate(m->cfg.dtype, js, l, fk, fv, m->cfg.n_kv_heads,
                                    m->cfg.head_dim, m->rope, side));
+        }
+    // quantized chunks; the staging area is reused every layer, which the
+    // side stream's order makes safe (this layer's copies start after the
+    // previous layer's decode kernels)
+    for (const cb_plan::QH2D& h : p->qh2d) {
+        const size_t src = (size_t)l * h.layer_bytes;
+        char* st = p->stage + h.stage_off;
+        CB_HIP(hipMemcpyAsync(st, h.k + src, h.bytes, hipMemcpyHostToDevice, side));
+        CB_HIP(hipMemcpyAsync(st + align_up(h.bytes, 256), h.v + src, h.bytes,
+                              hipMemcpyHostToDevice, side));
+        CB_HIP(hipMemcpyAsync(st + 2 * align_up(h.bytes, 256), h.qp + (size_t)l * h.qp_bytes,
+                              h.qp_bytes, hipMemcpyHostToDevice, side));
+    }
+    for (int b = 0; b < 2; ++b)
+        for (const QRotJobs& js : p->qjobs[b]) {
+            double bytes = 0;
+            for (int i = 0; i < js.n; ++i)
+                bytes += js.j[i].n_tokens * (double)m->kvd() * 2 * (es + (b == 0 ? 1.0 : 0.5));
+            Span sp(m, CB_K_ROTATE, side, 0, bytes);
+            CB_HIP(launch_dequant_rerotate(m->cfg.dtype, b == 0 ? 8 : 4, js, l, fk, fv,
+                                           m->cfg.n_kv_heads, m->cfg.head_dim, m->rope, side));
         }
     CB_HIP(hipEventRecord(p->fetched[l], side));
     p->fetch_done[l] = 1;
@@ -629,8 +678,25 @@ cb_status check_chunk(cb_model* m, const cb_chunk_kv& ck, int idx) {
     } else if (mk != MemKind::Device || mv != MemKind::Device) {
         return fail(CB_E_INVALID, "chunk %d: on_host = 0 but K/V are not device memory", idx);
     }
-    if (!aligned_to(ck.k, 16) || !aligned_to(ck.v, 16) || (ck.layer_stride * m->es()) % 16)
-        return fail(CB_E_SHAPE, "chunk %d: K/V and layer stride must be 16-byte aligned", idx);
+    if (ck.reserved != 0) return fail(CB_E_INVALID, "chunk %d: reserved field must be 0", idx);
+    if (ck.kv_format == CB_KV_PLAIN) {
+        if (ck.qparams) return fail(CB_E_INVALID, "chunk %d: qparams given for a plain chunk", idx);
+        if (!aligned_to(ck.k, 16) || !aligned_to(ck.v, 16) || (ck.layer_stride * m->es()) % 16)
+            return fail(CB_E_SHAPE, "chunk %d: K/V and layer stride must be 16-byte aligned", idx);
+        return CB_OK;
+    }
+    if (ck.kv_format != CB_KV_U8 && ck.kv_format != CB_KV_U4)
+        return fail(CB_E_INVALID, "chunk %d: kv_format %d", idx, ck.kv_format);
+    if (!ck.qparams) return fail(CB_E_INVALID, "chunk %d: quantized chunk without qparams", idx);
+    const MemKind mq = mem_kind(ck.qparams);
+    if (ck.on_host ? mq != MemKind::Pinned : mq != MemKind::Device)
+        return fail(ck.on_host ? CB_E_NOT_PINNED : CB_E_INVALID,
+                    "chunk %d: qparams must be in the same kind of memory as K/V", idx);
+    const int64_t stride_bytes = ck.kv_format == CB_KV_U8 ? ck.layer_stride : ck.layer_stride / 2;
+    if (!aligned_to(ck.k, 16) || !aligned_to(ck.v, 16) || !aligned_to(ck.qparams, 16) ||
+        (ck.kv_format == CB_KV_U4 && ck.layer_stride % 2) || stride_bytes % 16)
+        return fail(CB_E_SHAPE, "chunk %d: codes, qparams and layer stride must be 16-byte aligned",
+                    idx);
     return CB_OK;
 }
 
@@ -674,9 +740,46 @@ cb_status plan_layout(cb_plan* p) {
     const size_t es = p->m->es(), row_elems = p->m->kvd();
     std::vector<int64_t> first_row(p->pool.size(), -1);
     std::vector<RotJob> copy, inplace;
+    std::vector<QRotJob> qjobs[2];
+    std::vector<int64_t> staged_at(p->pool.size(), -1);
     for (const ReqInfo& q : p->reqs)
         for (size_t c = 0; c < q.ids.size(); ++c) {
             const cb_chunk_kv& ck = p->pool[q.ids[c]];
+            if (ck.kv_format != CB_KV_PLAIN) {
+                const int b = ck.kv_format == CB_KV_U8 ? 0 : 1;
+                const size_t code_bytes = (size_t)ck.n_tokens * row_elems / (b == 0 ? 1 : 2);
+                const size_t qp_bytes = 4 * row_elems * sizeof(float);
+                QRotJob j{};
+                j.dst_row = q.G + q.offsets[c];
+                j.n_tokens = ck.n_tokens;
+                j.delta = q.offsets[c];
+                if (!ck.on_host) {
+                    j.k = (const uint8_t*)ck.k;
+                    j.v = (const uint8_t*)ck.v;
+                    j.qp = ck.qparams;
+                    j.code_layer_stride = b == 0 ? ck.layer_stride : ck.layer_stride / 2;
+                    j.qp_layer_stride = 4 * (int64_t)row_elems;
+                } else {
+                    if (staged_at[q.ids[c]] < 0) {
+                        staged_at[q.ids[c]] = (int64_t)p->stage_bytes;
+                        p->qh2d.push_back({(const char*)ck.k, (const char*)ck.v,
+                                           (const char*)ck.qparams,
+                                           (size_t)(b == 0 ? ck.layer_stride : ck.layer_stride / 2),
+                                           code_bytes, qp_bytes, p->stage_bytes});
+                        p->stage_bytes += 2 * align_up(code_bytes, 256) + align_up(qp_bytes, 256);
+                    }
+                    // offsets into the staging area until the workspace exists
+                    const size_t o = (size_t)staged_at[q.ids[c]];
+                    j.k = (const uint8_t*)(uintptr_t)o;
+                    j.v = (const uint8_t*)(uintptr_t)(o + align_up(code_bytes, 256));
+                    j.qp = (const float*)(uintptr_t)(o + 2 * align_up(code_bytes, 256));
+                    j.code_layer_stride = 0;
+                    j.qp_layer_stride = 0;
+                    j.staged = 1;
+                }
+                qjobs[b].push_back(j);
+                continue;
+            }
             RotJob j{};
             j.src_layer_stride = ck.layer_stride;
             j.dst_row = q.G + q.offsets[c];
@@ -700,7 +803,14 @@ cb_status plan_layout(cb_plan* p) {
                 copy.push_back(j);
             }
         }
-    p->lookahead = p->h2d.empty() ? 2 : std::max(2, p->L);
+    p->lookahead = p->h2d.empty() && p->qh2d.empty() ? 2 : std::max(2, p->L);
+    for (int b = 0; b < 2; ++b)
+        for (size_t i = 0; i < qjobs[b].size(); ++i) {
+            if (i % kMaxQRotJobs == 0) p->qjobs[b].push_back(QRotJobs{});
+            QRotJobs& js = p->qjobs[b].back();
+            js.j[js.n++] = qjobs[b][i];
+            js.max_tokens = std::max(js.max_tokens, qjobs[b][i].n_tokens);
+        }
     for (auto [src, dst] : {std::make_pair(&copy, &p->jobs_copy),
                             std::make_pair(&inplace, &p->jobs_inplace)})
         for (size_t i = 0; i < src->size(); ++i) {
@@ -1101,6 +1211,60 @@ cb_status cb_rope_rerotate(int32_t dtype, const void* k_in, void* k_out, const v
     js.n = 1;
     js.max_tokens = n_tokens;
     CB_HIP(launch_rerotate(dtype, js, 0, k_out, v_out, n_heads, head_dim, rt, as_stream(stream)));
+    return CB_OK;
+}
+
+cb_status cb_quantize_kv(int32_t dtype, const void* x, int32_t n_layers, int32_t n_tokens,
+                         int32_t row, int64_t x_layer_stride, int32_t bits, void* codes,
+                         float* scale, float* zero, int64_t param_stride, void* stream) {
+    if (dtype != CB_F32 && dtype != CB_BF16) return fail(CB_E_INVALID, "dtype %d", dtype);
+    if (bits != 8 && bits != 4) return fail(CB_E_INVALID, "bits must be 8 or 4, got %d", bits);
+    if (n_layers < 0 || n_tokens < 0) return fail(CB_E_SHAPE, "negative sizes");
+    if (n_layers == 0 || n_tokens == 0) return CB_OK;
+    if (row <= 0 || row % 8) return fail(CB_E_SHAPE, "row %d must be a positive multiple of 8", row);
+    if (x_layer_stride < (int64_t)n_tokens * row || param_stride < row)
+        return fail(CB_E_SHAPE, "layer stride below n_tokens*row or param_stride below row");
+    if (!x || !codes || !scale || !zero) return fail(CB_E_INVALID, "NULL buffer");
+    if (!aligned_to(x, 16) || !aligned_to(codes, 16) || !aligned_to(scale, 16) ||
+        !aligned_to(zero, 16) || (x_layer_stride * elem_size(dtype)) % 16 || param_stride % 4)
+        return fail(CB_E_SHAPE, "buffers, the layer stride and param_stride must be 16-byte aligned");
+    CB_HIP(launch_quantize(dtype, x, n_layers, n_tokens, row, x_layer_stride, bits, codes, scale,
+                           zero, param_stride, as_stream(stream)));
+    return CB_OK;
+}
+
+cb_status cb_dequant_rerotate(int32_t dtype, int32_t kv_format, const void* k_codes,
+                              const void* v_codes, const float* qparams, void* k_out,
+                              void* v_out, int32_t n_tokens, int32_t n_heads, int32_t head_dim,
+                              int32_t delta, double rope_base, void* stream) {
+    if (dtype != CB_F32 && dtype != CB_BF16) return fail(CB_E_INVALID, "dtype %d", dtype);
+    if (kv_format != CB_KV_U8 && kv_format != CB_KV_U4)
+        return fail(CB_E_INVALID, "kv_format %d is not a quantized format", kv_format);
+    if (n_tokens > 0 && (!k_codes || !k_out || !qparams || (v_codes && !v_out)))
+        return fail(CB_E_INVALID, "NULL buffer");
+    if (n_tokens < 0 || n_heads <= 0 || head_dim <= 0 || head_dim % 8)
+        return fail(CB_E_SHAPE, "bad sizes (head_dim must be a multiple of 8)");
+    if (!aligned_to(k_codes, 16) || !aligned_to(v_codes, 16) || !aligned_to(qparams, 16) ||
+        !aligned_to(k_out, 16) || !aligned_to(v_out, 16))
+        return fail(CB_E_SHAPE, "buffers must be 16-byte aligned");
+    if (!(rope_base > 1.0)) return fail(CB_E_INVALID, "rope_base must be > 1");
+    if (delta == INT32_MIN) return fail(CB_E_INVALID, "delta out of range");
+    if (n_tokens == 0) return CB_OK;
+    RopeTab rt;
+    const int ad = delta < 0 ? -delta : delta;
+    cb_status st = get_rope(rope_base, head_dim, ad + 1, &rt);
+    if (st != CB_OK) return st;
+    QRotJobs js{};
+    QRotJob& j = js.j[0];
+    j.k = (const uint8_t*)k_codes;
+    j.v = (const uint8_t*)v_codes;
+    j.qp = qparams;
+    j.n_tokens = n_tokens;
+    j.delta = delta;
+    js.n = 1;
+    js.max_tokens = n_tokens;
+    CB_HIP(launch_dequant_rerotate(dtype, kv_format == CB_KV_U8 ? 8 : 4, js, 0, k_out, v_out,
+                                   n_heads, head_dim, rt, as_stream(stream)));
     return CB_OK;
 }
 

@@ -24,8 +24,22 @@ def make_model(npk, case, dt):
                      layers, rope_base=s.rope_base, rms_eps=s.rms_eps)
 
 
-def chunk_inputs(case, dt, on_host=False):
-    """Chunk caches as [L][n_c][Hkv][dh] tensors (device, or pinned host)."""
+def quant_chunk(codes, bits, on_host=False):
+    """One chunk descriptor from oracle codes (K codes, V codes, qparams)."""
+    kc, vc, qp = codes
+    t = [torch.from_numpy(np.ascontiguousarray(a)) for a in (kc, vc, qp)]
+    t = [x.pin_memory() if on_host else x.cuda() for x in t]
+    L, n, width = kc.shape
+    return {"k": t[0], "v": t[1], "qparams": t[2], "n_tokens": n, "on_host": int(on_host),
+            "layer_stride": n * width * 8 // bits, "kv_format": 1 if bits == 8 else 2}
+
+
+def chunk_inputs(case, dt, on_host=False, quant=None):
+    """Chunk caches as [L][n_c][Hkv][dh] tensors (device, or pinned host);
+    quant = (codes from helpers.quantize_case, bits) passes them as codes."""
+    if quant is not None:
+        codes, bits = quant
+        return [quant_chunk(c, bits, on_host) for c in codes]
     chunks = []
     for k, v in case.chunks:
         kt, vt = dev(k, dt), dev(v, dt)
@@ -38,11 +52,13 @@ def chunk_inputs(case, dt, on_host=False):
     return chunks
 
 
-def run_gpu_blend(npk, model, case, dt, schedule, dev_mode=0, on_host=False, plan=False):
+def run_gpu_blend(npk, model, case, dt, schedule, dev_mode=0, on_host=False, plan=False,
+                  quant=None, chunks=None):
     s = case.shape
     N, Nc, L = case.n_tokens, case.n_chunk_tokens, s.n_layers
     tdt = TORCH_DT[dt]
-    chunks = chunk_inputs(case, dt, on_host)
+    if chunks is None:
+        chunks = chunk_inputs(case, dt, on_host, quant)
     x0 = dev(case.x0, dt)
     fk = torch.full((L, N, s.n_kv_heads, s.head_dim), float("nan"), dtype=tdt, device="cuda")
     fv = torch.full_like(fk, float("nan"))
@@ -88,13 +104,17 @@ def pool_inputs(bcase, dt, on_host=False):
 
 
 def run_gpu_batch(npk, model, bcase, dt, schedules=None, recompute_bp=1500,
-                  schedule_kind=0, dev_mode=0, on_host=False, dev_fill=float("nan")):
+                  schedule_kind=0, dev_mode=0, on_host=False, dev_fill=float("nan"),
+                  override=None):
     """cb_blend_batch over the whole batch; returns the stacked outputs split
-    per request (views) plus the raw stacked tensors."""
+    per request (views) plus the raw stacked tensors.  override: {pool index:
+    chunk descriptor} replacing the plain pool entries (e.g. quantized)."""
     s = bcase.shape
     L = s.n_layers
     tdt = TORCH_DT[dt]
     pool = pool_inputs(bcase, dt, on_host)
+    for i, c in (override or {}).items():
+        pool[i] = c
     reqs = []
     for i, r in enumerate(bcase.requests):
         d = {"chunk_ids": r["chunk_ids"], "n_suffix": r["n_suffix"]}

@@ -106,3 +106,21 @@ def make_batch_case(shape, pool_lens, requests, seed=0, dtype="f64", n_layers=No
                           [int(o) for o in offsets], int(r["n_suffix"]), dtype))
         xs.append(x0)
     return BatchCase(shape, w, pool, requests, cases, np.concatenate(xs, axis=0), dtype)
+
+
+def quantize_case(case, bits):
+    """The case's chunk caches stored as per-channel codes by the oracle's
+    encoder.  Returns (codes, decoded case): codes per chunk as (K codes
+    [L][n][C*bits/8] uint8, V codes, qparams [L][4][C] float32 = k scale,
+    k zero, v scale, v zero), and a Case whose chunks are the oracle's
+    decoded values (the oracle's input for the same fusion)."""
+    s = case.shape
+    codes, decoded = [], []
+    for k, v in case.chunks:
+        kc, ks, kz = oracle.quantize_channels(k, bits)
+        vc, vs, vz = oracle.quantize_channels(v, bits)
+        qp = np.stack([ks, kz, vs, vz], axis=1).astype(np.float32)
+        codes.append((oracle.pack_codes(kc, bits), oracle.pack_codes(vc, bits), qp))
+        decoded.append((oracle.dequantize_channels(kc, ks, kz, s.n_kv_heads, s.head_dim),
+                        oracle.dequantize_channels(vc, vs, vz, s.n_kv_heads, s.head_dim)))
+    return codes, dataclasses.replace(case, chunks=decoded)

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(npk):
 
 
 def test_abi_version(npk):
-    assert npk.cb_abi_version() == npk.CB_ABI_VERSION == 1
+    assert npk.cb_abi_version() == npk.CB_ABI_VERSION == 2
 
 
 @pytest.mark.parametrize("n", [0, 1, 10, 384, 3840, 7680, 8192])
@@ -91,6 +91,27 @@ def test_kernel_entry_validation(npk):
                                  None) == npk.CB_E_SHAPE
     assert R["cb_deviation"](npk.CB_F32, 16, 16, 16, 16, 4, 64, 3, 16, None) == npk.CB_E_INVALID
     assert R["cb_gather_rows"](16, 16, 16, 4, 6, None) == npk.CB_E_SHAPE
+    # quantized chunk entries: bit widths, formats, row sizes, alignment
+    assert R["cb_quantize_kv"](npk.CB_BF16, 16, 2, 8, 64, 512, 6, 16, 16, 16, 256,
+                               None) == npk.CB_E_INVALID
+    assert R["cb_quantize_kv"](npk.CB_BF16, 16, 2, 8, 60, 480, 8, 16, 16, 16, 240,
+                               None) == npk.CB_E_SHAPE
+    assert R["cb_quantize_kv"](npk.CB_BF16, 16, 2, 8, 64, 100, 8, 16, 16, 16, 256,
+                               None) == npk.CB_E_SHAPE
+    assert R["cb_quantize_kv"](npk.CB_BF16, 8, 2, 8, 64, 512, 8, 16, 16, 16, 256,
+                               None) == npk.CB_E_SHAPE
+    assert R["cb_quantize_kv"](npk.CB_BF16, None, 2, 8, 64, 512, 4, 16, 16, 16, 256,
+                               None) == npk.CB_E_INVALID
+    assert R["cb_quantize_kv"](npk.CB_BF16, None, 0, 8, 64, 512, 4, None, None, None, 256,
+                               None) == npk.CB_OK
+    assert R["cb_dequant_rerotate"](npk.CB_BF16, npk.CB_KV_PLAIN, 16, 16, 16, 16, 16, 4, 2, 64, 3,
+                                    1e4, None) == npk.CB_E_INVALID
+    assert R["cb_dequant_rerotate"](npk.CB_BF16, npk.CB_KV_U8, 16, 16, None, 16, 16, 4, 2, 64, 3,
+                                    1e4, None) == npk.CB_E_INVALID
+    assert R["cb_dequant_rerotate"](npk.CB_BF16, npk.CB_KV_U4, 16, 16, 16, 16, 16, 4, 2, 60, 3,
+                                    1e4, None) == npk.CB_E_SHAPE
+    assert R["cb_dequant_rerotate"](npk.CB_BF16, npk.CB_KV_U8, 24, 16, 16, 16, 16, 4, 2, 64, 3,
+                                    1e4, None) == npk.CB_E_SHAPE
     assert R["cb_rmsnorm"](npk.CB_F32, None, npk.CB_F32, None, None, 3, 8, 1e-5,
                            None) == npk.CB_E_INVALID
     # NULL handles are rejected, never dereferenced
@@ -99,6 +120,25 @@ def test_kernel_entry_validation(npk):
     assert R["cb_synchronize"](None) == npk.CB_E_INVALID
     R["cb_plan_destroy"](None)
     R["cb_model_destroy"](None)
+
+
+def test_chunk_descriptor_layout(npk, tmp_path):
+    """The ctypes mirrors of the request structs have the C layout that a C
+    compiler gives the header."""
+    import subprocess
+    src = tmp_path / "layout.c"
+    src.write_text('#include <stdio.h>\n#include <stddef.h>\n#include "cacheblend.h"\n'
+                   'int main(void) { printf("%zu %zu %zu %zu %zu\\n", sizeof(cb_chunk_kv), '
+                   'offsetof(cb_chunk_kv, kv_format), offsetof(cb_chunk_kv, qparams), '
+                   'sizeof(cb_request), sizeof(cb_batch_request)); return 0; }\n')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)],
+                   check=True)
+    got = [int(x) for x in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    assert got == [ctypes.sizeof(npk.cb_chunk_kv), npk.cb_chunk_kv.kv_format.offset,
+                   npk.cb_chunk_kv.qparams.offset, ctypes.sizeof(npk.cb_request),
+                   ctypes.sizeof(npk.cb_batch_request)]
 
 
 def test_binding_has_no_fallback():
