@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--r-bp", type=int, default=None)
     ap.add_argument("--schedule", default=None, choices=[None, "gradual", "fixed"])
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--kv-format", default="plain", choices=["plain", "u8", "u4"],
+                    help="storage of the chunk caches: model dtype, or per-channel 8/4-bit "
+                         "codes made by cb_quantize_kv after the precompute")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--no-full-compare", action="store_true")
@@ -167,7 +170,10 @@ def make_model(npk, S, seed, torch):
     return model, layers, emb
 
 
-def make_inputs(npk, w, seed, torch):
+BITS = {"plain": None, "u8": 8, "u4": 4}
+
+
+def make_inputs(npk, w, seed, torch, kv_format="plain"):
     """Uniform random tokens, embedding rows as layer-0 input, chunk caches
     precomputed alone with cb_prefill at chunk-local positions."""
     from workloads import make_tokens
@@ -183,16 +189,23 @@ def make_inputs(npk, w, seed, torch):
         k = torch.empty((S.n_layers, n, S.n_kv_heads, S.head_dim), dtype=bf, device=dev)
         v = torch.empty_like(k)
         npk.cb_prefill(model, x0[o:o + n], n, 0, k, v)
+        if BITS[kv_format]:
+            c = npk.quantize_chunk(k, v, BITS[kv_format])
+            del k, v
+        else:
+            c = {"k": k, "v": v, "n_tokens": n, "layer_stride": n * S.kv_dim}
         if w.kv_on_host:
             torch.cuda.synchronize()
-            k, v = k.cpu().pin_memory(), v.cpu().pin_memory()
-        chunks.append({"k": k, "v": v, "n_tokens": n, "on_host": int(w.kv_on_host),
-                       "layer_stride": n * S.kv_dim})
+            for key in ("k", "v", "qparams"):
+                if key in c:
+                    c[key] = c[key].cpu().pin_memory()
+        c["on_host"] = int(w.kv_on_host)
+        chunks.append(c)
     torch.cuda.synchronize()
     return model, layers, x0, chunks
 
 
-def make_batch_inputs(npk, w, seed, torch, pool_on_host):
+def make_batch_inputs(npk, w, seed, torch, pool_on_host, kv_format="plain"):
     """Batched serving slice: a chunk pool with Zipf reuse (see
     workloads.make_batched_requests).  Every pool chunk a request uses is
     precomputed alone with cb_prefill and stored once, all chunks of a layer
@@ -213,25 +226,38 @@ def make_batch_inputs(npk, w, seed, torch, pool_on_host):
         row[i] = U
         U += int(pool_lens[i])
     where = dict(device="cpu", pin_memory=True) if pool_on_host else dict(device=dev)
-    pk = torch.empty((L, U, kvd), dtype=bf, **where)
-    pv = torch.empty((L, U, kvd), dtype=bf, **where)
-    for i in used:
+    bits = BITS[kv_format]
+    width = kvd if not bits else kvd * bits // 8         # elements (codes: bytes) per row
+    edt = bf if not bits else torch.uint8
+    pk = torch.empty((L, U, width), dtype=edt, **where)
+    pv = torch.empty((L, U, width), dtype=edt, **where)
+    pq = torch.empty((len(used), L, 4, kvd), dtype=torch.float32, **where) if bits else None
+    for j, i in enumerate(used):
         n, o = int(pool_lens[i]), row[i]
         x = emb[torch.from_numpy(pool_tok[i]).to(dev)].contiguous()
-        k = torch.empty((L, n, kvd), dtype=bf, device=dev)
+        k = torch.empty((L, n, S.n_kv_heads, S.head_dim), dtype=bf, device=dev)
         v = torch.empty_like(k)
         npk.cb_prefill(model, x, n, 0, k, v)
+        if bits:
+            q = npk.quantize_chunk(k, v, bits)
+            k, v = q["k"], q["v"]
+            pq[j].copy_(q["qparams"])
         for l in range(L):
-            pk[l, o:o + n].copy_(k[l])
-            pv[l, o:o + n].copy_(v[l])
+            pk[l, o:o + n].copy_(k[l].reshape(n, width))
+            pv[l, o:o + n].copy_(v[l].reshape(n, width))
     torch.cuda.synchronize()
     pool = []
+    esz = 1 if bits else 2
     for i in range(len(pool_lens)):
         if i in row:
-            off = row[i] * kvd * 2
-            pool.append({"k": pk.data_ptr() + off, "v": pv.data_ptr() + off,
-                         "n_tokens": int(pool_lens[i]), "on_host": int(pool_on_host),
-                         "layer_stride": U * kvd})
+            off = row[i] * width * esz
+            e = {"k": pk.data_ptr() + off, "v": pv.data_ptr() + off,
+                 "n_tokens": int(pool_lens[i]), "on_host": int(pool_on_host),
+                 "layer_stride": U * kvd}
+            if bits:
+                e["kv_format"] = npk.CB_KV_U8 if bits == 8 else npk.CB_KV_U4
+                e["qparams"] = pq.data_ptr() + used.index(i) * L * 4 * kvd * 4
+            pool.append(e)
         else:   # never referenced, never read
             pool.append({"k": 0, "v": 0, "n_tokens": 1, "on_host": 0, "layer_stride": kvd})
     toks = np.concatenate([np.concatenate([pool_tok[i] for i in r["chunk_ids"]] + [t])
@@ -240,7 +266,7 @@ def make_batch_inputs(npk, w, seed, torch, pool_on_host):
     del emb
     info = {"pool_lens": pool_lens, "requests": reqs, "unique_chunks": len(used),
             "unique_tokens": U}
-    return model, layers, x0, pool, (pk, pv), info
+    return model, layers, x0, pool, (pk, pv, pq), info
 
 
 # ------------------------------------------------------------------ HBM traffic
@@ -402,7 +428,8 @@ def main_batched(args, npk, torch, w):
     S = w.shape
     L = S.n_layers
     log(f"[bench] workload {w.name}: building inputs (pool in pinned host memory)")
-    model, layers, x0, pool, pool_bufs, info = make_batch_inputs(npk, w, args.seed, torch, True)
+    model, layers, x0, pool, pool_bufs, info = make_batch_inputs(npk, w, args.seed, torch, True,
+                                                                 args.kv_format)
     reqs = info["requests"]
     lens = [sum(int(info["pool_lens"][i]) for i in r["chunk_ids"]) for r in reqs]
     Ntot = sum(lens) + sum(r["n_suffix"] for r in reqs)
@@ -430,7 +457,10 @@ def main_batched(args, npk, torch, w):
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) / args.steps * 1e3
-    h2d_bytes = 2 * L * info["unique_tokens"] * S.kv_dim * 2
+    bits = BITS[args.kv_format]
+    h2d_bytes = 2 * L * info["unique_tokens"] * S.kv_dim * (bits / 8 if bits else 2)
+    if bits:
+        h2d_bytes += info["unique_chunks"] * L * 4 * S.kv_dim * 4
     out = {"metric": "effective prompt tok/s of a batch of requests at r=15%, Llama-7B shape",
            "value": Ntot / (ms / 1e3), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": ms, "ms_per_layer": ms / L,
@@ -442,7 +472,7 @@ def main_batched(args, npk, torch, w):
                       "unique_chunks_used": info["unique_chunks"],
                       "unique_chunk_tokens": info["unique_tokens"], "recompute_bp": w.r_bp,
                       "schedule": w.schedule_kind, "pool": "pinned host",
-                      "h2d_bytes_per_step": h2d_bytes},
+                      "chunk_kv_format": args.kv_format, "h2d_bytes_per_step": h2d_bytes},
            "h2d_gbs_effective": h2d_bytes / (ms / 1e3) / 1e9}
 
     if not args.no_profile:
@@ -469,13 +499,16 @@ def main_batched(args, npk, torch, w):
 
     if not args.no_full_compare:
         log("[bench] same batch with the pool resident in HBM")
-        pk_, pv_ = pool_bufs
+        pk_, pv_, pq_ = pool_bufs
         dk, dv = pk_.to(dev), pv_.to(dev)
+        dq = pq_.to(dev) if pq_ is not None else None
         dpool = []
         for e in pool:
             if e["k"]:
                 e = dict(e, k=dk.data_ptr() + (e["k"] - pk_.data_ptr()),
                          v=dv.data_ptr() + (e["v"] - pv_.data_ptr()), on_host=0)
+                if dq is not None:
+                    e["qparams"] = dq.data_ptr() + (e["qparams"] - pq_.data_ptr())
             dpool.append(e)
         step(dpool)
         torch.cuda.synchronize()
@@ -487,7 +520,7 @@ def main_batched(args, npk, torch, w):
         msr = (time.perf_counter() - tr0) / nr * 1e3
         out["hbm_pool_ms_per_step"] = msr
         out["hbm_pool_tok_s"] = Ntot / (msr / 1e3)
-        del dk, dv
+        del dk, dv, dq
 
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle sample")
@@ -531,7 +564,7 @@ def main():
     S = w.shape
     N, Nc, L = w.n_tokens, w.n_chunk_tokens, S.n_layers
     log(f"[bench] workload {w.name}: building inputs")
-    model, layers, x0, chunks = make_inputs(npk, w, args.seed, torch)
+    model, layers, x0, chunks = make_inputs(npk, w, args.seed, torch, args.kv_format)
     kind = npk.CB_SCHED_GRADUAL if w.schedule_kind == "gradual" else npk.CB_SCHED_FIXED
     sched = npk.cb_schedule(Nc, w.r_bp, kind, L)
     dev = torch.device("cuda:0")
@@ -568,7 +601,7 @@ def main():
                       "chunks": f"{len(w.chunk_lens)}x{w.chunk_lens[0]}",
                       "suffix_tokens": w.n_suffix, "recompute_bp": w.r_bp,
                       "schedule": w.schedule_kind, "kept_rows_per_layer": sched,
-                      "chunk_kv_on_host": w.kv_on_host}}
+                      "chunk_kv_on_host": w.kv_on_host, "chunk_kv_format": args.kv_format}}
 
     # per-kernel-class durations (HIP events around each launch, own pass)
     if not args.no_profile:
@@ -591,7 +624,8 @@ def main():
         st["attention"]["flops"] = 4.0 * S.n_q_heads * S.head_dim * att_terms * pk
         kernels = kernel_breakdown(st, pk)
         out["kernels"] = kernels
-        out["roofline"] = roofline(st, kernels, lambda k: recorded_traffic(k, args.workload))
+        out["roofline"] = roofline(st, kernels, lambda k: recorded_traffic(k, args.workload)
+                                   if args.kv_format == "plain" else None)
 
     if not args.no_full_compare:
         log("[bench] full recompute (r = 100%) comparison")
