@@ -16,7 +16,8 @@ Pages followed (cited by page title and section):
         "HKVD（High KV Deviation）トークン選定" (gradual filtering and the
         top-k selection code), "RoPE（Rotary Position Embedding）との整合性"
         (rotation matrix R(m), theta_i), "設定パラメータ" (check layer,
-        ratio, min tokens).
+        ratio, min tokens), "パイプライン実行とロードコントローラ" (load
+        and recompute delays, the optimal ratio r*).
   [CB2] "CacheBlend: Fast Large Language Model Serving for RAG with Cached
         Knowledge Fusion" explainer (abeam.tech): sections "チャンク単位でKVを
         保存する" (positions corrected to the real input positions) and
@@ -24,6 +25,9 @@ Pages followed (cited by page title and section):
         only; selected tokens attend over the whole input).
   [PC]  "論文解説: Prompt Cache — モジュラーAttention再利用による低レイテンシ推論"
         (0h-n0.github.io): section "RoPEにおける位置調整" (k(p) = R(p-p')k(p')).
+  [CA]  "論文解説: CachedAttention — マルチターン会話のKVキャッシュ階層管理によるコスト50%削減"
+        (0h-n0.github.io):
+        "エビクションポリシー" (LRU from GPU HBM to CPU DRAM).
   [CG]  "論文解説: CacheGen — KVキャッシュ圧縮とストリーミングで長文コンテキストの
         LLM推論を高速化" (0h-n0.github.io): "技術的詳細", step 1 "チャネル別
         量子化" (per-channel scale and zero point) and "圧縮率と品質のトレード
@@ -394,6 +398,67 @@ def unpack_codes(packed, bits: int) -> np.ndarray:
     out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.uint8)
     out[..., 0::2] = packed & 15
     out[..., 1::2] = packed >> 4
+    return out
+
+
+# --------------------------------------------------------------------------
+# Load controller  [CB1 "パイプライン実行とロードコントローラ": T_recompute =
+# r T_prefill; T_load = PerTokenKVSize * L / Throughput(D) with L the input
+# tokens; r* = max(r_min, T_load / T_prefill)]
+# --------------------------------------------------------------------------
+def load_time(per_token_kv_bytes, n_tokens, throughput_bytes_per_s):
+    """T_load in seconds."""
+    return per_token_kv_bytes * n_tokens / throughput_bytes_per_s
+
+
+def controller_ratio(t_prefill_s, per_token_kv_bytes, n_tokens, throughput_bytes_per_s,
+                     r_min_bp):
+    """r* in basis points: max(r_min, T_load / T_prefill), the ratio taken to
+    the nearest basis point (halves up) and capped at 10000 (where the load
+    takes longer than a full prefill, recomputing everything is quicker)."""
+    t_load = load_time(per_token_kv_bytes, n_tokens, throughput_bytes_per_s)
+    ratio = t_load / t_prefill_s
+    bp = math.floor(ratio * 10000.0 + 0.5)
+    return int(min(10000, max(r_min_bp, bp)))
+
+
+# --------------------------------------------------------------------------
+# HBM tier of the chunk store  [CA "エビクションポリシー": least recently used
+# entries leave GPU HBM when it is full; PC "キャッシュヒット率とエビクション":
+# hit rate H = sum_i p_i * [module i in cache], LRU eviction]
+# --------------------------------------------------------------------------
+def lru_replay(capacity_bytes, batches):
+    """Replays batches of chunk uses against an LRU store of a byte budget.
+
+    batches: list of batches, each a list of (key, bytes) uses in prompt
+    order.  Per batch: every use is looked up first (a hit refreshes the
+    entry to most recent); then, in order, every use whose key is not
+    resident is inserted as most recent, evicting least recently used
+    entries until it fits (an entry larger than the budget is not
+    inserted).  Returns per batch the list of hit flags and the keys
+    evicted, in eviction order."""
+    from collections import OrderedDict
+    store = OrderedDict()          # key -> bytes; last = most recent
+    used = 0
+    out = []
+    for batch in batches:
+        hits = []
+        for key, _ in batch:
+            hit = key in store
+            if hit:
+                store.move_to_end(key)
+            hits.append(hit)
+        evicted = []
+        for key, size in batch:
+            if key in store or size > capacity_bytes:
+                continue
+            while used + size > capacity_bytes:
+                old, osz = store.popitem(last=False)
+                used -= osz
+                evicted.append(old)
+            store[key] = size
+            used += size
+        out.append((hits, evicted))
     return out
 
 

@@ -436,3 +436,87 @@ def test_code_bytes_vs_printed_ratio(bits, ratio):
     codes = np.zeros((L, n, H * dh), dtype=np.uint8)
     fp16_bytes = oracle.kv_size_bytes(L, H, dh, n, 2) // 2      # K alone
     assert fp16_bytes / oracle.pack_codes(codes, bits).nbytes == ratio
+
+
+# ------------------------------------------------------------ load controller
+# CacheBlend explainer, "パイプライン実行とロードコントローラ".
+
+def test_controller_worked_example_golden():
+    for line in open(os.path.join(GOLDEN, "load_controller_example.txt")):
+        if line.startswith("#") or not line.strip():
+            continue
+        rec_ms, r, load_ms, tok_bytes, n, r_min, want = line.split()
+        t_prefill = float(rec_ms) / 1e3 / float(r)
+        thr = int(tok_bytes) * int(n) / (float(load_ms) / 1e3)
+        assert oracle.load_time(int(tok_bytes), int(n), thr) == pytest.approx(float(load_ms) / 1e3)
+        assert oracle.controller_ratio(t_prefill, int(tok_bytes), int(n), thr,
+                                       int(r_min)) == int(want)
+
+
+def test_load_time_vs_printed_transfer():
+    """CachedAttention explainer, cost analysis: about 10.5 GB of 70B KV for
+    4000 tokens takes about 330 ms over 32 GB/s."""
+    per_token = oracle.kv_size_bytes(80, 64, 128, 1, 2)
+    assert oracle.load_time(per_token, 4000, 32e9) == pytest.approx(0.33, abs=0.01)
+
+
+def test_controller_properties():
+    rng = np.random.default_rng(31)
+    for _ in range(200):
+        tp = float(rng.uniform(1e-3, 1.0))
+        thr = float(rng.uniform(1e9, 64e9))
+        tok = int(rng.integers(1024, 1 << 16))
+        n = int(rng.integers(1, 1 << 17))
+        rmin = int(rng.integers(0, 10001))
+        r = oracle.controller_ratio(tp, tok, n, thr, rmin)
+        tl = oracle.load_time(tok, n, thr)
+        assert rmin <= r <= 10000 or (r == 10000 and rmin <= 10000)
+        if r < 10000:
+            # the chosen recompute time covers the load to within half a basis point
+            assert r / 10000 * tp >= tl - 0.5e-4 * tp
+            assert r == rmin or abs(r / 10000 - tl / tp) <= 0.5e-4 + 1e-12
+        else:
+            assert tl >= 0.99995 * tp or rmin == 10000
+    # load hidden under r_min: r_min wins; instant storage: r_min
+    assert oracle.controller_ratio(1.0, 1, 1, 1e12, 1500) == 1500
+    # load slower than a full prefill: recompute everything
+    assert oracle.controller_ratio(0.001, 1 << 20, 1 << 20, 1e9, 1500) == 10000
+
+
+# ------------------------------------------------------------ LRU chunk tier
+# CachedAttention explainer, "エビクションポリシー"; Prompt Cache explainer,
+# "キャッシュヒット率とエビクション".
+
+def test_lru_replay_hand_example():
+    """Budget 3 units, unit-size entries.  Batch [1,2,3]: all miss, stored.
+    Batch [1,4]: 1 hits (now most recent: order 2,3,1), 4 evicts 2.
+    Batch [2,3]: 2 misses, 3 hits (order 1,4,3); 2 evicts 1.
+    Batch [1,4,1]: 1 misses twice in the lookup, 4 hits (order 3,2,4);
+    inserting 1 evicts 3, the repeated 1 is already resident."""
+    b = lambda *ks: [(k, 1) for k in ks]
+    out = oracle.lru_replay(3, [b(1, 2, 3), b(1, 4), b(2, 3), b(1, 4, 1)])
+    assert out == [([False] * 3, []), ([True, False], [2]), ([False, True], [1]),
+                   ([False, True, False], [3])]
+
+
+def test_lru_replay_sizes_and_oversize():
+    """Byte budgets: a large entry evicts several least-recent ones; an
+    entry above the budget is never stored and evicts nothing."""
+    out = oracle.lru_replay(10, [[("a", 4), ("b", 3), ("c", 3)], [("d", 6)], [("e", 11)],
+                                 [("c", 3), ("b", 3)]])
+    assert out[1] == ([False], ["a", "b"])
+    assert out[2] == ([False], [])
+    assert out[3] == ([True, False], ["d"])       # c was refreshed by its hit
+
+
+def test_lru_hit_rate_matches_brute_force():
+    """With a budget holding every key, the hit flags are 'seen before in an
+    earlier batch' exactly; with budget 0 nothing ever hits."""
+    rng = np.random.default_rng(32)
+    batches = [[(int(k), 5) for k in rng.integers(0, 20, size=8)] for _ in range(12)]
+    out = oracle.lru_replay(10 ** 9, batches)
+    seen = set()
+    for batch, (hits, ev) in zip(batches, out):
+        assert hits == [k in seen for k, _ in batch] and ev == []
+        seen |= {k for k, _ in batch}
+    assert all(not any(h) for h, _ in oracle.lru_replay(0, batches))
