@@ -283,6 +283,80 @@ typedef struct cb_batch_outputs {
 cb_status cb_blend_batch(cb_model* model, const cb_batch_request* req,
                          const cb_batch_outputs* out, void* stream);
 
+/* ------------------------------------------------------------- chunk store
+ * Load controller (CacheBlend explainer (0h-n0), "パイプライン実行とロード
+ * コントローラ"): recomputing a fraction r of the prompt costs r T_prefill,
+ * loading the chunk caches costs T_load = per_token_kv_bytes * n_tokens /
+ * throughput, and layer-wise pipelining hides the load when r T_prefill >=
+ * T_load; the controller picks r* = max(r_min, T_load / T_prefill).
+ * *r_bp_out = r* in basis points: the ratio to the nearest basis point
+ * (halves up), at least r_min_bp, at most 10000.  Times in seconds, bytes
+ * and throughput (bytes/s) positive and finite; host only. */
+cb_status cb_controller_ratio(double t_prefill_s, double per_token_kv_bytes, int64_t n_tokens,
+                              double throughput_bytes_per_s, int32_t r_min_bp,
+                              int32_t* r_bp_out);
+
+/* HBM tier in front of chunk caches held in pinned host memory
+ * (CachedAttention explainer (0h-n0), "エビクションポリシー"; Prompt Cache
+ * explainer (0h-n0), "キャッシュヒット率とエビクション"): whole chunk caches
+ * are kept in device memory up to a byte budget; the least recently used
+ * leave first.
+ *
+ * Protocol, all on one caller stream: cb_cache_resolve for the chunk uses
+ * of a request or batch, the fusion with the resolved descriptors, then
+ * cb_cache_admit with the same uses.  A key names one chunk cache (content,
+ * length and format) for the life of the tier, e.g. a hash of its text. */
+typedef struct cb_chunk_cache cb_chunk_cache;
+
+typedef struct cb_cache_stat {
+    int64_t lookups;            /* host chunk uses looked up                 */
+    int64_t hits;               /* of which served from HBM                  */
+    int64_t admitted;           /* entries copied in                         */
+    int64_t evicted;            /* entries released                          */
+    int64_t resident_entries;
+    int64_t resident_bytes;     /* device bytes held by entries              */
+    int64_t copied_bytes;       /* host -> device bytes of admissions        */
+} cb_cache_stat;
+
+/* A tier on the current device for chunks of n_layers layers of row =
+ * H_kv*d_head elements in dtype (quantized chunks are stored as codes plus
+ * parameters); capacity_bytes of device memory for entries (0: nothing is
+ * ever kept).  The tier owns a stream (default priority) and a memory pool. */
+cb_status cb_cache_create(int32_t n_layers, int32_t row, int32_t dtype, int64_t capacity_bytes,
+                          cb_chunk_cache** out);
+/* Waits for all work on the device, then releases every entry. */
+void cb_cache_destroy(cb_chunk_cache* cache);
+/* For each of n uses (keys and chunks host [n]): a pinned-host chunk whose
+ * key is resident is replaced in out (host [n]) by the descriptor of its HBM
+ * copy and becomes the most recently used (a hit); every other chunk is
+ * copied to out unchanged.  hits (host [n] or NULL): 1 for a hit.  `stream`
+ * waits for earlier admissions.  A resolved device descriptor stays valid
+ * for work queued on `stream` before the next cb_cache_admit. */
+cb_status cb_cache_resolve(cb_chunk_cache* cache, int32_t n, const uint64_t* keys,
+                           const cb_chunk_kv* chunks, cb_chunk_kv* out, int32_t* hits,
+                           void* stream);
+/* Call after queuing the fusion that reads the resolved descriptors.  In
+ * order, every pinned-host use whose key is not resident is copied into HBM
+ * as the most recently used entry, releasing least recently used entries
+ * until it fits (a chunk above the budget is skipped).  Copies and releases
+ * run on the tier's stream after everything queued on `stream` so far.
+ * Chunks must be pinned and stay valid until the copies are done (the next
+ * cb_cache_resolve makes its stream wait for them; or synchronize the
+ * device).  CB_E_OOM if the device has no memory for an entry (entries
+ * admitted before it stay). */
+cb_status cb_cache_admit(cb_chunk_cache* cache, int32_t n, const uint64_t* keys,
+                         const cb_chunk_kv* chunks, void* stream);
+cb_status cb_cache_stats(cb_chunk_cache* cache, cb_cache_stat* out);
+/* Host-only replay of the tier's policy on batches of uses (batch b has
+ * batch_sizes[b] consecutive entries of keys / sizes in bytes), each batch
+ * looked up then admitted as above: hits_out [total uses] gets 1 for a hit;
+ * evicted_per_batch [n_batches] the number of entries released after each
+ * batch, and evicted_out (NULL, or room for one key per use) their keys in
+ * release order.  For tests and capacity planning. */
+cb_status cb_cache_replay(int64_t capacity_bytes, int32_t n_batches, const int32_t* batch_sizes,
+                          const uint64_t* keys, const int64_t* sizes, int32_t* hits_out,
+                          uint64_t* evicted_out, int32_t* evicted_per_batch);
+
 /* ------------------------------------------------------------- timing
  * Per-kernel-class timing of the fusion path with HIP events recorded on the
  * stream each kernel runs on (the caller's stream, or the side stream for

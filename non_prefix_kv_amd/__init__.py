@@ -83,6 +83,11 @@ class cb_kernel_stat(ctypes.Structure):
                 ("bytes", ctypes.c_double)]
 
 
+class cb_cache_stat(ctypes.Structure):
+    _fields_ = [(n, _c_i64) for n in ("lookups", "hits", "admitted", "evicted",
+                                       "resident_entries", "resident_bytes", "copied_bytes")]
+
+
 KERNEL_CLASSES = ("rotate", "rmsnorm", "gemm_qkv", "deviation", "select", "scatter",
                   "attention", "gemm_o", "gemm_gateup", "gemm_down")
 
@@ -109,6 +114,16 @@ _fn = {
     "cb_plan_destroy": (None, _c_p),
     "cb_blend_batch": (ctypes.c_int, _c_p, _P(cb_batch_request), _P(cb_batch_outputs), _c_p),
     "cb_prefill": (ctypes.c_int, _c_p, _c_p, _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p),
+    "cb_controller_ratio": (ctypes.c_int, ctypes.c_double, ctypes.c_double, _c_i64,
+                            ctypes.c_double, _c_i32, _P(_c_i32)),
+    "cb_cache_create": (ctypes.c_int, _c_i32, _c_i32, _c_i32, _c_i64, _P(_c_p)),
+    "cb_cache_destroy": (None, _c_p),
+    "cb_cache_resolve": (ctypes.c_int, _c_p, _c_i32, _P(ctypes.c_uint64), _P(cb_chunk_kv),
+                         _P(cb_chunk_kv), _P(_c_i32), _c_p),
+    "cb_cache_admit": (ctypes.c_int, _c_p, _c_i32, _P(ctypes.c_uint64), _P(cb_chunk_kv), _c_p),
+    "cb_cache_stats": (ctypes.c_int, _c_p, _P(cb_cache_stat)),
+    "cb_cache_replay": (ctypes.c_int, _c_i64, _c_i32, _P(_c_i32), _P(ctypes.c_uint64),
+                        _P(_c_i64), _P(_c_i32), _P(ctypes.c_uint64), _P(_c_i32)),
     "cb_profile_enable": (ctypes.c_int, _c_p, _c_i32),
     "cb_profile_read": (ctypes.c_int, _c_p, _P(cb_kernel_stat)),
     "cb_rope_rerotate": (ctypes.c_int, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
@@ -228,6 +243,8 @@ def _chunk_array(chunks):
     """chunks: list of dicts {k, v, n_tokens, on_host, layer_stride} with
     tensors or ints, plus kv_format (CB_KV_U8 / CB_KV_U4) and qparams for
     quantized chunks."""
+    if isinstance(chunks, ctypes.Array):
+        return chunks
     arr = (cb_chunk_kv * max(1, len(chunks)))()
     for i, c in enumerate(chunks):
         arr[i].k = _ptr(c["k"])
@@ -341,6 +358,78 @@ class Plan:
 def cb_prefill(model, x0, n_tokens, pos0, k_out, v_out, hidden_out=None, stream=None):
     _check(RAW["cb_prefill"](model.handle, _ptr(x0), n_tokens, pos0, _ptr(k_out), _ptr(v_out),
                              _ptr(hidden_out), _stream(stream)))
+
+
+# ------------------------------------------------------------------ chunk store
+def cb_controller_ratio(t_prefill_s, per_token_kv_bytes, n_tokens, throughput_bytes_per_s,
+                        r_min_bp=1500):
+    """r* = max(r_min, T_load / T_prefill) in basis points."""
+    out = _c_i32()
+    _check(RAW["cb_controller_ratio"](t_prefill_s, per_token_kv_bytes, n_tokens,
+                                      throughput_bytes_per_s, r_min_bp, ctypes.byref(out)))
+    return out.value
+
+
+def cb_cache_replay(capacity_bytes, batches):
+    """batches: list of lists of (key, bytes).  Returns [(hit flags, evicted
+    keys)] per batch, as the tier's policy decides them."""
+    sizes = [len(b) for b in batches]
+    total = sum(sizes)
+    keys = (ctypes.c_uint64 * max(1, total))(*[k for b in batches for k, _ in b])
+    nbytes = (_c_i64 * max(1, total))(*[n for b in batches for _, n in b])
+    hits = (_c_i32 * max(1, total))()
+    ev = (ctypes.c_uint64 * max(1, total))()
+    per = (_c_i32 * max(1, len(batches)))()
+    bs = (_c_i32 * max(1, len(batches)))(*sizes)
+    _check(RAW["cb_cache_replay"](capacity_bytes, len(batches), bs, keys, nbytes, hits, ev, per))
+    out, at, e = [], 0, 0
+    for b, n in enumerate(sizes):
+        out.append(([bool(hits[at + i]) for i in range(n)], [ev[e + j] for j in range(per[b])]))
+        at += n
+        e += per[b]
+    return out
+
+
+class ChunkCache:
+    """cb_chunk_cache: HBM tier for pinned-host chunk caches."""
+
+    def __init__(self, n_layers, row, dtype, capacity_bytes):
+        h = _c_p()
+        _check(RAW["cb_cache_create"](n_layers, row, dtype, int(capacity_bytes), ctypes.byref(h)))
+        self.handle = h
+
+    def resolve(self, keys, chunks, stream=None):
+        """Returns (resolved chunk array, hit flags) for cb_blend /
+        cb_blend_batch (the array replaces the chunk dicts)."""
+        n = len(chunks)
+        arr = _chunk_array(chunks)
+        out = (cb_chunk_kv * max(1, n))()
+        hits = (_c_i32 * max(1, n))()
+        ka = (ctypes.c_uint64 * max(1, n))(*keys)
+        _check(RAW["cb_cache_resolve"](self.handle, n, ka, arr, out, hits, _stream(stream)))
+        return out, [bool(hits[i]) for i in range(n)]
+
+    def admit(self, keys, chunks, stream=None):
+        n = len(chunks)
+        arr = _chunk_array(chunks)
+        ka = (ctypes.c_uint64 * max(1, n))(*keys)
+        _check(RAW["cb_cache_admit"](self.handle, n, ka, arr, _stream(stream)))
+
+    def stats(self):
+        st = cb_cache_stat()
+        _check(RAW["cb_cache_stats"](self.handle, ctypes.byref(st)))
+        return {n: getattr(st, n) for n, _ in cb_cache_stat._fields_}
+
+    def close(self):
+        if getattr(self, "handle", None):
+            RAW["cb_cache_destroy"](self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def cb_profile_enable(model, enable=True):

@@ -25,6 +25,7 @@
 #include <vector>
 
 #include "../../include/cacheblend.h"
+#include "host.h"
 #include "kernels.h"
 
 using namespace cb;
@@ -34,13 +35,18 @@ namespace {
 
 thread_local std::string g_err;
 
-cb_status fail(cb_status st, const char* fmt, ...) {
+cb_status vfail(cb_status st, const char* fmt, va_list ap) {
     char buf[512];
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    g_err = buf;
+    return st;
+}
+
+cb_status fail(cb_status st, const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
-    vsnprintf(buf, sizeof buf, fmt, ap);
+    vfail(st, fmt, ap);
     va_end(ap);
-    g_err = buf;
     return st;
 }
 
@@ -137,7 +143,20 @@ cb_status make_schedule(int n, int r_bp, int kind, int L, int* s) {
 
 bool aligned_to(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-enum class MemKind { Device, Pinned, Other };
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+namespace cb {
+
+cb_status set_error(cb_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vfail(st, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
 MemKind mem_kind(const void* p) {
     hipPointerAttribute_t at;
     memset(&at, 0, sizeof at);
@@ -150,9 +169,7 @@ MemKind mem_kind(const void* p) {
     return MemKind::Other;
 }
 
-size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
-}  // namespace
+}  // namespace cb
 
 // ---------------------------------------------------------------- model
 struct cb_model {

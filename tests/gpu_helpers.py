@@ -105,14 +105,15 @@ def pool_inputs(bcase, dt, on_host=False):
 
 def run_gpu_batch(npk, model, bcase, dt, schedules=None, recompute_bp=1500,
                   schedule_kind=0, dev_mode=0, on_host=False, dev_fill=float("nan"),
-                  override=None):
+                  override=None, pool=None):
     """cb_blend_batch over the whole batch; returns the stacked outputs split
     per request (views) plus the raw stacked tensors.  override: {pool index:
-    chunk descriptor} replacing the plain pool entries (e.g. quantized)."""
+    chunk descriptor} replacing the plain pool entries (e.g. quantized);
+    pool: the whole pool (chunk dicts or a resolved descriptor array)."""
     s = bcase.shape
     L = s.n_layers
     tdt = TORCH_DT[dt]
-    pool = pool_inputs(bcase, dt, on_host)
+    pool = pool_inputs(bcase, dt, on_host) if pool is None else pool
     for i, c in (override or {}).items():
         pool[i] = c
     reqs = []

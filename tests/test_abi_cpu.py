@@ -146,3 +146,72 @@ def test_binding_has_no_fallback():
     src = open(os.path.join(ROOT, "non_prefix_kv_amd", "__init__.py")).read()
     assert "raise ImportError" in src
     assert "oracle" not in src
+
+
+# ------------------------------------------------------------ chunk store (host logic)
+def test_controller_matches_oracle(npk):
+    import numpy as np
+    rng = np.random.default_rng(41)
+    for _ in range(500):
+        tp = float(rng.uniform(1e-4, 2.0))
+        tok = float(rng.integers(512, 1 << 18))
+        n = int(rng.integers(0, 1 << 17))
+        thr = float(rng.uniform(1e8, 1e11))
+        rmin = int(rng.integers(0, 10001))
+        assert npk.cb_controller_ratio(tp, tok, n, thr, rmin) == \
+            oracle.controller_ratio(tp, tok, n, thr, rmin)
+    # the worked example of the pages (Llama-7B 4K: 3 ms at 15%, 16 ms load)
+    assert npk.cb_controller_ratio(0.02, 16384, 4096, 16384 * 4096 / 0.016, 1500) == 8000
+
+
+def test_controller_rejects_bad_args(npk):
+    R = npk.RAW["cb_controller_ratio"]
+    out = ctypes.c_int32()
+    assert R(0.0, 1.0, 1, 1.0, 0, ctypes.byref(out)) == npk.CB_E_INVALID
+    assert R(1.0, 1.0, -1, 1.0, 0, ctypes.byref(out)) == npk.CB_E_INVALID
+    assert R(1.0, 1.0, 1, float("inf"), 0, ctypes.byref(out)) == npk.CB_E_INVALID
+    assert R(1.0, 1.0, 1, 1.0, 10001, ctypes.byref(out)) == npk.CB_E_INVALID
+    assert R(1.0, 1.0, 1, 1.0, 0, None) == npk.CB_E_INVALID
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_cache_replay_matches_oracle(npk, seed):
+    """The tier's LRU decisions (hits and releases, in order) equal the
+    oracle's replay on Zipf-distributed chunk streams of varied sizes and
+    budgets."""
+    import numpy as np
+    rng = np.random.default_rng(seed)
+    pool = 60
+    p = np.arange(1, pool + 1, dtype=np.float64) ** -1.1
+    p /= p.sum()
+    size = {k: int(rng.integers(1, 40)) * 4096 for k in range(pool)}
+    batches = []
+    for _ in range(int(rng.integers(1, 30))):
+        ids = rng.choice(pool, size=int(rng.integers(0, 12)), p=p)
+        batches.append([(int(k) * 7919 + 3, size[int(k)]) for k in ids])
+    for cap in (0, 4096, 20 * 4096, 200 * 4096, 10 ** 12):
+        got = npk.cb_cache_replay(cap, batches)
+        want = oracle.lru_replay(cap, batches)
+        assert got == [(h, list(e)) for h, e in want], cap
+
+
+def test_cache_replay_hand_example(npk):
+    b = lambda *ks: [(k, 1) for k in ks]
+    assert npk.cb_cache_replay(3, [b(1, 2, 3), b(1, 4), b(2, 3), b(1, 4, 1)]) == \
+        [([False] * 3, []), ([True, False], [2]), ([False, True], [1]),
+         ([False, True, False], [3])]
+
+
+def test_cache_entry_validation(npk):
+    R = npk.RAW
+    h = ctypes.c_void_p()
+    assert R["cb_cache_create"](0, 256, npk.CB_BF16, 1 << 20, ctypes.byref(h)) == npk.CB_E_SHAPE
+    assert R["cb_cache_create"](2, 250, npk.CB_BF16, 1 << 20, ctypes.byref(h)) == npk.CB_E_SHAPE
+    assert R["cb_cache_create"](2, 256, 7, 1 << 20, ctypes.byref(h)) == npk.CB_E_INVALID
+    assert R["cb_cache_create"](2, 256, npk.CB_BF16, -1, ctypes.byref(h)) == npk.CB_E_SHAPE
+    assert R["cb_cache_create"](2, 256, npk.CB_BF16, 1, None) == npk.CB_E_INVALID
+    assert R["cb_cache_resolve"](None, 0, None, None, None, None, None) == npk.CB_E_INVALID
+    assert R["cb_cache_admit"](None, 0, None, None, None) == npk.CB_E_INVALID
+    assert R["cb_cache_stats"](None, None) == npk.CB_E_INVALID
+    assert R["cb_cache_replay"](-1, 0, None, None, None, None, None, None) == npk.CB_E_INVALID
+    R["cb_cache_destroy"](None)
