@@ -45,6 +45,11 @@ def parse():
     ap.add_argument("--kv-format", default="plain", choices=["plain", "u8", "u4"],
                     help="storage of the chunk caches: model dtype, or per-channel 8/4-bit "
                          "codes made by cb_quantize_kv after the precompute")
+    ap.add_argument("--serve-batches", type=int, default=0,
+                    help="batched workloads: serve a stream of this many batches over one "
+                         "chunk pool through the HBM chunk tier (steps/warmup are ignored)")
+    ap.add_argument("--tier-gib", type=float, default=24.0,
+                    help="HBM tier capacity for --serve-batches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--no-full-compare", action="store_true")
@@ -376,6 +381,219 @@ def roofline(st, kernels, traffic):
             "frac": ach / PEAK_HBM_GBS, "traffic": None, "kernel": dom}
 
 
+def pinned_empty(shape, dtype, torch):
+    """A pinned host tensor in one hipHostMalloc block of exactly its size
+    (torch's pinned allocator rounds blocks up to a power of two).  The
+    block lives as long as the tensor."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so.7")         # the HIP runtime torch loaded
+    nbytes = int(np.prod(shape)) * torch.empty((), dtype=dtype).element_size()
+    ptr = ctypes.c_void_p()
+    if hip.hipHostMalloc(ctypes.byref(ptr), ctypes.c_size_t(nbytes), ctypes.c_uint(0)) != 0:
+        raise MemoryError(f"hipHostMalloc of {nbytes} bytes failed")
+
+    class Block(ctypes.Structure):          # frees the block with its last reference
+        _fields_ = [("data", ctypes.c_uint8 * nbytes)]
+
+        def __del__(self, hip=hip, p=ptr.value):
+            hip.hipHostFree(ctypes.c_void_p(p))
+
+    blk = Block.from_address(ptr.value)
+    t = torch.frombuffer(blk, dtype=torch.uint8)
+    return t.view(dtype).view(shape)
+
+
+def h2d_throughput(torch, nbytes=1 << 30):
+    """Pinned host -> device copy rate (bytes/s) of one large copy."""
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(3):
+        dst.copy_(src, non_blocking=True)
+    torch.cuda.synchronize()
+    rate = 3 * nbytes / (time.perf_counter() - t0)
+    del src, dst
+    torch.cuda.empty_cache()
+    torch.cuda.memory.empty_cache() if hasattr(torch.cuda, "memory") else None
+    return rate
+
+
+def main_serve(args, npk, torch, w):
+    """A stream of batches over one chunk pool in pinned host memory, served
+    through the HBM chunk tier (cb_cache_resolve, cb_blend_batch,
+    cb_cache_commit per batch): `warmup` batches fill the tier, then
+    `serve_batches` further batches are timed; then the same timed batches
+    with every chunk copied from host memory.  The load controller's r* is
+    reported from the measured full-recompute time and host-copy rate."""
+    from workloads import make_request_stream, make_batch_tokens
+    S = w.shape
+    L, kvd = S.n_layers, S.kv_dim
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    B = args.serve_batches
+    W = max(1, args.warmup)          # batches that fill the tier before the timed ones
+    bits = BITS[args.kv_format]
+    log(f"[serve] {B} batches of {w.name}, chunk format {args.kv_format}, tier {args.tier_gib} GiB")
+    thr = h2d_throughput(torch)      # before the pool takes the pinned memory
+    model, layers, emb = make_model(npk, S, args.seed, torch)
+    pool_lens, batches = make_request_stream(w, args.seed, W + B)
+    all_reqs = [r for b in batches for r in b]
+    pool_tok, _ = make_batch_tokens(S, pool_lens, all_reqs, args.seed)
+    used = sorted({i for r in all_reqs for i in r["chunk_ids"]})
+    width = kvd if not bits else kvd * bits // 8
+    edt = bf if not bits else torch.uint8
+    row_of, U = {}, 0
+    for i in used:
+        row_of[i] = U
+        U += int(pool_lens[i])
+    # one pinned buffer per K and V: [L][U][width]; chunk i owns rows row_of[i]..
+    pk = pinned_empty((L, U, width), edt, torch)
+    pv = pinned_empty((L, U, width), edt, torch)
+    pq = pinned_empty((len(used), L, 4, kvd), torch.float32, torch) if bits else None
+    esz = 1 if bits else 2
+    pool = [{"k": 0, "v": 0, "n_tokens": 1, "on_host": 0, "layer_stride": kvd}
+            for _ in pool_lens]
+    for j, i in enumerate(used):
+        n, o = int(pool_lens[i]), row_of[i]
+        x = emb[torch.from_numpy(pool_tok[i]).to(dev)].contiguous()
+        k = torch.empty((L, n, S.n_kv_heads, S.head_dim), dtype=bf, device=dev)
+        v = torch.empty_like(k)
+        npk.cb_prefill(model, x, n, 0, k, v)
+        e = {"k": pk.data_ptr() + o * width * esz, "v": pv.data_ptr() + o * width * esz,
+             "n_tokens": n, "on_host": 1, "layer_stride": U * kvd}
+        if bits:
+            q = npk.quantize_chunk(k, v, bits)
+            k, v = q["k"], q["v"]
+            pq[j].copy_(q["qparams"])
+            e["kv_format"] = q["kv_format"]
+            e["qparams"] = pq[j].data_ptr()
+        pk[:, o:o + n].copy_(k.reshape(L, n, width))
+        pv[:, o:o + n].copy_(v.reshape(L, n, width))
+        pool[i] = e
+    torch.cuda.synchronize()
+    inputs = []
+    for reqs in batches:
+        _, suf = make_batch_tokens(S, pool_lens, reqs, args.seed)
+        toks = np.concatenate([np.concatenate([pool_tok[i] for i in r["chunk_ids"]] + [t])
+                               for r, t in zip(reqs, suf)]).astype(np.int64)
+        x0 = emb[torch.from_numpy(toks).to(dev)].contiguous()
+        n_tot = int(toks.shape[0])
+        n_c = sum(int(pool_lens[i]) for r in reqs for i in r["chunk_ids"])
+        inputs.append((reqs, x0, n_tot, n_c))
+    del emb
+    n_max = max(t for _, _, t, _ in inputs)
+    fk_buf = torch.empty(L * n_max * kvd, dtype=bf, device=dev)
+    fv_buf = torch.empty_like(fk_buf)
+
+    def fused(n):        # contiguous [L][n][H_kv][d_h] views of one buffer
+        shape = (L, n, S.n_kv_heads, S.head_dim)
+        return fk_buf[:L * n * kvd].view(shape), fv_buf[:L * n * kvd].view(shape)
+
+    kind = npk.CB_SCHED_GRADUAL if w.schedule_kind == "gradual" else npk.CB_SCHED_FIXED
+    keys = list(range(len(pool)))
+    per_token_bytes = 2 * L * kvd * (bits / 8 if bits else 2)
+
+    def run_stream(tier, part, marks=None):
+        host_bytes = 0
+        hits = uses = 0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for reqs, x0, n_tot, _ in part:
+            if marks is not None:
+                marks.append(torch.cuda.Event(enable_timing=True))
+                marks[-1].record()
+            ids = {i for r in reqs for i in r["chunk_ids"]}
+            # chunks this batch does not use are never read: not looked up either
+            p = [e if i in ids else dict(e, on_host=0) for i, e in enumerate(pool)]
+            bp = p
+            if tier is not None:
+                p, h = tier.resolve(keys, bp)
+                hits += sum(h[i] for i in ids)
+                uses += len(ids)
+            host_bytes += sum(int(pool_lens[i]) for i in ids) * per_token_bytes
+            fk, fv = fused(n_tot)
+            npk.cb_blend_batch(model, p, reqs, x0, fk, fv, recompute_bp=w.r_bp,
+                               schedule_kind=kind)
+            if tier is not None:
+                tier.commit(keys)
+        if marks is not None:
+            marks.append(torch.cuda.Event(enable_timing=True))
+            marks[-1].record()
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, hits, uses, host_bytes
+
+    def spans(marks):
+        return [round(a.elapsed_time(b), 1) for a, b in zip(marks, marks[1:])]
+
+    cap = int(args.tier_gib * (1 << 30))
+    warm, timed = inputs[:W], inputs[W:]
+    # without the tier first: releasing the tier's device memory afterwards
+    # slows the device for a while, which would land in this pass
+    log(f"[serve] {B} timed batches, every chunk from host memory")
+    run_stream(None, warm[-1:])
+    m_host = []
+    t_host, _, _, host_bytes = run_stream(None, timed, m_host)
+    tier = npk.ChunkCache(L, kvd, npk.CB_BF16, cap)
+    log(f"[serve] {W} batches fill the tier")
+    _, w_hits, w_uses, _ = run_stream(tier, warm)
+    st0 = tier.stats()
+    log(f"[serve] the same {B} batches through the tier")
+    m_tier = []
+    t_tier, hits, uses, _ = run_stream(tier, timed, m_tier)
+    st = tier.stats()
+    tier.close()
+    tokens = sum(t for _, _, t, _ in timed)
+    # load controller: measured copy rate and full-recompute time of batch 0
+    log("[serve] controller inputs: host copy rate, full recompute of batch 0")
+    reqs0, x00, n0, nc0 = inputs[0]
+    fk, fv = fused(n0)
+    npk.cb_blend_batch(model, pool, reqs0, x00, fk, fv, recompute_bp=10000, schedule_kind=kind)
+    torch.cuda.synchronize()
+    tf0 = time.perf_counter()
+    fk, fv = fused(n0)
+    npk.cb_blend_batch(model, pool, reqs0, x00, fk, fv, recompute_bp=10000, schedule_kind=kind)
+    torch.cuda.synchronize()
+    t_full = time.perf_counter() - tf0
+    ids0 = {i for r in reqs0 for i in r["chunk_ids"]}
+    unique0 = sum(int(pool_lens[i]) for i in ids0)
+    miss_tokens = unique0 * (1 - hits / max(1, uses))
+    r_star_host = npk.cb_controller_ratio(t_full, per_token_bytes, unique0, thr, w.r_bp)
+    r_star_tier = npk.cb_controller_ratio(t_full, per_token_bytes, int(round(miss_tokens)), thr,
+                                          w.r_bp)
+    out = {"metric": "effective prompt tok/s over a stream of batches, HBM chunk tier in front "
+                     "of pinned host memory",
+           "value": tokens / t_tier, "unit": "tok/s", "n_gpus": 1, "steps": B, "warmup": W,
+           "ms_per_step": t_tier / B * 1e3, "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic: random-init N(0,0.02) weights, uniform random tokens, pool "
+                   "chunk caches precomputed alone by cb_prefill",
+           "config": {"workload": w.name + "-stream", "batches": B,
+                      "requests_per_batch": w.n_requests, "prompt_tokens": tokens,
+                      "pool_chunks_used": len(used),
+                      "pool_tokens_used": sum(int(pool_lens[i]) for i in used),
+                      "chunk_kv_format": args.kv_format, "tier_bytes": cap,
+                      "recompute_bp": w.r_bp, "schedule": w.schedule_kind},
+           "batch_tokens": [t for _, _, t, _ in timed],
+           "batch_ms": spans(m_tier),
+           "tier": {"hit_rate": hits / max(1, uses), "hit_rate_fill_batches": w_hits / max(1, w_uses),
+                    "lookups": st["lookups"] - st0["lookups"], "hits": st["hits"] - st0["hits"],
+                    "admitted": st["admitted"] - st0["admitted"],
+                    "evicted": st["evicted"] - st0["evicted"],
+                    "resident_bytes": st["resident_bytes"],
+                    "copied_bytes": st["copied_bytes"] - st0["copied_bytes"]},
+           "no_tier": {"ms_per_step": t_host / B * 1e3, "tok_s": tokens / t_host,
+                       "batch_ms": spans(m_host),
+                       "host_bytes_per_step": host_bytes / B},
+           "controller": {"h2d_bytes_per_s": thr, "t_full_recompute_batch0_ms": t_full * 1e3,
+                          "r_min_bp": w.r_bp, "r_star_bp_all_from_host": r_star_host,
+                          "r_star_bp_with_tier_misses": r_star_tier,
+                          "t_load_batch0_ms_all_from_host":
+                              unique0 * per_token_bytes / thr * 1e3}}
+    print(json.dumps(out), flush=True)
+
+
 def cpu_baseline_batch(w, seed, reqs, pool_lens, n_total):
     """The oracle on two requests of the batch (the first two), first three
     layers each at full width and context; each request's time is composed
@@ -554,7 +772,10 @@ def main():
     import dataclasses
 
     if args.workload in BATCHED_WORKLOADS:
-        main_batched(args, npk, torch, BATCHED_WORKLOADS[args.workload])
+        if args.serve_batches > 0:
+            main_serve(args, npk, torch, BATCHED_WORKLOADS[args.workload])
+        else:
+            main_batched(args, npk, torch, BATCHED_WORKLOADS[args.workload])
         return
     w = WORKLOADS[args.workload]
     if args.r_bp is not None:

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 2
+#define CB_ABI_VERSION 3
 
 typedef enum cb_status {
     CB_OK = 0,
@@ -129,7 +129,14 @@ typedef enum cb_kv_format { CB_KV_PLAIN = 0, CB_KV_U8 = 1, CB_KV_U4 = 2 } cb_kv_
  * library's side stream.  Quantized chunks also pass qparams:
  * [L][4][H_kv*d_head] float32 (k scale, k zero, v scale, v zero of every
  * channel), in the same kind of memory as k and v.  k, v and qparams must
- * be 16-byte aligned, and the bytes of a layer stride a multiple of 16. */
+ * be 16-byte aligned, and the bytes of a layer stride a multiple of 16.
+ *
+ * Staging (host chunks only, all three or none): stage_k / stage_v
+ * (device, [L][n_tokens][H_kv*d_head] dense, in the chunk's format) and,
+ * for quantized chunks, stage_qparams (device [L][4][H_kv*d_head]).  Each
+ * layer's fetch then copies the host layer there and reads it from there,
+ * so after the fusion the staging buffers hold a device copy of the chunk
+ * (the HBM tier, cb_cache_*, hands out such buffers). */
 typedef struct cb_chunk_kv {
     const void* k;
     const void* v;
@@ -139,6 +146,9 @@ typedef struct cb_chunk_kv {
     int32_t kv_format;        /* cb_kv_format                              */
     int32_t reserved;         /* must be 0                                 */
     const float* qparams;     /* U8/U4: [L][4][H_kv*d_head]; PLAIN: NULL   */
+    void* stage_k;            /* NULL, or device copy destinations         */
+    void* stage_v;
+    float* stage_qparams;
 } cb_chunk_kv;
 
 typedef struct cb_request {
@@ -303,54 +313,53 @@ cb_status cb_controller_ratio(double t_prefill_s, double per_token_kv_bytes, int
  * leave first.
  *
  * Protocol, all on one caller stream: cb_cache_resolve for the chunk uses
- * of a request or batch, the fusion with the resolved descriptors, then
- * cb_cache_admit with the same uses.  A key names one chunk cache (content,
- * length and format) for the life of the tier, e.g. a hash of its text. */
+ * of a request or batch, the fusion with the resolved descriptors (queued
+ * on the same stream), then cb_cache_commit.  A missed chunk is copied to
+ * the device once, by the fusion's own per-layer fetch, into the entry the
+ * lookup reserved for it (the staging fields of cb_chunk_kv); commit makes
+ * those entries available to later lookups.  A key names one chunk cache
+ * (content, length and format) for the life of the tier, e.g. a hash of
+ * its text. */
 typedef struct cb_chunk_cache cb_chunk_cache;
 
 typedef struct cb_cache_stat {
     int64_t lookups;            /* host chunk uses looked up                 */
     int64_t hits;               /* of which served from HBM                  */
-    int64_t admitted;           /* entries copied in                         */
+    int64_t admitted;           /* entries filled by fusions and committed   */
     int64_t evicted;            /* entries released                          */
     int64_t resident_entries;
     int64_t resident_bytes;     /* device bytes held by entries              */
-    int64_t copied_bytes;       /* host -> device bytes of admissions        */
+    int64_t copied_bytes;       /* host -> device bytes staged into entries  */
 } cb_cache_stat;
 
 /* A tier on the current device for chunks of n_layers layers of row =
  * H_kv*d_head elements in dtype (quantized chunks are stored as codes plus
  * parameters); capacity_bytes of device memory for entries (0: nothing is
- * ever kept).  The tier owns a stream (default priority) and a memory pool. */
+ * ever kept).  Entries come from a memory pool of the tier. */
 cb_status cb_cache_create(int32_t n_layers, int32_t row, int32_t dtype, int64_t capacity_bytes,
                           cb_chunk_cache** out);
 /* Waits for all work on the device, then releases every entry. */
 void cb_cache_destroy(cb_chunk_cache* cache);
-/* For each of n uses (keys and chunks host [n]): a pinned-host chunk whose
- * key is resident is replaced in out (host [n]) by the descriptor of its HBM
- * copy and becomes the most recently used (a hit); every other chunk is
- * copied to out unchanged.  hits (host [n] or NULL): 1 for a hit.  `stream`
- * waits for earlier admissions.  A resolved device descriptor stays valid
- * for work queued on `stream` before the next cb_cache_admit. */
+/* For each of n uses (keys and chunks host [n]), out (host [n]) receives:
+ * for a pinned-host chunk whose key is resident, the descriptor of its HBM
+ * copy (a hit, which becomes the most recently used); for another
+ * pinned-host chunk, the chunk with staging buffers of a new entry, when
+ * least recently used entries that this call does not use can be released
+ * to make room (else the chunk unchanged); any other chunk unchanged.
+ * hits (host [n] or NULL): 1 for a hit.  Entries are allocated and
+ * released in the order of `stream`.  Entries reserved by an earlier
+ * resolve that was not committed are released. */
 cb_status cb_cache_resolve(cb_chunk_cache* cache, int32_t n, const uint64_t* keys,
                            const cb_chunk_kv* chunks, cb_chunk_kv* out, int32_t* hits,
                            void* stream);
-/* Call after queuing the fusion that reads the resolved descriptors.  In
- * order, every pinned-host use whose key is not resident is copied into HBM
- * as the most recently used entry, releasing least recently used entries
- * until it fits (a chunk above the budget is skipped).  Copies and releases
- * run on the tier's stream after everything queued on `stream` so far.
- * Chunks must be pinned and stay valid until the copies are done (the next
- * cb_cache_resolve makes its stream wait for them; or synchronize the
- * device).  CB_E_OOM if the device has no memory for an entry (entries
- * admitted before it stay). */
-cb_status cb_cache_admit(cb_chunk_cache* cache, int32_t n, const uint64_t* keys,
-                         const cb_chunk_kv* chunks, void* stream);
+/* After the fusion that reads the resolved descriptors is queued: the
+ * entries that resolve reserved for these keys become resident. */
+cb_status cb_cache_commit(cb_chunk_cache* cache, int32_t n, const uint64_t* keys);
 cb_status cb_cache_stats(cb_chunk_cache* cache, cb_cache_stat* out);
 /* Host-only replay of the tier's policy on batches of uses (batch b has
  * batch_sizes[b] consecutive entries of keys / sizes in bytes), each batch
- * looked up then admitted as above: hits_out [total uses] gets 1 for a hit;
- * evicted_per_batch [n_batches] the number of entries released after each
+ * resolved and committed: hits_out [total uses] gets 1 for a hit;
+ * evicted_per_batch [n_batches] the number of entries released in each
  * batch, and evicted_out (NULL, or room for one key per use) their keys in
  * release order.  For tests and capacity planning. */
 cb_status cb_cache_replay(int64_t capacity_bytes, int32_t n_batches, const int32_t* batch_sizes,

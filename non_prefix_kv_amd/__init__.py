@@ -17,7 +17,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ------------------------------------------------------------------ constants
-CB_ABI_VERSION = 2
+CB_ABI_VERSION = 3
 CB_OK, CB_E_INVALID, CB_E_SHAPE, CB_E_NOT_PINNED, CB_E_SCHEDULE = 0, -1, -2, -3, -4
 CB_E_OOM, CB_E_HIP, CB_E_BAD_STATE, CB_E_UNSUPPORTED = -5, -6, -7, -8
 CB_F32, CB_BF16 = 0, 1
@@ -43,7 +43,8 @@ class cb_layer_weights(ctypes.Structure):
 class cb_chunk_kv(ctypes.Structure):
     _fields_ = [("k", _c_p), ("v", _c_p), ("n_tokens", _c_i32), ("on_host", _c_i32),
                 ("layer_stride", _c_i64), ("kv_format", _c_i32), ("reserved", _c_i32),
-                ("qparams", _c_p)]
+                ("qparams", _c_p), ("stage_k", _c_p), ("stage_v", _c_p),
+                ("stage_qparams", _c_p)]
 
 
 class cb_request(ctypes.Structure):
@@ -120,7 +121,7 @@ _fn = {
     "cb_cache_destroy": (None, _c_p),
     "cb_cache_resolve": (ctypes.c_int, _c_p, _c_i32, _P(ctypes.c_uint64), _P(cb_chunk_kv),
                          _P(cb_chunk_kv), _P(_c_i32), _c_p),
-    "cb_cache_admit": (ctypes.c_int, _c_p, _c_i32, _P(ctypes.c_uint64), _P(cb_chunk_kv), _c_p),
+    "cb_cache_commit": (ctypes.c_int, _c_p, _c_i32, _P(ctypes.c_uint64)),
     "cb_cache_stats": (ctypes.c_int, _c_p, _P(cb_cache_stat)),
     "cb_cache_replay": (ctypes.c_int, _c_i64, _c_i32, _P(_c_i32), _P(ctypes.c_uint64),
                         _P(_c_i64), _P(_c_i32), _P(ctypes.c_uint64), _P(_c_i32)),
@@ -254,6 +255,9 @@ def _chunk_array(chunks):
         arr[i].layer_stride = c["layer_stride"]
         arr[i].kv_format = int(c.get("kv_format", CB_KV_PLAIN))
         arr[i].qparams = _ptr(c.get("qparams"))
+        arr[i].stage_k = _ptr(c.get("stage_k"))
+        arr[i].stage_v = _ptr(c.get("stage_v"))
+        arr[i].stage_qparams = _ptr(c.get("stage_qparams"))
     return arr
 
 
@@ -391,7 +395,8 @@ def cb_cache_replay(capacity_bytes, batches):
 
 
 class ChunkCache:
-    """cb_chunk_cache: HBM tier for pinned-host chunk caches."""
+    """cb_chunk_cache: HBM tier for pinned-host chunk caches.  Per request or
+    batch: resolve, queue the fusion with the resolved descriptors, commit."""
 
     def __init__(self, n_layers, row, dtype, capacity_bytes):
         h = _c_p()
@@ -409,11 +414,10 @@ class ChunkCache:
         _check(RAW["cb_cache_resolve"](self.handle, n, ka, arr, out, hits, _stream(stream)))
         return out, [bool(hits[i]) for i in range(n)]
 
-    def admit(self, keys, chunks, stream=None):
-        n = len(chunks)
-        arr = _chunk_array(chunks)
-        ka = (ctypes.c_uint64 * max(1, n))(*keys)
-        _check(RAW["cb_cache_admit"](self.handle, n, ka, arr, _stream(stream)))
+    def commit(self, keys):
+        """After the fusion that reads the resolved descriptors is queued."""
+        ka = (ctypes.c_uint64 * max(1, len(keys)))(*keys)
+        _check(RAW["cb_cache_commit"](self.handle, len(keys), ka))
 
     def stats(self):
         st = cb_cache_stat()

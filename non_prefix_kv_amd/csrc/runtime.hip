@@ -259,6 +259,24 @@ struct cb_plan {
         size_t stage_off;         // staging offset: k codes, v codes, parameters
     };
     std::vector<QH2D> qh2d;
+    // host chunks with caller-given staging buffers: each layer is copied
+    // there (dense layers) and every use reads it from there
+    struct StageCopy {
+        const char* src_k;
+        const char* src_v;
+        const char* src_qp;
+        size_t src_layer_bytes;   // code/value bytes between layers of the source
+        size_t bytes;             // code/value bytes per layer
+        size_t qp_bytes;          // parameter bytes per layer (0: plain)
+        char* dst_k;
+        char* dst_v;
+        char* dst_qp;
+    };
+    std::vector<StageCopy> stage_copies;
+    // quantization parameters of host chunks (all layers, one copy per
+    // chunk) go to the device with the first fetch: per-layer copies of a
+    // few KiB would each become a small copy kernel on the side stream
+    bool params_sent = false;
     size_t stage_bytes = 0;
     char* stage = nullptr;
     std::vector<QRotJobs> qjobs[2];   // [0]: 8-bit, [1]: 4-bit codes
@@ -524,6 +542,21 @@ cb_status do_fetch(cb_plan* p, int l) {
     const size_t es = m->es(), row_bytes = (size_t)m->kvd() * es;
     char* fk = (char*)p->fused_k + (size_t)l * layer_elems(p) * es;
     char* fv = (char*)p->fused_v + (size_t)l * layer_elems(p) * es;
+    if (!p->params_sent) {
+        for (const cb_plan::StageCopy& c : p->stage_copies)
+            if (c.qp_bytes)
+                CB_HIP(hipMemcpyAsync(c.dst_qp, c.src_qp, c.qp_bytes * p->L, hipMemcpyHostToDevice,
+                                      side));
+        for (const cb_plan::QH2D& h : p->qh2d)
+            CB_HIP(hipMemcpyAsync(p->stage + h.stage_off + 2 * align_up(h.bytes, 256), h.qp,
+                                  h.qp_bytes * p->L, hipMemcpyHostToDevice, side));
+        p->params_sent = true;
+    }
+    for (const cb_plan::StageCopy& c : p->stage_copies) {
+        const size_t src = (size_t)l * c.src_layer_bytes, dst = (size_t)l * c.bytes;
+        CB_HIP(hipMemcpyAsync(c.dst_k + dst, c.src_k + src, c.bytes, hipMemcpyHostToDevice, side));
+        CB_HIP(hipMemcpyAsync(c.dst_v + dst, c.src_v + src, c.bytes, hipMemcpyHostToDevice, side));
+    }
     for (const cb_plan::H2D& h : p->h2d) {
         const size_t src = (size_t)l * h.layer_bytes, dst = (size_t)h.dst_row * row_bytes;
         CB_HIP(hipMemcpyAsync(fk + dst, h.k + src, h.bytes, hipMemcpyHostToDevice, side));
@@ -544,8 +577,6 @@ cb_status do_fetch(cb_plan* p, int l) {
         CB_HIP(hipMemcpyAsync(st, h.k + src, h.bytes, hipMemcpyHostToDevice, side));
         CB_HIP(hipMemcpyAsync(st + align_up(h.bytes, 256), h.v + src, h.bytes,
                               hipMemcpyHostToDevice, side));
-        CB_HIP(hipMemcpyAsync(st + 2 * align_up(h.bytes, 256), h.qp + (size_t)l * h.qp_bytes,
-                              h.qp_bytes, hipMemcpyHostToDevice, side));
     }
     for (int b = 0; b < 2; ++b)
         for (const QRotJobs& js : p->qjobs[b]) {
@@ -696,6 +727,18 @@ cb_status check_chunk(cb_model* m, const cb_chunk_kv& ck, int idx) {
         return fail(CB_E_INVALID, "chunk %d: on_host = 0 but K/V are not device memory", idx);
     }
     if (ck.reserved != 0) return fail(CB_E_INVALID, "chunk %d: reserved field must be 0", idx);
+    if (ck.stage_k || ck.stage_v || ck.stage_qparams) {
+        const bool quant = ck.kv_format != CB_KV_PLAIN;
+        if (!ck.on_host || !ck.stage_k || !ck.stage_v || quant != (ck.stage_qparams != nullptr))
+            return fail(CB_E_INVALID,
+                        "chunk %d: staging needs a host chunk and all of its stage buffers", idx);
+        if (mem_kind(ck.stage_k) != MemKind::Device || mem_kind(ck.stage_v) != MemKind::Device ||
+            (quant && mem_kind(ck.stage_qparams) != MemKind::Device))
+            return fail(CB_E_INVALID, "chunk %d: stage buffers must be device memory", idx);
+        if (!aligned_to(ck.stage_k, 16) || !aligned_to(ck.stage_v, 16) ||
+            (quant && !aligned_to(ck.stage_qparams, 16)))
+            return fail(CB_E_SHAPE, "chunk %d: stage buffers must be 16-byte aligned", idx);
+    }
     if (ck.kv_format == CB_KV_PLAIN) {
         if (ck.qparams) return fail(CB_E_INVALID, "chunk %d: qparams given for a plain chunk", idx);
         if (!aligned_to(ck.k, 16) || !aligned_to(ck.v, 16) || (ck.layer_stride * m->es()) % 16)
@@ -776,6 +819,20 @@ cb_status plan_layout(cb_plan* p) {
                     j.qp = ck.qparams;
                     j.code_layer_stride = b == 0 ? ck.layer_stride : ck.layer_stride / 2;
                     j.qp_layer_stride = 4 * (int64_t)row_elems;
+                } else if (ck.stage_k) {
+                    if (staged_at[q.ids[c]] < 0) {
+                        staged_at[q.ids[c]] = 0;
+                        p->stage_copies.push_back(
+                            {(const char*)ck.k, (const char*)ck.v, (const char*)ck.qparams,
+                             (size_t)(b == 0 ? ck.layer_stride : ck.layer_stride / 2), code_bytes,
+                             qp_bytes, (char*)ck.stage_k, (char*)ck.stage_v,
+                             (char*)ck.stage_qparams});
+                    }
+                    j.k = (const uint8_t*)ck.stage_k;
+                    j.v = (const uint8_t*)ck.stage_v;
+                    j.qp = ck.stage_qparams;
+                    j.code_layer_stride = (int64_t)code_bytes;
+                    j.qp_layer_stride = 4 * (int64_t)row_elems;
                 } else {
                     if (staged_at[q.ids[c]] < 0) {
                         staged_at[q.ids[c]] = (int64_t)p->stage_bytes;
@@ -783,15 +840,16 @@ cb_status plan_layout(cb_plan* p) {
                                            (const char*)ck.qparams,
                                            (size_t)(b == 0 ? ck.layer_stride : ck.layer_stride / 2),
                                            code_bytes, qp_bytes, p->stage_bytes});
-                        p->stage_bytes += 2 * align_up(code_bytes, 256) + align_up(qp_bytes, 256);
+                        p->stage_bytes += 2 * align_up(code_bytes, 256) +
+                                          align_up(qp_bytes * p->L, 256);
                     }
                     // offsets into the staging area until the workspace exists
                     const size_t o = (size_t)staged_at[q.ids[c]];
                     j.k = (const uint8_t*)(uintptr_t)o;
                     j.v = (const uint8_t*)(uintptr_t)(o + align_up(code_bytes, 256));
                     j.qp = (const float*)(uintptr_t)(o + 2 * align_up(code_bytes, 256));
-                    j.code_layer_stride = 0;
-                    j.qp_layer_stride = 0;
+                    j.code_layer_stride = 0;                       // one layer staged at a time
+                    j.qp_layer_stride = 4 * (int64_t)row_elems;    // every layer's parameters
                     j.staged = 1;
                 }
                 qjobs[b].push_back(j);
@@ -805,6 +863,18 @@ cb_status plan_layout(cb_plan* p) {
             if (!ck.on_host) {
                 j.k_src = ck.k;
                 j.v_src = ck.v;
+                copy.push_back(j);
+            } else if (ck.stage_k) {
+                const size_t bytes = (size_t)ck.n_tokens * row_elems * es;
+                if (first_row[q.ids[c]] < 0) {
+                    first_row[q.ids[c]] = j.dst_row;
+                    p->stage_copies.push_back({(const char*)ck.k, (const char*)ck.v, nullptr,
+                                               (size_t)ck.layer_stride * es, bytes, 0,
+                                               (char*)ck.stage_k, (char*)ck.stage_v, nullptr});
+                }
+                j.k_src = ck.stage_k;
+                j.v_src = ck.stage_v;
+                j.src_layer_stride = (int64_t)ck.n_tokens * row_elems;
                 copy.push_back(j);
             } else if (first_row[q.ids[c]] < 0) {
                 first_row[q.ids[c]] = j.dst_row;
@@ -820,7 +890,8 @@ cb_status plan_layout(cb_plan* p) {
                 copy.push_back(j);
             }
         }
-    p->lookahead = p->h2d.empty() && p->qh2d.empty() ? 2 : std::max(2, p->L);
+    p->lookahead = p->h2d.empty() && p->qh2d.empty() && p->stage_copies.empty()
+                       ? 2 : std::max(2, p->L);
     for (int b = 0; b < 2; ++b)
         for (size_t i = 0; i < qjobs[b].size(); ++i) {
             if (i % kMaxQRotJobs == 0) p->qjobs[b].push_back(QRotJobs{});

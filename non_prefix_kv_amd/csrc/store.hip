@@ -13,14 +13,18 @@
 // and Prompt Cache explainer, section "キャッシュヒット率とエビクション"
 // (hit rate, LRU eviction).  Entries are whole chunk caches (all layers, K,
 // V and, for quantized chunks, their parameters) in one device allocation
-// from a memory pool of the tier.  Copies in and releases run on the tier's
-// own stream, ordered after the work the caller queued before
-// cb_cache_admit, so an entry is never overwritten or released while a
-// fusion queued earlier still reads it.
+// from a memory pool of the tier.  A missed chunk gets a new entry at lookup
+// and the fusion's per-layer fetch copies the chunk into it (the staging
+// fields of cb_chunk_kv), so every chunk crosses the host link once.
+// Entries are allocated and released in the order of the caller's stream:
+// a release is queued after every fusion queued before it, so no fusion
+// still reads the memory; and the entries a lookup hands out are never
+// released by that same lookup.
 #include <cmath>
 #include <list>
 #include <mutex>
 #include <unordered_map>
+#include <unordered_set>
 #include <vector>
 
 #include <hip/hip_runtime.h>
@@ -54,15 +58,23 @@ public:
     }
 
     // Stores key as the most recently used, evicting least recently used
-    // keys until `bytes` fit; their keys are appended to `evicted` in
-    // eviction order.  An entry above the budget is refused (false).
-    bool insert(uint64_t key, int64_t bytes, std::vector<uint64_t>* evicted) {
-        if (bytes > cap_ || contains(key)) return false;
-        while (used_ + bytes > cap_) {
-            const uint64_t old = order_.back();
+    // keys outside `keep` until `bytes` fit; the evicted keys are appended
+    // to `evicted` in eviction order.  When even evicting every key outside
+    // `keep` cannot make room, nothing changes (false).
+    bool insert(uint64_t key, int64_t bytes, const std::unordered_set<uint64_t>& keep,
+                std::vector<uint64_t>* evicted) {
+        if (contains(key) || bytes < 0) return false;
+        int64_t room = cap_ - used_;
+        for (const auto& kv : map_)
+            if (!keep.count(kv.first)) room += kv.second.second;
+        if (bytes > room) return false;
+        for (auto it = order_.end(); used_ + bytes > cap_ && it != order_.begin();) {
+            --it;
+            if (keep.count(*it)) continue;
+            const uint64_t old = *it;
             used_ -= map_[old].second;
             map_.erase(old);
-            order_.pop_back();
+            it = order_.erase(it);
             evicted->push_back(old);
         }
         order_.push_front(key);
@@ -105,13 +117,11 @@ struct cb_chunk_cache {
     LruPolicy lru{0};
     struct Entry {
         void* mem = nullptr;
-        cb_chunk_kv dev{};
+        cb_chunk_kv dev{};          // the device copy, once filled
+        bool committed = false;     // filled by a fusion the caller committed
     };
     std::unordered_map<uint64_t, Entry> entries;
-    hipStream_t stream = nullptr;     // copies in and releases
     hipMemPool_t pool = nullptr;
-    hipEvent_t after_caller = nullptr, done = nullptr;
-    bool pending = false;
     cb_cache_stat st{};
     std::mutex mu;
 
@@ -161,13 +171,16 @@ cb_status cb_cache_replay(int64_t capacity_bytes, int32_t n_batches, const int32
         if (sizes[i] < 0) return set_error(CB_E_INVALID, "use %lld has a negative size", (long long)i);
     LruPolicy lru(capacity_bytes);
     std::vector<uint64_t> ev;
+    std::unordered_set<uint64_t> keep;
     int64_t at = 0, n_ev = 0;
     for (int b = 0; b < n_batches; ++b) {
         const int n = batch_sizes[b];
         for (int i = 0; i < n; ++i) hits_out[at + i] = lru.touch(keys[at + i]) ? 1 : 0;
+        keep.clear();
+        keep.insert(keys + at, keys + at + n);
         ev.clear();
         for (int i = 0; i < n; ++i)
-            if (!lru.contains(keys[at + i])) lru.insert(keys[at + i], sizes[at + i], &ev);
+            if (!lru.contains(keys[at + i])) lru.insert(keys[at + i], sizes[at + i], keep, &ev);
         if (evicted_out)
             for (uint64_t k : ev) evicted_out[n_ev++] = k;
         evicted_per_batch[b] = (int32_t)ev.size();
@@ -194,10 +207,7 @@ cb_status cb_cache_create(int32_t n_layers, int32_t row, int32_t dtype, int64_t 
     props.allocType = hipMemAllocationTypePinned;
     props.location.type = hipMemLocationTypeDevice;
     props.location.id = c->device;
-    if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking);
     if (e == hipSuccess) e = hipMemPoolCreate(&c->pool, &props);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->after_caller, hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&c->done, hipEventDisableTiming);
     if (e != hipSuccess) {
         (void)hipGetLastError();
         cb_cache_destroy(c);
@@ -213,14 +223,8 @@ void cb_cache_destroy(cb_chunk_cache* c) {
     if (!c) return;
     // fusions queued on any stream may still read entries
     (void)hipDeviceSynchronize();
-    if (c->stream) {
-        for (auto& kv : c->entries) (void)hipFreeAsync(kv.second.mem, c->stream);
-        (void)hipStreamSynchronize(c->stream);
-        (void)hipStreamDestroy(c->stream);
-    }
+    for (auto& kv : c->entries) (void)hipFree(kv.second.mem);
     if (c->pool) (void)hipMemPoolDestroy(c->pool);
-    if (c->after_caller) (void)hipEventDestroy(c->after_caller);
-    if (c->done) (void)hipEventDestroy(c->done);
     delete c;
 }
 
@@ -230,7 +234,24 @@ cb_status cb_cache_resolve(cb_chunk_cache* c, int32_t n, const uint64_t* keys,
     if (!c) return set_error(CB_E_INVALID, "cache is NULL");
     if (n < 0) return set_error(CB_E_INVALID, "n < 0");
     if (n > 0 && (!keys || !chunks || !out)) return set_error(CB_E_INVALID, "NULL buffer");
+    for (int i = 0; i < n; ++i) {
+        const cb_chunk_kv& h = chunks[i];
+        if (!h.on_host) continue;
+        if (h.stage_k || h.stage_v || h.stage_qparams)
+            return set_error(CB_E_INVALID, "use %d: chunk already has staging buffers", i);
+        if (h.n_tokens <= 0 ||
+            (h.kv_format != CB_KV_PLAIN && h.kv_format != CB_KV_U8 && h.kv_format != CB_KV_U4))
+            return set_error(CB_E_INVALID, "use %d: bad chunk descriptor", i);
+    }
+    const hipStream_t st = (hipStream_t)stream;
     std::lock_guard<std::mutex> lk(c->mu);
+    // entries reserved by a lookup that was never committed hold no data
+    for (auto it = c->entries.begin(); it != c->entries.end();) {
+        if (it->second.committed) { ++it; continue; }
+        CB_HIP_S(hipFreeAsync(it->second.mem, st));
+        c->lru.erase(it->first);
+        it = c->entries.erase(it);
+    }
     for (int i = 0; i < n; ++i) {
         out[i] = chunks[i];
         bool hit = false;
@@ -248,84 +269,61 @@ cb_status cb_cache_resolve(cb_chunk_cache* c, int32_t n, const uint64_t* keys,
         }
         if (hits) hits[i] = hit ? 1 : 0;
     }
-    if (c->pending) CB_HIP_S(hipStreamWaitEvent((hipStream_t)stream, c->done, 0));
-    return CB_OK;
-}
-
-cb_status cb_cache_admit(cb_chunk_cache* c, int32_t n, const uint64_t* keys,
-                         const cb_chunk_kv* chunks, void* stream) {
-    if (!c) return set_error(CB_E_INVALID, "cache is NULL");
-    if (n < 0) return set_error(CB_E_INVALID, "n < 0");
-    if (n > 0 && (!keys || !chunks)) return set_error(CB_E_INVALID, "NULL buffer");
-    // validate every use before anything is queued
-    for (int i = 0; i < n; ++i) {
-        const cb_chunk_kv& h = chunks[i];
-        if (!h.on_host) continue;
-        if (!h.k || !h.v || h.n_tokens <= 0 || h.layer_stride < (int64_t)h.n_tokens * c->row)
-            return set_error(CB_E_INVALID, "use %d: bad chunk descriptor", i);
-        if (h.kv_format != CB_KV_PLAIN && h.kv_format != CB_KV_U8 && h.kv_format != CB_KV_U4)
-            return set_error(CB_E_INVALID, "use %d: kv_format %d", i, h.kv_format);
-        if (h.kv_format != CB_KV_PLAIN && !h.qparams)
-            return set_error(CB_E_INVALID, "use %d: quantized chunk without qparams", i);
-        if (h.kv_format == CB_KV_U4 && (h.layer_stride % 2))
-            return set_error(CB_E_SHAPE, "use %d: odd layer stride of 4-bit codes", i);
-        if (cb::mem_kind(h.k) != cb::MemKind::Pinned || cb::mem_kind(h.v) != cb::MemKind::Pinned ||
-            (h.qparams && cb::mem_kind(h.qparams) != cb::MemKind::Pinned))
-            return set_error(CB_E_NOT_PINNED, "use %d: host chunk is not pinned", i);
-    }
-    std::lock_guard<std::mutex> lk(c->mu);
-    CB_HIP_S(hipEventRecord(c->after_caller, (hipStream_t)stream));
-    CB_HIP_S(hipStreamWaitEvent(c->stream, c->after_caller, 0));
+    // reserve entries for the misses; this call's entries are never released here
+    std::unordered_set<uint64_t> keep;
+    for (int i = 0; i < n; ++i)
+        if (chunks[i].on_host) keep.insert(keys[i]);
     std::vector<uint64_t> ev;
     for (int i = 0; i < n; ++i) {
         const cb_chunk_kv& h = chunks[i];
         if (!h.on_host || c->lru.contains(keys[i])) continue;
         const int64_t bytes = c->entry_bytes(h);
         ev.clear();
-        if (!c->lru.insert(keys[i], bytes, &ev)) continue;      // above the budget
+        if (!c->lru.insert(keys[i], bytes, keep, &ev)) continue;   // no room: stays on host
         for (uint64_t k : ev) {
-            CB_HIP_S(hipFreeAsync(c->entries[k].mem, c->stream));
+            CB_HIP_S(hipFreeAsync(c->entries[k].mem, st));
             c->entries.erase(k);
             ++c->st.evicted;
         }
         void* mem = nullptr;
-        if (hipMallocFromPoolAsync(&mem, (size_t)bytes, c->pool, c->stream) != hipSuccess) {
+        if (hipMallocFromPoolAsync(&mem, (size_t)bytes, c->pool, st) != hipSuccess) {
             (void)hipGetLastError();
             c->lru.erase(keys[i]);
-            // the entries admitted so far in this call stay valid
-            CB_HIP_S(hipEventRecord(c->done, c->stream));
-            c->pending = true;
-            return set_error(CB_E_OOM, "HBM tier: no device memory for an entry of %lld bytes",
-                             (long long)bytes);
+            continue;                                               // stays on host
         }
         const int64_t layer_elems = (int64_t)h.n_tokens * c->row;
-        const size_t width = (size_t)code_bytes(h.kv_format, layer_elems, c->dtype);
-        const size_t spitch = (size_t)code_bytes(h.kv_format, h.layer_stride, c->dtype);
-        const size_t plane = (size_t)round256((int64_t)width * c->L);
+        const int64_t plane = round256(code_bytes(h.kv_format, layer_elems * c->L, c->dtype));
         char* k = (char*)mem;
-        char* v = k + plane;
-        CB_HIP_S(hipMemcpy2DAsync(k, width, h.k, spitch, width, c->L, hipMemcpyHostToDevice,
-                                  c->stream));
-        CB_HIP_S(hipMemcpy2DAsync(v, width, h.v, spitch, width, c->L, hipMemcpyHostToDevice,
-                                  c->stream));
-        cb_chunk_kv d = h;
-        d.k = k;
-        d.v = v;
-        d.on_host = 0;
-        d.layer_stride = layer_elems;
-        c->st.copied_bytes += 2 * (int64_t)width * c->L;
-        if (h.kv_format != CB_KV_PLAIN) {
-            float* qp = (float*)(v + plane);
-            const size_t qb = (size_t)c->L * 4 * c->row * sizeof(float);
-            CB_HIP_S(hipMemcpyAsync(qp, h.qparams, qb, hipMemcpyHostToDevice, c->stream));
-            d.qparams = qp;
-            c->st.copied_bytes += (int64_t)qb;
-        }
-        c->entries[keys[i]] = {mem, d};
+        cb_chunk_cache::Entry& e = c->entries[keys[i]];
+        e.mem = mem;
+        e.committed = false;
+        e.dev = h;
+        e.dev.k = k;
+        e.dev.v = k + plane;
+        e.dev.on_host = 0;
+        e.dev.layer_stride = layer_elems;
+        e.dev.qparams = h.kv_format != CB_KV_PLAIN ? (const float*)(k + 2 * plane) : nullptr;
+        e.dev.stage_k = e.dev.stage_v = nullptr;
+        e.dev.stage_qparams = nullptr;
+        out[i].stage_k = k;
+        out[i].stage_v = k + plane;
+        out[i].stage_qparams = h.kv_format != CB_KV_PLAIN ? (float*)(k + 2 * plane) : nullptr;
+        c->st.copied_bytes += 2 * code_bytes(h.kv_format, layer_elems * c->L, c->dtype) +
+                              (h.kv_format != CB_KV_PLAIN ? (int64_t)c->L * 4 * c->row * 4 : 0);
+    }
+    return CB_OK;
+}
+
+cb_status cb_cache_commit(cb_chunk_cache* c, int32_t n, const uint64_t* keys) {
+    if (!c) return set_error(CB_E_INVALID, "cache is NULL");
+    if (n < 0 || (n > 0 && !keys)) return set_error(CB_E_INVALID, "bad keys");
+    std::lock_guard<std::mutex> lk(c->mu);
+    for (int i = 0; i < n; ++i) {
+        auto it = c->entries.find(keys[i]);
+        if (it == c->entries.end() || it->second.committed) continue;
+        it->second.committed = true;
         ++c->st.admitted;
     }
-    CB_HIP_S(hipEventRecord(c->done, c->stream));
-    c->pending = true;
     return CB_OK;
 }
 

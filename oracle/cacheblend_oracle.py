@@ -434,9 +434,10 @@ def lru_replay(capacity_bytes, batches):
     order.  Per batch: every use is looked up first (a hit refreshes the
     entry to most recent); then, in order, every use whose key is not
     resident is inserted as most recent, evicting least recently used
-    entries until it fits (an entry larger than the budget is not
-    inserted).  Returns per batch the list of hit flags and the keys
-    evicted, in eviction order."""
+    entries that this batch does not use until it fits; when that cannot
+    make room (or the entry is larger than the budget) it is not inserted.
+    Returns per batch the list of hit flags and the keys evicted, in
+    eviction order."""
     from collections import OrderedDict
     store = OrderedDict()          # key -> bytes; last = most recent
     used = 0
@@ -448,14 +449,20 @@ def lru_replay(capacity_bytes, batches):
             if hit:
                 store.move_to_end(key)
             hits.append(hit)
+        in_batch = {key for key, _ in batch}
         evicted = []
         for key, size in batch:
-            if key in store or size > capacity_bytes:
+            if key in store:
                 continue
-            while used + size > capacity_bytes:
-                old, osz = store.popitem(last=False)
-                used -= osz
-                evicted.append(old)
+            evictable = [k for k in store if k not in in_batch]      # least recent first
+            free = capacity_bytes - used
+            if size > free + sum(store[k] for k in evictable):
+                continue
+            for k in evictable:
+                if used + size <= capacity_bytes:
+                    break
+                used -= store.pop(k)
+                evicted.append(k)
             store[key] = size
             used += size
         out.append((hits, evicted))

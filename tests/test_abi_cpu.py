@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(npk):
 
 
 def test_abi_version(npk):
-    assert npk.cb_abi_version() == npk.CB_ABI_VERSION == 2
+    assert npk.cb_abi_version() == npk.CB_ABI_VERSION == 3
 
 
 @pytest.mark.parametrize("n", [0, 1, 10, 384, 3840, 7680, 8192])
@@ -200,6 +200,9 @@ def test_cache_replay_hand_example(npk):
     assert npk.cb_cache_replay(3, [b(1, 2, 3), b(1, 4), b(2, 3), b(1, 4, 1)]) == \
         [([False] * 3, []), ([True, False], [2]), ([False, True], [1]),
          ([False, True, False], [3])]
+    # a batch's own entries are not released for its misses
+    assert npk.cb_cache_replay(3, [b(1, 2, 3), b(1, 2, 5, 6), b(6)])[1:] == \
+        [([True, True, False, False], [3]), ([False], [1])]
 
 
 def test_cache_entry_validation(npk):
@@ -211,7 +214,7 @@ def test_cache_entry_validation(npk):
     assert R["cb_cache_create"](2, 256, npk.CB_BF16, -1, ctypes.byref(h)) == npk.CB_E_SHAPE
     assert R["cb_cache_create"](2, 256, npk.CB_BF16, 1, None) == npk.CB_E_INVALID
     assert R["cb_cache_resolve"](None, 0, None, None, None, None, None) == npk.CB_E_INVALID
-    assert R["cb_cache_admit"](None, 0, None, None, None) == npk.CB_E_INVALID
+    assert R["cb_cache_commit"](None, 0, None) == npk.CB_E_INVALID
     assert R["cb_cache_stats"](None, None) == npk.CB_E_INVALID
     assert R["cb_cache_replay"](-1, 0, None, None, None, None, None, None) == npk.CB_E_INVALID
     R["cb_cache_destroy"](None)

@@ -1,9 +1,8 @@
 """The HBM tier of the chunk store (cb_cache_*) on the GPU: fusions whose
-pinned-host chunks are served from the tier give the same bits as fusions
-that stream every chunk from host memory; the tier's hits and releases
-follow its LRU policy (checked against the oracle's replay, which the CPU
-tests pin); quantized chunks are kept as codes.  Host chunk memory stays
-alive until the device is synchronized after each admission."""
+pinned-host chunks are staged into or served from the tier give the same
+bits as fusions that stream every chunk from host memory; the tier's hits
+and releases follow its LRU policy (checked against the oracle's replay,
+which the CPU tests pin); quantized chunks are kept as codes."""
 import numpy as np
 import pytest
 import torch
@@ -84,7 +83,7 @@ def test_tier_fusions_bit_identical_and_lru(lib, cap_entries, quant):
                 c["on_host"] = 0
         resolved, hits = tier.resolve(keys, host_pool)
         _, got = run_gpu_batch(lib, model, bc, dt, pool=resolved)
-        tier.admit(keys, host_pool)
+        tier.commit(keys)
         torch.cuda.synchronize()
         for key in want:
             assert nan_eq(got[key], want[key]), (j, key)
@@ -104,25 +103,49 @@ def test_tier_fusions_bit_identical_and_lru(lib, cap_entries, quant):
 
 
 def test_tier_single_request_and_validation(lib):
+    """cb_blend (one request) through the tier: a staged miss, then a hit,
+    both bit-identical to host streaming; an uncommitted reservation is
+    dropped by the next lookup; descriptor checks."""
+    from tests.helpers import make_case
+    from tests.gpu_helpers import run_gpu_blend, chunk_inputs
+    from workloads import WORKLOADS
     dt = "bf16"
     L, row = TINY.n_layers, TINY.kv_dim
-    bc = batches_over_one_pool(dt)[0]
-    model = make_model(lib, bc, dt)
+    tw = WORKLOADS["tiny"]
+    case = make_case(TINY, tw.chunk_lens, tw.n_suffix, seed=3, dtype=dt)
+    model = make_model(lib, case, dt)
+    sched = oracle.schedule(case.n_chunk_tokens, 1500, "gradual", L)
+    host = chunk_inputs(case, dt, on_host=True)
+    want = run_gpu_blend(lib, model, case, dt, sched, chunks=host)
     tier = lib.ChunkCache(L, row, lib.CB_BF16, 1 << 30)
-    pool = pool_inputs(bc, dt, on_host=True)
-    # pageable host memory cannot be admitted
-    bad = [dict(c) for c in pool]
-    used = [i for i, c in enumerate(bc.pool) if c is not None][0]
-    bad[used]["k"] = bad[used]["k"].clone()
-    bad[used]["k"] = torch.empty(bad[used]["k"].shape, dtype=bad[used]["k"].dtype)
-    with pytest.raises(lib.CBError) as e:
-        tier.admit([used], [bad[used]])
-    assert e.value.status == lib.CB_E_NOT_PINNED
+    keys = [11, 12, 13]
+    for rnd in range(3):
+        resolved, hits = tier.resolve(keys, host)
+        assert hits == [rnd > 0] * 3
+        if rnd == 0:
+            assert all(resolved[i].stage_k for i in range(3))
+        got = run_gpu_blend(lib, model, case, dt, sched, chunks=resolved)
+        tier.commit(keys)
+        torch.cuda.synchronize()
+        for key in ("fused_k", "fused_v", "sel", "hidden"):
+            assert torch.equal(got[key], want[key]), (rnd, key)
+    # a reservation that is never committed does not become a hit
+    tier2 = lib.ChunkCache(L, row, lib.CB_BF16, 1 << 30)
+    tier2.resolve(keys, host)
+    _, hits = tier2.resolve(keys, host)
+    assert hits == [False] * 3
     # same key, other length: rejected at lookup
-    tier.admit([5], [pool[used]])
-    torch.cuda.synchronize()
-    other = dict(pool[used], n_tokens=pool[used]["n_tokens"] - 1)
+    other = [dict(host[0], n_tokens=host[0]["n_tokens"] - 1)]
     with pytest.raises(lib.CBError) as e:
-        tier.resolve([5], [other])
+        tier.resolve([11], other)
+    assert e.value.status == lib.CB_E_INVALID
+    # staging on a device chunk is rejected by the fusion
+    dev_chunks = chunk_inputs(case, dt)
+    bad = [dict(c) for c in dev_chunks]
+    bad[0]["stage_k"] = bad[1]["k"]
+    bad[0]["stage_v"] = bad[1]["v"]
+    with pytest.raises(lib.CBError) as e:
+        run_gpu_blend(lib, model, case, dt, sched, chunks=bad)
     assert e.value.status == lib.CB_E_INVALID
     tier.close()
+    tier2.close()

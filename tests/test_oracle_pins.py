@@ -509,6 +509,17 @@ def test_lru_replay_sizes_and_oversize():
     assert out[3] == ([True, False], ["d"])       # c was refreshed by its hit
 
 
+def test_lru_replay_protects_the_batch():
+    """Entries a batch uses are not released to make room for its own
+    misses: budget 3, batch [1,2,3] stored; batch [1,2,5,6]: 1, 2 hit, 5
+    evicts 3, and 6 finds only entries of this batch to release, so it is
+    not stored."""
+    b = lambda *ks: [(k, 1) for k in ks]
+    out = oracle.lru_replay(3, [b(1, 2, 3), b(1, 2, 5, 6), b(6)])
+    assert out[1] == ([True, True, False, False], [3])
+    assert out[2] == ([False], [1])
+
+
 def test_lru_hit_rate_matches_brute_force():
     """With a budget holding every key, the hit flags are 'seen before in an
     earlier batch' exactly; with budget 0 nothing ever hits."""

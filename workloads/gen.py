@@ -91,6 +91,27 @@ def make_batched_requests(w: BatchedWorkload, seed: int = 0):
     return pool_lens.astype(np.int64), reqs
 
 
+def make_request_stream(w: BatchedWorkload, seed: int = 0, n_batches: int = 1):
+    """A stream of batches over one chunk pool: batch 0 is
+    make_batched_requests(w, seed); batch j > 0 draws its requests the same
+    way from its own generator (the pool lengths are batch 0's)."""
+    pool_lens, first = make_batched_requests(w, seed)
+    ranks = np.arange(1, w.pool_size + 1, dtype=np.float64)
+    p = ranks ** (-w.zipf_s)
+    p /= p.sum()
+    batches = [first]
+    for j in range(1, n_batches):
+        g = np.random.Generator(np.random.PCG64([int(seed), int(j), 98]))
+        reqs = []
+        for _ in range(w.n_requests):
+            n = int(g.integers(w.chunks_per_req[0], w.chunks_per_req[1] + 1))
+            ids = g.choice(w.pool_size, size=n, replace=False, p=p)
+            suffix = int(g.integers(w.suffix_range[0], w.suffix_range[1] + 1))
+            reqs.append({"chunk_ids": [int(i) for i in ids], "n_suffix": suffix})
+        batches.append(reqs)
+    return pool_lens, batches
+
+
 def make_batch_tokens(shape: ModelShape, pool_lens, reqs, seed: int = 0):
     """Token ids of every pool chunk and of every request's suffix (seeded;
     a chunk has the same tokens wherever it is used)."""
