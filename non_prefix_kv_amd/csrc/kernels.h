@@ -70,10 +70,13 @@ hipError_t launch_dequant_rerotate(int dtype, int bits, const QRotJobs& jobs, in
                                    void* k_dst, void* v_dst, int n_heads, int head_dim,
                                    const RopeTab& rope, hipStream_t s);
 
-// Codes, scale and zero of x [n_layers][n_tokens][row] per layer and channel.
+// Codes, scale and zero of x [n_layers][n_tokens][row] per layer and channel;
+// ws: scratch of quantize_workspace() bytes (per-slice channel ranges).
+size_t quantize_workspace(int n_layers, int n_tokens, int row);
 hipError_t launch_quantize(int dtype, const void* x, int n_layers, int n_tokens, int row,
                            int64_t x_layer_stride, int bits, void* codes, float* scale,
-                           float* zero, int64_t param_stride, hipStream_t s);
+                           float* zero, int64_t param_stride, void* ws, size_t ws_bytes,
+                           hipStream_t s);
 
 // p[i] = base + i for i < n.
 hipError_t launch_iota(int* p, int n, int base, hipStream_t s);

@@ -10,9 +10,11 @@
 // float32 with IEEE operations (correctly rounded division, no contraction),
 // so a float32 reference reproduces every code.
 //
-// Both kernels are bound by HBM: encoding reads x twice (the second pass
-// mostly from L2) and writes b/8 bytes per element; decoding reads b/8 bytes
-// and writes the model dtype.
+// All kernels are bound by HBM: encoding reads x twice (once for the
+// per-channel range, once to encode) and writes b/8 bytes per element;
+// decoding reads b/8 bytes and writes the model dtype.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace cb {
@@ -55,23 +57,27 @@ __device__ __forceinline__ void load_codes(const uint8_t* p, float* x) {
     }
 }
 
-// Grid (ceil(row / 512), n_layers), 4 waves.  Lane i of every wave owns
-// channels c .. c+7 (c = 512 * blockIdx.x + 8 i); wave w takes tokens w,
-// w + 4, ...; the per-wave minima and maxima meet in LDS.
-template <typename T, int BITS>
-__global__ __launch_bounds__(kThreads) void quantize_kernel(
-    const T* __restrict__ x, int n_tokens, int row, int64_t x_ls, uint8_t* __restrict__ codes,
-    float* __restrict__ scale, float* __restrict__ zero, int64_t ps) {
+// Encoding runs in two launches over a grid (ceil(row / 512), n_layers,
+// splits): each workgroup owns 512 channels (8 per lane) of one layer and a
+// contiguous slice of the tokens, its 4 waves taking every 4th token.
+// minmax_kernel writes the slice's per-channel minima and maxima; codes_kernel
+// combines the partials of all slices (min / max are exact in any order),
+// derives scale and zero, and encodes its slice.
+template <typename T>
+__global__ __launch_bounds__(kThreads) void minmax_kernel(
+    const T* __restrict__ x, int n_tokens, int row, int64_t x_ls, int tok_per_split,
+    float* __restrict__ part) {
     __shared__ float red_lo[kQuantWaves][kChanPerBlock], red_hi[kQuantWaves][kChanPerBlock];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l = blockIdx.y;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l = blockIdx.y, sp = blockIdx.z;
     const int c = blockIdx.x * kChanPerBlock + lane * 8;
     const bool live = c < row;
     const T* xl = x + (int64_t)l * x_ls;
+    const int t0 = sp * tok_per_split, t1 = min(n_tokens, t0 + tok_per_split);
     float lo[8], hi[8], v[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) { lo[i] = INFINITY; hi[i] = -INFINITY; }
     if (live)
-        for (int t = w; t < n_tokens; t += kQuantWaves) {
+        for (int t = t0 + w; t < t1; t += kQuantWaves) {
             Vec8<T>::load(xl + (int64_t)t * row + c, v);
 #pragma unroll
             for (int i = 0; i < 8; ++i) { lo[i] = fminf(lo[i], v[i]); hi[i] = fmaxf(hi[i], v[i]); }
@@ -79,30 +85,51 @@ __global__ __launch_bounds__(kThreads) void quantize_kernel(
 #pragma unroll
     for (int i = 0; i < 8; ++i) { red_lo[w][lane * 8 + i] = lo[i]; red_hi[w][lane * 8 + i] = hi[i]; }
     __syncthreads();
-    if (!live) return;
-    const float levels = (float)((1 << BITS) - 1);
-    float s[8];
+    if (w != 0 || !live) return;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float a = red_lo[0][lane * 8 + i], b = red_hi[0][lane * 8 + i];
+    for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int u = 1; u < kQuantWaves; ++u) {
-            a = fminf(a, red_lo[u][lane * 8 + i]);
-            b = fmaxf(b, red_hi[u][lane * 8 + i]);
+            lo[i] = fminf(lo[i], red_lo[u][lane * 8 + i]);
+            hi[i] = fmaxf(hi[i], red_hi[u][lane * 8 + i]);
         }
-        lo[i] = a;
-        s[i] = __fsub_rn(b, a) / levels;
+    // partials: [layer][split][2][row]
+    float* p = part + ((int64_t)l * gridDim.z + sp) * 2 * row + c;
+    Vec8<float>::store(p, lo);
+    Vec8<float>::store(p + row, hi);
+}
+
+template <typename T, int BITS>
+__global__ __launch_bounds__(kThreads) void codes_kernel(
+    const T* __restrict__ x, int n_tokens, int row, int64_t x_ls, int tok_per_split,
+    const float* __restrict__ part, uint8_t* __restrict__ codes, float* __restrict__ scale,
+    float* __restrict__ zero, int64_t ps) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l = blockIdx.y, sp = blockIdx.z;
+    const int c = blockIdx.x * kChanPerBlock + lane * 8;
+    if (c >= row) return;
+    float lo[8], hi[8], v[8], s[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) { lo[i] = INFINITY; hi[i] = -INFINITY; }
+    const float* p = part + (int64_t)l * gridDim.z * 2 * row + c;
+    for (int u = 0; u < (int)gridDim.z; ++u) {
+        Vec8<float>::load(p + (int64_t)u * 2 * row, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lo[i] = fminf(lo[i], v[i]);
+        Vec8<float>::load(p + (int64_t)u * 2 * row + row, v);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hi[i] = fmaxf(hi[i], v[i]);
     }
-    if (w == 0) {
-        float* sp = scale + (int64_t)l * ps + c;
-        float* zp = zero + (int64_t)l * ps + c;
-        *reinterpret_cast<floatx4*>(sp) = floatx4{s[0], s[1], s[2], s[3]};
-        *reinterpret_cast<floatx4*>(sp + 4) = floatx4{s[4], s[5], s[6], s[7]};
-        *reinterpret_cast<floatx4*>(zp) = floatx4{lo[0], lo[1], lo[2], lo[3]};
-        *reinterpret_cast<floatx4*>(zp + 4) = floatx4{lo[4], lo[5], lo[6], lo[7]};
+    const float levels = (float)((1 << BITS) - 1);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] = __fsub_rn(hi[i], lo[i]) / levels;
+    if (sp == 0 && w == 0) {
+        Vec8<float>::store(scale + (int64_t)l * ps + c, s);
+        Vec8<float>::store(zero + (int64_t)l * ps + c, lo);
     }
+    const T* xl = x + (int64_t)l * x_ls;
     uint8_t* cl = codes + (int64_t)l * n_tokens * row * BITS / 8;
-    for (int t = w; t < n_tokens; t += kQuantWaves) {
+    const int t0 = sp * tok_per_split, t1 = min(n_tokens, t0 + tok_per_split);
+    for (int t = t0 + w; t < t1; t += kQuantWaves) {
         Vec8<T>::load(xl + (int64_t)t * row + c, v);
         float q[8];
 #pragma unroll
@@ -166,17 +193,33 @@ __global__ __launch_bounds__(kThreads) void dequant_rerotate_kernel(
     }
 }
 
+constexpr int kTokPerSplit = 64;
+constexpr int kMaxSplits = 256;
+
+int quant_splits(int n_tokens) {
+    return std::min(kMaxSplits, (n_tokens + kTokPerSplit - 1) / kTokPerSplit);
+}
+
 template <int BITS>
 hipError_t launch_quantize_bits(int dtype, const void* x, int n_layers, int n_tokens, int row,
                                 int64_t x_ls, void* codes, float* scale, float* zero, int64_t ps,
-                                hipStream_t s) {
-    dim3 grid((row + kChanPerBlock - 1) / kChanPerBlock, n_layers);
-    if (dtype == BF16)
-        hipLaunchKernelGGL((quantize_kernel<bf16, BITS>), grid, dim3(kThreads), 0, s,
-                           (const bf16*)x, n_tokens, row, x_ls, (uint8_t*)codes, scale, zero, ps);
-    else
-        hipLaunchKernelGGL((quantize_kernel<float, BITS>), grid, dim3(kThreads), 0, s,
-                           (const float*)x, n_tokens, row, x_ls, (uint8_t*)codes, scale, zero, ps);
+                                float* part, hipStream_t s) {
+    const int splits = quant_splits(n_tokens);
+    const int per = (n_tokens + splits - 1) / splits;
+    dim3 grid((row + kChanPerBlock - 1) / kChanPerBlock, n_layers, splits);
+    if (dtype == BF16) {
+        hipLaunchKernelGGL(minmax_kernel<bf16>, grid, dim3(kThreads), 0, s, (const bf16*)x,
+                           n_tokens, row, x_ls, per, part);
+        hipLaunchKernelGGL((codes_kernel<bf16, BITS>), grid, dim3(kThreads), 0, s,
+                           (const bf16*)x, n_tokens, row, x_ls, per, (const float*)part,
+                           (uint8_t*)codes, scale, zero, ps);
+    } else {
+        hipLaunchKernelGGL(minmax_kernel<float>, grid, dim3(kThreads), 0, s, (const float*)x,
+                           n_tokens, row, x_ls, per, part);
+        hipLaunchKernelGGL((codes_kernel<float, BITS>), grid, dim3(kThreads), 0, s,
+                           (const float*)x, n_tokens, row, x_ls, per, (const float*)part,
+                           (uint8_t*)codes, scale, zero, ps);
+    }
     return hipGetLastError();
 }
 
@@ -199,18 +242,25 @@ hipError_t launch_dequant_bits(int dtype, const QRotJobs& jobs, int layer, void*
 
 }  // namespace
 
+size_t quantize_workspace(int n_layers, int n_tokens, int row) {
+    if (n_layers <= 0 || n_tokens <= 0 || row <= 0) return 0;
+    return (size_t)n_layers * quant_splits(n_tokens) * 2 * row * sizeof(float);
+}
+
 hipError_t launch_quantize(int dtype, const void* x, int n_layers, int n_tokens, int row,
                            int64_t x_layer_stride, int bits, void* codes, float* scale,
-                           float* zero, int64_t param_stride, hipStream_t s) {
+                           float* zero, int64_t param_stride, void* ws, size_t ws_bytes,
+                           hipStream_t s) {
     if (n_layers <= 0 || n_tokens <= 0) return hipSuccess;
-    if (row <= 0 || row % 8 || param_stride < row || x_layer_stride < (int64_t)n_tokens * row)
+    if (row <= 0 || row % 8 || param_stride < row || x_layer_stride < (int64_t)n_tokens * row ||
+        !ws || ws_bytes < quantize_workspace(n_layers, n_tokens, row))
         return hipErrorInvalidValue;
     if (bits == 8)
         return launch_quantize_bits<8>(dtype, x, n_layers, n_tokens, row, x_layer_stride, codes,
-                                       scale, zero, param_stride, s);
+                                       scale, zero, param_stride, (float*)ws, s);
     if (bits == 4)
         return launch_quantize_bits<4>(dtype, x, n_layers, n_tokens, row, x_layer_stride, codes,
-                                       scale, zero, param_stride, s);
+                                       scale, zero, param_stride, (float*)ws, s);
     return hipErrorInvalidValue;
 }
 

@@ -1316,8 +1316,17 @@ cb_status cb_quantize_kv(int32_t dtype, const void* x, int32_t n_layers, int32_t
     if (!aligned_to(x, 16) || !aligned_to(codes, 16) || !aligned_to(scale, 16) ||
         !aligned_to(zero, 16) || (x_layer_stride * elem_size(dtype)) % 16 || param_stride % 4)
         return fail(CB_E_SHAPE, "buffers, the layer stride and param_stride must be 16-byte aligned");
-    CB_HIP(launch_quantize(dtype, x, n_layers, n_tokens, row, x_layer_stride, bits, codes, scale,
-                           zero, param_stride, as_stream(stream)));
+    const hipStream_t st = as_stream(stream);
+    const size_t wsb = quantize_workspace(n_layers, n_tokens, row);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, wsb, st) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(CB_E_OOM, "quantization scratch of %zu bytes", wsb);
+    }
+    const hipError_t e = launch_quantize(dtype, x, n_layers, n_tokens, row, x_layer_stride, bits,
+                                         codes, scale, zero, param_stride, ws, wsb, st);
+    (void)hipFreeAsync(ws, st);
+    if (e != hipSuccess) return fail(CB_E_HIP, "quantize launch: %s", hipGetErrorString(e));
     return CB_OK;
 }
 

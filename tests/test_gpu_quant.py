@@ -44,7 +44,8 @@ def gpu_quantize(lib, x, dt, bits, layer_stride=None):
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("bits", [8, 4])
 @pytest.mark.parametrize("L,n,row,pad", [(3, 37, 256, 0), (2, 5, 1032, 16), (1, 640, 4096, 0),
-                                         (2, 1, 64, 8), (1, 3, 8, 0)])
+                                         (2, 1, 64, 8), (1, 3, 8, 0), (2, 129, 72, 0),
+                                         (1, 25601, 64, 0)])
 def test_quantize_kernel_bit_exact(lib, dt, bits, L, n, row, pad):
     print(f"[quantize] dt={dt} bits={bits} L={L} n={n} row={row}", flush=True)
     rng = np.random.default_rng(L * 1000 + n + row)
