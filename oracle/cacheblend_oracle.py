@@ -402,6 +402,48 @@ def unpack_codes(packed, bits: int) -> np.ndarray:
 
 
 # --------------------------------------------------------------------------
+# First token and one decode step on the fused cache  [CB2 "用語解説": the KV
+# cache lets generation skip recomputing past tokens; TTFT is the time to
+# the first output token]
+# --------------------------------------------------------------------------
+def lm_head(x, final_norm, w_lm, eps):
+    """Logits of rows x [rows][d]: W_lm rmsnorm(x; final_norm)."""
+    x = np.atleast_2d(np.asarray(x, dtype=np.float64))
+    return rmsnorm(x, np.asarray(final_norm, np.float64), eps) @ np.asarray(w_lm, np.float64).T
+
+
+def argmax_first(v):
+    """Index of the largest entry: NaN above everything, smallest index among
+    equal values."""
+    v = np.asarray(v, dtype=np.float64)
+    nan = np.flatnonzero(np.isnan(v))
+    if nan.size:
+        return int(nan[0])
+    return int(np.flatnonzero(v == v.max())[0])
+
+
+def decode_step(weights, shape, x_new, fused_k, fused_v, n_ctx, dtype=np.float64):
+    """One token (input row x_new [d]) at position n_ctx through every layer,
+    attending over the first n_ctx rows of fused_k / fused_v [L][>=n_ctx]
+    [Hkv][dh] and its own key and value.  Returns (hidden [d], k_new
+    [L][Hkv][dh], v_new)."""
+    L = shape.n_layers
+    W = _cast_weights(weights[:L], dtype)
+    x = np.asarray(x_new, dtype=dtype)[None, :]
+    pos = np.array([n_ctx])
+    ks, vs = [], []
+    for l in range(L):
+        q, k, v = qkv_rows(W[l], shape, x, pos)
+        K = np.concatenate([np.asarray(fused_k[l][:n_ctx], dtype=dtype), k], axis=0)
+        V = np.concatenate([np.asarray(fused_v[l][:n_ctx], dtype=dtype), v], axis=0)
+        att = attention(q, pos, K, V, np.arange(n_ctx + 1))
+        x = finish_rows(W[l], shape, x, att)
+        ks.append(k[0])
+        vs.append(v[0])
+    return x[0], np.stack(ks), np.stack(vs)
+
+
+# --------------------------------------------------------------------------
 # Load controller  [CB1 "パイプライン実行とロードコントローラ": T_recompute =
 # r T_prefill; T_load = PerTokenKVSize * L / Throughput(D) with L the input
 # tokens; r* = max(r_min, T_load / T_prefill)]

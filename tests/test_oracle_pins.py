@@ -531,3 +531,53 @@ def test_lru_hit_rate_matches_brute_force():
         assert hits == [k in seen for k, _ in batch] and ev == []
         seen |= {k for k, _ in batch}
     assert all(not any(h) for h, _ in oracle.lru_replay(0, batches))
+
+
+# ------------------------------------------------------------ first token, decode step
+# CacheBlend explainer (abeam.tech), "用語解説" (KV cache reuse in generation, TTFT).
+
+def test_decode_step_equals_longer_prefill():
+    """Decoding token N on the full-prefill cache of tokens 0..N-1 equals
+    the last row of a full prefill of tokens 0..N (the cache is exactly what
+    incremental decoding needs), and its K/V rows equal that prefill's row N.
+    GQA and MHA shapes."""
+    for shape in (TINY, ModelShape(2, 256, 14, 2, 128, 512, vocab=512)):
+        case = make_case(shape, (50, 31), 9, seed=5)
+        x = case.x0
+        n = x.shape[0] - 1
+        k_ctx, v_ctx, _ = oracle.prefill(case.weights, shape, x[:n])
+        k_all, v_all, outs = oracle.prefill(case.weights, shape, x)
+        h, kn, vn = oracle.decode_step(case.weights, shape, x[n], k_ctx, v_ctx, n)
+        assert np.max(np.abs(h - outs[-1][n])) <= 1e-10 * np.max(np.abs(outs[-1][n]))
+        assert np.max(np.abs(kn - k_all[:, n])) <= 1e-10 * np.max(np.abs(k_all[:, n]))
+        assert np.max(np.abs(vn - v_all[:, n])) <= 1e-10 * np.max(np.abs(v_all[:, n]))
+    # no context at all: the token attends to itself only (a one-token prefill)
+    h0, _, _ = oracle.decode_step(case.weights, shape, x[0], k_ctx[:, :0], v_ctx[:, :0], 0)
+    _, _, o1 = oracle.prefill(case.weights, shape, x[:1])
+    assert np.allclose(h0, o1[-1][0], rtol=0, atol=1e-12 * np.max(np.abs(o1[-1][0])))
+
+
+def test_lm_head_vs_library():
+    rng = np.random.default_rng(51)
+    x = rng.standard_normal((3, 64))
+    g = rng.uniform(0.5, 1.5, 64)
+    w = rng.standard_normal((100, 64)) * 0.02
+    xt = torch.from_numpy(x)
+    want = torch.nn.functional.rms_norm(xt, (64,), torch.from_numpy(g), eps=1e-5) @ \
+        torch.from_numpy(w).T.contiguous()
+    assert np.allclose(oracle.lm_head(x, g, w, 1e-5), want.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_argmax_first_brute_force():
+    rng = np.random.default_rng(52)
+    for _ in range(300):
+        v = rng.integers(-3, 4, size=int(rng.integers(1, 9))).astype(np.float64)
+        if rng.random() < 0.2:
+            v[rng.integers(0, v.size)] = np.nan
+        best = None
+        for i, x in enumerate(v):       # NaN first, then larger, then earlier
+            key = (0 if np.isnan(x) else 1, 0.0 if np.isnan(x) else -x, i)
+            best = key if best is None or key < best else best
+        assert oracle.argmax_first(v) == best[2]
+    assert oracle.argmax_first(np.array([1.0, 3.0, 3.0])) == 1
+    assert oracle.argmax_first(np.array([-np.inf, -np.inf])) == 0
