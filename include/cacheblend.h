@@ -234,6 +234,34 @@ void cb_plan_destroy(cb_plan* plan);
 cb_status cb_prefill(cb_model* model, const void* x0, int32_t n_tokens, int32_t pos0,
                      void* k_out, void* v_out, float* hidden_out, void* stream);
 
+/* ------------------------------------------------------------- first token
+ * What the fused cache is used for next (CacheBlend explainer (abeam.tech),
+ * "用語解説": the KV cache spares generation from recomputing past tokens;
+ * TTFT is the time to the first output token).
+ *
+ * cb_lm_head: for each of `rows` rows of x (device float32 [rows][d], e.g.
+ * the last row of hidden_out), logits[r] = W_lm rmsnorm(x[r]; final_norm)
+ * (device float32 [rows][vocab]); final_norm [d] and w_lm [vocab][d] are
+ * device pointers in the model dtype.  argmax (device int32 [rows] or
+ * NULL): index of the largest logit, NaN above all, smallest index among
+ * equals.
+ *
+ * cb_decode_step: one more token through every layer on top of a fused
+ * cache.  x: device [d] model dtype (the new token's embedding) at position
+ * n_ctx; fused_k / fused_v: device, layer l's rows 0..n_ctx-1 at element
+ * l * layer_rows * H_kv*d_head (layer_rows >= n_ctx; a request inside a
+ * batch passes its first row and the batch's total rows).  Per layer the
+ * token's RoPE'd key and its value are written to k_new / v_new (device
+ * [L][H_kv][d_head], model dtype), and it attends over the n_ctx cached
+ * keys plus its own.  hidden_out: device float32 [d], the last layer's
+ * output row (before the final norm). */
+cb_status cb_lm_head(cb_model* model, const float* x, int32_t rows, const void* final_norm,
+                     const void* w_lm, int32_t vocab, float* logits, int32_t* argmax,
+                     void* stream);
+cb_status cb_decode_step(cb_model* model, const void* x, int32_t n_ctx, const void* fused_k,
+                         const void* fused_v, int64_t layer_rows, void* k_new, void* v_new,
+                         float* hidden_out, void* stream);
+
 /* ------------------------------------------------------------- batches
  * Several requests fused in one call (the serving case of the CacheBlend
  * explainer (0h-n0), section "vLLM統合": many RAG requests whose contexts
@@ -385,6 +413,8 @@ typedef enum cb_kernel_class {
     CB_K_GEMM_O,
     CB_K_GEMM_GATEUP,
     CB_K_GEMM_DOWN,
+    CB_K_DECODE_GEMV,   /* decode step and LM head matrix-vector products */
+    CB_K_DECODE_ATTN,   /* decode-step attention over the fused cache     */
     CB_K_COUNT
 } cb_kernel_class;
 

@@ -90,7 +90,8 @@ class cb_cache_stat(ctypes.Structure):
 
 
 KERNEL_CLASSES = ("rotate", "rmsnorm", "gemm_qkv", "deviation", "select", "scatter",
-                  "attention", "gemm_o", "gemm_gateup", "gemm_down")
+                  "attention", "gemm_o", "gemm_gateup", "gemm_down", "decode_gemv",
+                  "decode_attention")
 
 
 def _sig(name, res, *args):
@@ -125,6 +126,9 @@ _fn = {
     "cb_cache_stats": (ctypes.c_int, _c_p, _P(cb_cache_stat)),
     "cb_cache_replay": (ctypes.c_int, _c_i64, _c_i32, _P(_c_i32), _P(ctypes.c_uint64),
                         _P(_c_i64), _P(_c_i32), _P(ctypes.c_uint64), _P(_c_i32)),
+    "cb_lm_head": (ctypes.c_int, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_p),
+    "cb_decode_step": (ctypes.c_int, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_i64, _c_p, _c_p, _c_p,
+                       _c_p),
     "cb_profile_enable": (ctypes.c_int, _c_p, _c_i32),
     "cb_profile_read": (ctypes.c_int, _c_p, _P(cb_kernel_stat)),
     "cb_rope_rerotate": (ctypes.c_int, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
@@ -362,6 +366,22 @@ class Plan:
 def cb_prefill(model, x0, n_tokens, pos0, k_out, v_out, hidden_out=None, stream=None):
     _check(RAW["cb_prefill"](model.handle, _ptr(x0), n_tokens, pos0, _ptr(k_out), _ptr(v_out),
                              _ptr(hidden_out), _stream(stream)))
+
+
+# ------------------------------------------------------------------ first token
+def cb_lm_head(model, x, rows, final_norm, w_lm, vocab, logits, argmax=None, stream=None):
+    """logits [rows][vocab] = W_lm rmsnorm(x); argmax (int32 [rows]) optional."""
+    _check(RAW["cb_lm_head"](model.handle, _ptr(x), rows, _ptr(final_norm), _ptr(w_lm), vocab,
+                             _ptr(logits), _ptr(argmax), _stream(stream)))
+
+
+def cb_decode_step(model, x, n_ctx, fused_k, fused_v, layer_rows, k_new, v_new, hidden_out,
+                   stream=None):
+    """One token (embedding x) at position n_ctx through every layer over the
+    fused cache; writes its K/V per layer and the last layer's row."""
+    _check(RAW["cb_decode_step"](model.handle, _ptr(x), n_ctx, _ptr(fused_k), _ptr(fused_v),
+                                 layer_rows, _ptr(k_new), _ptr(v_new), _ptr(hidden_out),
+                                 _stream(stream)))
 
 
 # ------------------------------------------------------------------ chunk store

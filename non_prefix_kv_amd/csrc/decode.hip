@@ -1,0 +1,343 @@
+// First token and one decode step on a fused cache: matrix-vector products
+// for one row, a split-key attention of one query over the fused keys, and
+// an argmax over the vocabulary.
+//
+// The decode step is what the fused cache is for: the CacheBlend explainer
+// (abeam.tech), section "用語解説", describes the KV cache as what lets
+// generation avoid recomputing past tokens, and TTFT as the time until the
+// first output token, which the prefill (here the fusion) dominates.
+//
+// Everything here reads each weight (or cached key / value) once per step,
+// so it is bound by HBM bandwidth: every wave streams whole contiguous weight
+// rows with 16-byte loads, many waves per CU keep enough bytes in flight, and
+// the epilogues (RoPE, residual, SwiGLU) run on the reduced dot products.
+#include "kernels.h"
+
+namespace cb {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / 64;
+constexpr int kSegKeys = 256;              // keys per decode-attention workgroup
+
+// One wave computes two dot products of length K between x and weight rows
+// (a pair of output columns, or gate and up rows of one SwiGLU column).
+template <typename T>
+__device__ __forceinline__ void dot2(const T* __restrict__ x, const T* __restrict__ wa,
+                                     const T* __restrict__ wb, int K, int lane, float& sa,
+                                     float& sb) {
+    float a = 0.f, b = 0.f;
+#pragma unroll 2
+    for (int k = lane * 8; k < K; k += 512) {
+        float xv[8], av[8], bv[8];
+        Vec8<T>::load(x + k, xv);
+        Vec8<T>::load(wa + k, av);
+        if (wb) Vec8<T>::load(wb + k, bv);
+        else
+#pragma unroll
+            for (int i = 0; i < 8; ++i) bv[i] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            a += xv[i] * av[i];
+            b += xv[i] * bv[i];
+        }
+    }
+    sa = warp_sum(a);
+    sb = warp_sum(b);
+}
+
+template <typename T, int EPI>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
+    const int lane = threadIdx.x & 63;
+    const int u = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    const int units = EPI == EPI_SWIGLU ? g.N : (g.N + 1) / 2;
+    if (u >= units) return;
+    const T* x = static_cast<const T*>(g.x);
+    const int64_t K = g.K;
+    if constexpr (EPI == EPI_SWIGLU) {
+        float gt, up;
+        dot2(x, static_cast<const T*>(g.b0) + u * K, static_cast<const T*>(g.b1) + u * K, g.K,
+             lane, gt, up);
+        if (lane == 0) static_cast<T*>(g.out0)[u] = from_f32<T>(gt / (1.f + __expf(-gt)) * up);
+        return;
+    } else {
+        const int r0 = 2 * u;
+        const bool two = r0 + 1 < g.N;
+        const T* w;
+        int local;
+        void* out;
+        bool rope = false;
+        if (EPI == EPI_QKV && r0 >= g.n0 + g.n1) {
+            w = static_cast<const T*>(g.b2); local = r0 - g.n0 - g.n1; out = g.out2;
+        } else if (EPI == EPI_QKV && r0 >= g.n0) {
+            w = static_cast<const T*>(g.b1); local = r0 - g.n0; out = g.out1; rope = true;
+        } else {
+            w = static_cast<const T*>(g.b0); local = r0; out = g.out0; rope = EPI == EPI_QKV;
+        }
+        float a, b;
+        dot2(x, w + local * K, two ? w + (local + 1) * K : nullptr, g.K, lane, a, b);
+        if (lane != 0) return;
+        if constexpr (EPI == EPI_QKV) {
+            float y0 = a, y1 = b;
+            if (rope) {
+                const float2 cs = g.rope.tab[(int64_t)g.pos * g.rope.half + ((local % g.head_dim) >> 1)];
+                y0 = a * cs.x - b * cs.y;
+                y1 = a * cs.y + b * cs.x;
+            }
+            static_cast<T*>(out)[local] = from_f32<T>(y0);
+            static_cast<T*>(out)[local + 1] = from_f32<T>(y1);
+        } else {
+            float* o = static_cast<float*>(g.out0);
+            if (EPI == EPI_RESID) {
+                a += g.resid[r0];
+                if (two) b += g.resid[r0 + 1];
+            }
+            o[r0] = a;
+            if (two) o[r0 + 1] = b;
+        }
+    }
+}
+
+// Order of the argmax: larger first, NaN above everything, smaller index
+// first among equals (so the result is unique).
+__device__ __forceinline__ bool better(float a, int ia, float b, int ib) {
+    const bool na = a != a, nb = b != b;
+    if (na != nb) return na;
+    if (!na && a != b) return a > b;
+    return ia < ib;
+}
+
+__global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ v, int n,
+                                                      int64_t stride, int* __restrict__ out) {
+    __shared__ float bv[16];
+    __shared__ int bi[16];
+    const float* row = v + blockIdx.x * stride;
+    float best = -INFINITY;
+    int idx = n;                       // sentinel: loses to every real entry
+    for (int i = threadIdx.x; i < n; i += 1024)
+        if (idx == n || better(row[i], i, best, idx)) { best = row[i]; idx = i; }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ob = __shfl_xor(best, o, 64);
+        const int oi = __shfl_xor(idx, o, 64);
+        if (oi != n && (idx == n || better(ob, oi, best, idx))) { best = ob; idx = oi; }
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) { bv[w] = best; bi[w] = idx; }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        for (int k = 1; k < 16; ++k)
+            if (bi[k] != n && (bi[0] == n || better(bv[k], bi[k], bv[0], bi[0]))) {
+                bv[0] = bv[k];
+                bi[0] = bi[k];
+            }
+        out[blockIdx.x] = bi[0] == n ? 0 : bi[0];
+    }
+}
+
+// Split-key attention of one query row (all query heads) over n_ctx cached
+// keys plus the step's own key.  Grid (kv heads, key segments of 256); the
+// G query heads that share a KV head are handled together, so each cached
+// key and value row is read once.  A key row is spread over DH/8 lanes (8
+// elements each); a wave takes 64/(DH/8) keys per instruction.  Output:
+// per (query head, segment) the running maximum, the sum of exponentials and
+// the unnormalized output, merged by decode_combine_kernel.
+template <typename T, int DH, int GMAX>
+__global__ __launch_bounds__(kThreads) void decode_attention_kernel(DecodeAttnArgs a) {
+    constexpr int LPK = DH / 8, KPI = 64 / LPK, PER_WAVE = kSegKeys / kWaves;
+    __shared__ float sc[GMAX][kSegKeys];
+    __shared__ float red[GMAX][kWaves];
+    __shared__ float osum[kWaves][GMAX][DH];
+    const int h = blockIdx.x, seg = blockIdx.y, nseg = gridDim.y;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int sub = lane / LPK, li = lane % LPK;
+    const int G = GMAX == 1 ? 1 : a.group;
+    const int kvd = a.n_kv_heads * DH;
+    const int n_keys = a.n_ctx + 1;
+    const int j0 = seg * kSegKeys;
+    float q[GMAX][8];
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+        if (g < G) {
+            Vec8<T>::load(static_cast<const T*>(a.q) + (int64_t)(h * G + g) * DH + li * 8, q[g]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) q[g][i] *= a.scale;
+        }
+    }
+    auto key_row = [&](const void* cache, const void* fresh, int j) -> const T* {
+        return j < a.n_ctx ? static_cast<const T*>(cache) + (int64_t)j * kvd + h * DH + li * 8
+                           : static_cast<const T*>(fresh) + h * DH + li * 8;
+    };
+    // scores
+    for (int it = 0; it < PER_WAVE / KPI; ++it) {
+        const int jl = w * PER_WAVE + it * KPI + sub, j = j0 + jl;
+        const bool ok = j < n_keys;
+        float kv[8];
+        if (ok) Vec8<T>::load(key_row(a.k, a.k_new, j), kv);
+#pragma unroll
+        for (int g = 0; g < GMAX; ++g) {
+            if (g >= G) break;
+            float s = 0.f;
+            if (ok)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) s += q[g][i] * kv[i];
+#pragma unroll
+            for (int o = 1; o < LPK; o <<= 1) s += __shfl_xor(s, o, 64);
+            if (li == 0) sc[g][jl] = ok ? s : -INFINITY;
+        }
+    }
+    __syncthreads();
+    // softmax statistics of the segment (thread t owns key t)
+    const int t = threadIdx.x;
+    float m[GMAX], l[GMAX];
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+        if (g >= G) break;
+        float v = sc[g][t];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+        if (lane == 0) red[g][w] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+        if (g >= G) break;
+        m[g] = fmaxf(fmaxf(red[g][0], red[g][1]), fmaxf(red[g][2], red[g][3]));
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+        if (g >= G) break;
+        const float s = sc[g][t];
+        const float p = s == -INFINITY ? 0.f : __expf(s - m[g]);
+        sc[g][t] = p;
+        float v = p;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+        if (lane == 0) red[g][w] = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+        if (g >= G) break;
+        l[g] = red[g][0] + red[g][1] + red[g][2] + red[g][3];
+    }
+    // values
+    float o[GMAX][8];
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[g][i] = 0.f;
+    for (int it = 0; it < PER_WAVE / KPI; ++it) {
+        const int jl = w * PER_WAVE + it * KPI + sub, j = j0 + jl;
+        if (j >= n_keys) continue;
+        float vv[8];
+        Vec8<T>::load(key_row(a.v, a.v_new, j), vv);
+#pragma unroll
+        for (int g = 0; g < GMAX; ++g) {
+            if (g >= G) break;
+            const float p = sc[g][jl];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[g][i] += p * vv[i];
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < GMAX; ++g) {
+        if (g >= G) break;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int off = LPK; off < 64; off <<= 1) o[g][i] += __shfl_xor(o[g][i], off, 64);
+        if (sub == 0)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) osum[w][g][li * 8 + i] = o[g][i];
+    }
+    __syncthreads();
+    for (int e = t; e < G * DH; e += kThreads) {
+        const int g = e / DH, d = e % DH;
+        const float sum = osum[0][g][d] + osum[1][g][d] + osum[2][g][d] + osum[3][g][d];
+        const int64_t slot = (int64_t)(h * G + g) * nseg + seg;
+        a.part_o[slot * DH + d] = sum;
+        if (d == 0) {
+            a.part_ml[2 * slot] = m[g];
+            a.part_ml[2 * slot + 1] = l[g];
+        }
+    }
+}
+
+template <typename T>
+__global__ void decode_combine_kernel(DecodeAttnArgs a, int nseg, int dh) {
+    const int hq = blockIdx.x;
+    for (int d = threadIdx.x; d < dh; d += blockDim.x) {
+        float mx = -INFINITY;
+        for (int s = 0; s < nseg; ++s) mx = fmaxf(mx, a.part_ml[2 * ((int64_t)hq * nseg + s)]);
+        float num = 0.f, den = 0.f;
+        for (int s = 0; s < nseg; ++s) {
+            const int64_t slot = (int64_t)hq * nseg + s;
+            const float ms = a.part_ml[2 * slot];
+            const float wgt = ms == -INFINITY ? 0.f : __expf(ms - mx);
+            den += wgt * a.part_ml[2 * slot + 1];
+            num += wgt * a.part_o[slot * dh + d];
+        }
+        static_cast<T*>(a.out)[(int64_t)hq * dh + d] = from_f32<T>(num / den);
+    }
+}
+
+template <typename T>
+hipError_t gemv_t(int epi, const GemvArgs& g, hipStream_t s) {
+    const int units = epi == EPI_SWIGLU ? g.N : (g.N + 1) / 2;
+    const dim3 grid((units + kWaves - 1) / kWaves), block(kThreads);
+    switch (epi) {
+        case EPI_STORE_F32: hipLaunchKernelGGL((gemv_kernel<T, EPI_STORE_F32>), grid, block, 0, s, g); break;
+        case EPI_QKV: hipLaunchKernelGGL((gemv_kernel<T, EPI_QKV>), grid, block, 0, s, g); break;
+        case EPI_RESID: hipLaunchKernelGGL((gemv_kernel<T, EPI_RESID>), grid, block, 0, s, g); break;
+        case EPI_SWIGLU: hipLaunchKernelGGL((gemv_kernel<T, EPI_SWIGLU>), grid, block, 0, s, g); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int DH>
+hipError_t decode_attn_t(const DecodeAttnArgs& a, hipStream_t s) {
+    const int nseg = (a.n_ctx + 1 + kSegKeys - 1) / kSegKeys;
+    const dim3 grid(a.n_kv_heads, nseg);
+    if (a.group == 1)
+        hipLaunchKernelGGL((decode_attention_kernel<T, DH, 1>), grid, dim3(kThreads), 0, s, a);
+    else
+        hipLaunchKernelGGL((decode_attention_kernel<T, DH, 8>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(decode_combine_kernel<T>, dim3(a.n_kv_heads * a.group), dim3(DH), 0, s, a,
+                       nseg, DH);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_gemv(int dtype, int epi, const GemvArgs& g, hipStream_t s) {
+    if (g.N <= 0) return hipSuccess;
+    if (g.K <= 0 || g.K % 8) return hipErrorInvalidValue;
+    if (epi == EPI_QKV && (g.n0 % 2 || g.n1 % 2 || g.head_dim % 2 || !g.rope.tab || g.pos < 0 ||
+                           g.pos >= g.rope.n_pos || g.rope.half != g.head_dim / 2))
+        return hipErrorInvalidValue;
+    return dtype == BF16 ? gemv_t<bf16>(epi, g, s) : gemv_t<float>(epi, g, s);
+}
+
+hipError_t launch_argmax(const float* v, int rows, int n, int64_t stride, int* out, hipStream_t s) {
+    if (rows <= 0 || n <= 0) return hipSuccess;
+    hipLaunchKernelGGL(argmax_kernel, dim3(rows), dim3(1024), 0, s, v, n, stride, out);
+    return hipGetLastError();
+}
+
+int decode_attention_segments(int n_ctx) { return (n_ctx + 1 + kSegKeys - 1) / kSegKeys; }
+
+hipError_t launch_decode_attention(int dtype, const DecodeAttnArgs& a, hipStream_t s) {
+    if (a.n_ctx < 0 || a.group < 1 || a.group > 8 || !a.part_o || !a.part_ml)
+        return hipErrorInvalidValue;
+    if (a.head_dim == 128)
+        return dtype == BF16 ? decode_attn_t<bf16, 128>(a, s) : decode_attn_t<float, 128>(a, s);
+    if (a.head_dim == 64)
+        return dtype == BF16 ? decode_attn_t<bf16, 64>(a, s) : decode_attn_t<float, 64>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace cb

@@ -182,6 +182,55 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& g, hipStream_t s);
 
+// ------------------------------------------------------------------ decode
+// One-row products y = W x for a decode step (W [N][K] row-major, x [K] in
+// the model dtype), with the GEMM epilogues: EPI_QKV (q | k | v rows, RoPE
+// at `pos` on q and k, model dtype outputs out0/out1/out2), EPI_RESID and
+// EPI_STORE_F32 (f32 out0, + resid), EPI_SWIGLU (SiLU(b0 x) * (b1 x), N
+// columns, model dtype out0).
+struct GemvArgs {
+    const void* x;
+    const void* b0;
+    const void* b1;
+    const void* b2;
+    int N, K;
+    int n0, n1;
+    void* out0;
+    void* out1;
+    void* out2;
+    const float* resid;
+    RopeTab rope;
+    int pos;
+    int head_dim;
+};
+hipError_t launch_gemv(int dtype, int epi, const GemvArgs& g, hipStream_t s);
+
+// out[r] = argmax of row r of v ([rows][n], row stride `stride`): larger
+// first, NaN above all, smaller index among equals.
+hipError_t launch_argmax(const float* v, int rows, int n, int64_t stride, int* out, hipStream_t s);
+
+// Attention of one query row (q [Hq][dh]) at position n_ctx over keys
+// 0..n_ctx-1 of k / v ([n_ctx][Hkv][dh], model dtype) and its own key and
+// value k_new / v_new ([Hkv][dh]); out [Hq][dh].  part_o [Hq][segments][dh]
+// and part_ml [Hq][segments][2]: float scratch for the key segments.
+struct DecodeAttnArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* k_new;
+    const void* v_new;
+    void* out;
+    int n_ctx;
+    int n_kv_heads;
+    int group;          // query heads per KV head
+    int head_dim;
+    float scale;
+    float* part_o;
+    float* part_ml;
+};
+int decode_attention_segments(int n_ctx);
+hipError_t launch_decode_attention(int dtype, const DecodeAttnArgs& a, hipStream_t s);
+
 // ------------------------------------------------------------------ attention
 // Causal attention of query rows over one request's keys.  A request range
 // covers output rows q0..q0+nq-1 (row i reads q row qidx[i], qidx null: i,

@@ -1231,6 +1231,140 @@ cb_status cb_prefill(cb_model* m, const void* x0, int32_t n_tokens, int32_t pos0
     return st;
 }
 
+cb_status cb_lm_head(cb_model* m, const float* x, int32_t rows, const void* final_norm,
+                     const void* w_lm, int32_t vocab, float* logits, int32_t* argmax,
+                     void* stream) {
+    if (!m || !x || !final_norm || !w_lm || !logits) return fail(CB_E_INVALID, "NULL argument");
+    if (rows <= 0 || vocab <= 0) return fail(CB_E_INVALID, "rows %d, vocab %d", rows, vocab);
+    const cb_model_cfg& c = m->cfg;
+    if (!aligned_to(x, 16) || !aligned_to(w_lm, 16) || !aligned_to(final_norm, 16))
+        return fail(CB_E_SHAPE, "x, final_norm and w_lm must be 16-byte aligned");
+    const hipStream_t st = as_stream(stream);
+    const size_t es = m->es();
+    void* hn = nullptr;
+    if (hipMallocFromPoolAsync(&hn, (size_t)rows * c.d_model * es, m->pool, st) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(CB_E_OOM, "LM head scratch");
+    }
+    cb_status status = CB_OK;
+    auto run = [&]() -> cb_status {
+        CB_HIP(launch_rmsnorm(F32, x, nullptr, c.dtype, final_norm, hn, nullptr, rows, c.d_model,
+                              c.rms_eps, st));
+        for (int r = 0; r < rows; ++r) {
+            GemvArgs g{};
+            g.x = (const char*)hn + (size_t)r * c.d_model * es;
+            g.b0 = w_lm;
+            g.N = vocab;
+            g.K = c.d_model;
+            g.out0 = logits + (int64_t)r * vocab;
+            Span sp(m, CB_K_DECODE_GEMV, st, 2.0 * vocab * c.d_model,
+                    (double)vocab * c.d_model * es + vocab * 4.0);
+            CB_HIP(launch_gemv(c.dtype, EPI_STORE_F32, g, st));
+        }
+        if (argmax) CB_HIP(launch_argmax(logits, rows, vocab, vocab, argmax, st));
+        return CB_OK;
+    };
+    status = run();
+    (void)hipFreeAsync(hn, st);
+    return status;
+}
+
+cb_status cb_decode_step(cb_model* m, const void* x, int32_t n_ctx, const void* fused_k,
+                         const void* fused_v, int64_t layer_rows, void* k_new, void* v_new,
+                         float* hidden_out, void* stream) {
+    if (!m || !x || !k_new || !v_new || !hidden_out) return fail(CB_E_INVALID, "NULL argument");
+    if (n_ctx < 0 || layer_rows < n_ctx || (n_ctx > 0 && (!fused_k || !fused_v)))
+        return fail(CB_E_INVALID, "n_ctx %d, layer_rows %lld", n_ctx, (long long)layer_rows);
+    const cb_model_cfg& c = m->cfg;
+    const int G = c.n_q_heads / c.n_kv_heads;
+    if (G > 8) return fail(CB_E_UNSUPPORTED, "more than 8 query heads per KV head");
+    if (!aligned_to(x, 16) || !aligned_to(fused_k, 16) || !aligned_to(fused_v, 16) ||
+        !aligned_to(k_new, 16) || !aligned_to(v_new, 16) || !aligned_to(hidden_out, 16))
+        return fail(CB_E_SHAPE, "buffers must be 16-byte aligned");
+    cb_status st0 = ensure_rope(m, n_ctx + 1);
+    if (st0 != CB_OK) return st0;
+    const hipStream_t st = as_stream(stream);
+    const size_t es = m->es(), d = c.d_model, qd = m->qd(), kvd = m->kvd(), F = c.ffn_dim;
+    // split-attention partials: [Hq][segments][d_head] outputs, [Hq][segments][2] statistics
+    const size_t nseg = (size_t)decode_attention_segments(n_ctx);
+    size_t off = 0;
+    auto take = [&](size_t b) { const size_t o = off; off = align_up(off + b, 256); return o; };
+    const size_t oX = take(d * 4), oH = take(d * 4), oN = take(d * es), oQ = take(qd * es),
+                 oA = take(qd * es), oF = take(F * es),
+                 oP = take((size_t)c.n_q_heads * nseg * c.head_dim * 4),
+                 oM = take((size_t)c.n_q_heads * nseg * 2 * 4);
+    char* ws = nullptr;
+    if (hipMallocFromPoolAsync((void**)&ws, off, m->pool, st) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(CB_E_OOM, "decode scratch of %zu bytes", off);
+    }
+    float* X = (float*)(ws + oX);
+    float* Hres = (float*)(ws + oH);
+    void *Hn = ws + oN, *Q = ws + oQ, *att = ws + oA, *act = ws + oF;
+    const double ctx_bytes = 2.0 * (n_ctx + 1) * kvd * es;
+    auto run = [&]() -> cb_status {
+        for (int l = 0; l < c.n_layers; ++l) {
+            const cb_layer_weights& w = m->w[l];
+            const bool last = l + 1 == c.n_layers;
+            char* kl = (char*)k_new + (size_t)l * kvd * es;
+            char* vl = (char*)v_new + (size_t)l * kvd * es;
+            CB_HIP(launch_rmsnorm(l == 0 ? c.dtype : F32, l == 0 ? x : (const void*)X, nullptr,
+                                  c.dtype, w.attn_norm, Hn, l == 0 ? X : nullptr, 1, c.d_model,
+                                  c.rms_eps, st));
+            {
+                GemvArgs g{};
+                g.x = Hn; g.b0 = w.wq; g.b1 = w.wk; g.b2 = w.wv;
+                g.N = (int)(qd + 2 * kvd); g.K = (int)d; g.n0 = (int)qd; g.n1 = (int)kvd;
+                g.out0 = Q; g.out1 = kl; g.out2 = vl;
+                g.rope = m->rope; g.pos = n_ctx; g.head_dim = c.head_dim;
+                Span sp(m, CB_K_DECODE_GEMV, st, 2.0 * g.N * d, ((double)g.N * d + g.N) * es);
+                CB_HIP(launch_gemv(c.dtype, EPI_QKV, g, st));
+            }
+            {
+                DecodeAttnArgs a{};
+                a.q = Q;
+                a.k = (const char*)fused_k + (size_t)l * layer_rows * kvd * es;
+                a.v = (const char*)fused_v + (size_t)l * layer_rows * kvd * es;
+                a.k_new = kl; a.v_new = vl; a.out = att;
+                a.n_ctx = n_ctx; a.n_kv_heads = c.n_kv_heads; a.group = G;
+                a.head_dim = c.head_dim;
+                a.scale = 1.0f / sqrtf((float)c.head_dim);
+                a.part_o = (float*)(ws + oP);
+                a.part_ml = (float*)(ws + oM);
+                Span sp(m, CB_K_DECODE_ATTN, st, 4.0 * qd * (n_ctx + 1), ctx_bytes);
+                CB_HIP(launch_decode_attention(c.dtype, a, st));
+            }
+            {
+                GemvArgs g{};
+                g.x = att; g.b0 = w.wo; g.N = (int)d; g.K = (int)qd;
+                g.out0 = Hres; g.resid = X;
+                Span sp(m, CB_K_DECODE_GEMV, st, 2.0 * d * qd, (double)d * qd * es + d * 8.0);
+                CB_HIP(launch_gemv(c.dtype, EPI_RESID, g, st));
+            }
+            CB_HIP(launch_rmsnorm(F32, Hres, nullptr, c.dtype, w.mlp_norm, Hn, nullptr, 1,
+                                  c.d_model, c.rms_eps, st));
+            {
+                GemvArgs g{};
+                g.x = Hn; g.b0 = w.w_gate; g.b1 = w.w_up; g.N = (int)F; g.K = (int)d;
+                g.out0 = act;
+                Span sp(m, CB_K_DECODE_GEMV, st, 4.0 * F * d, 2.0 * F * d * es + F * es);
+                CB_HIP(launch_gemv(c.dtype, EPI_SWIGLU, g, st));
+            }
+            {
+                GemvArgs g{};
+                g.x = act; g.b0 = w.w_down; g.N = (int)d; g.K = (int)F;
+                g.out0 = last ? hidden_out : X; g.resid = Hres;
+                Span sp(m, CB_K_DECODE_GEMV, st, 2.0 * d * F, (double)d * F * es + d * 8.0);
+                CB_HIP(launch_gemv(c.dtype, EPI_RESID, g, st));
+            }
+        }
+        return CB_OK;
+    };
+    const cb_status status = run();
+    (void)hipFreeAsync(ws, st);
+    return status;
+}
+
 cb_status cb_profile_enable(cb_model* m, int32_t enable) {
     if (!m) return fail(CB_E_INVALID, "model is NULL");
     if (enable) {

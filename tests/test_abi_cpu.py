@@ -114,6 +114,8 @@ def test_kernel_entry_validation(npk):
                                     1e4, None) == npk.CB_E_SHAPE
     assert R["cb_rmsnorm"](npk.CB_F32, None, npk.CB_F32, None, None, 3, 8, 1e-5,
                            None) == npk.CB_E_INVALID
+    assert R["cb_lm_head"](None, 16, 1, 16, 16, 10, 16, None, None) == npk.CB_E_INVALID
+    assert R["cb_decode_step"](None, 16, 4, 16, 16, 4, 16, 16, 16, None) == npk.CB_E_INVALID
     # NULL handles are rejected, never dereferenced
     assert R["cb_fetch_kv"](None, 0) == npk.CB_E_INVALID
     assert R["cb_prefill_layer"](None, 0) == npk.CB_E_INVALID
