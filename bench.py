@@ -53,6 +53,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--no-full-compare", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the first-token (LM head) and decode-step measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
     ap.add_argument("--trace-summary", metavar="CSV",
@@ -88,19 +90,20 @@ def _short(name):
         n = int(m.group(1))
         ident = rest[len(m.group(1)):len(m.group(1)) + n]
         targs = rest[len(m.group(1)) + n:]
-        targs = targs[1:targs.index("EE")] if targs.startswith("I") and "EE" in targs else ""
         out = []
-        while targs:
-            if targs.startswith("DF16b"):
-                out.append("bf16")
-                targs = targs[5:]
-            elif targs.startswith("Li"):
-                e = targs.index("E")
-                out.append(targs[2:e])
-                targs = targs[e + 1:]
-            else:
-                out.append({"f": "f32", "i": "int"}.get(targs[0], targs[0]))
-                targs = targs[1:]
+        if targs.startswith("I"):          # template arguments up to the closing E
+            targs = targs[1:]
+            while targs and not targs.startswith("E"):
+                if targs.startswith("DF16b"):
+                    out.append("bf16")
+                    targs = targs[5:]
+                elif targs.startswith("Li") and "E" in targs:
+                    e = targs.index("E")
+                    out.append(targs[2:e])
+                    targs = targs[e + 1:]
+                else:
+                    out.append({"f": "f32", "i": "int"}.get(targs[0], targs[0]))
+                    targs = targs[1:]
         return f"{ident}<{', '.join(out)}>" if out else ident
     n = name.replace("void ", "").replace("cb::(anonymous namespace)::", "")
     return re.sub(r"\(.*\)$", "", n)
@@ -188,7 +191,6 @@ def make_inputs(npk, w, seed, torch, kv_format="plain"):
     model, layers, emb = make_model(npk, S, seed, torch)
     tok = torch.from_numpy(make_tokens(S, w.n_tokens, seed)).to(dev)
     x0 = emb[tok].contiguous()
-    del emb
     chunks = []
     for o, n in zip(w.offsets, w.chunk_lens):
         k = torch.empty((S.n_layers, n, S.n_kv_heads, S.head_dim), dtype=bf, device=dev)
@@ -207,7 +209,7 @@ def make_inputs(npk, w, seed, torch, kv_format="plain"):
         c["on_host"] = int(w.kv_on_host)
         chunks.append(c)
     torch.cuda.synchronize()
-    return model, layers, x0, chunks
+    return model, layers, x0, chunks, emb       # the embedding feeds the decode step
 
 
 def make_batch_inputs(npk, w, seed, torch, pool_on_host, kv_format="plain"):
@@ -749,6 +751,71 @@ def main_batched(args, npk, torch, w):
 
 
 # ------------------------------------------------------------------ main
+def first_token_and_decode(args, npk, torch, w, model, emb, hid, fk, fv, sched, blend_ms):
+    """TTFT = blend + LM head on the last prompt row; then one decode step of
+    that token over the fused cache (HIP events per kernel class in a
+    separate pass).  LM head weights: N(0, 0.02) like the other weights,
+    final norm gain 1."""
+    S = w.shape
+    L, N = S.n_layers, w.n_tokens
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(args.seed * 1_000_003 + 8)
+    w_lm = (torch.randn((S.vocab, S.d_model), generator=gen, device=dev) * 0.02).to(bf)
+    g_f = torch.ones(S.d_model, dtype=bf, device=dev)
+    logits = torch.empty((1, S.vocab), device=dev)
+    tok = torch.empty((1,), dtype=torch.int32, device=dev)
+    last = hid[w.n_suffix + sched[-1] - 1:].contiguous()
+    kn = torch.empty((L, S.n_kv_heads, S.head_dim), dtype=bf, device=dev)
+    vn = torch.empty_like(kn)
+    h1 = torch.empty((S.d_model,), device=dev)
+
+    def lm():
+        npk.cb_lm_head(model, last, 1, g_f, w_lm, S.vocab, logits, tok)
+
+    def decode():
+        npk.cb_decode_step(model, x_tok, N, fk, fv, N, kn, vn, h1)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / reps * 1e3
+
+    log("[bench] first token and one decode step")
+    lm_ms = timed(lm, 20)
+    x_tok = emb[tok.long()].reshape(-1).contiguous()
+    dec_ms = timed(decode, 20)
+    es = 2
+    w_bytes = L * (S.q_dim * S.d_model + 2 * S.kv_dim * S.d_model + S.d_model * S.q_dim
+                   + 3 * S.ffn_dim * S.d_model) * es
+    kv_bytes = L * 2 * (N + 1) * S.kv_dim * es
+    npk.cb_profile_enable(model, True)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        decode()
+    torch.cuda.synchronize()
+    st = npk.cb_profile_read(model)
+    npk.cb_profile_enable(model, False)
+    cls = {}
+    for k in ("decode_gemv", "decode_attention"):
+        e = st[k]
+        if e["launches"]:
+            cls[k] = {"launches_per_step": e["launches"] / 5, "ms_per_step": e["total_ms"] / 5,
+                      "gbs": e["bytes"] / (e["total_ms"] / 1e3) / 1e9,
+                      "frac_hbm": e["bytes"] / (e["total_ms"] / 1e3) / 8e12}
+    return {"ttft_ms": blend_ms + lm_ms,
+            "first_token": {"lm_head_ms": lm_ms, "token": int(tok.item()), "vocab": S.vocab},
+            "decode_step": {"ms": dec_ms, "algorithmic_bytes": w_bytes + kv_bytes,
+                            "gbs": (w_bytes + kv_bytes) / (dec_ms / 1e3) / 1e9,
+                            "frac_hbm": (w_bytes + kv_bytes) / (dec_ms / 1e3) / 8e12,
+                            "kernels": cls}}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -785,7 +852,7 @@ def main():
     S = w.shape
     N, Nc, L = w.n_tokens, w.n_chunk_tokens, S.n_layers
     log(f"[bench] workload {w.name}: building inputs")
-    model, layers, x0, chunks = make_inputs(npk, w, args.seed, torch, args.kv_format)
+    model, layers, x0, chunks, emb = make_inputs(npk, w, args.seed, torch, args.kv_format)
     kind = npk.CB_SCHED_GRADUAL if w.schedule_kind == "gradual" else npk.CB_SCHED_FIXED
     sched = npk.cb_schedule(Nc, w.r_bp, kind, L)
     dev = torch.device("cuda:0")
@@ -847,6 +914,9 @@ def main():
         out["kernels"] = kernels
         out["roofline"] = roofline(st, kernels, lambda k: recorded_traffic(k, args.workload)
                                    if args.kv_format == "plain" else None)
+
+    if not args.no_decode:
+        out.update(first_token_and_decode(args, npk, torch, w, model, emb, hid, fk, fv, sched, ms))
 
     if not args.no_full_compare:
         log("[bench] full recompute (r = 100%) comparison")

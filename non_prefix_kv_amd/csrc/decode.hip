@@ -19,17 +19,19 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kSegKeys = 256;              // keys per decode-attention workgroup
+constexpr int kSegKeys = 64;               // keys per decode-attention workgroup
 
-// One wave computes two dot products of length K between x and weight rows
-// (a pair of output columns, or gate and up rows of one SwiGLU column).
-template <typename T>
+// Two dot products of length K between x and weight rows wa, wb (a pair of
+// output columns, or the gate and up rows of one SwiGLU column), taken by
+// WPU waves together: wave `part` of them reads the 512-element pieces
+// part, part + WPU, ... of the rows.  Returns the wave's partial sums.
+template <typename T, int WPU>
 __device__ __forceinline__ void dot2(const T* __restrict__ x, const T* __restrict__ wa,
-                                     const T* __restrict__ wb, int K, int lane, float& sa,
-                                     float& sb) {
+                                     const T* __restrict__ wb, int K, int lane, int part,
+                                     float& sa, float& sb) {
     float a = 0.f, b = 0.f;
-#pragma unroll 2
-    for (int k = lane * 8; k < K; k += 512) {
+#pragma unroll 4
+    for (int k = part * 512 + lane * 8; k < K; k += 512 * WPU) {
         float xv[8], av[8], bv[8];
         Vec8<T>::load(x + k, xv);
         Vec8<T>::load(wa + k, av);
@@ -47,55 +49,74 @@ __device__ __forceinline__ void dot2(const T* __restrict__ x, const T* __restric
     sb = warp_sum(b);
 }
 
-template <typename T, int EPI>
+// A workgroup of 4 waves computes 4 / WPU units (WPU waves per unit, which
+// split K); a unit is a pair of output rows, or one SwiGLU column.  Few
+// output rows take WPU = 4 so that enough workgroups stream the weights.
+template <typename T, int EPI, int WPU>
 __global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
-    const int lane = threadIdx.x & 63;
-    const int u = blockIdx.x * kWaves + (threadIdx.x >> 6);
+    __shared__ float part_s[kWaves][2];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int u = blockIdx.x * (kWaves / WPU) + wave / WPU, part = wave % WPU;
     const int units = EPI == EPI_SWIGLU ? g.N : (g.N + 1) / 2;
-    if (u >= units) return;
+    const bool live = u < units;
     const T* x = static_cast<const T*>(g.x);
     const int64_t K = g.K;
+    const T* wa = nullptr;
+    const T* wb = nullptr;
+    int local = 0;
+    void* out = nullptr;
+    bool rope = false, two = true;
+    if (live) {
+        if constexpr (EPI == EPI_SWIGLU) {
+            wa = static_cast<const T*>(g.b0) + u * K;
+            wb = static_cast<const T*>(g.b1) + u * K;
+        } else {
+            const int r0 = 2 * u;
+            two = r0 + 1 < g.N;
+            const T* w;
+            if (EPI == EPI_QKV && r0 >= g.n0 + g.n1) {
+                w = static_cast<const T*>(g.b2); local = r0 - g.n0 - g.n1; out = g.out2;
+            } else if (EPI == EPI_QKV && r0 >= g.n0) {
+                w = static_cast<const T*>(g.b1); local = r0 - g.n0; out = g.out1; rope = true;
+            } else {
+                w = static_cast<const T*>(g.b0); local = r0; out = g.out0; rope = EPI == EPI_QKV;
+            }
+            wa = w + local * K;
+            wb = two ? w + (local + 1) * K : nullptr;
+        }
+    }
+    float a = 0.f, b = 0.f;
+    if (live) dot2<T, WPU>(x, wa, wb, g.K, lane, part, a, b);
+    if constexpr (WPU > 1) {
+        if (lane == 0) { part_s[wave][0] = a; part_s[wave][1] = b; }
+        __syncthreads();
+        if (part != 0) return;
+        for (int p = 1; p < WPU; ++p) {
+            a += part_s[wave + p][0];
+            b += part_s[wave + p][1];
+        }
+    }
+    if (!live || lane != 0) return;
     if constexpr (EPI == EPI_SWIGLU) {
-        float gt, up;
-        dot2(x, static_cast<const T*>(g.b0) + u * K, static_cast<const T*>(g.b1) + u * K, g.K,
-             lane, gt, up);
-        if (lane == 0) static_cast<T*>(g.out0)[u] = from_f32<T>(gt / (1.f + __expf(-gt)) * up);
-        return;
+        static_cast<T*>(g.out0)[u] = from_f32<T>(a / (1.f + __expf(-a)) * b);
+    } else if constexpr (EPI == EPI_QKV) {
+        float y0 = a, y1 = b;
+        if (rope) {
+            const float2 cs = g.rope.tab[(int64_t)g.pos * g.rope.half + ((local % g.head_dim) >> 1)];
+            y0 = a * cs.x - b * cs.y;
+            y1 = a * cs.y + b * cs.x;
+        }
+        static_cast<T*>(out)[local] = from_f32<T>(y0);
+        static_cast<T*>(out)[local + 1] = from_f32<T>(y1);
     } else {
         const int r0 = 2 * u;
-        const bool two = r0 + 1 < g.N;
-        const T* w;
-        int local;
-        void* out;
-        bool rope = false;
-        if (EPI == EPI_QKV && r0 >= g.n0 + g.n1) {
-            w = static_cast<const T*>(g.b2); local = r0 - g.n0 - g.n1; out = g.out2;
-        } else if (EPI == EPI_QKV && r0 >= g.n0) {
-            w = static_cast<const T*>(g.b1); local = r0 - g.n0; out = g.out1; rope = true;
-        } else {
-            w = static_cast<const T*>(g.b0); local = r0; out = g.out0; rope = EPI == EPI_QKV;
+        float* o = static_cast<float*>(g.out0);
+        if (EPI == EPI_RESID) {
+            a += g.resid[r0];
+            if (two) b += g.resid[r0 + 1];
         }
-        float a, b;
-        dot2(x, w + local * K, two ? w + (local + 1) * K : nullptr, g.K, lane, a, b);
-        if (lane != 0) return;
-        if constexpr (EPI == EPI_QKV) {
-            float y0 = a, y1 = b;
-            if (rope) {
-                const float2 cs = g.rope.tab[(int64_t)g.pos * g.rope.half + ((local % g.head_dim) >> 1)];
-                y0 = a * cs.x - b * cs.y;
-                y1 = a * cs.y + b * cs.x;
-            }
-            static_cast<T*>(out)[local] = from_f32<T>(y0);
-            static_cast<T*>(out)[local + 1] = from_f32<T>(y1);
-        } else {
-            float* o = static_cast<float*>(g.out0);
-            if (EPI == EPI_RESID) {
-                a += g.resid[r0];
-                if (two) b += g.resid[r0 + 1];
-            }
-            o[r0] = a;
-            if (two) o[r0 + 1] = b;
-        }
+        o[r0] = a;
+        if (two) o[r0 + 1] = b;
     }
 }
 
@@ -137,17 +158,20 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ 
 }
 
 // Split-key attention of one query row (all query heads) over n_ctx cached
-// keys plus the step's own key.  Grid (kv heads, key segments of 256); the
-// G query heads that share a KV head are handled together, so each cached
-// key and value row is read once.  A key row is spread over DH/8 lanes (8
-// elements each); a wave takes 64/(DH/8) keys per instruction.  Output:
-// per (query head, segment) the running maximum, the sum of exponentials and
-// the unnormalized output, merged by decode_combine_kernel.
+// keys plus the step's own key.  Grid (kv heads, key segments of 64); the G
+// query heads that share a KV head are handled together, so each cached key
+// and value row is read once.  A key row is spread over DH/8 lanes (8
+// elements each); each wave owns 16 keys and issues all of their K and V
+// loads before using them.  Output: per (query head, segment) the maximum,
+// the sum of exponentials and the unnormalized output, merged by
+// decode_combine_kernel.
 template <typename T, int DH, int GMAX>
 __global__ __launch_bounds__(kThreads) void decode_attention_kernel(DecodeAttnArgs a) {
     constexpr int LPK = DH / 8, KPI = 64 / LPK, PER_WAVE = kSegKeys / kWaves;
+    constexpr int ITERS = PER_WAVE / KPI;
+    static_assert(ITERS * KPI == PER_WAVE, "keys per wave");
     __shared__ float sc[GMAX][kSegKeys];
-    __shared__ float red[GMAX][kWaves];
+    __shared__ float stat[GMAX][2];
     __shared__ float osum[kWaves][GMAX][DH];
     const int h = blockIdx.x, seg = blockIdx.y, nseg = gridDim.y;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -155,7 +179,24 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(DecodeAttnAr
     const int G = GMAX == 1 ? 1 : a.group;
     const int kvd = a.n_kv_heads * DH;
     const int n_keys = a.n_ctx + 1;
-    const int j0 = seg * kSegKeys;
+    const int j0 = seg * kSegKeys + w * PER_WAVE;
+    auto row = [&](const void* cache, const void* fresh, int j) -> const T* {
+        return j < a.n_ctx ? static_cast<const T*>(cache) + (int64_t)j * kvd + h * DH + li * 8
+                           : static_cast<const T*>(fresh) + h * DH + li * 8;
+    };
+    // every K and V load of this lane, issued first
+    float kr[ITERS][8], vr[ITERS][8];
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int j = j0 + it * KPI + sub;
+        if (j < n_keys) {
+            Vec8<T>::load(row(a.k, a.k_new, j), kr[it]);
+            Vec8<T>::load(row(a.v, a.v_new, j), vr[it]);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) kr[it][i] = vr[it][i] = 0.f;
+        }
+    }
     float q[GMAX][8];
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
@@ -165,86 +206,54 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(DecodeAttnAr
             for (int i = 0; i < 8; ++i) q[g][i] *= a.scale;
         }
     }
-    auto key_row = [&](const void* cache, const void* fresh, int j) -> const T* {
-        return j < a.n_ctx ? static_cast<const T*>(cache) + (int64_t)j * kvd + h * DH + li * 8
-                           : static_cast<const T*>(fresh) + h * DH + li * 8;
-    };
     // scores
-    for (int it = 0; it < PER_WAVE / KPI; ++it) {
-        const int jl = w * PER_WAVE + it * KPI + sub, j = j0 + jl;
-        const bool ok = j < n_keys;
-        float kv[8];
-        if (ok) Vec8<T>::load(key_row(a.k, a.k_new, j), kv);
+#pragma unroll
+    for (int it = 0; it < ITERS; ++it) {
+        const int jl = w * PER_WAVE + it * KPI + sub;
+        const bool ok = seg * kSegKeys + jl < n_keys;
 #pragma unroll
         for (int g = 0; g < GMAX; ++g) {
             if (g >= G) break;
             float s = 0.f;
-            if (ok)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) s += q[g][i] * kv[i];
+            for (int i = 0; i < 8; ++i) s += q[g][i] * kr[it][i];
 #pragma unroll
             for (int o = 1; o < LPK; o <<= 1) s += __shfl_xor(s, o, 64);
             if (li == 0) sc[g][jl] = ok ? s : -INFINITY;
         }
     }
     __syncthreads();
-    // softmax statistics of the segment (thread t owns key t)
-    const int t = threadIdx.x;
-    float m[GMAX], l[GMAX];
-#pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-        if (g >= G) break;
-        float v = sc[g][t];
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-        if (lane == 0) red[g][w] = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-        if (g >= G) break;
-        m[g] = fmaxf(fmaxf(red[g][0], red[g][1]), fmaxf(red[g][2], red[g][3]));
-    }
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-        if (g >= G) break;
-        const float s = sc[g][t];
-        const float p = s == -INFINITY ? 0.f : __expf(s - m[g]);
-        sc[g][t] = p;
-        float v = p;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-        if (lane == 0) red[g][w] = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < GMAX; ++g) {
-        if (g >= G) break;
-        l[g] = red[g][0] + red[g][1] + red[g][2] + red[g][3];
-    }
-    // values
-    float o[GMAX][8];
-#pragma unroll
-    for (int g = 0; g < GMAX; ++g)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) o[g][i] = 0.f;
-    for (int it = 0; it < PER_WAVE / KPI; ++it) {
-        const int jl = w * PER_WAVE + it * KPI + sub, j = j0 + jl;
-        if (j >= n_keys) continue;
-        float vv[8];
-        Vec8<T>::load(key_row(a.v, a.v_new, j), vv);
+    // softmax statistics of the segment: wave 0, lane t owns key t
+    if (w == 0) {
 #pragma unroll
         for (int g = 0; g < GMAX; ++g) {
             if (g >= G) break;
-            const float p = sc[g][jl];
+            const float s = sc[g][lane];
+            float m = s;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[g][i] += p * vv[i];
+            for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+            const float p = s == -INFINITY ? 0.f : __expf(s - m);
+            float l = p;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+            sc[g][lane] = p;
+            if (lane == 0) { stat[g][0] = m; stat[g][1] = l; }
         }
     }
+    __syncthreads();
+    // values
+    float o[GMAX][8];
 #pragma unroll
     for (int g = 0; g < GMAX; ++g) {
         if (g >= G) break;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[g][i] = 0.f;
+#pragma unroll
+        for (int it = 0; it < ITERS; ++it) {
+            const float p = sc[g][w * PER_WAVE + it * KPI + sub];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) o[g][i] += p * vr[it][i];
+        }
 #pragma unroll
         for (int i = 0; i < 8; ++i)
 #pragma unroll
@@ -254,48 +263,92 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(DecodeAttnAr
             for (int i = 0; i < 8; ++i) osum[w][g][li * 8 + i] = o[g][i];
     }
     __syncthreads();
-    for (int e = t; e < G * DH; e += kThreads) {
+    for (int e = threadIdx.x; e < G * DH; e += kThreads) {
         const int g = e / DH, d = e % DH;
         const float sum = osum[0][g][d] + osum[1][g][d] + osum[2][g][d] + osum[3][g][d];
         const int64_t slot = (int64_t)(h * G + g) * nseg + seg;
         a.part_o[slot * DH + d] = sum;
         if (d == 0) {
-            a.part_ml[2 * slot] = m[g];
-            a.part_ml[2 * slot + 1] = l[g];
+            a.part_ml[2 * slot] = stat[g][0];
+            a.part_ml[2 * slot + 1] = stat[g][1];
         }
     }
 }
 
+// Merge of the segments of one query head (one workgroup per head): the
+// largest segment maximum M, weights exp(m_s - M), then the weighted sums of
+// the segment outputs (two thread groups of d_head threads split the
+// segments, coalesced over d) and of the exponential sums.
 template <typename T>
-__global__ void decode_combine_kernel(DecodeAttnArgs a, int nseg, int dh) {
-    const int hq = blockIdx.x;
-    for (int d = threadIdx.x; d < dh; d += blockDim.x) {
-        float mx = -INFINITY;
-        for (int s = 0; s < nseg; ++s) mx = fmaxf(mx, a.part_ml[2 * ((int64_t)hq * nseg + s)]);
-        float num = 0.f, den = 0.f;
-        for (int s = 0; s < nseg; ++s) {
-            const int64_t slot = (int64_t)hq * nseg + s;
-            const float ms = a.part_ml[2 * slot];
-            const float wgt = ms == -INFINITY ? 0.f : __expf(ms - mx);
-            den += wgt * a.part_ml[2 * slot + 1];
-            num += wgt * a.part_o[slot * dh + d];
-        }
-        static_cast<T*>(a.out)[(int64_t)hq * dh + d] = from_f32<T>(num / den);
+__global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeAttnArgs a, int nseg,
+                                                                  int dh) {
+    __shared__ float red[kWaves];
+    __shared__ float acc[kThreads];
+    const int hq = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+    const float* ml = a.part_ml + (int64_t)hq * nseg * 2;
+    const float* po = a.part_o + (int64_t)hq * nseg * dh;
+    float mx = -INFINITY;
+    for (int s = t; s < nseg; s += kThreads) mx = fmaxf(mx, ml[2 * s]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) red[w] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    float den = 0.f;
+    for (int s = t; s < nseg; s += kThreads) {
+        const float m = ml[2 * s];
+        den += m == -INFINITY ? 0.f : __expf(m - mx) * ml[2 * s + 1];
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
+    if (lane == 0) red[w] = den;
+    __syncthreads();
+    den = red[0] + red[1] + red[2] + red[3];
+    const int groups = kThreads / dh, gi = t / dh, d = t % dh;
+    float num = 0.f;
+    if (gi < groups) {
+#pragma unroll 8
+        for (int s = gi; s < nseg; s += groups) {
+            const float m = ml[2 * s];
+            const float o = po[(int64_t)s * dh + d];
+            num += (m == -INFINITY ? 0.f : __expf(m - mx)) * o;
+        }
+    }
+    acc[t] = num;
+    __syncthreads();
+    if (t < dh) {
+        float sum = 0.f;
+        for (int g = 0; g < groups; ++g) sum += acc[g * dh + t];
+        static_cast<T*>(a.out)[(int64_t)hq * dh + t] = from_f32<T>(sum / den);
+    }
+}
+
+template <typename T, int EPI>
+hipError_t gemv_e(const GemvArgs& g, int units, hipStream_t s) {
+    // enough workgroups to stream the weights: split K over more waves when
+    // there are few units
+    const dim3 block(kThreads);
+    if (units >= 8192) {
+        hipLaunchKernelGGL((gemv_kernel<T, EPI, 1>), dim3((units + 3) / 4), block, 0, s, g);
+    } else if (units >= 4096) {
+        hipLaunchKernelGGL((gemv_kernel<T, EPI, 2>), dim3((units + 1) / 2), block, 0, s, g);
+    } else {
+        hipLaunchKernelGGL((gemv_kernel<T, EPI, 4>), dim3(units), block, 0, s, g);
+    }
+    return hipGetLastError();
 }
 
 template <typename T>
 hipError_t gemv_t(int epi, const GemvArgs& g, hipStream_t s) {
     const int units = epi == EPI_SWIGLU ? g.N : (g.N + 1) / 2;
-    const dim3 grid((units + kWaves - 1) / kWaves), block(kThreads);
     switch (epi) {
-        case EPI_STORE_F32: hipLaunchKernelGGL((gemv_kernel<T, EPI_STORE_F32>), grid, block, 0, s, g); break;
-        case EPI_QKV: hipLaunchKernelGGL((gemv_kernel<T, EPI_QKV>), grid, block, 0, s, g); break;
-        case EPI_RESID: hipLaunchKernelGGL((gemv_kernel<T, EPI_RESID>), grid, block, 0, s, g); break;
-        case EPI_SWIGLU: hipLaunchKernelGGL((gemv_kernel<T, EPI_SWIGLU>), grid, block, 0, s, g); break;
-        default: return hipErrorInvalidValue;
+        case EPI_STORE_F32: return gemv_e<T, EPI_STORE_F32>(g, units, s);
+        case EPI_QKV: return gemv_e<T, EPI_QKV>(g, units, s);
+        case EPI_RESID: return gemv_e<T, EPI_RESID>(g, units, s);
+        case EPI_SWIGLU: return gemv_e<T, EPI_SWIGLU>(g, units, s);
     }
-    return hipGetLastError();
+    return hipErrorInvalidValue;
 }
 
 template <typename T, int DH>
@@ -306,8 +359,8 @@ hipError_t decode_attn_t(const DecodeAttnArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((decode_attention_kernel<T, DH, 1>), grid, dim3(kThreads), 0, s, a);
     else
         hipLaunchKernelGGL((decode_attention_kernel<T, DH, 8>), grid, dim3(kThreads), 0, s, a);
-    hipLaunchKernelGGL(decode_combine_kernel<T>, dim3(a.n_kv_heads * a.group), dim3(DH), 0, s, a,
-                       nseg, DH);
+    hipLaunchKernelGGL(decode_combine_kernel<T>, dim3(a.n_kv_heads * a.group), dim3(kThreads), 0,
+                       s, a, nseg, DH);
     return hipGetLastError();
 }
 
