@@ -50,6 +50,9 @@ def parse():
                          "chunk pool through the HBM chunk tier (steps/warmup are ignored)")
     ap.add_argument("--tier-gib", type=float, default=24.0,
                     help="HBM tier capacity for --serve-batches")
+    ap.add_argument("--selection-study", action="store_true",
+                    help="single-request workloads: cross-layer rank correlation of the KV "
+                         "deviation, and output error vs full prefill for selection variants")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--no-full-compare", action="store_true")
@@ -751,6 +754,70 @@ def main_batched(args, npk, torch, w):
 
 
 # ------------------------------------------------------------------ main
+def selection_study(args, npk, torch, w):
+    """On the synthetic model of the workload: (1) Spearman's rho of the true
+    per-token KV deviation between consecutive layers (every chunk row
+    recomputed at every layer, so layer l's deviation is that of the full
+    prefill against the chunk caches); (2) for recompute ratios and selection
+    variants, the error of the suffix rows' last-layer output and of the
+    fused K/V against full prefill (relative Frobenius norms)."""
+    import oracle                      # Spearman's rho only (host-side statistics)
+    S = w.shape
+    L, N, Nc = S.n_layers, w.n_tokens, w.n_chunk_tokens
+    dev = torch.device("cuda:0")
+    bf = torch.bfloat16
+    model, layers, x0, chunks, emb = make_inputs(npk, w, args.seed, torch, "plain")
+    del emb
+    fk = torch.empty((L, N, S.n_kv_heads, S.head_dim), dtype=bf, device=dev)
+    fv = torch.empty_like(fk)
+    devs = torch.empty((L, Nc), device=dev)
+
+    def run(sched, mode=npk.CB_DEV_KV, scores=None):
+        hid = torch.empty((w.n_suffix + sched[-1], S.d_model), device=dev)
+        npk.cb_blend(model, chunks, list(w.offsets), w.n_suffix, x0, fk, fv, hidden_out=hid,
+                     deviation=devs, schedule=sched, dev_mode=mode, given_scores=scores)
+        torch.cuda.synchronize()
+        return hid[-w.n_suffix:].clone()
+
+    log("[study] full recompute: true deviations at every layer")
+    full = [Nc] * (L + 1)
+    h_full = run(full)
+    k_full, v_full = fk.clone(), fv.clone()
+    d_all = devs.cpu().numpy().astype(np.float64)
+    rho = oracle.layer_rank_correlation(d_all)
+    kv_norm = float(torch.sqrt((k_full.float() ** 2).sum() + (v_full.float() ** 2).sum()))
+
+    def errors(h):
+        e_h = float(torch.linalg.norm(h - h_full) / torch.linalg.norm(h_full))
+        e_kv = float(torch.sqrt(((fk.float() - k_full.float()) ** 2).sum()
+                                + ((fv.float() - v_full.float()) ** 2).sum())) / kv_norm
+        return {"suffix_output": e_h, "fused_kv": e_kv}
+
+    rng = np.random.default_rng(args.seed + 1)
+    random_scores = torch.from_numpy(rng.standard_normal(Nc).astype(np.float32)).to(dev)
+    table = []
+    zero = [0] * (L + 1)
+    table.append({"r_bp": 0, "variant": "full KV reuse", **errors(run(zero))})
+    for r in (500, 1000, 1500, 1800):
+        for kind in ("gradual", "fixed"):
+            code = npk.CB_SCHED_GRADUAL if kind == "gradual" else npk.CB_SCHED_FIXED
+            sched = npk.cb_schedule(Nc, r, code, L)
+            for name, mode, sc in (("KV", npk.CB_DEV_KV, None), ("K", npk.CB_DEV_K, None),
+                                   ("V", npk.CB_DEV_V, None),
+                                   ("random", npk.CB_DEV_GIVEN, random_scores)):
+                if kind == "fixed" and name in ("K", "V"):
+                    continue
+                table.append({"r_bp": r, "schedule": kind, "variant": name,
+                              **errors(run(sched, mode, sc))})
+    out = {"study": "selection variants", "workload": w.name,
+           "data": "synthetic: random-init N(0,0.02) weights, uniform random tokens",
+           "hkvd_rank_correlation": {"per_layer_pair": [round(x, 4) for x in rho],
+                                     "mean": float(np.nanmean(rho)),
+                                     "min": float(np.nanmin(rho))},
+           "errors_vs_full_prefill": table}
+    print(json.dumps(out), flush=True)
+
+
 def first_token_and_decode(args, npk, torch, w, model, emb, hid, fk, fv, sched, blend_ms):
     """TTFT = blend + LM head on the last prompt row; then one decode step of
     that token over the fused cache (HIP events per kernel class in a
@@ -845,6 +912,9 @@ def main():
             main_batched(args, npk, torch, BATCHED_WORKLOADS[args.workload])
         return
     w = WORKLOADS[args.workload]
+    if args.selection_study:
+        selection_study(args, npk, torch, w)
+        return
     if args.r_bp is not None:
         w = dataclasses.replace(w, r_bp=args.r_bp)
     if args.schedule is not None:

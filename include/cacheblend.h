@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 3
+#define CB_ABI_VERSION 4
 
 typedef enum cb_status {
     CB_OK = 0,
@@ -79,8 +79,13 @@ typedef enum cb_schedule_kind { CB_SCHED_GRADUAL = 0, CB_SCHED_FIXED = 1 } cb_sc
 
 /* Deviation measure: sum of squared differences between the recomputed row
  * and the re-rotated cached row, over K and V (default), K only or V only
- * (CacheBlend explainer (0h-n0), eq. 1 and the selection code). */
-typedef enum cb_dev_mode { CB_DEV_KV = 0, CB_DEV_K = 1, CB_DEV_V = 2 } cb_dev_mode;
+ * (CacheBlend explainer (0h-n0), eq. 1 and the selection code).  GIVEN
+ * ranks by per-token scores the caller supplies (given_scores) in place of
+ * a measured deviation, through the same selection and gradual filtering:
+ * for baselines such as random scores, or for scores computed outside the
+ * library (e.g. query-aware ones, which the CacheBlend explainer's outlook
+ * names as follow-up work). */
+typedef enum cb_dev_mode { CB_DEV_KV = 0, CB_DEV_K = 1, CB_DEV_V = 2, CB_DEV_GIVEN = 3 } cb_dev_mode;
 
 typedef struct cb_model_cfg {
     int32_t n_layers;
@@ -165,6 +170,9 @@ typedef struct cb_request {
     int32_t schedule_kind;          /* cb_schedule_kind                     */
     int32_t dev_mode;               /* cb_dev_mode                          */
     int32_t min_tokens;             /* N < min_tokens: plain full prefill   */
+    const float* given_scores;      /* CB_DEV_GIVEN: device [N_c], the score
+                                       of each chunk token by position;
+                                       otherwise NULL                       */
 } cb_request;
 
 /* Outputs of a fusion.  N = chunk tokens N_c + suffix. */
@@ -299,6 +307,8 @@ typedef struct cb_batch_request {
     int32_t schedule_kind;
     int32_t dev_mode;
     int32_t min_tokens;           /* per request: N_b < min_tokens -> full prefill */
+    const float* given_scores;    /* CB_DEV_GIVEN: device [sum N_c], request b's
+                                     scores by position at columns C_b..; else NULL */
 } cb_batch_request;
 
 typedef struct cb_batch_outputs {

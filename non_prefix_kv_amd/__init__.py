@@ -17,12 +17,12 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ------------------------------------------------------------------ constants
-CB_ABI_VERSION = 3
+CB_ABI_VERSION = 4
 CB_OK, CB_E_INVALID, CB_E_SHAPE, CB_E_NOT_PINNED, CB_E_SCHEDULE = 0, -1, -2, -3, -4
 CB_E_OOM, CB_E_HIP, CB_E_BAD_STATE, CB_E_UNSUPPORTED = -5, -6, -7, -8
 CB_F32, CB_BF16 = 0, 1
 CB_SCHED_GRADUAL, CB_SCHED_FIXED = 0, 1
-CB_DEV_KV, CB_DEV_K, CB_DEV_V = 0, 1, 2
+CB_DEV_KV, CB_DEV_K, CB_DEV_V, CB_DEV_GIVEN = 0, 1, 2, 3
 CB_KV_PLAIN, CB_KV_U8, CB_KV_U4 = 0, 1, 2
 
 _c_i32, _c_i64, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
@@ -52,7 +52,7 @@ class cb_request(ctypes.Structure):
                 ("chunk_offsets", ctypes.POINTER(_c_i32)), ("n_suffix", _c_i32),
                 ("x0", _c_p), ("schedule", ctypes.POINTER(_c_i32)),
                 ("recompute_bp", _c_i32), ("schedule_kind", _c_i32), ("dev_mode", _c_i32),
-                ("min_tokens", _c_i32)]
+                ("min_tokens", _c_i32), ("given_scores", _c_p)]
 
 
 class cb_outputs(ctypes.Structure):
@@ -70,7 +70,7 @@ class cb_batch_request(ctypes.Structure):
     _fields_ = [("n_pool", _c_i32), ("pool", ctypes.POINTER(cb_chunk_kv)),
                 ("n_requests", _c_i32), ("items", ctypes.POINTER(cb_batch_item)),
                 ("x0", _c_p), ("recompute_bp", _c_i32), ("schedule_kind", _c_i32),
-                ("dev_mode", _c_i32), ("min_tokens", _c_i32)]
+                ("dev_mode", _c_i32), ("min_tokens", _c_i32), ("given_scores", _c_p)]
 
 
 class cb_batch_outputs(ctypes.Structure):
@@ -266,7 +266,7 @@ def _chunk_array(chunks):
 
 
 def _request(chunks, offsets, n_suffix, x0, schedule, recompute_bp, schedule_kind, dev_mode,
-             min_tokens):
+             min_tokens, given_scores=None):
     arr = _chunk_array(chunks)
     offs = (_c_i32 * max(1, len(offsets)))(*offsets)
     sched = None
@@ -274,7 +274,7 @@ def _request(chunks, offsets, n_suffix, x0, schedule, recompute_bp, schedule_kin
         sched = (_c_i32 * len(schedule))(*schedule)
     req = cb_request(len(chunks), arr, offs, n_suffix, _ptr(x0),
                      sched if sched is not None else ctypes.POINTER(_c_i32)(),
-                     recompute_bp, schedule_kind, dev_mode, min_tokens)
+                     recompute_bp, schedule_kind, dev_mode, min_tokens, _ptr(given_scores))
     return req, (arr, offs, sched)
 
 
@@ -286,10 +286,11 @@ def _outputs(fused_k, fused_v, sel_idx, sel_count, hidden_out, deviation):
 
 def cb_blend(model, chunks, offsets, n_suffix, x0, fused_k, fused_v, sel_idx=None,
              hidden_out=None, deviation=None, schedule=None, recompute_bp=1500,
-             schedule_kind=CB_SCHED_GRADUAL, dev_mode=CB_DEV_KV, min_tokens=0, stream=None):
+             schedule_kind=CB_SCHED_GRADUAL, dev_mode=CB_DEV_KV, min_tokens=0, stream=None,
+             given_scores=None):
     """Queues one fusion; returns the host list sel_count[l] = s[l+1]."""
     req, keep = _request(chunks, offsets, n_suffix, x0, schedule, recompute_bp, schedule_kind,
-                         dev_mode, min_tokens)
+                         dev_mode, min_tokens, given_scores)
     L = model.cfg.n_layers
     cnt = (_c_i32 * L)()
     out = _outputs(fused_k, fused_v, sel_idx, cnt, hidden_out, deviation)
@@ -300,7 +301,7 @@ def cb_blend(model, chunks, offsets, n_suffix, x0, fused_k, fused_v, sel_idx=Non
 
 def cb_blend_batch(model, pool, requests, x0, fused_k, fused_v, sel_idx=None, hidden_out=None,
                    deviation=None, recompute_bp=1500, schedule_kind=CB_SCHED_GRADUAL,
-                   dev_mode=CB_DEV_KV, min_tokens=0, stream=None):
+                   dev_mode=CB_DEV_KV, min_tokens=0, stream=None, given_scores=None):
     """Queues the fusion of a batch.  pool: chunk dicts as for cb_blend;
     requests: list of dicts {chunk_ids: [...], n_suffix, schedule (optional)}.
     Returns sel_count as a list per request of s_b[l+1]."""
@@ -319,7 +320,7 @@ def cb_blend_batch(model, pool, requests, x0, fused_k, fused_v, sel_idx=None, hi
             keep.append(sa)
             items[i].schedule = sa
     req = cb_batch_request(len(pool), parr, len(requests), items, _ptr(x0), recompute_bp,
-                           schedule_kind, dev_mode, min_tokens)
+                           schedule_kind, dev_mode, min_tokens, _ptr(given_scores))
     L = model.cfg.n_layers
     cnt = (_c_i32 * (L * len(requests)))()
     out = cb_batch_outputs(_ptr(fused_k), _ptr(fused_v), _ptr(sel_idx), cnt, _ptr(hidden_out),
@@ -337,9 +338,9 @@ class Plan:
     def __init__(self, model, chunks, offsets, n_suffix, x0, fused_k, fused_v, sel_idx=None,
                  hidden_out=None, deviation=None, schedule=None, recompute_bp=1500,
                  schedule_kind=CB_SCHED_GRADUAL, dev_mode=CB_DEV_KV, min_tokens=0,
-                 stream=None):
+                 stream=None, given_scores=None):
         req, self._keep = _request(chunks, offsets, n_suffix, x0, schedule, recompute_bp,
-                                   schedule_kind, dev_mode, min_tokens)
+                                   schedule_kind, dev_mode, min_tokens, given_scores)
         self._cnt = (_c_i32 * model.cfg.n_layers)()
         out = _outputs(fused_k, fused_v, sel_idx, self._cnt, hidden_out, deviation)
         h = _c_p()

@@ -152,6 +152,12 @@ hipError_t launch_topk(const float* dev, int n, int k, int* idx_out, hipStream_t
 // position) then of the suffix rows; pos_q / row_q their local positions and
 // global rows.  Optional: sel_pos[out_col + t] = kept local positions, and
 // (when dev_out) dev_out[out_col + pos] = the deviation of every chunk row.
+// dev[q.c_off + i] = scores[q.out_col + pos_r[q.r_off + i]] for the chunk
+// rows of every request of the table (caller-given scores in place of a
+// measured deviation).
+hipError_t launch_given_scores(const float* scores, const ReqTab& t, const int* pos_r,
+                               float* dev, hipStream_t s);
+
 hipError_t launch_select(const float* dev, const ReqTab& t, const int* pos_r, const int* row_r,
                          int* sel_local, int* pos_q, int* row_q, int* sel_pos, float* dev_out,
                          hipStream_t s);

@@ -218,6 +218,7 @@ struct cb_plan {
     std::vector<cb_chunk_kv> pool;
     const void* x0 = nullptr;
     int dev_mode = CB_DEV_KV;
+    const float* given = nullptr;     // CB_DEV_GIVEN scores, [sum N_c]
     int kv_pos0 = 0;              // position of key row 0 of a request
     // outputs
     void* fused_k = nullptr;
@@ -641,7 +642,10 @@ cb_status do_layer(cb_plan* p, int l) {
     CB_HIP(hipStreamWaitEvent(st, p->fetched[l], 0));
     // 3. deviation of the recomputed chunk rows against the rotated cache
     const bool measure = lr.nC > 0 && (lr.select_needed || p->deviation);
-    if (measure) {
+    if (measure && p->dev_mode == CB_DEV_GIVEN) {
+        Span sp(m, CB_K_DEVIATION, st, 0, lr.nC * 12.0);
+        for (const ReqTab& t : tabs) CB_HIP(launch_given_scores(p->given, t, pos_r, p->dev, st));
+    } else if (measure) {
         const double parts = p->dev_mode == CB_DEV_KV ? 4 : 2;
         Span sp(m, CB_K_DEVIATION, st, 0, lr.nC * (parts * kvd * es + 8.0));
         for (const ReqTab& t : tabs)
@@ -918,7 +922,11 @@ cb_status validate_request(cb_model* m, const cb_request* r, const cb_outputs* o
     if (r->n_chunks < 0 || r->n_suffix < 0) return fail(CB_E_INVALID, "negative counts");
     if (r->n_chunks > 0 && (!r->chunks || !r->chunk_offsets))
         return fail(CB_E_INVALID, "chunks/chunk_offsets are NULL");
-    if (r->dev_mode < 0 || r->dev_mode > 2) return fail(CB_E_INVALID, "dev_mode %d", r->dev_mode);
+    if (r->dev_mode < 0 || r->dev_mode > 3) return fail(CB_E_INVALID, "dev_mode %d", r->dev_mode);
+    if ((r->dev_mode == CB_DEV_GIVEN) != (r->given_scores != nullptr))
+        return fail(CB_E_INVALID, "given_scores goes with dev_mode CB_DEV_GIVEN, and only with it");
+    if (r->given_scores && mem_kind(r->given_scores) != MemKind::Device)
+        return fail(CB_E_INVALID, "given_scores must be device memory");
     p->L = m->cfg.n_layers;
     ReqInfo q;
     int64_t o_next = 0;
@@ -946,6 +954,7 @@ cb_status validate_request(cb_model* m, const cb_request* r, const cb_outputs* o
     p->reqs.push_back(std::move(q));
     p->x0 = r->x0;
     p->dev_mode = r->dev_mode;
+    p->given = r->given_scores;
     p->fused_k = o->fused_k;
     p->fused_v = o->fused_v;
     p->sel_idx = o->sel_idx;
@@ -961,7 +970,11 @@ cb_status validate_batch(cb_model* m, const cb_batch_request* r, const cb_batch_
     if (!r->x0) return fail(CB_E_INVALID, "x0 is NULL");
     if (r->n_requests <= 0 || !r->items) return fail(CB_E_INVALID, "no requests");
     if (r->n_pool < 0 || (r->n_pool > 0 && !r->pool)) return fail(CB_E_INVALID, "pool is NULL");
-    if (r->dev_mode < 0 || r->dev_mode > 2) return fail(CB_E_INVALID, "dev_mode %d", r->dev_mode);
+    if (r->dev_mode < 0 || r->dev_mode > 3) return fail(CB_E_INVALID, "dev_mode %d", r->dev_mode);
+    if ((r->dev_mode == CB_DEV_GIVEN) != (r->given_scores != nullptr))
+        return fail(CB_E_INVALID, "given_scores goes with dev_mode CB_DEV_GIVEN, and only with it");
+    if (r->given_scores && mem_kind(r->given_scores) != MemKind::Device)
+        return fail(CB_E_INVALID, "given_scores must be device memory");
     p->L = m->cfg.n_layers;
     p->pool.assign(r->pool, r->pool + r->n_pool);
     std::vector<char> checked(r->n_pool, 0);
@@ -999,6 +1012,7 @@ cb_status validate_batch(cb_model* m, const cb_batch_request* r, const cb_batch_
     }
     p->x0 = r->x0;
     p->dev_mode = r->dev_mode;
+    p->given = r->given_scores;
     p->fused_k = o->fused_k;
     p->fused_v = o->fused_v;
     p->sel_idx = o->sel_idx;

@@ -60,6 +60,14 @@ __global__ __launch_bounds__(kDevThreads) void deviation_kernel(
     if (lane == 0) dev[q.c_off + i] = acc;
 }
 
+__global__ __launch_bounds__(kDevThreads) void given_scores_kernel(
+    const float* __restrict__ scores, const ReqTab t, const int* __restrict__ pos_r,
+    float* __restrict__ dev) {
+    const ReqRows& q = t.r[blockIdx.y];
+    const int i = blockIdx.x * kDevThreads + threadIdx.x;
+    if (i < q.n_c) dev[q.c_off + i] = scores[q.out_col + pos_r[q.r_off + i]];
+}
+
 __device__ __forceinline__ uint32_t rank_key(float f) {
     if (f != f) return 0u;                      // NaN ranks above everything
     uint32_t b = __float_as_uint(f);
@@ -214,6 +222,15 @@ hipError_t launch_deviation(int dtype, const void* k_new, const void* v_new,
         hipLaunchKernelGGL(deviation_kernel<float>, grid, block, 0, s, (const float*)k_new,
                            (const float*)v_new, (const float*)k_cached,
                            (const float*)v_cached, grow, t, kv_dim, mode, dev);
+    return hipGetLastError();
+}
+
+hipError_t launch_given_scores(const float* scores, const ReqTab& t, const int* pos_r,
+                               float* dev, hipStream_t s) {
+    if (t.n <= 0 || t.max_c <= 0) return hipSuccess;
+    if (t.n > kMaxReq || !scores) return hipErrorInvalidValue;
+    dim3 grid((t.max_c + kDevThreads - 1) / kDevThreads, t.n);
+    hipLaunchKernelGGL(given_scores_kernel, grid, dim3(kDevThreads), 0, s, scores, t, pos_r, dev);
     return hipGetLastError();
 }
 

@@ -274,7 +274,7 @@ def check_offsets(chunks, offsets):
 
 
 def blend(weights, shape, x0, chunks, offsets, n_suffix, sched, dev_mode="KV",
-          min_tokens=0, dtype=np.float64, n_layers=None, timings=None):
+          min_tokens=0, dtype=np.float64, n_layers=None, timings=None, given_scores=None):
     """Fuse independently precomputed chunk KVs with selective recompute.
 
     weights: per-layer dicts; x0: [N][d] embeddings of all prompt tokens in
@@ -286,7 +286,9 @@ def blend(weights, shape, x0, chunks, offsets, n_suffix, sched, dev_mode="KV",
     chunk positions per layer, ascending), dev [L][N_c] (NaN where not
     measured), layer_pos/layer_out (rows and outputs of every layer), hidden
     (final rows).  When `timings` is a list, the wall time of every layer is
-    appended to it (seconds); the arithmetic is unaffected.
+    appended to it (seconds); the arithmetic is unaffected.  dev_mode 'GIVEN'
+    ranks chunk tokens by given_scores [N_c] (by position) instead of the
+    measured deviation, with the same top-k rule and schedule.
     """
     L = shape.n_layers if n_layers is None else n_layers
     W = _cast_weights(weights[:L], dtype)
@@ -314,7 +316,10 @@ def blend(weights, shape, x0, chunks, offsets, n_suffix, sched, dev_mode="KV",
         q, k, v = qkv_rows(W[l], shape, x, R)      # Step 2
         nC = len(C)
         if nC:
-            d = kv_deviation(k[:nC], v[:nC], fk[l][C], fv[l][C], dev_mode)
+            if dev_mode == "GIVEN":
+                d = np.asarray(given_scores, dtype=np.float64)[C]
+            else:
+                d = kv_deviation(k[:nC], v[:nC], fk[l][C], fv[l][C], dev_mode)
             dev[l, C] = d
             keep = (np.arange(nC) if sched[l + 1] == nC
                     else topk_select(d, sched[l + 1]))
@@ -398,6 +403,41 @@ def unpack_codes(packed, bits: int) -> np.ndarray:
     out = np.empty(packed.shape[:-1] + (2 * packed.shape[-1],), dtype=np.uint8)
     out[..., 0::2] = packed & 15
     out[..., 1::2] = packed >> 4
+    return out
+
+
+# --------------------------------------------------------------------------
+# Cross-layer consistency of HKVD tokens  [CB1 "HKVD（High KV Deviation）
+# トークン選定", insight 2: tokens of high KV deviation stay highly correlated
+# between consecutive layers, checked with Spearman's rank correlation]
+# --------------------------------------------------------------------------
+def spearman(a, b):
+    """Spearman's rho: the Pearson correlation of the ranks (ties share the
+    mean of their ranks)."""
+    def ranks(x):
+        x = np.asarray(x, dtype=np.float64)
+        order = np.argsort(x, kind="stable")
+        r = np.empty(x.size)
+        r[order] = np.arange(1, x.size + 1)
+        for v in np.unique(x):                     # average ranks of ties
+            m = x == v
+            if m.sum() > 1:
+                r[m] = r[m].mean()
+        return r
+    ra, rb = ranks(a), ranks(b)
+    ra -= ra.mean()
+    rb -= rb.mean()
+    return float((ra * rb).sum() / np.sqrt((ra * ra).sum() * (rb * rb).sum()))
+
+
+def layer_rank_correlation(dev):
+    """rho between the deviations of consecutive layers over the tokens
+    measured at both ([L][N_c] with NaN where not measured): list of L-1
+    values (NaN where fewer than 3 tokens are shared)."""
+    out = []
+    for l in range(len(dev) - 1):
+        m = ~np.isnan(dev[l]) & ~np.isnan(dev[l + 1])
+        out.append(spearman(dev[l][m], dev[l + 1][m]) if m.sum() >= 3 else float("nan"))
     return out
 
 

@@ -103,7 +103,7 @@ def _properties(npk, w, chunks, fk, fv, sel, dev, sched, Nc, L, S, layers_to_che
 def _bench_setup(npk, name, seed=0):
     import bench
     w = WORKLOADS[name]
-    model, layers, x0, chunks = bench.make_inputs(npk, w, seed, torch)
+    model, layers, x0, chunks, _ = bench.make_inputs(npk, w, seed, torch)
     return w, model, layers, x0, chunks
 
 

@@ -581,3 +581,49 @@ def test_argmax_first_brute_force():
         assert oracle.argmax_first(v) == best[2]
     assert oracle.argmax_first(np.array([1.0, 3.0, 3.0])) == 1
     assert oracle.argmax_first(np.array([-np.inf, -np.inf])) == 0
+
+
+# ------------------------------------------------------------ selection variants
+# CacheBlend explainer (0h-n0), "HKVD（High KV Deviation）トークン選定".
+
+def test_spearman_vs_library():
+    import scipy.stats
+    rng = np.random.default_rng(71)
+    for _ in range(50):
+        n = int(rng.integers(3, 40))
+        a = rng.integers(0, 6, size=n).astype(float)       # with ties
+        b = a + rng.standard_normal(n)
+        assert oracle.spearman(a, b) == pytest.approx(scipy.stats.spearmanr(a, b)[0], abs=1e-12)
+    x = np.arange(10.0)
+    assert oracle.spearman(x, x ** 3) == pytest.approx(1.0)
+    assert oracle.spearman(x, -x) == pytest.approx(-1.0)
+
+
+def test_given_scores_closed_forms(tiny_case):
+    """Constant scores tie everywhere: the position rule keeps the first
+    s[l+1] positions.  Scores = -position keep the same set; scores =
+    position keep the last ones, narrowing gradually."""
+    case = tiny_case
+    nc = case.n_chunk_tokens
+    sched = oracle.schedule(nc, 1500, "gradual", TINY.n_layers)
+    for scores, want in ((np.zeros(nc), lambda k, prev: prev[:k]),
+                         (-np.arange(nc, dtype=float), lambda k, prev: prev[:k]),
+                         (np.arange(nc, dtype=float), lambda k, prev: prev[len(prev) - k:])):
+        ref = oracle.blend(case.weights, case.shape, case.x0, case.chunks, case.offsets,
+                           case.n_suffix, sched, dev_mode="GIVEN", given_scores=scores)
+        prev = np.arange(nc)
+        for l in range(TINY.n_layers):
+            prev = want(sched[l + 1], prev) if sched[l + 1] < len(prev) else prev
+            assert np.array_equal(ref["sel"][l], prev), l
+
+
+def test_given_scores_equal_to_deviation_reproduce_hkvd(tiny_case):
+    """Feeding the check layer's measured deviation back as given scores
+    (fixed schedule, one narrowing step) reproduces the HKVD selection."""
+    case = tiny_case
+    nc = case.n_chunk_tokens
+    sched = oracle.schedule(nc, 1500, "fixed", TINY.n_layers)
+    ref = run_blend(case, sched)
+    g = oracle.blend(case.weights, case.shape, case.x0, case.chunks, case.offsets,
+                     case.n_suffix, sched, dev_mode="GIVEN", given_scores=ref["dev"][1])
+    assert np.array_equal(g["sel"][1], ref["sel"][1])
