@@ -63,6 +63,8 @@ def parse():
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="summarize a rocprofv3 kernel_trace.csv of a bench run (timed steps "
                          "only) as a markdown table, then exit")
+    ap.add_argument("--match", metavar="REGEX",
+                    help="with --trace-summary: every dispatch whose kernel name matches")
     ap.add_argument("--counter-summary", metavar="CSV", nargs="+",
                     help="average rocprofv3 counter_collection.csv values per kernel over the "
                          "timed steps, then exit")
@@ -112,9 +114,17 @@ def _short(name):
     return re.sub(r"\(.*\)$", "", n)
 
 
-def trace_summary(path):
+def trace_summary(path, match=None):
+    """Per-kernel table of a rocprofv3 kernel trace: the timed steps (see the
+    marker rule above), or, with `match`, every dispatch whose kernel name
+    matches that regular expression."""
     import csv
-    rows = _timed_rows(list(csv.DictReader(open(path))), lambda r: int(r["Start_Timestamp"]))
+    import re
+    rows = list(csv.DictReader(open(path)))
+    if match:
+        rows = [r for r in rows if re.search(match, r["Kernel_Name"])]
+    else:
+        rows = _timed_rows(rows, lambda r: int(r["Start_Timestamp"]))
     agg = {}
     for r in rows:
         k = _short(r["Kernel_Name"])
@@ -892,7 +902,7 @@ def main():
                                    "data-parallel serving by request)", "n_gpus": args.gpus}))
         sys.exit(2)
     if args.trace_summary:
-        trace_summary(args.trace_summary)
+        trace_summary(args.trace_summary, args.match)
         return
     if args.counter_summary:
         counter_summary(args.counter_summary)
