@@ -498,15 +498,21 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a, const 
     }
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (n_seg > 1) {
-        // Partial of this segment: unnormalized O, running max (log2 units) and sum.
+        // Partial of this segment: O normalized by the segment's own sum (bf16,
+        // half the bytes of the unnormalized float sums), running max (log2
+        // units) and sum.
         const int64_t slot = ((int64_t)qt * a.n_q_heads + h) * a.max_seg + seg;
-        float* po = a.part_o + (slot * QT32 + ql) * D;
+        bf16* po = a.part_o + (slot * QT32 + ql) * D;
+        const float inv_s = l_tot > 0.f ? 1.0f / l_tot : 0.f;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4)
-                *reinterpret_cast<floatx4*>(po + dt * 32 + 8 * i4 + 4 * g) =
-                    floatx4{o[dt][i4 * 4], o[dt][i4 * 4 + 1], o[dt][i4 * 4 + 2], o[dt][i4 * 4 + 3]};
+                *reinterpret_cast<bf16x4*>(po + dt * 32 + 8 * i4 + 4 * g) =
+                    bf16x4{static_cast<bf16>(o[dt][i4 * 4] * inv_s),
+                           static_cast<bf16>(o[dt][i4 * 4 + 1] * inv_s),
+                           static_cast<bf16>(o[dt][i4 * 4 + 2] * inv_s),
+                           static_cast<bf16>(o[dt][i4 * 4 + 3] * inv_s)};
         if (g == 0) {
             float* pm = a.part_ml + (slot * QT32 + ql) * 2;
             pm[0] = m_run;
@@ -565,11 +571,14 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a, cons
     const float Mu = M == -INFINITY ? 0.f : M;
     float L = 0.f;
     floatx4 acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
     for (int sg = 0; sg < n_seg; ++sg) {
         const float* pm = a.part_ml + ((slot0 + sg) * QT32 + ql) * 2;
-        const float w = __builtin_amdgcn_exp2f(pm[0] - Mu);
-        L += w * pm[1];
-        acc += w * *reinterpret_cast<const floatx4*>(a.part_o + ((slot0 + sg) * QT32 + ql) * D + c);
+        const bf16x4 ov = *reinterpret_cast<const bf16x4*>(a.part_o + ((slot0 + sg) * QT32 + ql) * D + c);
+        const float wl = __builtin_amdgcn_exp2f(pm[0] - Mu) * pm[1];   // weight x segment sum
+        L += wl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += wl * static_cast<float>(ov[e]);
     }
     const float inv = L > 0.f ? 1.0f / L : 0.f;
     bf16x4 v{static_cast<bf16>(acc[0] * inv), static_cast<bf16>(acc[1] * inv),
@@ -616,7 +625,7 @@ SplitPlan split_plan(const AttnRange* t, int n, int n_q_heads, int head_dim) {
     p.seg_keys = ((max_kv + want - 1) / want + KB32 - 1) / KB32 * KB32;
     p.max_seg = (max_kv + p.seg_keys - 1) / p.seg_keys;
     if (p.max_seg <= 1) return SplitPlan{};
-    p.bytes = (size_t)n * n_q_heads * p.max_seg * QT32 * (head_dim + 2) * sizeof(float);
+    p.bytes = (size_t)n * n_q_heads * p.max_seg * QT32 * (head_dim * sizeof(bf16) + 2 * sizeof(float));
     return p;
 }
 
@@ -631,8 +640,8 @@ hipError_t launch32(const AttnArgs& a0, const AttnTiles& tl, void* ws, size_t ws
     a.part_ml = nullptr;
     if (sp.bytes) {
         if (!ws || ws_bytes < sp.bytes) return hipErrorInvalidValue;
-        a.part_o = static_cast<float*>(ws);
-        a.part_ml = a.part_o + (size_t)tl.n * a.n_q_heads * sp.max_seg * QT32 * D;
+        a.part_o = static_cast<bf16*>(ws);
+        a.part_ml = reinterpret_cast<float*>(a.part_o + (size_t)tl.n * a.n_q_heads * sp.max_seg * QT32 * D);
     }
     const int64_t blocks = (int64_t)tl.n * a.n_q_heads * a.max_seg;
     if (blocks > INT_MAX) return hipErrorInvalidValue;

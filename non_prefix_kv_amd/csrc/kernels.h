@@ -268,7 +268,7 @@ struct AttnArgs {
     // a combine pass merges them.  Set by the launcher.
     int seg_keys;
     int max_seg;
-    float* part_o;      // [tiles][Hq][max_seg][tile height][dh]
+    bf16* part_o;       // [tiles][Hq][max_seg][tile height][dh], normalized per segment
     float* part_ml;     // [tiles][Hq][max_seg][tile height][2]
 };
 

@@ -153,7 +153,8 @@ def test_rmsnorm_vs_oracle(lib, dt, rows, d):
 @pytest.mark.parametrize("m,n,k", [(1, 16, 64), (7, 130, 64), (130, 128, 256), (832, 384, 4096),
                                    (257, 1000, 1024), (128, 11008, 512), (3, 4096, 11008),
                                    (1600, 520, 384), (2048, 256, 128), (1537, 2000, 1152),
-                                   (832, 4096, 4096), (1000, 1536, 2048), (640, 2816, 1536)])
+                                   (832, 4096, 4096), (1000, 1536, 2048), (640, 2816, 1536),
+                                   (832, 22016, 1024), (700, 10000, 512), (947, 6000, 256)])
 def test_gemm_vs_definition(lib, dt, m, n, k):
     rng = np.random.default_rng(m * 7 + n)
     a = round_to(rng.standard_normal((m, k)), dt)
