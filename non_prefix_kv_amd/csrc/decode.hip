@@ -157,6 +157,39 @@ __global__ __launch_bounds__(1024) void argmax_kernel(const float* __restrict__ 
     }
 }
 
+// Sum over the N (2, 4, 8 or 16) lanes of a row group with DPP lane moves
+// (full-rate VALU): swap neighbours, swap pairs, mirror within 8, mirror
+// within 16.  Every lane of the group ends with the group's sum.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 CTRL, 0xF, 0xF, false));
+}
+// Reduction (sum, or max when MAX) over the N lanes of a row group.
+template <int N, bool MAX = false>
+__device__ __forceinline__ float group_reduce(float v) {
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+    if constexpr (N >= 2) v = op(v, dpp<0xB1>(v));      // quad_perm 1,0,3,2
+    if constexpr (N >= 4) v = op(v, dpp<0x4E>(v));      // quad_perm 2,3,0,1
+    if constexpr (N >= 8) v = op(v, dpp<0x141>(v));     // row_half_mirror
+    if constexpr (N >= 16) v = op(v, dpp<0x140>(v));    // row_mirror
+    return v;
+}
+template <int N>
+__device__ __forceinline__ float group_sum(float v) { return group_reduce<N, false>(v); }
+
+// Reduction over the whole wave: rows of 16 by DPP, then the four row
+// results read into scalar registers.
+template <bool MAX>
+__device__ __forceinline__ float wave_reduce(float v) {
+    v = group_reduce<16, MAX>(v);
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return MAX ? fmaxf(fmaxf(r0, r1), fmaxf(r2, r3)) : (r0 + r1) + (r2 + r3);
+}
+
 // Split-key attention of one query row (all query heads) over n_ctx cached
 // keys plus the step's own key.  Grid (kv heads, key segments of 64); the G
 // query heads that share a KV head are handled together, so each cached key
@@ -172,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(DecodeAttnAr
     static_assert(ITERS * KPI == PER_WAVE, "keys per wave");
     __shared__ float sc[GMAX][kSegKeys];
     __shared__ float stat[GMAX][2];
-    __shared__ float osum[kWaves][GMAX][DH];
+    __shared__ float osum[kWaves][KPI][GMAX][DH];     // per key subgroup partial outputs
     const int h = blockIdx.x, seg = blockIdx.y, nseg = gridDim.y;
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const int sub = lane / LPK, li = lane % LPK;
@@ -217,8 +250,7 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(DecodeAttnAr
             float s = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) s += q[g][i] * kr[it][i];
-#pragma unroll
-            for (int o = 1; o < LPK; o <<= 1) s += __shfl_xor(s, o, 64);
+            s = group_sum<LPK>(s);
             if (li == 0) sc[g][jl] = ok ? s : -INFINITY;
         }
     }
@@ -229,13 +261,9 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(DecodeAttnAr
         for (int g = 0; g < GMAX; ++g) {
             if (g >= G) break;
             const float s = sc[g][lane];
-            float m = s;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+            const float m = wave_reduce<true>(s);
             const float p = s == -INFINITY ? 0.f : __expf(s - m);
-            float l = p;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+            const float l = wave_reduce<false>(p);
             sc[g][lane] = p;
             if (lane == 0) { stat[g][0] = m; stat[g][1] = l; }
         }
@@ -254,18 +282,16 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(DecodeAttnAr
 #pragma unroll
             for (int i = 0; i < 8; ++i) o[g][i] += p * vr[it][i];
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-#pragma unroll
-            for (int off = LPK; off < 64; off <<= 1) o[g][i] += __shfl_xor(o[g][i], off, 64);
-        if (sub == 0)
-#pragma unroll
-            for (int i = 0; i < 8; ++i) osum[w][g][li * 8 + i] = o[g][i];
+        Vec8<float>::store(&osum[w][sub][g][li * 8], o[g]);
     }
     __syncthreads();
     for (int e = threadIdx.x; e < G * DH; e += kThreads) {
         const int g = e / DH, d = e % DH;
-        const float sum = osum[0][g][d] + osum[1][g][d] + osum[2][g][d] + osum[3][g][d];
+        float sum = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < kWaves; ++ww)
+#pragma unroll
+            for (int k = 0; k < KPI; ++k) sum += osum[ww][k][g][d];
         const int64_t slot = (int64_t)(h * G + g) * nseg + seg;
         a.part_o[slot * DH + d] = sum;
         if (d == 0) {
@@ -275,22 +301,24 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(DecodeAttnAr
     }
 }
 
-// Merge of the segments of one query head (one workgroup per head): the
-// largest segment maximum M, weights exp(m_s - M), then the weighted sums of
-// the segment outputs (two thread groups of d_head threads split the
-// segments, coalesced over d) and of the exponential sums.
+// Merge of the key segments.  Workgroup (query head, 32-dimension slice):
+// every thread first forms the largest segment maximum M and the weighted
+// sum of exponentials over all segments (a few floats per segment), then the
+// 256 threads = 32 dimensions x 8 segment slices accumulate the weighted
+// segment outputs, and the 8 slices meet in LDS.
+constexpr int kCombSlices = kThreads / 32;
+
 template <typename T>
 __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeAttnArgs a, int nseg,
                                                                   int dh) {
     __shared__ float red[kWaves];
-    __shared__ float acc[kThreads];
-    const int hq = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+    __shared__ float acc[kCombSlices][32];
+    const int hq = blockIdx.x, d0 = blockIdx.y * 32, t = threadIdx.x, lane = t & 63, w = t >> 6;
     const float* ml = a.part_ml + (int64_t)hq * nseg * 2;
     const float* po = a.part_o + (int64_t)hq * nseg * dh;
     float mx = -INFINITY;
     for (int s = t; s < nseg; s += kThreads) mx = fmaxf(mx, ml[2 * s]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    mx = wave_reduce<true>(mx);
     if (lane == 0) red[w] = mx;
     __syncthreads();
     mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
@@ -300,27 +328,27 @@ __global__ __launch_bounds__(kThreads) void decode_combine_kernel(DecodeAttnArgs
         const float m = ml[2 * s];
         den += m == -INFINITY ? 0.f : __expf(m - mx) * ml[2 * s + 1];
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) den += __shfl_xor(den, o, 64);
+    den = wave_reduce<false>(den);
     if (lane == 0) red[w] = den;
     __syncthreads();
     den = red[0] + red[1] + red[2] + red[3];
-    const int groups = kThreads / dh, gi = t / dh, d = t % dh;
+    const int d = d0 + (t & 31), sl = t >> 5;
     float num = 0.f;
-    if (gi < groups) {
-#pragma unroll 8
-        for (int s = gi; s < nseg; s += groups) {
+    if (d < dh) {
+#pragma unroll 4
+        for (int s = sl; s < nseg; s += kCombSlices) {
             const float m = ml[2 * s];
             const float o = po[(int64_t)s * dh + d];
             num += (m == -INFINITY ? 0.f : __expf(m - mx)) * o;
         }
     }
-    acc[t] = num;
+    acc[sl][t & 31] = num;
     __syncthreads();
-    if (t < dh) {
+    if (t < 32 && d0 + t < dh) {
         float sum = 0.f;
-        for (int g = 0; g < groups; ++g) sum += acc[g * dh + t];
-        static_cast<T*>(a.out)[(int64_t)hq * dh + t] = from_f32<T>(sum / den);
+#pragma unroll
+        for (int k = 0; k < kCombSlices; ++k) sum += acc[k][t];
+        static_cast<T*>(a.out)[(int64_t)hq * dh + d0 + t] = from_f32<T>(sum / den);
     }
 }
 
@@ -359,8 +387,8 @@ hipError_t decode_attn_t(const DecodeAttnArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((decode_attention_kernel<T, DH, 1>), grid, dim3(kThreads), 0, s, a);
     else
         hipLaunchKernelGGL((decode_attention_kernel<T, DH, 8>), grid, dim3(kThreads), 0, s, a);
-    hipLaunchKernelGGL(decode_combine_kernel<T>, dim3(a.n_kv_heads * a.group), dim3(kThreads), 0,
-                       s, a, nseg, DH);
+    hipLaunchKernelGGL(decode_combine_kernel<T>, dim3(a.n_kv_heads * a.group, DH / 32),
+                       dim3(kThreads), 0, s, a, nseg, DH);
     return hipGetLastError();
 }
 
