@@ -154,7 +154,8 @@ def test_rmsnorm_vs_oracle(lib, dt, rows, d):
                                    (257, 1000, 1024), (128, 11008, 512), (3, 4096, 11008),
                                    (1600, 520, 384), (2048, 256, 128), (1537, 2000, 1152),
                                    (832, 4096, 4096), (1000, 1536, 2048), (640, 2816, 1536),
-                                   (832, 22016, 1024), (700, 10000, 512), (947, 6000, 256)])
+                                   (832, 22016, 1024), (700, 10000, 512), (947, 6000, 256),
+                                   (600, 20000, 320), (520, 30000, 192)])
 def test_gemm_vs_definition(lib, dt, m, n, k):
     rng = np.random.default_rng(m * 7 + n)
     a = round_to(rng.standard_normal((m, k)), dt)
