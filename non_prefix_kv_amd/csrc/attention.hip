@@ -262,15 +262,21 @@ __global__ __launch_bounds__(kThreads, 2) void attention_kernel(AttnArgs a, cons
 }
 
 // ---------------------------------------------------------------------------
-// bf16 path: 32 queries per wave on 32x32x16 MFMAs.  Each K or V fragment
-// read from LDS now feeds a 32x32 output tile, halving LDS bytes per flop
-// relative to 16-query waves.  Two waves per workgroup (64 queries of one
-// head), 32-key blocks double-buffered in LDS with the next block prefetched
-// into registers.  Layout of v_mfma_f32_32x32x16_bf16: lane l supplies row
-// (l % 32) of A and column (l % 32) of B with reduction elements
-// 8 * (l / 32) + 0..7; accumulator element i of lane l is
-// C[8 * (i / 4) + 4 * (l / 32) + i % 4][l % 32].
+// bf16 path: 32 queries per wave on 32x32x16 MFMAs, four waves per
+// workgroup (128 queries of one head), 64-key blocks.  Layout of
+// v_mfma_f32_32x32x16_bf16: lane l supplies row (l % 32) of A and column
+// (l % 32) of B with reduction elements 8 * (l / 32) + 0..7; accumulator
+// element i of lane l is C[8 * (i / 4) + 4 * (l / 32) + i % 4][l % 32].
+//
+// K and V blocks go straight from memory into LDS (buffer_load ... lds: each
+// instruction of a wave writes 64 x 16 B to consecutive LDS bytes), two
+// stages: block kb+1 is copied while block kb is multiplied out.  LDS rows
+// are unpadded; the 16-byte chunks of a row are stored at a swizzled slot
+// (chunk ^ key(row)), and each lane fetches the global chunk that belongs in
+// its slot.  A 64-key block gives each wave two independent 32-key score
+// tiles (two MFMA chains in flight) and one softmax pass per 64 keys.
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ void mfma32(floatx16& acc, const bf16x8& a, const bf16x8& b) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
@@ -278,7 +284,7 @@ __device__ __forceinline__ void mfma32(floatx16& acc, const bf16x8& a, const bf1
 
 constexpr int kT32 = 256;   // threads per workgroup (4 waves)
 constexpr int QT32 = 128;   // queries per workgroup
-constexpr int KB32 = 32;    // keys per block
+constexpr int KBL = 64;     // keys per block
 constexpr float kLazyLog2 = 8.0f;   // rescale threshold of the running maximum (log2 units)
 constexpr int kSplitUnits = 2048;   // (query tile, head, key segment) units wanted per launch
 
@@ -291,17 +297,49 @@ __device__ __forceinline__ int xcd_order(int hw, int total) {
     return xcd * base + min(xcd, rem) + j;
 }
 
+// Raw buffer descriptor: base address, stride 0, range `bytes` (wave-uniform
+// values, read from the first lane so the descriptor lives in SGPRs).
+__device__ __forceinline__ i32x4 attn_rsrc(const void* base, int bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return i32x4{__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
+                 __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xFFFF)),
+                 __builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+
+// 16 bytes per lane from buffer offset voff into LDS at m0 + 16 * lane.
+// Inline assembly keeps the compiler from treating it as an LDS store it
+// must wait for; completion is tracked by explicit vmcnt waits and the
+// "memory" clobber keeps LDS accesses from moving across the copy.
+__device__ __forceinline__ void attn_dma16(i32x4 rsrc, int voff, uint32_t m0) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(m0)
+                 : "memory");
+}
+
+// Swizzle keys of the LDS rows (D*2 bytes each).  K is read as 16-byte
+// fragments, 16 lanes at a time over 16 rows of one chunk column: the slots
+// of 16 consecutive rows (D = 128) or of 8 rows of equal parity (D = 64,
+// two rows per 256-byte bank window) must differ.  V is read by transposing
+// 8-byte reads, 32 lanes at a time over 4 rows x 4 chunks: the 4 rows must
+// move the chunk column by distinct multiples of 4 (D = 128) or, for D = 64,
+// rows 2 apart (same bank half) must land in opposite 64-byte halves.
+template <int D> __device__ __forceinline__ int k_key(int r) {
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D> __device__ __forceinline__ int v_key(int r) {
+    return D == 128 ? 4 * (r & 3) : 4 * ((r >> 1) & 1);
+}
+
 template <int D>
-__global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a, const AttnTiles tl) {
-    constexpr int LDK = D + 8;                 // sK row stride (elements)
-    constexpr int LDV = D + 32;                // sV row stride: rows 1..3 apart fall 64 B
-                                               // apart in bank space (transposed reads)
+__global__ __launch_bounds__(kT32, 2) void attention64_kernel(AttnArgs a, const AttnTiles tl) {
+    constexpr int RB = D * 2;                  // bytes per LDS row
+    constexpr int CPR = RB / 16;               // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;              // rows per copy instruction
+    constexpr int CPW = KBL / 4 / RPI;         // copy instructions per wave (K, and again V)
     constexpr int NDS = D / 16;                // 16-dim reduction steps for S
     constexpr int NDT = D / 32;                // 32-dim output tiles
-    constexpr int KU = KB32 * D / 8 / kT32;    // 16-byte K (and V) pieces per thread
-    static_assert(KU >= 1 && KB32 * D / 8 == KU * kT32, "K tile split");
-    __shared__ __attribute__((aligned(16))) bf16 sK[2][KB32 * LDK];
-    __shared__ __attribute__((aligned(16))) bf16 sV[2][KB32 * LDV];
+    constexpr int BLK = KBL * RB;              // bytes of one K (or V) block
+    static_assert(CPW >= 1 && CPW * RPI * 4 == KBL, "copy split");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * BLK];   // [stage][K|V]
     __shared__ int sred[kT32 / 64];
 
     // logical id -> (tile, segment, head), tile fastest; tiles come longest first
@@ -314,7 +352,8 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a, const 
     const AttnRange& tile = tl.t[qt];
     const int n_kv = tile.n_kv;
     const int hk = h / (a.n_q_heads / a.n_kv_heads);
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int fr = lane & 31, g = lane >> 5;
     const int q_ld = a.n_q_heads * D, kv_ld = a.n_kv_heads * D;
 
@@ -337,9 +376,9 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a, const 
     // Key segment of this workgroup (whole range when not split).
     const int n_seg = a.seg_keys > 0 ? max(1, (nk + a.seg_keys - 1) / a.seg_keys) : 1;
     if (seg >= n_seg) return;                          // uniform over the workgroup
-    const int kb_beg = a.seg_keys > 0 ? seg * (a.seg_keys / KB32) : 0;
+    const int kb_beg = a.seg_keys > 0 ? seg * (a.seg_keys / KBL) : 0;
     const int k_end = a.seg_keys > 0 ? min(nk, (seg + 1) * a.seg_keys) : nk;
-    const int n_kb = k_end > kb_beg * KB32 ? (k_end - kb_beg * KB32 + KB32 - 1) / KB32 : 0;
+    const int n_kb = k_end > kb_beg * KBL ? (k_end - kb_beg * KBL + KBL - 1) / KBL : 0;
 
     const int qrow = a.qidx ? a.qidx[qi] : qi;
     const bf16* qp = static_cast<const bf16*>(a.q) + (int64_t)qrow * q_ld + h * D;
@@ -357,74 +396,76 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a, const 
 
     const bf16* kbase = static_cast<const bf16*>(a.k) + (int64_t)tile.g0 * kv_ld + hk * D;
     const bf16* vbase = static_cast<const bf16*>(a.v) + (int64_t)tile.g0 * kv_ld + hk * D;
-    // Two register stage sets (prefetch distance 2).  K and V blocks are
-    // fetched with buffer loads whose range ends at the last key: rows past
-    // it read as zero (their scores are masked).  Both are stored row-major;
-    // V^T fragments come from transposing LDS reads.
-    int voff[KU];
+    // Copies: wave w fills rows 16 w .. 16 w + 15 of the K and V blocks, RPI
+    // rows per instruction; lane l of instruction c goes to row
+    // 16 w + RPI c + l / CPR, slot l % CPR, and fetches the chunk stored there.
+    int k_voff[CPW], v_voff[CPW];
 #pragma unroll
-    for (int j = 0; j < KU; ++j) {
-        const int u = tid + j * kT32;
-        voff[j] = ((u / (D / 8)) * kv_ld + (u % (D / 8)) * 8) * 2;
+    for (int c = 0; c < CPW; ++c) {
+        const int r = 16 * wave + RPI * c + lane / CPR, slot = lane % CPR;
+        k_voff[c] = r * kv_ld * 2 + ((slot ^ k_key<D>(r)) & (CPR - 1)) * 16;
+        v_voff[c] = r * kv_ld * 2 + ((slot ^ v_key<D>(r)) & (CPR - 1)) * 16;
     }
-    u32x4 rk0[KU], rv0[KU], rk1[KU], rv1[KU];
-    auto load_block = [&](int kb, u32x4 (&rk)[KU], u32x4 (&rv)[KU]) {
-        const int k0 = (kb_beg + kb) * KB32;
-        const int rows = min(KB32, n_kv - k0);
-        const __amdgpu_buffer_rsrc_t rsk = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<bf16*>(kbase + (int64_t)k0 * kv_ld), (short)0, rows * kv_ld * 2, 0x00020000);
-        const __amdgpu_buffer_rsrc_t rsv = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<bf16*>(vbase + (int64_t)k0 * kv_ld), (short)0, rows * kv_ld * 2, 0x00020000);
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
+    auto issue = [&](int kb, int st) {
+        const int k0 = (kb_beg + kb) * KBL;
+        const int rows = min(KBL, n_kv - k0);      // rows past the last key read as zero
+        const i32x4 rk = attn_rsrc(kbase + (int64_t)k0 * kv_ld, rows * kv_ld * 2);
+        const i32x4 rv = attn_rsrc(vbase + (int64_t)k0 * kv_ld, rows * kv_ld * 2);
+        const uint32_t kd = lds0 + st * 2 * BLK + 16 * wave * RB;
 #pragma unroll
-        for (int j = 0; j < KU; ++j) {
-            rk[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsk, voff[j], 0, 0));
-            rv[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsv, voff[j], 0, 0));
+        for (int c = 0; c < CPW; ++c) {
+            attn_dma16(rk, k_voff[c], kd + c * RPI * RB);
+            attn_dma16(rv, v_voff[c], kd + BLK + c * RPI * RB);
         }
     };
-    auto store_block = [&](int buf, const u32x4 (&rk)[KU], const u32x4 (&rv)[KU]) {
-#pragma unroll
-        for (int j = 0; j < KU; ++j) {
-            const int u = tid + j * kT32;
-            const int r = u / (D / 8), c = (u % (D / 8)) * 8;
-            *reinterpret_cast<u32x4*>(&sK[buf][r * LDK + c]) = rk[j];
-            *reinterpret_cast<u32x4*>(&sV[buf][r * LDV + c]) = rv[j];
-        }
-    };
-    // Transposing read of V: within each 16-lane group the instruction hands
-    // lane j the j-th column of the 4 x 16 block addressed by the group
-    // (lane s points at row s / 4, columns 4 (s % 4) .. +3), so lane l gets 4
-    // consecutive keys of one dimension.  Row offset of this lane:
+    // K fragment (row kr, dims 16 s + 8 g ..) and transposed V reads: within
+    // each 16-lane group the transposing read hands lane j the j-th column of
+    // the 4 x 16 block the group addresses (lane s points at row s / 4,
+    // columns 4 (s % 4) .. +3), so lane l gets 4 consecutive keys of one dimension.
+    const int kkey = k_key<D>(fr);                          // same for rows fr + 32
     const int tr_g = lane >> 4, tr_s = lane & 15;
-    const int tr_off = (4 * (tr_g >> 1) + (tr_s >> 2)) * LDV + 16 * (tr_g & 1) + 4 * (tr_s & 3);
-    auto compute = [&](int cur, int kb) {
-        const int k0 = (kb_beg + kb) * KB32;
+    const int tr_row = 4 * (tr_g >> 1) + (tr_s >> 2);       // + 16 q4 (+ 8 for the upper half)
+    const int tr_col = 16 * (tr_g & 1) + 4 * (tr_s & 3);    // + 32 dt
+    const int vkey = v_key<D>(tr_row);                      // same for rows tr_row + 8 j
+    auto compute = [&](int st, int kb) {
+        const int k0 = (kb_beg + kb) * KBL;
         if (a.kv_pos0 + k0 > wmax) return;          // wave-uniform: nothing visible
-        floatx16 st;
+        const unsigned char* sk = smem + st * 2 * BLK;
+        const unsigned char* sv = sk + BLK;
+        floatx16 s2[2];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) st[i] = 0.f;
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s2[hh][i] = 0.f;
 #pragma unroll
         for (int s = 0; s < NDS; ++s) {
-            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&sK[cur][fr * LDK + s * 16 + g * 8]);
-            mfma32(st, kf, qf[s]);
+            const int off = fr * RB + (((2 * s + g) ^ kkey) & (CPR - 1)) * 16;
+            const bf16x8 k_lo = *reinterpret_cast<const bf16x8*>(sk + off);
+            const bf16x8 k_hi = *reinterpret_cast<const bf16x8*>(sk + off + 32 * RB);
+            mfma32(s2[0], k_lo, qf[s]);
+            mfma32(s2[1], k_hi, qf[s]);
         }
         // Scores stay unscaled; the running max is kept in scaled (log2)
         // units and the scale is folded into one FMA before v_exp_f32.
-        const bool need_mask = (k0 + KB32 > n_kv) || (a.kv_pos0 + k0 + KB32 - 1 > wmin);
+        const bool need_mask = (k0 + KBL > n_kv) || (a.kv_pos0 + k0 + KBL - 1 > wmin);
         if (need_mask) {
+            // key k0 + 4 g + c (c a compile-time offset) is visible iff c <= lim
+            const int lim = min(n_kv - 1, qpos - a.kv_pos0) - k0 - 4 * g;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int kj = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
-                if (kj >= n_kv || a.kv_pos0 + kj > qpos) st[i] = -INFINITY;
-            }
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (32 * hh + 8 * (i >> 2) + (i & 3) > lim) s2[hh][i] = -INFINITY;
         }
-        float mloc = st[0];
+        float mloc = fmaxf(s2[0][0], s2[1][0]);
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, st[i]);
+        for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, fmaxf(s2[0][i], s2[1][i]));
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * sl2;
         // The reference maximum only moves when a score exceeds it by more
         // than kLazyLog2 (probabilities then stay below 2^kLazyLog2): after
         // the first keys O and l are rarely rescaled.  Any reference gives
-        // the same normalized result; the combine pass merges segments by
+        // the same normalized result; the merge pass combines segments by
         // their own references.
         const bool grow = mloc > m_run + kLazyLog2;      // false for an all-masked block
         const float m_new = grow ? mloc : m_run;
@@ -436,65 +477,50 @@ __global__ __launch_bounds__(kT32, 2) void attention32_kernel(AttnArgs a, const 
             for (int t = 0; t < NDT; ++t) o[t] *= alpha;
         }
         m_run = m_new;
-        bf16x8 pf[2];
+        // P^T slot j of 16-key group q4 = 2 hh + j / 8 holds key
+        // 32 hh + 16 (j / 8) + 8 ((j % 8) / 4) + 4 g + j % 4: the key order
+        // of the transposed V reads below.
+        bf16x8 pf[4];
+        float lsum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(st[i], sl2, -m_use));
-            l_run += p;
-            pf[i >> 3][i & 7] = static_cast<bf16>(p);
-        }
-        // P^T slot j of half hh holds key 16 hh + 8 (j / 4) + 4 g + j % 4; the
-        // V^T fragment (row = dimension, 8 keys) is read in that key order.
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float p = __builtin_amdgcn_exp2f(fmaf(s2[hh][i], sl2, -m_use));
+                lsum += p;
+                pf[2 * hh + (i >> 3)][i & 7] = static_cast<bf16>(p);
+            }
+        l_run += lsum;
 #pragma unroll
         for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
+            for (int q4 = 0; q4 < 4; ++q4) {
                 typedef short i16x4 __attribute__((ext_vector_type(4)));
-                typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-                const bf16* vr = &sV[cur][tr_off + hh * 16 * LDV + dt * 32];
                 typedef short i16x8 __attribute__((ext_vector_type(8)));
-                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)vr);
-                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vr + 8 * LDV));
+                typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+                const int col = dt * 32 + tr_col;
+                const int off = (16 * q4 + tr_row) * RB + ((((col >> 3) ^ vkey) & (CPR - 1)) << 4) +
+                                (col & 7) * 2;
+                const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sv + off));
+                const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sv + off + 8 * RB));
                 const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                mfma32(o[dt], __builtin_bit_cast(bf16x8, w), pf[hh]);
+                mfma32(o[dt], __builtin_bit_cast(bf16x8, w), pf[q4]);
             }
     };
-    // Steady state unrolled by two: on entry block kb is in LDS buffer 0 and
-    // block kb+1 in register set 1; block kb+2 is fetched during the math.
-    if (n_kb > 0) load_block(0, rk0, rv0);
-    if (n_kb > 1) load_block(1, rk1, rv1);
-    if (n_kb > 0) store_block(0, rk0, rv0);
-    __syncthreads();
-    int kb = 0;
-    for (; kb + 3 < n_kb; kb += 2) {
-        load_block(kb + 2, rk0, rv0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(0, kb);
-        store_block(1, rk1, rv1);
-        __syncthreads();
-        load_block(kb + 3, rk1, rv1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(1, kb + 1);
-        store_block(0, rk0, rv0);
+    // Two stages: block kb+1 is copied into the other stage while block kb is
+    // multiplied out; the wait + barrier at the end publishes it (and tells
+    // every wave that stage kb's buffer is free again).
+    if (n_kb > 0) {
+        issue(0, 0);
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
         __syncthreads();
     }
-    if (kb + 2 < n_kb) {
-        load_block(kb + 2, rk0, rv0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(0, kb);
-        store_block(1, rk1, rv1);
+    for (int kb = 0; kb < n_kb; ++kb) {
+        const int st = kb & 1;
+        if (kb + 1 < n_kb) issue(kb + 1, st ^ 1);
+        compute(st, kb);
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
         __syncthreads();
-        compute(1, kb + 1);
-        store_block(0, rk0, rv0);
-        __syncthreads();
-        compute(0, kb + 2);
-    } else if (kb + 1 < n_kb) {
-        compute(0, kb);
-        store_block(1, rk1, rv1);
-        __syncthreads();
-        compute(1, kb + 1);
-    } else if (kb < n_kb) {
-        compute(0, kb);
     }
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
     if (n_seg > 1) {
@@ -622,7 +648,7 @@ SplitPlan split_plan(const AttnRange* t, int n, int n_q_heads, int head_dim) {
     // traffic), each at least 512 keys long.
     const int want = (int)std::min<int64_t>((kSplitUnits + units - 1) / units,
                                             (max_kv + 511) / 512);
-    p.seg_keys = ((max_kv + want - 1) / want + KB32 - 1) / KB32 * KB32;
+    p.seg_keys = ((max_kv + want - 1) / want + KBL - 1) / KBL * KBL;
     p.max_seg = (max_kv + p.seg_keys - 1) / p.seg_keys;
     if (p.max_seg <= 1) return SplitPlan{};
     p.bytes = (size_t)n * n_q_heads * p.max_seg * QT32 * (head_dim * sizeof(bf16) + 2 * sizeof(float));
@@ -645,7 +671,7 @@ hipError_t launch32(const AttnArgs& a0, const AttnTiles& tl, void* ws, size_t ws
     }
     const int64_t blocks = (int64_t)tl.n * a.n_q_heads * a.max_seg;
     if (blocks > INT_MAX) return hipErrorInvalidValue;
-    hipLaunchKernelGGL((attention32_kernel<D>), dim3((unsigned)blocks), dim3(kT32), 0, s, a, tl);
+    hipLaunchKernelGGL((attention64_kernel<D>), dim3((unsigned)blocks), dim3(kT32), 0, s, a, tl);
     if (sp.bytes)
         hipLaunchKernelGGL((attention_combine_kernel<D>), dim3(tl.n * (QT32 / kCombQ), a.n_q_heads),
                            dim3(256), 0, s, a, tl);
