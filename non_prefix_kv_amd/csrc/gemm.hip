@@ -331,7 +331,9 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
 }
 
 // ---------------------------------------------------------------------------
-// bf16 path with direct-to-LDS loads.  Each buffer_load ... lds of a wave
+// bf16 path with direct-to-LDS loads (the four-wave 128x128 kernel above
+// remains the f32 path and the fallback for K not a multiple of 256).  Each
+// buffer_load ... lds of a wave
 // writes 64 x 16 B to consecutive LDS bytes: the 8 lanes of one tile row
 // fetch that row's 16-byte chunks in swizzled order, so the LDS image is the
 // same conflict-free layout as above without staging registers or LDS store
@@ -376,17 +378,17 @@ __device__ __forceinline__ void wait_vm() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Epilogue of the direct-to-LDS kernel, staged through LDS so that global
-// traffic is row-contiguous: every wave writes its 64x64 fp32 block into a
-// row-major 128 x (128 + 8) tile (the 8-float pad puts the two half-waves of
-// a store on disjoint banks), then each thread finishes 4 consecutive
-// columns of 16 rows: one 16-byte residual / RoPE-table load and one vector
-// store per row.  `lds` is free, 16-byte aligned memory of >= 128*136 floats.
+// Epilogue of the direct-to-LDS kernels, staged through LDS so that global
+// traffic is row-contiguous: every wave writes (or adds) its 64x64 fp32
+// block into a row-major 128 x (128 + 8) tile (the 8-float pad puts the two
+// half-waves of a store on disjoint banks), then each thread finishes 4
+// consecutive columns of 128 / (NTH / 32) rows: one 16-byte residual /
+// RoPE-table load and one vector store per row.  `lds` is free, 16-byte
+// aligned memory of >= 128*136 floats.
 constexpr int kEpiLd = BN + 8;
-template <int EPI>
-__device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const floatx16 (&acc)[2][2],
-                                             int m_tile, int n_tile, int wm, int wn, int lane,
-                                             float* lds) {
+template <bool ADD>
+__device__ __forceinline__ void stage_acc(const floatx16 (&acc)[2][2], int wm, int wn, int lane,
+                                          float* lds) {
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -395,9 +397,16 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const floatx16 (
             for (int e = 0; e < 16; ++e) {
                 const int r = wm * 64 + i * 32 + 8 * (e / 4) + 4 * (lane / 32) + e % 4;
                 const int c = wn * 64 + j * 32 + lane % 32;
-                lds[r * kEpiLd + c] = acc[i][j][e];
+                if (ADD) lds[r * kEpiLd + c] += acc[i][j][e];
+                else lds[r * kEpiLd + c] = acc[i][j][e];
             }
-    __syncthreads();
+}
+
+template <int EPI, int NTH>
+__device__ __forceinline__ void epilogue_finish(const GemmArgs& g, int m_tile, int n_tile,
+                                                const float* lds) {
+    constexpr int RS = NTH / 32;                  // rows per pass
+    constexpr int NP = BM / RS;                   // passes
     const int t = threadIdx.x;
     const int cc = (t % 32) * 4;                  // first of this thread's 4 columns
     const int row0 = m_tile * BM + t / 32;
@@ -408,8 +417,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const floatx16 (
         const int gc = (oc / 32) * 64 + oc % 32;
         const int col = n_tile * (BN / 2) + oc;
 #pragma unroll 4
-        for (int p = 0; p < 16; ++p) {
-            const int rl = t / 32 + 8 * p, row = row0 + 8 * p;
+        for (int p = 0; p < NP; ++p) {
+            const int rl = t / 32 + RS * p, row = row0 + RS * p;
             if (row >= g.M) break;
             const float2 gt = *reinterpret_cast<const float2*>(&lds[rl * kEpiLd + gc]);
             const float2 up = *reinterpret_cast<const float2*>(&lds[rl * kEpiLd + gc + 32]);
@@ -440,8 +449,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const floatx16 (
         }
         const int hd = local % g.head_dim;         // multiple of 4: pairs (hd, hd+1), (hd+2, hd+3)
 #pragma unroll 4
-        for (int p = 0; p < 16; ++p) {
-            const int rl = t / 32 + 8 * p, row = row0 + 8 * p;
+        for (int p = 0; p < NP; ++p) {
+            const int rl = t / 32 + RS * p, row = row0 + RS * p;
             if (row >= g.M) break;
             const floatx4 x = *reinterpret_cast<const floatx4*>(&lds[rl * kEpiLd + cc]);
             floatx4 y = x;
@@ -462,8 +471,8 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const floatx16 (
     // STORE_F32 / RESID: fp32 rows; vector path when the row length allows
     const bool vec = (g.N % 4) == 0;
 #pragma unroll 4
-    for (int p = 0; p < 16; ++p) {
-        const int rl = t / 32 + 8 * p, row = row0 + 8 * p;
+    for (int p = 0; p < NP; ++p) {
+        const int rl = t / 32 + RS * p, row = row0 + RS * p;
         if (row >= g.M) break;
         floatx4 y = *reinterpret_cast<const floatx4*>(&lds[rl * kEpiLd + cc]);
         float* dst = static_cast<float*>(g.out0) + (int64_t)row * g.N + col;
@@ -482,11 +491,24 @@ __device__ __forceinline__ void epilogue_lds(const GemmArgs& g, const floatx16 (
 }
 
 
+
+// The direct-to-LDS kernel: a 128x128 tile per workgroup of eight waves, two
+// per SIMD, and a 4 x 32 KB ring.  Waves w and w + 4 compute the same 64x64
+// block over different halves of every K stage (16-wide steps 0-1 and 2-3),
+// so while one waits for fragments or at the barrier the other keeps the
+// SIMD's matrix unit busy; the two partial blocks are added in LDS before
+// the epilogue.  LDS bytes per MFMA are those of four waves of 64x64 over
+// whole stages, and each wave issues 4 of the stage's 32 copies.  Measured
+// on MI355X against that four-wave form: 832 x 4096 x 11008 955 vs 890
+// TFLOP/s, 832 x 22016 x 4096 788 vs 761; one wave per SIMD left the matrix
+// units idle in every s_waitcnt and barrier (40% busy).
+constexpr int kThreads8 = 512;
 template <int EPI, int S>
-__global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(GemmArgs g) {
+__global__ __launch_bounds__(kThreads8, 1) void gemm_dma8_kernel(GemmArgs g) {
     static_assert(S >= 3 && S <= 4, "stages");
     constexpr int BK = 64;                    // bf16 per stage row (128 B)
     constexpr int HALF = BM * BK;             // elements of the A (then B) part of a stage
+    constexpr int DPS = 4;                    // copies per wave per stage
     __shared__ __attribute__((aligned(16))) bf16 sm0[S * 2 * HALF];   // stage ring
     auto stage = [&](auto ic) -> bf16* { return sm0 + decltype(ic)::value * 2 * HALF; };
 
@@ -502,53 +524,56 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(GemmArgs g) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar descriptors
-    const int wm = wave >> 1, wn = wave & 1;
+    const int kh = wave >> 2;                 // which half of each K stage
+    const int wm = (wave >> 1) & 1, wn = wave & 1;
     const int Kb = g.K * 2;                   // bytes per row
 
-    // This wave loads rows 32*wave .. +31 of the A tile and of the B tile.
-    const bf16* a_base = static_cast<const bf16*>(g.a) + ((int64_t)m_tile * BM + 32 * wave) * g.K;
-    const int a_bytes = slice_bytes((int64_t)g.M - (int64_t)m_tile * BM - 32 * wave, Kb);
+    // This wave copies rows 16*wave .. +15 of the A tile and of the B tile.
+    const bf16* a_base = static_cast<const bf16*>(g.a) + ((int64_t)m_tile * BM + 16 * wave) * g.K;
+    const int64_t a_left = (int64_t)g.M - (int64_t)m_tile * BM - 16 * wave;
     const bf16* b_base;
-    int64_t b_rows;
+    int64_t b_left;
     if (EPI == EPI_SWIGLU) {
-        const int oc0 = n_tile * (BN / 2) + (wave >> 1) * 32;
-        b_base = static_cast<const bf16*>((wave & 1) ? g.b1 : g.b0) + (int64_t)oc0 * g.K;
-        b_rows = g.N - oc0;
+        // B rows 32 s .. 32 s + 31 of the tile: gate (s even) or up (s odd)
+        // rows of output columns n_tile*64 + (s/2)*32 ..; this wave's 16 rows
+        // are the (wave % 2)-th half of slice s = wave / 2
+        const int s = wave >> 1;
+        const int oc0 = n_tile * (BN / 2) + (s >> 1) * 32 + (wave & 1) * 16;
+        b_base = static_cast<const bf16*>((s & 1) ? g.b1 : g.b0) + (int64_t)oc0 * g.K;
+        b_left = g.N - oc0;
     } else if (EPI == EPI_QKV) {
-        // the whole 128-column tile lies inside one of q, k, v
         const int c0 = n_tile * BN;
         const void* mat;
         int local, rows;
         if (c0 < g.n0) { mat = g.b0; local = c0; rows = g.n0; }
         else if (c0 < g.n0 + g.n1) { mat = g.b1; local = c0 - g.n0; rows = g.n1; }
         else { mat = g.b2; local = c0 - g.n0 - g.n1; rows = g.N - g.n0 - g.n1; }
-        b_base = static_cast<const bf16*>(mat) + ((int64_t)local + 32 * wave) * g.K;
-        b_rows = rows - local - 32 * wave;
+        b_base = static_cast<const bf16*>(mat) + ((int64_t)local + 16 * wave) * g.K;
+        b_left = rows - local - 16 * wave;
     } else {
-        b_base = static_cast<const bf16*>(g.b0) + ((int64_t)n_tile * BN + 32 * wave) * g.K;
-        b_rows = g.N - (int64_t)n_tile * BN - 32 * wave;
+        b_base = static_cast<const bf16*>(g.b0) + ((int64_t)n_tile * BN + 16 * wave) * g.K;
+        b_left = g.N - (int64_t)n_tile * BN - 16 * wave;
     }
-    const int b_bytes = slice_bytes(b_rows, Kb);
+    const int a_bytes = (int)(a_left < 0 ? 0 : (a_left > 16 ? 16 : a_left)) * Kb;
+    const int b_bytes = (int)(b_left < 0 ? 0 : (b_left > 16 ? 16 : b_left)) * Kb;
 
     // Lane i fetches row i/8 (of 8) at LDS slot i%8, i.e. global chunk
-    // slot ^ key(row), key(r) = (r/2) % 8; rows 8j.. of the wave's 32 differ
-    // in key by 4 for odd j.
+    // slot ^ key(row), key(r) = (r/2) % 8; the second 8 rows of the wave's
+    // 16 differ in key by 4.
     const int r8 = lane >> 3, slot = lane & 7;
     const int v_even = r8 * Kb + ((slot ^ (r8 >> 1)) & 7) * 16;
     const int v_odd = r8 * Kb + ((slot ^ ((r8 >> 1) + 4)) & 7) * 16;
 
     const int KT = g.K / BK;
     auto issue = [&](int kt, bf16* buf) {
-        // stages past the end read nothing: an empty range makes every access miss
-        const bool live = kt < KT;
+        const bool live = kt < KT;            // stages past the end read nothing
         const i32x4 xa = make_rsrc(a_base, live ? a_bytes : 0);
         const i32x4 xb = make_rsrc(b_base, live ? b_bytes : 0);
-        const int ko = kt * 128;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int vo = (j & 1) ? v_odd : v_even;
-            const int so = ko + 8 * j * Kb;
-            const uint32_t da = (uint32_t)reinterpret_cast<uintptr_t>(buf + (32 * wave + 8 * j) * BK);
+        for (int j = 0; j < 2; ++j) {
+            const int vo = j ? v_odd : v_even;
+            const int so = kt * 128 + 8 * j * Kb;
+            const uint32_t da = (uint32_t)reinterpret_cast<uintptr_t>(buf + (16 * wave + 8 * j) * BK);
             dma16(xa, vo, so, da);
             dma16(xb, vo, so, da + HALF * 2);
         }
@@ -563,6 +588,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(GemmArgs g) {
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
     const int fr = lane & 31, fk = (lane >> 5) * 8;
+    const int ka = 32 * kh, kb2 = 32 * kh + 16;    // this wave's two 16-wide steps
     auto read_frags = [&](const bf16* buf, int ks, bf16x8 (&fa)[2], bf16x8 (&fb)[2]) {
 #pragma unroll
         for (int i = 0; i < 2; ++i)
@@ -578,14 +604,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(GemmArgs g) {
 #pragma unroll
             for (int j = 0; j < 2; ++j) mfma32(acc[i][j], fa[i], fb[j]);
     };
-    // One K stage out of buffer I (its first fragments already in fa0/fb0).
-    // The barrier that publishes stage kt+1 sits between the second and
-    // third 16-wide steps, so it overlaps queued MFMAs; after it the buffer
-    // of stage kt-1 is refilled with stage kt+S-1 and the first fragments of
-    // stage kt+1 are read while the last MFMAs of stage kt run.
-    bf16x8 fa0[2], fb0[2], fa1[2], fb1[2];
-    // Keeps each region's 4 MFMAs interleaved one to one with the 4 fragment
-    // reads of the next 16-wide step (the reads then return under the MFMAs).
     auto interleave = [&]() {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -593,22 +611,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(GemmArgs g) {
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
         }
     };
+    bf16x8 fa0[2], fb0[2], fa1[2], fb1[2];
+    // One K stage out of buffer I (this wave's first fragments already in
+    // fa0/fb0): the second step's fragments are read under the first step's
+    // MFMAs; the barrier publishing stage kt+1 follows; the copies of stage
+    // kt+S-1 go out between the second step's MFMAs, and the next stage's
+    // first fragments are read last.
     auto step = [&](auto ic, int kt) {
         constexpr int I = decltype(ic)::value;
         const bf16* buf = stage(ic);
-        read_frags(buf, 16, fa1, fb1);
+        read_frags(buf, kb2, fa1, fb1);
         mfma_step(fa0, fb0);
         interleave();
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(buf, 32, fa0, fb0);
-        mfma_step(fa1, fb1);
-        interleave();
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vm<(S - 3) * 8>();
+        wait_vm<(S - 3) * DPS>();
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(buf, 48, fa1, fb1);
-        // the copies of stage kt+S-1 go out between the MFMAs of this step
         {
             const int kn = kt + S - 1;
             bf16* dst = stage(std::integral_constant<int, (I + S - 1) % S>{});
@@ -617,28 +635,27 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(GemmArgs g) {
             const i32x4 xb = make_rsrc(b_base, live ? b_bytes : 0);
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
-                mfma32(acc[t >> 1][t & 1], fa0[t >> 1], fb0[t & 1]);
-                const int vo = (t & 1) ? v_odd : v_even;
-                const int so = kn * 128 + 8 * t * Kb;
-                const uint32_t da =
-                    (uint32_t)reinterpret_cast<uintptr_t>(dst + (32 * wave + 8 * t) * BK);
-                dma16(xa, vo, so, da);
-                dma16(xb, vo, so, da + HALF * 2);
+                mfma32(acc[t >> 1][t & 1], fa1[t >> 1], fb1[t & 1]);
+                if (t < 2) {
+                    const int vo = t ? v_odd : v_even;
+                    const int so = kn * 128 + 8 * t * Kb;
+                    const uint32_t da =
+                        (uint32_t)reinterpret_cast<uintptr_t>(dst + (16 * wave + 8 * t) * BK);
+                    dma16(xa, vo, so, da);
+                    dma16(xb, vo, so, da + HALF * 2);
+                }
             }
         }
         __builtin_amdgcn_sched_barrier(0);
-        // (after the last stage this reads a buffer of zeros that is never used)
-        read_frags(stage(std::integral_constant<int, (I + 1) % S>{}), 0, fa0, fb0);
-        mfma_step(fa1, fb1);
-        interleave();
-        __builtin_amdgcn_sched_barrier(0);
+        // (after the last stage this reads a buffer that is never used)
+        read_frags(stage(std::integral_constant<int, (I + 1) % S>{}), ka, fa0, fb0);
     };
     issue(0, stage(std::integral_constant<int, 0>{}));
     issue(1, stage(std::integral_constant<int, 1>{}));
     if constexpr (S > 3) issue(2, stage(std::integral_constant<int, 2>{}));
-    wait_vm<(S - 2) * 8>();
+    wait_vm<(S - 2) * DPS>();
     __builtin_amdgcn_s_barrier();
-    read_frags(sm0, 0, fa0, fb0);
+    read_frags(sm0, ka, fa0, fb0);
     for (int kt = 0; kt < KT; kt += S) {     // KT is a multiple of S
         step(std::integral_constant<int, 0>{}, kt);
         step(std::integral_constant<int, 1>{}, kt + 1);
@@ -650,7 +667,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_dma_kernel(GemmArgs g) {
     wait_vm<0>();
     __syncthreads();
     static_assert(S * 2 * HALF * 2 >= BM * kEpiLd * 4, "epilogue staging fits the stage ring");
-    epilogue_lds<EPI>(g, acc, m_tile, n_tile, wm, wn, lane, reinterpret_cast<float*>(sm0));
+    float* lds = reinterpret_cast<float*>(sm0);
+    if (kh == 1) stage_acc<false>(acc, wm, wn, lane, lds);
+    __syncthreads();
+    if (kh == 0) stage_acc<true>(acc, wm, wn, lane, lds);
+    __syncthreads();
+    epilogue_finish<EPI, kThreads8>(g, m_tile, n_tile, lds);
 }
 
 template <typename T, int EPI>
@@ -983,8 +1005,8 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
     const int m_tiles = (g.M + BM - 1) / BM;
     const int cols = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
     const int n_tiles = (g.N + cols - 1) / cols;
-    hipLaunchKernelGGL((gemm_dma_kernel<EPI, kDmaStages>), dim3(m_tiles * n_tiles),
-                       dim3(kThreads), 0, s, g);
+    hipLaunchKernelGGL((gemm_dma8_kernel<EPI, kDmaStages>), dim3(m_tiles * n_tiles),
+                       dim3(kThreads8), 0, s, g);
     return hipGetLastError();
 }
 
