@@ -983,11 +983,12 @@ int num_cus() {
 
 // Tile choice.  Both kernels run one workgroup per CU (256 at a time); a
 // 256x256 tile costs about 3 times a 128x128 one (4x the work at ~1.3x the
-// efficiency; 2.8 for the q/k/v product, whose RoPE epilogue is relatively
-// cheaper on large tiles).  Compare whole rounds of workgroups; ties go to
-// the small tile.  Measured on MI355X (bf16): large products (>= 4096 rows)
-// 1.2-1.3x faster on 256x256; at ~832 rows the q/k/v product gains
-// (880 vs 790 TF/s) while N = 4096 products lose badly (340 vs 760).
+// efficiency; 3.2 for the q/k/v product).  Compare whole rounds of
+// workgroups; ties go to the small tile.  Measured on MI355X (bf16): large
+// products (>= 4096 rows) 1.2-1.3x faster on 256x256; N = 4096 products at
+// ~832 rows lose badly there (340 vs 760 TF/s); the q/k/v product at ~832
+// rows (3 rounds of 128x128 against 1 of 256x256) runs 4% faster on the
+// eight-wave 128x128 kernel (4.79 vs 5.00 ms per 7B step).
 bool big_ok(int epi, const GemmArgs& g) {
     if (g.K % (BBK * kBigStages) != 0 || (int64_t)g.K * 2 * 64 + 64 >= (int64_t)1 << 31) return false;
     if (epi == EPI_QKV && (g.n0 % BBN != 0 || g.n1 % BBN != 0)) return false;
@@ -996,7 +997,7 @@ bool big_ok(int epi, const GemmArgs& g) {
     const int64_t big = ((g.M + BBM - 1) / BBM) * ((rows_b + BBN - 1) / BBN);
     const int64_t cus = num_cus();
     const double cost_small = (double)((small + cus - 1) / cus);
-    const double cost_big = (epi == EPI_QKV ? 2.8 : 3.0) * ((big + cus - 1) / cus);
+    const double cost_big = (epi == EPI_QKV ? 3.2 : 3.0) * ((big + cus - 1) / cus);
     return cost_big < cost_small;
 }
 
