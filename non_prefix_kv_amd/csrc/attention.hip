@@ -373,6 +373,7 @@ __global__ __launch_bounds__(kT32, 2) void attention64_kernel(AttnArgs a, const 
 #pragma unroll
     for (int w = 1; w < kT32 / 64; ++w) bmax = max(bmax, sred[w]);
     const int nk = min(n_kv, bmax - a.kv_pos0 + 1);
+    if (a.part_nk && seg == 0 && h == 0 && tid == 0) a.part_nk[qt] = nk;   // for the merge pass
     // Key segment of this workgroup (whole range when not split).
     const int n_seg = a.seg_keys > 0 ? max(1, (nk + a.seg_keys - 1) / a.seg_keys) : 1;
     if (seg >= n_seg) return;                          // uniform over the workgroup
@@ -562,55 +563,46 @@ __global__ __launch_bounds__(kT32, 2) void attention64_kernel(AttnArgs a, const 
 
 // Merges the segment partials of split tiles: with per-segment max m_s and
 // sum l_s, O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, M = max_s m_s.
-// Tiles that were not split were finished by their only workgroup.  One
-// thread per (query, 4 output dims); workgroups cover 8 queries of one tile
-// and head, so the merge is spread over the whole GPU.
-constexpr int kCombQ = 8;
+// Tiles that were not split were finished by their only workgroup.  D/8
+// threads per query, 8 output dims each (16-byte loads of the bf16
+// partials); a workgroup covers 2048 / D queries of one tile and head, so
+// the merge is spread over the whole GPU.  The number of segments of a tile
+// comes from the visible-key count its attention workgroups recorded.
 template <int D>
 __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a, const AttnTiles tl) {
-    constexpr int C4 = D / 4;                       // float4 chunks per query row
-    const int per_tile = QT32 / kCombQ;
+    constexpr int TPQ = D / 8;                      // threads per query
+    constexpr int QPW = 256 / TPQ;                  // queries per workgroup
+    const int per_tile = QT32 / QPW;
     const int qt = blockIdx.x / per_tile, qg = blockIdx.x % per_tile;
     const int h = blockIdx.y;
     const AttnRange& tile = tl.t[qt];
-    const int nq_t = tile.nq;
-    if (qg * kCombQ >= nq_t) return;
-    // key extent of the tile, as seen by its attention workgroups
-    __shared__ int wmx[4];
-    int mx = INT_MIN;
-    for (int i = threadIdx.x; i < nq_t; i += 256) mx = max(mx, a.q_pos[tile.q0 + i]);
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) mx = max(mx, __shfl_xor(mx, o, 64));
-    if ((threadIdx.x & 63) == 0) wmx[threadIdx.x >> 6] = mx;
-    __syncthreads();
-    mx = max(max(wmx[0], wmx[1]), max(wmx[2], wmx[3]));
-    const int nk = min(tile.n_kv, mx - a.kv_pos0 + 1);
-    const int n_seg = max(1, (nk + a.seg_keys - 1) / a.seg_keys);
+    const int ql = qg * QPW + (int)threadIdx.x / TPQ;
+    if (ql >= tile.nq) return;
+    const int n_seg = max(1, (a.part_nk[qt] + a.seg_keys - 1) / a.seg_keys);
     if (n_seg <= 1) return;
-    const int ql = qg * kCombQ + (int)threadIdx.x / C4;
-    const int c = ((int)threadIdx.x % C4) * 4;
-    if ((int)threadIdx.x >= kCombQ * C4 || ql >= nq_t) return;
+    const int c = ((int)threadIdx.x % TPQ) * 8;
     const int64_t slot0 = ((int64_t)qt * a.n_q_heads + h) * a.max_seg;
     float M = -INFINITY;
     for (int sg = 0; sg < n_seg; ++sg)
         M = fmaxf(M, a.part_ml[((slot0 + sg) * QT32 + ql) * 2]);
     const float Mu = M == -INFINITY ? 0.f : M;
     float L = 0.f;
-    floatx4 acc{0.f, 0.f, 0.f, 0.f};
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
     for (int sg = 0; sg < n_seg; ++sg) {
         const float* pm = a.part_ml + ((slot0 + sg) * QT32 + ql) * 2;
-        const bf16x4 ov = *reinterpret_cast<const bf16x4*>(a.part_o + ((slot0 + sg) * QT32 + ql) * D + c);
+        float ov[8];
+        Vec8<bf16>::load(a.part_o + ((slot0 + sg) * QT32 + ql) * D + c, ov);
         const float wl = __builtin_amdgcn_exp2f(pm[0] - Mu) * pm[1];   // weight x segment sum
         L += wl;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] += wl * static_cast<float>(ov[e]);
+        for (int e = 0; e < 8; ++e) acc[e] += wl * ov[e];
     }
     const float inv = L > 0.f ? 1.0f / L : 0.f;
-    bf16x4 v{static_cast<bf16>(acc[0] * inv), static_cast<bf16>(acc[1] * inv),
-             static_cast<bf16>(acc[2] * inv), static_cast<bf16>(acc[3] * inv)};
-    *reinterpret_cast<bf16x4*>(static_cast<bf16*>(a.out) +
-                               (int64_t)(tile.q0 + ql) * a.n_q_heads * D + h * D + c) = v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] *= inv;
+    Vec8<bf16>::store(static_cast<bf16*>(a.out) + (int64_t)(tile.q0 + ql) * a.n_q_heads * D + h * D + c,
+                      acc);
 }
 
 // Query tiles of height `qth` cut from the ranges, ordered by an estimate of
@@ -651,7 +643,8 @@ SplitPlan split_plan(const AttnRange* t, int n, int n_q_heads, int head_dim) {
     p.seg_keys = ((max_kv + want - 1) / want + KBL - 1) / KBL * KBL;
     p.max_seg = (max_kv + p.seg_keys - 1) / p.seg_keys;
     if (p.max_seg <= 1) return SplitPlan{};
-    p.bytes = (size_t)n * n_q_heads * p.max_seg * QT32 * (head_dim * sizeof(bf16) + 2 * sizeof(float));
+    p.bytes = (size_t)n * n_q_heads * p.max_seg * QT32 * (head_dim * sizeof(bf16) + 2 * sizeof(float)) +
+              (size_t)n * sizeof(int);
     return p;
 }
 
@@ -664,16 +657,18 @@ hipError_t launch32(const AttnArgs& a0, const AttnTiles& tl, void* ws, size_t ws
     a.max_seg = sp.max_seg;
     a.part_o = nullptr;
     a.part_ml = nullptr;
+    a.part_nk = nullptr;
     if (sp.bytes) {
         if (!ws || ws_bytes < sp.bytes) return hipErrorInvalidValue;
         a.part_o = static_cast<bf16*>(ws);
         a.part_ml = reinterpret_cast<float*>(a.part_o + (size_t)tl.n * a.n_q_heads * sp.max_seg * QT32 * D);
+        a.part_nk = reinterpret_cast<int*>(a.part_ml + (size_t)tl.n * a.n_q_heads * sp.max_seg * QT32 * 2);
     }
     const int64_t blocks = (int64_t)tl.n * a.n_q_heads * a.max_seg;
     if (blocks > INT_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL((attention64_kernel<D>), dim3((unsigned)blocks), dim3(kT32), 0, s, a, tl);
     if (sp.bytes)
-        hipLaunchKernelGGL((attention_combine_kernel<D>), dim3(tl.n * (QT32 / kCombQ), a.n_q_heads),
+        hipLaunchKernelGGL((attention_combine_kernel<D>), dim3(tl.n * (QT32 / (256 / (D / 8))), a.n_q_heads),
                            dim3(256), 0, s, a, tl);
     return hipGetLastError();
 }

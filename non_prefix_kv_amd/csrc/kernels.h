@@ -270,6 +270,7 @@ struct AttnArgs {
     int max_seg;
     bf16* part_o;       // [tiles][Hq][max_seg][tile height][dh], normalized per segment
     float* part_ml;     // [tiles][Hq][max_seg][tile height][2]
+    int* part_nk;       // [tiles] keys visible to each tile (written by its attention pass)
 };
 
 // Workspace bytes the split partials of these ranges need (0: no split).
