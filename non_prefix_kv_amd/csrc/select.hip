@@ -112,6 +112,7 @@ struct SelState {
 
 __device__ SelState radix_threshold(const float* __restrict__ dev, int n, int k,
                                     uint32_t* hist, int* bcast) {
+    __shared__ int wtot[4];
     uint32_t prefix = 0, mask = 0;
     int kk = k;
     for (int shift = 24; shift >= 0; shift -= 8) {
@@ -122,15 +123,25 @@ __device__ SelState radix_threshold(const float* __restrict__ dev, int n, int k,
             if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
         }
         __syncthreads();
-        if (threadIdx.x == 0) {
-            int cum = 0, d = 255;
-            for (int i = 0; i < 256; ++i) {
-                const int h = (int)hist[i];
-                if (cum + h >= kk) { d = i; break; }
-                cum += h;
+        // The digit is the first bin whose inclusive count reaches kk: a
+        // scan over the 256 bins by the first four waves (one bin per lane).
+        int h = 0, inc = 0;
+        if (threadIdx.x < 256) {
+            h = (int)hist[threadIdx.x];
+            inc = h;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const int t = __shfl_up(inc, o, 64);
+                if ((threadIdx.x & 63) >= o) inc += t;
             }
-            bcast[0] = d;
-            bcast[1] = kk - cum;
+            if ((threadIdx.x & 63) == 63) wtot[threadIdx.x >> 6] = inc;
+        }
+        __syncthreads();
+        if (threadIdx.x < 256) {
+            for (int w = 0; w < (int)(threadIdx.x >> 6); ++w) inc += wtot[w];
+            const int exc = inc - h;
+            if (exc < kk && inc >= kk) { bcast[0] = (int)threadIdx.x; bcast[1] = kk - exc; }
+            if (threadIdx.x == 255 && inc < kk) { bcast[0] = 255; bcast[1] = kk - inc; }
         }
         __syncthreads();
         prefix |= (uint32_t)bcast[0] << shift;
