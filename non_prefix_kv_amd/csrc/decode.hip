@@ -11,6 +11,8 @@
 // so it is bound by HBM bandwidth: every wave streams whole contiguous weight
 // rows with 16-byte loads, many waves per CU keep enough bytes in flight, and
 // the epilogues (RoPE, residual, SwiGLU) run on the reduced dot products.
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace cb {
@@ -301,6 +303,170 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(DecodeAttnAr
     }
 }
 
+// Decode attention on the matrix cores, for query-head groups (GQA): one
+// wave per (KV head, 64-key segment), no workgroup barriers (each wave owns
+// its LDS slice).  The group's query heads are the 16 columns of
+// v_mfma_f32_16x16x32_bf16 (unused ones zero): S^T = K Q^T with K rows
+// loaded straight into the A operand (lane l: key l % 16, dims
+// 8 (l / 16) ..), then the softmax over each query column (4 keys per lane,
+// 4 lanes per column), then O = P V with P taken from the score registers
+// as the A operand (its keys ordered 4q+0..3, 16+4q+0..3 per 32-key step)
+// and V read from LDS by transposing 8-byte reads that return exactly those
+// 4-key runs for one dimension.  V reaches LDS by buffer_load ... lds into
+// unpadded rows whose 16-byte chunks sit at chunk ^ key(row) so that the
+// transposing reads of 16 rows x 2 chunks touch distinct banks.
+// Output: the same per (query head, segment) maximum, sum of exponentials
+// and unnormalized output as decode_attention_kernel.
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4_t dec_rsrc(const void* base, int bytes) {
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    return i32x4_t{__builtin_amdgcn_readfirstlane((int)(uint32_t)p),
+                   __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xFFFF)),
+                   __builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+__device__ __forceinline__ void dec_dma16(i32x4_t rsrc, int voff, uint32_t m0) {
+    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(m0)
+                 : "memory");
+}
+template <int DH> __device__ __forceinline__ int dec_vkey(int r) {
+    return DH == 128 ? 2 * (r & 7) : 2 * ((r >> 1) & 3);
+}
+
+template <int DH>
+__global__ __launch_bounds__(kThreads) void decode_attention_mfma_kernel(DecodeAttnArgs a) {
+    constexpr int RB = DH * 2;                 // bytes per V row in LDS
+    constexpr int CPR = RB / 16;               // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;              // rows per copy instruction
+    constexpr int NKS = DH / 32;               // 32-dim steps of the scores
+    constexpr int NT = DH / 16;                // 16-dim output tiles
+    __shared__ __attribute__((aligned(16))) unsigned char sv_all[kWaves][kSegKeys * RB];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int h = blockIdx.y, G = a.group;
+    const int nseg = (a.n_ctx + 1 + kSegKeys - 1) / kSegKeys;
+    const int seg = blockIdx.x * kWaves + wave;
+    if (seg >= nseg) return;                   // wave-uniform; no barriers below
+    const int kvd = a.n_kv_heads * DH;
+    const int j0 = seg * kSegKeys, n_keys = a.n_ctx + 1;
+    const int c16 = lane & 15, q4 = lane >> 4;
+    unsigned char* sv = sv_all[wave];
+    const bf16* vbase = static_cast<const bf16*>(a.v) + (int64_t)j0 * kvd + h * DH;
+    // V rows of the cache into LDS (rows past the cache read as zero)
+    {
+        const int rows_c = min(kSegKeys, max(0, a.n_ctx - j0));
+        const i32x4_t rs = dec_rsrc(vbase, rows_c * kvd * 2);
+        const uint32_t l0 = (uint32_t)reinterpret_cast<uintptr_t>(sv);
+#pragma unroll
+        for (int c = 0; c < kSegKeys / RPI; ++c) {
+            const int r = c * RPI + lane / CPR, slot = lane % CPR;
+            dec_dma16(rs, r * kvd * 2 + ((slot ^ dec_vkey<DH>(r)) & (CPR - 1)) * 16, l0 + c * RPI * RB);
+        }
+    }
+    // K rows straight into the A operand; Q of the group as the B operand
+    bf16x8 kf[4][NKS], qf[NKS];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        const int j = j0 + 16 * t + c16;
+        const bf16* kr = j < a.n_ctx ? static_cast<const bf16*>(a.k) + (int64_t)j * kvd + h * DH
+                                     : static_cast<const bf16*>(a.k_new) + h * DH;
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            if (j < n_keys) kf[t][s] = *reinterpret_cast<const bf16x8*>(kr + 32 * s + 8 * q4);
+            else
+#pragma unroll
+                for (int e = 0; e < 8; ++e) kf[t][s][e] = static_cast<bf16>(0.f);
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+        if (c16 < G)
+            qf[s] = *reinterpret_cast<const bf16x8*>(static_cast<const bf16*>(a.q) +
+                                                    (int64_t)(h * G + c16) * DH + 32 * s + 8 * q4);
+        else
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qf[s][e] = static_cast<bf16>(0.f);
+    }
+    floatx4 st[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        st[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+            st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][s], qf[s], st[t], 0, 0, 0);
+    }
+    // softmax of query column c16 over the segment's keys 16 t + 4 q4 + i
+    float m = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float s = j0 + 16 * t + 4 * q4 + i < n_keys ? st[t][i] * a.scale : -INFINITY;
+            st[t][i] = s;
+            m = fmaxf(m, s);
+        }
+    m = fmaxf(m, __shfl_xor(m, 16, 64));
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    float l = 0.f;
+    bf16x8 pa[2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float p = st[t][i] == -INFINITY ? 0.f : __expf(st[t][i] - m);
+            l += p;
+            pa[t >> 1][(t & 1) * 4 + i] = static_cast<bf16>(p);
+        }
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+    // the new key's V row (not in the cache) goes to its slot by plain stores
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0): the copies have landed
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    if (a.n_ctx >= j0 && a.n_ctx < j0 + kSegKeys && lane < CPR) {
+        const int r = a.n_ctx - j0;
+        *reinterpret_cast<u32x4*>(sv + r * RB + ((lane ^ dec_vkey<DH>(r)) & (CPR - 1)) * 16) =
+            *reinterpret_cast<const u32x4*>(static_cast<const bf16*>(a.v_new) + h * DH + lane * 8);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);                     // lgkmcnt(0): stores visible to the wave
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // O = P V, 16 dims per tile, 32 keys per step
+    floatx4 o[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) o[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    typedef short i16x4 __attribute__((ext_vector_type(4)));
+    typedef short i16x8 __attribute__((ext_vector_type(8)));
+    typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int r = 32 * u + 4 * q4 + (c16 >> 2);           // + 16 for the second run
+            const int col = 16 * nt + 4 * (c16 & 3);
+            const int off = r * RB + ((((col >> 3) ^ dec_vkey<DH>(r)) & (CPR - 1)) << 4) + (col & 7) * 2;
+            const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sv + off));
+            const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sv + off + 16 * RB));
+            const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[u], __builtin_bit_cast(bf16x8, w), o[nt], 0, 0, 0);
+        }
+    // lane l holds O[query 4 q4 + i][dim 16 nt + c16]; stats of query c16 in every lane
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int g = 4 * q4 + i;
+        if (g < G) {
+            const int64_t slot = (int64_t)(h * G + g) * nseg + seg;
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) a.part_o[slot * DH + 16 * nt + c16] = o[nt][i];
+        }
+    }
+    if (q4 == 0 && c16 < G) {
+        const int64_t slot = (int64_t)(h * G + c16) * nseg + seg;
+        a.part_ml[2 * slot] = m;
+        a.part_ml[2 * slot + 1] = l;
+    }
+}
+
 // Merge of the key segments.  Workgroup (query head, 32-dimension slice):
 // every thread first forms the largest segment maximum M and the weighted
 // sum of exponentials over all segments (a few floats per segment), then the
@@ -383,7 +549,10 @@ template <typename T, int DH>
 hipError_t decode_attn_t(const DecodeAttnArgs& a, hipStream_t s) {
     const int nseg = (a.n_ctx + 1 + kSegKeys - 1) / kSegKeys;
     const dim3 grid(a.n_kv_heads, nseg);
-    if (a.group == 1)
+    if (std::is_same<T, bf16>::value && a.group > 1)
+        hipLaunchKernelGGL((decode_attention_mfma_kernel<DH>), dim3((nseg + kWaves - 1) / kWaves, a.n_kv_heads),
+                           dim3(kThreads), 0, s, a);
+    else if (a.group == 1)
         hipLaunchKernelGGL((decode_attention_kernel<T, DH, 1>), grid, dim3(kThreads), 0, s, a);
     else
         hipLaunchKernelGGL((decode_attention_kernel<T, DH, 8>), grid, dim3(kThreads), 0, s, a);

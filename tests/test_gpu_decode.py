@@ -35,13 +35,22 @@ def decode_inputs(shape, n_ctx, dt, seed, pad=0):
     return case, k, v, buf_k, buf_v, case.x0[n_ctx]
 
 
+_DECODE_SHAPES = {
+    "gqa": ModelShape(2, 256, 14, 2, 128, 512, vocab=512),      # 7 query heads per KV head
+    "gqa8": ModelShape(2, 256, 16, 2, 128, 512, vocab=512),     # 8
+    "gqa64": ModelShape(2, 256, 8, 2, 64, 512, vocab=512),      # 4, head dim 64
+}
+
+
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("shape_name,n_ctx,pad", [("tiny", 416, 0), ("tiny", 0, 3),
                                                   ("tiny", 255, 7), ("gqa", 600, 0),
-                                                  ("gqa", 1, 0)])
+                                                  ("gqa", 1, 0), ("gqa", 0, 0), ("gqa", 63, 2),
+                                                  ("gqa", 64, 0), ("gqa8", 300, 5),
+                                                  ("gqa64", 130, 1)])
 def test_decode_step_vs_oracle(lib, dt, shape_name, n_ctx, pad):
     print(f"[decode] dt={dt} {shape_name} n_ctx={n_ctx} pad={pad}", flush=True)
-    shape = TINY if shape_name == "tiny" else ModelShape(2, 256, 14, 2, 128, 512, vocab=512)
+    shape = TINY if shape_name == "tiny" else _DECODE_SHAPES[shape_name]
     case, k, v, bk, bv, x_new = decode_inputs(shape, n_ctx, dt, seed=7 + n_ctx, pad=pad)
     model = make_model(lib, case, dt)
     L = shape.n_layers
