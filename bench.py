@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--selection-study", action="store_true",
                     help="single-request workloads: cross-layer rank correlation of the KV "
                          "deviation, and output error vs full prefill for selection variants")
+    ap.add_argument("--kv-on-device", action="store_true",
+                    help="single-request workloads whose chunk caches default to pinned host "
+                         "memory: keep them in HBM instead (the load-overlap reference)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-profile", action="store_true")
     ap.add_argument("--no-full-compare", action="store_true")
@@ -929,6 +932,8 @@ def main():
         w = dataclasses.replace(w, r_bp=args.r_bp)
     if args.schedule is not None:
         w = dataclasses.replace(w, schedule_kind=args.schedule)
+    if args.kv_on_device:
+        w = dataclasses.replace(w, kv_on_host=False)
     S = w.shape
     N, Nc, L = w.n_tokens, w.n_chunk_tokens, S.n_layers
     log(f"[bench] workload {w.name}: building inputs")
@@ -970,6 +975,15 @@ def main():
                       "suffix_tokens": w.n_suffix, "recompute_bp": w.r_bp,
                       "schedule": w.schedule_kind, "kept_rows_per_layer": sched,
                       "chunk_kv_on_host": w.kv_on_host, "chunk_kv_format": args.kv_format}}
+    if w.kv_on_host and args.kv_format == "plain":
+        # row a1 streamed from pinned host memory: bytes per step against the
+        # measured pinned copy rate (the step hides them if it is not slower
+        # than with the caches in HBM: compare with --kv-on-device)
+        per_step = 2.0 * Nc * S.kv_dim * 2 * L
+        peak = h2d_throughput(torch)
+        out["h2d"] = {"bytes_per_step": per_step, "pinned_copy_gbs": peak / 1e9,
+                      "needed_gbs_at_step_rate": per_step / (ms / 1e3) / 1e9,
+                      "fraction_of_pinned_rate": per_step / (ms / 1e3) / peak}
 
     # per-kernel-class durations (HIP events around each launch, own pass)
     if not args.no_profile:
