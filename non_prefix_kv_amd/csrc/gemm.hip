@@ -332,7 +332,7 @@ __global__ __launch_bounds__(kThreads, 2) void gemm_kernel(GemmArgs g) {
 
 // ---------------------------------------------------------------------------
 // bf16 path with direct-to-LDS loads (the four-wave 128x128 kernel above
-// remains the f32 path and the fallback for K not a multiple of 256).  Each
+// remains the f32 path and the fallback for K not a multiple of 64).  Each
 // buffer_load ... lds of a wave
 // writes 64 x 16 B to consecutive LDS bytes: the 8 lanes of one tile row
 // fetch that row's 16-byte chunks in swizzled order, so the LDS image is the
@@ -493,7 +493,9 @@ __device__ __forceinline__ void epilogue_finish(const GemmArgs& g, int m_tile, i
 
 
 // The direct-to-LDS kernel: a 128x128 tile per workgroup of eight waves, two
-// per SIMD, and a 4 x 32 KB ring.  Waves w and w + 4 compute the same 64x64
+// per SIMD, and a ring of S x 32 KB stages (S = 5 fills the 160 KB of LDS:
+// 3-4 stages in flight; against 4 stages, 2% off the 7B step).  K need not
+// be a multiple of S: the stages past the last full turn run in a tail.  Waves w and w + 4 compute the same 64x64
 // block over different halves of every K stage (16-wide steps 0-1 and 2-3),
 // so while one waits for fragments or at the barrier the other keeps the
 // SIMD's matrix unit busy; the two partial blocks are added in LDS before
@@ -505,7 +507,7 @@ __device__ __forceinline__ void epilogue_finish(const GemmArgs& g, int m_tile, i
 constexpr int kThreads8 = 512;
 template <int EPI, int S>
 __global__ __launch_bounds__(kThreads8, 1) void gemm_dma8_kernel(GemmArgs g) {
-    static_assert(S >= 3 && S <= 4, "stages");
+    static_assert(S >= 3 && S <= 5, "stages");
     constexpr int BK = 64;                    // bf16 per stage row (128 B)
     constexpr int HALF = BM * BK;             // elements of the A (then B) part of a stage
     constexpr int DPS = 4;                    // copies per wave per stage
@@ -653,15 +655,22 @@ __global__ __launch_bounds__(kThreads8, 1) void gemm_dma8_kernel(GemmArgs g) {
     issue(0, stage(std::integral_constant<int, 0>{}));
     issue(1, stage(std::integral_constant<int, 1>{}));
     if constexpr (S > 3) issue(2, stage(std::integral_constant<int, 2>{}));
+    if constexpr (S > 4) issue(3, stage(std::integral_constant<int, 3>{}));
     wait_vm<(S - 2) * DPS>();
     __builtin_amdgcn_s_barrier();
     read_frags(sm0, ka, fa0, fb0);
-    for (int kt = 0; kt < KT; kt += S) {     // KT is a multiple of S
+    int kt = 0;
+    for (; kt + S <= KT; kt += S) {
         step(std::integral_constant<int, 0>{}, kt);
         step(std::integral_constant<int, 1>{}, kt + 1);
         step(std::integral_constant<int, 2>{}, kt + 2);
         if constexpr (S > 3) step(std::integral_constant<int, 3>{}, kt + 3);
+        if constexpr (S > 4) step(std::integral_constant<int, 4>{}, kt + 4);
     }
+    if (kt < KT) step(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < KT) step(std::integral_constant<int, 1>{}, kt + 1);
+    if constexpr (S > 3) if (kt + 2 < KT) step(std::integral_constant<int, 2>{}, kt + 2);
+    if constexpr (S > 4) if (kt + 3 < KT) step(std::integral_constant<int, 3>{}, kt + 3);
     // the trailing copies (empty ranges) still write LDS: let them land, and
     // let every wave finish its last fragment reads, before reusing LDS
     wait_vm<0>();
@@ -690,8 +699,8 @@ hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
 // Per K element this halves both the L2 -> LDS traffic and the LDS fragment
 // reads of the 128x128 kernel, which bound that kernel on large shapes.
 // LDS rows are 4 chunks of 16 bytes stored at chunk ^ ((row / 4) % 4) (zero
-// bank conflicts for 32x32 fragment reads, measured).  Same 4-stage ring,
-// mid-stage barrier and staged epilogue as the 128x128 kernel; the epilogue
+// bank conflicts for 32x32 fragment reads, measured).  A 4-stage ring, a
+// mid-stage barrier and a staged epilogue, as in the 128x128 kernel; the epilogue
 // goes through LDS in four passes of 64 rows.
 constexpr int BBM = 256, BBN = 256, BBK = 32, kBigStages = 4;
 constexpr int kBigLd = BBN + 8;
@@ -959,7 +968,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
     big_epilogue<EPI>(g, acc, m_tile, n_tile, wm, wn, lane, reinterpret_cast<float*>(smem));
 }
 
-constexpr int kDmaStages = 4;            // LDS ring depth of the bf16 kernel
+constexpr int kDmaStages = 5;            // LDS ring depth of the bf16 kernel
 
 template <int EPI>
 hipError_t launch_big(const GemmArgs& g, hipStream_t s) {
@@ -1011,10 +1020,10 @@ hipError_t launch_dma(const GemmArgs& g, hipStream_t s) {
     return hipGetLastError();
 }
 
-// The direct-to-LDS kernel needs whole 16-byte chunks per row, buffer
-// offsets below 2^31 and, for q/k/v, tiles that do not straddle matrices.
+// The direct-to-LDS kernel needs whole 64-element stages, buffer offsets
+// below 2^31 and, for q/k/v, tiles that do not straddle matrices.
 bool dma_ok(int epi, const GemmArgs& g) {
-    if (g.K % (64 * kDmaStages) != 0 || (int64_t)g.K * 2 * 32 + 128 >= (int64_t)1 << 31)
+    if (g.K % 64 != 0 || (int64_t)g.K * 2 * 32 + 128 >= (int64_t)1 << 31)
         return false;
     if (epi == EPI_QKV && (g.n0 % BN != 0 || g.n1 % BN != 0)) return false;
     return true;
