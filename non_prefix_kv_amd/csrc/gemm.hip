@@ -518,10 +518,13 @@ __global__ __launch_bounds__(kThreads8, 1) void gemm_dma8_kernel(GemmArgs g) {
     const int n_cols_per_tile = (EPI == EPI_SWIGLU) ? BN / 2 : BN;
     const int n_tiles = (g.N + n_cols_per_tile - 1) / n_cols_per_tile;
     const int tile = xcd_remap(blockIdx.x, m_tiles * n_tiles);
-    const int group = tile / (kGroupM * n_tiles);
-    const int first_m = group * kGroupM;
-    const int gm = min(m_tiles - first_m, kGroupM);
-    const int in_group = tile - group * kGroupM * n_tiles;
+    // rasterization groups: 4 row tiles for q/k/v (measured 2% faster than 8
+    // there, 3% slower for gate/up)
+    constexpr int GM = EPI == EPI_QKV ? 4 : kGroupM;
+    const int group = tile / (GM * n_tiles);
+    const int first_m = group * GM;
+    const int gm = min(m_tiles - first_m, GM);
+    const int in_group = tile - group * GM * n_tiles;
     const int m_tile = first_m + in_group % gm, n_tile = in_group / gm;
 
     const int tid = threadIdx.x, lane = tid & 63;
