@@ -971,6 +971,311 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
     big_epilogue<EPI>(g, acc, m_tile, n_tile, wm, wn, lane, reinterpret_cast<float*>(smem));
 }
 
+// ---------------------------------------------------------------------------
+// Mid-size tiles for products of roughly 800-900 rows: 224x192 per
+// workgroup.  Four row tiles cover up to 896 rows (128-row tiles pad 832
+// rows to 896 as well, 256-row tiles to 1024), and a 12288-wide q/k/v
+// product is exactly 256 tiles, one round of workgroups.  Four waves in a
+// 2x2 grid, each 112x96 as 7x6 blocks of v_mfma_f32_16x16x32_bf16; per
+// output element this moves 0.58x the L2 -> LDS bytes of the 128x128 tile.
+// K advances 32 per stage: one MFMA covers a whole stage, lane l supplying
+// row l % 16 and the 16-byte chunk l / 16 of a 64-byte LDS row.  Rows are
+// unpadded with chunk c stored at slot c ^ ((row / 2) % 4), so the eight
+// rows a group of eight lanes reads fall on distinct banks.  A ring of S
+// stages (26 KB each) is filled by direct-to-LDS copies, 26 per stage (14
+// A and 12 B blocks of 16 rows); wave w issues blocks w, w + 4, ..., so
+// waves 2 and 3 pad their seventh copy with an empty one into a spare
+// kilobyte, which keeps the vmcnt bookkeeping uniform.  The epilogue
+// stages the accumulators through LDS in two passes of 112 rows.
+constexpr int MBM = 224, MBN = 192, MBK = 32;
+constexpr int kMidStages = 5;
+constexpr int kMidCopies = 7;                         // copies per wave per stage
+constexpr int kMidABytes = MBM * MBK * 2;             // A part of a stage
+constexpr int kMidStage = (MBM + MBN) * MBK * 2;      // bytes per stage
+constexpr int kMidLd = MBN + 4;                       // epilogue staging row (floats)
+
+__device__ __forceinline__ int mid_swz(int r, int chunk) {   // byte offset in a stage part
+    return r * 64 + ((chunk ^ (r >> 1)) & 3) * 16;
+}
+
+// Accumulates in place in AGPRs.  Written as inline assembly: with the
+// builtin, the register allocator rotated half of the 168 accumulator
+// registers through VGPRs once per loop iteration (252 extra moves per two
+// K stages).  The assembler statement is opaque to the hazard recognizer,
+// so the kernel separates the last MFMA from any read of its result with
+// explicit wait states (mid_acc_fence).  Consecutive MFMAs on one
+// accumulator are 42 instructions apart in the main loop.
+__device__ __forceinline__ void mfma16x32(floatx4& acc, const bf16x8& a, const bf16x8& b) {
+    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+struct MidSrc {
+    const bf16* p;      // first row of a 16-row copy block
+    int64_t left;       // rows of its matrix from there on
+};
+
+// B rows 16 j .. 16 j + 15 of tile n_tile.  Gate/up: the 96 rows of wave
+// column wn are 48 gate rows then the 48 up rows of the same output columns.
+// q/k/v: blocks never straddle two matrices (row counts are multiples of 16).
+template <int EPI>
+__device__ __forceinline__ MidSrc mid_b_rows(const GemmArgs& g, int n_tile, int j) {
+    if (EPI == EPI_SWIGLU) {
+        const int wn = j / 6, jj = j % 6;
+        const int oc0 = n_tile * (MBN / 2) + 48 * wn + 16 * (jj % 3);
+        return {static_cast<const bf16*>(jj < 3 ? g.b0 : g.b1) + (int64_t)oc0 * g.K,
+                (int64_t)g.N - oc0};
+    }
+    const int r0 = n_tile * MBN + 16 * j;
+    if (EPI == EPI_QKV) {
+        if (r0 < g.n0) return {static_cast<const bf16*>(g.b0) + (int64_t)r0 * g.K, (int64_t)g.n0 - r0};
+        if (r0 < g.n0 + g.n1) {
+            const int l = r0 - g.n0;
+            return {static_cast<const bf16*>(g.b1) + (int64_t)l * g.K, (int64_t)g.n1 - l};
+        }
+        const int l = r0 - g.n0 - g.n1;
+        return {static_cast<const bf16*>(g.b2) + (int64_t)l * g.K,
+                (int64_t)(g.N - g.n0 - g.n1) - l};
+    }
+    return {static_cast<const bf16*>(g.b0) + (int64_t)r0 * g.K, (int64_t)g.N - r0};
+}
+
+// Rows row0 .. row0 + 111 of the tile, staged in LDS as [112][kMidLd] fp32.
+template <int EPI>
+__device__ __forceinline__ void mid_finish(const GemmArgs& g, int row0, int n_tile,
+                                           const float* lds) {
+    const int t = threadIdx.x;
+    if (EPI == EPI_SWIGLU) {
+        // 4 output columns per item: gate at LDS column 96 wn + o, up 48 further
+        for (int it = t; it < 112 * 24; it += 256) {
+            const int rl = it / 24, oc = 4 * (it % 24);
+            const int row = row0 + rl;
+            if (row >= g.M) break;
+            const int lc = 96 * (oc / 48) + oc % 48;
+            const floatx4 gt = *reinterpret_cast<const floatx4*>(&lds[rl * kMidLd + lc]);
+            const floatx4 up = *reinterpret_cast<const floatx4*>(&lds[rl * kMidLd + lc + 48]);
+            const int col = n_tile * (MBN / 2) + oc;
+            bf16* dst = static_cast<bf16*>(g.out0) + (int64_t)row * g.N + col;
+            if (col + 3 < g.N) {
+                *reinterpret_cast<bf16x4*>(dst) =
+                    bf16x4{static_cast<bf16>(silu_f(gt[0]) * up[0]), static_cast<bf16>(silu_f(gt[1]) * up[1]),
+                           static_cast<bf16>(silu_f(gt[2]) * up[2]), static_cast<bf16>(silu_f(gt[3]) * up[3])};
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (col + k < g.N) dst[k] = static_cast<bf16>(silu_f(gt[k]) * up[k]);
+            }
+        }
+        return;
+    }
+    for (int it = t; it < 112 * 48; it += 256) {
+        const int rl = it / 48, cg = 4 * (it % 48);
+        const int row = row0 + rl;
+        if (row >= g.M) break;
+        const int col = n_tile * MBN + cg;
+        if (col >= g.N) continue;
+        const floatx4 x = *reinterpret_cast<const floatx4*>(&lds[rl * kMidLd + cg]);
+        if (EPI == EPI_QKV) {
+            // the 4 columns lie in one of q, k, v (row counts are multiples of 16)
+            bf16* base;
+            int width, local;
+            bool rope;
+            if (col < g.n0) { base = static_cast<bf16*>(g.out0); width = g.n0; local = col; rope = true; }
+            else if (col < g.n0 + g.n1) {
+                base = static_cast<bf16*>(g.out1); width = g.n1; local = col - g.n0; rope = true;
+            } else {
+                base = static_cast<bf16*>(g.out2); width = g.N - g.n0 - g.n1;
+                local = col - g.n0 - g.n1; rope = false;
+            }
+            floatx4 y = x;
+            if (rope) {
+                const int hd = local % g.head_dim;        // multiple of 4: pairs (hd, hd+1), (hd+2, hd+3)
+                const floatx4 cs = *reinterpret_cast<const floatx4*>(
+                    &g.rope.tab[(int64_t)g.pos[row] * g.rope.half + (hd >> 1)]);
+                y[0] = x[0] * cs[0] - x[1] * cs[1];
+                y[1] = x[0] * cs[1] + x[1] * cs[0];
+                y[2] = x[2] * cs[2] - x[3] * cs[3];
+                y[3] = x[2] * cs[3] + x[3] * cs[2];
+            }
+            *reinterpret_cast<bf16x4*>(base + (int64_t)row * width + local) =
+                bf16x4{static_cast<bf16>(y[0]), static_cast<bf16>(y[1]), static_cast<bf16>(y[2]),
+                       static_cast<bf16>(y[3])};
+        } else {
+            float* dst = static_cast<float*>(g.out0) + (int64_t)row * g.N + col;
+            const float* res = nullptr;
+            if (EPI == EPI_RESID) res = g.resid + (int64_t)(g.ridx ? g.ridx[row] : row) * g.N + col;
+            if ((g.N % 4) == 0 && col + 3 < g.N) {
+                floatx4 y = x;
+                if (EPI == EPI_RESID) y += *reinterpret_cast<const floatx4*>(res);
+                *reinterpret_cast<floatx4*>(dst) = y;
+            } else {
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (col + k < g.N) dst[k] = x[k] + (EPI == EPI_RESID ? res[k] : 0.f);
+            }
+        }
+    }
+}
+
+template <int EPI, int S>
+__global__ __launch_bounds__(kThreads, 1) void gemm_mid_kernel(GemmArgs g) {
+    static_assert(S >= 3 && S <= 6 && (S - 2) * kMidCopies < 64, "stages");
+    __shared__ __attribute__((aligned(16))) char smem[S * kMidStage + 1024];
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
+    const uint32_t spare = lds0 + S * kMidStage;         // target of the empty copies
+
+    const int m_tiles = (g.M + MBM - 1) / MBM;
+    const int cols = EPI == EPI_SWIGLU ? MBN / 2 : MBN;
+    const int n_tiles = (g.N + cols - 1) / cols;
+    const int tile = xcd_remap(blockIdx.x, m_tiles * n_tiles);
+    const int group = tile / (kGroupM * n_tiles);
+    const int first_m = group * kGroupM;
+    const int gm = min(m_tiles - first_m, kGroupM);
+    const int in_group = tile - group * kGroupM * n_tiles;
+    const int m_tile = first_m + in_group % gm, n_tile = in_group / gm;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: scalar descriptors
+    const int wm = wave >> 1, wn = wave & 1;
+    const int Kb = g.K * 2;
+
+    // Copies 0-3 of this wave move A blocks 4 c + wave (rows 16 b .. 16 b + 15
+    // of the tile; blocks 14 and 15 do not exist: they lie past the
+    // descriptor's range, read as zero and land in the spare kilobyte);
+    // copies 4-6 move B blocks 4 (c - 4) + wave.  One descriptor covers the
+    // A tile, one per copy the B blocks (which may come from different
+    // matrices).
+    const int64_t a_left = (int64_t)g.M - (int64_t)m_tile * MBM;
+    const i32x4 da = make_rsrc(static_cast<const bf16*>(g.a) + (int64_t)m_tile * MBM * g.K,
+                               (int)(a_left <= 0 ? 0 : (a_left >= MBM ? MBM : a_left)) * Kb);
+    const bf16* b_src[3];
+    int b_bytes[3];
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+        const MidSrc sr = mid_b_rows<EPI>(g, n_tile, 4 * c + wave);
+        b_src[c] = sr.p;
+        b_bytes[c] = (int)(sr.left <= 0 ? 0 : (sr.left >= 16 ? 16 : sr.left)) * Kb;
+    }
+    // Lane i copies row i / 4 of a block into slot i % 4: global chunk
+    // slot ^ key(row), key(r) = (r / 2) % 4 (the same for every block).
+    const int r4 = lane >> 2, sl = lane & 3;
+    const int voff = r4 * Kb + ((sl ^ (r4 >> 1)) & 3) * 16;
+    const int KT = g.K / MBK;
+    const i32x4 none = make_rsrc(g.a, 0);
+    auto copy = [&](int c, int kt, int slot) {
+        const bool live = kt < KT;                       // stages past the end read nothing
+        if (c < 4) {
+            const int b = 4 * c + wave;
+            const uint32_t d = b < 14 ? lds0 + slot * kMidStage + 16 * b * 64 : spare;
+            dma16(live ? da : none, voff + 16 * b * Kb, kt * 64, d);
+        } else {
+            const int j = 4 * (c - 4) + wave;
+            const i32x4 r = make_rsrc(b_src[c - 4], live ? b_bytes[c - 4] : 0);
+            dma16(r, voff, kt * 64, lds0 + slot * kMidStage + kMidABytes + 16 * j * 64);
+        }
+    };
+
+    floatx4 acc[7][6];
+#pragma unroll
+    for (int i = 0; i < 7; ++i)
+#pragma unroll
+        for (int j = 0; j < 6; ++j) acc[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    const int fr = lane & 15, fq = lane >> 4;
+    auto frag = [&](int off) { return *reinterpret_cast<const bf16x8*>(smem + off); };
+    const int a_off = mid_swz(wm * 112 + fr, fq);             // + 16 i rows: + 1024 i bytes
+    const int b_off = kMidABytes + mid_swz(wn * 96 + fr, fq); // + 16 j rows
+    bf16x8 fa[7], fb[6], na[7], nb[6];
+    // One K stage out of ring slot `slot`, its fragments in (ca, cb): the 42
+    // MFMAs are interleaved with the 13 fragment reads of stage kt + 1 into
+    // (xa, xb) and this wave's copies of stage kt + S - 1 into the slot that
+    // stage kt - 1 left.  Slots are run-time values (a rolled loop keeps the
+    // accumulators in place); they only offset LDS addresses.
+    auto step = [&](int kt, int slot, const bf16x8 (&ca)[7], const bf16x8 (&cb)[6],
+                    bf16x8 (&xa)[7], bf16x8 (&xb)[6]) {
+        const int nxt = slot + 1 == S ? 0 : slot + 1;
+        const int fill = slot == 0 ? S - 1 : slot - 1;
+        const char* nbase = smem + nxt * kMidStage;
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<(S - 3) * kMidCopies>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int t = 0; t < 42; ++t) {
+            mfma16x32(acc[t / 6][t % 6], ca[t / 6], cb[t % 6]);
+            if (t % 3 == 2 && t / 3 < 13) {
+                const int q = t / 3;
+                if (q < 7) xa[q] = *reinterpret_cast<const bf16x8*>(nbase + a_off + 1024 * q);
+                else xb[q - 7] = *reinterpret_cast<const bf16x8*>(nbase + b_off + 1024 * (q - 7));
+            }
+            if (t % 6 == 5) copy(t / 6, kt + S - 1, fill);
+        }
+#pragma unroll
+        for (int k = 0; k < 13; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    for (int s0 = 0; s0 < S - 1; ++s0)
+#pragma unroll
+        for (int c = 0; c < kMidCopies; ++c) copy(c, s0, s0);
+    wait_vm<(S - 2) * kMidCopies>();
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int i = 0; i < 7; ++i) fa[i] = frag(a_off + 1024 * i);
+#pragma unroll
+    for (int j = 0; j < 6; ++j) fb[j] = frag(b_off + 1024 * j);
+    // KT is even (K is a multiple of 64): two stages per iteration, the
+    // fragment registers alternating
+    int slot = 0;
+    for (int kt = 0; kt < KT; kt += 2) {
+        step(kt, slot, fa, fb, na, nb);
+        slot = slot + 1 == S ? 0 : slot + 1;
+        step(kt + 1, slot, na, nb, fa, fb);
+        slot = slot + 1 == S ? 0 : slot + 1;
+    }
+    // wait states between the last MFMA and the first read of an accumulator
+    // (more than the 11 an 8-pass MFMA needs), then a fence per accumulator
+    // so that no read is scheduled above the wait
+    asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < 7; ++i)
+#pragma unroll
+        for (int j = 0; j < 6; ++j) asm volatile("" : "+a"(acc[i][j]));
+    // trailing (empty) copies still write LDS: let them land, and every
+    // wave finish its fragment reads, before the ring becomes staging space
+    wait_vm<0>();
+    __syncthreads();
+    static_assert(112 * kMidLd * 4 <= S * kMidStage, "epilogue staging fits the ring");
+    float* lds = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        if (wm == q) {
+#pragma unroll
+            for (int i = 0; i < 7; ++i)
+#pragma unroll
+                for (int j = 0; j < 6; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        lds[(16 * i + 4 * fq + e) * kMidLd + 96 * wn + 16 * j + fr] = acc[i][j][e];
+        }
+        __syncthreads();
+        mid_finish<EPI>(g, m_tile * MBM + 112 * q, n_tile, lds);
+        __syncthreads();
+    }
+}
+
+template <int EPI>
+hipError_t launch_mid(const GemmArgs& g, hipStream_t s) {
+    const int m_tiles = (g.M + MBM - 1) / MBM;
+    const int cols = (EPI == EPI_SWIGLU) ? MBN / 2 : MBN;
+    const int n_tiles = (g.N + cols - 1) / cols;
+    hipLaunchKernelGGL((gemm_mid_kernel<EPI, kMidStages>), dim3(m_tiles * n_tiles), dim3(kThreads),
+                       0, s, g);
+    return hipGetLastError();
+}
+
 constexpr int kDmaStages = 5;            // LDS ring depth of the bf16 kernel
 
 template <int EPI>
@@ -993,24 +1298,47 @@ int num_cus() {
     return n;
 }
 
-// Tile choice.  Both kernels run one workgroup per CU (256 at a time); a
-// 256x256 tile costs about 3 times a 128x128 one (4x the work at ~1.3x the
-// efficiency; 3.2 for the q/k/v product).  Compare whole rounds of
-// workgroups; ties go to the small tile.  Measured on MI355X (bf16): large
+// Tile choice.  All three bf16 kernels run one workgroup per CU (256 at a
+// time); compare whole rounds of workgroups, each round priced in units of
+// one 128x128 tile.  A 256x256 tile costs about 3 of them (4x the work at
+// ~1.3x the efficiency; 3.2 for the q/k/v product), a 224x192 tile
+// kMidCost.  Ties go to the smaller tile.  Measured on MI355X (bf16): large
 // products (>= 4096 rows) 1.2-1.3x faster on 256x256; N = 4096 products at
-// ~832 rows lose badly there (340 vs 760 TF/s); the q/k/v product at ~832
-// rows (3 rounds of 128x128 against 1 of 256x256) runs 4% faster on the
-// eight-wave 128x128 kernel (4.79 vs 5.00 ms per 7B step).
-bool big_ok(int epi, const GemmArgs& g) {
+// ~832 rows lose badly there (340 vs 760 TF/s).
+constexpr double kMidCost = 2.1;
+enum TileKind { TILE_128, TILE_256, TILE_224x192 };
+
+bool big_shape_ok(int epi, const GemmArgs& g) {
     if (g.K % (BBK * kBigStages) != 0 || (int64_t)g.K * 2 * 64 + 64 >= (int64_t)1 << 31) return false;
     if (epi == EPI_QKV && (g.n0 % BBN != 0 || g.n1 % BBN != 0)) return false;
+    return true;
+}
+
+bool mid_shape_ok(int epi, const GemmArgs& g) {
+    // copy offsets reach 256 rows (16 blocks of 16) into the A tile
+    if (g.K % (2 * MBK) != 0 || (int64_t)g.K * 2 * 256 >= (int64_t)1 << 31) return false;
+    if (epi == EPI_QKV && g.head_dim % 4 != 0) return false;
+    return true;
+}
+
+TileKind choose_tile(int epi, const GemmArgs& g) {
     const int64_t rows_b = epi == EPI_SWIGLU ? 2 * (int64_t)g.N : g.N;   // B rows
-    const int64_t small = ((g.M + BM - 1) / BM) * ((rows_b + BN - 1) / BN);
-    const int64_t big = ((g.M + BBM - 1) / BBM) * ((rows_b + BBN - 1) / BBN);
     const int64_t cus = num_cus();
-    const double cost_small = (double)((small + cus - 1) / cus);
-    const double cost_big = (epi == EPI_QKV ? 3.2 : 3.0) * ((big + cus - 1) / cus);
-    return cost_big < cost_small;
+    auto rounds = [&](int bm, int bn) {
+        const int64_t tiles = ((g.M + bm - 1) / bm) * ((rows_b + bn - 1) / bn);
+        return (double)((tiles + cus - 1) / cus);
+    };
+    TileKind best = TILE_128;
+    double cost = rounds(BM, BN);
+    if (mid_shape_ok(epi, g)) {
+        const double c = kMidCost * rounds(MBM, MBN);
+        if (c < cost) { cost = c; best = TILE_224x192; }
+    }
+    if (big_shape_ok(epi, g)) {
+        const double c = (epi == EPI_QKV ? 3.2 : 3.0) * rounds(BBM, BBN);
+        if (c < cost) { cost = c; best = TILE_256; }
+    }
+    return best;
 }
 
 template <int EPI>
@@ -1035,7 +1363,17 @@ bool dma_ok(int epi, const GemmArgs& g) {
 template <typename T>
 hipError_t launch_dtype(int epi, const GemmArgs& g, hipStream_t s) {
     if constexpr (is_bf16<T>()) {
-        if (big_ok(epi, g)) {
+        const TileKind tk = choose_tile(epi, g);
+        if (tk == TILE_224x192) {
+            switch (epi) {
+                case EPI_STORE_F32: return launch_mid<EPI_STORE_F32>(g, s);
+                case EPI_QKV: return launch_mid<EPI_QKV>(g, s);
+                case EPI_RESID: return launch_mid<EPI_RESID>(g, s);
+                case EPI_SWIGLU: return launch_mid<EPI_SWIGLU>(g, s);
+            }
+            return hipErrorInvalidValue;
+        }
+        if (tk == TILE_256) {
             switch (epi) {
                 case EPI_STORE_F32: return launch_big<EPI_STORE_F32>(g, s);
                 case EPI_QKV: return launch_big<EPI_QKV>(g, s);

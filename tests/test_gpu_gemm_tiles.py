@@ -1,0 +1,47 @@
+"""Projection tiles at full model width.
+
+The GEMM launcher picks among three tile shapes (128x128, 224x192, 256x256)
+by the number of rows and output columns.  The blend at r = 15% runs its
+projections on ~832-947 rows, where the 224x192 tile takes the q/k/v and
+gate/up products (Llama-2-7B shape) and the q/k/v, O and down products
+(Llama-2-13B shape).  One-layer prefills at those row counts exercise each
+epilogue on that tile (RoPE at real positions on q/k/v tiles that straddle
+the q|k and k|v boundaries, SiLU(gate)*up on interleaved gate/up rows, the
+gathered residual) against the oracle's prefill."""
+import dataclasses
+import gc
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.helpers import rel_err
+from tests.gpu_helpers import dev, host, make_model
+from workloads import WORKLOADS, make_weights_np, make_embedding_np, make_tokens
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name,rows,pos0", [("llama7b-4k", 832, 0), ("llama7b-4k", 889, 1000),
+                                            ("llama13b-8k", 1664, 77)])
+def test_prefill_projection_tiles_vs_oracle(lib, name, rows, pos0):
+    shape = dataclasses.replace(WORKLOADS[name].shape, n_layers=1)
+    w = make_weights_np(shape, seed=3, dtype="bf16")
+    x = make_embedding_np(shape, seed=3, dtype="bf16")[make_tokens(shape, rows, seed=3)]
+    model = make_model(lib, types.SimpleNamespace(shape=shape, weights=w), "bf16")
+    k = torch.empty((1, rows, shape.n_kv_heads, shape.head_dim), dtype=torch.bfloat16,
+                    device="cuda")
+    v = torch.empty_like(k)
+    hid = torch.empty((rows, shape.d_model), device="cuda")
+    lib.cb_prefill(model, dev(x, "bf16"), rows, pos0, k, v, hid)
+    torch.cuda.synchronize()
+    rk, rv, outs = oracle.prefill(w, shape, x, pos0=pos0, dtype=np.float32)
+    assert rel_err(host(k), rk) < 2e-2
+    assert rel_err(host(v), rv) < 2e-2
+    assert rel_err(host(hid), outs[-1]) < 2e-2
+    model.close()
+    del model, k, v, hid
+    gc.collect()
+    torch.cuda.empty_cache()

@@ -155,7 +155,10 @@ def test_rmsnorm_vs_oracle(lib, dt, rows, d):
                                    (1600, 520, 384), (2048, 256, 128), (1537, 2000, 1152),
                                    (832, 4096, 4096), (1000, 1536, 2048), (640, 2816, 1536),
                                    (832, 22016, 1024), (700, 10000, 512), (947, 6000, 256),
-                                   (600, 20000, 320), (520, 30000, 192)])
+                                   (600, 20000, 320), (520, 30000, 192),
+                                   # 224x192 tiles (ragged rows and columns, M = 224, K = 64)
+                                   (832, 12288, 4096), (833, 12288, 192), (650, 12000, 320),
+                                   (224, 40000, 64)])
 def test_gemm_vs_definition(lib, dt, m, n, k):
     rng = np.random.default_rng(m * 7 + n)
     a = round_to(rng.standard_normal((m, k)), dt)
