@@ -1040,22 +1040,30 @@ __device__ __forceinline__ MidSrc mid_b_rows(const GemmArgs& g, int n_tile, int 
 }
 
 // Rows row0 .. row0 + 111 of the tile, staged in LDS as [112][kMidLd] fp32.
+// Each thread keeps one group of 4 columns (its output matrix, RoPE pair
+// index and residual column are fixed) and walks every 5th row (every
+// 10th for gate/up, whose groups are 4 output columns of 96), unrolled so
+// that the position, RoPE-table and residual loads of several rows are in
+// flight together.
 template <int EPI>
 __device__ __forceinline__ void mid_finish(const GemmArgs& g, int row0, int n_tile,
                                            const float* lds) {
     const int t = threadIdx.x;
     if (EPI == EPI_SWIGLU) {
-        // 4 output columns per item: gate at LDS column 96 wn + o, up 48 further
-        for (int it = t; it < 112 * 24; it += 256) {
-            const int rl = it / 24, oc = 4 * (it % 24);
+        if (t >= 240) return;
+        const int oc = 4 * (t % 24);                 // of the tile's 96 output columns
+        const int lc = 96 * (oc / 48) + oc % 48;     // gate at lc, up at lc + 48
+        const int col = n_tile * (MBN / 2) + oc;
+        if (col >= g.N) return;
+        const bool full = col + 3 < g.N;
+#pragma unroll 4
+        for (int rl = t / 24; rl < 112; rl += 10) {
             const int row = row0 + rl;
             if (row >= g.M) break;
-            const int lc = 96 * (oc / 48) + oc % 48;
             const floatx4 gt = *reinterpret_cast<const floatx4*>(&lds[rl * kMidLd + lc]);
             const floatx4 up = *reinterpret_cast<const floatx4*>(&lds[rl * kMidLd + lc + 48]);
-            const int col = n_tile * (MBN / 2) + oc;
             bf16* dst = static_cast<bf16*>(g.out0) + (int64_t)row * g.N + col;
-            if (col + 3 < g.N) {
+            if (full) {
                 *reinterpret_cast<bf16x4*>(dst) =
                     bf16x4{static_cast<bf16>(silu_f(gt[0]) * up[0]), static_cast<bf16>(silu_f(gt[1]) * up[1]),
                            static_cast<bf16>(silu_f(gt[2]) * up[2]), static_cast<bf16>(silu_f(gt[3]) * up[3])};
@@ -1067,30 +1075,32 @@ __device__ __forceinline__ void mid_finish(const GemmArgs& g, int row0, int n_ti
         }
         return;
     }
-    for (int it = t; it < 112 * 48; it += 256) {
-        const int rl = it / 48, cg = 4 * (it % 48);
-        const int row = row0 + rl;
-        if (row >= g.M) break;
-        const int col = n_tile * MBN + cg;
-        if (col >= g.N) continue;
-        const floatx4 x = *reinterpret_cast<const floatx4*>(&lds[rl * kMidLd + cg]);
-        if (EPI == EPI_QKV) {
-            // the 4 columns lie in one of q, k, v (row counts are multiples of 16)
-            bf16* base;
-            int width, local;
-            bool rope;
-            if (col < g.n0) { base = static_cast<bf16*>(g.out0); width = g.n0; local = col; rope = true; }
-            else if (col < g.n0 + g.n1) {
-                base = static_cast<bf16*>(g.out1); width = g.n1; local = col - g.n0; rope = true;
-            } else {
-                base = static_cast<bf16*>(g.out2); width = g.N - g.n0 - g.n1;
-                local = col - g.n0 - g.n1; rope = false;
-            }
+    if (t >= 240) return;
+    const int cg = 4 * (t % 48);
+    const int col = n_tile * MBN + cg;
+    if (col >= g.N) return;
+    if (EPI == EPI_QKV) {
+        // the 4 columns lie in one of q, k, v (row counts are multiples of 16)
+        bf16* base;
+        int width, local;
+        bool rope;
+        if (col < g.n0) { base = static_cast<bf16*>(g.out0); width = g.n0; local = col; rope = true; }
+        else if (col < g.n0 + g.n1) {
+            base = static_cast<bf16*>(g.out1); width = g.n1; local = col - g.n0; rope = true;
+        } else {
+            base = static_cast<bf16*>(g.out2); width = g.N - g.n0 - g.n1;
+            local = col - g.n0 - g.n1; rope = false;
+        }
+        const int pair = (local % g.head_dim) >> 1;   // even: pairs (pair, pair + 1)
+#pragma unroll 4
+        for (int rl = t / 48; rl < 112; rl += 5) {
+            const int row = row0 + rl;
+            if (row >= g.M) break;
+            const floatx4 x = *reinterpret_cast<const floatx4*>(&lds[rl * kMidLd + cg]);
             floatx4 y = x;
             if (rope) {
-                const int hd = local % g.head_dim;        // multiple of 4: pairs (hd, hd+1), (hd+2, hd+3)
                 const floatx4 cs = *reinterpret_cast<const floatx4*>(
-                    &g.rope.tab[(int64_t)g.pos[row] * g.rope.half + (hd >> 1)]);
+                    &g.rope.tab[(int64_t)g.pos[row] * g.rope.half + pair]);
                 y[0] = x[0] * cs[0] - x[1] * cs[1];
                 y[1] = x[0] * cs[1] + x[1] * cs[0];
                 y[2] = x[2] * cs[2] - x[3] * cs[3];
@@ -1099,19 +1109,26 @@ __device__ __forceinline__ void mid_finish(const GemmArgs& g, int row0, int n_ti
             *reinterpret_cast<bf16x4*>(base + (int64_t)row * width + local) =
                 bf16x4{static_cast<bf16>(y[0]), static_cast<bf16>(y[1]), static_cast<bf16>(y[2]),
                        static_cast<bf16>(y[3])};
+        }
+        return;
+    }
+    const bool vec = (g.N % 4) == 0 && col + 3 < g.N;
+#pragma unroll 4
+    for (int rl = t / 48; rl < 112; rl += 5) {
+        const int row = row0 + rl;
+        if (row >= g.M) break;
+        const floatx4 x = *reinterpret_cast<const floatx4*>(&lds[rl * kMidLd + cg]);
+        float* dst = static_cast<float*>(g.out0) + (int64_t)row * g.N + col;
+        const float* res = nullptr;
+        if (EPI == EPI_RESID) res = g.resid + (int64_t)(g.ridx ? g.ridx[row] : row) * g.N + col;
+        if (vec) {
+            floatx4 y = x;
+            if (EPI == EPI_RESID) y += *reinterpret_cast<const floatx4*>(res);
+            *reinterpret_cast<floatx4*>(dst) = y;
         } else {
-            float* dst = static_cast<float*>(g.out0) + (int64_t)row * g.N + col;
-            const float* res = nullptr;
-            if (EPI == EPI_RESID) res = g.resid + (int64_t)(g.ridx ? g.ridx[row] : row) * g.N + col;
-            if ((g.N % 4) == 0 && col + 3 < g.N) {
-                floatx4 y = x;
-                if (EPI == EPI_RESID) y += *reinterpret_cast<const floatx4*>(res);
-                *reinterpret_cast<floatx4*>(dst) = y;
-            } else {
 #pragma unroll
-                for (int k = 0; k < 4; ++k)
-                    if (col + k < g.N) dst[k] = x[k] + (EPI == EPI_RESID ? res[k] : 0.f);
-            }
+            for (int k = 0; k < 4; ++k)
+                if (col + k < g.N) dst[k] = x[k] + (EPI == EPI_RESID ? res[k] : 0.f);
         }
     }
 }
@@ -1305,7 +1322,7 @@ int num_cus() {
 // kMidCost.  Ties go to the smaller tile.  Measured on MI355X (bf16): large
 // products (>= 4096 rows) 1.2-1.3x faster on 256x256; N = 4096 products at
 // ~832 rows lose badly there (340 vs 760 TF/s).
-constexpr double kMidCost = 2.1;
+constexpr double kMidCost = 2.35;
 enum TileKind { TILE_128, TILE_256, TILE_224x192 };
 
 bool big_shape_ok(int epi, const GemmArgs& g) {
