@@ -1203,7 +1203,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mid_kernel(GemmArgs g) {
     const int b_off = kMidABytes + mid_swz(wn * 96 + fr, fq); // + 16 j rows
     bf16x8 fa[7], fb[6], na[7], nb[6];
     // One K stage out of ring slot `slot`, its fragments in (ca, cb): the 42
-    // MFMAs are interleaved with the 13 fragment reads of stage kt + 1 into
+    // MFMAs (A fragment i with B fragments 0-5) are interleaved with the 13
+    // fragment reads of stage kt + 1 into
     // (xa, xb) and this wave's copies of stage kt + S - 1 into the slot that
     // stage kt - 1 left.  Slots are run-time values (a rolled loop keeps the
     // accumulators in place); they only offset LDS addresses.
@@ -1219,19 +1220,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mid_kernel(GemmArgs g) {
 #pragma unroll
         for (int t = 0; t < 42; ++t) {
             mfma16x32(acc[t / 6][t % 6], ca[t / 6], cb[t % 6]);
-            if (t % 3 == 2 && t / 3 < 13) {
-                const int q = t / 3;
-                if (q < 7) xa[q] = *reinterpret_cast<const bf16x8*>(nbase + a_off + 1024 * q);
-                else xb[q - 7] = *reinterpret_cast<const bf16x8*>(nbase + b_off + 1024 * (q - 7));
+            // one read per two MFMAs over the first 26, B fragments first:
+            // the next stage's first six MFMAs use all of them, while A
+            // fragment i is first used by its MFMA 6 i
+            if (t % 2 == 1 && t / 2 < 13) {
+                const int q = t / 2;
+                if (q < 6) xb[q] = *reinterpret_cast<const bf16x8*>(nbase + b_off + 1024 * q);
+                else xa[q - 6] = *reinterpret_cast<const bf16x8*>(nbase + a_off + 1024 * (q - 6));
             }
             if (t % 6 == 5) copy(t / 6, kt + S - 1, fill);
         }
 #pragma unroll
         for (int k = 0; k < 13; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);   // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
     for (int s0 = 0; s0 < S - 1; ++s0)
