@@ -60,6 +60,41 @@ __global__ __launch_bounds__(kDevThreads) void deviation_kernel(
     if (lane == 0) dev[q.c_off + i] = acc;
 }
 
+// One workgroup per row, for launches with few rows (a steady layer
+// measures a few hundred): four waves split the row so that each thread has
+// only a few independent 16-byte loads, all issued before any arithmetic,
+// instead of one wave walking the whole row (latency-bound at ~145 rows).
+// Partial sums are combined in a fixed order.
+template <typename T>
+__global__ __launch_bounds__(kDevThreads) void deviation_row_kernel(
+    const T* __restrict__ kn, const T* __restrict__ vn, const T* __restrict__ kc,
+    const T* __restrict__ vc, const int* __restrict__ grow, const ReqTab t, int kv_dim,
+    int mode, float* __restrict__ dev) {
+    __shared__ float part[kDevThreads / 64];
+    const ReqRows& q = t.r[blockIdx.y];
+    const int i = blockIdx.x;
+    if (i >= q.n_c) return;                           // uniform over the workgroup
+    const int r = q.r_off + i;
+    const int64_t no = (int64_t)r * kv_dim;
+    const int64_t co = (int64_t)(grow ? grow[r] : r) * kv_dim;
+    float acc = 0.f;
+    if (mode != 2)
+        for (int c = threadIdx.x * 8; c < kv_dim; c += kDevThreads * 8)
+            acc += sq_diff8(kn + no + c, kc + co + c);
+    if (mode != 1)
+        for (int c = threadIdx.x * 8; c < kv_dim; c += kDevThreads * 8)
+            acc += sq_diff8(vn + no + c, vc + co + c);
+    acc = warp_sum(acc);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float sum = part[0];
+#pragma unroll
+        for (int w = 1; w < kDevThreads / 64; ++w) sum += part[w];
+        dev[q.c_off + i] = sum;
+    }
+}
+
 __global__ __launch_bounds__(kDevThreads) void given_scores_kernel(
     const float* __restrict__ scores, const ReqTab t, const int* __restrict__ pos_r,
     float* __restrict__ dev) {
@@ -223,6 +258,19 @@ hipError_t launch_deviation(int dtype, const void* k_new, const void* v_new,
     if (t.n > kMaxReq || kv_dim % 8 != 0) return hipErrorInvalidValue;
     for (int b = 0; b < t.n; ++b)
         if (t.r[b].n_c > t.max_c || t.r[b].n_c < 0) return hipErrorInvalidValue;
+    // few rows: a workgroup per row; many rows: a wave per row
+    if ((int64_t)t.max_c * t.n < 1024) {
+        dim3 grid(t.max_c, t.n), block(kDevThreads);
+        if (dtype == BF16)
+            hipLaunchKernelGGL(deviation_row_kernel<bf16>, grid, block, 0, s, (const bf16*)k_new,
+                               (const bf16*)v_new, (const bf16*)k_cached, (const bf16*)v_cached,
+                               grow, t, kv_dim, mode, dev);
+        else
+            hipLaunchKernelGGL(deviation_row_kernel<float>, grid, block, 0, s, (const float*)k_new,
+                               (const float*)v_new, (const float*)k_cached,
+                               (const float*)v_cached, grow, t, kv_dim, mode, dev);
+        return hipGetLastError();
+    }
     const int per = kDevThreads / 64;
     dim3 grid((t.max_c + per - 1) / per, t.n), block(kDevThreads);
     if (dtype == BF16)

@@ -64,7 +64,8 @@ def test_rope_rerotate_closed_form_and_identity(lib, dt):
 # ---------------------------------------------------------------- deviation
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("mode,name", [(0, "KV"), (1, "K"), (2, "V")])
-@pytest.mark.parametrize("n,row", [(1, 8), (77, 256), (3840, 4096), (5, 1024)])
+@pytest.mark.parametrize("n,row", [(1, 8), (77, 256), (3840, 4096), (5, 1024), (145, 4096),
+                                   (1023, 1024), (1024, 1024)])
 def test_deviation_vs_oracle(lib, dt, mode, name, n, row):
     rng = np.random.default_rng(row + n)
     a = [round_to(rng.standard_normal((n, row)), dt) for _ in range(4)]
