@@ -981,7 +981,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
 // K advances 32 per stage: one MFMA covers a whole stage, lane l supplying
 // row l % 16 and the 16-byte chunk l / 16 of a 64-byte LDS row.  Rows are
 // unpadded with chunk c stored at slot c ^ ((row / 2) % 4), so the eight
-// rows a group of eight lanes reads fall on distinct banks.  A ring of S
+// rows a group of eight lanes reads fall on distinct banks.  A ring of 5
 // stages (26 KB each) is filled by direct-to-LDS copies, 26 per stage (14
 // A and 12 B blocks of 16 rows); wave w issues blocks w, w + 4, ..., so
 // waves 2 and 3 pad their seventh copy with an empty one into a spare
@@ -1135,7 +1135,7 @@ __device__ __forceinline__ void mid_finish(const GemmArgs& g, int row0, int n_ti
 
 template <int EPI, int S>
 __global__ __launch_bounds__(kThreads, 1) void gemm_mid_kernel(GemmArgs g) {
-    static_assert(S >= 3 && S <= 6 && (S - 2) * kMidCopies < 64, "stages");
+    static_assert(S == 5, "the paired copies and their vmcnt waits assume a 5-stage ring");
     __shared__ __attribute__((aligned(16))) char smem[S * kMidStage + 1024];
     const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
     const uint32_t spare = lds0 + S * kMidStage;         // target of the empty copies
@@ -1204,17 +1204,31 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mid_kernel(GemmArgs g) {
     bf16x8 fa[7], fb[6], na[7], nb[6];
     // One K stage out of ring slot `slot`, its fragments in (ca, cb): the 42
     // MFMAs (A fragment i with B fragments 0-5) are interleaved with the 13
-    // fragment reads of stage kt + 1 into
-    // (xa, xb) and this wave's copies of stage kt + S - 1 into the slot that
-    // stage kt - 1 left.  Slots are run-time values (a rolled loop keeps the
+    // fragment reads of stage kt + 1 into (xa, xb).  Copies go out in pairs
+    // of stages 2m, 2m + 1, whose 64-byte row pieces are the two halves of
+    // the same 128-byte lines, issued back to back per block: an even step
+    // kt refills the slots of stages kt - 1 and kt with stages kt + 4 and
+    // kt + 5 (measured: 7B step 19.44 -> 18.80 ms against one stage per
+    // step).  Slots are run-time values (a rolled loop keeps the
     // accumulators in place); they only offset LDS addresses.
-    auto step = [&](int kt, int slot, const bf16x8 (&ca)[7], const bf16x8 (&cb)[6],
+    auto step = [&](auto ev, int kt, int slot, const bf16x8 (&ca)[7], const bf16x8 (&cb)[6],
                     bf16x8 (&xa)[7], bf16x8 (&xb)[6]) {
+        constexpr bool EVEN = decltype(ev)::value;
         const int nxt = slot + 1 == S ? 0 : slot + 1;
         const int fill = slot == 0 ? S - 1 : slot - 1;
         const char* nbase = smem + nxt * kMidStage;
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm<(S - 3) * kMidCopies>();
+        if constexpr (EVEN) {
+            // stage kt+1 landed (only the pair kt+2, kt+3 may be in flight),
+            // and this wave's reads of stage kt have completed: its slot is
+            // refilled after the barrier
+            constexpr int N = 2 * kMidCopies;
+            __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+        } else {
+            // stage kt+1 landed: after its last copy come one copy of its
+            // pair partner kt+2 and the 14 copies of the last even step
+            wait_vm<2 * kMidCopies + 1>();
+        }
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -1228,7 +1242,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mid_kernel(GemmArgs g) {
                 if (q < 6) xb[q] = *reinterpret_cast<const bf16x8*>(nbase + b_off + 1024 * q);
                 else xa[q - 6] = *reinterpret_cast<const bf16x8*>(nbase + a_off + 1024 * (q - 6));
             }
-            if (t % 6 == 5) copy(t / 6, kt + S - 1, fill);
+            if (EVEN && t % 6 == 5) {          // the two halves of the same 128-byte lines
+                copy(t / 6, kt + S - 1, fill);
+                copy(t / 6, kt + S, slot);
+            }
         }
 #pragma unroll
         for (int k = 0; k < 13; ++k) {
@@ -1238,10 +1255,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mid_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);
         __builtin_amdgcn_sched_barrier(0);
     };
-    for (int s0 = 0; s0 < S - 1; ++s0)
+    // stages 0-3 as the pairs (0, 1), (2, 3); stage 0 has landed once at most
+    // one copy of stage 1 and the 14 of (2, 3) are outstanding
 #pragma unroll
-        for (int c = 0; c < kMidCopies; ++c) copy(c, s0, s0);
-    wait_vm<(S - 2) * kMidCopies>();
+    for (int c = 0; c < kMidCopies; ++c) { copy(c, 0, 0); copy(c, 1, 1); }
+#pragma unroll
+    for (int c = 0; c < kMidCopies; ++c) { copy(c, 2, 2); copy(c, 3, 3); }
+    wait_vm<2 * kMidCopies + 1>();
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int i = 0; i < 7; ++i) fa[i] = frag(a_off + 1024 * i);
@@ -1251,9 +1271,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mid_kernel(GemmArgs g) {
     // fragment registers alternating
     int slot = 0;
     for (int kt = 0; kt < KT; kt += 2) {
-        step(kt, slot, fa, fb, na, nb);
+        step(std::true_type{}, kt, slot, fa, fb, na, nb);
         slot = slot + 1 == S ? 0 : slot + 1;
-        step(kt + 1, slot, na, nb, fa, fb);
+        step(std::false_type{}, kt + 1, slot, na, nb, fa, fb);
         slot = slot + 1 == S ? 0 : slot + 1;
     }
     // wait states between the last MFMA and the first read of an accumulator
