@@ -702,10 +702,12 @@ hipError_t launch_t(const GemmArgs& g, hipStream_t s) {
 // Per K element this halves both the L2 -> LDS traffic and the LDS fragment
 // reads of the 128x128 kernel, which bound that kernel on large shapes.
 // LDS rows are 4 chunks of 16 bytes stored at chunk ^ ((row / 4) % 4) (zero
-// bank conflicts for 32x32 fragment reads, measured).  A 4-stage ring, a
-// mid-stage barrier and a staged epilogue, as in the 128x128 kernel; the epilogue
-// goes through LDS in four passes of 64 rows.
-constexpr int BBM = 256, BBN = 256, BBK = 32, kBigStages = 4;
+// bank conflicts for 32x32 fragment reads, measured).  A 5-stage ring (all
+// 160 KB) filled in pairs of stages that share 128-byte lines (7B step
+// 18.61 -> 18.47 ms, 13B 68.8 -> 67.3 ms against a 4-stage ring filled one
+// stage per step), a mid-stage barrier and a staged epilogue, as in the
+// 128x128 kernel; the epilogue goes through LDS in four passes of 64 rows.
+constexpr int BBM = 256, BBN = 256, BBK = 32, kBigStages = 5;
 constexpr int kBigLd = BBN + 8;
 
 __device__ __forceinline__ int big_swz(int r, int chunk) {     // byte offset in a stage half
@@ -822,7 +824,8 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
     constexpr int S = kBigStages;
     constexpr int HALF_B = BBM * BBK * 2;         // bytes of the A (then B) part of a stage
     constexpr int STAGE_B = 2 * HALF_B;
-    __shared__ __attribute__((aligned(16))) char smem[S * STAGE_B];   // 128 KB
+    static_assert(S == 5, "the paired copies and their vmcnt waits assume a 5-stage ring");
+    __shared__ __attribute__((aligned(16))) char smem[S * STAGE_B];   // 160 KB
     const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
 
     const int m_tiles = (g.M + BBM - 1) / BBM;
@@ -926,24 +929,38 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
         }
     };
     bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
-    auto step = [&](int kt, int buf) {
+    // Copies go out in pairs of stages (2m, 2m + 1), whose 64-byte row pieces
+    // are the two halves of the same 128-byte lines, back to back per copy:
+    // an even step kt refills the slots of stages kt - 1 and kt with stages
+    // kt + 4 and kt + 5 (stage kt's second-half fragments were read at the
+    // start of the step; lgkmcnt(0) before the barrier makes every wave's
+    // reads complete).  Slots are run-time values of a rolled loop.
+    auto step = [&](auto ev, int kt, int buf) {
+        constexpr bool EVEN = decltype(ev)::value;
+        const int nbuf = buf + 1 == S ? 0 : buf + 1;
+        const int fill = buf == 0 ? S - 1 : buf - 1;
         read_frags(buf, 1, fa1, fb1);
         mfma_all(fa0, fb0);
         __builtin_amdgcn_sched_barrier(0);
-        wait_vm<(S - 3) * 8>();
+        if constexpr (EVEN) {
+            // stage kt+1 landed: after its last copy come the 16 of the pair (kt+2, kt+3)
+            __builtin_amdgcn_s_waitcnt((16 & 15) | ((16 >> 4) << 14) | (7 << 4) | (0 << 8));
+        } else {
+            // stage kt+1 landed: after its last copy come one of its partner and 16 more
+            wait_vm<17>();
+        }
         __builtin_amdgcn_s_barrier();
         __builtin_amdgcn_sched_barrier(0);
         {
-            // second half: per part 2 MFMAs, one copy of stage kt+S-1 and one
-            // fragment read of stage kt+1 (after the last stage that reads a
-            // slot of zeros that is never used)
-            const int kn = kt + S - 1, nb = (buf + S - 1) % S;
-            const char* st = smem + ((buf + 1) % S) * STAGE_B;
+            const char* st = smem + nbuf * STAGE_B;
 #pragma unroll
             for (int part = 0; part < 8; ++part) {
                 mfma32(acc[part >> 1][2 * (part & 1)], fa1[part >> 1], fb1[2 * (part & 1)]);
                 mfma32(acc[part >> 1][2 * (part & 1) + 1], fa1[part >> 1], fb1[2 * (part & 1) + 1]);
-                copy_part(kn, nb, part);
+                if (EVEN) {
+                    copy_part(kt + S - 1, fill, part);
+                    copy_part(kt + S, buf, part);
+                }
                 if (part < 4)
                     fa0[part] = *reinterpret_cast<const bf16x8*>(
                         st + big_swz(wm * 128 + part * 32 + fr, fg));
@@ -955,15 +972,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_barrier(0);
     };
 #pragma unroll
-    for (int s0 = 0; s0 < S - 1; ++s0)
+    for (int part = 0; part < 8; ++part) { copy_part(0, 0, part); copy_part(1, 1, part); }
 #pragma unroll
-        for (int part = 0; part < 8; ++part) copy_part(s0, s0, part);
-    wait_vm<(S - 2) * 8>();
+    for (int part = 0; part < 8; ++part) { copy_part(2, 2, part); copy_part(3, 3, part); }
+    wait_vm<17>();                            // stage 0 landed
     __builtin_amdgcn_s_barrier();
     read_frags(0, 0, fa0, fb0);
-    for (int kt = 0; kt < KT; kt += S) {       // KT is a multiple of S
-#pragma unroll
-        for (int b = 0; b < S; ++b) step(kt + b, b);
+    int ring = 0;
+    for (int kt = 0; kt < KT; kt += 2) {      // KT is even
+        step(std::true_type{}, kt, ring);
+        ring = ring + 1 == S ? 0 : ring + 1;
+        step(std::false_type{}, kt + 1, ring);
+        ring = ring + 1 == S ? 0 : ring + 1;
     }
     wait_vm<0>();
     __syncthreads();
@@ -1350,7 +1370,7 @@ constexpr double kMidCost = 2.35;
 enum TileKind { TILE_128, TILE_256, TILE_224x192 };
 
 bool big_shape_ok(int epi, const GemmArgs& g) {
-    if (g.K % (BBK * kBigStages) != 0 || (int64_t)g.K * 2 * 64 + 64 >= (int64_t)1 << 31) return false;
+    if (g.K % (2 * BBK) != 0 || (int64_t)g.K * 2 * 64 + 64 >= (int64_t)1 << 31) return false;
     if (epi == EPI_QKV && (g.n0 % BBN != 0 || g.n1 % BBN != 0)) return false;
     return true;
 }

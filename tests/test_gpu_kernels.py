@@ -159,7 +159,9 @@ def test_rmsnorm_vs_oracle(lib, dt, rows, d):
                                    (600, 20000, 320), (520, 30000, 192),
                                    # 224x192 tiles (ragged rows and columns, M = 224, K = 64)
                                    (832, 12288, 4096), (833, 12288, 192), (650, 12000, 320),
-                                   (224, 40000, 64)])
+                                   (224, 40000, 64),
+                                   # 256x256 tiles (ragged rows and columns)
+                                   (2048, 8192, 256), (2000, 8000, 320), (4096, 4096, 1024)])
 def test_gemm_vs_definition(lib, dt, m, n, k):
     rng = np.random.default_rng(m * 7 + n)
     a = round_to(rng.standard_normal((m, k)), dt)
