@@ -7,7 +7,8 @@ gate/up products (Llama-2-7B shape) and the q/k/v, O and down products
 (Llama-2-13B shape).  One-layer prefills at those row counts exercise each
 epilogue on that tile (RoPE at real positions on q/k/v tiles that straddle
 the q|k and k|v boundaries, SiLU(gate)*up on interleaved gate/up rows, the
-gathered residual) against the oracle's prefill."""
+gathered residual) against the oracle's prefill.  A one-KV-head shape at
+4000 rows puts q, k and v in one 224x192 tile column range."""
 import dataclasses
 import gc
 import types
@@ -19,15 +20,22 @@ import torch
 import oracle
 from tests.helpers import rel_err
 from tests.gpu_helpers import dev, host, make_model
-from workloads import WORKLOADS, make_weights_np, make_embedding_np, make_tokens
+from workloads import WORKLOADS, ModelShape, make_weights_np, make_embedding_np, make_tokens
 
 pytestmark = pytest.mark.gpu
 
 
+# One KV head of 128 dims: the 224x192 q/k/v tiles 10 and 11 span q|k and
+# k|v (the k block is 128 rows), at 4000 rows where that tile is chosen.
+GQA_1KV = ModelShape(n_layers=1, d_model=2048, n_q_heads=16, n_kv_heads=1, head_dim=128,
+                     ffn_dim=5504, vocab=1024)
+
+
 @pytest.mark.parametrize("name,rows,pos0", [("llama7b-4k", 832, 0), ("llama7b-4k", 889, 1000),
-                                            ("llama13b-8k", 1664, 77)])
+                                            ("llama13b-8k", 1664, 77), ("gqa-1kv", 4000, 5)])
 def test_prefill_projection_tiles_vs_oracle(lib, name, rows, pos0):
-    shape = dataclasses.replace(WORKLOADS[name].shape, n_layers=1)
+    base = GQA_1KV if name == "gqa-1kv" else WORKLOADS[name].shape
+    shape = dataclasses.replace(base, n_layers=1)
     w = make_weights_np(shape, seed=3, dtype="bf16")
     x = make_embedding_np(shape, seed=3, dtype="bf16")[make_tokens(shape, rows, seed=3)]
     model = make_model(lib, types.SimpleNamespace(shape=shape, weights=w), "bf16")
