@@ -1362,7 +1362,9 @@ int num_cus() {
 // Tile choice.  All three bf16 kernels run one workgroup per CU (256 at a
 // time); compare whole rounds of workgroups, each round priced in units of
 // one 128x128 tile.  A 256x256 tile costs about 3 of them (4x the work at
-// ~1.3x the efficiency; 3.2 for the q/k/v product), a 224x192 tile
+// ~1.3x the efficiency): 2.9, so that one round of 256x256 beats three of
+// 128x128 (Yi-34B down projection, 1484 x 7168 x 20480: 616 vs 792 us;
+// 34B step 154 -> 141 ms), 3.1 for the q/k/v product; a 224x192 tile
 // kMidCost.  Ties go to the smaller tile.  Measured on MI355X (bf16): large
 // products (>= 4096 rows) 1.2-1.3x faster on 256x256; N = 4096 products at
 // ~832 rows lose badly there (340 vs 760 TF/s).
@@ -1396,7 +1398,7 @@ TileKind choose_tile(int epi, const GemmArgs& g) {
         if (c < cost) { cost = c; best = TILE_224x192; }
     }
     if (big_shape_ok(epi, g)) {
-        const double c = (epi == EPI_QKV ? 3.2 : 3.0) * rounds(BBM, BBN);
+        const double c = (epi == EPI_QKV ? 3.1 : 2.9) * rounds(BBM, BBN);
         if (c < cost) { cost = c; best = TILE_256; }
     }
     return best;
