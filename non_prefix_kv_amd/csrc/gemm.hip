@@ -819,6 +819,167 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& g, const floatx16 (
     }
 }
 
+// The same tile with a 4-stage ring filled one stage per step, fully
+// unrolled with compile-time slots (K a multiple of 128).  Faster than the
+// paired 5-stage kernel when many rounds of workgroups reuse the weights
+// (the 32-request batch: 416.6 vs 428.3 ms per step); the paired kernel wins
+// at 4 rounds or fewer, where the weights stream from HBM.
+constexpr int kBig4Stages = 4;
+
+template <int EPI>
+__global__ __launch_bounds__(kThreads, 1) void gemm_big4_kernel(GemmArgs g) {
+    constexpr int S = kBig4Stages;
+    constexpr int HALF_B = BBM * BBK * 2;         // bytes of the A (then B) part of a stage
+    constexpr int STAGE_B = 2 * HALF_B;
+    __shared__ __attribute__((aligned(16))) char smem[S * STAGE_B];   // 128 KB
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
+
+    const int m_tiles = (g.M + BBM - 1) / BBM;
+    const int n_cols_per_tile = (EPI == EPI_SWIGLU) ? BBN / 2 : BBN;
+    const int n_tiles = (g.N + n_cols_per_tile - 1) / n_cols_per_tile;
+    const int tile = xcd_remap(blockIdx.x, m_tiles * n_tiles);
+    const int group = tile / (kGroupM * n_tiles);
+    const int first_m = group * kGroupM;
+    const int gm = min(m_tiles - first_m, kGroupM);
+    const int in_group = tile - group * kGroupM * n_tiles;
+    const int m_tile = first_m + in_group % gm, n_tile = in_group / gm;
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int Kb = g.K * 2;
+
+    // This wave copies rows 64*wave .. +63 of the A tile and of the B tile.
+    const bf16* a_base = static_cast<const bf16*>(g.a) + ((int64_t)m_tile * BBM + 64 * wave) * g.K;
+    const int64_t a_rows = (int64_t)g.M - (int64_t)m_tile * BBM - 64 * wave;
+    const int a_bytes = (a_rows < 0 ? 0 : (a_rows > 64 ? 64 : (int)a_rows)) * Kb;
+    // B: two 32-row halves (for gate/up they come from different matrices)
+    const bf16* b_base[2];
+    int b_bytes[2];
+    if (EPI == EPI_SWIGLU) {
+        const int oc0 = n_tile * (BBN / 2) + wave * 32;
+        const int64_t rows = g.N - oc0;
+        const int by = (rows < 0 ? 0 : (rows > 32 ? 32 : (int)rows)) * Kb;
+        b_base[0] = static_cast<const bf16*>(g.b0) + (int64_t)oc0 * g.K;
+        b_base[1] = static_cast<const bf16*>(g.b1) + (int64_t)oc0 * g.K;
+        b_bytes[0] = b_bytes[1] = by;
+    } else {
+        const void* mat = g.b0;
+        int64_t local = (int64_t)n_tile * BBN, rows = g.N;
+        if (EPI == EPI_QKV) {
+            const int c0 = n_tile * BBN;
+            if (c0 < g.n0) { mat = g.b0; local = c0; rows = g.n0; }
+            else if (c0 < g.n0 + g.n1) { mat = g.b1; local = c0 - g.n0; rows = g.n1; }
+            else { mat = g.b2; local = c0 - g.n0 - g.n1; rows = g.N - g.n0 - g.n1; }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int64_t r0 = local + 64 * wave + 32 * h;
+            const int64_t left = rows - r0;
+            b_base[h] = static_cast<const bf16*>(mat) + r0 * g.K;
+            b_bytes[h] = (left < 0 ? 0 : (left > 32 ? 32 : (int)left)) * Kb;
+        }
+    }
+    // Lane i copies row i/4 (of 16) into LDS slot i%4: global chunk slot ^ key,
+    // key = (row/4) % 4 (the same for every 16-row block of the wave).
+    const int r16 = lane >> 2, slot = lane & 3;
+    const int voff = r16 * Kb + ((slot ^ (r16 >> 2)) & 3) * 16;
+    const int KT = g.K / BBK;
+
+    // Copies of stage kt into ring slot `buf`, 8 per wave; with `t` the
+    // copies are spread over the MFMA steps (see big_copy_part).
+    auto copy_part = [&](int kt, int buf, int part) {       // part 0..7
+        const bool live = kt < KT;
+        const int j = part & 3;                             // 16-row block within the 64
+        const uint32_t dst = lds0 + buf * STAGE_B + (part < 4 ? 0 : HALF_B) + (64 * wave + 16 * j) * 64;
+        const int so = kt * 64 + 16 * (j & 1) * Kb;
+        if (part < 4) {
+            const i32x4 r = make_rsrc(a_base, live ? a_bytes : 0);
+            dma16(r, voff, kt * 64 + 16 * j * Kb, dst);
+        } else {
+            const int h = j >> 1;
+            const i32x4 r = make_rsrc(b_base[h], live ? b_bytes[h] : 0);
+            dma16(r, voff, so, dst);
+        }
+    };
+
+    floatx16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+    const int fr = lane & 31, fg = lane >> 5;
+    auto read_frags = [&](int buf, int ks, bf16x8 (&fa)[4], bf16x8 (&fb)[4]) {
+        const char* st = smem + buf * STAGE_B;
+        const int chunk = ks * 2 + fg;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            fa[i] = *reinterpret_cast<const bf16x8*>(st + big_swz(wm * 128 + i * 32 + fr, chunk));
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            fb[j] = *reinterpret_cast<const bf16x8*>(st + HALF_B + big_swz(wn * 128 + j * 32 + fr, chunk));
+    };
+    // 16 MFMAs, with the 8 fragment reads of the next step one per two MFMAs.
+    auto mfma_all = [&](const bf16x8 (&fa)[4], const bf16x8 (&fb)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) mfma32(acc[i][j], fa[i], fb[j]);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
+    };
+    bf16x8 fa0[4], fb0[4], fa1[4], fb1[4];
+    auto step = [&](int kt, int buf) {
+        read_frags(buf, 1, fa1, fb1);
+        mfma_all(fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vm<(S - 3) * 8>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        {
+            // second half: per part 2 MFMAs, one copy of stage kt+S-1 and one
+            // fragment read of stage kt+1 (after the last stage that reads a
+            // slot of zeros that is never used)
+            const int kn = kt + S - 1, nb = (buf + S - 1) % S;
+            const char* st = smem + ((buf + 1) % S) * STAGE_B;
+#pragma unroll
+            for (int part = 0; part < 8; ++part) {
+                mfma32(acc[part >> 1][2 * (part & 1)], fa1[part >> 1], fb1[2 * (part & 1)]);
+                mfma32(acc[part >> 1][2 * (part & 1) + 1], fa1[part >> 1], fb1[2 * (part & 1) + 1]);
+                copy_part(kn, nb, part);
+                if (part < 4)
+                    fa0[part] = *reinterpret_cast<const bf16x8*>(
+                        st + big_swz(wm * 128 + part * 32 + fr, fg));
+                else
+                    fb0[part - 4] = *reinterpret_cast<const bf16x8*>(
+                        st + HALF_B + big_swz(wn * 128 + (part - 4) * 32 + fr, fg));
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+#pragma unroll
+    for (int s0 = 0; s0 < S - 1; ++s0)
+#pragma unroll
+        for (int part = 0; part < 8; ++part) copy_part(s0, s0, part);
+    wait_vm<(S - 2) * 8>();
+    __builtin_amdgcn_s_barrier();
+    read_frags(0, 0, fa0, fb0);
+    for (int kt = 0; kt < KT; kt += S) {       // KT is a multiple of S
+#pragma unroll
+        for (int b = 0; b < S; ++b) step(kt + b, b);
+    }
+    wait_vm<0>();
+    __syncthreads();
+    static_assert(S * STAGE_B >= 64 * kBigLd * 4, "epilogue staging fits the stage ring");
+    big_epilogue<EPI>(g, acc, m_tile, n_tile, wm, wn, lane, reinterpret_cast<float*>(smem));
+}
+
 template <int EPI>
 __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
     constexpr int S = kBigStages;
@@ -1339,12 +1500,18 @@ hipError_t launch_mid(const GemmArgs& g, hipStream_t s) {
 
 constexpr int kDmaStages = 5;            // LDS ring depth of the bf16 kernel
 
+int num_cus();
+
 template <int EPI>
 hipError_t launch_big(const GemmArgs& g, hipStream_t s) {
     const int m_tiles = (g.M + BBM - 1) / BBM;
     const int cols = (EPI == EPI_SWIGLU) ? BBN / 2 : BBN;
     const int n_tiles = (g.N + cols - 1) / cols;
-    hipLaunchKernelGGL((gemm_big_kernel<EPI>), dim3(m_tiles * n_tiles), dim3(kThreads), 0, s, g);
+    const int64_t tiles = (int64_t)m_tiles * n_tiles;
+    if (tiles > 4 * (int64_t)num_cus() && g.K % (BBK * kBig4Stages) == 0)
+        hipLaunchKernelGGL((gemm_big4_kernel<EPI>), dim3(tiles), dim3(kThreads), 0, s, g);
+    else
+        hipLaunchKernelGGL((gemm_big_kernel<EPI>), dim3(tiles), dim3(kThreads), 0, s, g);
     return hipGetLastError();
 }
 

@@ -160,8 +160,10 @@ def test_rmsnorm_vs_oracle(lib, dt, rows, d):
                                    # 224x192 tiles (ragged rows and columns, M = 224, K = 64)
                                    (832, 12288, 4096), (833, 12288, 192), (650, 12000, 320),
                                    (224, 40000, 64),
-                                   # 256x256 tiles (ragged rows and columns)
-                                   (2048, 8192, 256), (2000, 8000, 320), (4096, 4096, 1024)])
+                                   # 256x256 tiles (ragged rows and columns; the last one
+                                   # takes more than four rounds: the 4-stage kernel)
+                                   (2048, 8192, 256), (2000, 8000, 320), (4096, 4096, 1024),
+                                   (4000, 20000, 256)])
 def test_gemm_vs_definition(lib, dt, m, n, k):
     rng = np.random.default_rng(m * 7 + n)
     a = round_to(rng.standard_normal((m, k)), dt)
