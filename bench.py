@@ -328,11 +328,52 @@ def copy_calibration():
 
 
 # ------------------------------------------------------------------ CPU baseline
+def host_description():
+    """CPU model and the BLAS numpy links (the CPU baseline's context)."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = {}
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = {k: b.get(k) for k in ("name", "version", "openblas configuration")}
+    except Exception:
+        pass
+    return {"cpu_model": model, "numpy": np.__version__, "blas": blas}
+
+
+def _timed_layers(run, reps=3):
+    """Median over `reps` runs of each layer's wall time."""
+    per = []
+    for _ in range(reps):
+        times = []
+        run(times)
+        per.append(times)
+    return [float(np.median([t[l] for t in per])) for l in range(len(per[0]))]
+
+
+def _compose(times, sched, n_suffix, n_layers):
+    """Whole-prompt time from sampled layers 0, 1 and 2: layers 0 and 1 as
+    timed, every later layer as layer 2 scaled by its recomputed rows
+    (s[l] + suffix) over layer 2's."""
+    t = times[0] + times[1]
+    rows2 = sched[2] + n_suffix
+    for l in range(2, n_layers):
+        t += times[2] * (sched[l] + n_suffix) / rows2
+    return t
+
+
 def cpu_baseline(w, seed, n_tokens):
     """The oracle (float32 NumPy) on a bounded sample of the same workload: the
     first three layers (layer 0 = full recompute, layer 1 = check layer,
-    layer 2 = a steady layer) at full width and context; the whole-prompt time
-    is composed as t0 + t1 + (L - 2) * t2."""
+    layer 2 = a steady layer) at full width and context, each the median of
+    three runs; the whole prompt is composed from the real schedule, later
+    layers scaled from layer 2 by their recomputed rows."""
     import oracle
     from threadpoolctl import threadpool_info
     from workloads import make_weights_np
@@ -348,21 +389,24 @@ def cpu_baseline(w, seed, n_tokens):
         k = rng.standard_normal((ls, n, S.n_kv_heads, S.head_dim)).astype(np.float32)
         v = rng.standard_normal((ls, n, S.n_kv_heads, S.head_dim)).astype(np.float32)
         chunks.append((k, v))
-    sched = oracle.schedule(w.n_chunk_tokens, w.r_bp, w.schedule_kind, S.n_layers)[:ls + 1]
-    times = []
-    oracle.blend(weights, S3, x0, chunks, list(w.offsets), w.n_suffix, sched,
-                 dtype=np.float32, timings=times)
-    total = sum(times) + (S.n_layers - ls) * times[-1]
+    full = oracle.schedule(w.n_chunk_tokens, w.r_bp, w.schedule_kind, S.n_layers)
+    sched = full[:ls + 1]
+    times = _timed_layers(lambda t: oracle.blend(weights, S3, x0, chunks, list(w.offsets),
+                                                 w.n_suffix, sched, dtype=np.float32,
+                                                 timings=t))
+    total = _compose(times, full, w.n_suffix, S.n_layers) if ls == 3 else sum(times)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": n_tokens / total, "unit": "tok/s", "cores": int(threads),
             "kind": "oracle",
             "ms_per_layer": total / S.n_layers * 1e3,
             "sample": (f"oracle.blend float32 over layers 0-2 of the {w.name} workload "
                        f"(full width and context, random chunk caches, schedule "
-                       f"{sched}); layer times {[round(t, 3) for t in times]} s; "
-                       f"whole prompt composed as t0 + t1 + {S.n_layers - 2}*t2 = "
-                       f"{total:.2f} s"),
-            "host_cpus": len(os.sched_getaffinity(0))}
+                       f"{sched}); median of 3 runs per layer "
+                       f"{[round(t, 3) for t in times]} s; whole prompt composed as "
+                       f"t0 + t1 + sum over layers 2..{S.n_layers - 1} of t2 * "
+                       f"(s[l] + suffix) / (s[2] + suffix) = {total:.2f} s"),
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "host": host_description()}
 
 
 def kernel_breakdown(st, pk):
@@ -636,21 +680,24 @@ def cpu_baseline_batch(w, seed, reqs, pool_lens, n_total):
                   for m in lens]
         offs = list(np.cumsum([0] + lens)[:-1])
         sched = oracle.schedule(n_c, w.r_bp, w.schedule_kind, S.n_layers)[:ls + 1]
-        times = []
-        oracle.blend(weights, S3, x0, chunks, [int(o) for o in offs], r["n_suffix"], sched,
-                     dtype=np.float32, timings=times)
-        t = sum(times) + (S.n_layers - ls) * times[-1]
+        times = _timed_layers(lambda tt: oracle.blend(
+            weights, S3, x0, chunks, [int(o) for o in offs], r["n_suffix"], sched,
+            dtype=np.float32, timings=tt))
+        full = oracle.schedule(n_c, w.r_bp, w.schedule_kind, S.n_layers)
+        t = _compose(times, full, r["n_suffix"], S.n_layers) if ls == 3 else sum(times)
         total += t
         toks += n
         parts.append(f"{n} tokens: layers {[round(x, 3) for x in times]} s -> {t:.2f} s")
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     return {"value": toks / total, "unit": "tok/s", "cores": int(threads), "kind": "oracle",
             "sample": (f"oracle.blend float32 on the first two requests of the batch (random "
-                       f"chunk caches), layers 0-2 each at full width, whole prompt composed as "
-                       f"t0 + t1 + {S.n_layers - 2}*t2: " + "; ".join(parts) +
+                       f"chunk caches), layers 0-2 each at full width, median of 3 runs per "
+                       f"layer, whole prompt composed as t0 + t1 + later layers scaled from t2 "
+                       f"by their recomputed rows: " + "; ".join(parts) +
                        f"; the batch ({n_total} tokens) at the same rate would take "
                        f"{n_total / (toks / total):.1f} s"),
-            "host_cpus": len(os.sched_getaffinity(0))}
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "host": host_description()}
 
 
 def main_batched(args, npk, torch, w):
@@ -774,7 +821,7 @@ def selection_study(args, npk, torch, w):
     prefill against the chunk caches); (2) for recompute ratios and selection
     variants, the error of the suffix rows' last-layer output and of the
     fused K/V against full prefill (relative Frobenius norms)."""
-    import oracle                      # Spearman's rho only (host-side statistics)
+    import scipy.stats
     S = w.shape
     L, N, Nc = S.n_layers, w.n_tokens, w.n_chunk_tokens
     dev = torch.device("cuda:0")
@@ -797,7 +844,11 @@ def selection_study(args, npk, torch, w):
     h_full = run(full)
     k_full, v_full = fk.clone(), fv.clone()
     d_all = devs.cpu().numpy().astype(np.float64)
-    rho = oracle.layer_rank_correlation(d_all)
+    rho = []                           # consecutive layers, tokens measured at both
+    for l in range(L - 1):
+        m = ~np.isnan(d_all[l]) & ~np.isnan(d_all[l + 1])
+        rho.append(float(scipy.stats.spearmanr(d_all[l][m], d_all[l + 1][m])[0])
+                   if m.sum() >= 3 else float("nan"))
     kv_norm = float(torch.sqrt((k_full.float() ** 2).sum() + (v_full.float() ** 2).sum()))
 
     def errors(h):

@@ -182,6 +182,37 @@ def _stream(stream):
     return stream.cuda_stream
 
 
+def _need(t, name, dtype=None, numel=0, device=True):
+    """Argument checks before a raw pointer crosses the ABI: the library
+    cannot see the size behind a pointer, so a tensor that is too small, of
+    the wrong element type, not contiguous or on the wrong side would be
+    written past instead of rejected.  Failures raise CBError with the
+    library's codes (CB_E_INVALID for the kind of buffer, CB_E_SHAPE for its
+    size).  Plain integers are addresses the caller vouches for and are
+    passed as they are."""
+    if t is None or isinstance(t, int):
+        return
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise CBError(CB_E_INVALID, f"{name}: expected a tensor or an address, "
+                                    f"got {type(t).__name__}")
+    if device and not t.is_cuda:
+        raise CBError(CB_E_INVALID, f"{name} must be a device tensor")
+    if not device and t.is_cuda:
+        raise CBError(CB_E_INVALID, f"{name} must be a host tensor")
+    if not t.is_contiguous():
+        raise CBError(CB_E_INVALID, f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise CBError(CB_E_INVALID, f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() < numel:
+        raise CBError(CB_E_SHAPE, f"{name} holds {t.numel()} elements, needs at least {numel}")
+
+
+def _torch_dtype(code):
+    import torch
+    return torch.float32 if code == CB_F32 else torch.bfloat16
+
+
 def _dtype_code(t):
     import torch
     if t.dtype == torch.float32:
@@ -265,6 +296,62 @@ def _chunk_array(chunks):
     return arr
 
 
+def _check_chunks(model, chunks, what="chunk"):
+    """Element type, memory side and extent of chunk descriptors given as
+    dicts of tensors (a resolved descriptor array is passed unchecked)."""
+    import torch
+    if isinstance(chunks, ctypes.Array):
+        return
+    L = model.cfg.n_layers
+    row = model.cfg.n_kv_heads * model.cfg.head_dim
+    for i, c in enumerate(chunks):
+        fmt = int(c.get("kv_format", CB_KV_PLAIN))
+        n, stride = int(c["n_tokens"]), int(c["layer_stride"])
+        on_host = bool(c.get("on_host", 0))
+        if fmt == CB_KV_PLAIN:
+            dt, need = _torch_dtype(model.cfg.dtype), (L - 1) * stride + n * row
+        else:
+            per = 1 if fmt == CB_KV_U8 else 2
+            dt, need = torch.uint8, ((L - 1) * stride + n * row) // per
+            _need(c.get("qparams"), f"{what} {i} qparams", torch.float32, L * 4 * row,
+                  device=not on_host)
+        for key in ("k", "v"):
+            _need(c[key], f"{what} {i} {key}", dt, need, device=not on_host)
+
+
+def _schedule_last(model, n_chunk, n_tokens, schedule, recompute_bp, schedule_kind, min_tokens):
+    """s[L] of a request (the schedule the library derives, or the caller's)."""
+    L = model.cfg.n_layers
+    if min_tokens > 0 and n_tokens < min_tokens:
+        return n_chunk
+    if schedule is not None:
+        if len(schedule) != L + 1:
+            raise CBError(CB_E_SCHEDULE,
+                          f"schedule has {len(schedule)} entries, needs n_layers + 1 = {L + 1}")
+        return int(schedule[-1])
+    return cb_schedule(n_chunk, recompute_bp, schedule_kind, L)[-1]
+
+
+def _check_blend_args(model, chunks, n_suffix, x0, fused_k, fused_v, sel_idx, hidden_out,
+                      deviation, schedule, recompute_bp, schedule_kind, min_tokens, given_scores):
+    import torch
+    cfg = model.cfg
+    L, d, row = cfg.n_layers, cfg.d_model, cfg.n_kv_heads * cfg.head_dim
+    nc = sum(int(c["n_tokens"]) for c in chunks) if not isinstance(chunks, ctypes.Array) \
+        else sum(chunks[i].n_tokens for i in range(len(chunks)))
+    n = nc + n_suffix
+    mdt = _torch_dtype(cfg.dtype)
+    _check_chunks(model, chunks)
+    _need(x0, "x0", mdt, n * d)
+    _need(fused_k, "fused_k", mdt, L * n * row)
+    _need(fused_v, "fused_v", mdt, L * n * row)
+    _need(sel_idx, "sel_idx", torch.int32, L * nc)
+    _need(deviation, "deviation", torch.float32, L * nc)
+    _need(given_scores, "given_scores", torch.float32, nc)
+    last = _schedule_last(model, nc, n, schedule, recompute_bp, schedule_kind, min_tokens)
+    _need(hidden_out, "hidden_out", torch.float32, (last + n_suffix) * d)
+
+
 def _request(chunks, offsets, n_suffix, x0, schedule, recompute_bp, schedule_kind, dev_mode,
              min_tokens, given_scores=None):
     arr = _chunk_array(chunks)
@@ -289,6 +376,8 @@ def cb_blend(model, chunks, offsets, n_suffix, x0, fused_k, fused_v, sel_idx=Non
              schedule_kind=CB_SCHED_GRADUAL, dev_mode=CB_DEV_KV, min_tokens=0, stream=None,
              given_scores=None):
     """Queues one fusion; returns the host list sel_count[l] = s[l+1]."""
+    _check_blend_args(model, chunks, n_suffix, x0, fused_k, fused_v, sel_idx, hidden_out,
+                      deviation, schedule, recompute_bp, schedule_kind, min_tokens, given_scores)
     req, keep = _request(chunks, offsets, n_suffix, x0, schedule, recompute_bp, schedule_kind,
                          dev_mode, min_tokens, given_scores)
     L = model.cfg.n_layers
@@ -305,6 +394,32 @@ def cb_blend_batch(model, pool, requests, x0, fused_k, fused_v, sel_idx=None, hi
     """Queues the fusion of a batch.  pool: chunk dicts as for cb_blend;
     requests: list of dicts {chunk_ids: [...], n_suffix, schedule (optional)}.
     Returns sel_count as a list per request of s_b[l+1]."""
+    import torch
+    cfg = model.cfg
+    L, d, row = cfg.n_layers, cfg.d_model, cfg.n_kv_heads * cfg.head_dim
+    if not isinstance(pool, ctypes.Array):
+        _check_chunks(model, pool, "pool chunk")
+        lens = [int(c["n_tokens"]) for c in pool]
+    else:
+        lens = [pool[i].n_tokens for i in range(len(pool))]
+    nc_tot = n_tot = last_tot = 0
+    ids_ok = all(0 <= i < len(lens) for r in requests for i in r["chunk_ids"])
+    for r in requests if ids_ok else ():      # ids outside the pool: the library rejects them
+        nc = sum(lens[i] for i in r["chunk_ids"])
+        nc_tot += nc
+        n_tot += nc + r["n_suffix"]
+        last_tot += _schedule_last(model, nc, nc + r["n_suffix"], r.get("schedule"),
+                                   recompute_bp, schedule_kind, min_tokens) + r["n_suffix"]
+    mdt = _torch_dtype(cfg.dtype)
+    if not ids_ok:
+        n_tot = nc_tot = last_tot = 0
+    _need(x0, "x0", mdt, n_tot * d)
+    _need(fused_k, "fused_k", mdt, L * n_tot * row)
+    _need(fused_v, "fused_v", mdt, L * n_tot * row)
+    _need(sel_idx, "sel_idx", torch.int32, L * nc_tot)
+    _need(deviation, "deviation", torch.float32, L * nc_tot)
+    _need(given_scores, "given_scores", torch.float32, nc_tot)
+    _need(hidden_out, "hidden_out", torch.float32, last_tot * d)
     parr = _chunk_array(pool)
     items = (cb_batch_item * len(requests))()
     keep = []
@@ -339,6 +454,10 @@ class Plan:
                  hidden_out=None, deviation=None, schedule=None, recompute_bp=1500,
                  schedule_kind=CB_SCHED_GRADUAL, dev_mode=CB_DEV_KV, min_tokens=0,
                  stream=None, given_scores=None):
+        self.handle = None
+        _check_blend_args(model, chunks, n_suffix, x0, fused_k, fused_v, sel_idx, hidden_out,
+                          deviation, schedule, recompute_bp, schedule_kind, min_tokens,
+                          given_scores)
         req, self._keep = _request(chunks, offsets, n_suffix, x0, schedule, recompute_bp,
                                    schedule_kind, dev_mode, min_tokens, given_scores)
         self._cnt = (_c_i32 * model.cfg.n_layers)()
@@ -365,6 +484,14 @@ class Plan:
 
 
 def cb_prefill(model, x0, n_tokens, pos0, k_out, v_out, hidden_out=None, stream=None):
+    import torch
+    cfg = model.cfg
+    mdt = _torch_dtype(cfg.dtype)
+    kv = cfg.n_layers * n_tokens * cfg.n_kv_heads * cfg.head_dim
+    _need(x0, "x0", mdt, n_tokens * cfg.d_model)
+    _need(k_out, "k_out", mdt, kv)
+    _need(v_out, "v_out", mdt, kv)
+    _need(hidden_out, "hidden_out", torch.float32, n_tokens * cfg.d_model)
     _check(RAW["cb_prefill"](model.handle, _ptr(x0), n_tokens, pos0, _ptr(k_out), _ptr(v_out),
                              _ptr(hidden_out), _stream(stream)))
 
@@ -542,3 +669,4 @@ def cb_gemm(a, b, c, m, n, k, stream=None):
 def cb_attention(q, q_pos, n_q, k, v, n_kv, n_q_heads, n_kv_heads, head_dim, out, stream=None):
     _check(RAW["cb_attention"](_dtype_code(q), _ptr(q), _ptr(q_pos), n_q, _ptr(k), _ptr(v), n_kv,
                                n_q_heads, n_kv_heads, head_dim, _ptr(out), _stream(stream)))
+

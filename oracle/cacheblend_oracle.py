@@ -274,7 +274,8 @@ def check_offsets(chunks, offsets):
 
 
 def blend(weights, shape, x0, chunks, offsets, n_suffix, sched, dev_mode="KV",
-          min_tokens=0, dtype=np.float64, n_layers=None, timings=None, given_scores=None):
+          min_tokens=0, dtype=np.float64, n_layers=None, timings=None, given_scores=None,
+          forced_sel=None):
     """Fuse independently precomputed chunk KVs with selective recompute.
 
     weights: per-layer dicts; x0: [N][d] embeddings of all prompt tokens in
@@ -289,6 +290,13 @@ def blend(weights, shape, x0, chunks, offsets, n_suffix, sched, dev_mode="KV",
     appended to it (seconds); the arithmetic is unaffected.  dev_mode 'GIVEN'
     ranks chunk tokens by given_scores [N_c] (by position) instead of the
     measured deviation, with the same top-k rule and schedule.
+
+    forced_sel (teacher forcing): a list with one entry per layer, None or
+    the kept positions to use at that layer instead of the top-k of the
+    measured deviations.  A forced set must be s[l+1] distinct positions of
+    the layer's candidates.  Everything else is computed as usual, so a
+    checker can replay a run whose selection differed from this one's by
+    rounding at the threshold and keep comparing the layers after it.
     """
     L = shape.n_layers if n_layers is None else n_layers
     W = _cast_weights(weights[:L], dtype)
@@ -323,6 +331,14 @@ def blend(weights, shape, x0, chunks, offsets, n_suffix, sched, dev_mode="KV",
             dev[l, C] = d
             keep = (np.arange(nC) if sched[l + 1] == nC
                     else topk_select(d, sched[l + 1]))
+            if forced_sel is not None and forced_sel[l] is not None:
+                want = np.asarray(forced_sel[l], dtype=np.int64)
+                keep = np.searchsorted(C, want)
+                if (len(want) != sched[l + 1] or len(np.unique(want)) != len(want)
+                        or np.any(keep >= nC) or np.any(C[np.minimum(keep, nC - 1)] != want)):
+                    raise ValueError(f"forced selection of layer {l} is not {sched[l + 1]} "
+                                     "distinct candidate positions")
+                keep = np.sort(keep)
         else:
             keep = np.arange(0)
         rows = np.concatenate([keep, nC + np.arange(n_suffix)]).astype(np.int64)

@@ -8,7 +8,7 @@ import numpy as np
 
 import oracle
 from workloads import (make_weights_np, make_embedding_np, make_tokens, round_to,
-                       ModelShape)
+                       ModelShape, make_chunk_caches_np)
 
 
 @dataclasses.dataclass
@@ -31,11 +31,13 @@ class Case:
 
 
 def make_case(shape, chunk_lens, n_suffix, seed=0, dtype="f64", n_layers=None,
-              precompute_dtype=np.float64):
+              precompute_dtype=np.float64, random_caches=False):
     """Weights/x0 drawn from the seeded generators and rounded to `dtype`;
     chunk KVs precomputed by the oracle alone at chunk-local positions and
     rounded to `dtype` as a stored cache would be (`precompute_dtype` only
-    sets the arithmetic of that precompute, e.g. float32 at full width)."""
+    sets the arithmetic of that precompute, e.g. float32 at full width), or,
+    with random_caches, seeded N(0, 1) stand-ins (full-width parity cases,
+    where the precompute would dominate the test's CPU time)."""
     L = shape.n_layers if n_layers is None else n_layers
     if L != shape.n_layers:
         shape = dataclasses.replace(shape, n_layers=L)
@@ -44,9 +46,13 @@ def make_case(shape, chunk_lens, n_suffix, seed=0, dtype="f64", n_layers=None,
     n = int(sum(chunk_lens)) + n_suffix
     x0 = emb[make_tokens(shape, n, seed=seed)]
     chunks, offsets, o = [], [], 0
-    for nc in chunk_lens:
-        k, v, _ = oracle.prefill(w, shape, x0[o:o + nc], pos0=0, dtype=precompute_dtype)
-        chunks.append((round_to(k, dtype), round_to(v, dtype)))
+    stand_ins = make_chunk_caches_np(shape, chunk_lens, seed, dtype) if random_caches else None
+    for c, nc in enumerate(chunk_lens):
+        if stand_ins is not None:
+            chunks.append(stand_ins[c])
+        else:
+            k, v, _ = oracle.prefill(w, shape, x0[o:o + nc], pos0=0, dtype=precompute_dtype)
+            chunks.append((round_to(k, dtype), round_to(v, dtype)))
         offsets.append(o)
         o += nc
     return Case(shape, w, x0, chunks, offsets, n_suffix, dtype)

@@ -220,3 +220,36 @@ def test_cache_entry_validation(npk):
     assert R["cb_cache_stats"](None, None) == npk.CB_E_INVALID
     assert R["cb_cache_replay"](-1, 0, None, None, None, None, None, None) == npk.CB_E_INVALID
     R["cb_cache_destroy"](None)
+
+
+def test_binding_rejects_bad_buffers_before_the_call(npk):
+    """The binding checks kind, element type and extent of every tensor it
+    turns into a raw pointer (the library cannot see sizes behind pointers)
+    and raises CBError with the library's codes before anything is called:
+    here with a stand-in model whose handle is never used."""
+    import types
+    import torch
+    cfg = npk.cb_model_cfg(2, 64, 4, 2, 16, 128, 1e4, 1e-5, npk.CB_F32)
+    model = types.SimpleNamespace(cfg=cfg, handle=None)
+    k = torch.zeros((2, 8, 2, 16))
+    chunks = [{"k": k, "v": k, "n_tokens": 8, "layer_stride": 8 * 32}]
+    x0 = torch.zeros((12, 64))
+    fk = torch.zeros((2, 12, 2, 16))
+    with pytest.raises(npk.CBError) as e:       # device buffers given as host tensors
+        npk.cb_blend(model, chunks, [0], 4, x0, fk, fk)
+    assert e.value.status == npk.CB_E_INVALID and "device" in str(e.value)
+    with pytest.raises(npk.CBError) as e:       # schedule of the wrong length
+        npk.cb_blend(model, [], [], 4, None, None, None, schedule=[0, 0])
+    assert e.value.status == npk.CB_E_SCHEDULE
+    _need = npk._need
+    with pytest.raises(npk.CBError) as e:
+        _need(torch.zeros(10), "hidden_out", torch.float32, 11, device=False)
+    assert e.value.status == npk.CB_E_SHAPE
+    with pytest.raises(npk.CBError) as e:
+        _need(torch.zeros(10, dtype=torch.int64), "sel_idx", torch.int32, 10, device=False)
+    assert e.value.status == npk.CB_E_INVALID
+    with pytest.raises(npk.CBError) as e:
+        _need(torch.zeros(4, 4).t(), "x0", torch.float32, 16, device=False)
+    assert e.value.status == npk.CB_E_INVALID
+    _need(torch.zeros(10), "ok", torch.float32, 10, device=False)
+    _need(12345, "address", torch.float32, 10**9)          # raw addresses pass unchecked

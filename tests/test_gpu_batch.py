@@ -13,7 +13,7 @@ import torch
 import oracle
 from tests.helpers import make_batch_case, run_blend
 from tests.gpu_helpers import make_model, run_gpu_blend, run_gpu_batch, host, dev, pool_inputs
-from tests.test_gpu_blend import compare
+from tests.gpu_helpers import compare
 from workloads import TINY, BATCHED_TINY, make_batched_requests
 
 pytestmark = pytest.mark.gpu
@@ -40,7 +40,7 @@ def test_batch_vs_oracle(lib, tbatch, r, kind):
     for b, case in enumerate(bc.cases):
         sched = oracle.schedule(case.n_chunk_tokens, r, kind, L)
         assert per[b]["sel_count"] == sched[1:], b
-        compare(case, per[b], run_blend(case, sched), sched, dt)
+        compare(case, per[b], sched, dt)
 
 
 def test_batch_equals_single_requests(lib, tbatch):
@@ -100,7 +100,7 @@ def test_batch_edge_requests_vs_oracle(lib):
     for b, case in enumerate(bc.cases):
         assert per[b]["sel_count"] == scheds[b][1:]
         n_last = case.n_suffix + scheds[b][-1]
-        compare(case, per[b], run_blend(case, scheds[b]), scheds[b], dt,
+        compare(case, per[b], scheds[b], dt,
                 check_hidden=n_last > 0)
         for l in range(L):
             d = host(per[b]["dev"][l])
@@ -134,7 +134,7 @@ def test_batch_wider_than_one_launch(lib):
     for b in (0, 33, 69):
         case = bc.cases[b]
         sched = oracle.schedule(case.n_chunk_tokens, 1500, "gradual", L)
-        compare(case, per[b], run_blend(case, sched), sched, dt)
+        compare(case, per[b], sched, dt)
 
 
 def test_batch_error_paths(lib, tbatch):

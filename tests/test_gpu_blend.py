@@ -9,54 +9,11 @@ import torch
 
 import oracle
 from tests.helpers import make_case, run_blend, run_full, rel_err
-from tests.gpu_helpers import make_model, run_gpu_blend, dev, host, TORCH_DT
+from tests.gpu_helpers import make_model, run_gpu_blend, dev, host, TORCH_DT, compare, TOL
 from workloads import TINY, WORKLOADS, ModelShape
 
 pytestmark = pytest.mark.gpu
 TW = WORKLOADS["tiny"]
-TOL = {"f32": 1e-4, "bf16": 2e-2}
-
-
-def check_selection(gpu_sel, ref, l, k, band):
-    """Kept sets must agree; where GPU and oracle deviations differ only by
-    rounding, a swapped row must lie within `band` of the k-th deviation."""
-    got = set(gpu_sel.tolist())
-    want = set(ref["sel"][l].tolist())
-    if got == want:
-        return True
-    d = ref["dev"][l]
-    kth = np.sort(d[~np.isnan(d)])[::-1][k - 1]
-    for j in got ^ want:
-        assert abs(d[j] - kth) <= band * kth, (l, j, d[j], kth)
-    return False
-
-
-def compare(case, gpu, ref, sched, dt, check_hidden=True):
-    tol = TOL[dt]
-    L = case.shape.n_layers
-    Nc = case.n_chunk_tokens
-    same = True
-    for l in range(L):
-        k = sched[l + 1]
-        if k and sched[l] > k:
-            same = check_selection(gpu["sel"][l, :k].cpu().numpy(), ref, l, k,
-                                   1e-3 if dt == "f32" else 5e-2)
-        elif k:
-            np.testing.assert_array_equal(gpu["sel"][l, :k].cpu().numpy(), ref["sel"][l])
-        if not same:
-            break
-        assert rel_err(host(gpu["fused_k"][l]), ref["fused_k"][l]) < tol, ("K", l)
-        assert rel_err(host(gpu["fused_v"][l]), ref["fused_v"][l]) < tol, ("V", l)
-        if sched[l] and Nc:
-            d_ref = ref["dev"][l]
-            m = ~np.isnan(d_ref)
-            d_gpu = host(gpu["dev"][l])
-            if sched[l] > sched[l + 1]:
-                assert np.all(~np.isnan(d_gpu[m]))
-                assert rel_err(d_gpu[m], d_ref[m]) < (1e-3 if dt == "f32" else 5e-2)
-    if same and check_hidden:
-        assert rel_err(host(gpu["hidden"]), ref["hidden"]) < tol
-    return same
 
 
 @pytest.fixture(scope="module", params=["f32", "bf16"])
@@ -73,8 +30,7 @@ def test_tiny_blend_vs_oracle(lib, tiny, r, kind):
     sched = oracle.schedule(case.n_chunk_tokens, r, kind, TINY.n_layers)
     gpu = run_gpu_blend(lib, model, case, dt, sched)
     assert gpu["sel_count"] == sched[1:]
-    ref = run_blend(case, sched)
-    compare(case, gpu, ref, sched, dt)
+    compare(case, gpu, sched, dt)
 
 
 def test_tiny_full_recompute_equals_prefill(lib, tiny):
@@ -140,8 +96,7 @@ def test_dev_modes(lib, mode, name):
     model = make_model(lib, case, "f32")
     sched = oracle.schedule(case.n_chunk_tokens, 1500, "fixed", TINY.n_layers)
     gpu = run_gpu_blend(lib, model, case, "f32", sched, dev_mode=mode)
-    ref = run_blend(case, sched, dev_mode=name)
-    compare(case, gpu, ref, sched, "f32")
+    compare(case, gpu, sched, "f32", dev_mode=name)
 
 
 def test_gqa_head_dim128_blend_vs_oracle(lib):
@@ -152,7 +107,7 @@ def test_gqa_head_dim128_blend_vs_oracle(lib):
     for r, kind in ((1500, "gradual"), (10000, "fixed")):
         sched = oracle.schedule(case.n_chunk_tokens, r, kind, 2)
         gpu = run_gpu_blend(lib, model, case, "f32", sched)
-        compare(case, gpu, run_blend(case, sched), sched, "f32")
+        compare(case, gpu, sched, "f32")
 
 
 def test_single_chunk_r0_is_cache_bit_exact(lib):
@@ -172,7 +127,7 @@ def test_seeds_and_schedule_sweep_fp32(lib):
         for r in (100, 1000, 5000):
             sched = oracle.schedule(case.n_chunk_tokens, r, "gradual", 2)
             gpu = run_gpu_blend(lib, model, case, "f32", sched)
-            compare(case, gpu, run_blend(case, sched), sched, "f32")
+            compare(case, gpu, sched, "f32")
 
 
 def test_error_paths(lib, tiny):
@@ -218,7 +173,35 @@ def test_long_context_bf16_blend_vs_oracle(lib):
     model = make_model(lib, case, "bf16")
     sched = oracle.schedule(case.n_chunk_tokens, 1500, "gradual", TINY.n_layers)
     gpu = run_gpu_blend(lib, model, case, "bf16", sched)
-    compare(case, gpu, run_blend(case, sched), sched, "bf16")
+    compare(case, gpu, sched, "bf16")
     full = [case.n_chunk_tokens] * 3
     gpu = run_gpu_blend(lib, model, case, "bf16", full)
-    compare(case, gpu, run_blend(case, full), full, "bf16")
+    compare(case, gpu, full, "bf16")
+
+
+def test_binding_rejects_mismatched_outputs(lib, tiny):
+    """Outputs of the wrong element type or too small for the request are
+    rejected by the binding before any kernel is queued."""
+    dt, case, model = tiny
+    sched = oracle.schedule(case.n_chunk_tokens, 1500, "gradual", TINY.n_layers)
+    chunks = __import__("tests.gpu_helpers", fromlist=["x"]).chunk_inputs(case, dt)
+    x0 = dev(case.x0, dt)
+    L, N, Nc = TINY.n_layers, case.n_tokens, case.n_chunk_tokens
+    shape = (L, N, TINY.n_kv_heads, TINY.head_dim)
+    fk = torch.empty(shape, dtype=TORCH_DT[dt], device="cuda")
+    fv = torch.empty_like(fk)
+    other = torch.float32 if dt == "bf16" else torch.bfloat16
+    cases = [
+        dict(fused_k=torch.empty(shape, dtype=other, device="cuda")),
+        dict(fused_v=fv[:, :N - 1].contiguous()),
+        dict(sel_idx=torch.empty((L, Nc), dtype=torch.int64, device="cuda")),
+        dict(hidden_out=torch.empty((case.n_suffix + sched[-1] - 1, TINY.d_model),
+                                    device="cuda")),
+        dict(deviation=torch.empty((L, Nc - 1), device="cuda")),
+    ]
+    for over in cases:
+        kw = dict(fused_k=fk, fused_v=fv)
+        kw.update(over)
+        with pytest.raises(lib.CBError) as e:
+            lib.cb_blend(model, chunks, case.offsets, case.n_suffix, x0, schedule=sched, **kw)
+        assert e.value.status in (lib.CB_E_INVALID, lib.CB_E_SHAPE), over.keys()

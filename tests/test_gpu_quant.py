@@ -20,7 +20,7 @@ import oracle
 from tests.helpers import make_case, make_batch_case, quantize_case, run_blend, rel_err
 from tests.gpu_helpers import (make_model, run_gpu_blend, run_gpu_batch, quant_chunk, dev,
                                host, TORCH_DT)
-from tests.test_gpu_blend import compare
+from tests.gpu_helpers import compare
 from workloads import TINY, WORKLOADS, BATCHED_TINY, ModelShape, round_to, make_batched_requests
 
 pytestmark = pytest.mark.gpu
@@ -115,7 +115,7 @@ def test_blend_quantized_chunks_vs_oracle(lib, dt, bits):
         print(f"[blend-q] dt={dt} bits={bits} r={r} {kind}", flush=True)
         sched = oracle.schedule(case.n_chunk_tokens, r, kind, TINY.n_layers)
         gpu = run_gpu_blend(lib, model, dcase, dt, sched, quant=(codes, bits))
-        compare(dcase, gpu, run_blend(dcase, sched), sched, dt)
+        compare(dcase, gpu, sched, dt)
 
 
 @pytest.mark.parametrize("bits", [8, 4])
@@ -142,7 +142,7 @@ def test_gqa_head_dim128_quantized_vs_oracle(lib):
     model = make_model(lib, case, "f32")
     sched = oracle.schedule(case.n_chunk_tokens, 1500, "gradual", 2)
     gpu = run_gpu_blend(lib, model, dcase, "f32", sched, quant=(codes, 8), on_host=True)
-    compare(dcase, gpu, run_blend(dcase, sched), sched, "f32")
+    compare(dcase, gpu, sched, "f32")
 
 
 @pytest.mark.parametrize("dt", ["f32", "bf16"])
@@ -171,7 +171,7 @@ def test_batch_mixed_formats_vs_oracle(lib, dt):
     for b, case in enumerate(cases):
         sched = oracle.schedule(case.n_chunk_tokens, 1500, "gradual", TINY.n_layers)
         assert per[b]["sel_count"] == sched[1:], b
-        compare(case, per[b], run_blend(case, sched), sched, dt)
+        compare(case, per[b], sched, dt)
 
 
 def test_quantized_chunk_validation(lib):

@@ -315,6 +315,39 @@ def test_check_layer_identity(tiny_case, tiny_full):
         assert min(true_dev[list(kept)]) >= max(true_dev[dropped])
 
 
+def test_forced_selection_replay(tiny_case, tiny_full):
+    """Teacher forcing (the parity rule for selections that differ by
+    rounding at the threshold): forcing the sets the oracle picks itself
+    reproduces the run bit for bit; forcing any other valid set at the check
+    layer keeps the check-layer identity (fused-vs-full error = deviation of
+    the rows not kept, CacheBlend explainer (0h-n0), eq. 1 with the K/V merge
+    equations) and moves only the rows it changes; invalid sets raise."""
+    case = tiny_case
+    nc = case.n_chunk_tokens
+    sched = oracle.schedule(nc, 1500, "gradual", TINY.n_layers)
+    nat = run_blend(case, sched)
+    same = oracle.blend(case.weights, TINY, case.x0, case.chunks, case.offsets, case.n_suffix,
+                        sched, forced_sel=nat["sel"])
+    for key in ("fused_k", "fused_v", "hidden"):
+        assert np.array_equal(same[key], nat[key])
+    rng = np.random.default_rng(5)
+    forced = np.sort(rng.choice(nc, size=sched[2], replace=False))
+    alt = oracle.blend(case.weights, TINY, case.x0, case.chunks, case.offsets, case.n_suffix,
+                       sched, forced_sel=[None, forced])
+    assert np.array_equal(alt["sel"][1], forced)
+    assert np.array_equal(alt["fused_k"][0], nat["fused_k"][0])
+    assert np.array_equal(alt["dev"][1], nat["dev"][1])
+    k, v, _ = tiny_full
+    err = np.sum((alt["fused_k"][1][:nc] - k[1][:nc]) ** 2, axis=(1, 2)) + \
+        np.sum((alt["fused_v"][1][:nc] - v[1][:nc]) ** 2, axis=(1, 2))
+    dropped = np.setdiff1d(np.arange(nc), forced)
+    assert abs(err.sum() - alt["dev"][1][dropped].sum()) < 1e-9 * alt["dev"][1].sum()
+    for bad in (forced[:-1], np.concatenate([forced[:-1], forced[:1]]), forced + nc):
+        with pytest.raises(ValueError):
+            oracle.blend(case.weights, TINY, case.x0, case.chunks, case.offsets, case.n_suffix,
+                         sched, forced_sel=[None, bad])
+
+
 def test_deviation_falls_as_r_grows():
     """North-star check: total KV deviation of the fused cache from full
     prefill does not grow as r grows, and is zero at r = 100% (tiny config,

@@ -8,11 +8,13 @@ from .shapes import (ModelShape, Workload, TINY, LLAMA7B, LLAMA13B, YI34B,
                      WORKLOADS, BatchedWorkload, BATCHED_LLAMA7B, BATCHED_TINY,
                      BATCHED_WORKLOADS)
 from .gen import (make_weights_np, make_tokens, make_embedding_np, round_to,
-                  make_batched_requests, make_batch_tokens, make_request_stream)
+                  make_batched_requests, make_batch_tokens, make_request_stream,
+                  make_chunk_caches_np)
 
 __all__ = [
     "ModelShape", "Workload", "TINY", "LLAMA7B", "LLAMA13B", "YI34B", "WORKLOADS",
     "BatchedWorkload", "BATCHED_LLAMA7B", "BATCHED_TINY", "BATCHED_WORKLOADS",
     "make_weights_np", "make_tokens", "make_embedding_np", "round_to",
     "make_batched_requests", "make_batch_tokens", "make_request_stream",
+    "make_chunk_caches_np",
 ]

@@ -29,9 +29,16 @@ def round_to(a: np.ndarray, dtype: str) -> np.ndarray:
     if dtype == "f32":
         return np.asarray(a, dtype=np.float32).astype(np.float64)
     if dtype == "bf16":
-        import torch
-        t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32))
-        return t.to(torch.bfloat16).to(torch.float64).numpy()
+        # float32, then round to nearest even at bit 16 of the pattern
+        # (finite inputs): the conversion torch and the GPU use for bf16
+        f = np.array(a, dtype=np.float32, order="C")
+        u = f.view(np.uint32)
+        bias = u >> np.uint32(16)
+        bias &= np.uint32(1)
+        bias += np.uint32(0x7FFF)
+        u += bias
+        u &= np.uint32(0xFFFF0000)
+        return f.astype(np.float64)
     raise ValueError(dtype)
 
 
@@ -120,3 +127,20 @@ def make_batch_tokens(shape: ModelShape, pool_lens, reqs, seed: int = 0):
     suffix_tokens = [g.integers(0, shape.vocab, size=int(r["n_suffix"]), dtype=np.int64)
                      for r in reqs]
     return pool_tokens, suffix_tokens
+
+
+def make_chunk_caches_np(shape: ModelShape, chunk_lens, seed: int = 0, dtype: str = "f64",
+                         std: float = 1.0):
+    """Seeded stand-in chunk caches: K and V [L][n_c][H_kv][d_head] drawn
+    i.i.d. N(0, std^2) per chunk and rounded to `dtype`.  The fusion takes
+    any cached values, so parity checks at full model width can skip the
+    per-chunk precompute; std = 1 is the scale of a projected row of the
+    N(0, 0.02^2) weights at these widths."""
+    out = []
+    for c, n in enumerate(chunk_lens):
+        g = np.random.Generator(np.random.PCG64([int(seed), int(c), 97]))
+        shp = (shape.n_layers, int(n), shape.n_kv_heads, shape.head_dim)
+        k = round_to(g.standard_normal(shp, dtype=np.float64) * std, dtype)
+        v = round_to(g.standard_normal(shp, dtype=np.float64) * std, dtype)
+        out.append((k, v))
+    return out
