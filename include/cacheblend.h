@@ -514,6 +514,24 @@ cb_status cb_attention(int32_t dtype, const void* q, const int32_t* q_pos, int32
                        const void* k, const void* v, int32_t n_kv, int32_t n_q_heads,
                        int32_t n_kv_heads, int32_t head_dim, void* out, void* stream);
 
+/* ------------------------------------------------------------- no allocation
+ * For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * cb_attention_noalloc computes exactly what cb_attention computes (same
+ * arguments, same kernels, bit-identical results) but allocates nothing:
+ * the split-key partials that cb_attention places in a per-call workspace
+ * live in a fixed device array of CB_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library, one copy per GPU, held until the process ends.  A call whose
+ * partials would not fit returns CB_E_SHAPE (cb_attention serves it).  Every
+ * call on one GPU shares that array, so calls that overlap in time on one
+ * GPU (other streams, other threads) race; calls ordered on one stream do
+ * not.  The first call on a device looks up the array's address there. */
+#define CB_NOALLOC_SCRATCH_BYTES (80ull << 20)
+cb_status cb_attention_noalloc(int32_t dtype, const void* q, const int32_t* q_pos, int32_t n_q,
+                               const void* k, const void* v, int32_t n_kv, int32_t n_q_heads,
+                               int32_t n_kv_heads, int32_t head_dim, void* out, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

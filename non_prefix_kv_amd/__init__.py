@@ -147,7 +147,10 @@ _fn = {
     "cb_gemm": (ctypes.c_int, _c_i32, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p),
     "cb_attention": (ctypes.c_int, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_i32, _c_i32,
                      _c_i32, _c_i32, _c_p, _c_p),
+    "cb_attention_noalloc": (ctypes.c_int, _c_i32, _c_p, _c_p, _c_i32, _c_p, _c_p, _c_i32,
+                             _c_i32, _c_i32, _c_i32, _c_p, _c_p),
 }
+CB_NOALLOC_SCRATCH_BYTES = 80 << 20
 RAW = {name: _sig(name, spec[0], *spec[1:]) for name, spec in _fn.items()}
 EXPORTED = tuple(_fn)
 
@@ -670,3 +673,10 @@ def cb_attention(q, q_pos, n_q, k, v, n_kv, n_q_heads, n_kv_heads, head_dim, out
     _check(RAW["cb_attention"](_dtype_code(q), _ptr(q), _ptr(q_pos), n_q, _ptr(k), _ptr(v), n_kv,
                                n_q_heads, n_kv_heads, head_dim, _ptr(out), _stream(stream)))
 
+
+def cb_attention_noalloc(q, q_pos, n_q, k, v, n_kv, n_q_heads, n_kv_heads, head_dim, out,
+                         stream=None):
+    """cb_attention without any device allocation (fixed library scratch)."""
+    _check(RAW["cb_attention_noalloc"](_dtype_code(q), _ptr(q), _ptr(q_pos), n_q, _ptr(k),
+                                       _ptr(v), n_kv, n_q_heads, n_kv_heads, head_dim, _ptr(out),
+                                       _stream(stream)))
