@@ -417,7 +417,8 @@ typedef enum cb_kernel_class {
     CB_K_RMSNORM,
     CB_K_GEMM_QKV,
     CB_K_DEVIATION,
-    CB_K_SELECT,
+    CB_K_SELECT,        /* selection, and the kept positions of layers that keep
+                           every row (copied after the last layer)               */
     CB_K_SCATTER,
     CB_K_ATTENTION,
     CB_K_GEMM_O,

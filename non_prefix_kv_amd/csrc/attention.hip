@@ -282,6 +282,15 @@ __device__ __forceinline__ void mfma32(floatx16& acc, const bf16x8& a, const bf1
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
 }
 
+// Three-way maximum in one instruction.  fmaxf would first quiet each
+// operand (an extra instruction per score in IEEE mode); scores are finite
+// or -inf here, so the plain instruction gives the same result.
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+    float r;
+    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+    return r;
+}
+
 constexpr int kT32 = 256;   // threads per workgroup (4 waves)
 constexpr int QT32 = 128;   // queries per workgroup
 constexpr int KBL = 64;     // keys per block
@@ -396,7 +405,15 @@ __global__ __launch_bounds__(kT32, 2) void attention64_kernel(AttnArgs a, const 
     for (int t = 0; t < NDT; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+    float m_run = -INFINITY;
+    // Softmax denominators: every row of lacc holds the sum of the probabilities
+    // of the lane's query (the P.V MFMA against a ones operand).
+    floatx16 lacc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) lacc[i] = 0.f;
+    bf16x8 ones;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ones[j] = static_cast<bf16>(1.0f);
     const float sl2 = 1.4426950408889634f / sqrtf((float)D);
 
     const bf16* kbase = static_cast<const bf16*>(a.k) + (int64_t)tile.g0 * kv_ld + hk * D;
@@ -438,18 +455,35 @@ __global__ __launch_bounds__(kT32, 2) void attention64_kernel(AttnArgs a, const 
         if (a.kv_pos0 + k0 > wmax) return;          // wave-uniform: nothing visible
         const unsigned char* sk = smem + st * 2 * BLK;
         const unsigned char* sv = sk + BLK;
+        // S^T = K Q^T for the block's two 32-key halves: K fragments are read
+        // two reduction steps ahead of their MFMAs so the LDS latency hides
+        // behind the two independent MFMA chains.
         floatx16 s2[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int i = 0; i < 16; ++i) s2[hh][i] = 0.f;
+        bf16x8 k_lo[3], k_hi[3];
+        auto read_k = [&](int s) {
+            const int off = fr * RB + (((2 * s + g) ^ kkey) & (CPR - 1)) * 16;
+            k_lo[s % 3] = *reinterpret_cast<const bf16x8*>(sk + off);
+            k_hi[s % 3] = *reinterpret_cast<const bf16x8*>(sk + off + 32 * RB);
+        };
+        read_k(0);
+        read_k(1);
 #pragma unroll
         for (int s = 0; s < NDS; ++s) {
-            const int off = fr * RB + (((2 * s + g) ^ kkey) & (CPR - 1)) * 16;
-            const bf16x8 k_lo = *reinterpret_cast<const bf16x8*>(sk + off);
-            const bf16x8 k_hi = *reinterpret_cast<const bf16x8*>(sk + off + 32 * RB);
-            mfma32(s2[0], k_lo, qf[s]);
-            mfma32(s2[1], k_hi, qf[s]);
+            if (s + 2 < NDS) read_k(s + 2);
+            mfma32(s2[0], k_lo[s % 3], qf[s]);
+            mfma32(s2[1], k_hi[s % 3], qf[s]);
+        }
+        // keep that order: the scheduler would otherwise sink each read to
+        // its MFMA and expose the LDS latency at every step
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);           // reads of steps 0, 1
+#pragma unroll
+        for (int s = 0; s < NDS; ++s) {
+            if (s + 2 < NDS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);   // step s + 2
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                    // step s
         }
         // Scores stay unscaled; the running max is kept in scaled (log2)
         // units and the scale is folded into one FMA before v_exp_f32.
@@ -463,9 +497,10 @@ __global__ __launch_bounds__(kT32, 2) void attention64_kernel(AttnArgs a, const 
                 for (int i = 0; i < 16; ++i)
                     if (32 * hh + 8 * (i >> 2) + (i & 3) > lim) s2[hh][i] = -INFINITY;
         }
-        float mloc = fmaxf(s2[0][0], s2[1][0]);
+        float mloc = vmax3(s2[0][0], s2[1][0], s2[0][1]);
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mloc = fmaxf(mloc, fmaxf(s2[0][i], s2[1][i]));
+        for (int i = 1; i < 16; ++i)
+            mloc = i == 1 ? vmax3(mloc, s2[1][1], s2[1][1]) : vmax3(mloc, s2[0][i], s2[1][i]);
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * sl2;
         // The reference maximum only moves when a score exceeds it by more
         // than kLazyLog2 (probabilities then stay below 2^kLazyLog2): after
@@ -477,40 +512,43 @@ __global__ __launch_bounds__(kT32, 2) void attention64_kernel(AttnArgs a, const 
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         if (__ballot(grow)) {
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            l_run *= alpha;
+            lacc *= alpha;
 #pragma unroll
             for (int t = 0; t < NDT; ++t) o[t] *= alpha;
         }
         m_run = m_new;
-        // P^T slot j of 16-key group q4 = 2 hh + j / 8 holds key
+        // Per 16-key group q4: its transposed V reads first (they do not
+        // depend on P), then the group's probabilities, then one MFMA per
+        // 32-dim output tile (independent accumulators) and one more against
+        // a ones operand, which adds the group's probabilities of each query
+        // (the softmax denominator, from the same rounded P as the numerator).
+        // P^T slot j of group q4 = 2 hh + j / 8 holds key
         // 32 hh + 16 (j / 8) + 8 ((j % 8) / 4) + 4 g + j % 4: the key order
-        // of the transposed V reads below.
-        bf16x8 pf[4];
-        float lsum = 0.f;
+        // of the transposed V reads.
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+        for (int q4 = 0; q4 < 4; ++q4) {
+            typedef short i16x4 __attribute__((ext_vector_type(4)));
+            typedef short i16x8 __attribute__((ext_vector_type(8)));
+            typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+            bf16x8 vf[NDT];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const float p = __builtin_amdgcn_exp2f(fmaf(s2[hh][i], sl2, -m_use));
-                lsum += p;
-                pf[2 * hh + (i >> 3)][i & 7] = static_cast<bf16>(p);
-            }
-        l_run += lsum;
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-            for (int q4 = 0; q4 < 4; ++q4) {
-                typedef short i16x4 __attribute__((ext_vector_type(4)));
-                typedef short i16x8 __attribute__((ext_vector_type(8)));
-                typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+            for (int dt = 0; dt < NDT; ++dt) {
                 const int col = dt * 32 + tr_col;
                 const int off = (16 * q4 + tr_row) * RB + ((((col >> 3) ^ vkey) & (CPR - 1)) << 4) +
                                 (col & 7) * 2;
                 const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sv + off));
                 const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(sv + off + 8 * RB));
-                const i16x8 w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-                mfma32(o[dt], __builtin_bit_cast(bf16x8, w), pf[q4]);
+                vf[dt] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
             }
+            bf16x8 pf;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                pf[j] = static_cast<bf16>(__builtin_amdgcn_exp2f(
+                    fmaf(s2[q4 >> 1][(q4 & 1) * 8 + j], sl2, -m_use)));
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) mfma32(o[dt], vf[dt], pf);
+            mfma32(lacc, ones, pf);
+        }
     };
     // Two stages: block kb+1 is copied into the other stage while block kb is
     // multiplied out; the wait + barrier at the end publishes it (and tells
@@ -527,7 +565,7 @@ __global__ __launch_bounds__(kT32, 2) void attention64_kernel(AttnArgs a, const 
         __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
         __syncthreads();
     }
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const float l_tot = lacc[0];
     if (n_seg > 1) {
         // Partial of this segment: O normalized by the segment's own sum (bf16,
         // half the bytes of the unnormalized float sums), running max (log2

@@ -135,6 +135,19 @@ hipError_t launch_init_rows(const RowInitTab& t, int* pos, int* rows, hipStream_
 // Fills p[0..n) with the float value v.
 hipError_t launch_fill(float* p, int64_t n, float v, hipStream_t s);
 
+// Row copies within one int array of rows of row_len entries: row dst =
+// row src for every pair (sources are never destinations of the same call).
+constexpr int kMaxRowCopies = 64;
+struct RowCopy {
+    int dst, src;
+};
+struct IntRowCopies {
+    RowCopy c[kMaxRowCopies];
+    int n;
+};
+hipError_t launch_copy_int_rows(int* base, int64_t row_len, const IntRowCopies& t,
+                                hipStream_t s);
+
 // ------------------------------------------------------------------ selection
 // For every request of the table and i < n_c: dev[c_off + i] = deviation of
 // new row (r_off + i) against cached row crow = grow[r_off + i] (grow null:

@@ -176,6 +176,15 @@ __global__ __launch_bounds__(kThreads) void fill_kernel(float* p, int64_t n, flo
         p[i] = v;
 }
 
+// Row copies inside one int array of rows of row_len entries.
+__global__ __launch_bounds__(kThreads) void copy_int_rows_kernel(int* __restrict__ base,
+                                                                  int64_t row_len,
+                                                                  const IntRowCopies t) {
+    const RowCopy c = t.c[blockIdx.y];
+    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    if (i < row_len) base[c.dst * row_len + i] = base[c.src * row_len + i];
+}
+
 }  // namespace
 
 hipError_t launch_rerotate(int dtype, const RotJobs& jobs, int layer, void* k_dst, void* v_dst,
@@ -294,6 +303,18 @@ hipError_t launch_rmsnorm(int x_dtype, const void* x, const int* idx, int y_dtyp
     else
         hipLaunchKernelGGL((rmsnorm_kernel<bf16, float>), grid, block, 0, s, (const bf16*)x,
                            idx, (const float*)g, (float*)y, x_copy, d, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_copy_int_rows(int* base, int64_t row_len, const IntRowCopies& t,
+                                hipStream_t s) {
+    if (t.n <= 0 || row_len <= 0) return hipSuccess;
+    if (t.n > kMaxRowCopies) return hipErrorInvalidValue;
+    for (int i = 0; i < t.n; ++i)
+        if (t.c[i].dst < 0 || t.c[i].src < 0 || t.c[i].dst == t.c[i].src)
+            return hipErrorInvalidValue;
+    dim3 grid((unsigned)((row_len + kThreads - 1) / kThreads), t.n);
+    hipLaunchKernelGGL(copy_int_rows_kernel, grid, dim3(kThreads), 0, s, base, row_len, t);
     return hipGetLastError();
 }
 

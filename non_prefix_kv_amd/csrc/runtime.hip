@@ -233,6 +233,10 @@ struct cb_plan {
          *act = nullptr;
     int *pos_a = nullptr, *pos_b = nullptr, *row_a = nullptr, *row_b = nullptr,
         *sel_local = nullptr;
+    // layers run in place whose kept positions are asked for: sel_idx row
+    // first = row second (the last layer that wrote its row), filled after
+    // the last layer
+    std::vector<std::pair<int, int>> sel_rows_pending;
     void* attn_ws = nullptr;      // split-attention partials
     size_t attn_ws_bytes = 0;
     // fetch: host chunks copied once per layer into their first place of use,
@@ -593,6 +597,22 @@ cb_status do_fetch(cb_plan* p, int l) {
     return CB_OK;
 }
 
+// Kept positions of the layers run in place (copies of the row of the last
+// layer that selected), after the last layer.
+cb_status flush_sel_rows(cb_plan* p) {
+    if (p->sel_rows_pending.empty()) return CB_OK;
+    Span sp(p->m, CB_K_SELECT, p->stream, 0, 8.0 * p->Nctot * p->sel_rows_pending.size());
+    for (size_t i = 0; i < p->sel_rows_pending.size(); i += kMaxRowCopies) {
+        IntRowCopies t{};
+        t.n = (int)std::min<size_t>(kMaxRowCopies, p->sel_rows_pending.size() - i);
+        for (int j = 0; j < t.n; ++j)
+            t.c[j] = RowCopy{p->sel_rows_pending[i + j].first, p->sel_rows_pending[i + j].second};
+        CB_HIP(launch_copy_int_rows(p->sel_idx, p->Nctot, t, p->stream));
+    }
+    p->sel_rows_pending.clear();
+    return CB_OK;
+}
+
 cb_status do_layer(cb_plan* p, int l) {
     cb_model* m = p->m;
     const cb_model_cfg& c = m->cfg;
@@ -605,7 +625,7 @@ cb_status do_layer(cb_plan* p, int l) {
     CB_HIP(hipEventRecord(p->layer_start[l], st));
     if (mR == 0) {
         CB_HIP(hipStreamWaitEvent(st, p->fetched[l], 0));
-        return CB_OK;
+        return l == p->L - 1 ? flush_sel_rows(p) : CB_OK;
     }
     void* fk = (char*)p->fused_k + (size_t)l * layer_elems(p) * es;
     void* fv = (char*)p->fused_v + (size_t)l * layer_elems(p) * es;
@@ -640,36 +660,58 @@ cb_status do_layer(cb_plan* p, int l) {
     }
     // fused[l] is first read below: steps 1-2 overlap the fetch of this layer
     CB_HIP(hipStreamWaitEvent(st, p->fetched[l], 0));
-    // 3. deviation of the recomputed chunk rows against the rotated cache
+    // 3-4. deviation of the recomputed chunk rows against the rotated cache,
+    // then per request: keep the top s[l+1] chunk rows, then the suffix rows.
+    // A layer where every request keeps all the rows it recomputed keeps them
+    // in place: its query rows are its recomputed rows in the same order, so
+    // the row maps stay as they are and nothing is launched, unless the
+    // selection's outputs (kept positions, deviations by position) are asked for.
     const bool measure = lr.nC > 0 && (lr.select_needed || p->deviation);
-    if (measure && p->dev_mode == CB_DEV_GIVEN) {
-        Span sp(m, CB_K_DEVIATION, st, 0, lr.nC * 12.0);
-        for (const ReqTab& t : tabs) CB_HIP(launch_given_scores(p->given, t, pos_r, p->dev, st));
-    } else if (measure) {
-        const double parts = p->dev_mode == CB_DEV_KV ? 4 : 2;
-        Span sp(m, CB_K_DEVIATION, st, 0, lr.nC * (parts * kvd * es + 8.0));
-        for (const ReqTab& t : tabs)
-            CB_HIP(launch_deviation(dt, p->Kn, p->Vn, fk, fv, row_r, t, m->kvd(), p->dev_mode,
-                                    p->dev, st));
-    }
-    // 4. per request: keep the top s[l+1] chunk rows, then the suffix rows
+    // (with kept positions asked for, a layer after the first in place keeps
+    // the previous layer's positions: its sel_idx row is copied at the end)
+    const bool in_place =
+        !lr.select_needed && !(measure && p->deviation) && (!p->sel_idx || l > 0);
+    const int* qmap = p->sel_local;     // query row -> recomputed row (null: identity)
     {
         int* sel_pos = p->sel_idx ? p->sel_idx + (size_t)l * p->Nctot : nullptr;
         float* dev_out = (measure && p->deviation) ? p->deviation + (size_t)l * p->Nctot : nullptr;
-        Span sp(m, CB_K_SELECT, st, 0, 4.0 * lr.nC + 16.0 * mQ);
-        for (const ReqTab& t : tabs)
-            CB_HIP(launch_select(p->dev, t, pos_r, row_r, p->sel_local, pos_q, row_q, sel_pos,
-                                 dev_out, st));
+        if (in_place) {
+            qmap = nullptr;
+            pos_q = const_cast<int*>(pos_r);
+            row_q = const_cast<int*>(row_r);
+            if (p->sel_idx) {
+                int src = l - 1;
+                if (!p->sel_rows_pending.empty() && p->sel_rows_pending.back().first == l - 1)
+                    src = p->sel_rows_pending.back().second;
+                p->sel_rows_pending.push_back({l, src});
+            }
+        } else {
+            if (measure && p->dev_mode == CB_DEV_GIVEN) {
+                Span sp(m, CB_K_DEVIATION, st, 0, lr.nC * 12.0);
+                for (const ReqTab& t : tabs)
+                    CB_HIP(launch_given_scores(p->given, t, pos_r, p->dev, st));
+            } else if (measure) {
+                const double parts = p->dev_mode == CB_DEV_KV ? 4 : 2;
+                Span sp(m, CB_K_DEVIATION, st, 0, lr.nC * (parts * kvd * es + 8.0));
+                for (const ReqTab& t : tabs)
+                    CB_HIP(launch_deviation(dt, p->Kn, p->Vn, fk, fv, row_r, t, m->kvd(),
+                                            p->dev_mode, p->dev, st));
+            }
+            Span sp(m, CB_K_SELECT, st, 0, 4.0 * lr.nC + 16.0 * mQ);
+            for (const ReqTab& t : tabs)
+                CB_HIP(launch_select(p->dev, t, pos_r, row_r, p->sel_local, pos_q, row_q, sel_pos,
+                                     dev_out, st));
+        }
     }
     // 5. merge the kept rows' K/V into the fused cache
     {
         Span sp(m, CB_K_SCATTER, st, 0, 4.0 * mQ * kvd * es);
-        CB_HIP(launch_scatter_kv(dt, p->Kn, p->Vn, p->sel_local, row_q, fk, fv, mQ, m->kvd(), st));
+        CB_HIP(launch_scatter_kv(dt, p->Kn, p->Vn, qmap, row_q, fk, fv, mQ, m->kvd(), st));
     }
     // 6. attention of each request's kept rows over its whole fused cache
     {
         AttnArgs a{};
-        a.q = p->Q; a.qidx = p->sel_local; a.q_pos = pos_q;
+        a.q = p->Q; a.qidx = qmap; a.q_pos = pos_q;
         a.k = fk; a.v = fv; a.kv_pos0 = p->kv_pos0;
         a.n_q_heads = c.n_q_heads; a.n_kv_heads = c.n_kv_heads; a.head_dim = c.head_dim;
         a.out = p->attn;
@@ -683,7 +725,7 @@ cb_status do_layer(cb_plan* p, int l) {
     {
         GemmArgs go{};
         go.a = p->attn; go.b0 = w.wo; go.M = mQ; go.N = c.d_model; go.K = m->qd();
-        go.out0 = p->Hres; go.resid = p->X; go.ridx = p->sel_local;
+        go.out0 = p->Hres; go.resid = p->X; go.ridx = qmap;
         Span sp(m, CB_K_GEMM_O, st, 2.0 * mQ * d * qd, (mQ * qd + d * qd) * es + mQ * d * 8);
         CB_HIP(launch_gemm(dt, EPI_RESID, go, st));
     }
@@ -711,8 +753,11 @@ cb_status do_layer(cb_plan* p, int l) {
         Span sp(m, CB_K_GEMM_DOWN, st, 2.0 * mQ * d * F, (mQ * F + d * F) * es + mQ * d * 8);
         CB_HIP(launch_gemm(dt, EPI_RESID, gd, st));
     }
-    std::swap(p->pos_a, p->pos_b);
-    std::swap(p->row_a, p->row_b);
+    if (!in_place) {
+        std::swap(p->pos_a, p->pos_b);
+        std::swap(p->row_a, p->row_b);
+    }
+    if (l == p->L - 1) return flush_sel_rows(p);
     return CB_OK;
 }
 

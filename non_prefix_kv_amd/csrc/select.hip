@@ -314,3 +314,4 @@ hipError_t launch_select(const float* dev, const ReqTab& t, const int* pos_r, co
 }
 
 }  // namespace cb
+
