@@ -54,10 +54,17 @@ its reason in the design notes):
     theta_i = base^(-2i/d_head), causal softmax attention with GQA head map
     h -> floor(h * H_kv / H_q), SwiGLU MLP, no biases.
 
-Pin status: every function here is pinned by tests/test_oracle_pins.py except
-the constants of the gradual schedule (`schedule`, kind 'gradual'), which are
-a proposal the pages do not fix: parity unpinned (both sides consume the same
-integer schedule).
+  * Per-token attention deviation (first-layer rule of HKVD selection): for
+    a chunk row, the sum over query heads and keys of the squared difference
+    between its attention probabilities over the recomputed keys and over
+    the cached keys, at layers where every chunk row is recomputed (so the
+    first equal the full prefill's); later layers narrow by KV deviation.
+
+Pin status: every function here is pinned by tests/test_oracle_pins.py and
+tests/test_oracle_block_pins.py (the transformer block against transformers'
+Llama layer) except the constants of the gradual schedule (`schedule`, kind
+'gradual'), which are a proposal the pages do not fix: parity unpinned (both
+sides consume the same integer schedule).
 """
 import math
 import time
@@ -232,6 +239,36 @@ def kv_deviation(k_new, v_new, k_cached, v_cached, mode: str = "KV"):
     raise ValueError(mode)
 
 
+def attention_probs(q, qpos, k, kpos):
+    """Causal softmax probability rows: [nq, Hq, nk], row (i, h) over the keys
+    with kpos <= qpos[i], query head h reading KV head floor(h * Hkv / Hq)."""
+    nq, hq, dh = q.shape
+    hkv = k.shape[1]
+    hidden = np.asarray(kpos)[None, :] > np.asarray(qpos)[:, None]
+    out = np.zeros((nq, hq, k.shape[0]), dtype=q.dtype)
+    for h in range(hq):
+        g = (h * hkv) // hq
+        s = (q[:, h, :] @ k[:, g, :].T) / math.sqrt(dh)
+        s = np.where(hidden, -np.inf, s)
+        p = np.exp(s - np.max(s, axis=1, keepdims=True))
+        out[:, h, :] = p / np.sum(p, axis=1, keepdims=True)
+    return out
+
+
+def attention_deviation(q, qpos, k_new, k_cached, kpos):
+    """Per-token attention deviation [CB1 "KVキャッシュの定義と偏差メトリクス"
+    eq. 2 (attention deviation, L2 norm over the attention matrix) taken row
+    by row, as the first-layer rule of "HKVD（High KV Deviation）トークン選定"
+    ranks tokens by it]: for query row i, the sum over query heads and keys
+    of the squared difference between its causal attention probabilities
+    over the recomputed keys k_new and over the cached keys k_cached (same
+    positions kpos).  At a layer where every chunk row is recomputed the
+    first are the full-prefill probabilities and the second what full KV
+    reuse would attend with."""
+    d = attention_probs(q, qpos, k_new, kpos) - attention_probs(q, qpos, k_cached, kpos)
+    return np.sum((d * d).reshape(d.shape[0], -1), axis=1)
+
+
 def topk_select(dev, k: int) -> np.ndarray:
     """Indices of the k largest deviations, returned in ascending order.
 
@@ -289,7 +326,10 @@ def blend(weights, shape, x0, chunks, offsets, n_suffix, sched, dev_mode="KV",
     (final rows).  When `timings` is a list, the wall time of every layer is
     appended to it (seconds); the arithmetic is unaffected.  dev_mode 'GIVEN'
     ranks chunk tokens by given_scores [N_c] (by position) instead of the
-    measured deviation, with the same top-k rule and schedule.
+    measured deviation, with the same top-k rule and schedule.  dev_mode
+    'ATTN' ranks by attention deviation (attention_deviation) at every layer
+    whose candidates are all the chunk rows (up to and including the check
+    layer), and by the KV deviation over K and V at later layers.
 
     forced_sel (teacher forcing): a list with one entry per layer, None or
     the kept positions to use at that layer instead of the top-k of the
@@ -326,8 +366,13 @@ def blend(weights, shape, x0, chunks, offsets, n_suffix, sched, dev_mode="KV",
         if nC:
             if dev_mode == "GIVEN":
                 d = np.asarray(given_scores, dtype=np.float64)[C]
+            elif dev_mode == "ATTN" and nC == nc_tot:
+                # every chunk row recomputed: their new keys against the
+                # cached keys of the same positions (chunk rows 0..N_c-1)
+                d = attention_deviation(q[:nC], C, k[:nC], fk[l][:nc_tot], np.arange(nc_tot))
             else:
-                d = kv_deviation(k[:nC], v[:nC], fk[l][C], fv[l][C], dev_mode)
+                d = kv_deviation(k[:nC], v[:nC], fk[l][C], fv[l][C],
+                                 "KV" if dev_mode == "ATTN" else dev_mode)
             dev[l, C] = d
             keep = (np.arange(nC) if sched[l + 1] == nC
                     else topk_select(d, sched[l + 1]))

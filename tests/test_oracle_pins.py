@@ -660,3 +660,91 @@ def test_given_scores_equal_to_deviation_reproduce_hkvd(tiny_case):
     g = oracle.blend(case.weights, case.shape, case.x0, case.chunks, case.offsets,
                      case.n_suffix, sched, dev_mode="GIVEN", given_scores=ref["dev"][1])
     assert np.array_equal(g["sel"][1], ref["sel"][1])
+
+
+# ------------------------------------------------------ attention deviation
+# CacheBlend explainer (0h-n0), "KVキャッシュの定義と偏差メトリクス" eq. 2 and
+# the first-layer rule of "HKVD（High KV Deviation）トークン選定".
+
+def test_attention_deviation_brute_force():
+    """Probabilities and their squared differences by explicit loops."""
+    rng = np.random.default_rng(81)
+    for hq, hkv in ((2, 2), (3, 1), (4, 2)):
+        nq, nk, dh = 5, 7, 4
+        q = rng.standard_normal((nq, hq, dh))
+        k1 = rng.standard_normal((nk, hkv, dh))
+        k0 = rng.standard_normal((nk, hkv, dh))
+        qpos = np.sort(rng.choice(nk, size=nq, replace=False))
+        got = oracle.attention_deviation(q, qpos, k1, k0, np.arange(nk))
+        for i in range(nq):
+            tot = 0.0
+            for h in range(hq):
+                g = h * hkv // hq
+                rows = []
+                for kk in (k1, k0):
+                    sc = [sum(q[i, h, e] * kk[j, g, e] for e in range(dh)) / math.sqrt(dh)
+                          for j in range(qpos[i] + 1)]
+                    mx = max(sc)
+                    ex = [math.exp(x - mx) for x in sc]
+                    rows.append([x / sum(ex) for x in ex])
+                tot += sum((a - b) ** 2 for a, b in zip(*rows))
+            assert abs(got[i] - tot) < 1e-12 * max(1.0, tot), (hq, i)
+
+
+def test_attention_deviation_vs_library_and_closed_forms():
+    rng = np.random.default_rng(82)
+    nq, nk, hq, hkv, dh = 11, 40, 4, 2, 16
+    q = rng.standard_normal((nq, hq, dh))
+    k1 = rng.standard_normal((nk, hkv, dh))
+    k0 = k1 + 0.3 * rng.standard_normal((nk, hkv, dh))
+    qpos = np.sort(rng.choice(nk, size=nq, replace=False))
+    got = oracle.attention_deviation(q, qpos, k1, k0, np.arange(nk))
+    mask = torch.from_numpy(np.arange(nk)[None, :] > qpos[:, None])
+
+    def probs(k):
+        qt = torch.from_numpy(q).transpose(0, 1)                       # [hq, nq, dh]
+        kt = torch.from_numpy(k).repeat_interleave(hq // hkv, dim=1).transpose(0, 1)
+        s = qt @ kt.transpose(1, 2) / math.sqrt(dh)
+        return torch.softmax(s.masked_fill(mask, float("-inf")), dim=-1)
+    ref = ((probs(k1) - probs(k0)) ** 2).sum(dim=(0, 2)).numpy()
+    assert rel_err(got, ref) < 1e-12
+    # identical keys: exactly zero; any keys: 0 <= dev <= 2 per query head
+    assert np.array_equal(oracle.attention_deviation(q, qpos, k1, k1, np.arange(nk)),
+                          np.zeros(nq))
+    far = 50.0 * rng.standard_normal((nk, hkv, dh))
+    d = oracle.attention_deviation(q, qpos, k1, far, np.arange(nk))
+    assert np.all(d >= 0) and np.all(d <= 2 * hq + 1e-12)
+    # a query that sees one key has the same (one-hot) row under both
+    assert oracle.attention_deviation(q[:1], np.array([0]), k1, k0, np.arange(nk))[0] == 0.0
+
+
+def test_attention_deviation_blend(tiny_case, tiny_full):
+    """'ATTN' mode: at the check layer every chunk row is recomputed, so the
+    deviation is eq. 2 row by row between the full-prefill attention (its
+    queries and keys) and the attention over the re-rotated cache; the
+    first chunk (no preceding context) deviates by rounding only; later
+    layers narrow by KV deviation (the same as a KV-mode run forced onto the
+    same sets); r = 100% is the full prefill."""
+    case = tiny_case
+    nc, L = case.n_chunk_tokens, TINY.n_layers
+    sched = oracle.schedule(nc, 1500, "gradual", L)
+    res = oracle.blend(case.weights, TINY, case.x0, case.chunks, case.offsets, case.n_suffix,
+                       sched, dev_mode="ATTN")
+    # eq. 2 row-wise against the actual full prefill at layer 1
+    k, v, outs = tiny_full
+    q1, k1, _ = oracle.qkv_rows(case.weights[1], TINY, outs[0], np.arange(case.n_tokens))
+    fk0, _ = oracle.rerotate_chunks(TINY, case.chunks, case.offsets, case.n_tokens)
+    want = oracle.attention_deviation(q1[:nc], np.arange(nc), k1[:nc], fk0[1][:nc], np.arange(nc))
+    assert rel_err(res["dev"][1], want) < 1e-9
+    n0 = case.chunks[0][0].shape[1]
+    assert np.max(res["dev"][1][:n0]) < 1e-20 * np.max(res["dev"][1][n0:])
+    assert np.array_equal(res["sel"][1], np.sort(oracle.topk_select(res["dev"][1], sched[2])))
+    # layer 0 (all candidates) by attention deviation too: context-free keys, ~0
+    assert np.max(res["dev"][0]) < 1e-20
+    kv = oracle.blend(case.weights, TINY, case.x0, case.chunks, case.offsets, case.n_suffix,
+                      sched, dev_mode="KV", forced_sel=res["sel"])
+    for l in range(2, L):
+        assert np.array_equal(res["dev"][l], kv["dev"][l], equal_nan=True)
+    full = oracle.blend(case.weights, TINY, case.x0, case.chunks, case.offsets, case.n_suffix,
+                        [nc] * (L + 1), dev_mode="ATTN")
+    assert rel_err(full["fused_k"], k) < 1e-10 and rel_err(full["hidden"], outs[-1]) < 1e-10
