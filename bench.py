@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--r-bp", type=int, default=None)
     ap.add_argument("--schedule", default=None, choices=[None, "gradual", "fixed"])
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--dev-mode", default="kv", choices=["kv", "k", "v", "attn"],
+                    help="deviation measure of the selection (attn: attention deviation "
+                         "at the check layer, KV deviation after it)")
     ap.add_argument("--kv-format", default="plain", choices=["plain", "u8", "u4"],
                     help="storage of the chunk caches: model dtype, or per-channel 8/4-bit "
                          "codes made by cb_quantize_kv after the precompute")
@@ -998,9 +1001,13 @@ def main():
     sel = torch.empty((L, Nc), dtype=torch.int32, device=dev)
     hid = torch.empty((w.n_suffix + sched[-1], S.d_model), dtype=torch.float32, device=dev)
 
+    dev_mode = {"kv": npk.CB_DEV_KV, "k": npk.CB_DEV_K, "v": npk.CB_DEV_V,
+                "attn": npk.CB_DEV_ATTN}[args.dev_mode]
+
     def step(schedule=sched):
         npk.cb_blend(model, chunks, list(w.offsets), w.n_suffix, x0, fk, fv, sel_idx=sel,
-                     hidden_out=hid if schedule is sched else None, schedule=schedule)
+                     hidden_out=hid if schedule is sched else None, schedule=schedule,
+                     dev_mode=dev_mode)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
@@ -1025,6 +1032,7 @@ def main():
                       "chunks": f"{len(w.chunk_lens)}x{w.chunk_lens[0]}",
                       "suffix_tokens": w.n_suffix, "recompute_bp": w.r_bp,
                       "schedule": w.schedule_kind, "kept_rows_per_layer": sched,
+                      "deviation": args.dev_mode,
                       "chunk_kv_on_host": w.kv_on_host, "chunk_kv_format": args.kv_format}}
     if w.kv_on_host and args.kv_format == "plain":
         # row a1 streamed from pinned host memory: bytes per step against the

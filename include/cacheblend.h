@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 4
+#define CB_ABI_VERSION 5
 
 typedef enum cb_status {
     CB_OK = 0,
@@ -85,7 +85,22 @@ typedef enum cb_schedule_kind { CB_SCHED_GRADUAL = 0, CB_SCHED_FIXED = 1 } cb_sc
  * for baselines such as random scores, or for scores computed outside the
  * library (e.g. query-aware ones, which the CacheBlend explainer's outlook
  * names as follow-up work). */
-typedef enum cb_dev_mode { CB_DEV_KV = 0, CB_DEV_K = 1, CB_DEV_V = 2, CB_DEV_GIVEN = 3 } cb_dev_mode;
+/* ATTN (bf16 models): at every layer whose candidates are all the chunk rows
+ * (up to and including the check layer) rank by per-token attention
+ * deviation, as the explainer's first-layer rule does (section "HKVD（High KV
+ * Deviation）トークン選定", eq. 2 of "KVキャッシュの定義と偏差メトリクス"
+ * taken row by row): for chunk row j, the sum over query heads and keys of
+ * (p1 - p0)^2, p1 / p0 its causal softmax rows over the recomputed keys and
+ * over the re-rotated cached keys of the chunk positions.  There every chunk
+ * row is recomputed, so p1 is the full prefill's attention and p0 what full
+ * KV reuse would attend with.  Later layers rank by the KV deviation. */
+typedef enum cb_dev_mode {
+    CB_DEV_KV = 0,
+    CB_DEV_K = 1,
+    CB_DEV_V = 2,
+    CB_DEV_GIVEN = 3,
+    CB_DEV_ATTN = 4
+} cb_dev_mode;
 
 typedef struct cb_model_cfg {
     int32_t n_layers;
@@ -483,6 +498,17 @@ cb_status cb_dequant_rerotate(int32_t dtype, int32_t kv_format, const void* k_co
 cb_status cb_deviation(int32_t dtype, const void* k_new, const void* v_new,
                        const void* k_cached, const void* v_cached, int32_t n_rows,
                        int32_t row_elems, int32_t dev_mode, float* dev_out, void* stream);
+
+/* Per-token attention deviation (the CB_DEV_ATTN measure) of n rows at
+ * positions 0..n-1, bf16 only: q [n][Hq][dh] (RoPE applied), k_new and
+ * k_cached [n][Hkv][dh]; dev_out[j] = sum over query heads h and keys
+ * k <= j of (p1 - p0)^2, p1 / p0 the softmax rows of q_j . k / sqrt(dh)
+ * over k_new and over k_cached (query head h reads KV head h / (Hq/Hkv)).
+ * Allocates a workspace of Hq * n floats in stream order. */
+cb_status cb_attention_deviation(int32_t dtype, const void* q, const void* k_new,
+                                 const void* k_cached, int32_t n, int32_t n_q_heads,
+                                 int32_t n_kv_heads, int32_t head_dim, float* dev_out,
+                                 void* stream);
 
 /* HKVD selection: the k indices of the largest dev values under the total
  * order (NaN first, larger first, -0.0 == +0.0, then smaller index first),

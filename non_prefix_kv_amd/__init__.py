@@ -17,12 +17,12 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ------------------------------------------------------------------ constants
-CB_ABI_VERSION = 4
+CB_ABI_VERSION = 5
 CB_OK, CB_E_INVALID, CB_E_SHAPE, CB_E_NOT_PINNED, CB_E_SCHEDULE = 0, -1, -2, -3, -4
 CB_E_OOM, CB_E_HIP, CB_E_BAD_STATE, CB_E_UNSUPPORTED = -5, -6, -7, -8
 CB_F32, CB_BF16 = 0, 1
 CB_SCHED_GRADUAL, CB_SCHED_FIXED = 0, 1
-CB_DEV_KV, CB_DEV_K, CB_DEV_V, CB_DEV_GIVEN = 0, 1, 2, 3
+CB_DEV_KV, CB_DEV_K, CB_DEV_V, CB_DEV_GIVEN, CB_DEV_ATTN = 0, 1, 2, 3, 4
 CB_KV_PLAIN, CB_KV_U8, CB_KV_U4 = 0, 1, 2
 
 _c_i32, _c_i64, _c_p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
@@ -139,6 +139,8 @@ _fn = {
                             _c_i32, _c_i32, _c_i32, ctypes.c_double, _c_p),
     "cb_deviation": (ctypes.c_int, _c_i32, _c_p, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32, _c_p,
                      _c_p),
+    "cb_attention_deviation": (ctypes.c_int, _c_i32, _c_p, _c_p, _c_p, _c_i32, _c_i32, _c_i32,
+                               _c_i32, _c_p, _c_p),
     "cb_topk_select": (ctypes.c_int, _c_p, _c_i32, _c_i32, _c_p, _c_p),
     "cb_gather_rows": (ctypes.c_int, _c_p, _c_p, _c_p, _c_i32, _c_i64, _c_p),
     "cb_scatter_rows": (ctypes.c_int, _c_p, _c_p, _c_p, _c_i32, _c_i64, _c_p),
@@ -644,6 +646,16 @@ def cb_deviation(k_new, v_new, k_cached, v_cached, n_rows, row_elems, dev_mode, 
     _check(RAW["cb_deviation"](_dtype_code(k_new), _ptr(k_new), _ptr(v_new), _ptr(k_cached),
                                _ptr(v_cached), n_rows, row_elems, dev_mode, _ptr(dev_out),
                                _stream(stream)))
+
+
+def cb_attention_deviation(q, k_new, k_cached, n, n_q_heads, n_kv_heads, head_dim, dev_out,
+                           stream=None):
+    """Per-token attention deviation of n rows at positions 0..n-1 (bf16)."""
+    import torch
+    _need(dev_out, "dev_out", torch.float32, n)
+    _check(RAW["cb_attention_deviation"](_dtype_code(q), _ptr(q), _ptr(k_new), _ptr(k_cached), n,
+                                         n_q_heads, n_kv_heads, head_dim, _ptr(dev_out),
+                                         _stream(stream)))
 
 
 def cb_topk_select(dev, n, k, idx_out, stream=None):

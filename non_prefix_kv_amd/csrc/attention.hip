@@ -724,6 +724,199 @@ hipError_t launch_t(const AttnArgs& a, const AttnTiles& tl, hipStream_t s) {
 
 int tile_height(int dtype) { return dtype == BF16 ? QT32 : QT; }
 
+// Per-token attention deviation (CacheBlend explainer (0h-n0), eq. 2 taken
+// row by row, the first-layer rule of HKVD selection): for query row j of a
+// request whose every chunk row is recomputed, and query head h,
+//   dev_h[j] = sum_k (p1[k] - p0[k])^2,
+// p1 / p0 the causal softmax rows of q_j over the recomputed keys and over
+// the cached keys of the chunk positions 0..j.  One pass over the keys with
+// the running maxima m1, m0 and sums l1 = sum e1, l0 = sum e0, A = sum e1^2,
+// B = sum e1 e0, C = sum e0^2 (e = 2^(score - m), rescaled as m grows):
+//   dev_h = A / l1^2 - 2 B / (l1 l0) + C / l0^2,
+// which is sum (e1/l1 - e0/l0)^2 expanded.  Same tiles, LDS layout and
+// score MFMAs as attention64_kernel, with the block of recomputed keys in
+// place of V.  part[h][row] receives dev_h of every query row.
+template <int D>
+__global__ __launch_bounds__(kT32, 2) void attn_dev_kernel(AttnDevArgs a, const AttnDevTiles tl) {
+    constexpr int RB = D * 2, CPR = RB / 16, RPI = 64 / CPR, CPW = KBL / 4 / RPI;
+    constexpr int NDS = D / 16, BLK = KBL * RB;
+    static_assert(CPW >= 1 && CPW * RPI * 4 == KBL, "copy split");
+    __shared__ __attribute__((aligned(16))) unsigned char smem[2 * 2 * BLK];   // [stage][new|cached]
+    __shared__ int sred[kT32 / 64];
+
+    const int logical = xcd_order(blockIdx.x, tl.n * a.n_q_heads);
+    const int qt = logical % tl.n, h = logical / tl.n;
+    const AttnDevTile& tile = tl.t[qt];
+    const int hk = h / (a.n_q_heads / a.n_kv_heads);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int fr = lane & 31, g = lane >> 5;
+    const int q_ld = a.n_q_heads * D, kv_ld = a.n_kv_heads * D;
+
+    // query j (= its position, 0-based within the request's chunk rows)
+    const int ql = wave * 32 + fr;
+    const bool q_ok = ql < tile.nq;
+    const int qpos = tile.j0 + (q_ok ? ql : tile.nq - 1);
+    int wmax = qpos, wmin = qpos;
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) {
+        wmax = max(wmax, __shfl_xor(wmax, o, 64));
+        wmin = min(wmin, __shfl_xor(wmin, o, 64));
+    }
+    if (lane == 0) sred[wave] = wmax;
+    __syncthreads();
+    int bmax = sred[0];
+#pragma unroll
+    for (int w = 1; w < kT32 / 64; ++w) bmax = max(bmax, sred[w]);
+    const int nk = bmax + 1;                          // keys 0..bmax
+    const int n_kb = (nk + KBL - 1) / KBL;
+
+    const bf16* qp = static_cast<const bf16*>(a.q) + (int64_t)(tile.q_row0 + qpos) * q_ld + h * D;
+    bf16x8 qf[NDS];
+#pragma unroll
+    for (int s = 0; s < NDS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qp + s * 16 + g * 8);
+
+    const bf16* k1base = static_cast<const bf16*>(a.k_new) + (int64_t)tile.k_new_row0 * kv_ld + hk * D;
+    const bf16* k0base = static_cast<const bf16*>(a.k_cached) + (int64_t)tile.k_cached_row0 * kv_ld + hk * D;
+    int k_voff[CPW];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+        const int r = 16 * wave + RPI * c + lane / CPR, slot = lane % CPR;
+        k_voff[c] = r * kv_ld * 2 + ((slot ^ k_key<D>(r)) & (CPR - 1)) * 16;
+    }
+    const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(smem);
+    auto issue = [&](int kb, int st) {
+        const int k0 = kb * KBL;
+        const int rows = min(KBL, tile.n_keys - k0);   // rows past the last key read as zero
+        const i32x4 r1 = attn_rsrc(k1base + (int64_t)k0 * kv_ld, rows * kv_ld * 2);
+        const i32x4 r0 = attn_rsrc(k0base + (int64_t)k0 * kv_ld, rows * kv_ld * 2);
+        const uint32_t d = lds0 + st * 2 * BLK + 16 * wave * RB;
+#pragma unroll
+        for (int c = 0; c < CPW; ++c) {
+            attn_dma16(r1, k_voff[c], d + c * RPI * RB);
+            attn_dma16(r0, k_voff[c], d + BLK + c * RPI * RB);
+        }
+    };
+    const int kkey = k_key<D>(fr);
+    const float sl2 = 1.4426950408889634f / sqrtf((float)D);
+    float m1 = -INFINITY, m0 = -INFINITY, l1 = 0.f, l0 = 0.f, A = 0.f, B = 0.f, C = 0.f;
+    auto scores = [&](const unsigned char* sk, floatx16 (&s2)[2]) {
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) s2[hh][i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < NDS; ++s) {
+            const int off = fr * RB + (((2 * s + g) ^ kkey) & (CPR - 1)) * 16;
+            mfma32(s2[0], *reinterpret_cast<const bf16x8*>(sk + off), qf[s]);
+            mfma32(s2[1], *reinterpret_cast<const bf16x8*>(sk + off + 32 * RB), qf[s]);
+        }
+    };
+    auto compute = [&](int st, int kb) {
+        const int k0 = kb * KBL;
+        if (k0 > wmax) return;                          // wave-uniform: nothing visible
+        floatx16 s1[2], s0[2];
+        scores(smem + st * 2 * BLK, s1);
+        scores(smem + st * 2 * BLK + BLK, s0);
+        if (k0 + KBL - 1 > wmin) {
+            // key k0 + 4 g + c is visible iff c <= lim (query j sees keys 0..j)
+            const int lim = qpos - k0 - 4 * g;
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (32 * hh + 8 * (i >> 2) + (i & 3) > lim) {
+                        s1[hh][i] = -INFINITY;
+                        s0[hh][i] = -INFINITY;
+                    }
+        }
+        // Scores in log2 units first, so that the largest key's term is
+        // exactly 2^0, and both key sets through the same rounded operations
+        // (no contraction into FMAs, which the compiler could apply to one
+        // set and not the other): identical key sets give identical terms.
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                s1[hh][i] = __fmul_rn(s1[hh][i], sl2);
+                s0[hh][i] = __fmul_rn(s0[hh][i], sl2);
+            }
+        float b1 = vmax3(s1[0][0], s1[1][0], s1[0][1]), b0 = vmax3(s0[0][0], s0[1][0], s0[0][1]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i) {
+            b1 = i == 1 ? vmax3(b1, s1[1][1], s1[1][1]) : vmax3(b1, s1[0][i], s1[1][i]);
+            b0 = i == 1 ? vmax3(b0, s0[1][1], s0[1][1]) : vmax3(b0, s0[0][i], s0[1][i]);
+        }
+        b1 = fmaxf(b1, __shfl_xor(b1, 32, 64));
+        b0 = fmaxf(b0, __shfl_xor(b0, 32, 64));
+        // the query's own key is in the first block that reaches it, so
+        // the maxima are finite from the first visible block on
+        const float n1 = fmaxf(m1, b1), n0 = fmaxf(m0, b0);
+        const float f1 = m1 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m1 - n1);
+        const float f0 = m0 == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m0 - n0);
+        l1 = __fmul_rn(l1, f1);
+        l0 = __fmul_rn(l0, f0);
+        A = __fmul_rn(A, __fmul_rn(f1, f1));
+        B = __fmul_rn(B, __fmul_rn(f1, f0));
+        C = __fmul_rn(C, __fmul_rn(f0, f0));
+        m1 = n1; m0 = n0;
+        const float u1 = n1 == -INFINITY ? 0.f : n1, u0 = n0 == -INFINITY ? 0.f : n0;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float e1 = __builtin_amdgcn_exp2f(__fsub_rn(s1[hh][i], u1));
+                const float e0 = __builtin_amdgcn_exp2f(__fsub_rn(s0[hh][i], u0));
+                l1 += e1;
+                l0 += e0;
+                A = fmaf(e1, e1, A);
+                B = fmaf(e1, e0, B);
+                C = fmaf(e0, e0, C);
+            }
+    };
+    if (n_kb > 0) {
+        issue(0, 0);
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
+        __syncthreads();
+    }
+    for (int kb = 0; kb < n_kb; ++kb) {
+        const int st = kb & 1;
+        if (kb + 1 < n_kb) issue(kb + 1, st ^ 1);
+        compute(st, kb);
+        __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
+        __syncthreads();
+    }
+    // lanes l and l ^ 32 hold the same query's two halves of every block
+    // (same maxima): add their sums
+    l1 += __shfl_xor(l1, 32, 64);
+    l0 += __shfl_xor(l0, 32, 64);
+    A += __shfl_xor(A, 32, 64);
+    B += __shfl_xor(B, 32, 64);
+    C += __shfl_xor(C, 32, 64);
+    if (!q_ok || g) return;
+    // (A/l1^2 - B/(l1 l0)) + (C/l0^2 - B/(l1 l0)), each product rounded on its
+    // own (no contraction): identical key sets give exactly zero
+    const float i1 = 1.f / l1, i0 = 1.f / l0;
+    const float ta = __fmul_rn(__fmul_rn(A, i1), i1);
+    const float tb = __fmul_rn(__fmul_rn(B, i1), i0);
+    const float tc = __fmul_rn(__fmul_rn(C, i0), i0);
+    const float dev = fmaxf(0.f, __fadd_rn(__fsub_rn(ta, tb), __fsub_rn(tc, tb)));
+    a.part[(int64_t)h * a.part_stride + tile.q_row0 + qpos] = dev;
+}
+
+// out[c_off + j] = sum over heads (in head order) of part[h][row0 + j].
+__global__ __launch_bounds__(256) void attn_dev_sum_kernel(const float* __restrict__ part,
+                                                           int64_t part_stride, int n_heads,
+                                                           const AttnDevSums t,
+                                                           float* __restrict__ out) {
+    const AttnDevSum& r = t.r[blockIdx.y];
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= r.n) return;
+    float s = 0.f;
+    for (int h = 0; h < n_heads; ++h) s += part[(int64_t)h * part_stride + r.row0 + j];
+    out[r.out0 + j] = s;
+}
+
 }  // namespace
 
 size_t attention_workspace(int dtype, const AttnRange* r, int n_r, int n_q_heads, int head_dim) {
@@ -755,6 +948,56 @@ hipError_t launch_attention(int dtype, const AttnArgs& a, const AttnRange* r, in
                                   : launch32<64>(a, tl, ws, ws_bytes, s);
         else
             e = a.head_dim == 128 ? launch_t<float, 128>(a, tl, s) : launch_t<float, 64>(a, tl, s);
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+
+size_t attention_deviation_workspace(int n_q_heads, int64_t rows) {
+    return (size_t)n_q_heads * (size_t)std::max<int64_t>(rows, 1) * sizeof(float);
+}
+
+hipError_t launch_attention_deviation(int dtype, const AttnDevArgs& a0, const AttnDevReq* r,
+                                      int n_r, float* out, hipStream_t s) {
+    if (n_r <= 0) return hipSuccess;
+    if (dtype != BF16 || (a0.head_dim != 64 && a0.head_dim != 128) || a0.n_kv_heads <= 0 ||
+        a0.n_q_heads % a0.n_kv_heads != 0 || !a0.part || a0.part_stride <= 0)
+        return hipErrorInvalidValue;
+    std::vector<AttnDevTile> tiles;
+    for (int i = 0; i < n_r; ++i) {
+        if (r[i].n < 0 || (int64_t)r[i].q_row0 + r[i].n > a0.part_stride) return hipErrorInvalidValue;
+        for (int j = 0; j < r[i].n; j += QT32)
+            tiles.push_back(AttnDevTile{r[i].q_row0, j, std::min(QT32, r[i].n - j),
+                                        r[i].k_new_row0, r[i].k_cached_row0, r[i].n});
+    }
+    // longest first (later tiles see more keys)
+    std::stable_sort(tiles.begin(), tiles.end(), [](const AttnDevTile& x, const AttnDevTile& y) {
+        return x.j0 + x.nq > y.j0 + y.nq;
+    });
+    for (size_t i = 0; i < tiles.size(); i += kMaxAttnTiles) {
+        AttnDevTiles tl;
+        tl.n = (int)std::min<size_t>(kMaxAttnTiles, tiles.size() - i);
+        for (int j = 0; j < tl.n; ++j) tl.t[j] = tiles[i + j];
+        const dim3 grid((unsigned)(tl.n * a0.n_q_heads));
+        if (a0.head_dim == 128)
+            hipLaunchKernelGGL((attn_dev_kernel<128>), grid, dim3(kT32), 0, s, a0, tl);
+        else
+            hipLaunchKernelGGL((attn_dev_kernel<64>), grid, dim3(kT32), 0, s, a0, tl);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    for (int i = 0; i < n_r; i += kMaxReq) {
+        AttnDevSums t{};
+        t.n = std::min(kMaxReq, n_r - i);
+        int max_n = 0;
+        for (int j = 0; j < t.n; ++j) {
+            t.r[j] = AttnDevSum{r[i + j].q_row0, r[i + j].out0, r[i + j].n};
+            max_n = std::max(max_n, r[i + j].n);
+        }
+        if (max_n == 0) continue;
+        hipLaunchKernelGGL(attn_dev_sum_kernel, dim3((max_n + 255) / 256, t.n), dim3(256), 0, s,
+                           a0.part, a0.part_stride, a0.n_q_heads, t, out);
+        const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     return hipSuccess;

@@ -286,6 +286,42 @@ struct AttnArgs {
     int* part_nk;       // [tiles] keys visible to each tile (written by its attention pass)
 };
 
+// Per-token attention deviation of requests whose every chunk row is
+// recomputed (bf16).  Request i: its n chunk rows are query rows q_row0 ..
+// (row j at position j, RoPE'd queries in q [*][Hq*dh]), their recomputed
+// keys rows k_new_row0 .. of k_new and their cached (re-rotated) keys rows
+// k_cached_row0 .. of k_cached ([*][Hkv*dh]); out[out0 + j] = sum over query
+// heads and keys 0..j of the squared difference of the two softmax rows.
+// part: workspace [Hq][part_stride] floats (query rows < part_stride).
+struct AttnDevArgs {
+    const void* q;
+    const void* k_new;
+    const void* k_cached;
+    int n_q_heads, n_kv_heads, head_dim;
+    float* part;
+    int64_t part_stride;
+};
+struct AttnDevReq {
+    int q_row0, n, k_new_row0, k_cached_row0, out0;
+};
+struct AttnDevTile {
+    int q_row0, j0, nq, k_new_row0, k_cached_row0, n_keys;
+};
+struct AttnDevTiles {
+    AttnDevTile t[kMaxAttnTiles];
+    int n;
+};
+struct AttnDevSum {
+    int row0, out0, n;
+};
+struct AttnDevSums {
+    AttnDevSum r[kMaxReq];
+    int n;
+};
+size_t attention_deviation_workspace(int n_q_heads, int64_t rows);
+hipError_t launch_attention_deviation(int dtype, const AttnDevArgs& a, const AttnDevReq* r,
+                                      int n_r, float* out, hipStream_t s);
+
 // Workspace bytes the split partials of these ranges need (0: no split).
 size_t attention_workspace(int dtype, const AttnRange* r, int n_r, int n_q_heads, int head_dim);
 

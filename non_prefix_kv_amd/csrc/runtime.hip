@@ -237,6 +237,8 @@ struct cb_plan {
     // first = row second (the last layer that wrote its row), filled after
     // the last layer
     std::vector<std::pair<int, int>> sel_rows_pending;
+    float* attn_dev_part = nullptr;   // CB_DEV_ATTN: per-head deviations [Hq][max rows]
+    int64_t attn_dev_stride = 0;
     void* attn_ws = nullptr;      // split-attention partials
     size_t attn_ws_bytes = 0;
     // fetch: host chunks copied once per layer into their first place of use,
@@ -428,6 +430,10 @@ size_t carve(cb_plan* p, char* base, int max_rows) {
     p->row_a = (int*)take(R * 4);
     p->row_b = (int*)take(R * 4);
     p->sel_local = (int*)take(R * 4);
+    if (p->dev_mode == CB_DEV_ATTN) {
+        p->attn_dev_stride = (int64_t)R;
+        p->attn_dev_part = (float*)take(attention_deviation_workspace(c.n_q_heads, (int64_t)R));
+    }
     p->attn_ws = p->attn_ws_bytes ? take(p->attn_ws_bytes) : nullptr;
     p->stage = p->stage_bytes ? take(p->stage_bytes) : nullptr;
     return off;
@@ -690,6 +696,39 @@ cb_status do_layer(cb_plan* p, int l) {
                 Span sp(m, CB_K_DEVIATION, st, 0, lr.nC * 12.0);
                 for (const ReqTab& t : tabs)
                     CB_HIP(launch_given_scores(p->given, t, pos_r, p->dev, st));
+            } else if (measure && p->dev_mode == CB_DEV_ATTN) {
+                // attention deviation for the requests whose every chunk row
+                // is a candidate (their chunk rows are R rows r_off.. at
+                // positions 0.., cached rows G..), K and V deviation for the rest
+                std::vector<AttnDevReq> ad;
+                std::vector<ReqRows> kvr;
+                for (size_t b = 0; b < p->reqs.size(); ++b) {
+                    const ReqRows& x = lr.r[b];
+                    if (x.n_c == 0) continue;
+                    if (x.n_c == p->reqs[b].Nc)
+                        ad.push_back(AttnDevReq{x.r_off, x.n_c, x.r_off, p->reqs[b].G, x.c_off});
+                    else
+                        kvr.push_back(x);
+                }
+                if (!ad.empty()) {
+                    double fl = 0;
+                    for (const AttnDevReq& x : ad) fl += 4.0 * c.n_q_heads * c.head_dim * 0.5 * x.n * (x.n + 1.0);
+                    Span sp(m, CB_K_DEVIATION, st, fl, 0);
+                    AttnDevArgs a{};
+                    a.q = p->Q; a.k_new = p->Kn; a.k_cached = fk;
+                    a.n_q_heads = c.n_q_heads; a.n_kv_heads = c.n_kv_heads; a.head_dim = c.head_dim;
+                    a.part = p->attn_dev_part; a.part_stride = p->attn_dev_stride;
+                    const hipError_t e = launch_attention_deviation(dt, a, ad.data(), (int)ad.size(),
+                                                                    p->dev, st);
+                    if (e != hipSuccess)
+                        return fail(CB_E_HIP, "attention deviation launch: %s", hipGetErrorString(e));
+                }
+                if (!kvr.empty()) {
+                    Span sp(m, CB_K_DEVIATION, st, 0, 4.0 * kvd * es * lr.nC);
+                    for (const ReqTab& t : req_tabs(kvr))
+                        CB_HIP(launch_deviation(dt, p->Kn, p->Vn, fk, fv, row_r, t, m->kvd(),
+                                                CB_DEV_KV, p->dev, st));
+                }
             } else if (measure) {
                 const double parts = p->dev_mode == CB_DEV_KV ? 4 : 2;
                 Span sp(m, CB_K_DEVIATION, st, 0, lr.nC * (parts * kvd * es + 8.0));
@@ -967,7 +1006,10 @@ cb_status validate_request(cb_model* m, const cb_request* r, const cb_outputs* o
     if (r->n_chunks < 0 || r->n_suffix < 0) return fail(CB_E_INVALID, "negative counts");
     if (r->n_chunks > 0 && (!r->chunks || !r->chunk_offsets))
         return fail(CB_E_INVALID, "chunks/chunk_offsets are NULL");
-    if (r->dev_mode < 0 || r->dev_mode > 3) return fail(CB_E_INVALID, "dev_mode %d", r->dev_mode);
+    if (r->dev_mode < 0 || r->dev_mode > CB_DEV_ATTN)
+        return fail(CB_E_INVALID, "dev_mode %d", r->dev_mode);
+    if (r->dev_mode == CB_DEV_ATTN && m->cfg.dtype != CB_BF16)
+        return fail(CB_E_UNSUPPORTED, "dev_mode CB_DEV_ATTN needs a bf16 model");
     if ((r->dev_mode == CB_DEV_GIVEN) != (r->given_scores != nullptr))
         return fail(CB_E_INVALID, "given_scores goes with dev_mode CB_DEV_GIVEN, and only with it");
     if (r->given_scores && mem_kind(r->given_scores) != MemKind::Device)
@@ -1015,7 +1057,10 @@ cb_status validate_batch(cb_model* m, const cb_batch_request* r, const cb_batch_
     if (!r->x0) return fail(CB_E_INVALID, "x0 is NULL");
     if (r->n_requests <= 0 || !r->items) return fail(CB_E_INVALID, "no requests");
     if (r->n_pool < 0 || (r->n_pool > 0 && !r->pool)) return fail(CB_E_INVALID, "pool is NULL");
-    if (r->dev_mode < 0 || r->dev_mode > 3) return fail(CB_E_INVALID, "dev_mode %d", r->dev_mode);
+    if (r->dev_mode < 0 || r->dev_mode > CB_DEV_ATTN)
+        return fail(CB_E_INVALID, "dev_mode %d", r->dev_mode);
+    if (r->dev_mode == CB_DEV_ATTN && m->cfg.dtype != CB_BF16)
+        return fail(CB_E_UNSUPPORTED, "dev_mode CB_DEV_ATTN needs a bf16 model");
     if ((r->dev_mode == CB_DEV_GIVEN) != (r->given_scores != nullptr))
         return fail(CB_E_INVALID, "given_scores goes with dev_mode CB_DEV_GIVEN, and only with it");
     if (r->given_scores && mem_kind(r->given_scores) != MemKind::Device)
@@ -1573,6 +1618,34 @@ cb_status cb_deviation(int32_t dtype, const void* k_new, const void* v_new, cons
     t.r[0].n_c = n_rows;
     CB_HIP(launch_deviation(dtype, k_new, v_new, k_cached, v_cached, nullptr, t, row_elems,
                             dev_mode, dev_out, as_stream(stream)));
+    return CB_OK;
+}
+
+cb_status cb_attention_deviation(int32_t dtype, const void* q, const void* k_new,
+                                 const void* k_cached, int32_t n, int32_t n_q_heads,
+                                 int32_t n_kv_heads, int32_t head_dim, float* dev_out,
+                                 void* stream) {
+    if (dtype != CB_BF16) return fail(CB_E_UNSUPPORTED, "attention deviation needs bf16 (dtype %d)", dtype);
+    if (n < 0 || n_q_heads <= 0 || n_kv_heads <= 0 || n_q_heads % n_kv_heads)
+        return fail(CB_E_SHAPE, "bad sizes");
+    if (head_dim != 64 && head_dim != 128) return fail(CB_E_UNSUPPORTED, "head_dim %d", head_dim);
+    if (n == 0) return CB_OK;
+    if (!q || !k_new || !k_cached || !dev_out) return fail(CB_E_INVALID, "NULL buffer");
+    const hipStream_t st = as_stream(stream);
+    const size_t need = attention_deviation_workspace(n_q_heads, n);
+    void* ws = nullptr;
+    if (hipMallocAsync(&ws, need, st) != hipSuccess) {
+        (void)hipGetLastError();
+        return fail(CB_E_OOM, "attention deviation workspace of %zu bytes", need);
+    }
+    AttnDevArgs a{};
+    a.q = q; a.k_new = k_new; a.k_cached = k_cached;
+    a.n_q_heads = n_q_heads; a.n_kv_heads = n_kv_heads; a.head_dim = head_dim;
+    a.part = static_cast<float*>(ws); a.part_stride = n;
+    const AttnDevReq r{0, n, 0, 0, 0};
+    const hipError_t e = launch_attention_deviation(dtype, a, &r, 1, dev_out, st);
+    (void)hipFreeAsync(ws, st);
+    if (e != hipSuccess) return fail(CB_E_HIP, "attention deviation launch: %s", hipGetErrorString(e));
     return CB_OK;
 }
 

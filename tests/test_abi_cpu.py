@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(npk):
 
 
 def test_abi_version(npk):
-    assert npk.cb_abi_version() == npk.CB_ABI_VERSION == 4
+    assert npk.cb_abi_version() == npk.CB_ABI_VERSION == 5
 
 
 @pytest.mark.parametrize("n", [0, 1, 10, 384, 3840, 7680, 8192])
