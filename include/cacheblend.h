@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define CB_ABI_VERSION 5
+#define CB_ABI_VERSION 6
 
 typedef enum cb_status {
     CB_OK = 0,
@@ -218,18 +218,39 @@ cb_status cb_schedule(int32_t n_chunk_tokens, int32_t recompute_bp, int32_t kind
 
 /* ------------------------------------------------------------- model */
 /* Validates cfg and copies the weight pointer table (not the weights: the
- * caller keeps them alive until cb_model_destroy).  Builds the RoPE table on
- * the current device.  *out receives the handle. */
+ * caller keeps them alive until cb_model_destroy).  final_norm: device [d]
+ * in the model dtype, the gain of the RMSNorm before the LM head (used by
+ * cb_lm_head when it is given no final_norm), or NULL.  Builds the RoPE
+ * table on the current device.  *out receives the handle. */
 cb_status cb_model_create(const cb_model_cfg* cfg, const cb_layer_weights* layers,
-                          cb_model** out);
+                          const void* final_norm, cb_model** out);
 void cb_model_destroy(cb_model* model);
+
+/* Workspace of the model's fusion plans (cb_blend, cb_blend_batch, the
+ * layer-stepped plans, cb_prefill).  By default each plan allocates it in
+ * the order of its stream from a memory pool of the model.
+ *  ws != NULL: plans carve it from the caller's device buffer [ws, ws +
+ *    bytes) (256-byte aligned) and allocate nothing; the caller keeps it
+ *    alive and unused by anything else until the plans' work is done, and
+ *    plans of the model that run at the same time (other streams) race on it.
+ *  ws == NULL, bytes > 0: pool allocations, at most bytes per plan.
+ *  ws == NULL, bytes == 0: pool allocations without a limit.
+ * A plan whose workspace does not fit fails with CB_E_OOM before anything is
+ * queued.  cb_workspace_size gives the bytes a request needs (validating it
+ * as cb_plan_create does, allocating nothing). */
+cb_status cb_model_set_workspace(cb_model* model, void* ws, int64_t bytes);
+cb_status cb_workspace_size(cb_model* model, const cb_request* req, int64_t* bytes);
 
 /* ------------------------------------------------------------- fusion */
 /* One-shot fusion of a request: per layer, rotate the chunk caches to their
  * real positions, recompute the scheduled rows, measure deviation, keep the
  * top rows, merge them into the fused cache, attend over the whole fused
  * cache, finish the block.  Equivalent to cb_plan_create, then cb_fetch_kv
- * and cb_prefill_layer for every layer, then cb_plan_destroy. */
+ * and cb_prefill_layer for every layer, then cb_plan_destroy.
+ * (CacheBlend explainer (0h-n0), "選択的再計算" Steps 1-4 with the K/V merge
+ * equations, and "HKVD（High KV Deviation）トークン選定" for the kept rows;
+ * CacheBlend explainer (abeam.tech), "高いずれを持つトークンだけを再計算する":
+ * Q/K/V of the selected tokens only, which attend over the whole input.) */
 cb_status cb_blend(cb_model* model, const cb_request* req, const cb_outputs* out,
                    void* stream);
 
@@ -250,7 +271,10 @@ cb_status cb_prefill_layer(cb_plan* plan, int32_t layer);
 cb_status cb_synchronize(cb_plan* plan);
 void cb_plan_destroy(cb_plan* plan);
 
-/* Full prefill of n_tokens rows x0 (device [n][d], model dtype) at
+/* Full prefill (the reference the CacheBlend explainer (0h-n0) compares
+ * against, section "KVキャッシュの定義と偏差メトリクス": KV^full; and the
+ * per-chunk precompute of the abeam explainer's "チャンク単位でKVを保存する")
+ * of n_tokens rows x0 (device [n][d], model dtype) at
  * positions pos0..pos0+n-1.  k_out/v_out: device [L][n][H_kv][d_head] model
  * dtype; hidden_out: device [n][d] float32 or NULL.  With pos0 = 0 this
  * precomputes a chunk cache at chunk-local positions. */
@@ -264,8 +288,9 @@ cb_status cb_prefill(cb_model* model, const void* x0, int32_t n_tokens, int32_t 
  *
  * cb_lm_head: for each of `rows` rows of x (device float32 [rows][d], e.g.
  * the last row of hidden_out), logits[r] = W_lm rmsnorm(x[r]; final_norm)
- * (device float32 [rows][vocab]); final_norm [d] and w_lm [vocab][d] are
- * device pointers in the model dtype.  argmax (device int32 [rows] or
+ * (device float32 [rows][vocab]); final_norm [d] (NULL: the model's, from
+ * cb_model_create) and w_lm [vocab][d] are device pointers in the model
+ * dtype.  argmax (device int32 [rows] or
  * NULL): index of the largest logit, NaN above all, smallest index among
  * equals.
  *
@@ -510,13 +535,18 @@ cb_status cb_attention_deviation(int32_t dtype, const void* q, const void* k_new
                                  int32_t n_kv_heads, int32_t head_dim, float* dev_out,
                                  void* stream);
 
-/* HKVD selection: the k indices of the largest dev values under the total
+/* HKVD selection (CacheBlend explainer (0h-n0), "HKVD（High KV Deviation）
+ * トークン選定", selection code: the top k by deviation, re-sorted by
+ * position): the k indices of the largest dev values under the total
  * order (NaN first, larger first, -0.0 == +0.0, then smaller index first),
  * written ascending to idx_out[0..k).  0 <= k <= n. */
 cb_status cb_topk_select(const float* dev, int32_t n, int32_t k, int32_t* idx_out,
                          void* stream);
 
-/* dst row i = src row idx[i] (gather) / dst row idx[i] = src row i (scatter);
+/* Step 1 (input masking: gather the selected rows) and Step 3 (K/V merge:
+ * the recomputed rows of the selected tokens into the cached KV) of the
+ * CacheBlend explainer (0h-n0), "選択的再計算":
+ * dst row i = src row idx[i] (gather) / dst row idx[i] = src row i (scatter);
  * rows of row_bytes bytes (a multiple of 4); idx device int32[n_rows]. */
 cb_status cb_gather_rows(const void* src, void* dst, const int32_t* idx, int32_t n_rows,
                          int64_t row_bytes, void* stream);
@@ -533,7 +563,10 @@ cb_status cb_rmsnorm(int32_t x_dtype, const void* x, int32_t y_dtype, const void
 cb_status cb_gemm(int32_t dtype, const void* a, const void* b, float* c, int32_t m,
                   int32_t n, int32_t k, void* stream);
 
-/* Causal attention by real position: n_q query rows q [n_q][Hq][dh] at
+/* Step 4 of the CacheBlend explainer (0h-n0), "選択的再計算" (ordinary
+ * attention; the selected tokens attend over the whole input, abeam
+ * explainer, "高いずれを持つトークンだけを再計算する").
+ * Causal attention by real position: n_q query rows q [n_q][Hq][dh] at
  * positions q_pos (device int32, ascending) over keys k, v [n_kv][Hkv][dh] at
  * positions 0..n_kv-1; key j visible to query i iff j <= q_pos[i]; query
  * head h reads KV head h / (Hq/Hkv); out [n_q][Hq][dh] in dtype. */

@@ -17,7 +17,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # ------------------------------------------------------------------ constants
-CB_ABI_VERSION = 5
+CB_ABI_VERSION = 6
 CB_OK, CB_E_INVALID, CB_E_SHAPE, CB_E_NOT_PINNED, CB_E_SCHEDULE = 0, -1, -2, -3, -4
 CB_E_OOM, CB_E_HIP, CB_E_BAD_STATE, CB_E_UNSUPPORTED = -5, -6, -7, -8
 CB_F32, CB_BF16 = 0, 1
@@ -106,7 +106,9 @@ _fn = {
     "cb_abi_version": (ctypes.c_int,),
     "cb_last_error": (ctypes.c_char_p,),
     "cb_schedule": (ctypes.c_int, _c_i32, _c_i32, _c_i32, _c_i32, _P(_c_i32)),
-    "cb_model_create": (ctypes.c_int, _P(cb_model_cfg), _P(cb_layer_weights), _P(_c_p)),
+    "cb_model_create": (ctypes.c_int, _P(cb_model_cfg), _P(cb_layer_weights), _c_p, _P(_c_p)),
+    "cb_model_set_workspace": (ctypes.c_int, _c_p, _c_p, _c_i64),
+    "cb_workspace_size": (ctypes.c_int, _c_p, _P(cb_request), _P(_c_i64)),
     "cb_model_destroy": (None, _c_p),
     "cb_blend": (ctypes.c_int, _c_p, _P(cb_request), _P(cb_outputs), _c_p),
     "cb_plan_create": (ctypes.c_int, _c_p, _P(cb_request), _P(cb_outputs), _c_p, _P(_c_p)),
@@ -251,7 +253,7 @@ class Model:
     """
 
     def __init__(self, n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim,
-                 layers, rope_base=10000.0, rms_eps=1e-5, dtype=None):
+                 layers, rope_base=10000.0, rms_eps=1e-5, dtype=None, final_norm=None):
         if dtype is None:
             dtype = _dtype_code(layers[0]["wq"])
         self.cfg = cb_model_cfg(n_layers, d_model, n_q_heads, n_kv_heads, head_dim, ffn_dim,
@@ -265,8 +267,35 @@ class Model:
                     raise ValueError(f"layer {i} {f} is not contiguous")
                 setattr(arr[i], f, t.data_ptr())
         h = _c_p()
-        _check(RAW["cb_model_create"](ctypes.byref(self.cfg), arr, ctypes.byref(h)))
+        if final_norm is not None:
+            _need(final_norm, "final_norm", _torch_dtype(dtype), d_model)
+        self._final_norm = final_norm
+        _check(RAW["cb_model_create"](ctypes.byref(self.cfg), arr, _ptr(final_norm),
+                                      ctypes.byref(h)))
         self.handle = h
+        self._ws = None
+
+    def set_workspace(self, ws=None, nbytes=0):
+        """Plans carve their workspace from the device buffer ws (a tensor
+        kept referenced here, or an address) of nbytes bytes; ws None with
+        nbytes > 0 limits pool allocations to nbytes; (None, 0) restores the
+        default."""
+        if ws is not None and not isinstance(ws, int):
+            _need(ws, "workspace")
+            nbytes = nbytes or ws.numel() * ws.element_size()
+        self._ws = ws
+        _check(RAW["cb_model_set_workspace"](self.handle, _ptr(ws), int(nbytes)))
+
+    def workspace_size(self, chunks, offsets, n_suffix, x0, schedule=None, recompute_bp=1500,
+                       schedule_kind=CB_SCHED_GRADUAL, dev_mode=CB_DEV_KV, min_tokens=0,
+                       given_scores=None):
+        """Bytes of workspace cb_blend needs for this request."""
+        req, keep = _request(chunks, offsets, n_suffix, x0, schedule, recompute_bp,
+                             schedule_kind, dev_mode, min_tokens, given_scores)
+        out = _c_i64()
+        _check(RAW["cb_workspace_size"](self.handle, ctypes.byref(req), ctypes.byref(out)))
+        del keep
+        return out.value
 
     def close(self):
         if getattr(self, "handle", None):

@@ -175,6 +175,12 @@ MemKind mem_kind(const void* p) {
 struct cb_model {
     cb_model_cfg cfg;
     std::vector<cb_layer_weights> w;
+    const void* final_norm = nullptr;   // gain of the final RMSNorm (cb_lm_head), or NULL
+    // plan workspaces: carved from a caller's buffer (ws_user), or taken from
+    // the model's pool, at most ws_limit bytes when ws_limit > 0
+    void* ws_user = nullptr;
+    size_t ws_user_bytes = 0;
+    size_t ws_limit = 0;
     RopeTab rope;
     int device = 0;
     hipStream_t side = nullptr;   // fetch (H2D + rotation) stream, default priority
@@ -228,6 +234,8 @@ struct cb_plan {
     float* deviation = nullptr;
     // workspace
     void* ws = nullptr;
+    bool ws_owned = false;        // allocated from the model's pool (else the caller's)
+    size_t ws_bytes = 0;
     float *X = nullptr, *Hres = nullptr, *dev = nullptr;
     void *Hn = nullptr, *Q = nullptr, *Kn = nullptr, *Vn = nullptr, *attn = nullptr,
          *act = nullptr;
@@ -439,7 +447,9 @@ size_t carve(cb_plan* p, char* base, int max_rows) {
     return off;
 }
 
-cb_status plan_alloc(cb_plan* p) {
+// Workspace bytes of a laid-out plan (most stacked rows of any layer, the
+// largest attention split of any layer, staging); max_rows receives the rows.
+size_t plan_bytes(cb_plan* p, int* max_rows_out) {
     const cb_model_cfg& c = p->m->cfg;
     int max_rows = 0;
     size_t aw = 0;
@@ -451,11 +461,31 @@ cb_status plan_alloc(cb_plan* p) {
                                               c.head_dim));
     }
     p->attn_ws_bytes = aw;
-    const size_t bytes = carve(p, nullptr, max_rows);
-    if (hipMallocFromPoolAsync(&p->ws, bytes, p->m->pool, p->stream) != hipSuccess) {
-        (void)hipGetLastError();
-        return fail(CB_E_OOM, "workspace of %zu bytes", bytes);
+    *max_rows_out = max_rows;
+    return carve(p, nullptr, max_rows);
+}
+
+cb_status plan_alloc(cb_plan* p) {
+    int max_rows = 0;
+    const size_t bytes = plan_bytes(p, &max_rows);
+    const cb_model* m = p->m;
+    if (m->ws_user) {
+        if (bytes > m->ws_user_bytes)
+            return fail(CB_E_OOM, "workspace of %zu bytes exceeds the caller's %zu bytes", bytes,
+                        m->ws_user_bytes);
+        p->ws = m->ws_user;
+    } else {
+        if (m->ws_limit && bytes > m->ws_limit)
+            return fail(CB_E_OOM, "workspace of %zu bytes exceeds the limit of %zu bytes", bytes,
+                        m->ws_limit);
+        if (hipMallocFromPoolAsync(&p->ws, bytes, p->m->pool, p->stream) != hipSuccess) {
+            (void)hipGetLastError();
+            p->ws = nullptr;
+            return fail(CB_E_OOM, "workspace of %zu bytes", bytes);
+        }
+        p->ws_owned = true;
     }
+    p->ws_bytes = bytes;
     carve(p, (char*)p->ws, max_rows);
     // decode jobs of staged chunks point into the staging area from now on
     for (auto& set : p->qjobs)
@@ -523,7 +553,7 @@ void plan_free(cb_plan* p) {
         // the side stream may still be rotating: main waits for its last event
         for (int l = 0; l < p->L; ++l)
             if (p->fetch_done[l]) (void)hipStreamWaitEvent(p->stream, p->fetched[l], 0);
-        (void)hipFreeAsync(p->ws, p->stream);
+        if (p->ws_owned) (void)hipFreeAsync(p->ws, p->stream);
     }
     {
         std::lock_guard<std::mutex> lk(p->m->mu);
@@ -1162,7 +1192,7 @@ cb_status cb_schedule(int32_t n_chunk_tokens, int32_t recompute_bp, int32_t kind
 }
 
 cb_status cb_model_create(const cb_model_cfg* cfg, const cb_layer_weights* layers,
-                          cb_model** out) {
+                          const void* final_norm, cb_model** out) {
     if (!out) return fail(CB_E_INVALID, "out is NULL");
     *out = nullptr;
     cb_status st = validate_cfg(cfg);
@@ -1176,9 +1206,12 @@ cb_status cb_model_create(const cb_model_cfg* cfg, const cb_layer_weights* layer
             if (!aligned_to(q, 16)) return fail(CB_E_SHAPE, "layer %d weight not 16-byte aligned", l);
         }
     }
+    if (final_norm && !aligned_to(final_norm, 16))
+        return fail(CB_E_SHAPE, "final_norm not 16-byte aligned");
     cb_model* m = new cb_model();
     m->cfg = *cfg;
     m->w.assign(layers, layers + cfg->n_layers);
+    m->final_norm = final_norm;
     if (hipGetDevice(&m->device) != hipSuccess) {
         delete m;
         return fail(CB_E_HIP, "hipGetDevice failed");
@@ -1250,6 +1283,38 @@ cb_status cb_plan_create(cb_model* m, const cb_request* r, const cb_outputs* o, 
     }
     *out = p;
     return CB_OK;
+}
+
+cb_status cb_model_set_workspace(cb_model* m, void* ws, int64_t bytes) {
+    if (!m) return fail(CB_E_INVALID, "model is NULL");
+    if (bytes < 0) return fail(CB_E_INVALID, "negative workspace size");
+    if (ws) {
+        if (!aligned_to(ws, 256)) return fail(CB_E_SHAPE, "workspace must be 256-byte aligned");
+        if (mem_kind(ws) != MemKind::Device)
+            return fail(CB_E_INVALID, "workspace must be device memory");
+    }
+    m->ws_user = ws;
+    m->ws_user_bytes = ws ? (size_t)bytes : 0;
+    m->ws_limit = ws ? 0 : (size_t)bytes;
+    return CB_OK;
+}
+
+cb_status cb_workspace_size(cb_model* m, const cb_request* r, int64_t* bytes) {
+    if (!m || !r || !bytes) return fail(CB_E_INVALID, "NULL argument");
+    // the request is validated as cb_plan_create would; outputs only give
+    // addresses to the layout and are never touched
+    cb_outputs o{};
+    char probe_out[256];
+    o.fused_k = o.fused_v = probe_out;
+    cb_plan* p = new cb_plan();
+    p->m = m;
+    cb_status st = validate_request(m, r, &o, p);
+    if (st == CB_OK) {
+        int max_rows = 0;
+        *bytes = (int64_t)plan_bytes(p, &max_rows);
+    }
+    delete p;
+    return st;
 }
 
 cb_status cb_fetch_kv(cb_plan* p, int32_t layer) {
@@ -1338,7 +1403,10 @@ cb_status cb_prefill(cb_model* m, const void* x0, int32_t n_tokens, int32_t pos0
 cb_status cb_lm_head(cb_model* m, const float* x, int32_t rows, const void* final_norm,
                      const void* w_lm, int32_t vocab, float* logits, int32_t* argmax,
                      void* stream) {
-    if (!m || !x || !final_norm || !w_lm || !logits) return fail(CB_E_INVALID, "NULL argument");
+    if (m && !final_norm) final_norm = m->final_norm;
+    if (!m || !x || !w_lm || !logits) return fail(CB_E_INVALID, "NULL argument");
+    if (!final_norm)
+        return fail(CB_E_INVALID, "no final_norm: pass one or give it to cb_model_create");
     if (rows <= 0 || vocab <= 0) return fail(CB_E_INVALID, "rows %d, vocab %d", rows, vocab);
     const cb_model_cfg& c = m->cfg;
     if (!aligned_to(x, 16) || !aligned_to(w_lm, 16) || !aligned_to(final_norm, 16))

@@ -34,7 +34,7 @@ def test_exports_every_declared_symbol(npk):
 
 
 def test_abi_version(npk):
-    assert npk.cb_abi_version() == npk.CB_ABI_VERSION == 5
+    assert npk.cb_abi_version() == npk.CB_ABI_VERSION == 6
 
 
 @pytest.mark.parametrize("n", [0, 1, 10, 384, 3840, 7680, 8192])
@@ -59,19 +59,19 @@ def test_schedule_rejects_bad_args(npk):
 def test_model_create_validation(npk):
     raw = npk.RAW["cb_model_create"]
     h = ctypes.c_void_p()
-    assert raw(None, None, ctypes.byref(h)) == npk.CB_E_INVALID
+    assert raw(None, None, None, ctypes.byref(h)) == npk.CB_E_INVALID
     cfg = npk.cb_model_cfg(2, 256, 4, 4, 96, 1024, 1e4, 1e-5, npk.CB_BF16)
-    assert raw(ctypes.byref(cfg), None, ctypes.byref(h)) == npk.CB_E_UNSUPPORTED
+    assert raw(ctypes.byref(cfg), None, None, ctypes.byref(h)) == npk.CB_E_UNSUPPORTED
     cfg = npk.cb_model_cfg(2, 256, 4, 3, 64, 1024, 1e4, 1e-5, npk.CB_BF16)
-    assert raw(ctypes.byref(cfg), None, ctypes.byref(h)) == npk.CB_E_SHAPE
+    assert raw(ctypes.byref(cfg), None, None, ctypes.byref(h)) == npk.CB_E_SHAPE
     cfg = npk.cb_model_cfg(2, 250, 4, 4, 64, 1024, 1e4, 1e-5, npk.CB_BF16)
-    assert raw(ctypes.byref(cfg), None, ctypes.byref(h)) == npk.CB_E_SHAPE
+    assert raw(ctypes.byref(cfg), None, None, ctypes.byref(h)) == npk.CB_E_SHAPE
     cfg = npk.cb_model_cfg(2, 256, 4, 4, 64, 1024, 1e4, 1e-5, 5)
-    assert raw(ctypes.byref(cfg), None, ctypes.byref(h)) == npk.CB_E_INVALID
+    assert raw(ctypes.byref(cfg), None, None, ctypes.byref(h)) == npk.CB_E_INVALID
     cfg = npk.cb_model_cfg(2, 256, 4, 4, 64, 1024, 1e4, 1e-5, npk.CB_F32)
-    assert raw(ctypes.byref(cfg), None, ctypes.byref(h)) == npk.CB_E_INVALID   # NULL layers
+    assert raw(ctypes.byref(cfg), None, None, ctypes.byref(h)) == npk.CB_E_INVALID   # NULL layers
     w = (npk.cb_layer_weights * 2)()
-    assert raw(ctypes.byref(cfg), w, ctypes.byref(h)) == npk.CB_E_INVALID     # NULL weights
+    assert raw(ctypes.byref(cfg), w, None, ctypes.byref(h)) == npk.CB_E_INVALID     # NULL weights
     assert not h.value
 
 
