@@ -9,7 +9,9 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libcacheblend.so")
+# CACHEBLEND_LIB selects another build of the same library (e.g. the
+# host-sanitized one the CPU tests load)
+LIB_PATH = os.environ.get("CACHEBLEND_LIB") or os.path.join(_HERE, "libcacheblend.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "

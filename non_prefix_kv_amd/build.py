@@ -26,9 +26,19 @@ FLAGS = [
 ]
 
 
-def _compile(src):
-    obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+# Host code built again with AddressSanitizer and UndefinedBehaviorSanitizer
+# (host side only: each flag after -Xarch_host; the GPU code is unchanged),
+# for the CPU tests of the host-only entry points.
+SAN_OUT = os.path.join(PKG, "_build_san", "libcacheblend_san.so")
+SAN_FLAGS = ["-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host",
+             "-fno-omit-frame-pointer"]
+
+
+def _compile(src, san=False):
+    odir = os.path.dirname(SAN_OUT) if san else OBJ_DIR
+    obj = os.path.join(odir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *(SAN_FLAGS if san else []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in (r.stderr or "").splitlines()
                     if "packed-fp32-ops" not in l)
@@ -37,24 +47,35 @@ def _compile(src):
     return obj, err
 
 
-def build(verbose=True):
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    jobs = min(len(srcs), int(os.environ.get("MAX_JOBS", "8")))
-    with cf.ThreadPoolExecutor(jobs) as ex:
-        results = list(ex.map(_compile, srcs))
-    for obj, err in results:
-        if err.strip() and verbose:
-            print(err, file=sys.stderr)
-    tmp = OUT + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
-           *[o for o, _ in results]]
+def _link(objs, out, extra=()):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *extra, "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose=True, sanitized=True):
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    os.makedirs(os.path.dirname(SAN_OUT), exist_ok=True)
+    srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+    jobs = max(1, int(os.environ.get("MAX_JOBS", "8")))
+    with cf.ThreadPoolExecutor(jobs) as ex:
+        plain = [ex.submit(_compile, src) for src in srcs]
+        san = [ex.submit(_compile, src, True) for src in srcs] if sanitized else []
+        results = [f.result() for f in plain]
+        san_results = [f.result() for f in san]
+    for obj, err in results:
+        if err.strip() and verbose:
+            print(err, file=sys.stderr)
+    _link([o for o, _ in results], OUT)
+    if sanitized:
+        # the sanitizer runtimes are not linked into a shared library: they
+        # come from the ASan runtime preloaded by the process that loads it
+        _link([o for o, _ in san_results], SAN_OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT}" + (f" and {SAN_OUT}" if sanitized else ""))
     return OUT
 
 
