@@ -282,13 +282,12 @@ __device__ __forceinline__ void mfma32(floatx16& acc, const bf16x8& a, const bf1
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
 }
 
-// Three-way maximum in one instruction.  fmaxf would first quiet each
-// operand (an extra instruction per score in IEEE mode); scores are finite
-// or -inf here, so the plain instruction gives the same result.
+// Three-way maximum: the compiler forms v_max3_f32 from the pair of fmaxf
+// (quieting only the first operands it cannot prove canonical), and, seeing
+// that the scores come from MFMAs, places the wait states their results
+// need before the first read.
 __device__ __forceinline__ float vmax3(float a, float b, float c) {
-    float r;
-    asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
-    return r;
+    return fmaxf(fmaxf(a, b), c);
 }
 
 constexpr int kT32 = 256;   // threads per workgroup (4 waves)
@@ -322,9 +321,11 @@ __device__ __forceinline__ i32x4 attn_rsrc(const void* base, int bytes) {
 // 16 bytes per lane from buffer offset voff into LDS at m0 + 16 * lane.
 // Inline assembly keeps the compiler from treating it as an LDS store it
 // must wait for; completion is tracked by explicit vmcnt waits and the
-// "memory" clobber keeps LDS accesses from moving across the copy.
+// "memory" clobber keeps LDS accesses from moving across the copy.  The
+// s_nop is the one wait state the load needs after the write of M0, which
+// the hazard recognizer cannot see inside the statement.
 __device__ __forceinline__ void attn_dma16(i32x4 rsrc, int voff, uint32_t m0) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(m0)
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(m0)
                  : "memory");
 }
 

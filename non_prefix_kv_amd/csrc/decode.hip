@@ -325,8 +325,10 @@ __device__ __forceinline__ i32x4_t dec_rsrc(const void* base, int bytes) {
                    __builtin_amdgcn_readfirstlane((int)((p >> 32) & 0xFFFF)),
                    __builtin_amdgcn_readfirstlane(bytes), 0x00020000};
 }
+// 16 bytes per lane into LDS at m0 + 16 * lane, as in the prefill attention
+// (the s_nop: one wait state after the write of M0).
 __device__ __forceinline__ void dec_dma16(i32x4_t rsrc, int voff, uint32_t m0) {
-    asm volatile("buffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(m0)
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(rsrc), "{m0}"(m0)
                  : "memory");
 }
 template <int DH> __device__ __forceinline__ int dec_vkey(int r) {

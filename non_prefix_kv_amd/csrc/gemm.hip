@@ -357,13 +357,22 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, int bytes) {
 // Issued as inline assembly so that the compiler's memory model does not see
 // a store to LDS (it would otherwise wait for every outstanding copy before
 // any LDS read); completion is tracked by the explicit vmcnt waits below and
-// the "memory" clobber keeps LDS reads from moving across the copy.
+// the "memory" clobber keeps LDS reads from moving across the copy.  The
+// hazard recognizer cannot see inside the statement: the s_nop is the one
+// wait state the load needs after the scalar write of M0.  A descriptor or
+// offset word written by v_readfirstlane needs five before the load; the
+// kernels make their byte counts scalar (uniform_int) once, before the K
+// loops that rebuild descriptors, so that no such write sits near a copy.
 __device__ __forceinline__ void dma16(i32x4 rsrc, int voff, int soff, uint32_t m0) {
-    asm volatile("buffer_load_dwordx4 %0, %1, %2 offen lds"
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
                  :
                  : "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(m0)
                  : "memory");
 }
+
+// A value the whole wave agrees on, held in a scalar register from here on
+// (the descriptors built from it in a K loop then need no v_readfirstlane).
+__device__ __forceinline__ int uniform_int(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 // Byte range of the wave's 32-row slice: rows left (clamped to 0..32) x row bytes.
 __device__ __forceinline__ int slice_bytes(int64_t rows_left, int row_bytes) {
@@ -559,8 +568,8 @@ __global__ __launch_bounds__(kThreads8, 1) void gemm_dma8_kernel(GemmArgs g) {
         b_base = static_cast<const bf16*>(g.b0) + ((int64_t)n_tile * BN + 16 * wave) * g.K;
         b_left = g.N - (int64_t)n_tile * BN - 16 * wave;
     }
-    const int a_bytes = (int)(a_left < 0 ? 0 : (a_left > 16 ? 16 : a_left)) * Kb;
-    const int b_bytes = (int)(b_left < 0 ? 0 : (b_left > 16 ? 16 : b_left)) * Kb;
+    const int a_bytes = uniform_int((int)(a_left < 0 ? 0 : (a_left > 16 ? 16 : a_left)) * Kb);
+    const int b_bytes = uniform_int((int)(b_left < 0 ? 0 : (b_left > 16 ? 16 : b_left)) * Kb);
 
     // Lane i fetches row i/8 (of 8) at LDS slot i%8, i.e. global chunk
     // slot ^ key(row), key(r) = (r/2) % 8; the second 8 rows of the wave's
@@ -852,14 +861,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big4_kernel(GemmArgs g) {
     // This wave copies rows 64*wave .. +63 of the A tile and of the B tile.
     const bf16* a_base = static_cast<const bf16*>(g.a) + ((int64_t)m_tile * BBM + 64 * wave) * g.K;
     const int64_t a_rows = (int64_t)g.M - (int64_t)m_tile * BBM - 64 * wave;
-    const int a_bytes = (a_rows < 0 ? 0 : (a_rows > 64 ? 64 : (int)a_rows)) * Kb;
+    const int a_bytes = uniform_int((a_rows < 0 ? 0 : (a_rows > 64 ? 64 : (int)a_rows)) * Kb);
     // B: two 32-row halves (for gate/up they come from different matrices)
     const bf16* b_base[2];
     int b_bytes[2];
     if (EPI == EPI_SWIGLU) {
         const int oc0 = n_tile * (BBN / 2) + wave * 32;
         const int64_t rows = g.N - oc0;
-        const int by = (rows < 0 ? 0 : (rows > 32 ? 32 : (int)rows)) * Kb;
+        const int by = uniform_int((rows < 0 ? 0 : (rows > 32 ? 32 : (int)rows)) * Kb);
         b_base[0] = static_cast<const bf16*>(g.b0) + (int64_t)oc0 * g.K;
         b_base[1] = static_cast<const bf16*>(g.b1) + (int64_t)oc0 * g.K;
         b_bytes[0] = b_bytes[1] = by;
@@ -877,7 +886,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big4_kernel(GemmArgs g) {
             const int64_t r0 = local + 64 * wave + 32 * h;
             const int64_t left = rows - r0;
             b_base[h] = static_cast<const bf16*>(mat) + r0 * g.K;
-            b_bytes[h] = (left < 0 ? 0 : (left > 32 ? 32 : (int)left)) * Kb;
+            b_bytes[h] = uniform_int((left < 0 ? 0 : (left > 32 ? 32 : (int)left)) * Kb);
         }
     }
     // Lane i copies row i/4 (of 16) into LDS slot i%4: global chunk slot ^ key,
@@ -1007,14 +1016,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
     // This wave copies rows 64*wave .. +63 of the A tile and of the B tile.
     const bf16* a_base = static_cast<const bf16*>(g.a) + ((int64_t)m_tile * BBM + 64 * wave) * g.K;
     const int64_t a_rows = (int64_t)g.M - (int64_t)m_tile * BBM - 64 * wave;
-    const int a_bytes = (a_rows < 0 ? 0 : (a_rows > 64 ? 64 : (int)a_rows)) * Kb;
+    const int a_bytes = uniform_int((a_rows < 0 ? 0 : (a_rows > 64 ? 64 : (int)a_rows)) * Kb);
     // B: two 32-row halves (for gate/up they come from different matrices)
     const bf16* b_base[2];
     int b_bytes[2];
     if (EPI == EPI_SWIGLU) {
         const int oc0 = n_tile * (BBN / 2) + wave * 32;
         const int64_t rows = g.N - oc0;
-        const int by = (rows < 0 ? 0 : (rows > 32 ? 32 : (int)rows)) * Kb;
+        const int by = uniform_int((rows < 0 ? 0 : (rows > 32 ? 32 : (int)rows)) * Kb);
         b_base[0] = static_cast<const bf16*>(g.b0) + (int64_t)oc0 * g.K;
         b_base[1] = static_cast<const bf16*>(g.b1) + (int64_t)oc0 * g.K;
         b_bytes[0] = b_bytes[1] = by;
@@ -1032,7 +1041,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_big_kernel(GemmArgs g) {
             const int64_t r0 = local + 64 * wave + 32 * h;
             const int64_t left = rows - r0;
             b_base[h] = static_cast<const bf16*>(mat) + r0 * g.K;
-            b_bytes[h] = (left < 0 ? 0 : (left > 32 ? 32 : (int)left)) * Kb;
+            b_bytes[h] = uniform_int((left < 0 ? 0 : (left > 32 ? 32 : (int)left)) * Kb);
         }
     }
     // Lane i copies row i/4 (of 16) into LDS slot i%4: global chunk slot ^ key,
@@ -1179,15 +1188,10 @@ __device__ __forceinline__ int mid_swz(int r, int chunk) {   // byte offset in a
     return r * 64 + ((chunk ^ (r >> 1)) & 3) * 16;
 }
 
-// Accumulates in place in AGPRs.  Written as inline assembly: with the
-// builtin, the register allocator rotated half of the 168 accumulator
-// registers through VGPRs once per loop iteration (252 extra moves per two
-// K stages).  The assembler statement is opaque to the hazard recognizer,
-// so the kernel separates the last MFMA from any read of its result with
-// explicit wait states (mid_acc_fence).  Consecutive MFMAs on one
-// accumulator are 42 instructions apart in the main loop.
+// Accumulates in place: each MFMA's C operand and result are the same
+// registers (the empty register pins after the main loop keep it so).
 __device__ __forceinline__ void mfma16x32(floatx4& acc, const bf16x8& a, const bf16x8& b) {
-    asm volatile("v_mfma_f32_16x16x32_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
 }
 
 struct MidSrc {
@@ -1351,7 +1355,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mid_kernel(GemmArgs g) {
     for (int c = 0; c < 3; ++c) {
         const MidSrc sr = mid_b_rows<EPI>(g, n_tile, 4 * c + wave);
         b_src[c] = sr.p;
-        b_bytes[c] = (int)(sr.left <= 0 ? 0 : (sr.left >= 16 ? 16 : sr.left)) * Kb;
+        b_bytes[c] = uniform_int((int)(sr.left <= 0 ? 0 : (sr.left >= 16 ? 16 : sr.left)) * Kb);
     }
     // Lane i copies row i / 4 of a block into slot i % 4: global chunk
     // slot ^ key(row), key(r) = (r / 2) % 4 (the same for every block).
@@ -1457,10 +1461,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mid_kernel(GemmArgs g) {
         step(std::false_type{}, kt + 1, slot, na, nb, fa, fb);
         slot = slot + 1 == S ? 0 : slot + 1;
     }
-    // wait states between the last MFMA and the first read of an accumulator
-    // (more than the 11 an 8-pass MFMA needs), then a fence per accumulator
-    // so that no read is scheduled above the wait
-    asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
+    // Empty statements that take each accumulator in AGPRs: without them the
+    // register allocator gives 21 of the 42 MFMAs a result register other
+    // than their C operand and copies the accumulators back once per loop
+    // iteration (252 v_accvgpr_mov per two K stages).  They emit nothing;
+    // the wait states between the last MFMA and the first read of its result
+    // are placed by the compiler, which sees every MFMA.
 #pragma unroll
     for (int i = 0; i < 7; ++i)
 #pragma unroll
