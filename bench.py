@@ -66,6 +66,11 @@ def parse():
                     help="skip the first-token (LM head) and decode-step measurement")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device copy of known size (counter calibration)")
+    ap.add_argument("--kernel", choices=["rotate", "deviation", "rmsnorm", "scatter", "copy",
+                                         "memcpy"],
+                    help="only time one bandwidth-bound step alone through its C-ABI entry, "
+                         "at the shape the llama2-7b-shape step gives it, then exit")
+    ap.add_argument("--reps", type=int, default=200, help="launches timed with --kernel")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="summarize a rocprofv3 kernel_trace.csv of a bench run (timed steps "
                          "only) as a markdown table, then exit")
@@ -74,6 +79,12 @@ def parse():
     ap.add_argument("--counter-summary", metavar="CSV", nargs="+",
                     help="average rocprofv3 counter_collection.csv values per kernel over the "
                          "timed steps, then exit")
+    ap.add_argument("--calibration", metavar="CSV", nargs=2,
+                    help="with --counter-summary: FETCH_SIZE and WRITE_SIZE counter files of "
+                         "--copy-calibration; prints a markdown table of HBM bytes per "
+                         "dispatch and derived rates instead of the JSON")
+    ap.add_argument("--all-dispatches", action="store_true",
+                    help="with --counter-summary: every dispatch, not only the timed steps")
     return ap.parse_args()
 
 
@@ -146,7 +157,7 @@ def trace_summary(path, match=None):
     print(f"\n{len(rows)} dispatches, {total / 1e6:.3f} ms of kernel time")
 
 
-def counter_summary(paths):
+def counter_summary(paths, calibration=None, all_dispatches=False):
     import csv
     out = {}
     for path in paths:
@@ -154,14 +165,139 @@ def counter_summary(paths):
         by_dispatch = {}
         for r in rows:
             by_dispatch.setdefault(int(r["Dispatch_Id"]), []).append(r)
-        disp = _timed_rows([v[0] for v in by_dispatch.values()], lambda r: int(r["Dispatch_Id"]))
+        disp = [v[0] for v in by_dispatch.values()]
+        if not all_dispatches:
+            disp = _timed_rows(disp, lambda r: int(r["Dispatch_Id"]))
         for r0 in disp:
             k = _short(r0["Kernel_Name"])
             for r in by_dispatch[int(r0["Dispatch_Id"])]:
                 out.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
     res = {k: {c: {"dispatches": len(v), "mean": sum(v) / len(v)} for c, v in d.items()}
            for k, d in out.items()}
-    print(json.dumps(res, indent=1))
+    if not calibration:
+        print(json.dumps(res, indent=1))
+        return
+    counter_table(res, calibration)
+
+
+def _copy_counter(path, counter):
+    """Value of `counter` (KiB) on the calibration copy (the move_rows
+    kernel of --copy-calibration: 256 MiB read, 256 MiB written)."""
+    import csv
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter and "move_rows_kernel" in r["Kernel_Name"]]
+    return vals[-1]
+
+
+def counter_table(res, calibration):
+    """Markdown table per kernel: HBM bytes per dispatch from FETCH_SIZE and
+    WRITE_SIZE scaled so that the calibration copy reads its 256 MiB, and,
+    where the SQ counters were taken, the matrix-core busy fraction (MFMA
+    busy cycles over 1024 SIMDs x the kernel's GPU cycles, GRBM_GUI_ACTIVE
+    summed over 8 XCDs), the wave-cycle fractions spent waiting, the VALU
+    instructions per MFMA, LDS bank conflicts per LDS instruction cycle and
+    the L2 hit rate."""
+    mib = 256 * 1024                                  # the copy's bytes, KiB
+    f_scale = mib / _copy_counter(calibration[0], "FETCH_SIZE")
+    w_scale = mib / _copy_counter(calibration[1], "WRITE_SIZE")
+    print(f"FETCH_SIZE x {f_scale:.4f}, WRITE_SIZE x {w_scale:.4f} (calibration copy of 256 MiB)\n")
+    cols = ["dispatches", "read MiB", "written MiB", "MFMA busy", "wait any", "wait LDS",
+            "VALU/MFMA", "LDS conflicts", "L2 hit"]
+    print("| kernel | " + " | ".join(cols) + " |")
+    print("|---|" + "---:|" * len(cols))
+
+    def m(d, c):
+        return d[c]["mean"] if c in d else None
+    order = sorted(res, key=lambda k: -(m(res[k], "FETCH_SIZE") or 0) * res[k].get(
+        "FETCH_SIZE", {"dispatches": 1})["dispatches"])
+    for k in order:
+        d = res[k]
+        n = min(v["dispatches"] for v in d.values())     # counters repeated across passes count twice
+        f, w = m(d, "FETCH_SIZE"), m(d, "WRITE_SIZE")
+        cyc = m(d, "GRBM_GUI_ACTIVE")
+        wc = m(d, "SQ_WAVE_CYCLES")
+        cells = [str(n),
+                 f"{f * f_scale / 1024:.2f}" if f is not None else "",
+                 f"{w * w_scale / 1024:.2f}" if w is not None else "",
+                 f"{m(d, 'SQ_VALU_MFMA_BUSY_CYCLES') / (1024 * cyc / 8):.3f}"
+                 if cyc and m(d, "SQ_VALU_MFMA_BUSY_CYCLES") is not None else "",
+                 f"{m(d, 'SQ_WAIT_ANY') / wc:.2f}" if wc and m(d, "SQ_WAIT_ANY") is not None else "",
+                 f"{m(d, 'SQ_WAIT_INST_LDS') / wc:.3f}"
+                 if wc and m(d, "SQ_WAIT_INST_LDS") is not None else "",
+                 f"{m(d, 'SQ_INSTS_VALU') / m(d, 'SQ_INSTS_MFMA'):.1f}"
+                 if m(d, "SQ_INSTS_MFMA") else "",
+                 f"{m(d, 'SQ_LDS_BANK_CONFLICT') / m(d, 'SQ_ACTIVE_INST_LDS'):.3f}"
+                 if m(d, "SQ_ACTIVE_INST_LDS") else "",
+                 f"{m(d, 'TCC_HIT_sum') / (m(d, 'TCC_HIT_sum') + m(d, 'TCC_MISS_sum')):.2f}"
+                 if m(d, "TCC_HIT_sum") is not None and m(d, "TCC_MISS_sum") is not None
+                 and m(d, "TCC_HIT_sum") + m(d, "TCC_MISS_sum") > 0 else ""]
+        print(f"| {k} | " + " | ".join(cells) + " |")
+
+
+def kernel_alone(kind, reps):
+    """One bandwidth-bound step launched `reps` times back to back on the
+    current stream, timed with events on that stream.  Shapes are those of
+    the llama2-7b-shape step (6 chunks x 640 rows, 32 heads x 128, 832
+    recomputed rows); algorithmic bytes are each operand read once and each
+    result written once.  Launches cycle through enough buffer sets (over
+    1 GiB together) that none finds its operands still in the 256 MB
+    last-level cache from an earlier launch."""
+    import torch
+    import non_prefix_kv_amd as npk
+    bf, dev = torch.bfloat16, "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    rnd = lambda *sh, dt=bf: torch.randn(sh, generator=g, device=dev).to(dt)
+    n_c, H, D, R = 3840, 32, 128, 832
+    row = H * D
+
+    def ring(make, set_bytes):
+        return [make() for _ in range(max(1, -(-(1 << 30) // set_bytes)))]
+    if kind == "rotate":       # K rotated by one delta, V copied, every chunk row
+        sets = ring(lambda: [rnd(n_c, H, D) for _ in range(4)], 4 * n_c * row * 2)
+        fn = lambda b: npk.cb_rope_rerotate(b[0], b[2], b[1], b[3], n_c, H, D, 1234)
+        algo, shape = 4 * n_c * row * 2, f"{n_c} rows x {H} heads x {D}, bf16 K and V"
+    elif kind == "deviation":  # sum of squared K and V differences per row
+        sets = ring(lambda: [rnd(n_c, row) for _ in range(4)] + [torch.empty(n_c, device=dev)],
+                    4 * n_c * row * 2)
+        fn = lambda b: npk.cb_deviation(b[0], b[1], b[2], b[3], n_c, row, npk.CB_DEV_KV, b[4])
+        algo, shape = 4 * n_c * row * 2 + 4 * n_c, f"{n_c} rows x {row}, bf16 K and V"
+    elif kind == "rmsnorm":    # float32 residual rows -> bf16 normalized rows
+        sets = ring(lambda: [rnd(R, row, dt=torch.float32), rnd(row),
+                             torch.empty((R, row), dtype=bf, device=dev)], R * row * 6)
+        fn = lambda b: npk.cb_rmsnorm(b[0], b[1], b[2], R, row)
+        algo, shape = R * row * (4 + 2) + row * 2, f"{R} rows x {row}, float32 in, bf16 out"
+    elif kind == "copy":       # the rotation's bytes as a plain row copy (reference)
+        idx = torch.arange(n_c, dtype=torch.int32, device=dev)
+        sets = ring(lambda: [rnd(n_c, 2 * row), torch.empty((n_c, 2 * row), dtype=bf, device=dev)],
+                    4 * n_c * row * 2)
+        fn = lambda b: npk.cb_gather_rows(b[0], b[1], idx, n_c, 2 * row * 2)
+        algo, shape = 4 * n_c * row * 2, f"{n_c} rows x {4 * row} B copied"
+    elif kind == "memcpy":     # the same bytes through the runtime's device copy (reference)
+        sets = ring(lambda: [rnd(n_c, 2 * row), torch.empty((n_c, 2 * row), dtype=bf, device=dev)],
+                    4 * n_c * row * 2)
+        fn = lambda b: b[1].copy_(b[0])
+        algo, shape = 4 * n_c * row * 2, f"{n_c} rows x {4 * row} B, torch device copy"
+    else:                      # recomputed rows into their places in a chunk-sized buffer
+        idx = torch.randperm(n_c, generator=g, device=dev)[:R].to(torch.int32)
+        sets = ring(lambda: [rnd(R, row), rnd(n_c, row)], (R + n_c) * row * 2)
+        fn = lambda b: npk.cb_scatter_rows(b[0], b[1], idx, R, row * 2)
+        algo, shape = 2 * R * row * 2, f"{R} rows x {row * 2} B into {n_c} rows"
+    for i in range(len(sets)):
+        fn(sets[i])
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for i in range(reps):
+        fn(sets[i % len(sets)])
+    e1.record(st)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    gbs = algo / us / 1e3
+    print(json.dumps({"kernel": kind, "shape": shape, "reps": reps, "buffer_sets": len(sets),
+                      "us_per_launch": us, "algorithmic_bytes": algo, "gbs": gbs,
+                      "frac_hbm": gbs / 8000.0}))
 
 
 def log(*a):
@@ -962,10 +1098,13 @@ def main():
         trace_summary(args.trace_summary, args.match)
         return
     if args.counter_summary:
-        counter_summary(args.counter_summary)
+        counter_summary(args.counter_summary, args.calibration, args.all_dispatches)
         return
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.kernel:
+        kernel_alone(args.kernel, args.reps)
         return
     import torch
     import non_prefix_kv_amd as npk

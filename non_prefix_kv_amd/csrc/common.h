@@ -62,6 +62,24 @@ template <> __device__ __forceinline__ Frag<float> load_frag<float>(const float*
     return f;
 }
 
+// The same 8 elements read with the non-temporal hint, for operands that
+// are streamed once and not read again soon (chunk caches, cached rows):
+// they then displace less of what the next kernels read from the caches.
+template <typename T>
+__device__ __forceinline__ Frag<T> load_frag_nt(const T* p);
+template <> __device__ __forceinline__ Frag<bf16> load_frag_nt<bf16>(const bf16* p) {
+    Frag<bf16> f;
+    f.v = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+    return f;
+}
+template <> __device__ __forceinline__ Frag<float> load_frag_nt<float>(const float* p) {
+    Frag<float> f;
+    const floatx4 a = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+    const floatx4 b = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p + 4));
+    f.v = floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return f;
+}
+
 // 8 consecutive elements of a row, loaded to / stored from float registers.
 template <typename T> struct Vec8;
 template <> struct Vec8<bf16> {

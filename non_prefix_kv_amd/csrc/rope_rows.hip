@@ -35,7 +35,13 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
     const T* ks = j.k_src ? static_cast<const T*>(j.k_src) + s_off : kd + d_off;
 
     float x[8];
-    Vec8<T>::load(ks, x);
+    if (j.k_src) {          // a chunk cache row: read once, not again soon
+        const Frag<T> f = load_frag_nt<T>(ks);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = to_f32(f.v[i]);
+    } else {
+        Vec8<T>::load(ks, x);
+    }
     const int ad = j.delta < 0 ? -j.delta : j.delta;
     const float sg = j.delta < 0 ? -1.f : 1.f;
     const float2* tr = tab + (int64_t)ad * half + ((c % head_dim) >> 1);
@@ -48,7 +54,12 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
         y[2 * p + 1] = x[2 * p] * sn + x[2 * p + 1] * cs.x;
     }
     Vec8<T>::store(kd + d_off, y);
-    if (j.v_src) Vec8<T>::copy(static_cast<const T*>(j.v_src) + s_off, vd + d_off);
+    if (j.v_src) {
+        const u32x4* vs = reinterpret_cast<const u32x4*>(static_cast<const T*>(j.v_src) + s_off);
+        u32x4* vo = reinterpret_cast<u32x4*>(vd + d_off);
+#pragma unroll
+        for (int w = 0; w < (int)sizeof(T) / 2; ++w) vo[w] = __builtin_nontemporal_load(vs + w);
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void move_rows_kernel(

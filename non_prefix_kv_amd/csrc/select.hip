@@ -24,10 +24,12 @@ constexpr int kDevThreads = 256;
 constexpr int kSelThreads = 1024;
 constexpr int kSelWaves = kSelThreads / 64;
 
+// a: a freshly computed row (likely still in L2); b: the cached row, read
+// once with the non-temporal hint
 template <typename T>
 __device__ __forceinline__ float sq_diff8(const T* a, const T* b) {
     Frag<T> x = load_frag<T>(a);
-    Frag<T> y = load_frag<T>(b);
+    Frag<T> y = load_frag_nt<T>(b);
     float s = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
