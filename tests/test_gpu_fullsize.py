@@ -5,6 +5,9 @@
   launch shapes of every kernel are those of the benchmark's layers 0-3.
 * Yi-34B width (GQA 56/8), three layers with given scores: bit-exact kept
   sets and every layer against the oracle.
+* Llama-2-13B width (d 5120, 40 x 128 heads, F 13824), three layers on a
+  reduced prompt, KV deviation at r = 15% and at r = 100% (the full
+  prefill), every layer against the oracle.
 * The full 32-layer benchmark configuration (bench.py's own input builder),
   through properties that hold at any size: schedule counts, nested
   ascending kept sets, the top-k property of the reported deviations, and
@@ -92,6 +95,31 @@ def test_yi34b_width_given_scores_vs_oracle(lib):
         print(f"yi34b width, {L} layers: errors {errs}", flush=True)
         del model, gpu
         _free()
+
+
+def test_llama13b_width_vs_oracle(lib):
+    """Llama-2-13B width in bf16 on a reduced prompt (6 x 512 chunk tokens +
+    256 suffix), three layers, KV deviation (CacheBlend explainer (0h-n0),
+    "選択的再計算" Steps 1-4): gradual r = 15% (layer 2 runs the steady
+    launch shapes at ~730 rows) with the oracle replayed on the GPU's kept
+    sets, and r = 100%, where the fusion is the oracle's full prefill of the
+    whole prompt.  Every layer's fused K/V and the last rows are compared
+    (float32 oracle, seeded stand-in chunk caches)."""
+    w = WORKLOADS["llama13b-8k"]
+    shape = dataclasses.replace(w.shape, n_layers=3)
+    case = make_case(shape, (512,) * 6, 256, seed=2, dtype="bf16", random_caches=True)
+    model = make_model(lib, case, "bf16")
+    nc = case.n_chunk_tokens
+    for sched in (oracle.schedule(nc, 1500, "gradual", 3), [nc] * 4):
+        gpu = run_gpu_blend(lib, model, case, "bf16", sched)
+        _, swaps, errs = compare(case, gpu, sched, "bf16", oracle_dtype=np.float32)
+        print(f"llama13b width, schedule {sched}: swaps {swaps}, errors {errs}", flush=True)
+        assert sum(swaps) <= 0.02 * max(1, sum(sched[2:]))
+        if sched[1] == nc and sched[-1] == nc:
+            assert sum(swaps) == 0
+        del gpu
+    del model
+    _free()
 
 
 def _properties(npk, w, chunks, fk, fv, sel, dev, sched, Nc, L, S, layers_to_check):
