@@ -68,6 +68,12 @@ template <> __device__ __forceinline__ Frag<float> lds_frag<float>(const float* 
 
 __device__ __forceinline__ float silu_f(float x) { return x / (1.0f + __expf(-x)); }
 
+// Output row of q/k/v result row `row`: K and V rows go to kv_rows[row] when
+// a row map is given; Q rows stay in result order.
+__device__ __forceinline__ int64_t qkv_out_row(const GemmArgs& g, int row, bool kv) {
+    return (kv && g.kv_rows) ? (int64_t)g.kv_rows[row] : (int64_t)row;
+}
+
 // Maps the hardware workgroup id to a logical tile id such that each XCD
 // (ids are dealt round-robin over the 8 XCDs) receives a contiguous range.
 __device__ __forceinline__ int xcd_remap(int hw, int total) {
@@ -152,10 +158,10 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const Acc (&acc)[NT]
                         off = (int64_t)row * g.n0 + seg_col;
                     } else if (col < g.n0 + g.n1) {
                         dst = static_cast<T*>(g.out1); seg_col = col - g.n0;
-                        off = (int64_t)row * g.n1 + seg_col;
+                        off = qkv_out_row(g, row, true) * g.n1 + seg_col;
                     } else {
                         dst = static_cast<T*>(g.out2); seg_col = col - g.n0 - g.n1;
-                        off = (int64_t)row * (g.N - g.n0 - g.n1) + seg_col;
+                        off = qkv_out_row(g, row, true) * (g.N - g.n0 - g.n1) + seg_col;
                     }
                     if (col < g.n0 + g.n1) {
                         const int d = seg_col % g.head_dim;
@@ -448,8 +454,8 @@ __device__ __forceinline__ void epilogue_finish(const GemmArgs& g, int m_tile, i
         const int c0 = n_tile * BN;
         bf16* base;
         int width, local;
-        bool rope;
-        if (c0 < g.n0) { base = static_cast<bf16*>(g.out0); width = g.n0; local = col; rope = true; }
+        bool rope, kv = true;
+        if (c0 < g.n0) { base = static_cast<bf16*>(g.out0); width = g.n0; local = col; rope = true; kv = false; }
         else if (c0 < g.n0 + g.n1) {
             base = static_cast<bf16*>(g.out1); width = g.n1; local = col - g.n0; rope = true;
         } else {
@@ -471,7 +477,7 @@ __device__ __forceinline__ void epilogue_finish(const GemmArgs& g, int m_tile, i
                 y[2] = x[2] * cs[2] - x[3] * cs[3];
                 y[3] = x[2] * cs[3] + x[3] * cs[2];
             }
-            *reinterpret_cast<bf16x4*>(base + (int64_t)row * width + local) =
+            *reinterpret_cast<bf16x4*>(base + qkv_out_row(g, row, kv) * width + local) =
                 bf16x4{static_cast<bf16>(y[0]), static_cast<bf16>(y[1]), static_cast<bf16>(y[2]),
                        static_cast<bf16>(y[3])};
         }
@@ -773,8 +779,8 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& g, const floatx16 (
                 const int c0 = n_tile * BBN;
                 bf16* base;
                 int width, local;
-                bool rope;
-                if (c0 < g.n0) { base = static_cast<bf16*>(g.out0); width = g.n0; local = col; rope = true; }
+                bool rope, kv = true;
+                if (c0 < g.n0) { base = static_cast<bf16*>(g.out0); width = g.n0; local = col; rope = true; kv = false; }
                 else if (c0 < g.n0 + g.n1) {
                     base = static_cast<bf16*>(g.out1); width = g.n1; local = col - g.n0; rope = true;
                 } else {
@@ -796,7 +802,7 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& g, const floatx16 (
                             y[2] = x[2] * cs[2] - x[3] * cs[3];
                             y[3] = x[2] * cs[3] + x[3] * cs[2];
                         }
-                        *reinterpret_cast<bf16x4*>(base + (int64_t)row * width + local) =
+                        *reinterpret_cast<bf16x4*>(base + qkv_out_row(g, row, kv) * width + local) =
                             bf16x4{static_cast<bf16>(y[0]), static_cast<bf16>(y[1]),
                                    static_cast<bf16>(y[2]), static_cast<bf16>(y[3])};
                     }
@@ -1268,8 +1274,8 @@ __device__ __forceinline__ void mid_finish(const GemmArgs& g, int row0, int n_ti
         // the 4 columns lie in one of q, k, v (row counts are multiples of 16)
         bf16* base;
         int width, local;
-        bool rope;
-        if (col < g.n0) { base = static_cast<bf16*>(g.out0); width = g.n0; local = col; rope = true; }
+        bool rope, kv = true;
+        if (col < g.n0) { base = static_cast<bf16*>(g.out0); width = g.n0; local = col; rope = true; kv = false; }
         else if (col < g.n0 + g.n1) {
             base = static_cast<bf16*>(g.out1); width = g.n1; local = col - g.n0; rope = true;
         } else {
@@ -1291,7 +1297,7 @@ __device__ __forceinline__ void mid_finish(const GemmArgs& g, int row0, int n_ti
                 y[2] = x[2] * cs[2] - x[3] * cs[3];
                 y[3] = x[2] * cs[3] + x[3] * cs[2];
             }
-            *reinterpret_cast<bf16x4*>(base + (int64_t)row * width + local) =
+            *reinterpret_cast<bf16x4*>(base + qkv_out_row(g, row, kv) * width + local) =
                 bf16x4{static_cast<bf16>(y[0]), static_cast<bf16>(y[1]), static_cast<bf16>(y[2]),
                        static_cast<bf16>(y[3])};
         }

@@ -198,6 +198,8 @@ struct GemmArgs {
     const int* pos;     // EPI_QKV positions per row
     RopeTab rope;
     int head_dim;
+    const int* kv_rows; // EPI_QKV: row of out1 / out2 that result row r of K / V goes to
+                        // (nullptr = r; K and V then land straight in a cache)
 };
 hipError_t launch_gemm(int dtype, int epi, const GemmArgs& g, hipStream_t s);
 

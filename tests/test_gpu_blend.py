@@ -207,37 +207,40 @@ def test_binding_rejects_mismatched_outputs(lib, tiny):
         assert e.value.status in (lib.CB_E_INVALID, lib.CB_E_SHAPE), over.keys()
 
 
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
 @pytest.mark.parametrize("kind", ["gradual", "fixed"])
-def test_layers_keeping_every_row_in_place(lib, kind):
+def test_layers_keeping_every_row_in_place(lib, kind, dt):
     """Layers where every recomputed row is kept leave the row maps as they
-    are and launch no selection when neither kept positions nor deviations
+    are, launch no selection and write their new K/V straight into the fused
+    cache from the q/k/v epilogue when neither kept positions nor deviations
     are asked for; the fusion is bit-identical to one that asks for them
-    (which runs the selection at every layer), and matches the oracle."""
+    (which runs the selection and the scatter at every layer), and matches
+    the oracle."""
     shape = ModelShape(5, 256, 4, 4, 64, 512, vocab=512)
-    case = make_case(shape, (100, 37, 160), 19, seed=6, dtype="bf16")
-    model = make_model(lib, case, "bf16")
+    case = make_case(shape, (100, 37, 160), 19, seed=6, dtype=dt)
+    model = make_model(lib, case, dt)
     sched = oracle.schedule(case.n_chunk_tokens, 1500, kind, shape.n_layers)
     assert any(a == b for a, b in zip(sched, sched[1:]))
-    full = run_gpu_blend(lib, model, case, "bf16", sched)
+    full = run_gpu_blend(lib, model, case, dt, sched)
     L, N = shape.n_layers, case.n_tokens
-    fk = torch.full((L, N, shape.n_kv_heads, shape.head_dim), float("nan"), dtype=torch.bfloat16,
+    fk = torch.full((L, N, shape.n_kv_heads, shape.head_dim), float("nan"), dtype=TORCH_DT[dt],
                     device="cuda")
     fv = torch.full_like(fk, float("nan"))
     hid = torch.full((case.n_suffix + sched[-1], shape.d_model), float("nan"), device="cuda")
     from tests.gpu_helpers import chunk_inputs
-    lib.cb_blend(model, chunk_inputs(case, "bf16"), case.offsets, case.n_suffix,
-                 dev(case.x0, "bf16"), fk, fv, hidden_out=hid, schedule=sched)
+    lib.cb_blend(model, chunk_inputs(case, dt), case.offsets, case.n_suffix,
+                 dev(case.x0, dt), fk, fv, hidden_out=hid, schedule=sched)
     torch.cuda.synchronize()
     assert torch.equal(fk, full["fused_k"]) and torch.equal(fv, full["fused_v"])
     assert torch.equal(hid, full["hidden"])
     # kept positions asked for without deviations: in-place layers get the
     # positions of the last layer that selected, copied after the last layer
     sel = torch.full((L, case.n_chunk_tokens), -1, dtype=torch.int32, device="cuda")
-    lib.cb_blend(model, chunk_inputs(case, "bf16"), case.offsets, case.n_suffix,
-                 dev(case.x0, "bf16"), fk, fv, sel_idx=sel, schedule=sched)
+    lib.cb_blend(model, chunk_inputs(case, dt), case.offsets, case.n_suffix,
+                 dev(case.x0, dt), fk, fv, sel_idx=sel, schedule=sched)
     torch.cuda.synchronize()
     for l in range(L):
         k = sched[l + 1]
         assert torch.equal(sel[l, :k], full["sel"][l, :k]), l
     assert torch.equal(fk, full["fused_k"]) and torch.equal(fv, full["fused_v"])
-    compare(case, full, sched, "bf16")
+    compare(case, full, sched, dt)
