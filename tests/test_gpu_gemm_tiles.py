@@ -8,7 +8,8 @@ gate/up products (Llama-2-7B shape) and the q/k/v, O and down products
 epilogue on that tile (RoPE at real positions on q/k/v tiles that straddle
 the q|k and k|v boundaries, SiLU(gate)*up on interleaved gate/up rows, the
 gathered residual) against the oracle's prefill.  A one-KV-head shape at
-4000 rows puts q, k and v in one 224x192 tile column range."""
+4000 rows puts q, k and v in one 224x192 tile column range.  A 16640-row
+prefill runs every epilogue on the 4-stage 256x256 kernel of long launches."""
 import dataclasses
 import gc
 import types
@@ -51,5 +52,42 @@ def test_prefill_projection_tiles_vs_oracle(lib, name, rows, pos0):
     assert rel_err(host(hid), outs[-1]) < 2e-2
     model.close()
     del model, k, v, hid
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+def test_long_prefill_four_stage_tiles(lib):
+    """Products of more than four rounds of 256x256 tiles take the 4-stage
+    kernel (gemm_big4_kernel): a one-layer prefill of 16640 rows at the
+    Llama-2-7B width runs its q/k/v + RoPE (65 x 48 tiles), O + residual and
+    down + residual (65 x 16) and gate/up + SwiGLU (65 x 86) products there.
+    Causality fixes the first 4096 rows to those of the 4096-row prefill of
+    the same tokens, whose products run the 5-stage kernel (one to three
+    rounds): same per-element accumulation order, so bit-identical.  The
+    4096-row prefill is compared with the oracle's."""
+    shape = dataclasses.replace(WORKLOADS["llama7b-4k"].shape, n_layers=1)
+    w = make_weights_np(shape, seed=4, dtype="bf16")
+    long_rows, short_rows = 16640, 4096
+    x = make_embedding_np(shape, seed=4, dtype="bf16")[make_tokens(shape, long_rows, seed=4)]
+    model = make_model(lib, types.SimpleNamespace(shape=shape, weights=w), "bf16")
+    out = {}
+    for rows in (long_rows, short_rows):
+        k = torch.empty((1, rows, shape.n_kv_heads, shape.head_dim), dtype=torch.bfloat16,
+                        device="cuda")
+        v = torch.empty_like(k)
+        hid = torch.empty((rows, shape.d_model), device="cuda")
+        lib.cb_prefill(model, dev(x[:rows], "bf16"), rows, 0, k, v, hid)
+        torch.cuda.synchronize()
+        out[rows] = (k, v, hid)
+    kl, vl, hl = out[long_rows]
+    ks, vs, hs = out[short_rows]
+    assert torch.equal(kl[:, :short_rows], ks) and torch.equal(vl[:, :short_rows], vs)
+    assert torch.equal(hl[:short_rows], hs)
+    rk, rv, outs = oracle.prefill(w, shape, x[:short_rows], pos0=0, dtype=np.float32)
+    assert rel_err(host(ks), rk) < 2e-2
+    assert rel_err(host(vs), rv) < 2e-2
+    assert rel_err(host(hs), outs[-1]) < 2e-2
+    model.close()
+    del model, out, kl, vl, hl, ks, vs, hs
     gc.collect()
     torch.cuda.empty_cache()
