@@ -692,27 +692,30 @@ cb_status do_layer(cb_plan* p, int l) {
     const bool measure = lr.nC > 0 && (lr.select_needed || p->deviation);
     const bool in_place =
         !lr.select_needed && !(measure && p->deviation) && (!p->sel_idx || l > 0);
-    // 2. QKV projection with RoPE at the real positions.  In place, K and V
-    // go straight to their rows of fused[l] (every recomputed row is kept),
-    // after this layer's fetch has written the rotated cache there; otherwise
-    // they go to the work rows and steps 1-2 overlap the fetch.
-    if (in_place) CB_HIP(hipStreamWaitEvent(st, p->fetched[l], 0));
+    // 2. QKV projection with RoPE at the real positions.  In place, with
+    // every chunk in device memory, K and V go straight to their rows of
+    // fused[l] (every recomputed row is kept), after this layer's fetch has
+    // written the rotated cache there (device fetches run ahead and are long
+    // done).  Otherwise they go to the work rows and steps 1-2 overlap the
+    // fetch: chunks copied from host memory may still be arriving.
+    const bool direct_kv = in_place && p->h2d.empty() && p->qh2d.empty() && p->stage_copies.empty();
+    if (direct_kv) CB_HIP(hipStreamWaitEvent(st, p->fetched[l], 0));
     {
         GemmArgs g{};
         g.a = p->Hn; g.b0 = w.wq; g.b1 = w.wk; g.b2 = w.wv;
         g.n0 = m->qd(); g.n1 = m->kvd();
         g.M = mR; g.N = m->qd() + 2 * m->kvd(); g.K = c.d_model;
         g.out0 = p->Q;
-        g.out1 = in_place ? fk : p->Kn;
-        g.out2 = in_place ? fv : p->Vn;
-        g.kv_rows = in_place ? row_r : nullptr;
+        g.out1 = direct_kv ? fk : p->Kn;
+        g.out2 = direct_kv ? fv : p->Vn;
+        g.kv_rows = direct_kv ? row_r : nullptr;
         g.pos = pos_r; g.rope = m->rope; g.head_dim = c.head_dim;
         const double n = g.N;
         Span sp(m, CB_K_GEMM_QKV, st, 2.0 * mR * n * d, (mR * d + n * d + mR * n) * es);
         CB_HIP(launch_gemm(dt, EPI_QKV, g, st));
     }
     // fused[l] is first read below
-    if (!in_place) CB_HIP(hipStreamWaitEvent(st, p->fetched[l], 0));
+    if (!direct_kv) CB_HIP(hipStreamWaitEvent(st, p->fetched[l], 0));
     // 3-4. deviation of the recomputed chunk rows against the rotated cache,
     // then per request: keep the top s[l+1] chunk rows, then the suffix rows.
     const int* qmap = p->sel_local;     // query row -> recomputed row (null: identity)
@@ -780,8 +783,8 @@ cb_status do_layer(cb_plan* p, int l) {
                                      dev_out, st));
         }
     }
-    // 5. merge the kept rows' K/V into the fused cache (in place: done by step 2)
-    if (!in_place) {
+    // 5. merge the kept rows' K/V into the fused cache (done by step 2 if direct)
+    if (!direct_kv) {
         Span sp(m, CB_K_SCATTER, st, 0, 4.0 * mQ * kvd * es);
         CB_HIP(launch_scatter_kv(dt, p->Kn, p->Vn, qmap, row_q, fk, fv, mQ, m->kvd(), st));
     }
