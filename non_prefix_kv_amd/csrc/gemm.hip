@@ -463,21 +463,35 @@ __device__ __forceinline__ void epilogue_finish(const GemmArgs& g, int m_tile, i
             rope = false;
         }
         const int hd = local % g.head_dim;         // multiple of 4: pairs (hd, hd+1), (hd+2, hd+3)
-#pragma unroll 4
+        // positions and output rows of all the thread's rows, then their
+        // RoPE factors, before the first store (two dependent round trips)
+        int pr[NP], orow[NP];
+        floatx4 cs[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int row = row0 + RS * p;
+            pr[p] = row < g.M && rope ? g.pos[row] : 0;
+            orow[p] = row < g.M ? (int)qkv_out_row(g, row, kv) : 0;
+        }
+        if (rope) {
+#pragma unroll
+            for (int p = 0; p < NP; ++p)
+                cs[p] = *reinterpret_cast<const floatx4*>(
+                    &g.rope.tab[(int64_t)pr[p] * g.rope.half + (hd >> 1)]);
+        }
+#pragma unroll
         for (int p = 0; p < NP; ++p) {
             const int rl = t / 32 + RS * p, row = row0 + RS * p;
             if (row >= g.M) break;
             const floatx4 x = *reinterpret_cast<const floatx4*>(&lds[rl * kEpiLd + cc]);
             floatx4 y = x;
             if (rope) {
-                const floatx4 cs = *reinterpret_cast<const floatx4*>(
-                    &g.rope.tab[(int64_t)g.pos[row] * g.rope.half + (hd >> 1)]);
-                y[0] = x[0] * cs[0] - x[1] * cs[1];
-                y[1] = x[0] * cs[1] + x[1] * cs[0];
-                y[2] = x[2] * cs[2] - x[3] * cs[3];
-                y[3] = x[2] * cs[3] + x[3] * cs[2];
+                y[0] = x[0] * cs[p][0] - x[1] * cs[p][1];
+                y[1] = x[0] * cs[p][1] + x[1] * cs[p][0];
+                y[2] = x[2] * cs[p][2] - x[3] * cs[p][3];
+                y[3] = x[2] * cs[p][3] + x[3] * cs[p][2];
             }
-            *reinterpret_cast<bf16x4*>(base + qkv_out_row(g, row, kv) * width + local) =
+            *reinterpret_cast<bf16x4*>(base + (int64_t)orow[p] * width + local) =
                 bf16x4{static_cast<bf16>(y[0]), static_cast<bf16>(y[1]), static_cast<bf16>(y[2]),
                        static_cast<bf16>(y[3])};
         }
@@ -485,6 +499,29 @@ __device__ __forceinline__ void epilogue_finish(const GemmArgs& g, int m_tile, i
     }
     // STORE_F32 / RESID: fp32 rows; vector path when the row length allows
     const bool vec = (g.N % 4) == 0;
+    if (EPI == EPI_RESID && vec && col + 3 < g.N) {
+        // residual row indices of all the thread's rows, then the residual
+        // values, before the first store (two dependent round trips)
+        int rr[NP];
+        floatx4 rv[NP];
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int row = row0 + RS * p;
+            rr[p] = row < g.M ? (g.ridx ? g.ridx[row] : row) : -1;
+        }
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+            rv[p] = rr[p] >= 0 ? *reinterpret_cast<const floatx4*>(g.resid + (int64_t)rr[p] * g.N + col)
+                               : floatx4{};
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int rl = t / 32 + RS * p, row = row0 + RS * p;
+            if (row >= g.M) break;
+            const floatx4 y = *reinterpret_cast<const floatx4*>(&lds[rl * kEpiLd + cc]) + rv[p];
+            *reinterpret_cast<floatx4*>(static_cast<float*>(g.out0) + (int64_t)row * g.N + col) = y;
+        }
+        return;
+    }
 #pragma unroll 4
     for (int p = 0; p < NP; ++p) {
         const int rl = t / 32 + RS * p, row = row0 + RS * p;
@@ -788,43 +825,81 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs& g, const floatx16 (
                     local = col - g.n0 - g.n1; rope = false;
                 }
                 const int hd = local % g.head_dim;
-#pragma unroll 4
+                // positions and output rows of the thread's 16 rows, then
+                // their RoPE factors, before the first store
+                int pr[16], orow[16];
+                floatx4 cs[16];
+#pragma unroll
+                for (int p = 0; p < 16; ++p) {
+                    const int row = row0 + 4 * p;
+                    pr[p] = row < g.M && rope ? g.pos[row] : 0;
+                    orow[p] = row < g.M ? (int)qkv_out_row(g, row, kv) : 0;
+                }
+                if (rope) {
+#pragma unroll
+                    for (int p = 0; p < 16; ++p)
+                        cs[p] = *reinterpret_cast<const floatx4*>(
+                            &g.rope.tab[(int64_t)pr[p] * g.rope.half + (hd >> 1)]);
+                }
+#pragma unroll
                 for (int p = 0; p < 16; ++p) {
                     const int rl = t / 64 + 4 * p, row = row0 + 4 * p;
                     if (row < g.M) {
                         const floatx4 x = *reinterpret_cast<const floatx4*>(&lds[rl * kBigLd + cc]);
                         floatx4 y = x;
                         if (rope) {
-                            const floatx4 cs = *reinterpret_cast<const floatx4*>(
-                                &g.rope.tab[(int64_t)g.pos[row] * g.rope.half + (hd >> 1)]);
-                            y[0] = x[0] * cs[0] - x[1] * cs[1];
-                            y[1] = x[0] * cs[1] + x[1] * cs[0];
-                            y[2] = x[2] * cs[2] - x[3] * cs[3];
-                            y[3] = x[2] * cs[3] + x[3] * cs[2];
+                            y[0] = x[0] * cs[p][0] - x[1] * cs[p][1];
+                            y[1] = x[0] * cs[p][1] + x[1] * cs[p][0];
+                            y[2] = x[2] * cs[p][2] - x[3] * cs[p][3];
+                            y[3] = x[2] * cs[p][3] + x[3] * cs[p][2];
                         }
-                        *reinterpret_cast<bf16x4*>(base + qkv_out_row(g, row, kv) * width + local) =
+                        *reinterpret_cast<bf16x4*>(base + (int64_t)orow[p] * width + local) =
                             bf16x4{static_cast<bf16>(y[0]), static_cast<bf16>(y[1]),
                                    static_cast<bf16>(y[2]), static_cast<bf16>(y[3])};
                     }
                 }
             } else {
                 const bool vec = (g.N % 4) == 0;
-#pragma unroll 4
-                for (int p = 0; p < 16; ++p) {
-                    const int rl = t / 64 + 4 * p, row = row0 + 4 * p;
-                    if (row < g.M) {
-                        floatx4 y = *reinterpret_cast<const floatx4*>(&lds[rl * kBigLd + cc]);
-                        float* dst = static_cast<float*>(g.out0) + (int64_t)row * g.N + col;
-                        const float* res = nullptr;
-                        if (EPI == EPI_RESID)
-                            res = g.resid + (int64_t)(g.ridx ? g.ridx[row] : row) * g.N + col;
-                        if (vec && col + 3 < g.N) {
-                            if (EPI == EPI_RESID) y += *reinterpret_cast<const floatx4*>(res);
-                            *reinterpret_cast<floatx4*>(dst) = y;
-                        } else {
+                if (EPI == EPI_RESID && vec && col + 3 < g.N) {
+                    // residual row indices of the thread's 16 rows, then
+                    // the residual values, before the first store
+                    int rr[16];
+                    floatx4 rv[16];
 #pragma unroll
-                            for (int k = 0; k < 4; ++k)
-                                if (col + k < g.N) dst[k] = y[k] + (EPI == EPI_RESID ? res[k] : 0.f);
+                    for (int p = 0; p < 16; ++p) {
+                        const int row = row0 + 4 * p;
+                        rr[p] = row < g.M ? (g.ridx ? g.ridx[row] : row) : -1;
+                    }
+#pragma unroll
+                    for (int p = 0; p < 16; ++p)
+                        rv[p] = rr[p] >= 0
+                                    ? *reinterpret_cast<const floatx4*>(g.resid + (int64_t)rr[p] * g.N + col)
+                                    : floatx4{};
+#pragma unroll
+                    for (int p = 0; p < 16; ++p) {
+                        const int rl = t / 64 + 4 * p, row = row0 + 4 * p;
+                        if (row < g.M)
+                            *reinterpret_cast<floatx4*>(static_cast<float*>(g.out0) + (int64_t)row * g.N + col) =
+                                *reinterpret_cast<const floatx4*>(&lds[rl * kBigLd + cc]) + rv[p];
+                    }
+                } else {
+#pragma unroll 4
+                    for (int p = 0; p < 16; ++p) {
+                        const int rl = t / 64 + 4 * p, row = row0 + 4 * p;
+                        if (row < g.M) {
+                            floatx4 y = *reinterpret_cast<const floatx4*>(&lds[rl * kBigLd + cc]);
+                            float* dst = static_cast<float*>(g.out0) + (int64_t)row * g.N + col;
+                            const float* res = nullptr;
+                            if (EPI == EPI_RESID)
+                                res = g.resid + (int64_t)(g.ridx ? g.ridx[row] : row) * g.N + col;
+                            if (vec && col + 3 < g.N) {
+                                if (EPI == EPI_RESID) y += *reinterpret_cast<const floatx4*>(res);
+                                *reinterpret_cast<floatx4*>(dst) = y;
+                            } else {
+#pragma unroll
+                                for (int k = 0; k < 4; ++k)
+                                    if (col + k < g.N) dst[k] = y[k] + (EPI == EPI_RESID ? res[k] : 0.f);
+                            }
                         }
                     }
                 }
@@ -1283,27 +1358,71 @@ __device__ __forceinline__ void mid_finish(const GemmArgs& g, int row0, int n_ti
             local = col - g.n0 - g.n1; rope = false;
         }
         const int pair = (local % g.head_dim) >> 1;   // even: pairs (pair, pair + 1)
-#pragma unroll 4
-        for (int rl = t / 48; rl < 112; rl += 5) {
-            const int row = row0 + rl;
-            if (row >= g.M) break;
+        // The thread's rows rl = t / 48 + 5 i < 112.  Their positions and
+        // output rows, then their RoPE factors, are all loaded before the
+        // first store: two dependent round trips per half tile instead of
+        // two or three per group of rows.
+        constexpr int NR = 23;
+        const int r0 = t / 48;
+        int pr[NR], orow[NR];
+        floatx4 cs[NR];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int rl = r0 + 5 * i, row = row0 + rl;
+            const bool ok = rl < 112 && row < g.M;
+            pr[i] = ok && rope ? g.pos[row] : 0;
+            orow[i] = ok ? (int)qkv_out_row(g, row, kv) : 0;
+        }
+        if (rope) {
+#pragma unroll
+            for (int i = 0; i < NR; ++i)
+                cs[i] = *reinterpret_cast<const floatx4*>(
+                    &g.rope.tab[(int64_t)pr[i] * g.rope.half + pair]);
+        }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int rl = r0 + 5 * i, row = row0 + rl;
+            if (rl >= 112 || row >= g.M) break;
             const floatx4 x = *reinterpret_cast<const floatx4*>(&lds[rl * kMidLd + cg]);
             floatx4 y = x;
             if (rope) {
-                const floatx4 cs = *reinterpret_cast<const floatx4*>(
-                    &g.rope.tab[(int64_t)g.pos[row] * g.rope.half + pair]);
-                y[0] = x[0] * cs[0] - x[1] * cs[1];
-                y[1] = x[0] * cs[1] + x[1] * cs[0];
-                y[2] = x[2] * cs[2] - x[3] * cs[3];
-                y[3] = x[2] * cs[3] + x[3] * cs[2];
+                y[0] = x[0] * cs[i][0] - x[1] * cs[i][1];
+                y[1] = x[0] * cs[i][1] + x[1] * cs[i][0];
+                y[2] = x[2] * cs[i][2] - x[3] * cs[i][3];
+                y[3] = x[2] * cs[i][3] + x[3] * cs[i][2];
             }
-            *reinterpret_cast<bf16x4*>(base + qkv_out_row(g, row, kv) * width + local) =
+            *reinterpret_cast<bf16x4*>(base + (int64_t)orow[i] * width + local) =
                 bf16x4{static_cast<bf16>(y[0]), static_cast<bf16>(y[1]), static_cast<bf16>(y[2]),
                        static_cast<bf16>(y[3])};
         }
         return;
     }
     const bool vec = (g.N % 4) == 0 && col + 3 < g.N;
+    if (EPI == EPI_RESID && vec) {
+        // residual row indices of the thread's rows t / 48 + 5 i < 112, then
+        // the residual values, before the first store
+        constexpr int NR = 23;
+        const int r0 = t / 48;
+        int rr[NR];
+        floatx4 rv[NR];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int rl = r0 + 5 * i, row = row0 + rl;
+            rr[i] = rl < 112 && row < g.M ? (g.ridx ? g.ridx[row] : row) : -1;
+        }
+#pragma unroll
+        for (int i = 0; i < NR; ++i)
+            rv[i] = rr[i] >= 0 ? *reinterpret_cast<const floatx4*>(g.resid + (int64_t)rr[i] * g.N + col)
+                               : floatx4{};
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int rl = r0 + 5 * i, row = row0 + rl;
+            if (rl >= 112 || row >= g.M) break;
+            *reinterpret_cast<floatx4*>(static_cast<float*>(g.out0) + (int64_t)row * g.N + col) =
+                *reinterpret_cast<const floatx4*>(&lds[rl * kMidLd + cg]) + rv[i];
+        }
+        return;
+    }
 #pragma unroll 4
     for (int rl = t / 48; rl < 112; rl += 5) {
         const int row = row0 + rl;
