@@ -290,6 +290,14 @@ __device__ __forceinline__ float vmax3(float a, float b, float c) {
     return fmaxf(fmaxf(a, b), c);
 }
 
+// max(x, x of lane ^ 32): the wave's two halves exchanged by a VALU permute
+// (v_permlane32_swap: lanes 32-63 of the first operand trade places with
+// lanes 0-31 of the second, here both x) instead of an LDS-routed shuffle.
+__device__ __forceinline__ float max_xor32(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 constexpr int kT32 = 256;   // threads per workgroup (4 waves)
 constexpr int QT32 = 128;   // queries per workgroup
 constexpr int KBL = 64;     // keys per block
@@ -407,14 +415,9 @@ __global__ __launch_bounds__(kT32, 2) void attention64_kernel(AttnArgs a, const 
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[t][i] = 0.f;
     float m_run = -INFINITY;
-    // Softmax denominators: every row of lacc holds the sum of the probabilities
-    // of the lane's query (the P.V MFMA against a ones operand).
-    floatx16 lacc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) lacc[i] = 0.f;
-    bf16x8 ones;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) ones[j] = static_cast<bf16>(1.0f);
+    // Softmax denominator: the lane's share of its query's probabilities
+    // (lanes l and l + 32 hold the two halves of every key block).
+    float l_part = 0.f;
     const float sl2 = 1.4426950408889634f / sqrtf((float)D);
 
     const bf16* kbase = static_cast<const bf16*>(a.k) + (int64_t)tile.g0 * kv_ld + hk * D;
@@ -502,7 +505,7 @@ __global__ __launch_bounds__(kT32, 2) void attention64_kernel(AttnArgs a, const 
 #pragma unroll
         for (int i = 1; i < 16; ++i)
             mloc = i == 1 ? vmax3(mloc, s2[1][1], s2[1][1]) : vmax3(mloc, s2[0][i], s2[1][i]);
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64)) * sl2;
+        mloc = max_xor32(mloc) * sl2;
         // The reference maximum only moves when a score exceeds it by more
         // than kLazyLog2 (probabilities then stay below 2^kLazyLog2): after
         // the first keys O and l are rarely rescaled.  Any reference gives
@@ -513,16 +516,17 @@ __global__ __launch_bounds__(kT32, 2) void attention64_kernel(AttnArgs a, const 
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         if (__ballot(grow)) {
             const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-            lacc *= alpha;
+            l_part *= alpha;
 #pragma unroll
             for (int t = 0; t < NDT; ++t) o[t] *= alpha;
         }
         m_run = m_new;
         // Per 16-key group q4: its transposed V reads first (they do not
-        // depend on P), then the group's probabilities, then one MFMA per
-        // 32-dim output tile (independent accumulators) and one more against
-        // a ones operand, which adds the group's probabilities of each query
-        // (the softmax denominator, from the same rounded P as the numerator).
+        // depend on P), then the group's probabilities, added to the lane's
+        // share of the denominator in fp32 before their rounding to bf16 for
+        // the MFMAs (the two differ by the mean rounding error of the
+        // probabilities, a relative 2^-9 / sqrt(keys)), then one MFMA per
+        // 32-dim output tile (independent accumulators).
         // P^T slot j of group q4 = 2 hh + j / 8 holds key
         // 32 hh + 16 (j / 8) + 8 ((j % 8) / 4) + 4 g + j % 4: the key order
         // of the transposed V reads.
@@ -543,12 +547,13 @@ __global__ __launch_bounds__(kT32, 2) void attention64_kernel(AttnArgs a, const 
             }
             bf16x8 pf;
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                pf[j] = static_cast<bf16>(__builtin_amdgcn_exp2f(
-                    fmaf(s2[q4 >> 1][(q4 & 1) * 8 + j], sl2, -m_use)));
+            for (int j = 0; j < 8; ++j) {
+                const float e = __builtin_amdgcn_exp2f(fmaf(s2[q4 >> 1][(q4 & 1) * 8 + j], sl2, -m_use));
+                l_part += e;
+                pf[j] = static_cast<bf16>(e);
+            }
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) mfma32(o[dt], vf[dt], pf);
-            mfma32(lacc, ones, pf);
         }
     };
     // Two stages: block kb+1 is copied into the other stage while block kb is
@@ -566,7 +571,7 @@ __global__ __launch_bounds__(kT32, 2) void attention64_kernel(AttnArgs a, const 
         __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));   // vmcnt(0)
         __syncthreads();
     }
-    const float l_tot = lacc[0];
+    const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
     if (n_seg > 1) {
         // Partial of this segment: O normalized by the segment's own sum (bf16,
         // half the bytes of the unnormalized float sums), running max (log2
