@@ -137,13 +137,16 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_vec_kernel(
     __shared__ float red[kThreads / 64];
     const int r = blockIdx.x;
     const TX* xr = x + (int64_t)(idx ? idx[r] : r) * d;
-    float v[MAXV][8];
+    float v[MAXV][8], gv[MAXV][8];
     float ss = 0.f;
+    // the gains are loaded with the row, before the block-wide sum, so that
+    // the sum's barrier is the only wait between the loads and the stores
 #pragma unroll
     for (int k = 0; k < MAXV; ++k) {
         const int c = (k * kThreads + threadIdx.x) * 8;
         if (c < d) {
             Vec8<TX>::load(xr + c, v[k]);
+            Vec8<TY>::load(g + c, gv[k]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) ss += v[k][i] * v[k][i];
         }
@@ -156,10 +159,9 @@ __global__ __launch_bounds__(kThreads) void rmsnorm_vec_kernel(
     for (int k = 0; k < MAXV; ++k) {
         const int c = (k * kThreads + threadIdx.x) * 8;
         if (c < d) {
-            float gv[8], o[8];
-            Vec8<TY>::load(g + c, gv);
+            float o[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) o[i] = v[k][i] * inv * gv[i];
+            for (int i = 0; i < 8; ++i) o[i] = v[k][i] * inv * gv[k][i];
             Vec8<TY>::store(yr + c, o);
             if (xcr) Vec8<float>::store(xcr + c, v[k]);
         }
