@@ -22,105 +22,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr int kSegKeys = 64;               // keys per decode-attention workgroup
-
-// Two dot products of length K between x and weight rows wa, wb (a pair of
-// output columns, or the gate and up rows of one SwiGLU column), taken by
-// WPU waves together: wave `part` of them reads the 512-element pieces
-// part, part + WPU, ... of the rows.  Returns the wave's partial sums.
-template <typename T, int WPU>
-__device__ __forceinline__ void dot2(const T* __restrict__ x, const T* __restrict__ wa,
-                                     const T* __restrict__ wb, int K, int lane, int part,
-                                     float& sa, float& sb) {
-    float a = 0.f, b = 0.f;
-#pragma unroll 4
-    for (int k = part * 512 + lane * 8; k < K; k += 512 * WPU) {
-        float xv[8], av[8], bv[8];
-        Vec8<T>::load(x + k, xv);
-        Vec8<T>::load(wa + k, av);
-        if (wb) Vec8<T>::load(wb + k, bv);
-        else
-#pragma unroll
-            for (int i = 0; i < 8; ++i) bv[i] = 0.f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            a += xv[i] * av[i];
-            b += xv[i] * bv[i];
-        }
-    }
-    sa = warp_sum(a);
-    sb = warp_sum(b);
-}
-
-// A workgroup of 4 waves computes 4 / WPU units (WPU waves per unit, which
-// split K); a unit is a pair of output rows, or one SwiGLU column.  The
-// launcher uses WPU = 4 for every shape.
-template <typename T, int EPI, int WPU>
-__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
-    __shared__ float part_s[kWaves][2];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int u = blockIdx.x * (kWaves / WPU) + wave / WPU, part = wave % WPU;
-    const int units = EPI == EPI_SWIGLU ? g.N : (g.N + 1) / 2;
-    const bool live = u < units;
-    const T* x = static_cast<const T*>(g.x);
-    const int64_t K = g.K;
-    const T* wa = nullptr;
-    const T* wb = nullptr;
-    int local = 0;
-    void* out = nullptr;
-    bool rope = false, two = true;
-    if (live) {
-        if constexpr (EPI == EPI_SWIGLU) {
-            wa = static_cast<const T*>(g.b0) + u * K;
-            wb = static_cast<const T*>(g.b1) + u * K;
-        } else {
-            const int r0 = 2 * u;
-            two = r0 + 1 < g.N;
-            const T* w;
-            if (EPI == EPI_QKV && r0 >= g.n0 + g.n1) {
-                w = static_cast<const T*>(g.b2); local = r0 - g.n0 - g.n1; out = g.out2;
-            } else if (EPI == EPI_QKV && r0 >= g.n0) {
-                w = static_cast<const T*>(g.b1); local = r0 - g.n0; out = g.out1; rope = true;
-            } else {
-                w = static_cast<const T*>(g.b0); local = r0; out = g.out0; rope = EPI == EPI_QKV;
-            }
-            wa = w + local * K;
-            wb = two ? w + (local + 1) * K : nullptr;
-        }
-    }
-    float a = 0.f, b = 0.f;
-    if (live) dot2<T, WPU>(x, wa, wb, g.K, lane, part, a, b);
-    if constexpr (WPU > 1) {
-        if (lane == 0) { part_s[wave][0] = a; part_s[wave][1] = b; }
-        __syncthreads();
-        if (part != 0) return;
-        for (int p = 1; p < WPU; ++p) {
-            a += part_s[wave + p][0];
-            b += part_s[wave + p][1];
-        }
-    }
-    if (!live || lane != 0) return;
-    if constexpr (EPI == EPI_SWIGLU) {
-        static_cast<T*>(g.out0)[u] = from_f32<T>(a / (1.f + __expf(-a)) * b);
-    } else if constexpr (EPI == EPI_QKV) {
-        float y0 = a, y1 = b;
-        if (rope) {
-            const float2 cs = g.rope.tab[(int64_t)g.pos * g.rope.half + ((local % g.head_dim) >> 1)];
-            y0 = a * cs.x - b * cs.y;
-            y1 = a * cs.y + b * cs.x;
-        }
-        static_cast<T*>(out)[local] = from_f32<T>(y0);
-        static_cast<T*>(out)[local + 1] = from_f32<T>(y1);
-    } else {
-        const int r0 = 2 * u;
-        float* o = static_cast<float*>(g.out0);
-        if (EPI == EPI_RESID) {
-            a += g.resid[r0];
-            if (two) b += g.resid[r0 + 1];
-        }
-        o[r0] = a;
-        if (two) o[r0 + 1] = b;
-    }
-}
+constexpr int kGemvUnits = 1;              // output units per GEMV wave group
 
 // Order of the argmax: larger first, NaN above everything, smaller index
 // first among equals (so the result is unique).
@@ -190,6 +92,131 @@ __device__ __forceinline__ float wave_reduce(float v) {
     const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
     const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
     return MAX ? fmaxf(fmaxf(r0, r1), fmaxf(r2, r3)) : (r0 + r1) + (r2 + r3);
+}
+
+// R dot products of length K between x and weight rows w[0..R-1] (a null
+// row reads as zero), taken by WPU waves together: wave `part` of them reads
+// the 512-element pieces part, part + WPU, ... of the rows, each piece of x
+// once for all R rows.  Returns the whole products in every lane of a wave
+// when WPU = 1, else the wave's partial sums.
+template <typename T, int WPU, int R>
+__device__ __forceinline__ void dot_rows(const T* __restrict__ x, const T* const (&w)[R], int K,
+                                         int lane, int part, float (&s)[R]) {
+    // a group past the last unit loads nothing; in a live group (its first
+    // row is live) a null row reads the first row instead, with no branch
+    // between the loads, and its sum is dropped at the end
+    if (!w[0]) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) s[r] = 0.f;
+        return;
+    }
+    const T* wr[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) wr[r] = w[r] ? w[r] : w[0];
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = 0.f;
+#pragma unroll 2
+    for (int k = part * 512 + lane * 8; k < K; k += 512 * WPU) {
+        float xv[8], wv[R][8];
+        Vec8<T>::load(x + k, xv);
+#pragma unroll
+        for (int r = 0; r < R; ++r) Vec8<T>::load(wr[r] + k, wv[r]);
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[r] += xv[i] * wv[r][i];
+    }
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = w[r] ? wave_reduce<false>(acc[r]) : 0.f;
+}
+
+// A workgroup of 4 waves computes 4 / WPU groups of U units (WPU waves per
+// group, which split K); a unit is a pair of output rows, or one SwiGLU
+// column.  The U units of a group share every load of x.
+template <typename T, int EPI, int WPU, int U>
+__global__ __launch_bounds__(kThreads) void gemv_kernel(GemvArgs g) {
+    constexpr int R = 2 * U;
+    __shared__ float part_s[kWaves][R];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int grp = blockIdx.x * (kWaves / WPU) + wave / WPU, part = wave % WPU;
+    const int units = EPI == EPI_SWIGLU ? g.N : (g.N + 1) / 2;
+    const T* x = static_cast<const T*>(g.x);
+    const int64_t K = g.K;
+    const T* w[R];
+    int local[U];
+    void* out[U];
+    bool rope[U], two[U], live[U];
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        const int u = grp * U + j;
+        live[j] = u < units;
+        w[2 * j] = w[2 * j + 1] = nullptr;
+        local[j] = 0;
+        out[j] = nullptr;
+        rope[j] = false;
+        two[j] = true;
+        if (!live[j]) continue;
+        if constexpr (EPI == EPI_SWIGLU) {
+            w[2 * j] = static_cast<const T*>(g.b0) + u * K;
+            w[2 * j + 1] = static_cast<const T*>(g.b1) + u * K;
+        } else {
+            const int r0 = 2 * u;
+            two[j] = r0 + 1 < g.N;
+            const T* m;
+            if (EPI == EPI_QKV && r0 >= g.n0 + g.n1) {
+                m = static_cast<const T*>(g.b2); local[j] = r0 - g.n0 - g.n1; out[j] = g.out2;
+            } else if (EPI == EPI_QKV && r0 >= g.n0) {
+                m = static_cast<const T*>(g.b1); local[j] = r0 - g.n0; out[j] = g.out1; rope[j] = true;
+            } else {
+                m = static_cast<const T*>(g.b0); local[j] = r0; out[j] = g.out0; rope[j] = EPI == EPI_QKV;
+            }
+            w[2 * j] = m + local[j] * K;
+            w[2 * j + 1] = two[j] ? m + (local[j] + 1) * K : nullptr;
+        }
+    }
+    float s[R];
+    dot_rows<T, WPU, R>(x, w, g.K, lane, part, s);
+    if constexpr (WPU > 1) {
+        if (lane == 0)
+#pragma unroll
+            for (int r = 0; r < R; ++r) part_s[wave][r] = s[r];
+        __syncthreads();
+        if (part != 0) return;
+#pragma unroll
+        for (int p = 1; p < WPU; ++p)
+#pragma unroll
+            for (int r = 0; r < R; ++r) s[r] += part_s[wave + p][r];
+    }
+    // lane j stores unit j
+#pragma unroll
+    for (int j = 0; j < U; ++j) {
+        if (lane != j || !live[j]) continue;
+        const float a = s[2 * j], b = s[2 * j + 1];
+        const int u = grp * U + j;
+        if constexpr (EPI == EPI_SWIGLU) {
+            static_cast<T*>(g.out0)[u] = from_f32<T>(a / (1.f + __expf(-a)) * b);
+        } else if constexpr (EPI == EPI_QKV) {
+            float y0 = a, y1 = b;
+            if (rope[j]) {
+                const float2 cs = g.rope.tab[(int64_t)g.pos * g.rope.half + ((local[j] % g.head_dim) >> 1)];
+                y0 = a * cs.x - b * cs.y;
+                y1 = a * cs.y + b * cs.x;
+            }
+            static_cast<T*>(out[j])[local[j]] = from_f32<T>(y0);
+            static_cast<T*>(out[j])[local[j] + 1] = from_f32<T>(y1);
+        } else {
+            const int r0 = 2 * u;
+            float* o = static_cast<float*>(g.out0);
+            float y0 = a, y1 = b;
+            if (EPI == EPI_RESID) {
+                y0 += g.resid[r0];
+                if (two[j]) y1 += g.resid[r0 + 1];
+            }
+            o[r0] = y0;
+            if (two[j]) o[r0 + 1] = y1;
+        }
+    }
 }
 
 // Split-key attention of one query row (all query heads) over n_ctx cached
@@ -525,8 +552,11 @@ hipError_t gemv_e(const GemvArgs& g, int units, hipStream_t s) {
     // K split over the 4 waves of a workgroup for every shape: short waves
     // leave a short tail when the last ones finish (measured on MI355X, 7B
     // decode step: 2.75 ms of GEMVs with 4 waves per unit, 2.86 with 2, 2.96
-    // with 1 for the products of >= 8192 units)
-    hipLaunchKernelGGL((gemv_kernel<T, EPI, 4>), dim3(units), dim3(kThreads), 0, s, g);
+    // with 1 for the products of >= 8192 units).  One unit per workgroup:
+    // 2.62 ms, against 2.88 with two units sharing the loads of x and 4.97
+    // with four (fewer, longer workgroups keep fewer bytes in flight)
+    hipLaunchKernelGGL((gemv_kernel<T, EPI, 4, kGemvUnits>), dim3((units + kGemvUnits - 1) / kGemvUnits),
+                       dim3(kThreads), 0, s, g);
     return hipGetLastError();
 }
 
