@@ -97,6 +97,13 @@ template <> struct Vec8<bf16> {
     static __device__ __forceinline__ void copy(const bf16* s, bf16* d) {
         *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(s);
     }
+    // with the non-temporal hint: rows written once and not read again soon
+    static __device__ __forceinline__ void store_nt(bf16* p, const float* x) {
+        bf16x8 v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = static_cast<bf16>(x[i]);
+        __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+    }
 };
 template <> struct Vec8<float> {
     static __device__ __forceinline__ void load(const float* p, float* x) {
@@ -112,6 +119,10 @@ template <> struct Vec8<float> {
     static __device__ __forceinline__ void copy(const float* s, float* d) {
         *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(s);
         *reinterpret_cast<u32x4*>(d + 4) = *reinterpret_cast<const u32x4*>(s + 4);
+    }
+    static __device__ __forceinline__ void store_nt(float* p, const float* x) {
+        __builtin_nontemporal_store(floatx4{x[0], x[1], x[2], x[3]}, reinterpret_cast<floatx4*>(p));
+        __builtin_nontemporal_store(floatx4{x[4], x[5], x[6], x[7]}, reinterpret_cast<floatx4*>(p + 4));
     }
 };
 

@@ -53,12 +53,15 @@ __global__ __launch_bounds__(kThreads) void rerotate_kernel(
         y[2 * p] = x[2 * p] * cs.x - x[2 * p + 1] * sn;
         y[2 * p + 1] = x[2 * p] * sn + x[2 * p + 1] * cs.x;
     }
-    Vec8<T>::store(kd + d_off, y);
+    // the fused rows are read again only by later layers' kernels: written
+    // with the non-temporal hint, like the chunk rows are read
+    Vec8<T>::store_nt(kd + d_off, y);
     if (j.v_src) {
         const u32x4* vs = reinterpret_cast<const u32x4*>(static_cast<const T*>(j.v_src) + s_off);
         u32x4* vo = reinterpret_cast<u32x4*>(vd + d_off);
 #pragma unroll
-        for (int w = 0; w < (int)sizeof(T) / 2; ++w) vo[w] = __builtin_nontemporal_load(vs + w);
+        for (int w = 0; w < (int)sizeof(T) / 2; ++w)
+            __builtin_nontemporal_store(__builtin_nontemporal_load(vs + w), vo + w);
     }
 }
 
