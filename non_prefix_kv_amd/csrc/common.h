@@ -97,6 +97,12 @@ template <> struct Vec8<bf16> {
     static __device__ __forceinline__ void copy(const bf16* s, bf16* d) {
         *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(s);
     }
+    // with the non-temporal hint: rows read once in a pass
+    static __device__ __forceinline__ void load_nt(const bf16* p, float* x) {
+        const bf16x8 v = __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = static_cast<float>(v[i]);
+    }
     // with the non-temporal hint: rows written once and not read again soon
     static __device__ __forceinline__ void store_nt(bf16* p, const float* x) {
         bf16x8 v;
@@ -119,6 +125,12 @@ template <> struct Vec8<float> {
     static __device__ __forceinline__ void copy(const float* s, float* d) {
         *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(s);
         *reinterpret_cast<u32x4*>(d + 4) = *reinterpret_cast<const u32x4*>(s + 4);
+    }
+    static __device__ __forceinline__ void load_nt(const float* p, float* x) {
+        const floatx4 a = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p));
+        const floatx4 b = __builtin_nontemporal_load(reinterpret_cast<const floatx4*>(p + 4));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
     }
     static __device__ __forceinline__ void store_nt(float* p, const float* x) {
         __builtin_nontemporal_store(floatx4{x[0], x[1], x[2], x[3]}, reinterpret_cast<floatx4*>(p));

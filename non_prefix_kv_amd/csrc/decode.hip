@@ -121,7 +121,7 @@ __device__ __forceinline__ void dot_rows(const T* __restrict__ x, const T* const
         float xv[8], wv[R][8];
         Vec8<T>::load(x + k, xv);
 #pragma unroll
-        for (int r = 0; r < R; ++r) Vec8<T>::load(wr[r] + k, wv[r]);
+        for (int r = 0; r < R; ++r) Vec8<T>::load_nt(wr[r] + k, wv[r]);   // weights: once per step
 #pragma unroll
         for (int r = 0; r < R; ++r)
 #pragma unroll
@@ -251,9 +251,9 @@ __global__ __launch_bounds__(kThreads) void decode_attention_kernel(DecodeAttnAr
 #pragma unroll
     for (int it = 0; it < ITERS; ++it) {
         const int j = j0 + it * KPI + sub;
-        if (j < n_keys) {
-            Vec8<T>::load(row(a.k, a.k_new, j), kr[it]);
-            Vec8<T>::load(row(a.v, a.v_new, j), vr[it]);
+        if (j < n_keys) {            // cached rows: read once per step
+            Vec8<T>::load_nt(row(a.k, a.k_new, j), kr[it]);
+            Vec8<T>::load_nt(row(a.v, a.v_new, j), vr[it]);
         } else {
 #pragma unroll
             for (int i = 0; i < 8; ++i) kr[it][i] = vr[it][i] = 0.f;
