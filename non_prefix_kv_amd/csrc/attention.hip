@@ -303,10 +303,11 @@ constexpr int QT32 = 128;   // queries per workgroup
 constexpr int KBL = 64;     // keys per block
 constexpr float kLazyLog2 = 8.0f;   // rescale threshold of the running maximum (log2 units)
 // (query tile, head, key segment) units wanted per launch.  Measured on
-// MI355X, 832 queries x 4096 keys x 32 heads in the 7B step: 1024 units
-// (5 segments) 2.84 ms of attention + merge per step, 2048 (8 segments)
-// 3.03, 4096 (16 segments of 256 keys) 3.78, 512-768 the same as 1024.
-constexpr int kSplitUnits = 1024;
+// MI355X, 832 queries x 4096 keys x 32 heads in the 7B step: 768 units
+// (4 segments) 2.54 ms of attention + merge per step, 512 (3 segments)
+// 2.58, 1024 (5 segments) 2.60, 1536 2.77; earlier, with a slower kernel,
+// 2048 (8 segments) and 4096 (16 segments of 256 keys) were slower still.
+constexpr int kSplitUnits = 768;
 
 // Hardware workgroup ids are dealt round-robin over the 8 XCDs; renumber so
 // each XCD gets a contiguous logical range (blocks that read the same key
