@@ -308,6 +308,7 @@ constexpr float kLazyLog2 = 8.0f;   // rescale threshold of the running maximum 
 // 2.58, 1024 (5 segments) 2.60, 1536 2.77; earlier, with a slower kernel,
 // 2048 (8 segments) and 4096 (16 segments of 256 keys) were slower still.
 constexpr int kSplitUnits = 768;
+constexpr int kFewSegs = 4;   // the merge's one-round-trip path takes up to this many segments
 
 // Hardware workgroup ids are dealt round-robin over the 8 XCDs; renumber so
 // each XCD gets a contiguous logical range (blocks that read the same key
@@ -627,10 +628,46 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a, cons
     const AttnRange& tile = tl.t[qt];
     const int ql = qg * QPW + (int)threadIdx.x / TPQ;
     if (ql >= tile.nq) return;
-    const int n_seg = max(1, (a.part_nk[qt] + a.seg_keys - 1) / a.seg_keys);
-    if (n_seg <= 1) return;
     const int c = ((int)threadIdx.x % TPQ) * 8;
     const int64_t slot0 = ((int64_t)qt * a.n_q_heads + h) * a.max_seg;
+    bf16* dst = static_cast<bf16*>(a.out) + (int64_t)(tile.q0 + ql) * a.n_q_heads * D + h * D + c;
+    if (a.max_seg <= kFewSegs) {
+        // Up to kFewSegs segments: every slot's partial is loaded together
+        // with the segment count, one round trip instead of three (slots
+        // past max_seg repeat the last one and are never used).
+        float2 ml[kFewSegs];
+        bf16x8 ov[kFewSegs];
+#pragma unroll
+        for (int sg = 0; sg < kFewSegs; ++sg) {
+            const int64_t sl = slot0 + min(sg, a.max_seg - 1);
+            ml[sg] = *reinterpret_cast<const float2*>(a.part_ml + (sl * QT32 + ql) * 2);
+            ov[sg] = *reinterpret_cast<const bf16x8*>(a.part_o + (sl * QT32 + ql) * D + c);
+        }
+        const int n_seg = max(1, (a.part_nk[qt] + a.seg_keys - 1) / a.seg_keys);
+        if (n_seg <= 1) return;
+        float M = -INFINITY;
+#pragma unroll
+        for (int sg = 0; sg < kFewSegs; ++sg)
+            if (sg < n_seg) M = fmaxf(M, ml[sg].x);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        float L = 0.f;
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int sg = 0; sg < kFewSegs; ++sg) {
+            if (sg >= n_seg) break;
+            const float wl = __builtin_amdgcn_exp2f(ml[sg].x - Mu) * ml[sg].y;
+            L += wl;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) acc[e] += wl * static_cast<float>(ov[sg][e]);
+        }
+        const float inv = L > 0.f ? 1.0f / L : 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] *= inv;
+        Vec8<bf16>::store(dst, acc);
+        return;
+    }
+    const int n_seg = max(1, (a.part_nk[qt] + a.seg_keys - 1) / a.seg_keys);
+    if (n_seg <= 1) return;
     float M = -INFINITY;
     for (int sg = 0; sg < n_seg; ++sg)
         M = fmaxf(M, a.part_ml[((slot0 + sg) * QT32 + ql) * 2]);
@@ -650,8 +687,7 @@ __global__ __launch_bounds__(256) void attention_combine_kernel(AttnArgs a, cons
     const float inv = L > 0.f ? 1.0f / L : 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] *= inv;
-    Vec8<bf16>::store(static_cast<bf16*>(a.out) + (int64_t)(tile.q0 + ql) * a.n_q_heads * D + h * D + c,
-                      acc);
+    Vec8<bf16>::store(dst, acc);
 }
 
 // Query tiles of height `qth` cut from the ranges, ordered by an estimate of
