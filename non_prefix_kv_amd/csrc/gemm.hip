@@ -555,7 +555,10 @@ __device__ __forceinline__ void epilogue_finish(const GemmArgs& g, int m_tile, i
 // whole stages, and each wave issues 4 of the stage's 32 copies.  Measured
 // on MI355X against that four-wave form: 832 x 4096 x 11008 955 vs 890
 // TFLOP/s, 832 x 22016 x 4096 788 vs 761; one wave per SIMD left the matrix
-// units idle in every s_waitcnt and barrier (40% busy).
+// units idle in every s_waitcnt and barrier (40% busy).  Also measured and
+// dropped: register-staged copies into four LDS buffers with two register
+// sets (five stages in flight), on the 7B step O 1.42 -> 1.53 ms and down
+// 3.31 -> 3.43 ms per step.
 constexpr int kThreads8 = 512;
 template <int EPI, int S>
 __global__ __launch_bounds__(kThreads8, 1) void gemm_dma8_kernel(GemmArgs g) {
