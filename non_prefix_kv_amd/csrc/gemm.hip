@@ -10,8 +10,8 @@
 //
 // Tiling for gfx950: a 128x128 output tile per 256-thread workgroup, four
 // wave64s in a 2x2 grid, each wave 64x64: 2x2 32x32x16 MFMA tiles for bf16
-// (the 32x32 form issues about 1.4x the flops per cycle of the 16x16x32 form
-// on gfx950: 1.87 vs 1.35 PFLOP/s measured in a register-only loop), 4x4
+// (in register-only loops at one wave per SIMD the 32x32 form runs at about
+// 1.95 PFLOP/s, the 16x16x32 form at 1.86 with an 8x8 accumulator grid), 4x4
 // 16x16 tiles of 16x16x4 f32 MFMAs for f32.  K advances
 // 128 bytes per step (64 bf16 / 32 f32) through double-buffered LDS.  LDS rows
 // are unpadded 128-byte rows of eight 16-byte chunks stored at a swizzled
