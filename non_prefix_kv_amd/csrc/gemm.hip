@@ -1636,10 +1636,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_mid_kernel(GemmArgs g) {
 // and read as zero.  LDS rows are 128 bytes with chunk c of row r at slot
 // c ^ ((r / 2) % 8): the 16 rows of one fragment read and the 8 rows of one
 // wave's store fall on distinct banks.  Measured and dropped: a second
-// register set (loads two stages ahead) and stores split evenly over both
-// K steps of a stage (neither changed the time), and B fragments loaded by
-// each wave straight into its MFMA operand registers with only A through LDS
-// (gate/up 5.05 -> 7.90 ms per 7B step).
+// register set (loads two stages ahead), stores split evenly over both K
+// steps of a stage, or all in the first (none changed the time), and B
+// fragments loaded by each wave straight into its MFMA operand registers
+// with only A through LDS (gate/up 5.05 -> 7.90 ms per 7B step).
 constexpr int kRsK = 64;                              // K per stage
 constexpr int kRsABytes = MBM * kRsK * 2;             // 28 KB
 constexpr int kRsBuf = (MBM + MBN) * kRsK * 2;        // 52 KB
