@@ -160,6 +160,10 @@ def test_rmsnorm_vs_oracle(lib, dt, rows, d):
                                    # 224x192 tiles (ragged rows and columns, M = 224, K = 64)
                                    (832, 12288, 4096), (833, 12288, 192), (650, 12000, 320),
                                    (224, 40000, 64),
+                                   # 224x192 register-staged tiles (K a multiple of 128,
+                                   # down to two K stages; ragged rows and columns)
+                                   (833, 12000, 128), (650, 12100, 384), (1300, 7000, 256),
+                                   (833, 12100, 1280),
                                    # 256x256 tiles (ragged rows and columns; the last one
                                    # takes more than four rounds: the 4-stage kernel)
                                    (2048, 8192, 256), (2000, 8000, 320), (4096, 4096, 1024),
