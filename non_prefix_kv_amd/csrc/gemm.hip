@@ -1753,8 +1753,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_rs_kernel(GemmArgs g) {
     // fragments of the next step are read from `rbuf` (chunk column `o`)
     // into (xa, xb).  In a stage's second step (SECOND) the registers of
     // stage kt + 2 are also stored to buffer `fill` and stage kt + 3 is
-    // loaded; the barrier at the start of the next stage publishes the
-    // stores (and frees the buffer they go to two stages later).
+    // loaded.  The barrier at the start of the next stage publishes these
+    // stores; the one at the start of this stage freed their buffer (stage
+    // kt - 1's, read last in that stage's first step).
     // Stage kt lives in buffer kt % 3; near the end the loads repeat the
     // last stage and the stores and reads go to buffers never read again,
     // so the loop body is the same for every stage.
