@@ -456,9 +456,13 @@ __global__ __launch_bounds__(kT32, 2) void attention64_kernel(AttnArgs a, const 
     const int tr_row = 4 * (tr_g >> 1) + (tr_s >> 2);       // + 16 q4 (+ 8 for the upper half)
     const int tr_col = 16 * (tr_g & 1) + 4 * (tr_s & 3);    // + 32 dt
     const int vkey = v_key<D>(tr_row);                      // same for rows tr_row + 8 j
+    // A wave whose 32 query slots all lie past the tile's last query (the
+    // short last tile of a range) has nothing to compute; it still copies its
+    // share of every block and meets every barrier.
+    const bool wave_live = wave * 32 < tile.nq;
     auto compute = [&](int st, int kb) {
         const int k0 = (kb_beg + kb) * KBL;
-        if (a.kv_pos0 + k0 > wmax) return;          // wave-uniform: nothing visible
+        if (!wave_live || a.kv_pos0 + k0 > wmax) return;   // wave-uniform
         const unsigned char* sk = smem + st * 2 * BLK;
         const unsigned char* sv = sk + BLK;
         // S^T = K Q^T for the block's two 32-key halves: K fragments are read
