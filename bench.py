@@ -70,6 +70,10 @@ def parse():
                                          "memcpy"],
                     help="only time one bandwidth-bound step alone through its C-ABI entry, "
                          "at the shape the llama2-7b-shape step gives it, then exit")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time the library's GEMM (fp32 store) beside the vendor BLAS "
+                         "(torch linear, bf16 out) on the llama2-7b-shape step's projection "
+                         "shapes, weights cold, then exit")
     ap.add_argument("--reps", type=int, default=200, help="launches timed with --kernel")
     ap.add_argument("--trace-summary", metavar="CSV",
                     help="summarize a rocprofv3 kernel_trace.csv of a bench run (timed steps "
@@ -232,6 +236,50 @@ def counter_table(res, calibration):
                  if m(d, "TCC_HIT_sum") is not None and m(d, "TCC_MISS_sum") is not None
                  and m(d, "TCC_HIT_sum") + m(d, "TCC_MISS_sum") > 0 else ""]
         print(f"| {k} | " + " | ".join(cells) + " |")
+
+
+def vendor_gemm(reps=30):
+    """The library's GEMM (cb_gemm: bf16 operands, fp32 store, no epilogue)
+    and the vendor BLAS (torch.nn.functional.linear: hipBLASLt, bf16 out) on
+    the projection shapes of the llama2-7b-shape step: 4096 rows (layers 0-1),
+    947 rows (layer 1's MLP, layer 2's q/k/v) and 832 rows (steady layers).
+    Each launch takes the next weight of a ring larger than the last-level
+    cache, as in the step, where every layer has its own weights."""
+    import torch
+    import non_prefix_kv_amd as npk
+    dev, bf = "cuda", torch.bfloat16
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    d, F = 4096, 11008
+    shapes = [(m, k, n, name) for m in (4096, 947, 832)
+              for (k, n, name) in ((d, 3 * d, "qkv"), (d, d, "o"), (d, 2 * F, "gateup"),
+                                   (F, d, "down"))]
+    out = []
+    st = torch.cuda.current_stream()
+    for m, k, n, name in shapes:
+        nw = max(2, -(-(1 << 30) // (n * k * 2)))
+        ws = [torch.randn((n, k), generator=g, device=dev).to(bf) for _ in range(nw)]
+        x = torch.randn((m, k), generator=g, device=dev).to(bf)
+        c = torch.empty((m, n), dtype=torch.float32, device=dev)
+        row = {"shape": f"{m}x{n}x{k}", "proj": name, "rows": m}
+        for lib in ("cb_gemm", "hipblaslt"):
+            fn = ((lambda w: npk.cb_gemm(x, w, c, m, n, k)) if lib == "cb_gemm"
+                  else (lambda w: torch.nn.functional.linear(x, w)))
+            for i in range(3):
+                fn(ws[i % nw])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            st.synchronize()
+            e0.record(st)
+            for i in range(reps):
+                fn(ws[i % nw])
+            e1.record(st)
+            e1.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            row[lib] = {"us": round(us, 1), "frac_mfma_bf16": round(2.0 * m * n * k / us / 2.5e9, 3)}
+        print(json.dumps(row), flush=True)
+        out.append(row)
+        del ws
+    print(json.dumps({"vendor_gemm": out}))
 
 
 def kernel_alone(kind, reps):
@@ -1105,6 +1153,9 @@ def main():
         return
     if args.kernel:
         kernel_alone(args.kernel, args.reps)
+        return
+    if args.vendor_gemm:
+        vendor_gemm()
         return
     import torch
     import non_prefix_kv_amd as npk
