@@ -159,6 +159,33 @@ def trace_summary(path, match=None):
     for k, (n, t) in sorted(agg.items(), key=lambda kv: -kv[1][1]):
         print(f"| {k} | {n} | {t / n / 1e3:.1f} | {t / 1e6:.3f} | {100 * t / total:.1f}% |")
     print(f"\n{len(rows)} dispatches, {total / 1e6:.3f} ms of kernel time")
+    if not match and rows:
+        _timeline(rows)
+
+
+def _timeline(rows):
+    """Wall time of the timed dispatches (first start to last end), the share
+    of it in which some kernel runs (union of the dispatch intervals), and the
+    kernel time per hardware queue (the caller's stream and the library's side
+    stream land on different queues).  Totals over all timed steps."""
+    iv = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows)
+    wall = iv[-1][1] - iv[0][0]
+    busy, cs, ce = 0, iv[0][0], iv[0][1]
+    for a, b in iv[1:]:
+        if a > ce:
+            busy += ce - cs
+            cs, ce = a, b
+        else:
+            ce = max(ce, b)
+    busy += ce - cs
+    per_q = {}
+    for r in rows:
+        q = r.get("Queue_Id", "?")
+        per_q[q] = per_q.get(q, 0) + int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    print(f"\nTimeline: wall {wall / 1e6:.3f} ms over the timed dispatches; some kernel running "
+          f"{busy / wall:.3f} of it (idle {(wall - busy) / 1e6:.3f} ms)")
+    for q, t in sorted(per_q.items(), key=lambda kv: -kv[1]):
+        print(f"- queue {q}: {t / 1e6:.3f} ms of kernel time")
 
 
 def counter_summary(paths, calibration=None, all_dispatches=False):
