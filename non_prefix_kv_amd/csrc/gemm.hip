@@ -1938,9 +1938,58 @@ bool dma_ok(int epi, const GemmArgs& g) {
     return true;
 }
 
+// The product restricted to result rows [r0, r0 + m), for the plain-store
+// and SwiGLU epilogues: A and the output move by r0 rows.
+GemmArgs row_slice(int epi, const GemmArgs& g, int r0, int m) {
+    GemmArgs h = g;
+    h.M = m;
+    h.a = static_cast<const bf16*>(g.a) + (int64_t)r0 * g.K;
+    if (epi == EPI_STORE_F32) h.out0 = static_cast<float*>(g.out0) + (int64_t)r0 * g.N;
+    else h.out0 = static_cast<bf16*>(g.out0) + (int64_t)r0 * g.N;
+    return h;
+}
+
+// A product a few rows taller than a whole number of 224-row tiles (947
+// rows: layer 1's MLP and layer 2's q/k/v at 7B width, r = 15%) would spend
+// a round of 224x192 tiles, or a larger tile, on its last rows.  Split: the
+// whole 224-row tiles on 224x192 tiles, the remaining rows (at most
+// kSplitRows) on 128x128 tiles, when the cost model prices the two launches
+// below the best single one.  Only the plain-store and SwiGLU products
+// take it: at the widths served here the q/k/v and residual products price a
+// split above their single launch.
+constexpr int kSplitRows = 64;
+
+bool try_row_split(int epi, const GemmArgs& g, hipStream_t s, hipError_t* err) {
+    const int rem = g.M % MBM, m_main = g.M - rem;
+    if (epi != EPI_STORE_F32 && epi != EPI_SWIGLU) return false;
+    if (m_main == 0 || rem == 0 || rem > kSplitRows) return false;
+    if (!mid_shape_ok(epi, g) || !dma_ok(epi, g)) return false;
+    const int64_t rows_b = epi == EPI_SWIGLU ? 2 * (int64_t)g.N : g.N;
+    const int64_t cus = num_cus();
+    auto rounds = [&](int64_t m, int bm, int bn) {
+        const int64_t tiles = ((m + bm - 1) / bm) * ((rows_b + bn - 1) / bn);
+        return (double)((tiles + cus - 1) / cus);
+    };
+    double best = rounds(g.M, BM, BN);
+    best = std::min(best, kMidCost * rounds(g.M, MBM, MBN));
+    if (big_shape_ok(epi, g))
+        best = std::min(best, (epi == EPI_QKV ? 3.1 : 2.9) * rounds(g.M, BBM, BBN));
+    const double split = kMidCost * rounds(m_main, MBM, MBN) + rounds(rem, BM, BN);
+    if (!(split < best)) return false;
+    const GemmArgs lo = row_slice(epi, g, 0, m_main), hi = row_slice(epi, g, m_main, rem);
+    hipError_t e = epi == EPI_SWIGLU ? launch_mid<EPI_SWIGLU>(lo, s)
+                                     : launch_mid<EPI_STORE_F32>(lo, s);
+    if (e == hipSuccess)
+        e = epi == EPI_SWIGLU ? launch_dma<EPI_SWIGLU>(hi, s) : launch_dma<EPI_STORE_F32>(hi, s);
+    *err = e;
+    return true;
+}
+
 template <typename T>
 hipError_t launch_dtype(int epi, const GemmArgs& g, hipStream_t s) {
     if constexpr (is_bf16<T>()) {
+        hipError_t split_err;
+        if (try_row_split(epi, g, s, &split_err)) return split_err;
         const TileKind tk = choose_tile(epi, g);
         if (tk == TILE_224x192) {
             switch (epi) {

@@ -7,7 +7,8 @@ gate/up products (Llama-2-7B shape) and the q/k/v, O and down products
 (Llama-2-13B shape).  One-layer prefills at those row counts exercise each
 epilogue on that tile (RoPE at real positions on q/k/v tiles that straddle
 the q|k and k|v boundaries, SiLU(gate)*up on interleaved gate/up rows, the
-gathered residual) against the oracle's prefill.  A one-KV-head shape at
+gathered residual) against the oracle's prefill; at 947 rows the gate/up
+product runs split, 896 rows on 224x192 tiles and 51 on 128x128.  A one-KV-head shape at
 4000 rows puts q, k and v in one 224x192 tile column range.  A 16640-row
 prefill runs every epilogue on the 4-stage 256x256 kernel of long launches."""
 import dataclasses
@@ -33,6 +34,7 @@ GQA_1KV = ModelShape(n_layers=1, d_model=2048, n_q_heads=16, n_kv_heads=1, head_
 
 
 @pytest.mark.parametrize("name,rows,pos0", [("llama7b-4k", 832, 0), ("llama7b-4k", 889, 1000),
+                                            ("llama7b-4k", 947, 300),
                                             ("llama13b-8k", 1664, 77), ("gqa-1kv", 4000, 5)])
 def test_prefill_projection_tiles_vs_oracle(lib, name, rows, pos0):
     base = GQA_1KV if name == "gqa-1kv" else WORKLOADS[name].shape

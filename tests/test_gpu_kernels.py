@@ -167,7 +167,9 @@ def test_rmsnorm_vs_oracle(lib, dt, rows, d):
                                    # 256x256 tiles (ragged rows and columns; the last one
                                    # takes more than four rounds: the 4-stage kernel)
                                    (2048, 8192, 256), (2000, 8000, 320), (4096, 4096, 1024),
-                                   (4000, 20000, 256)])
+                                   (4000, 20000, 256),
+                                   # rows split: 896 on 224x192 tiles, the last 51 on 128x128
+                                   (947, 22016, 1024)])
 def test_gemm_vs_definition(lib, dt, m, n, k):
     rng = np.random.default_rng(m * 7 + n)
     a = round_to(rng.standard_normal((m, k)), dt)
